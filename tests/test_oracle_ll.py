@@ -1,0 +1,158 @@
+"""Pins for the oracle's self-synchronizing slots (flash-comm, abstract: each data block carries evidence
+of its readiness and the receiver validates the blocks it needs without a barrier; the reduction order
+is fixed whatever the arrival order).
+
+Pins: with small-integer payloads every fp32 partial sum is exact, so a complete block must equal the
+exact sum; every kind of stale epoch word must be detected, the flags must equal the injected set
+exactly, pending blocks stay untouched, and a retry after the late blocks arrive must give the same
+bits as a run where everything was on time."""
+import numpy as np
+import pytest
+
+from tensor_all_reduce_amd import datagen as dg
+
+M32 = 0xFFFFFFFF
+
+
+def bf16(x):
+    return dg.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def f32(b):
+    return dg.bf16_bits_to_f32(b)
+
+
+def set_epochs(slots, ep):
+    s = slots.copy()
+    s &= np.uint64(0xFFFFFFFF)
+    s |= ep.astype(np.uint64) << np.uint64(32)
+    return s
+
+
+def int_payload(rng, n):
+    return bf16(rng.integers(-32, 33, size=n).astype(np.float32))  # |sum of 8| <= 256: exact in bf16
+
+
+@pytest.mark.parametrize("B", [32, 64, 128])
+def test_all_valid_exact_sum(orc, B):
+    rng = np.random.default_rng(B)
+    R, n, e = 8, 2 * B * 40, 77
+    xs = [int_payload(rng, n) for _ in range(R)]
+    slots = [orc.ll_pack(x, B, e) for x in xs]
+    out, stale, done, cnt = orc.ll_unpack_reduce(slots, n, B, e)
+    exact = np.sum([f32(x).astype(np.float64) for x in xs], axis=0)
+    assert np.array_equal(f32(out).astype(np.float64), exact)
+    assert not stale.any() and done.all() and list(cnt) == [0, 0]
+
+
+def test_slot_layout(orc):
+    """Slot k = bf16 element 2k in bits 0..15, element 2k+1 in bits 16..31, epoch in bits 32..63."""
+    x = np.array([0x1111, 0x2222, 0x3333, 0x4444], np.uint16)
+    s = orc.ll_pack(x, 2, 0xDEADBEEF)
+    assert list(s) == [0xDEADBEEF22221111, 0xDEADBEEF44443333]
+
+
+def test_write_order_does_not_matter(orc):
+    rng = np.random.default_rng(5)
+    n, B, e = 2 * 64 * 32, 64, 9
+    x = bf16(rng.standard_normal(n))
+    a = orc.ll_pack(x, B, e)
+    b = orc.ll_pack(x, B, e, order=rng.permutation(n // 2 // B).astype(np.int32))
+    assert np.array_equal(a, b)
+
+
+STALE_WORDS = {
+    "prev": lambda e: (e - 1) & M32, "next": lambda e: (e + 1) & M32, "zero": lambda e: 0 if e else 1,
+    "not": lambda e: (~e) & M32, "msb": lambda e: e ^ 0x80000000, "lowbit": lambda e: e ^ 1,
+}
+
+
+@pytest.mark.parametrize("e", [0, 1, 0x2A, 0x7FFFFFFF, 0x80000000, 0xFFFFFFFF])
+@pytest.mark.parametrize("kind", sorted(STALE_WORDS) + ["torn"])
+def test_every_stale_word_detected(orc, e, kind):
+    """One (rank, block) copy carries a wrong word (or, torn, a single wrong slot); the receiver must flag
+    exactly that pair, leave that block untouched and pending, and finish every other block."""
+    rng = np.random.default_rng([sorted(STALE_WORDS).index(kind) if kind in STALE_WORDS else 99, e])
+    R, B = 4, 64
+    nblk = 16
+    n = 2 * B * nblk
+    xs = [int_payload(rng, n) for _ in range(R)]
+    slots = [orc.ll_pack(x, B, e) for x in xs]
+    r_bad, b_bad = 2, 5
+    ep = np.full(n // 2, e, np.uint32)
+    if kind == "torn":
+        ep[b_bad * B + 17] = (e - 1) & M32
+    else:
+        ep[b_bad * B:(b_bad + 1) * B] = STALE_WORDS[kind](e)
+    slots[r_bad] = set_epochs(slots[r_bad], ep)
+    sentinel = np.full(n, 0x7E7E, np.uint16)
+    out, stale, done, cnt = orc.ll_unpack_reduce(slots, n, B, e, out=sentinel.copy())
+    want = np.zeros((R, nblk), np.uint8)
+    want[r_bad, b_bad] = 1
+    assert np.array_equal(stale, want)
+    assert done[b_bad] == 0 and done.sum() == nblk - 1
+    assert list(cnt) == [1, 1]
+    blk = slice(b_bad * 2 * B, (b_bad + 1) * 2 * B)
+    assert np.all(out[blk] == 0x7E7E)
+    exact = np.sum([f32(x).astype(np.float64) for x in xs], axis=0)
+    keep = np.ones(n, bool)
+    keep[blk] = False
+    assert np.array_equal(f32(out[keep]).astype(np.float64), exact[keep])
+
+
+def test_seeded_stale_mix_flags_and_retry(orc):
+    """The workload's stale mix (2% of (rank, block) pairs, several kinds of wrong words): flags equal
+    the injected set, counters count it, and after the late blocks are rewritten with the right epoch a
+    second pass completes every pending block with the same bits as an all-valid run."""
+    cfg = dg.CONFIGS[4]
+    R, B, e = cfg.R, cfg.block_slots, cfg.epoch
+    n = 2 * B * 512
+    nslots, nblk = n // 2, n // 2 // B
+    xs = [dg.partial(cfg, r, n) for r in range(R)]
+    good = [orc.ll_pack(x, B, e, order=dg.write_order(cfg, r, nblk)) for r, x in enumerate(xs)]
+    eps, masks = zip(*[dg.stale_epochs(cfg, r, nslots, p=0.05) for r in range(R)])
+    late = [set_epochs(g, ep) for g, ep in zip(good, eps)]
+    inj = np.stack(masks)
+    assert inj.sum() > 0
+    ref_out, _, ref_done, ref_cnt = orc.ll_unpack_reduce(good, n, B, e)
+    assert ref_done.all() and list(ref_cnt) == [0, 0]
+
+    out = np.zeros(n, np.uint16)
+    done = np.zeros(nblk, np.uint8)
+    cnt = np.zeros(2, np.uint32)
+    out, stale, done, cnt = orc.ll_unpack_reduce(late, n, B, e, out=out, done=done, counters=cnt)
+    assert np.array_equal(stale, inj)
+    pending = inj.any(axis=0)
+    assert cnt[0] == inj.sum() and cnt[1] == pending.sum()
+    assert np.array_equal(done.astype(bool), ~pending)
+    # the retry: late blocks have now arrived
+    cnt2 = np.zeros(2, np.uint32)
+    out, stale2, done, cnt2 = orc.ll_unpack_reduce(good, n, B, e, out=out, done=done, counters=cnt2)
+    assert done.all() and list(cnt2) == [0, 0]
+    assert np.array_equal(out, ref_out)
+
+
+def test_whole_rank_stale(orc):
+    """A rank that never wrote this round (its slots all carry the previous epoch): every block pending."""
+    rng = np.random.default_rng(8)
+    R, B, e = 8, 64, 1000
+    n = 2 * B * 8
+    xs = [int_payload(rng, n) for _ in range(R)]
+    slots = [orc.ll_pack(x, B, e) for x in xs]
+    slots[7] = orc.ll_pack(xs[7], B, e - 1)
+    out, stale, done, cnt = orc.ll_unpack_reduce(slots, n, B, e)
+    assert stale[7].all() and not stale[:7].any()
+    assert not done.any() and list(cnt) == [8, 8]
+
+
+def test_done_blocks_are_skipped(orc):
+    """Blocks already marked done are not examined again: their output and flags stay as they are."""
+    rng = np.random.default_rng(12)
+    R, B, e = 2, 32, 3
+    n = 2 * B * 4
+    xs = [int_payload(rng, n) for _ in range(R)]
+    slots = [orc.ll_pack(x, B, e - 1) for x in xs]  # all stale
+    done = np.array([1, 0, 1, 0], np.uint8)
+    out, stale, done2, cnt = orc.ll_unpack_reduce(slots, n, B, e, out=np.full(n, 5, np.uint16), done=done)
+    assert np.array_equal(stale, np.array([[0, 1, 0, 1]] * 2, np.uint8))
+    assert list(cnt) == [4, 2] and np.all(out == 5)
