@@ -1,0 +1,141 @@
+/* fc.h -- C ABI of libfc.so: one GPU's share of a "flash all-reduce" on MI355X (gfx950).
+ *
+ * The operations follow three descriptions of tensor-parallel all-reduce for LLM inference:
+ *  - Flash Communication: Reducing Tensor Parallelization Bottleneck for Fast Large Language Model
+ *    Inference (abstract; summary "Core ideas of the solution"): low-bit fine-grained quantization of
+ *    activations, and a two-step all-reduce (reduce-scatter, then all-gather).
+ *  - flash-comm (abstract): self-synchronizing transfers, each data block carrying evidence of its
+ *    readiness that the receiver validates without a barrier; reduction order decoupled from
+ *    transport order.
+ *  - TokenWeave: Efficient Compute-Communication Overlap for Distributed LLM Inference (abstract):
+ *    fused AllReduce-RMSNorm on few compute units, overlapped with the other half-batch's compute.
+ * The pages fix no bit widths, layouts or formulas; the choices made here are stated per call.
+ *
+ * Conventions for every call
+ *  - Pointers are DEVICE pointers unless marked [host].  The caller owns all memory and keeps it alive
+ *    until the enqueued work has finished.  No call allocates, frees or synchronizes.
+ *  - Each call validates its arguments on the host before touching the GPU, then enqueues its kernel(s)
+ *    on `stream` (0 = the null stream) and returns.  Device faults are asynchronous and surface at the
+ *    caller's next synchronization.
+ *  - Status codes: FC_E_NULL a required pointer is NULL; FC_E_ARG a value outside the supported set
+ *    (bits not 4/8, group not 32/64/128/256, R not in [1,16], eps not > 0, block_slots not
+ *    32/64/128/256, an input range that partially overlaps an output range); FC_E_SHAPE sizes that do
+ *    not divide (n % group, L % group, n % hidden, hidden % 16, n % (2*block_slots)) or exceed the
+ *    limits below; FC_E_ALIGN a data pointer not 16-byte aligned (meta: 4-byte); FC_E_LAUNCH the HIP
+ *    launch failed (the hipError_t is kept for fc_last_hip_error()).
+ *  - Out-of-contract values (NaN, Inf, |x| > 65504, group ranges or sums outside the fp16 range) give
+ *    unspecified results but never an out-of-bounds access.
+ *  - bf16 and fp16 values are passed as their uint16_t bit patterns.
+ *  - Element counts are limited to 2^31 - 16 per rank buffer (n, L, rows*hidden).
+ */
+#ifndef FC_H
+#define FC_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FC_ABI_VERSION 1
+
+typedef enum {
+    FC_OK = 0,
+    FC_E_NULL = 1,
+    FC_E_ARG = 2,
+    FC_E_SHAPE = 3,
+    FC_E_ALIGN = 4,
+    FC_E_LAUNCH = 5
+} fc_status;
+
+/* One quantized message of n elements in flat groups of `group` consecutive elements.
+ *  codes: n*bits/8 bytes.  bits = 8: byte i holds code i.  bits = 4: byte i holds code 2i in its low
+ *         nibble and code 2i+1 in its high nibble.  Codes are unsigned, 0 .. 2^bits - 1.
+ *  meta:  n/group words; bits 0..15 = fp16 scale s, bits 16..31 = fp16 zero-point z of the group.
+ *  Value of code q: fl(q*s + z) in fp32 (q*s is exact, so this is one rounding).
+ *  Quantizer (asymmetric min/max): z = largest fp16 <= min(x) (a -0 minimum counts as +0);
+ *  s = smallest fp16 >= fp32((max(x) - z) / (2^bits - 1)), or +0 when max(x) == z;
+ *  q = round-half-even((x - z) * fp32(1/s)) clamped to [0, 2^bits - 1] (all codes 0 when s == 0). */
+typedef struct {
+    uint8_t* codes;
+    uint32_t* meta;
+} fc_qmsg;
+
+/* Fused residual-add + RMSNorm epilogue (TokenWeave, abstract), per row of `hidden` elements of the
+ * fp32 all-reduced value y:
+ *   h = y + residual (fp32);  residual_out = bf16(h);  r = 1/sqrt(mean(h*h) + eps);
+ *   out = bf16((h * r) * gamma).  bf16 rounding is to nearest even. */
+typedef struct {
+    const uint16_t* residual;  /* bf16 [rows*hidden], or NULL for no residual add */
+    const uint16_t* gamma;     /* bf16 [hidden], required */
+    float eps;                 /* > 0 */
+    int64_t hidden;            /* row length H: a multiple of 16, at most 131072 */
+    uint16_t* out;             /* bf16 [rows*hidden], required */
+    uint16_t* residual_out;    /* bf16 [rows*hidden] or NULL; may be exactly `residual` (in place) */
+} fc_norm;
+
+/* Group-quantize n bf16 values (Flash Communication: low-bit fine-grained activation quantization).
+ * x: bf16 [n], 16-byte aligned; n % group == 0.  Several ranks' buffers laid end to end may be
+ * quantized in one call (their boundaries fall on group boundaries).  out.codes: n*bits/8 bytes,
+ * out.meta: n/group words. */
+fc_status fc_quantize(const uint16_t* x, int64_t n, int bits, int group, fc_qmsg out, hipStream_t stream);
+
+/* Reduce-scatter receive side (Flash Communication, two-step all-reduce, step one; flash-comm: fixed
+ * reduction order).  For each of n_shards shards, in[shard*R + r] [host array] is rank r's quantized
+ * chunk of that shard (L elements, bits_in, `group`).  Each element is dequantized from every rank and
+ * summed in fp32 as a left fold in ascending rank order (rank 0 first), whatever order the chunks
+ * arrived in; the fp32 sum is requantized at bits_out into out[shard] [host array] (L elements), the
+ * payload of the all-gather step.  L % group == 0.  Several launches are enqueued when n_shards * R
+ * exceeds 128. */
+fc_status fc_reduce_shard(const fc_qmsg* in, int R, int64_t L, int n_shards, int bits_in, int bits_out,
+                          int group, const fc_qmsg* out, hipStream_t stream);
+
+/* All-gather receive side (Flash Communication, two-step all-reduce, step two).  shards[s] [host array,
+ * R entries] holds elements [s*L, (s+1)*L) of the flat [rows, hidden] result.  Each element is
+ * dequantized to fp32.  y (bf16 [R*L], or NULL) receives bf16(value).  norm (or NULL) applies the
+ * residual-add + RMSNorm epilogue to the fp32 values, rows = R*L/hidden.  y and norm may not both be
+ * NULL. */
+fc_status fc_gather_dequant(const fc_qmsg* shards, int R, int64_t L, int bits, int group, uint16_t* y,
+                            const fc_norm* norm, hipStream_t stream);
+
+/* Unquantized fused all-reduce + residual-add + RMSNorm (TokenWeave, abstract).  parts [host array, R
+ * entries]: bf16 [rows*hidden] partial sums.  y = fp32 left fold over ranks in ascending order, then the
+ * epilogue of `norm` (required).  max_workgroups bounds the number of workgroups (the compute-unit
+ * footprint); 0 = one workgroup per row.  Rows are independent, so any split of the rows into
+ * separate calls gives the same bits. */
+fc_status fc_reduce_rmsnorm(const uint16_t* const* parts, int R, int64_t rows, const fc_norm* norm,
+                            int max_workgroups, hipStream_t stream);
+
+/* Self-synchronizing receive side (flash-comm, abstract).  slots [host array, R entries]: uint64 [n/2]
+ * per rank; slot k = bf16 element 2k (bits 0..15), element 2k+1 (bits 16..31), epoch word (bits
+ * 32..63).  A block is `block_slots` consecutive slots; nblk = n/2/block_slots.  For each block b with
+ * done[b] == 0: stale[r*nblk + b] = 1 if any slot of rank r's copy carries an epoch word != epoch, else
+ * 0; if no rank is stale the block is reduced (fp32 left fold in ascending rank order, bf16 out) and
+ * done[b] = 1, otherwise out is left untouched and the block is pending.  Blocks with done[b] != 0 are
+ * skipped entirely.  counters[0] += stale (rank, block) pairs seen, counters[1] += pending blocks; the
+ * caller zeroes counters.  Calling again after late blocks have been rewritten completes them with the
+ * same bits as if they had been on time.  n % (2*block_slots) == 0. */
+fc_status fc_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, int block_slots, uint32_t epoch,
+                              uint16_t* out, uint8_t* stale, uint8_t* done, uint32_t* counters,
+                              hipStream_t stream);
+
+/* Sender side of the slots above, used to emulate a peer's writes: packs bf16 [n] into n/2 slots tagged
+ * with `epoch`, writing blocks in the order block_order[0..nblk) (an int32 permutation of the block
+ * indices, or NULL for ascending).  The result does not depend on the order. */
+fc_status fc_ll_pack(const uint16_t* x, int64_t n, int block_slots, uint32_t epoch, const int32_t* block_order,
+                     uint64_t* slots, hipStream_t stream);
+
+/* Measurement helper: copies `bytes` (a multiple of 16, 16-byte aligned pointers, no overlap) with
+ * 16-byte loads and stores; its bandwidth is the practical HBM ceiling the kernels above are compared
+ * with. */
+fc_status fc_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
+const char* fc_status_string(fc_status s);
+int fc_last_hip_error(void); /* hipError_t of the last FC_E_LAUNCH on this thread */
+int fc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FC_H */

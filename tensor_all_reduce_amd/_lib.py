@@ -1,0 +1,166 @@
+"""ctypes binding for libfc.so (see include/fc.h): argument marshalling only.
+
+Every function takes torch tensors (device memory) and passes their addresses, sizes and the current
+HIP stream to the C ABI of the same name; all arithmetic runs in the HIP kernels.  A non-OK status
+raises :class:`FcError`.  If the library has not been built, importing this module raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch  # loads PyTorch's HIP runtime first; libfc.so binds to that same runtime
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfc.so")
+
+FC_OK, FC_E_NULL, FC_E_ARG, FC_E_SHAPE, FC_E_ALIGN, FC_E_LAUNCH = range(6)
+
+
+class FcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.fc_status_string(status).decode()
+        if status == FC_E_LAUNCH:
+            msg += " (hipError %d)" % _lib.fc_last_hip_error()
+        super().__init__(f"{where}: {msg}")
+
+
+class QMsg(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("meta", C.c_void_p)]
+
+
+class Norm(C.Structure):
+    _fields_ = [("residual", C.c_void_p), ("gamma", C.c_void_p), ("eps", C.c_float), ("hidden", C.c_int64),
+                ("out", C.c_void_p), ("residual_out", C.c_void_p)]
+
+
+def _hip_runtimes_mapped() -> set[str]:
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m tensor_all_reduce_amd.build` "
+                          "(or __graft_entry__.build()); there is no CPU fallback")
+    lib = C.CDLL(LIB_PATH)
+    rts = _hip_runtimes_mapped()
+    if len(rts) > 1:
+        raise ImportError("two HIP runtimes are mapped in this process (%s); libfc.so must share "
+                          "PyTorch's" % ", ".join(sorted(rts)))
+    vp, i64, i32, u32 = C.c_void_p, C.c_int64, C.c_int, C.c_uint32
+    lib.fc_status_string.restype = C.c_char_p
+    lib.fc_status_string.argtypes = [i32]
+    lib.fc_last_hip_error.restype = i32
+    lib.fc_abi_version.restype = i32
+    lib.fc_quantize.argtypes = [vp, i64, i32, i32, QMsg, vp]
+    lib.fc_reduce_shard.argtypes = [C.POINTER(QMsg), i32, i64, i32, i32, i32, i32, C.POINTER(QMsg), vp]
+    lib.fc_gather_dequant.argtypes = [C.POINTER(QMsg), i32, i64, i32, i32, vp, C.POINTER(Norm), vp]
+    lib.fc_reduce_rmsnorm.argtypes = [C.POINTER(vp), i32, i64, C.POINTER(Norm), i32, vp]
+    lib.fc_ll_unpack_reduce.argtypes = [C.POINTER(vp), i32, i64, i32, u32, vp, vp, vp, vp, vp]
+    lib.fc_ll_pack.argtypes = [vp, i64, i32, u32, vp, vp, vp]
+    lib.fc_copy.argtypes = [vp, vp, i64, vp]
+    for f in ("fc_quantize", "fc_reduce_shard", "fc_gather_dequant", "fc_reduce_rmsnorm", "fc_ll_unpack_reduce",
+              "fc_ll_pack", "fc_copy"):
+        getattr(lib, f).restype = i32
+    return lib
+
+
+_lib = _load()
+lib = _lib
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(st: int, where: str):
+    if st != FC_OK:
+        raise FcError(st, where)
+
+
+def _qmsg(m) -> QMsg:
+    codes, meta = m
+    return QMsg(_ptr(codes), _ptr(meta))
+
+
+def _norm(norm) -> Norm | None:
+    if norm is None:
+        return None
+    return Norm(_ptr(norm.get("residual")), _ptr(norm["gamma"]), float(norm.get("eps", 1e-5)), int(norm["hidden"]),
+                _ptr(norm["out"]), _ptr(norm.get("residual_out")))
+
+
+def fc_quantize(x, bits: int, group: int, codes, meta, n: int | None = None, stream=None) -> None:
+    """Group-quantize bf16 `x` (n elements, default x.numel()) into `codes` and `meta`."""
+    n = x.numel() if n is None else n
+    _check(_lib.fc_quantize(_ptr(x), n, bits, group, QMsg(_ptr(codes), _ptr(meta)), _stream(stream)), "fc_quantize")
+
+
+def fc_reduce_shard(inputs, R: int, L: int, bits_in: int, bits_out: int, group: int, outputs, stream=None) -> None:
+    """inputs: n_shards*R (codes, meta) pairs, [shard][rank]; outputs: n_shards (codes, meta) pairs."""
+    n_shards = len(outputs)
+    ins = (QMsg * len(inputs))(*[_qmsg(m) for m in inputs])
+    outs = (QMsg * n_shards)(*[_qmsg(m) for m in outputs])
+    _check(_lib.fc_reduce_shard(ins, R, L, n_shards, bits_in, bits_out, group, outs, _stream(stream)),
+           "fc_reduce_shard")
+
+
+def fc_gather_dequant(shards, L: int, bits: int, group: int, y=None, norm: dict | None = None, stream=None) -> None:
+    """shards: R (codes, meta) pairs; y: bf16 [R*L] or None; norm: dict(residual, gamma, eps, hidden, out,
+    residual_out) or None."""
+    R = len(shards)
+    arr = (QMsg * R)(*[_qmsg(m) for m in shards])
+    nm = _norm(norm)
+    _check(_lib.fc_gather_dequant(arr, R, L, bits, group, _ptr(y), C.byref(nm) if nm is not None else None,
+                                  _stream(stream)), "fc_gather_dequant")
+
+
+def fc_reduce_rmsnorm(parts, rows: int, norm: dict, max_workgroups: int = 0, stream=None) -> None:
+    R = len(parts)
+    arr = (C.c_void_p * R)(*[_ptr(p) for p in parts])
+    nm = _norm(norm)
+    _check(_lib.fc_reduce_rmsnorm(arr, R, rows, C.byref(nm), max_workgroups, _stream(stream)), "fc_reduce_rmsnorm")
+
+
+def fc_ll_unpack_reduce(slots, n: int, block_slots: int, epoch: int, out, stale, done, counters, stream=None) -> None:
+    R = len(slots)
+    arr = (C.c_void_p * R)(*[_ptr(s) for s in slots])
+    _check(_lib.fc_ll_unpack_reduce(arr, R, n, block_slots, epoch & 0xFFFFFFFF, _ptr(out), _ptr(stale), _ptr(done),
+                                    _ptr(counters), _stream(stream)), "fc_ll_unpack_reduce")
+
+
+def fc_ll_pack(x, block_slots: int, epoch: int, slots, block_order=None, n: int | None = None, stream=None) -> None:
+    n = x.numel() if n is None else n
+    _check(_lib.fc_ll_pack(_ptr(x), n, block_slots, epoch & 0xFFFFFFFF, _ptr(block_order), _ptr(slots),
+                           _stream(stream)), "fc_ll_pack")
+
+
+def fc_copy(src, dst, nbytes: int | None = None, stream=None) -> None:
+    nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(_lib.fc_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "fc_copy")
+
+
+def fc_abi_version() -> int:
+    return _lib.fc_abi_version()

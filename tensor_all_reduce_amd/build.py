@@ -1,0 +1,74 @@
+"""Build libfc.so (the HIP kernels + C ABI) in-tree for gfx950.
+
+``python -m tensor_all_reduce_amd.build`` compiles every source under ``csrc/`` with hipcc and links
+the shared library next to this file.  The library is linked against the HIP runtime that PyTorch
+loads (torch/lib/libamdhip64.so), so that torch's streams and device pointers are valid inside it:
+one HIP runtime per process.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libfc.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+SOURCES = ["fc_kernels.hip", "fc_api.cpp"]
+
+# -ffp-contract=off: a*b+c stays two roundings unless written as an explicit fma, which the bit-exact
+# quantization codes depend on.  Packed fp32 instructions are disabled.
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-function",
+          "-I", INCLUDE, "-I", CSRC]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-fno-gpu-rdc"]
+
+
+def torch_lib_dir() -> str:
+    import importlib.util
+    spec = importlib.util.find_spec("torch")
+    if spec is None or not spec.origin:
+        raise RuntimeError("torch is required to locate the HIP runtime it loads")
+    return os.path.join(os.path.dirname(spec.origin), "lib")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        sys.stderr.write(out + "\n")
+        raise RuntimeError("command failed: " + " ".join(cmd))
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        path = os.path.join(CSRC, src)
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        if src.endswith(".hip"):
+            cmd = [HIPCC, *DEVICE, *COMMON, "-c", path, "-o", obj]
+        else:
+            cmd = [HIPCC, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-c", path, "-o", obj]
+        out = _run(cmd)
+        if verbose and out.strip():
+            print(out)
+        objs.append(obj)
+    tlib = torch_lib_dir()
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
+           "-L" + tlib, "-l:libamdhip64.so", "-Wl,-rpath," + tlib, "-Wl,--no-undefined"]
+    _run(cmd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

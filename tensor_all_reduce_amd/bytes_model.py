@@ -1,0 +1,56 @@
+"""Algorithmic HBM bytes of each call: every input read once and every output written once, at its
+stored width (bf16 2 B, codes bits/8 B, one 4-byte meta word per group, 8-byte slots).  The RMSNorm
+weight gamma counts once per call.  These are the bytes a kernel cannot avoid moving; achieved GB/s =
+these bytes / measured time."""
+from __future__ import annotations
+
+
+def quantize(n: int, bits: int, group: int) -> dict:
+    return dict(read=2 * n, write=n * bits // 8 + 4 * (n // group))
+
+
+def reduce_shard(R: int, L: int, bits_in: int, bits_out: int, group: int, n_shards: int) -> dict:
+    return dict(read=n_shards * R * (L * bits_in // 8 + 4 * (L // group)),
+                write=n_shards * (L * bits_out // 8 + 4 * (L // group)))
+
+
+def gather(R: int, L: int, bits: int, group: int, hidden: int, plain: bool, norm: bool, residual: bool,
+           residual_out: bool) -> dict:
+    n = R * L
+    rd = R * (L * bits // 8 + 4 * (L // group))
+    wr = 0
+    if plain:
+        wr += 2 * n
+    if norm:
+        rd += 2 * hidden + (2 * n if residual else 0)
+        wr += 2 * n + (2 * n if residual_out else 0)
+    return dict(read=rd, write=wr)
+
+
+def reduce_rmsnorm(R: int, rows: int, hidden: int, residual: bool, residual_out: bool) -> dict:
+    n = rows * hidden
+    return dict(read=2 * R * n + 2 * hidden + (2 * n if residual else 0),
+                write=2 * n + (2 * n if residual_out else 0))
+
+
+def ll_unpack(R: int, n: int, block_slots: int, completed_blocks: int | None = None) -> dict:
+    """Slots read once per rank (4 B per element: half payload, half epoch word), done flags read, stale
+    flags and done flags written, output written for the blocks completed (all of them by default)."""
+    nblk = n // 2 // block_slots
+    done_b = nblk if completed_blocks is None else completed_blocks
+    return dict(read=R * 4 * n + nblk, write=2 * 2 * block_slots * done_b + R * nblk + done_b)
+
+
+def total(d: dict) -> int:
+    return d["read"] + d["write"]
+
+
+def two_step_whole(R, T, H, bits_rs, bits_ag, group, residual=True, residual_out=True) -> dict:
+    """The whole emulated all-reduce on one GPU: every rank's quantize, every shard's reduce, one gather +
+    epilogue of the result."""
+    n = T * H
+    L = n // R
+    q = quantize(R * n, bits_rs, group)
+    r = reduce_shard(R, L, bits_rs, bits_ag, group, R)
+    g = gather(R, L, bits_ag, group, H, plain=False, norm=True, residual=residual, residual_out=residual_out)
+    return dict(quantize=q, reduce_shard=r, gather_norm=g)

@@ -1,0 +1,178 @@
+// fc_device.h -- device helpers for the gfx950 kernels: number formats, wavefront DPP reductions, and the
+// per-lane group quantizer / dequantizer.  Compiled with -ffp-contract=off: every float expression below
+// is exactly the sequence of IEEE operations written, except where __builtin_fmaf is spelled out.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fc {
+
+// ---- bit casts and formats ------------------------------------------------------------------------
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// bf16 held in the low / high half of a 32-bit word -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return u2f(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return u2f(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair (a in the low half), round to nearest even (native gfx950 conversion).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    f2 v = {a, b};
+    bf2 r = __builtin_convertvector(v, bf2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t f16_rne(float x) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+// Largest fp16 <= v: nearest-even conversion, then one step toward -inf if it landed above v.
+__device__ __forceinline__ uint32_t f16_rd(float v) {
+    uint32_t h = f16_rne(v);
+    if (f16_to_f32(h) > v) h = ((h & 0x7fffu) == 0) ? 0x8001u : ((h & 0x8000u) ? h + 1u : h - 1u);
+    return h;
+}
+// Smallest fp16 >= v.
+__device__ __forceinline__ uint32_t f16_ru(float v) {
+    uint32_t h = f16_rne(v);
+    if (f16_to_f32(h) < v) h = ((h & 0x7fffu) == 0) ? 0x0001u : ((h & 0x8000u) ? h - 1u : h + 1u);
+    return h;
+}
+
+// ---- wavefront reductions -------------------------------------------------------------------------
+// DPP controls (GFX9 encoding): quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror.
+// Applied in this sequence, the first k of them leave every lane of an aligned 2^k-lane group holding
+// the reduction over that group.
+enum : int { DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140 };
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return u2f((uint32_t)__builtin_amdgcn_mov_dpp((int)f2u(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int LANES>
+__device__ __forceinline__ float group_min(float v) {
+    if constexpr (LANES >= 2) v = fminf(v, dpp<DPP_XOR1>(v));
+    if constexpr (LANES >= 4) v = fminf(v, dpp<DPP_XOR2>(v));
+    if constexpr (LANES >= 8) v = fminf(v, dpp<DPP_HALF_MIRROR>(v));
+    if constexpr (LANES >= 16) v = fminf(v, dpp<DPP_MIRROR>(v));
+    static_assert(LANES <= 16, "groups span at most one DPP row");
+    return v;
+}
+template <int LANES>
+__device__ __forceinline__ float group_max(float v) {
+    if constexpr (LANES >= 2) v = fmaxf(v, dpp<DPP_XOR1>(v));
+    if constexpr (LANES >= 4) v = fmaxf(v, dpp<DPP_XOR2>(v));
+    if constexpr (LANES >= 8) v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+    if constexpr (LANES >= 16) v = fmaxf(v, dpp<DPP_MIRROR>(v));
+    return v;
+}
+// Sum over the whole wavefront; every lane gets the same bits (each step adds a commutative pair).
+__device__ __forceinline__ float wave_sum(float v) {
+    v = v + dpp<DPP_XOR1>(v);
+    v = v + dpp<DPP_XOR2>(v);
+    v = v + dpp<DPP_HALF_MIRROR>(v);
+    v = v + dpp<DPP_MIRROR>(v);
+    v = v + __shfl_xor(v, 16, 64);
+    v = v + __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// ---- group quantizer --------------------------------------------------------------------------------
+// One lane holds E consecutive elements of a group that spans LPG aligned consecutive lanes.  Produces
+// the lane's packed codes (E*BITS/32 words) and the group's meta word (scale | zero << 16).
+// Codes: (x - z) * inv rounded to nearest even by adding 1.5*2^23 (exact for 0 <= v < 2^22; here
+// 0 <= v <= qmax*(1+2^-22) because z <= x and s >= (max - z)/qmax up to one rounding); the integer is
+// then read from the low mantissa bits and clamped, which also bounds out-of-contract inputs.
+template <int BITS, int E, int LPG>
+__device__ __forceinline__ void quantize_lane(const float (&v)[E], uint32_t (&w)[E * BITS / 32], uint32_t& meta) {
+    constexpr int QMAX = (1 << BITS) - 1;
+    float lo = v[0], hi = v[0];
+#pragma unroll
+    for (int i = 1; i < E; ++i) {
+        lo = fminf(lo, v[i]);
+        hi = fmaxf(hi, v[i]);
+    }
+    lo = group_min<LPG>(lo);
+    hi = group_max<LPG>(hi);
+    lo = lo + 0.0f;  // -0 -> +0
+    const uint32_t zb = f16_rd(lo);
+    const float z = f16_to_f32(zb);
+    const float diff = hi - z;
+    uint32_t sb = 0;
+    float inv = 0.0f;
+    if (diff != 0.0f) {
+        const float t = diff / (float)QMAX;
+        sb = f16_ru(t);
+        inv = 1.0f / f16_to_f32(sb);
+    }
+    meta = sb | (zb << 16);
+    constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
+    constexpr uint32_t MAGIC_BITS = 0x4B400000u;
+    uint32_t c[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        const float d = v[i] - z;
+        const float q = d * inv;
+        const uint32_t m = f2u(q + MAGIC);
+        c[i] = min(m - MAGIC_BITS, (uint32_t)QMAX);
+    }
+#pragma unroll
+    for (int k = 0; k < E * BITS / 32; ++k) {
+        if constexpr (BITS == 8) {
+            w[k] = c[4 * k] | (c[4 * k + 1] << 8) | (c[4 * k + 2] << 16) | (c[4 * k + 3] << 24);
+        } else {
+            uint32_t x = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x |= c[8 * k + j] << (4 * j);
+            w[k] = x;
+        }
+    }
+}
+
+// ---- dequantization of one packed code word -------------------------------------------------------
+// fl(q*s + z): q*s is exact (at most 8 x 11 significant bits), so one fused multiply-add gives the same
+// bits as the two separate operations.
+template <int BITS>
+struct Unpack;
+
+template <>
+struct Unpack<8> {
+    static constexpr int PER_WORD = 4;
+    __device__ __forceinline__ static void run(uint32_t w, float s, float z, float* out) {
+        out[0] = __builtin_fmaf((float)(w & 0xffu), s, z);
+        out[1] = __builtin_fmaf((float)((w >> 8) & 0xffu), s, z);
+        out[2] = __builtin_fmaf((float)((w >> 16) & 0xffu), s, z);
+        out[3] = __builtin_fmaf((float)(w >> 24), s, z);
+    }
+};
+
+template <>
+struct Unpack<4> {
+    static constexpr int PER_WORD = 8;
+    __device__ __forceinline__ static void run(uint32_t w, float s, float z, float* out) {
+        const uint32_t ev = w & 0x0f0f0f0fu;         // byte k = code 2k
+        const uint32_t od = (w >> 4) & 0x0f0f0f0fu;  // byte k = code 2k+1
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            out[2 * k] = __builtin_fmaf((float)((ev >> (8 * k)) & 0xffu), s, z);
+            out[2 * k + 1] = __builtin_fmaf((float)((od >> (8 * k)) & 0xffu), s, z);
+        }
+    }
+};
+
+__device__ __forceinline__ float meta_scale(uint32_t m) { return f16_to_f32(m & 0xffffu); }
+__device__ __forceinline__ float meta_zero(uint32_t m) { return f16_to_f32(m >> 16); }
+
+// 16-byte global memory access
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+__device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ void st8(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
+
+}  // namespace fc

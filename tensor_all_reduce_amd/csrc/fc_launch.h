@@ -1,0 +1,88 @@
+// fc_launch.h -- launch parameters passed from the validating C-ABI layer to the kernel launchers.
+// Internal to libfc.so.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace fc {
+
+constexpr int kMaxRanks = 16;
+constexpr int kMaxReduceIn = 128;  // (shard, rank) message pointers per reduce launch (kernel-argument table)
+
+struct QuantizeParams {
+    const uint16_t* x;
+    int64_t n;
+    int bits, group;
+    uint8_t* codes;
+    uint32_t* meta;
+};
+
+struct ReduceParams {
+    const uint8_t* in_codes[kMaxReduceIn];  // [shard * R + rank]
+    const uint32_t* in_meta[kMaxReduceIn];
+    uint8_t* out_codes[kMaxRanks];          // [shard]
+    uint32_t* out_meta[kMaxRanks];
+    int R, n_shards;
+    int64_t L;
+    int bits_in, bits_out, group;
+};
+
+struct NormParams {
+    const uint16_t* residual;
+    const uint16_t* gamma;
+    float eps;
+    int64_t hidden;
+    uint16_t* out;
+    uint16_t* residual_out;
+};
+
+struct GatherParams {
+    const uint8_t* codes[kMaxRanks];  // [shard]
+    const uint32_t* meta[kMaxRanks];
+    int R;
+    int64_t L;
+    int bits, group;
+    uint16_t* y;     // plain output or nullptr
+    bool has_norm;
+    NormParams norm;
+};
+
+struct ReduceNormParams {
+    const uint16_t* parts[kMaxRanks];
+    int R;
+    int64_t rows;
+    NormParams norm;
+    int max_workgroups;
+};
+
+struct LLParams {
+    const uint64_t* slots[kMaxRanks];
+    int R;
+    int64_t n;
+    int block_slots;
+    uint32_t epoch;
+    uint16_t* out;
+    uint8_t* stale;
+    uint8_t* done;
+    uint32_t* counters;
+};
+
+struct PackParams {
+    const uint16_t* x;
+    int64_t n;
+    int block_slots;
+    uint32_t epoch;
+    const int32_t* order;
+    uint64_t* slots;
+};
+
+hipError_t launch_quantize(const QuantizeParams& p, hipStream_t s);
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
+hipError_t launch_gather(const GatherParams& p, hipStream_t s);
+hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t s);
+hipError_t launch_ll_unpack(const LLParams& p, hipStream_t s);
+hipError_t launch_ll_pack(const PackParams& p, hipStream_t s);
+hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+
+}  // namespace fc

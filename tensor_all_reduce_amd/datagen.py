@@ -156,3 +156,57 @@ def stale_epochs(cfg: Config, rank: int, nslots: int, epoch: int | None = None,
         else:  # torn: one slot of the block not yet written
             ep[b * B + int(rv.integers(0, B))] = (e - 1) & M
     return ep, stale
+
+
+def _seed_words(seed) -> list[int]:
+    """Flatten an int or a nested tuple of ints into seed words."""
+    if isinstance(seed, (tuple, list)):
+        out = []
+        for s in seed:
+            out += _seed_words(s)
+        return out
+    return [int(seed)]
+
+
+def synth_bf16(seed, n: int, sigma: float = 1.0, outlier_p: float = 0.0, outlier_factor: float = 1.0) -> np.ndarray:
+    """Seeded bf16 bits of an arbitrary test shape, same recipe as `partial` (seed: int or tuple of ints)."""
+    rng = np.random.default_rng(np.random.SeedSequence([0xFC, 0xEE] + _seed_words(seed)))
+    v = rng.standard_normal(n, dtype=np.float32) * np.float32(sigma)
+    if outlier_p > 0:
+        m = rng.random(n, dtype=np.float32) < outlier_p
+        v[m] *= np.float32(outlier_factor)
+    return f32_to_bf16_bits(v)
+
+
+def synth_f32(seed, n: int, sigma: float = 1.0) -> np.ndarray:
+    """Seeded fp32 values (stand-ins for fp32 partial sums, e.g. requantization inputs)."""
+    rng = np.random.default_rng(np.random.SeedSequence([0xFC, 0xEF] + _seed_words(seed)))
+    return rng.standard_normal(n, dtype=np.float32) * np.float32(sigma)
+
+
+def adversarial_groups(group: int, seed: int = 0) -> np.ndarray:
+    """bf16 bits of groups built to hit the quantizer's edge cases: constant groups, signed zeros, fp16
+    subnormal-range values (zero-point not an fp16 value), values at the top of the fp16 range, exact
+    half-step ties on a power-of-two grid, one huge outlier among tiny values, all-negative groups."""
+    rng = np.random.default_rng(np.random.SeedSequence([0xFC, 0xAD, seed]))
+    G = group
+    gs = []
+    gs.append(np.full(G, 1.5, np.float32))
+    gs.append(np.full(G, -0.0, np.float32))
+    z = np.zeros(G, np.float32)
+    z[::2] = -0.0
+    gs.append(z)
+    gs.append((rng.standard_normal(G) * 3e-6).astype(np.float32))
+    gs.append(np.full(G, 9.6112489700317383e-07, np.float32))
+    top = rng.choice([-65280.0, 65280.0, 32768.0, -1.0], size=G).astype(np.float32)
+    gs.append(top)
+    k = rng.integers(0, 16, size=G).astype(np.float32)
+    tie = k + 0.5
+    tie[0], tie[1] = 0.0, 15.0
+    gs.append(tie.astype(np.float32))
+    o = (rng.standard_normal(G) * 1e-3).astype(np.float32)
+    o[G // 3] = 6.0e4
+    gs.append(o)
+    gs.append(-np.abs(rng.standard_normal(G)).astype(np.float32) - 2.0)
+    gs.append(np.linspace(-1, 1, G).astype(np.float32))
+    return f32_to_bf16_bits(np.concatenate(gs))

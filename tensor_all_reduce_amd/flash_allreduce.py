@@ -1,0 +1,133 @@
+"""Host-side orchestration of one GPU's share of the flash all-reduce: buffers and call sequences.
+
+PyTorch supplies device memory and the stream; every step runs in libfc.so's kernels.  The argument
+tables (message pointers per shard and rank) are built once per buffer set, so enqueueing a step costs
+a few ctypes calls and can be captured in a HIP graph.
+
+Emulation on one GPU: the R ranks' partial sums are R buffers in local HBM, and the "transport" of each
+step is the message buffer one call writes and the next call reads.  Ranks exchange data only through
+those buffers.
+
+Two-step layout (Flash Communication, summary "Core ideas of the solution"): rank r's message holds
+the whole [T*H] partial, quantized; shard s is elements [s*L, (s+1)*L) with L = T*H/R, so rank r's chunk
+of shard s sits at a fixed offset inside rank r's message.  After the reduce-scatter, shard s's
+requantized message (the all-gather payload) sits at offset s inside one contiguous buffer.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from . import _lib
+
+u8, i16, i32, i64 = torch.uint8, torch.int16, torch.int32, torch.int64
+
+
+def bf16_buffer(n: int, device) -> torch.Tensor:
+    """bf16 bit patterns are held in int16 tensors (the kernels see raw 16-bit words)."""
+    return torch.empty(n, dtype=i16, device=device)
+
+
+class TwoStepAllReduce:
+    """Buffers and enqueue functions for the quantized two-step all-reduce of R emulated ranks.
+
+    parts: int16 [R, T*H] (bf16 bits), filled by the caller.  Steps: quantize (all ranks, one launch),
+    reduce_scatter (all shards, or one shard = one GPU's real share), all_gather (dequantize every
+    shard, optionally with the residual-add + RMSNorm epilogue)."""
+
+    def __init__(self, R: int, T: int, H: int, bits_rs: int, bits_ag: int, group: int, device="cuda",
+                 parts: torch.Tensor | None = None):
+        self.R, self.T, self.H, self.b1, self.b2, self.G = R, T, H, bits_rs, bits_ag, group
+        n = T * H
+        assert n % R == 0, "T*H must split into R shards"
+        self.n, self.L = n, n // R
+        L = self.L
+        dev = torch.device(device)
+        self.parts = parts if parts is not None else torch.empty(R, n, dtype=i16, device=dev)
+        self.codes1 = torch.empty(R, n * bits_rs // 8, dtype=u8, device=dev)
+        self.meta1 = torch.empty(R, n // group, dtype=i32, device=dev)
+        self.codes2 = torch.empty(n * bits_ag // 8, dtype=u8, device=dev)
+        self.meta2 = torch.empty(n // group, dtype=i32, device=dev)
+        cb1, mb1 = L * bits_rs // 8, L // group
+        cb2 = L * bits_ag // 8
+        # (shard, rank) -> rank's chunk of the shard inside rank's message
+        self._rs_in = (_lib.QMsg * (R * R))(*[
+            _lib.QMsg(self.codes1[r].data_ptr() + s * cb1, self.meta1[r].data_ptr() + 4 * s * mb1)
+            for s in range(R) for r in range(R)])
+        self._rs_out = (_lib.QMsg * R)(*[
+            _lib.QMsg(self.codes2.data_ptr() + s * cb2, self.meta2.data_ptr() + 4 * s * mb1) for s in range(R)])
+        self._ag_in = self._rs_out
+        self._q = _lib.QMsg(self.codes1.data_ptr(), self.meta1.data_ptr())
+
+    # -- messages of one shard (views), e.g. to upload or inspect one GPU's share
+    def rank_chunk(self, r: int, s: int):
+        cb1, mb1 = self.L * self.b1 // 8, self.L // self.G
+        return self.codes1[r, s * cb1:(s + 1) * cb1], self.meta1[r, s * mb1:(s + 1) * mb1]
+
+    def shard_msg(self, s: int):
+        cb2, mb = self.L * self.b2 // 8, self.L // self.G
+        return self.codes2[s * cb2:(s + 1) * cb2], self.meta2[s * mb:(s + 1) * mb]
+
+    # -- steps
+    def quantize(self, stream=None):
+        st = _lib.lib.fc_quantize(self.parts.data_ptr(), self.R * self.n, self.b1, self.G, self._q,
+                                  _lib._stream(stream))
+        _lib._check(st, "fc_quantize")
+
+    def reduce_scatter(self, shard: int | None = None, stream=None):
+        """All shards in one launch (shard=None), or only `shard` (one GPU's real share)."""
+        R = self.R
+        if shard is None:
+            ins, outs, ns = self._rs_in, self._rs_out, R
+        else:
+            qs = C.sizeof(_lib.QMsg)
+            ins = C.cast(C.addressof(self._rs_in) + qs * shard * R, C.POINTER(_lib.QMsg))
+            outs = C.cast(C.addressof(self._rs_out) + qs * shard, C.POINTER(_lib.QMsg))
+            ns = 1
+        st = _lib.lib.fc_reduce_shard(ins, R, self.L, ns, self.b1, self.b2, self.G, outs, _lib._stream(stream))
+        _lib._check(st, "fc_reduce_shard")
+
+    def make_norm(self, gamma, out, residual=None, residual_out=None, eps: float = 1e-5) -> _lib.Norm:
+        return _lib.Norm(residual.data_ptr() if residual is not None else None, gamma.data_ptr(), float(eps), self.H,
+                         out.data_ptr(), residual_out.data_ptr() if residual_out is not None else None)
+
+    def all_gather(self, y=None, norm: _lib.Norm | None = None, stream=None):
+        st = _lib.lib.fc_gather_dequant(self._ag_in, self.R, self.L, self.b2, self.G,
+                                        y.data_ptr() if y is not None else None,
+                                        C.byref(norm) if norm is not None else None, _lib._stream(stream))
+        _lib._check(st, "fc_gather_dequant")
+
+    def run(self, y=None, norm=None, stream=None):
+        self.quantize(stream)
+        self.reduce_scatter(None, stream)
+        self.all_gather(y, norm, stream)
+
+
+class ReduceRMSNorm:
+    """Unquantized fused reduce + residual-add + RMSNorm over R bf16 partials [rows, H] (TokenWeave)."""
+
+    def __init__(self, parts: list, rows: int, H: int, gamma, out, residual=None, residual_out=None, eps=1e-5):
+        self.R, self.rows, self.H = len(parts), rows, H
+        self._parts = (C.c_void_p * self.R)(*[p.data_ptr() for p in parts])
+        self.norm = _lib.Norm(residual.data_ptr() if residual is not None else None, gamma.data_ptr(), float(eps), H,
+                              out.data_ptr(), residual_out.data_ptr() if residual_out is not None else None)
+
+    def run(self, max_workgroups: int = 0, stream=None):
+        st = _lib.lib.fc_reduce_rmsnorm(self._parts, self.R, self.rows, C.byref(self.norm), max_workgroups,
+                                        _lib._stream(stream))
+        _lib._check(st, "fc_reduce_rmsnorm")
+
+
+class LLUnpackReduce:
+    """Receiver of R ranks' epoch-tagged slot buffers (flash-comm self-synchronizing blocks)."""
+
+    def __init__(self, slots: list, n: int, block_slots: int, out, stale, done, counters):
+        self.R, self.n, self.B = len(slots), n, block_slots
+        self._slots = (C.c_void_p * self.R)(*[s.data_ptr() for s in slots])
+        self._ptrs = (out.data_ptr(), stale.data_ptr(), done.data_ptr(), counters.data_ptr())
+
+    def run(self, epoch: int, stream=None):
+        st = _lib.lib.fc_ll_unpack_reduce(self._slots, self.R, self.n, self.B, epoch & 0xFFFFFFFF, *self._ptrs,
+                                          _lib._stream(stream))
+        _lib._check(st, "fc_ll_unpack_reduce")

@@ -1,0 +1,167 @@
+"""CPU tests of the C ABI boundary: libfc.so loads, exports every function include/fc.h declares, shares
+PyTorch's HIP runtime, and rejects invalid arguments on the host before any HIP call (so these run
+without a GPU; the device addresses used here are never dereferenced)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fc.h")
+
+A = 1 << 20  # a fake, 16-byte aligned "device address" base; never dereferenced by validation
+
+
+@pytest.fixture(scope="module")
+def L():
+    from tensor_all_reduce_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert {"fc_quantize", "fc_reduce_shard", "fc_gather_dequant", "fc_reduce_rmsnorm", "fc_ll_unpack_reduce",
+            "fc_ll_pack", "fc_copy", "fc_status_string", "fc_last_hip_error", "fc_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(L.lib, n), n
+    assert L.fc_abi_version() == 1
+
+
+def test_single_hip_runtime(L):
+    assert len(L._hip_runtimes_mapped()) <= 1
+
+
+def test_status_strings(L):
+    for s in range(6):
+        assert L.lib.fc_status_string(s).startswith(b"FC_")
+
+
+def q(codes, meta):
+    from tensor_all_reduce_amd._lib import QMsg
+    return QMsg(codes, meta)
+
+
+def test_quantize_validation(L):
+    f = L.lib.fc_quantize
+    ok = q(A + 0x100000, A + 0x200000)
+    assert f(A, 1024, 5, 32, ok, None) == L.FC_E_ARG          # bits
+    assert f(A, 1024, 8, 48, ok, None) == L.FC_E_ARG          # group
+    assert f(A, -32, 8, 32, ok, None) == L.FC_E_ARG
+    assert f(A, 1000, 8, 32, ok, None) == L.FC_E_SHAPE        # ragged group
+    assert f(A, 0, 8, 32, ok, None) == L.FC_OK                # empty: nothing to do, no launch
+    assert f(None, 1024, 8, 32, ok, None) == L.FC_E_NULL
+    assert f(A, 1024, 8, 32, q(None, A), None) == L.FC_E_NULL
+    assert f(A + 2, 1024, 8, 32, ok, None) == L.FC_E_ALIGN
+    assert f(A, 1024, 8, 32, q(A + 0x100008, A + 0x200000), None) == L.FC_E_ALIGN
+    assert f(A, 1024, 8, 32, q(A + 0x100000, A + 0x200002), None) == L.FC_E_ALIGN
+    assert f(A, 1024, 8, 32, q(A + 1024, A + 0x200000), None) == L.FC_E_ARG   # codes overlap x
+    assert f(A, 1024, 8, 32, q(A + 0x100000, A + 0x100000 + 512), None) == L.FC_E_ARG  # meta overlaps codes
+
+
+def test_reduce_shard_validation(L):
+    f = L.lib.fc_reduce_shard
+    QA = L.QMsg * 4
+    ins = QA(*[q(A + 0x10000 * i, A + 0x400000 + 0x1000 * i) for i in range(4)])
+    outs = (L.QMsg * 2)(q(A + 0x800000, A + 0x900000), q(A + 0x810000, A + 0x910000))
+    assert f(ins, 0, 1024, 2, 8, 8, 32, outs, None) == L.FC_E_ARG
+    assert f(ins, 17, 1024, 2, 8, 8, 32, outs, None) == L.FC_E_ARG
+    assert f(ins, 2, 1024, 2, 3, 8, 32, outs, None) == L.FC_E_ARG
+    assert f(ins, 2, 1024, 2, 8, 8, 100, outs, None) == L.FC_E_ARG
+    assert f(ins, 2, 1000, 2, 8, 8, 32, outs, None) == L.FC_E_SHAPE
+    assert f(ins, 2, 0, 2, 8, 8, 32, outs, None) == L.FC_OK
+    assert f(None, 2, 1024, 2, 8, 8, 32, outs, None) == L.FC_E_NULL
+    bad = QA(*[q(A + 0x10000 * i + (8 if i == 3 else 0), A + 0x400000 + 0x1000 * i) for i in range(4)])
+    assert f(bad, 2, 1024, 2, 8, 8, 32, outs, None) == L.FC_E_ALIGN
+    alias = (L.QMsg * 2)(q(A + 0x10000, A + 0x900000), q(A + 0x810000, A + 0x910000))  # output = an input
+    assert f(ins, 2, 1024, 2, 8, 8, 32, alias, None) == L.FC_E_ARG
+    twin = (L.QMsg * 2)(q(A + 0x800000, A + 0x900000), q(A + 0x800000, A + 0x910000))  # two shards, one buffer
+    assert f(ins, 2, 1024, 2, 8, 8, 32, twin, None) == L.FC_E_ARG
+
+
+def norm(L, **kw):
+    d = dict(residual=A + 0x100000, gamma=A + 0x200000, eps=1e-5, hidden=256, out=A + 0x300000,
+             residual_out=A + 0x400000)
+    d.update(kw)
+    return L.Norm(d["residual"], d["gamma"], d["eps"], d["hidden"], d["out"], d["residual_out"])
+
+
+def test_gather_validation(L):
+    f = L.lib.fc_gather_dequant
+    sh = (L.QMsg * 2)(q(A + 0x800000, A + 0x900000), q(A + 0x810000, A + 0x910000))
+    assert f(sh, 2, 512, 8, 32, None, None, None) == L.FC_E_NULL          # neither output
+    assert f(sh, 2, 500, 8, 32, A, None, None) == L.FC_E_SHAPE
+    assert f(sh, 2, 512, 8, 32, A + 8, None, None) == L.FC_E_ALIGN
+    assert f(sh, 2, 512, 8, 32, A + 0x800000 - 64, None, None) == L.FC_E_ARG  # y overlaps shard codes
+    n = norm(L, hidden=200)
+    assert f(sh, 2, 512, 8, 32, None, C.byref(n), None) == L.FC_E_SHAPE   # hidden % 16
+    n = norm(L, hidden=96)
+    assert f(sh, 2, 512, 8, 32, None, C.byref(n), None) == L.FC_E_SHAPE   # n % hidden
+    n = norm(L, eps=0.0)
+    assert f(sh, 2, 512, 8, 32, None, C.byref(n), None) == L.FC_E_ARG
+    n = norm(L, eps=float("nan"))
+    assert f(sh, 2, 512, 8, 32, None, C.byref(n), None) == L.FC_E_ARG
+    n = norm(L, gamma=None)
+    assert f(sh, 2, 512, 8, 32, None, C.byref(n), None) == L.FC_E_NULL
+    n = norm(L, residual_out=A + 0x300000 + 512)   # overlaps out
+    assert f(sh, 2, 512, 8, 32, None, C.byref(n), None) == L.FC_E_ARG
+    n = norm(L, residual_out=A + 0x100000 + 16)    # partially overlaps residual
+    assert f(sh, 2, 512, 8, 32, None, C.byref(n), None) == L.FC_E_ARG
+    n = norm(L, out=A + 0x300002)
+    assert f(sh, 2, 512, 8, 32, None, C.byref(n), None) == L.FC_E_ALIGN
+    n = norm(L)
+    assert f(sh, 0, 512, 8, 32, None, C.byref(n), None) == L.FC_E_ARG
+    assert f(sh, 2, 0, 8, 32, None, C.byref(n), None) == L.FC_OK
+
+
+def test_reduce_rmsnorm_validation(L):
+    f = L.lib.fc_reduce_rmsnorm
+    parts = (C.c_void_p * 2)(A + 0x1000000, A + 0x2000000)
+    n = norm(L)
+    assert f(parts, 2, 4, None, 0, None) == L.FC_E_NULL
+    assert f(parts, 2, 4, C.byref(n), -1, None) == L.FC_E_ARG
+    assert f(parts, 0, 4, C.byref(n), 0, None) == L.FC_E_ARG
+    assert f(parts, 2, 0, C.byref(n), 0, None) == L.FC_OK
+    n2 = norm(L, hidden=131072)
+    assert f(parts, 2, 4, C.byref(n2), 0, None) == L.FC_E_SHAPE
+    bad = (C.c_void_p * 2)(A + 0x1000000, A + 0x2000004)
+    assert f(bad, 2, 4, C.byref(n), 0, None) == L.FC_E_ALIGN
+    over = (C.c_void_p * 2)(A + 0x1000000, A + 0x300000)   # a partial is the output
+    assert f(over, 2, 4, C.byref(n), 0, None) == L.FC_E_ARG
+    nul = (C.c_void_p * 2)(A + 0x1000000, None)
+    assert f(nul, 2, 4, C.byref(n), 0, None) == L.FC_E_NULL
+
+
+def test_ll_validation(L):
+    f = L.lib.fc_ll_unpack_reduce
+    sl = (C.c_void_p * 2)(A + 0x1000000, A + 0x2000000)
+    args = dict(out=A + 0x3000000, stale=A + 0x4000000, done=A + 0x5000000, cnt=A + 0x6000000)
+    g = lambda R=2, n=4096, B=64, **kw: f(sl, R, n, B, 7, kw.get("out", args["out"]), kw.get("stale", args["stale"]),
+                                          kw.get("done", args["done"]), kw.get("cnt", args["cnt"]), None)
+    assert g(B=48) == L.FC_E_ARG
+    assert g(n=4096 + 64) == L.FC_E_SHAPE
+    assert g(n=0) == L.FC_OK
+    assert g(out=None) == L.FC_E_NULL
+    assert g(out=A + 0x3000008) == L.FC_E_ALIGN
+    assert g(cnt=A + 0x6000002) == L.FC_E_ALIGN
+    assert g(done=A + 0x4000000 + 8) == L.FC_E_ARG   # done inside the stale flags
+    assert g(out=A + 0x1000000 + 64) == L.FC_E_ARG   # out inside rank 0's slots
+    p = L.lib.fc_ll_pack
+    assert p(A, 4096, 60, 7, None, A + 0x1000000, None) == L.FC_E_ARG
+    assert p(A, 4000, 64, 7, None, A + 0x1000000, None) == L.FC_E_SHAPE
+    assert p(A, 4096, 64, 7, None, A + 8, None) == L.FC_E_ALIGN
+    assert p(A, 4096, 64, 7, None, A + 1024, None) == L.FC_E_ARG
+
+
+def test_copy_validation(L):
+    f = L.lib.fc_copy
+    assert f(A, A + 0x100000, 100, None) == L.FC_E_SHAPE
+    assert f(A, A + 64, 1024, None) == L.FC_E_ARG
+    assert f(A, A + 0x100000, 0, None) == L.FC_OK
+    assert f(None, A, 1024, None) == L.FC_E_NULL

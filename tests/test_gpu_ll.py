@@ -1,0 +1,178 @@
+"""GPU parity of the self-synchronizing slots (fc_ll_pack, fc_ll_unpack_reduce; flash-comm) against the
+CPU oracle: stale flags, done flags, counters and outputs bit-exact, on the 8-rank workload with its
+seeded stale mix and shuffled write order, on every kind of wrong epoch word, and across a retry."""
+import numpy as np
+import pytest
+
+from tensor_all_reduce_amd import datagen as dg
+
+pytestmark = pytest.mark.gpu
+M32 = 0xFFFFFFFF
+
+
+@pytest.fixture(scope="module")
+def fc():
+    from tensor_all_reduce_amd import _lib
+    return _lib
+
+
+def set_epochs_host(slots, ep):
+    s = slots.copy()
+    s &= np.uint64(0xFFFFFFFF)
+    s |= ep.astype(np.uint64) << np.uint64(32)
+    return s
+
+
+def inject_gpu(slots_d, ep):
+    """Harness: overwrite the epoch words of a device slot buffer (emulates blocks that have not arrived)."""
+    import torch
+    v = slots_d.view(torch.int32).view(-1, 2)
+    v[:, 1] = torch.from_numpy(ep.view(np.int32)).to(slots_d.device)
+
+
+class GpuLL:
+    def __init__(self, R, n, B):
+        import torch
+        self.R, self.n, self.B = R, n, B
+        self.nblk = n // 2 // B
+        self.out = torch.zeros(n, dtype=torch.int16, device="cuda")
+        self.stale = torch.full((R * self.nblk,), 0xAB, dtype=torch.uint8, device="cuda")
+        self.done = torch.zeros(self.nblk, dtype=torch.uint8, device="cuda")
+        self.cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
+
+    def run(self, fc, slots_d, epoch):
+        self.cnt.zero_()
+        fc.fc_ll_unpack_reduce(slots_d, self.n, self.B, epoch, self.out, self.stale, self.done, self.cnt)
+        from gpu_helpers import down
+        return (down(self.out, np.uint16), down(self.stale, np.uint8).reshape(self.R, self.nblk),
+                down(self.done, np.uint8), down(self.cnt, np.uint32))
+
+
+@pytest.mark.parametrize("B", [32, 64, 128, 256])
+def test_pack_matches_oracle(fc, orc, B):
+    import torch
+    from gpu_helpers import assert_equal_bits, down, up
+    n = 2 * B * 77
+    x = dg.synth_bf16((B,), n)
+    order = np.random.default_rng(B).permutation(n // 2 // B).astype(np.int32)
+    for o in (None, order):
+        slots = torch.empty(n // 2, dtype=torch.int64, device="cuda")
+        fc.fc_ll_pack(up(x), B, 0xC0FFEE, slots, block_order=up(o) if o is not None else None)
+        assert_equal_bits(down(slots, np.uint64), orc.ll_pack(x, B, 0xC0FFEE, order=o), "slots")
+
+
+def test_workload_stale_mix_and_retry(fc, orc):
+    """8 ranks x [128, 8192]: blocks written in a seeded order per rank, 2% of (rank, block) copies stale
+    (mostly the previous epoch; also zero, next, inverted, top bit, random words and torn blocks).
+    Pass 1 flags exactly the injected pairs and completes the rest; after the late blocks arrive a second
+    pass completes every pending block with the same bits as an all-on-time run."""
+    from gpu_helpers import assert_equal_bits, up
+    import torch
+    cfg = dg.CONFIGS[4]
+    R, n, B, e = cfg.R, cfg.n, cfg.block_slots, cfg.epoch
+    nslots, nblk = n // 2, n // 2 // B
+    xs = [dg.partial(cfg, r) for r in range(R)]
+    orders = [dg.write_order(cfg, r, nblk) for r in range(R)]
+    eps, masks = zip(*[dg.stale_epochs(cfg, r, nslots) for r in range(R)])
+    inj = np.stack(masks)
+    # device: pack (sender emulation), then mark the late blocks
+    slots_d = []
+    for r in range(R):
+        s = torch.empty(nslots, dtype=torch.int64, device="cuda")
+        fc.fc_ll_pack(up(xs[r]), B, e, s, block_order=up(orders[r]))
+        slots_d.append(s)
+    for r in range(R):
+        inject_gpu(slots_d[r], eps[r])
+    g = GpuLL(R, n, B)
+    out1, st1, dn1, c1 = g.run(fc, slots_d, e)
+    # oracle, from the same bf16 inputs
+    good = [orc.ll_pack(xs[r], B, e, order=orders[r]) for r in range(R)]
+    late = [set_epochs_host(good[r], eps[r]) for r in range(R)]
+    ro, rst, rdn, rc = orc.ll_unpack_reduce(late, n, B, e)
+    assert_equal_bits(st1, rst, "stale flags")
+    assert_equal_bits(st1, inj, "stale flags == injected")
+    assert_equal_bits(dn1, rdn, "done")
+    assert_equal_bits(c1, rc, "counters")
+    assert c1[1] > 0.10 * nblk  # about 1 - 0.98^8 of the blocks are pending
+    assert_equal_bits(out1[np.repeat(rdn.astype(bool), 2 * B)], ro[np.repeat(rdn.astype(bool), 2 * B)], "out (done)")
+    assert np.all(out1[np.repeat(~rdn.astype(bool), 2 * B)] == 0), "pending blocks must stay untouched"
+    # retry after the late blocks arrive
+    for r in range(R):
+        inject_gpu(slots_d[r], np.full(nslots, e, np.uint32))
+    out2, st2, dn2, c2 = g.run(fc, slots_d, e)
+    ro2, _, rdn2, rc2 = orc.ll_unpack_reduce(good, n, B, e, out=ro.copy(), done=rdn.copy())
+    full, _, _, _ = orc.ll_unpack_reduce(good, n, B, e)
+    assert dn2.all() and list(c2) == [0, 0] and list(rc2) == [0, 0]
+    assert_equal_bits(out2, full, "retry == all on time")
+    assert_equal_bits(out2, ro2, "retry == oracle retry")
+
+
+STALE_WORDS = {
+    "prev": lambda e: (e - 1) & M32, "next": lambda e: (e + 1) & M32, "zero": lambda e: 0 if e else 1,
+    "not": lambda e: (~e) & M32, "msb": lambda e: e ^ 0x80000000, "lowbit": lambda e: e ^ 1,
+}
+
+
+@pytest.mark.parametrize("e", [0, 0x2A, 0xFFFFFFFF])
+@pytest.mark.parametrize("kind", sorted(STALE_WORDS) + ["torn", "rank"])
+@pytest.mark.parametrize("B", [32, 256])
+def test_every_stale_word(fc, orc, e, kind, B):
+    import torch
+    from gpu_helpers import assert_equal_bits, up
+    R, nblk = 3, 40
+    n = 2 * B * nblk
+    xs = [dg.synth_bf16((B, r, 4), n) for r in range(R)]
+    eps = [np.full(n // 2, e, np.uint32) for _ in range(R)]
+    rng = np.random.default_rng(B)
+    if kind == "rank":
+        eps[1][:] = (e - 1) & M32
+    else:
+        for b in rng.choice(nblk, 5, replace=False):
+            r = int(rng.integers(0, R))
+            if kind == "torn":
+                eps[r][b * B + int(rng.integers(0, B))] = (e - 1) & M32
+            else:
+                eps[r][b * B:(b + 1) * B] = STALE_WORDS[kind](e)
+    slots_d = []
+    for r in range(R):
+        s = torch.empty(n // 2, dtype=torch.int64, device="cuda")
+        fc.fc_ll_pack(up(xs[r]), B, e, s)
+        inject_gpu(s, eps[r])
+        slots_d.append(s)
+    g = GpuLL(R, n, B)
+    out, st, dn, c = g.run(fc, slots_d, e)
+    late = [set_epochs_host(orc.ll_pack(xs[r], B, e), eps[r]) for r in range(R)]
+    ro, rst, rdn, rc = orc.ll_unpack_reduce(late, n, B, e)
+    assert_equal_bits(st, rst, "stale")
+    assert_equal_bits(dn, rdn, "done")
+    assert_equal_bits(c, rc, "counters")
+    assert_equal_bits(out, ro, "out")
+
+
+@pytest.mark.parametrize("R", [1, 2, 16])
+def test_rank_counts_and_done_skip(fc, orc, R):
+    """R from 1 to 16; blocks already done are skipped (flags and outputs untouched, nothing counted)."""
+    import torch
+    from gpu_helpers import assert_equal_bits, down, up
+    B, nblk, e = 64, 33, 5
+    n = 2 * B * nblk
+    xs = [dg.synth_bf16((R, r, 6), n) for r in range(R)]
+    slots_d = []
+    for r in range(R):
+        s = torch.empty(n // 2, dtype=torch.int64, device="cuda")
+        fc.fc_ll_pack(up(xs[r]), B, e - 1, s)   # nothing has arrived: every copy stale
+        slots_d.append(s)
+    g = GpuLL(R, n, B)
+    done0 = (np.arange(nblk) % 3 == 0).astype(np.uint8)
+    g.done.copy_(torch.from_numpy(done0))
+    g.out.fill_(77)
+    out, st, dn, c = g.run(fc, slots_d, e)
+    ro, rst, rdn, rc = orc.ll_unpack_reduce([orc.ll_pack(x, B, e - 1) for x in xs], n, B, e,
+                                            out=np.full(n, 77, np.uint16), done=done0.copy())
+    assert_equal_bits(dn, rdn, "done")
+    assert_equal_bits(c, rc, "counters")
+    assert_equal_bits(out, ro, "out")
+    # flags: examined blocks per the oracle; skipped blocks keep the sentinel the buffer started with
+    skipped = done0.astype(bool)
+    assert np.all(st[:, skipped] == 0xAB)
+    assert_equal_bits(st[:, ~skipped], rst[:, ~skipped], "stale (examined)")
