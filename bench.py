@@ -1,20 +1,30 @@
 #!/usr/bin/env python
-"""Benchmark of one MI355X's share of the flash all-reduce (quantize -> reduce-scatter -> all-gather
-dequantize + residual-add + RMSNorm), on synthetic inputs already resident in HBM.
+"""Benchmark of one MI355X's share of the flash all-reduce, on synthetic inputs already resident in HBM.
 
-A step is the whole emulated all-reduce of one batch on one GPU: all R ranks' group quantization (one
-launch), all R shards' fixed-order dequant-reduce-requant (one launch), and the all-gather dequantize
-with the fused RMSNorm epilogue (one launch).  Steps are replayed from a HIP graph; each step uses its
-own buffer set, and the sets together exceed twice the 256 MB last-level cache, so every step reads
-from HBM ("cold").  value = algorithmic bytes per step / time per step.
+Headline step (`value`): the whole emulated quantized all-reduce of the Llama-3-8B decode workload (8
+ranks x [64, 4096] bf16, int8 groups of 128) on one GPU: every rank's group quantization (one launch),
+every shard's fixed-order dequant-reduce-requant (one launch) and the all-gather dequantize with the
+fused residual-add + RMSNorm epilogue (one launch).  Steps are replayed from a HIP graph, each on its own
+buffer set; the sets together exceed twice the 256 MB last-level cache, so inputs come from HBM.
+value = algorithmic bytes per step / time per step (GB/s).
+
+The other hot-path rows are measured at their own workloads and reported under "rows": the 70B prefill
+two-step path (int4 reduce-scatter / int8 all-gather), the self-synchronizing slot receiver (first pass
+with late blocks, then the retry), and the unquantized reduce-RMSNorm on two wave-aware half batches,
+alone and overlapped with a bf16 GEMM on a second stream, with a workgroup-cap sweep.
 
 Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+`python bench.py --pmc-summary FETCH_CSV WRITE_CSV OUT` turns two rocprofv3 --pmc runs into the traffic
+summary that later runs report (see profiles/).
 """
 import argparse
+import csv
+import hashlib
 import json
 import math
 import os
 import platform
+import statistics
 import sys
 import time
 
@@ -24,27 +34,107 @@ sys.path.insert(0, ROOT)
 METRIC = "fused quant-reduce-RMSNorm effective GB/s (% HBM peak) + µs per call"
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
+KERNEL_SOURCES = ["tensor_all_reduce_amd/csrc/fc_kernels.hip", "tensor_all_reduce_amd/csrc/fc_device.h"]
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def traffic_file(slug):
+    return os.path.join(PROFILES, f"pmc_traffic_{slug}.txt")
+
+
+def kernel_of_call(call, cfg):
+    """Substring naming the kernel instantiation a call launches for this workload."""
+    return {"quantize": f"k_quantize<{cfg.bits_rs}, {cfg.group}>",
+            "reduce_shard": f"k_reduce<{cfg.bits_rs}, {cfg.bits_ag}, {cfg.group}>",
+            "gather_norm": f"k_rows<fc::GatherProducer<{cfg.bits_ag}>"}[call]
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--steps", type=int, default=600)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=2, help="two-step workload: 1, 2 or 3")
+    ap.add_argument("--config", type=int, default=2, help="headline two-step workload: 1, 2 or 3")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-resident)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel-reps", type=int, default=0, help="graph replays per kernel timing (0 = auto)")
+    ap.add_argument("--rows", default="all", help="other hot-path rows to measure: all | none | comma list of "
+                                                  "prefill,ll,rmsnorm")
+    ap.add_argument("--kernel-reps", type=int, default=0, help="graph replays per call timing (0 = auto)")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"))
     return ap.parse_args()
 
 
+def sources_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------------------------------------
+# HBM traffic from hardware counters
+# ---------------------------------------------------------------------------------------------------------
+def pmc_summary(fetch_csv, write_csv, out_path):
+    """Median FETCH_SIZE and WRITE_SIZE per kernel (KiB per dispatch), scaled by what the same counters
+    read for the 1 GiB copy kernel (whose true traffic is 1 GiB each way)."""
+    def load(path, counter):
+        d = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                d.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: statistics.median(v) for k, v in d.items()}
+    f, w = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    copy = next(k for k in f if "k_copy" in k)
+    fs, ws = (1 << 20) / f[copy], (1 << 20) / w[copy]
+    lines = [f"# HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (separate runs)",
+             f"# scale factors from the 1 GiB copy kernel: fetch x{fs:.4f}, write x{ws:.4f}",
+             f"sources_sha {sources_sha()}"]
+    for k in sorted(f):
+        if not k.startswith(("fc::", "void fc::")):
+            continue
+        lines.append(f"kernel {round(f[k] * fs * 1024)} {round(w.get(k, 0.0) * ws * 1024)} {k}")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def load_traffic(cfg):
+    """{kernel name: (fetch bytes, write bytes)} of this workload, if the summary was taken on the current
+    kernel sources (else None: the counters no longer describe the kernels)."""
+    path = traffic_file(cfg.slug)
+    if not os.path.exists(path):
+        return None
+    sha, kern = None, {}
+    for line in open(path):
+        p = line.split()
+        if not p or p[0].startswith("#"):
+            continue
+        if p[0] == "sources_sha":
+            sha = p[1]
+        elif p[0] == "kernel":
+            kern[" ".join(p[3:])] = (int(p[1]), int(p[2]))
+    return kern if sha == sources_sha() else None
+
+
+def traffic_for(call, cfg, traffic):
+    if not traffic:
+        return None
+    key = kernel_of_call(call, cfg)
+    for name, (fb, wb) in traffic.items():
+        if key in name:
+            return {"fetch": fb, "write": wb, "total": fb + wb, "kernel": name}
+    return None
+
+
+# ---------------------------------------------------------------------------------------------------------
 def cpu_baseline(cfg, seconds):
     """The oracle (single-threaded C++) on the same workload, whole steps repeated for about `seconds`."""
     sys.path.insert(0, os.path.join(ROOT, "oracle"))
     import oracle
     from tensor_all_reduce_amd import bytes_model as bm, datagen as dg
-    if cfg.n > (1 << 22):  # the 70B prefill step takes minutes on one core: time one row block
+    if cfg.n > (1 << 22):  # the 70B prefill step takes minutes on one core: time a block of rows
         T = max(cfg.R, (1 << 22) // cfg.H // cfg.R * cfg.R)
         sample = f"{T} of {cfg.T} tokens x all {cfg.R} ranks, whole steps repeated"
     else:
@@ -70,37 +160,76 @@ def cpu_baseline(cfg, seconds):
             "host_cores": os.cpu_count()}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build emulates the R ranks on one GPU "
-              "(inter-GPU transfers are local HBM buffers); run with --gpus 1", file=sys.stderr)
-        return 2
-    import numpy as np
-    import torch
-    from tensor_all_reduce_amd import _lib, bytes_model as bm, datagen as dg
-    from tensor_all_reduce_amd.flash_allreduce import TwoStepAllReduce
+# ---------------------------------------------------------------------------------------------------------
+class Ctx:
+    def __init__(self):
+        import numpy as np
+        import torch
+        self.np, self.torch = np, torch
+        self.dev = torch.device("cuda:0")
 
-    cfg = dg.CONFIGS[args.config]
-    assert cfg.kind == "two_step", "the benchmark's metric is the quantized two-step path"
-    dev = torch.device("cuda:0")
+    def up(self, a):
+        return self.torch.from_numpy(self.np.ascontiguousarray(a).view(self.np.int16)).to(self.dev)
+
+    def ev(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def graph(self, fn, count):
+        g = self.torch.cuda.CUDAGraph()
+        with self.torch.cuda.graph(g):
+            for k in range(count):
+                fn(k)
+        return g
+
+    def time_graph(self, g, reps, per):
+        """Replay `g` reps times; microseconds per item (per = items per replay)."""
+        torch = self.torch
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = self.ev(), self.ev()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * per)
+
+
+def copy_ceiling(cx):
+    from tensor_all_reduce_amd import _lib
+    torch = cx.torch
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=cx.dev)
+    dst = torch.empty(nb, dtype=torch.uint8, device=cx.dev)
+    _lib.fc_copy(src, dst)
+    torch.cuda.synchronize()
+    a, b = cx.ev(), cx.ev()
+    a.record()
+    for _ in range(10):
+        _lib.fc_copy(src, dst)
+    b.record()
+    torch.cuda.synchronize()
+    return 2 * nb * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
+def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic):
+    """The quantized two-step path: timed whole steps, then each call alone."""
+    torch = cx.torch
+    from tensor_all_reduce_amd import bytes_model as bm, datagen as dg
+    from tensor_all_reduce_amd.flash_allreduce import TwoStepAllReduce
     R, T, H, G, b1, b2 = cfg.R, cfg.T, cfg.H, cfg.group, cfg.bits_rs, cfg.bits_ag
     calls = bm.two_step_whole(R, T, H, b1, b2, G)
     step_bytes = sum(bm.total(v) for v in calls.values())
-
-    # ---- inputs, resident in HBM before timing
-    def up(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
-    parts0 = up(np.stack(dg.partials(cfg)))
-    res0, gam = up(dg.residual(cfg)), up(dg.gamma(cfg))
-    set_bytes = step_bytes
-    nsets = 1 if args.warm else max(1, math.ceil(2 * MALL_BYTES / set_bytes))
+    # every call's own working set over all buffer sets exceeds twice the last-level cache
+    nsets = 1 if warm else max(1, math.ceil(2 * MALL_BYTES / min(bm.total(v) for v in calls.values())))
+    parts0 = cx.up(cx.np.stack(dg.partials(cfg)))
+    res0, gam = cx.up(dg.residual(cfg)), cx.up(dg.gamma(cfg))
     sets = []
     for k in range(nsets):
-        p = TwoStepAllReduce(R, T, H, b1, b2, G, device=dev, parts=parts0.clone() if k else parts0)
+        p = TwoStepAllReduce(R, T, H, b1, b2, G, device=cx.dev, parts=parts0.clone() if k else parts0)
         res = res0.clone() if k else res0
-        out = torch.empty(cfg.n, dtype=torch.int16, device=dev)
-        rout = torch.empty(cfg.n, dtype=torch.int16, device=dev)
+        out = torch.empty(cfg.n, dtype=torch.int16, device=cx.dev)
+        rout = torch.empty(cfg.n, dtype=torch.int16, device=cx.dev)
         sets.append((p, p.make_norm(gam, out, residual=res, residual_out=rout, eps=cfg.eps), (res, out, rout)))
     torch.cuda.synchronize()
 
@@ -108,100 +237,249 @@ def main():
         p, norm, _ = sets[k]
         p.run(norm=norm)
 
-    # warm-up (eager, then graph)
-    for k in range(min(args.warmup, nsets)):
+    for k in range(min(warmup, nsets)):
         step(k)
     torch.cuda.synchronize()
-    g_all = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_all):
-        for k in range(nsets):
-            step(k)
-    tail = args.steps % nsets
-    g_tail = None
-    if tail:
-        g_tail = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_tail):
-            for k in range(tail):
-                step(k)
-    for _ in range(max(1, args.warmup // nsets)):
+    g_all = cx.graph(step, nsets)
+    g_tail = cx.graph(step, steps % nsets) if steps % nsets else None
+    for _ in range(max(1, warmup // nsets)):
         g_all.replay()
     torch.cuda.synchronize()
-
-    # ---- timed region: exactly args.steps steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region: exactly `steps` steps
+    e0, e1 = cx.ev(), cx.ev()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     e0.record()
-    for _ in range(args.steps // nsets):
+    for _ in range(steps // nsets):
         g_all.replay()
     if g_tail is not None:
         g_tail.replay()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms_step = e0.elapsed_time(e1) / args.steps
-    value = step_bytes / (ms_step * 1e-3) / 1e9
+    ms_step = e0.elapsed_time(e1) / steps
 
-    # ---- per-call durations: each call alone, replayed from a graph over the same buffer sets
-    def time_call(fn, reps):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for k in range(nsets):
-                fn(k)
-        g.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / (reps * nsets)  # microseconds per launch
-
-    reps = args.kernel_reps or max(1, args.steps // nsets)
-    fns = {
-        "quantize": lambda k: sets[k][0].quantize(),
-        "reduce_shard": lambda k: sets[k][0].reduce_scatter(),
-        "gather_norm": lambda k: sets[k][0].all_gather(norm=sets[k][1]),
-    }
+    reps = kernel_reps or max(2, steps // nsets)
+    fns = {"quantize": lambda k: sets[k][0].quantize(), "reduce_shard": lambda k: sets[k][0].reduce_scatter(),
+           "gather_norm": lambda k: sets[k][0].all_gather(norm=sets[k][1])}
     per_call = {}
     for name, fn in fns.items():
-        us = time_call(fn, reps)
+        us = cx.time_graph(cx.graph(fn, nsets), reps, nsets)
         by = bm.total(calls[name])
-        per_call[name] = {"us": round(us, 3), "bytes": by, "GB/s": round(by / (us * 1e-6) / 1e9, 1),
-                          "frac_hbm": round(by / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
-    dom = max(per_call, key=lambda k: per_call[k]["us"])
+        gbps = by / (us * 1e-6) / 1e9
+        per_call[name] = {"us": round(us, 3), "bytes": by, "GB/s": round(gbps, 1),
+                          "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_for(name, cfg, traffic)}
+    del sets, g_all, g_tail
+    torch.cuda.empty_cache()
+    return dict(ms_step=ms_step, wall=wall, step_bytes=step_bytes, nsets=nsets, per_call=per_call)
 
-    # ---- practical copy ceiling (1 GiB each way)
-    nb = 1 << 30
-    src = torch.empty(nb, dtype=torch.uint8, device=dev)
-    dst = torch.empty(nb, dtype=torch.uint8, device=dev)
-    _lib.fc_copy(src, dst)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+def bench_ll(cx):
+    """Self-synchronizing slots, 8 ranks x [128, 8192], 64-slot blocks, 2% late (rank, block) copies with the
+    seeded mix of wrong epoch words: time the first pass and the retry after the late blocks arrive."""
+    torch, np = cx.torch, cx.np
+    from tensor_all_reduce_amd import _lib, bytes_model as bm, datagen as dg
+    from tensor_all_reduce_amd.flash_allreduce import LLUnpackReduce
+    cfg = dg.CONFIGS[4]
+    R, n, B, e = cfg.R, cfg.n, cfg.block_slots, cfg.epoch
+    nslots, nblk = n // 2, n // 2 // B
+    set_bytes = R * 4 * n
+    nsets = max(1, math.ceil(2 * MALL_BYTES / set_bytes))
+    xs = [cx.up(dg.partial(cfg, r)) for r in range(R)]
+    orders = [torch.from_numpy(dg.write_order(cfg, r, nblk)).to(cx.dev) for r in range(R)]
+    eps, masks = zip(*[dg.stale_epochs(cfg, r, nslots) for r in range(R)])
+    late_ep = [torch.from_numpy(ep.view(np.int32)).to(cx.dev) for ep in eps]
+    good_ep = torch.full((nslots,), e, dtype=torch.int64, device=cx.dev).to(torch.int32)
+    sets = []
+    for k in range(nsets):
+        slots = [torch.empty(nslots, dtype=torch.int64, device=cx.dev) for _ in range(R)]
+        for r in range(R):
+            _lib.fc_ll_pack(xs[r], B, e, slots[r], block_order=orders[r])
+        out = torch.zeros(n, dtype=torch.int16, device=cx.dev)
+        stale = torch.zeros(R * nblk, dtype=torch.uint8, device=cx.dev)
+        done = torch.zeros(nblk, dtype=torch.uint8, device=cx.dev)
+        cnt = torch.zeros(2, dtype=torch.int32, device=cx.dev)
+        sets.append((slots, LLUnpackReduce(slots, n, B, out, stale, done, cnt), done, cnt))
+
+    def set_epochs(which):
+        for slots, _, _, _ in sets:
+            for r in range(R):
+                slots[r].view(torch.int32).view(-1, 2)[:, 1] = which[r] if which is not None else good_ep
+
+    def reset():
+        for _, _, done, cnt in sets:
+            done.zero_()
+            cnt.zero_()
+    g = cx.graph(lambda k: sets[k][1].run(e), nsets)
+    t1, t2 = [], []
+    for _ in range(5):
+        set_epochs(late_ep)
+        reset()
+        torch.cuda.synchronize()
+        t1.append(_once(cx, g, nsets))
+        cnt0 = sets[0][3].cpu().numpy().view(np.uint32).copy()
+        set_epochs(None)
+        torch.cuda.synchronize()
+        t2.append(_once(cx, g, nsets))
+    pending = int(cnt0[1])
+    by1 = bm.total(bm.ll_unpack(R, n, B, completed_blocks=nblk - pending))
+    us1, us2 = statistics.median(t1), statistics.median(t2)
+    res = {"workload": cfg.name, "pass1_us": round(us1, 2), "pass1_bytes": by1,
+           "pass1_GB/s": round(by1 / (us1 * 1e-6) / 1e9, 1), "stale_pairs": int(cnt0[0]), "pending_blocks": pending,
+           "blocks": nblk, "retry_us": round(us2, 2), "buffer_sets": nsets}
+    del sets, g
+    torch.cuda.empty_cache()
+    return res
+
+
+def _once(cx, g, per):
+    torch = cx.torch
+    a, b = cx.ev(), cx.ev()
     a.record()
-    for _ in range(10):
-        _lib.fc_copy(src, dst)
+    g.replay()
     b.record()
     torch.cuda.synchronize()
-    copy_gbps = 2 * nb * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
-    del src, dst
+    return a.elapsed_time(b) * 1e3 / per
 
+
+def bench_rmsnorm_overlap(cx):
+    """Unquantized fused reduce + residual-add + RMSNorm, 8 ranks x [8192, 8192] split into two wave-aware
+    halves of 4096 rows: each half alone (per workgroup cap), the bf16 GEMM [4096,8192]x[8192,8192] alone,
+    and half A's reduce on one stream overlapped with the GEMM on another."""
+    torch, np = cx.torch, cx.np
+    from tensor_all_reduce_amd import bytes_model as bm, datagen as dg
+    from tensor_all_reduce_amd.flash_allreduce import ReduceRMSNorm
+    cfg = dg.CONFIGS[5]
+    R, T, H = cfg.R, cfg.T, cfg.H
+    a = cfg.splits[0]
+    parts = [cx.up(dg.partial(cfg, r)) for r in range(R)]
+    res, gam = cx.up(dg.residual(cfg)), cx.up(dg.gamma(cfg))
+    out = torch.empty(T * H, dtype=torch.int16, device=cx.dev)
+    rout = torch.empty(T * H, dtype=torch.int16, device=cx.dev)
+    halves = []
+    for lo, hi in ((0, a), (a, T)):
+        sl = slice(lo * H, hi * H)
+        halves.append(ReduceRMSNorm([p[sl] for p in parts], hi - lo, H, gam, out[sl], residual=res[sl],
+                                    residual_out=rout[sl], eps=cfg.eps))
+    half_bytes = bm.total(bm.reduce_rmsnorm(R, a, H, True, True))
+    gen = torch.Generator(device=cx.dev)
+    gen.manual_seed(0xFC07)
+    A = torch.randn(a, H, device=cx.dev, dtype=torch.bfloat16, generator=gen)
+    Bm = torch.randn(H, H, device=cx.dev, dtype=torch.bfloat16, generator=gen)
+    C = torch.empty(a, H, device=cx.dev, dtype=torch.bfloat16)
+    s1, s2 = torch.cuda.Stream(device=cx.dev), torch.cuda.Stream(device=cx.dev)
+    reps = 8
+
+    def timed(stream, fn):
+        ea, eb = cx.ev(), cx.ev()
+        with torch.cuda.stream(stream):
+            ea.record()
+            for _ in range(reps):
+                fn()
+            eb.record()
+        return ea, eb
+
+    def gemm():
+        torch.matmul(A, Bm, out=C)
+    # warm up
+    for h in halves:
+        h.run(stream=s1)
+    with torch.cuda.stream(s2):
+        gemm()
+    torch.cuda.synchronize()
+    ga, gb = timed(s2, gemm)
+    torch.cuda.synchronize()
+    gemm_us = ga.elapsed_time(gb) * 1e3 / reps
+    sweep = {}
+    for mw in (8, 16, 32, 64, 128, 256, 0):
+        ea, eb = timed(s1, lambda: halves[0].run(max_workgroups=mw, stream=s1))
+        torch.cuda.synchronize()
+        alone = ea.elapsed_time(eb) * 1e3 / reps
+        # overlapped: both streams start after a common event
+        start = cx.ev()
+        start.record(torch.cuda.current_stream())
+        s1.wait_event(start)
+        s2.wait_event(start)
+        ra, rb = timed(s1, lambda: halves[0].run(max_workgroups=mw, stream=s1))
+        qa, qb = timed(s2, gemm)
+        end1, end2 = cx.ev(), cx.ev()
+        end1.record(s1)
+        end2.record(s2)
+        torch.cuda.synchronize()
+        over_r = ra.elapsed_time(rb) * 1e3 / reps
+        over_g = qa.elapsed_time(qb) * 1e3 / reps
+        makespan = max(start.elapsed_time(end1), start.elapsed_time(end2)) * 1e3 / reps
+        sweep[str(mw) if mw else "rows"] = {
+            "alone_us": round(alone, 1), "alone_GB/s": round(half_bytes / (alone * 1e-6) / 1e9, 1),
+            "overlap_reduce_us": round(over_r, 1), "overlap_gemm_us": round(over_g, 1),
+            "overlap_makespan_us": round(makespan, 1), "serial_us": round(alone + gemm_us, 1)}
+    # both halves back to back at the default grid
+    ea, eb = timed(s1, lambda: (halves[0].run(stream=s1), halves[1].run(stream=s1)))
+    torch.cuda.synchronize()
+    both = ea.elapsed_time(eb) * 1e3 / reps
+    res = {"workload": cfg.name, "half_bytes": half_bytes, "both_halves_us": round(both, 1),
+           "both_halves_GB/s": round(2 * half_bytes / (both * 1e-6) / 1e9, 1),
+           "gemm_alone_us": round(gemm_us, 1), "gemm_TFLOP/s": round(2 * a * H * H / (gemm_us * 1e-6) / 1e12, 1),
+           "max_workgroups_sweep": sweep}
+    del parts, halves, A, Bm, C
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build emulates the R ranks on one GPU "
+              "(inter-GPU transfers are local HBM buffers); run with --gpus 1", file=sys.stderr)
+        return 2
+    from tensor_all_reduce_amd import datagen as dg
+    cx = Ctx()
+    cfg = dg.CONFIGS[args.config]
+    traffic = load_traffic(cfg)
+    assert cfg.kind == "two_step", "the benchmark's metric is the quantized two-step path"
+    main_r = bench_two_step(cx, cfg, args.steps, args.warmup, args.warm, args.kernel_reps, traffic)
+    ms_step = main_r["ms_step"]
+    value = main_r["step_bytes"] / (ms_step * 1e-3) / 1e9
+    per_call = main_r["per_call"]
+    dom = max(per_call, key=lambda k: per_call[k]["us"])
+    copy_gbps = copy_ceiling(cx)
+    tr = per_call[dom]["traffic"]
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": cfg.name, "R": R, "T": T, "H": H, "bits_rs": b1, "bits_ag": b2, "group": G,
-                   "mode": "whole emulated all-reduce on one GPU", "cache": "warm" if args.warm else "cold",
-                   "buffer_sets": nsets, "launch": "hip graph, 3 kernels per step"},
-        "us_per_step": round(ms_step * 1e3, 3), "bytes_per_step": step_bytes,
+        "config": {"workload": cfg.name, "R": cfg.R, "T": cfg.T, "H": cfg.H, "bits_rs": cfg.bits_rs,
+                   "bits_ag": cfg.bits_ag, "group": cfg.group, "mode": "whole emulated all-reduce on one GPU",
+                   "cache": "warm" if args.warm else "cold", "buffer_sets": main_r["nsets"],
+                   "launch": "hip graph, 3 kernels per step"},
+        "us_per_step": round(ms_step * 1e3, 3), "bytes_per_step": main_r["step_bytes"],
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "copy_ceiling_GBps": round(copy_gbps, 1), "pct_copy_ceiling": round(100 * value / copy_gbps, 2),
         "calls": per_call,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": per_call[dom]["GB/s"], "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": per_call[dom]["frac_hbm"], "traffic": None},
-        "wall_s": round(wall, 3),
+                     "unit": "GB/s", "frac": per_call[dom]["frac_hbm"],
+                     "traffic": tr["total"] if tr else None},
+        "wall_s": round(main_r["wall"], 3),
     }
+    rows = {"prefill", "ll", "rmsnorm"} if args.rows == "all" else set() if args.rows == "none" else set(
+        args.rows.split(","))
+    extra = {}
+    if "prefill" in rows and args.config != 3:
+        c3 = dg.CONFIGS[3]
+        r3 = bench_two_step(cx, c3, 30, 5, False, 0, load_traffic(c3))
+        v3 = r3["step_bytes"] / (r3["ms_step"] * 1e-3) / 1e9
+        extra["prefill_two_step"] = {"workload": c3.name, "us_per_step": round(r3["ms_step"] * 1e3, 2),
+                                     "GB/s": round(v3, 1), "pct_hbm_peak": round(100 * v3 / HBM_PEAK_GBPS, 2),
+                                     "pct_copy_ceiling": round(100 * v3 / copy_gbps, 2), "calls": r3["per_call"]}
+    if "ll" in rows:
+        extra["self_sync_slots"] = bench_ll(cx)
+    if "rmsnorm" in rows:
+        extra["tokenweave_reduce_rmsnorm"] = bench_rmsnorm_overlap(cx)
+    if extra:
+        line["rows"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)

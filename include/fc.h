@@ -20,7 +20,7 @@
  *  - Status codes: FC_E_NULL a required pointer is NULL; FC_E_ARG a value outside the supported set
  *    (bits not 4/8, group not 32/64/128/256, R not in [1,16], eps not > 0, block_slots not
  *    32/64/128/256, an input range that partially overlaps an output range); FC_E_SHAPE sizes that do
- *    not divide (n % group, L % group, n % hidden, hidden % 16, n % (2*block_slots)) or exceed the
+ *    not divide (n % group, L % group, n % hidden, hidden % 8, n % (2*block_slots)) or exceed the
  *    limits below; FC_E_ALIGN a data pointer not 16-byte aligned (meta: 4-byte); FC_E_LAUNCH the HIP
  *    launch failed (the hipError_t is kept for fc_last_hip_error()).
  *  - Out-of-contract values (NaN, Inf, |x| > 65504, group ranges or sums outside the fp16 range) give
@@ -70,7 +70,7 @@ typedef struct {
     const uint16_t* residual;  /* bf16 [rows*hidden], or NULL for no residual add */
     const uint16_t* gamma;     /* bf16 [hidden], required */
     float eps;                 /* > 0 */
-    int64_t hidden;            /* row length H: a multiple of 16, at most 131072 */
+    int64_t hidden;            /* row length H: a multiple of 8, at most 65536 */
     uint16_t* out;             /* bf16 [rows*hidden], required */
     uint16_t* residual_out;    /* bf16 [rows*hidden] or NULL; may be exactly `residual` (in place) */
 } fc_norm;
@@ -126,9 +126,9 @@ fc_status fc_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, in
 fc_status fc_ll_pack(const uint16_t* x, int64_t n, int block_slots, uint32_t epoch, const int32_t* block_order,
                      uint64_t* slots, hipStream_t stream);
 
-/* Measurement helper: copies `bytes` (a multiple of 16, 16-byte aligned pointers, no overlap) with
- * 16-byte loads and stores; its bandwidth is the practical HBM ceiling the kernels above are compared
- * with. */
+/* Measurement helper: copies `bytes` (a multiple of 16, at most 2^40, 16-byte aligned pointers, no
+ * overlap) with one non-temporal 16-byte load and store per lane; its bandwidth is the practical HBM
+ * ceiling the kernels above are compared with. */
 fc_status fc_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
 const char* fc_status_string(fc_status s);

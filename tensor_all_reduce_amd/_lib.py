@@ -13,7 +13,9 @@ import os
 import torch  # loads PyTorch's HIP runtime first; libfc.so binds to that same runtime
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libfc.so")
+# FC_LIB_PATH loads another build of the same library (e.g. one compiled with a different cache policy,
+# to compare the two); by default the in-tree build is used.
+LIB_PATH = os.environ.get("FC_LIB_PATH", os.path.join(HERE, "libfc.so"))
 
 FC_OK, FC_E_NULL, FC_E_ARG, FC_E_SHAPE, FC_E_ALIGN, FC_E_LAUNCH = range(6)
 

@@ -40,7 +40,7 @@ fc_status launched(hipError_t e) {
 fc_status check_norm(const fc_norm* nm, int64_t n) {
     if (!nm->gamma || !nm->out) return FC_E_NULL;
     if (!(nm->eps > 0.0f) || nm->eps != nm->eps || nm->eps > 3.0e38f) return FC_E_ARG;
-    if (nm->hidden <= 0 || nm->hidden % 16 != 0 || nm->hidden > kMaxHidden || n % nm->hidden != 0) return FC_E_SHAPE;
+    if (nm->hidden <= 0 || nm->hidden % 8 != 0 || nm->hidden > kMaxHidden || n % nm->hidden != 0) return FC_E_SHAPE;
     if (!aligned(nm->gamma, 16) || !aligned(nm->out, 16) || (nm->residual && !aligned(nm->residual, 16)) ||
         (nm->residual_out && !aligned(nm->residual_out, 16)))
         return FC_E_ALIGN;
@@ -200,7 +200,7 @@ fc_status fc_reduce_rmsnorm(const uint16_t* const* parts, int R, int64_t rows, c
                             hipStream_t stream) {
     if (R < 1 || R > fc::kMaxRanks || rows < 0 || max_workgroups < 0) return FC_E_ARG;
     if (!norm) return FC_E_NULL;
-    if (norm->hidden <= 0 || norm->hidden % 16 != 0 || norm->hidden > kMaxHidden) return FC_E_SHAPE;
+    if (norm->hidden <= 0 || norm->hidden % 8 != 0 || norm->hidden > kMaxHidden) return FC_E_SHAPE;
     if (rows > kMaxElems / norm->hidden) return FC_E_SHAPE;
     const int64_t n = rows * norm->hidden;
     const fc_status st = check_norm(norm, n);
@@ -268,7 +268,7 @@ fc_status fc_ll_pack(const uint16_t* x, int64_t n, int block_slots, uint32_t epo
 
 fc_status fc_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
     if (bytes < 0) return FC_E_ARG;
-    if (bytes % 16 != 0) return FC_E_SHAPE;
+    if (bytes % 16 != 0 || bytes > (int64_t(1) << 40)) return FC_E_SHAPE;
     if (bytes == 0) return FC_OK;
     if (!src || !dst) return FC_E_NULL;
     if (!aligned(src, 16) || !aligned(dst, 16)) return FC_E_ALIGN;

@@ -61,7 +61,8 @@ __device__ __forceinline__ float group_min(float v) {
     if constexpr (LANES >= 4) v = fminf(v, dpp<DPP_XOR2>(v));
     if constexpr (LANES >= 8) v = fminf(v, dpp<DPP_HALF_MIRROR>(v));
     if constexpr (LANES >= 16) v = fminf(v, dpp<DPP_MIRROR>(v));
-    static_assert(LANES <= 16, "groups span at most one DPP row");
+    if constexpr (LANES >= 32) v = fminf(v, __shfl_xor(v, 16, 64));
+    static_assert(LANES <= 32, "a group spans at most half a wavefront");
     return v;
 }
 template <int LANES>
@@ -70,6 +71,7 @@ __device__ __forceinline__ float group_max(float v) {
     if constexpr (LANES >= 4) v = fmaxf(v, dpp<DPP_XOR2>(v));
     if constexpr (LANES >= 8) v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
     if constexpr (LANES >= 16) v = fmaxf(v, dpp<DPP_MIRROR>(v));
+    if constexpr (LANES >= 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
     return v;
 }
 // Sum over the whole wavefront; every lane gets the same bits (each step adds a commutative pair).
@@ -169,10 +171,64 @@ struct Unpack<4> {
 __device__ __forceinline__ float meta_scale(uint32_t m) { return f16_to_f32(m & 0xffffu); }
 __device__ __forceinline__ float meta_zero(uint32_t m) { return f16_to_f32(m >> 16); }
 
-// 16-byte global memory access
+// ---- global memory access ------------------------------------------------------------------------
+// Every kernel lays its data out so that one wavefront-wide memory instruction covers one contiguous
+// span (lane i at base + i * width), so each instruction moves whole cache lines.  Data read or written
+// exactly once is "streamed"; FC_STREAM_NT selects the non-temporal cache policy for it (reused data
+// such as gamma always uses the default policy).
+#ifndef FC_STREAM_NT
+#define FC_STREAM_NT 1
+#endif
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
-__device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
-__device__ __forceinline__ void st8(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
+
+__device__ __forceinline__ uint4 lds16(const void* p) {
+#if FC_STREAM_NT
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+#else
+    return *reinterpret_cast<const uint4*>(p);
+#endif
+}
+__device__ __forceinline__ uint2 lds8(const void* p) {
+#if FC_STREAM_NT
+    const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+    return make_uint2(v.x, v.y);
+#else
+    return *reinterpret_cast<const uint2*>(p);
+#endif
+}
+__device__ __forceinline__ uint32_t lds4(const void* p) {
+#if FC_STREAM_NT
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+#else
+    return *reinterpret_cast<const uint32_t*>(p);
+#endif
+}
+__device__ __forceinline__ void sts16(void* p, uint4 v) {
+#if FC_STREAM_NT
+    const v4u w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<v4u*>(p));
+#else
+    *reinterpret_cast<uint4*>(p) = v;
+#endif
+}
+__device__ __forceinline__ void sts8(void* p, uint2 v) {
+#if FC_STREAM_NT
+    const v2u w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<v2u*>(p));
+#else
+    *reinterpret_cast<uint2*>(p) = v;
+#endif
+}
+__device__ __forceinline__ void sts4(void* p, uint32_t v) {
+#if FC_STREAM_NT
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+#else
+    *reinterpret_cast<uint32_t*>(p) = v;
+#endif
+}
 
 }  // namespace fc

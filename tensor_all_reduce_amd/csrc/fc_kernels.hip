@@ -1,62 +1,96 @@
 // fc_kernels.hip -- gfx950 kernels of the flash all-reduce path and their launchers.
 //
-// Every kernel streams HBM with 16-byte accesses per lane, keeps intermediate fp32 values in
-// registers, and reduces across lanes with DPP (group min/max) or wave sums (RMSNorm).  None uses
-// matrix cores: nothing on this path is a contraction.
+// Layout rule for every kernel: one wavefront-wide memory instruction covers one contiguous span, lane i
+// at base + i * width (16 bytes of bf16, 16 or 8 bytes of codes, 16 bytes = 2 slots), so each instruction
+// moves whole cache lines.  A lane therefore holds 8 consecutive bf16 elements (or 16 codes) per
+// instruction, and a quantization group spans G/8 (or G/16) aligned lanes whose min/max are combined
+// with DPP.  Intermediate fp32 values stay in registers; RMSNorm row sums use DPP inside a wavefront and
+// LDS across wavefronts.  Nothing here is a contraction, so matrix cores are not used.
 #include "fc_device.h"
 #include "fc_launch.h"
 
 namespace fc {
 
+__device__ __forceinline__ void unpack_bf16x8(uint4 u, float (&v)[8]) {
+    v[0] = bf16_lo(u.x);
+    v[1] = bf16_hi(u.x);
+    v[2] = bf16_lo(u.y);
+    v[3] = bf16_hi(u.y);
+    v[4] = bf16_lo(u.z);
+    v[5] = bf16_hi(u.z);
+    v[6] = bf16_lo(u.w);
+    v[7] = bf16_hi(u.w);
+}
+
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&v)[8]) {
+    return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7]));
+}
+
+// Dequantize the 8 codes of one lane-chunk (8 bytes of 8-bit codes or 4 bytes of 4-bit codes).
+template <int BITS>
+__device__ __forceinline__ void dequant8(const void* p, float s, float z, float (&y)[8]) {
+    if constexpr (BITS == 8) {
+        const uint2 w = lds8(p);
+        Unpack<8>::run(w.x, s, z, y);
+        Unpack<8>::run(w.y, s, z, y + 4);
+    } else {
+        Unpack<4>::run(lds4(p), s, z, y);
+    }
+}
+
 // =====================================================================================================
 // Group quantization (Flash Communication, summary "Core ideas of the solution": low-bit fine-grained
-// quantization of activations).  One lane quantizes E consecutive elements: 16 for 8-bit codes, 32 for
-// 4-bit codes, so that each lane writes exactly 16 bytes of codes; a group of G spans G/E lanes.
+// quantization of activations).  Lane-chunk = 8 bf16 (16 bytes); a group of G spans G/8 lanes.  Each
+// lane handles K lane-chunks, 64 chunks apart: K = 4 independent 16-byte loads in flight for large
+// inputs, K = 1 (four times as many workgroups) for small, latency-bound ones.
 // =====================================================================================================
-template <int BITS, int G>
+template <int BITS, int G, int K>
 __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ x, int64_t nchunks,
                                                   uint8_t* __restrict__ codes, uint32_t* __restrict__ meta) {
-    constexpr int E = BITS == 8 ? 16 : 32;
-    constexpr int LPG = G / E;
-    const int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const bool valid = c0 < nchunks;
-    // Lanes past the end recompute the last chunk (whole groups lie on either side of the end), so every
-    // lane of a DPP group holds valid data; only the stores are masked.
-    const int64_t c = valid ? c0 : nchunks - 1;
-    float v[E];
-    const uint16_t* xp = x + c * E;
+    constexpr int LPG = G / 8;
+    constexpr int CB = BITS;  // code bytes per 8-element chunk: 8 or 4
+    const int lane = threadIdx.x & 63;
+    const int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 * K) + lane;
+    float v[K][8];
 #pragma unroll
-    for (int k = 0; k < E / 8; ++k) {
-        const uint4 u = ld16(xp + 8 * k);
-        v[8 * k + 0] = bf16_lo(u.x);
-        v[8 * k + 1] = bf16_hi(u.x);
-        v[8 * k + 2] = bf16_lo(u.y);
-        v[8 * k + 3] = bf16_hi(u.y);
-        v[8 * k + 4] = bf16_lo(u.z);
-        v[8 * k + 5] = bf16_hi(u.z);
-        v[8 * k + 6] = bf16_lo(u.w);
-        v[8 * k + 7] = bf16_hi(u.w);
+    for (int k = 0; k < K; ++k) {
+        // Chunks past the end: whole groups lie on either side of it, so these lanes recompute the last
+        // chunk (keeping their DPP partners' data valid) and store nothing.
+        const int64_t c = min(base + 64 * k, nchunks - 1);
+        unpack_bf16x8(lds16(x + c * 8), v[k]);
     }
-    uint32_t w[E * BITS / 32];
-    uint32_t m;
-    quantize_lane<BITS, E, LPG>(v, w, m);
-    if (valid) {
-        st16(codes + c * 16, make_uint4(w[0], w[1], w[2], w[3]));
-        if ((threadIdx.x % LPG) == 0) meta[c / LPG] = m;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        uint32_t w[BITS / 4];
+        uint32_t m;
+        quantize_lane<BITS, 8, LPG>(v[k], w, m);
+        const int64_t c = base + 64 * k;
+        if (c < nchunks) {
+            if constexpr (BITS == 8) sts8(codes + c * CB, make_uint2(w[0], w[1]));
+            else sts4(codes + c * CB, w[0]);
+            if ((lane % LPG) == 0) meta[c / LPG] = m;
+        }
+    }
+}
+
+template <int BITS, int K>
+static void quantize_k(const QuantizeParams& p, int64_t nchunks, hipStream_t s) {
+    const dim3 grid((unsigned)((nchunks + 256 * K - 1) / (256 * K)));
+    switch (p.group) {
+        case 32: k_quantize<BITS, 32, K><<<grid, 256, 0, s>>>(p.x, nchunks, p.codes, p.meta); break;
+        case 64: k_quantize<BITS, 64, K><<<grid, 256, 0, s>>>(p.x, nchunks, p.codes, p.meta); break;
+        case 128: k_quantize<BITS, 128, K><<<grid, 256, 0, s>>>(p.x, nchunks, p.codes, p.meta); break;
+        default: k_quantize<BITS, 256, K><<<grid, 256, 0, s>>>(p.x, nchunks, p.codes, p.meta); break;
     }
 }
 
 template <int BITS>
 static hipError_t quantize_bits(const QuantizeParams& p, hipStream_t s) {
-    constexpr int E = BITS == 8 ? 16 : 32;
-    const int64_t nchunks = p.n / E;
-    const dim3 grid((unsigned)((nchunks + 255) / 256));
-    switch (p.group) {
-        case 32: k_quantize<BITS, 32><<<grid, 256, 0, s>>>(p.x, nchunks, p.codes, p.meta); break;
-        case 64: k_quantize<BITS, 64><<<grid, 256, 0, s>>>(p.x, nchunks, p.codes, p.meta); break;
-        case 128: k_quantize<BITS, 128><<<grid, 256, 0, s>>>(p.x, nchunks, p.codes, p.meta); break;
-        default: k_quantize<BITS, 256><<<grid, 256, 0, s>>>(p.x, nchunks, p.codes, p.meta); break;
-    }
+    const int64_t nchunks = p.n / 8;
+    // below ~4096 workgroups of K = 4 the launch cannot fill the chip's 256 compute units several times
+    if (nchunks >= (int64_t)4096 * 1024) quantize_k<BITS, 4>(p, nchunks, s);
+    else quantize_k<BITS, 1>(p, nchunks, s);
     return hipGetLastError();
 }
 
@@ -65,10 +99,11 @@ hipError_t launch_quantize(const QuantizeParams& p, hipStream_t s) {
 }
 
 // =====================================================================================================
-// Reduce-scatter receive side (two-step all-reduce, step one).  Block row y = shard; each lane owns E
-// consecutive elements of the shard (E = 32 if either width is 4 bits, else 16), dequantizes them from
-// every rank's message, folds them in fp32 in ascending rank order (flash-comm: reduction order fixed,
-// independent of arrival order) and requantizes the fp32 sums for the all-gather step.
+// Reduce-scatter receive side (two-step all-reduce, step one).  Block row y = shard; lane-chunk = 16
+// elements (16 or 8 bytes of codes per rank); a group spans G/16 lanes.  Each lane dequantizes its chunk
+// from every rank's message and folds the values in fp32 in ascending rank order (flash-comm:
+// reduction order fixed, independent of arrival order), then requantizes the fp32 sums for the
+// all-gather step.
 // =====================================================================================================
 struct ReduceKArgs {
     const uint8_t* in_codes[kMaxReduceIn];
@@ -76,35 +111,43 @@ struct ReduceKArgs {
     uint8_t* out_codes[kMaxRanks];
     uint32_t* out_meta[kMaxRanks];
     int R;
-    int64_t nchunks;  // lanes' chunks per shard = L / E
+    int64_t nchunks;  // 16-element chunks per shard = L / 16
 };
 
 template <int B1, int B2, int G>
 __global__ __launch_bounds__(256) void k_reduce(const ReduceKArgs a) {
-    constexpr int E = (B1 == 4 || B2 == 4) ? 32 : 16;
+    constexpr int E = 16;
     constexpr int LPG = G / E;
-    constexpr int IN_BYTES = E * B1 / 8;   // 16 or 32
-    constexpr int IN_W4 = IN_BYTES / 16;   // uint4 loads per rank
-    constexpr int RB = 8;                  // ranks loaded per batch
+    constexpr int IN_W = B1 / 2;  // input code words (4 bytes) per rank: 4 or 2
+    constexpr int RB = 8;         // ranks loaded per batch
     const int shard = blockIdx.y;
     const int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const bool valid = c0 < a.nchunks;
-    const int64_t c = valid ? c0 : a.nchunks - 1;
-    const int64_t gidx = (c * E) / G;
+    const int64_t c = valid ? c0 : a.nchunks - 1;  // whole groups lie on either side of the end
+    const int64_t gidx = c / LPG;
     const int R = a.R;
     float acc[E];
     for (int r0 = 0; r0 < R; r0 += RB) {
-        uint4 wv[RB][IN_W4];
+        uint32_t wv[RB][IN_W];
         uint32_t mv[RB];
+        // All RB loads are issued unconditionally (ranks past R re-read rank R-1 and are ignored), so no
+        // branch separates them and they are all in flight together.
 #pragma unroll
         for (int j = 0; j < RB; ++j) {
-            if (r0 + j < R) {
-                const int t = shard * R + r0 + j;
-                const uint8_t* cp = a.in_codes[t] + c * IN_BYTES;
-#pragma unroll
-                for (int k = 0; k < IN_W4; ++k) wv[j][k] = ld16(cp + 16 * k);
-                mv[j] = a.in_meta[t][gidx];
+            const int t = shard * R + min(r0 + j, R - 1);
+            const uint8_t* cp = a.in_codes[t] + c * (E * B1 / 8);
+            if constexpr (B1 == 8) {
+                const uint4 u = lds16(cp);
+                wv[j][0] = u.x;
+                wv[j][1] = u.y;
+                wv[j][2] = u.z;
+                wv[j][3] = u.w;
+            } else {
+                const uint2 u = lds8(cp);
+                wv[j][0] = u.x;
+                wv[j][1] = u.y;
             }
+            mv[j] = a.in_meta[t][gidx];
         }
 #pragma unroll
         for (int j = 0; j < RB; ++j) {
@@ -112,10 +155,8 @@ __global__ __launch_bounds__(256) void k_reduce(const ReduceKArgs a) {
                 const float sc = meta_scale(mv[j]);
                 const float z = meta_zero(mv[j]);
                 float d[E];
-                const uint32_t* ww = reinterpret_cast<const uint32_t*>(&wv[j][0]);
 #pragma unroll
-                for (int k = 0; k < E / Unpack<B1>::PER_WORD; ++k)
-                    Unpack<B1>::run(ww[k], sc, z, d + k * Unpack<B1>::PER_WORD);
+                for (int k = 0; k < IN_W; ++k) Unpack<B1>::run(wv[j][k], sc, z, d + k * Unpack<B1>::PER_WORD);
                 if (r0 + j == 0) {
 #pragma unroll
                     for (int e = 0; e < E; ++e) acc[e] = d[e];
@@ -126,15 +167,14 @@ __global__ __launch_bounds__(256) void k_reduce(const ReduceKArgs a) {
             }
         }
     }
-    constexpr int OW = E * B2 / 32;  // output words per lane: 4 or 8
-    uint32_t w[OW];
+    uint32_t w[E * B2 / 32];
     uint32_t m;
     quantize_lane<B2, E, LPG>(acc, w, m);
     if (valid) {
-        uint8_t* op = a.out_codes[shard] + c * (OW * 4);
-#pragma unroll
-        for (int k = 0; k < OW / 4; ++k) st16(op + 16 * k, make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]));
-        if ((threadIdx.x % LPG) == 0) a.out_meta[shard][c / LPG] = m;
+        uint8_t* op = a.out_codes[shard] + c * (E * B2 / 8);
+        if constexpr (B2 == 8) sts16(op, make_uint4(w[0], w[1], w[2], w[3]));
+        else sts8(op, make_uint2(w[0], w[1]));
+        if ((threadIdx.x % LPG) == 0) a.out_meta[shard][gidx] = m;
     }
 }
 
@@ -149,8 +189,7 @@ static void reduce_launch_g(const ReduceKArgs& a, int group, dim3 grid, hipStrea
 }
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
-    const int E = (p.bits_in == 4 || p.bits_out == 4) ? 32 : 16;
-    const int64_t nchunks = p.L / E;
+    const int64_t nchunks = p.L / 16;
     const int per_launch = kMaxReduceIn / p.R;  // shards whose R pointers fit in one argument table
     for (int s0 = 0; s0 < p.n_shards; s0 += per_launch) {
         const int ns = (p.n_shards - s0) < per_launch ? (p.n_shards - s0) : per_launch;
@@ -177,44 +216,35 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
 }
 
 // =====================================================================================================
-// All-gather receive side, plain mode: dequantize every shard to bf16.  Block row y = shard; each lane
-// dequantizes the E codes held in 16 bytes (16 for 8-bit codes, 32 for 4-bit codes).
+// All-gather receive side, plain mode: dequantize every shard to bf16.  Block row y = shard;
+// lane-chunk = 8 elements (codes 8 or 4 bytes in, 16 bytes of bf16 out).
 // =====================================================================================================
 struct GatherKArgs {
     const uint8_t* codes[kMaxRanks];
     const uint32_t* meta[kMaxRanks];
     int64_t L;
-    int64_t nchunks;  // per shard
+    int64_t nchunks;  // 8-element chunks per shard
     int log2g;
     uint16_t* y;
 };
 
 template <int BITS>
 __global__ __launch_bounds__(256) void k_gather_plain(const GatherKArgs a) {
-    constexpr int E = BITS == 8 ? 16 : 32;
     const int shard = blockIdx.y;
     const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (c >= a.nchunks) return;
-    const uint4 w = ld16(a.codes[shard] + c * 16);
-    const uint32_t m = a.meta[shard][(c * E) >> a.log2g];
-    const float sc = meta_scale(m), z = meta_zero(m);
-    float d[E];
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) Unpack<BITS>::run(ww[k], sc, z, d + k * Unpack<BITS>::PER_WORD);
-    uint16_t* yp = a.y + shard * a.L + c * E;
-#pragma unroll
-    for (int k = 0; k < E / 8; ++k)
-        st16(yp + 8 * k, make_uint4(pack_bf16x2(d[8 * k], d[8 * k + 1]), pack_bf16x2(d[8 * k + 2], d[8 * k + 3]),
-                                    pack_bf16x2(d[8 * k + 4], d[8 * k + 5]), pack_bf16x2(d[8 * k + 6], d[8 * k + 7])));
+    const uint32_t m = a.meta[shard][(c * 8) >> a.log2g];
+    float d[8];
+    dequant8<BITS>(a.codes[shard] + c * BITS, meta_scale(m), meta_zero(m), d);
+    sts16(a.y + shard * a.L + c * 8, pack_bf16x8(d));
 }
 
 // =====================================================================================================
-// Row kernels: produce the fp32 all-reduced value y of one row chunk by chunk (16 elements = 32 bytes of
-// bf16 per lane and chunk), then apply the residual-add + RMSNorm epilogue (TokenWeave, abstract: fused
-// AllReduce-RMSNorm).  A workgroup owns a row at a time, keeps h in registers (CPT chunks per lane),
-// reduces sum(h^2) with DPP inside each wave and LDS across waves, and walks rows with a stride of the
-// grid size so that the grid (the compute-unit footprint) can be capped.
+// Row kernels: produce the fp32 all-reduced value y of one row, 8 elements (one lane-chunk) at a time,
+// then apply the residual-add + RMSNorm epilogue (TokenWeave, abstract: fused AllReduce-RMSNorm).  A
+// workgroup owns a row at a time and keeps h in registers (CPT chunks per lane, chunk j of a row at
+// lane j % BT); sum(h^2) is reduced with DPP inside each wavefront and LDS across wavefronts.  Rows are
+// walked with a stride of the grid size, so the grid (the compute-unit footprint) can be capped.
 // =====================================================================================================
 struct NormKArgs {
     const uint16_t* residual;
@@ -225,42 +255,76 @@ struct NormKArgs {
     uint16_t* residual_out;
 };
 
-// y from the R requantized shards of the all-gather step.
-template <int BITS>
+// y from the R requantized shards of the all-gather step.  UNIFORM: every row lies inside one shard
+// (L % H == 0), so the row's shard is the same for the whole workgroup and its message pointers are read
+// straight from the kernel arguments; otherwise a chunk's shard is found per lane through a pointer
+// table staged in LDS (which costs a barrier before the first load).
+template <int BITS, bool UNIFORM>
 struct GatherProducer {
     const uint8_t* codes[kMaxRanks];
     const uint32_t* meta[kMaxRanks];
     uint32_t L;
     int log2g;
 
+    static constexpr bool kNeedsSync = !UNIFORM;
     struct Shared {
         const uint8_t* codes[kMaxRanks];
         const uint32_t* meta[kMaxRanks];
     };
+    struct Row {
+        const uint8_t* codes;
+        const uint32_t* meta;
+        uint32_t base;  // flat index of the shard's first element
+    };
     __device__ void init(Shared& sh) const {
-        if (threadIdx.x == 0) {
+        if constexpr (!UNIFORM) {
+            if (threadIdx.x == 0) {
 #pragma unroll
-            for (int k = 0; k < kMaxRanks; ++k) {
-                sh.codes[k] = codes[k];
-                sh.meta[k] = meta[k];
+                for (int k = 0; k < kMaxRanks; ++k) {
+                    sh.codes[k] = codes[k];
+                    sh.meta[k] = meta[k];
+                }
             }
         }
     }
-    __device__ __forceinline__ void load(const Shared& sh, uint32_t i, float (&y)[16]) const {
-        const uint32_t s = i / L;  // a 16-element chunk never straddles a shard (L % 32 == 0)
-        const uint32_t off = i - s * L;
-        const uint32_t m = sh.meta[s][off >> log2g];
-        const float sc = meta_scale(m), z = meta_zero(m);
-        if constexpr (BITS == 8) {
-            const uint4 w = ld16(sh.codes[s] + off);
-            Unpack<8>::run(w.x, sc, z, y);
-            Unpack<8>::run(w.y, sc, z, y + 4);
-            Unpack<8>::run(w.z, sc, z, y + 8);
-            Unpack<8>::run(w.w, sc, z, y + 12);
+    __device__ __forceinline__ Row begin_row(uint32_t rbase) const {
+        if constexpr (UNIFORM) {
+            const uint32_t s = rbase / L;
+            return Row{codes[s], meta[s], s * L};
         } else {
-            const uint2 w = ld8(sh.codes[s] + off / 2);
-            Unpack<4>::run(w.x, sc, z, y);
-            Unpack<4>::run(w.y, sc, z, y + 8);
+            return Row{nullptr, nullptr, 0};
+        }
+    }
+    struct Raw {
+        uint2 codes;  // 8 codes: 8 bytes (8-bit) or the low word (4-bit)
+        uint32_t meta;
+    };
+    // Issue the loads of chunk i (no waiting); decode() turns them into y once they have arrived.
+    __device__ __forceinline__ void fetch(const Shared& sh, const Row& row, uint32_t i, Raw& raw) const {
+        const uint8_t* cp;
+        const uint32_t* mp;
+        uint32_t off;
+        if constexpr (UNIFORM) {
+            cp = row.codes;
+            mp = row.meta;
+            off = i - row.base;
+        } else {
+            const uint32_t s = i / L;  // an 8-element chunk never straddles a shard (L % 32 == 0)
+            cp = sh.codes[s];
+            mp = sh.meta[s];
+            off = i - s * L;
+        }
+        raw.meta = mp[off >> log2g];
+        if constexpr (BITS == 8) raw.codes = lds8(cp + off);
+        else raw.codes = make_uint2(lds4(cp + off / 2), 0u);
+    }
+    __device__ __forceinline__ void decode(const Raw& raw, float (&y)[8]) const {
+        const float sc = meta_scale(raw.meta), z = meta_zero(raw.meta);
+        if constexpr (BITS == 8) {
+            Unpack<8>::run(raw.codes.x, sc, z, y);
+            Unpack<8>::run(raw.codes.y, sc, z, y + 4);
+        } else {
+            Unpack<4>::run(raw.codes.x, sc, z, y);
         }
     }
 };
@@ -270,35 +334,36 @@ struct BF16ReduceProducer {
     const uint16_t* parts[kMaxRanks];
     int R;
 
+    static constexpr bool kNeedsSync = false;
     struct Shared {};
+    struct Row {};
     __device__ void init(Shared&) const {}
-    __device__ __forceinline__ void load(const Shared&, uint32_t i, float (&y)[16]) const {
+    __device__ __forceinline__ Row begin_row(uint32_t) const { return Row{}; }
+    struct Raw {
+        float y[8];
+    };
+    __device__ __forceinline__ void decode(const Raw& raw, float (&y)[8]) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = raw.y[e];
+    }
+    __device__ __forceinline__ void fetch(const Shared&, const Row&, uint32_t i, Raw& raw) const {
+        float (&y)[8] = raw.y;
         constexpr int RB = 8;
         for (int r0 = 0; r0 < R; r0 += RB) {
-            uint4 a[RB], b[RB];
+            uint4 a[RB];
+#pragma unroll
+            for (int j = 0; j < RB; ++j) a[j] = lds16(parts[min(r0 + j, R - 1)] + i);  // past R: unused
 #pragma unroll
             for (int j = 0; j < RB; ++j) {
                 if (r0 + j < R) {
-                    a[j] = ld16(parts[r0 + j] + i);
-                    b[j] = ld16(parts[r0 + j] + i + 8);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < RB; ++j) {
-                if (r0 + j < R) {
-                    const uint32_t w[8] = {a[j].x, a[j].y, a[j].z, a[j].w, b[j].x, b[j].y, b[j].z, b[j].w};
-                    float v[16];
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        v[2 * k] = bf16_lo(w[k]);
-                        v[2 * k + 1] = bf16_hi(w[k]);
-                    }
+                    float v[8];
+                    unpack_bf16x8(a[j], v);
                     if (r0 + j == 0) {
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) y[e] = v[e];
+                        for (int e = 0; e < 8; ++e) y[e] = v[e];
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) y[e] = y[e] + v[e];
+                        for (int e = 0; e < 8; ++e) y[e] = y[e] + v[e];
                     }
                 }
             }
@@ -306,100 +371,130 @@ struct BF16ReduceProducer {
     }
 };
 
-__device__ __forceinline__ void unpack_bf16x16(uint4 a, uint4 b, float (&v)[16]) {
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        v[2 * k] = bf16_lo(w[k]);
-        v[2 * k + 1] = bf16_hi(w[k]);
-    }
-}
-
-__device__ __forceinline__ void store_bf16x16(uint16_t* p, const float (&v)[16]) {
-    st16(p, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                       pack_bf16x2(v[6], v[7])));
-    st16(p + 8, make_uint4(pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]), pack_bf16x2(v[12], v[13]),
-                           pack_bf16x2(v[14], v[15])));
-}
-
-template <class P, int BT, int CPT>
-__global__ __launch_bounds__(BT) void k_rows(const P p, const NormKArgs na, int64_t rows) {
-    __shared__ float s_part[BT / 64];
+// A workgroup of RPB * BT lanes keeps RPB rows in flight (sub-block j owns row base + j); RPB > 1 is used
+// when the grid is capped well below the number of rows, so that each compute unit still has enough
+// loads in flight.
+template <class P, int BT, int CPT, int RPB>
+__global__ __launch_bounds__(BT * RPB) void k_rows(const P p, const NormKArgs na, int64_t rows) {
+    __shared__ float s_part[RPB][BT / 64];
     __shared__ typename P::Shared sh;
     p.init(sh);
-    __syncthreads();
+    if constexpr (P::kNeedsSync) __syncthreads();
     const int H = na.hidden;
-    const int nch = H >> 4;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const uint32_t rbase = (uint32_t)(row * H);
-        float h[CPT][16];
+    const int nch = H >> 3;
+    const int sub = threadIdx.x / BT;           // row slot inside the workgroup
+    const int t = threadIdx.x - sub * BT;       // lane inside the row
+    const int lane = threadIdx.x & 63, wid = t >> 6;
+    // Loads are never issued inside a lane-divergent branch (the compiler would wait for each one before
+    // leaving the branch): lanes past the end of a row load a clamped, valid chunk and only their stores
+    // and contributions are masked.
+    // gamma does not depend on the row: load this lane's chunks once (for the longest rows, whose
+    // registers are taken by h, reload it per row instead)
+    constexpr bool kHoistGamma = CPT <= 4;
+    uint4 g[kHoistGamma ? CPT : 1];  // kept as bf16 words until used, so that nothing waits for it early
+    if constexpr (kHoistGamma) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) g[k] = ld16(na.gamma + min(t + k * BT, nch - 1) * 8);
+    }
+    for (int64_t row0 = (int64_t)blockIdx.x * RPB; row0 < rows; row0 += (int64_t)gridDim.x * RPB) {
+        const int64_t row = row0 + sub;
+        const bool has_row = row < rows;
+        const uint32_t rbase = (uint32_t)((has_row ? row : rows - 1) * H);
+        const typename P::Row pr = p.begin_row(rbase);
+        uint32_t idx[CPT];
+        bool ok[CPT];
+        typename P::Raw raw[CPT];
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int ch = t + k * BT;
+            ok[k] = has_row && ch < nch;
+            idx[k] = rbase + min(ch, nch - 1) * 8;
+            p.fetch(sh, pr, idx[k], raw[k]);
+        }
+        uint4 rres[CPT];
+        if (na.residual) {
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) rres[k] = lds16(na.residual + idx[k]);
+        }
+        float h[CPT][8];
         float ss = 0.0f;
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
-            const int ch = threadIdx.x + k * BT;
-            if (ch < nch) {
-                const uint32_t i = rbase + ch * 16;
-                p.load(sh, i, h[k]);
-                if (na.residual) {
-                    float rv[16];
-                    unpack_bf16x16(ld16(na.residual + i), ld16(na.residual + i + 8), rv);
+            p.decode(raw[k], h[k]);
+            if (na.residual) {
+                float rv[8];
+                unpack_bf16x8(rres[k], rv);
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) h[k][e] = h[k][e] + rv[e];
-                }
-                if (na.residual_out) store_bf16x16(na.residual_out + i, h[k]);
-#pragma unroll
-                for (int e = 0; e < 16; ++e) ss = __builtin_fmaf(h[k][e], h[k][e], ss);
+                for (int e = 0; e < 8; ++e) h[k][e] = h[k][e] + rv[e];
             }
+            if (na.residual_out && ok[k]) sts16(na.residual_out + idx[k], pack_bf16x8(h[k]));
+            float sk = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sk = __builtin_fmaf(h[k][e], h[k][e], sk);
+            ss += ok[k] ? sk : 0.0f;
         }
         const float ws = wave_sum(ss);
-        if (lane == 0) s_part[wid] = ws;
+        if (lane == 0) s_part[sub][wid] = ws;
         __syncthreads();
         float tot = 0.0f;
 #pragma unroll
-        for (int w = 0; w < BT / 64; ++w) tot += s_part[w];
+        for (int w = 0; w < BT / 64; ++w) tot += s_part[sub][w];
         __syncthreads();
         const float ms = tot / (float)H;
         const float rinv = 1.0f / sqrtf(ms + na.eps);
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
-            const int ch = threadIdx.x + k * BT;
-            if (ch < nch) {
-                float g[16];
-                unpack_bf16x16(ld16(na.gamma + ch * 16), ld16(na.gamma + ch * 16 + 8), g);
-                float o[16];
+            float gk[8];
+            unpack_bf16x8(kHoistGamma ? g[k] : ld16(na.gamma + (idx[k] - rbase)), gk);
+            float o[8];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float a = h[k][e] * rinv;
-                    o[e] = a * g[e];
-                }
-                store_bf16x16(na.out + rbase + ch * 16, o);
+            for (int e = 0; e < 8; ++e) {
+                const float a = h[k][e] * rinv;
+                o[e] = a * gk[e];
             }
+            if (ok[k]) sts16(na.out + idx[k], pack_bf16x8(o));
         }
     }
 }
 
-// Threads per row and chunks per thread for a row of nch 16-element chunks.
+// Threads per row and chunks per thread for a row of nch 8-element chunks.
 struct RowShape {
     int bt, cpt;
 };
 static RowShape row_shape(int64_t hidden) {
-    const int64_t nch = hidden / 16;
+    const int64_t nch = hidden / 8;
     if (nch <= 64) return {64, 1};
     if (nch <= 128) return {128, 1};
     if (nch <= 256) return {256, 1};
     if (nch <= 512) return {256, 2};
     if (nch <= 1024) return {256, 4};
     if (nch <= 2048) return {512, 4};
-    return {1024, 4};
+    if (nch <= 4096) return {1024, 4};
+    return {1024, 8};
 }
 
+// grid: workgroups wanted (one per row, or the caller's cap).  A cap of at most a quarter of the rows
+// on rows of at most 256 lanes puts several rows in flight per workgroup: 4, or 2 when each lane holds 4
+// chunks (so that the loads in flight still fit in registers).
 template <class P>
 static hipError_t launch_rows(const P& p, const NormKArgs& na, int64_t rows, int grid, hipStream_t s) {
     const RowShape rs = row_shape(na.hidden);
+    if (rs.bt <= 256 && (int64_t)grid * 4 <= rows) {
+#define FC_ROWSN(BT, CPT, RPB)                                              \
+        if (rs.bt == BT && rs.cpt == CPT) {                                 \
+            k_rows<P, BT, CPT, RPB><<<grid, BT * RPB, 0, s>>>(p, na, rows); \
+            return hipGetLastError();                                      \
+        }
+        FC_ROWSN(64, 1, 4)
+        FC_ROWSN(128, 1, 4)
+        FC_ROWSN(256, 1, 4)
+        FC_ROWSN(256, 2, 4)
+        FC_ROWSN(256, 4, 2)
+#undef FC_ROWSN
+    }
 #define FC_ROWS(BT, CPT)                                                    \
     if (rs.bt == BT && rs.cpt == CPT) {                                     \
-        k_rows<P, BT, CPT><<<grid, BT, 0, s>>>(p, na, rows);                \
+        k_rows<P, BT, CPT, 1><<<grid, BT, 0, s>>>(p, na, rows);             \
         return hipGetLastError();                                          \
     }
     FC_ROWS(64, 1)
@@ -409,6 +504,7 @@ static hipError_t launch_rows(const P& p, const NormKArgs& na, int64_t rows, int
     FC_ROWS(256, 4)
     FC_ROWS(512, 4)
     FC_ROWS(1024, 4)
+    FC_ROWS(1024, 8)
 #undef FC_ROWS
     return hipErrorInvalidValue;
 }
@@ -423,6 +519,24 @@ static int ilog2(int v) {
     return l;
 }
 
+template <int BITS, bool UNIFORM>
+static hipError_t gather_norm_layout(const GatherParams& p, const NormKArgs& na, int64_t rows, hipStream_t s) {
+    GatherProducer<BITS, UNIFORM> g;
+    for (int i = 0; i < kMaxRanks; ++i) {
+        g.codes[i] = i < p.R ? p.codes[i] : nullptr;
+        g.meta[i] = i < p.R ? p.meta[i] : nullptr;
+    }
+    g.L = (uint32_t)p.L;
+    g.log2g = ilog2(p.group);
+    return launch_rows(g, na, rows, (int)rows, s);
+}
+
+template <int BITS>
+static hipError_t gather_norm_bits(const GatherParams& p, const NormKArgs& na, int64_t rows, hipStream_t s) {
+    return (p.L % p.norm.hidden == 0) ? gather_norm_layout<BITS, true>(p, na, rows, s)
+                                      : gather_norm_layout<BITS, false>(p, na, rows, s);
+}
+
 hipError_t launch_gather(const GatherParams& p, hipStream_t s) {
     if (p.y) {
         GatherKArgs a;
@@ -430,9 +544,8 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t s) {
             a.codes[i] = i < p.R ? p.codes[i] : nullptr;
             a.meta[i] = i < p.R ? p.meta[i] : nullptr;
         }
-        const int E = p.bits == 8 ? 16 : 32;
         a.L = p.L;
-        a.nchunks = p.L / E;
+        a.nchunks = p.L / 8;
         a.log2g = ilog2(p.group);
         a.y = p.y;
         const dim3 grid((unsigned)((a.nchunks + 255) / 256), (unsigned)p.R);
@@ -442,28 +555,9 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (p.has_norm) {
-        const NormKArgs na = norm_args(p.norm);
         const int64_t rows = (int64_t)p.R * p.L / p.norm.hidden;
-        const int grid = (int)rows;
-        if (p.bits == 8) {
-            GatherProducer<8> g;
-            for (int i = 0; i < kMaxRanks; ++i) {
-                g.codes[i] = i < p.R ? p.codes[i] : nullptr;
-                g.meta[i] = i < p.R ? p.meta[i] : nullptr;
-            }
-            g.L = (uint32_t)p.L;
-            g.log2g = ilog2(p.group);
-            return launch_rows(g, na, rows, grid, s);
-        } else {
-            GatherProducer<4> g;
-            for (int i = 0; i < kMaxRanks; ++i) {
-                g.codes[i] = i < p.R ? p.codes[i] : nullptr;
-                g.meta[i] = i < p.R ? p.meta[i] : nullptr;
-            }
-            g.L = (uint32_t)p.L;
-            g.log2g = ilog2(p.group);
-            return launch_rows(g, na, rows, grid, s);
-        }
+        return p.bits == 8 ? gather_norm_bits<8>(p, norm_args(p.norm), rows, s)
+                           : gather_norm_bits<4>(p, norm_args(p.norm), rows, s);
     }
     return hipSuccess;
 }
@@ -480,13 +574,14 @@ hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t s) {
 
 // =====================================================================================================
 // Self-synchronizing slots (flash-comm, abstract): the receiver validates each block's epoch words
-// itself, with no barrier.  Each lane owns 4 slots (32 bytes per rank, 8 output elements); a block of
-// B slots spans LPB = B/4 aligned lanes, so its verdict is a field of a wavefront ballot.
+// itself, with no barrier.  A wavefront owns a tile of 256 slots read by two instructions of 128 slots
+// (2 slots = 16 bytes per lane).  A block of B slots covers B/2 aligned lanes of one instruction when
+// B <= 128 (its verdict is a field of that instruction's ballot), or both instructions when B = 256.
 // =====================================================================================================
 struct LLKArgs {
     const uint64_t* slots[kMaxRanks];
     int R;
-    int64_t nthreads;  // nslots / 4
+    int64_t nslots;
     int64_t nblk;
     uint32_t epoch;
     uint16_t* out;
@@ -495,56 +590,87 @@ struct LLKArgs {
     uint32_t* counters;
 };
 
-template <int LPB>
+template <int B>
 __global__ __launch_bounds__(256) void k_ll_unpack(const LLKArgs a) {
     __shared__ uint32_t s_cnt[2];
     if (threadIdx.x < 2) s_cnt[threadIdx.x] = 0;
     __syncthreads();
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    constexpr int LB = B <= 128 ? B / 2 : 64;  // lanes of one instruction inside one block
+    const uint64_t field = LB == 64 ? ~0ull : ((1ull << LB) - 1ull);
     const int lane = threadIdx.x & 63;
-    const bool valid = t < a.nthreads;
-    const int64_t b = t / LPB;
-    const bool leader = (lane % LPB) == 0;
-    const bool active = valid && a.done[b] == 0;
-    const uint64_t field = LPB == 64 ? ~0ull : ((1ull << LPB) - 1ull);
-    const int shift = lane & ~(LPB - 1);
-    float acc[8];
-    bool all_valid = true;
+    const int64_t tile = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 256;
+    int64_t slot[2], blk[2];
+    bool active[2], all_valid[2] = {true, true}, leader[2];
+    // Loads are issued by every lane (a lane-divergent branch around a load would make the compiler
+    // wait for it): lanes outside the buffer or in blocks already done read a valid, clamped address and
+    // their results are masked.
+    int64_t src[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        slot[k] = tile + k * 128 + 2 * lane;
+        const bool inside = slot[k] < a.nslots;
+        blk[k] = inside ? slot[k] / B : a.nblk - 1;
+        const uint8_t dn = a.done[blk[k]];
+        active[k] = inside && dn == 0;
+        src[k] = active[k] ? slot[k] : 0;
+        leader[k] = B <= 128 ? (lane % LB) == 0 : (k == 0 && lane == 0);
+    }
+    float acc[2][4];
     uint32_t n_stale = 0;
-    for (int r = 0; r < a.R; ++r) {
-        uint4 s0 = make_uint4(0, a.epoch, 0, a.epoch), s1 = s0;
-        if (active) {
-            const uint64_t* sp = a.slots[r] + 4 * t;
-            s0 = ld16(sp);
-            s1 = ld16(sp + 2);
-        }
-        // slot = {payload dword, epoch dword}: epoch words are .y and .w of each 16-byte load
-        const bool st = (s0.y != a.epoch) | (s0.w != a.epoch) | (s1.y != a.epoch) | (s1.w != a.epoch);
-        const uint64_t bal = __ballot(st);
-        const bool blk_stale = ((bal >> shift) & field) != 0;
-        if (active && leader) {
-            a.stale[(int64_t)r * a.nblk + b] = blk_stale ? 1 : 0;
-            n_stale += blk_stale ? 1u : 0u;
-        }
-        all_valid = all_valid && !blk_stale;
-        const float v[8] = {bf16_lo(s0.x), bf16_hi(s0.x), bf16_lo(s0.z), bf16_hi(s0.z),
-                            bf16_lo(s1.x), bf16_hi(s1.x), bf16_lo(s1.z), bf16_hi(s1.z)};
-        if (r == 0) {
+    const int shift = lane & ~(LB - 1);
+    constexpr int RB = 8;  // ranks whose slots are loaded before any is examined (a batch past the last
+                           // rank re-reads the last rank's slots, which are ignored)
+    for (int r0 = 0; r0 < a.R; r0 += RB) {
+        uint4 sv[RB][2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = v[e];
-        } else {
+        for (int j = 0; j < RB; ++j)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = acc[e] + v[e];
+            for (int k = 0; k < 2; ++k)
+                sv[j][k] = lds16(a.slots[min(r0 + j, a.R - 1)] + src[k]);  // ranks past R: unused
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+            const int r = r0 + j;
+            if (r >= a.R) break;  // uniform across the wavefront
+            bool st[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k)  // epoch words: the high halves of the two slots
+                st[k] = active[k] && ((sv[j][k].y != a.epoch) | (sv[j][k].w != a.epoch));
+            const uint64_t b0 = __ballot(st[0]), b1 = __ballot(st[1]);
+            bool bst[2];
+            if constexpr (B == 256) {
+                bst[0] = bst[1] = (b0 | b1) != 0;
+            } else {
+                bst[0] = ((b0 >> shift) & field) != 0;
+                bst[1] = ((b1 >> shift) & field) != 0;
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                if (active[k] && leader[k]) {
+                    a.stale[(int64_t)r * a.nblk + blk[k]] = bst[k] ? 1 : 0;
+                    n_stale += bst[k] ? 1u : 0u;
+                }
+                all_valid[k] = all_valid[k] && !bst[k];
+                const uint4 q = sv[j][k];
+                const float v[4] = {bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.z), bf16_hi(q.z)};
+                if (r == 0) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[k][e] = v[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[k][e] = acc[k][e] + v[e];
+                }
+            }
         }
     }
     uint32_t n_pending = 0;
-    if (active) {
-        if (all_valid) {
-            st16(a.out + 8 * t, make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                                           pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])));
-            if (leader) a.done[b] = 1;
-        } else if (leader) {
-            n_pending = 1;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (!active[k]) continue;
+        if (all_valid[k]) {
+            sts8(a.out + 2 * slot[k], make_uint2(pack_bf16x2(acc[k][0], acc[k][1]), pack_bf16x2(acc[k][2], acc[k][3])));
+            if (leader[k]) a.done[blk[k]] = 1;
+        } else if (leader[k]) {
+            n_pending += 1;
         }
     }
     if (n_stale) atomicAdd(&s_cnt[0], n_stale);
@@ -557,68 +683,57 @@ hipError_t launch_ll_unpack(const LLParams& p, hipStream_t s) {
     LLKArgs a;
     for (int i = 0; i < kMaxRanks; ++i) a.slots[i] = i < p.R ? p.slots[i] : nullptr;
     a.R = p.R;
-    const int64_t nslots = p.n / 2;
-    a.nthreads = nslots / 4;
-    a.nblk = nslots / p.block_slots;
+    a.nslots = p.n / 2;
+    a.nblk = a.nslots / p.block_slots;
     a.epoch = p.epoch;
     a.out = p.out;
     a.stale = p.stale;
     a.done = p.done;
     a.counters = p.counters;
-    const dim3 grid((unsigned)((a.nthreads + 255) / 256));
+    const dim3 grid((unsigned)((a.nslots + 1023) / 1024));  // 4 wavefronts x 256 slots per workgroup
     switch (p.block_slots) {
-        case 32: k_ll_unpack<8><<<grid, 256, 0, s>>>(a); break;
-        case 64: k_ll_unpack<16><<<grid, 256, 0, s>>>(a); break;
-        case 128: k_ll_unpack<32><<<grid, 256, 0, s>>>(a); break;
-        default: k_ll_unpack<64><<<grid, 256, 0, s>>>(a); break;
+        case 32: k_ll_unpack<32><<<grid, 256, 0, s>>>(a); break;
+        case 64: k_ll_unpack<64><<<grid, 256, 0, s>>>(a); break;
+        case 128: k_ll_unpack<128><<<grid, 256, 0, s>>>(a); break;
+        default: k_ll_unpack<256><<<grid, 256, 0, s>>>(a); break;
     }
     return hipGetLastError();
 }
 
-// Sender emulation: lane j of the write order packs 4 slots of block order[j / LPB].
-// An order entry outside [0, nblk) (not a permutation: out of contract) writes nothing.
+// Sender emulation: lane t of the write order packs 2 slots (4 bf16 in, 16 bytes out) of block
+// order[t / (B/2)].  An order entry outside [0, nblk) (not a permutation: out of contract) writes nothing.
 __global__ __launch_bounds__(256) void k_ll_pack(const uint16_t* __restrict__ x, int64_t nthreads, int lpb,
-                                                 int block_slots, const int32_t* __restrict__ order, uint32_t epoch,
-                                                 uint64_t* __restrict__ slots) {
+                                                 int block_slots, int64_t nblk, const int32_t* __restrict__ order,
+                                                 uint32_t epoch, uint64_t* __restrict__ slots) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= nthreads) return;
     const int64_t j = t / lpb;
     const int64_t b = order ? (int64_t)order[j] : j;
-    if (b < 0 || b >= nthreads / lpb) return;
-    const int64_t k0 = b * block_slots + 4 * (t % lpb);
-    const uint4 xv = ld16(x + 2 * k0);
-    st16(slots + k0, make_uint4(xv.x, epoch, xv.y, epoch));
-    st16(slots + k0 + 2, make_uint4(xv.z, epoch, xv.w, epoch));
+    if (b < 0 || b >= nblk) return;
+    const int64_t k0 = b * block_slots + 2 * (t % lpb);
+    const uint2 xv = lds8(x + 2 * k0);
+    sts16(slots + k0, make_uint4(xv.x, epoch, xv.y, epoch));
 }
 
 hipError_t launch_ll_pack(const PackParams& p, hipStream_t s) {
-    const int64_t nthreads = p.n / 8;
+    const int64_t nthreads = p.n / 4;  // 2 slots = 4 elements per lane
     const dim3 grid((unsigned)((nthreads + 255) / 256));
-    k_ll_pack<<<grid, 256, 0, s>>>(p.x, nthreads, p.block_slots / 4, p.block_slots, p.order, p.epoch, p.slots);
+    k_ll_pack<<<grid, 256, 0, s>>>(p.x, nthreads, p.block_slots / 2, p.block_slots, p.n / 2 / p.block_slots, p.order,
+                                   p.epoch, p.slots);
     return hipGetLastError();
 }
 
 // =====================================================================================================
-// Copy ceiling: 16-byte loads and stores, 4 per lane per iteration, grid-stride.
+// Copy ceiling: one 16-byte streamed load and store per lane.
 // =====================================================================================================
 __global__ __launch_bounds__(256) void k_copy(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t n16) {
-    const int64_t stride = (int64_t)gridDim.x * 256 * 4;
-    for (int64_t base = (int64_t)blockIdx.x * 256 * 4 + threadIdx.x; base < n16; base += stride) {
-        uint4 v[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (base + k * 256 < n16) v[k] = src[base + k * 256];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (base + k * 256 < n16) dst[base + k * 256] = v[k];
-    }
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n16) sts16(dst + i, lds16(src + i));
 }
 
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s) {
     const int64_t n16 = bytes / 16;
-    int64_t blocks = (n16 + 1023) / 1024;
-    if (blocks > 8192) blocks = 8192;
-    if (blocks < 1) blocks = 1;
+    const int64_t blocks = (n16 + 255) / 256;  // bytes <= 2^40 keeps this under the grid limit
     k_copy<<<(unsigned)blocks, 256, 0, s>>>(reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst), n16);
     return hipGetLastError();
 }

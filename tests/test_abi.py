@@ -99,8 +99,8 @@ def test_gather_validation(L):
     assert f(sh, 2, 500, 8, 32, A, None, None) == L.FC_E_SHAPE
     assert f(sh, 2, 512, 8, 32, A + 8, None, None) == L.FC_E_ALIGN
     assert f(sh, 2, 512, 8, 32, A + 0x800000 - 64, None, None) == L.FC_E_ARG  # y overlaps shard codes
-    n = norm(L, hidden=200)
-    assert f(sh, 2, 512, 8, 32, None, C.byref(n), None) == L.FC_E_SHAPE   # hidden % 16
+    n = norm(L, hidden=100)
+    assert f(sh, 2, 512, 8, 32, None, C.byref(n), None) == L.FC_E_SHAPE   # hidden % 8
     n = norm(L, hidden=96)
     assert f(sh, 2, 512, 8, 32, None, C.byref(n), None) == L.FC_E_SHAPE   # n % hidden
     n = norm(L, eps=0.0)

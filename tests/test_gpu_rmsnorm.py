@@ -23,7 +23,8 @@ def _run(fc, parts_d, rows, H, gam_d, res_d=None, rout_d=None, max_wg=0, eps=1e-
 
 
 @pytest.mark.parametrize("R", [1, 2, 5, 8, 16])
-@pytest.mark.parametrize("rows,H", [(3, 256), (5, 4096), (7, 8192), (2, 12288), (4, 1024), (2, 20480)])
+@pytest.mark.parametrize("rows,H", [(3, 256), (5, 4096), (7, 8192), (2, 12288), (4, 1024), (2, 20480), (3, 1000),
+                                    (2, 65536)])
 def test_reduce_rmsnorm_parity(fc, orc, R, rows, H):
     import torch
     from gpu_helpers import assert_bf16_close, down, up

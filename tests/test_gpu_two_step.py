@@ -68,7 +68,7 @@ def _shard_msgs(orc, R, L, bits, group, seed, sigma=6.0):
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("group", [32, 128])
 @pytest.mark.parametrize("R,T,H", [(2, 4, 256), (8, 64, 4096), (8, 3, 4096), (4, 16, 8192), (3, 6, 2048),
-                                   (8, 1, 4096), (1, 5, 12288), (16, 2, 1024)])
+                                   (8, 1, 4096), (1, 5, 12288), (16, 2, 1024), (5, 8, 1000), (2, 2, 65536)])
 def test_gather_parity(fc, orc, bits, group, R, T, H):
     """Plain dequantize and the fused residual-add + RMSNorm epilogue; includes rows that straddle shards
     (T*H/R not a multiple of H, e.g. one decode token) and row lengths needing 1..4 chunks per lane."""
