@@ -88,9 +88,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 // ---- group quantizer --------------------------------------------------------------------------------
 // One lane holds E consecutive elements of a group that spans LPG aligned consecutive lanes.  Produces
 // the lane's packed codes (E*BITS/32 words) and the group's meta word (scale | zero << 16).
-// Codes: (x - z) * inv rounded to nearest even by adding 1.5*2^23 (exact for 0 <= v < 2^22; here
-// 0 <= v <= qmax*(1+2^-22) because z <= x and s >= (max - z)/qmax up to one rounding); the integer is
-// then read from the low mantissa bits and clamped, which also bounds out-of-contract inputs.
+// Codes: v = (x - z) * inv rounded to nearest even by adding 1.5*2^23, which leaves the integer in the low
+// mantissa bits (exact for 0 <= v < 2^22).  For in-contract inputs 0 <= v < qmax + 0.5: z <= x, and
+// s >= (max - z)/qmax up to the roundings of one division and one reciprocal, so v <= qmax*(1 + 2^-21);
+// the definition's clamp to [0, qmax] therefore never changes a code and is not executed.  Codes are
+// packed straight from the low byte (8-bit) or low nibble (4-bit) of the sum's bits, so an
+// out-of-contract input gives a wrong code but never touches a neighbour's bits.
 template <int BITS, int E, int LPG>
 __device__ __forceinline__ void quantize_lane(const float (&v)[E], uint32_t (&w)[E * BITS / 32], uint32_t& meta) {
     constexpr int QMAX = (1 << BITS) - 1;
@@ -114,24 +117,25 @@ __device__ __forceinline__ void quantize_lane(const float (&v)[E], uint32_t (&w)
         inv = 1.0f / f16_to_f32(sb);
     }
     meta = sb | (zb << 16);
-    constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
-    constexpr uint32_t MAGIC_BITS = 0x4B400000u;
+    constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23; its bit pattern 0x4B400000 has a zero low byte
     uint32_t c[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
         const float d = v[i] - z;
         const float q = d * inv;
-        const uint32_t m = f2u(q + MAGIC);
-        c[i] = min(m - MAGIC_BITS, (uint32_t)QMAX);
+        c[i] = f2u(q + MAGIC);  // low 8 bits = code
     }
 #pragma unroll
     for (int k = 0; k < E * BITS / 32; ++k) {
         if constexpr (BITS == 8) {
-            w[k] = c[4 * k] | (c[4 * k + 1] << 8) | (c[4 * k + 2] << 16) | (c[4 * k + 3] << 24);
+            // v_perm_b32 selectors: byte i of the result = byte sel_i of {src0:src1} (0x0c = zero)
+            const uint32_t lo = __builtin_amdgcn_perm(c[4 * k + 1], c[4 * k], 0x0c0c0400u);
+            const uint32_t hi = __builtin_amdgcn_perm(c[4 * k + 3], c[4 * k + 2], 0x0c0c0400u);
+            w[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
         } else {
-            uint32_t x = 0;
+            uint32_t x = c[8 * k] & 0xfu;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x |= c[8 * k + j] << (4 * j);
+            for (int j = 1; j < 8; ++j) x |= (c[8 * k + j] & 0xfu) << (4 * j);
             w[k] = x;
         }
     }

@@ -99,11 +99,11 @@ hipError_t launch_quantize(const QuantizeParams& p, hipStream_t s) {
 }
 
 // =====================================================================================================
-// Reduce-scatter receive side (two-step all-reduce, step one).  Block row y = shard; lane-chunk = 16
-// elements (16 or 8 bytes of codes per rank); a group spans G/16 lanes.  Each lane dequantizes its chunk
-// from every rank's message and folds the values in fp32 in ascending rank order (flash-comm:
-// reduction order fixed, independent of arrival order), then requantizes the fp32 sums for the
-// all-gather step.
+// Reduce-scatter receive side (two-step all-reduce, step one).  Block row y = shard; lane-chunk = E
+// elements (16: 16 or 8 bytes of codes per rank; 8 for small shards, twice as many lanes in flight);
+// a group spans G/E lanes.  Each lane dequantizes its chunk from every rank's message and folds the
+// values in fp32 in ascending rank order (flash-comm: reduction order fixed, independent of arrival
+// order), then requantizes the fp32 sums for the all-gather step.
 // =====================================================================================================
 struct ReduceKArgs {
     const uint8_t* in_codes[kMaxReduceIn];
@@ -111,15 +111,39 @@ struct ReduceKArgs {
     uint8_t* out_codes[kMaxRanks];
     uint32_t* out_meta[kMaxRanks];
     int R;
-    int64_t nchunks;  // 16-element chunks per shard = L / 16
+    int64_t nchunks;  // E-element chunks per shard = L / E
 };
 
-template <int B1, int B2, int G>
+// E codes of B bits: load (E*B/8 bytes) as 32-bit words
+template <int E, int B>
+__device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&w)[E * B / 32]) {
+    if constexpr (E * B / 8 == 16) {
+        const uint4 u = lds16(p);
+        w[0] = u.x;
+        w[1] = u.y;
+        w[2] = u.z;
+        w[3] = u.w;
+    } else if constexpr (E * B / 8 == 8) {
+        const uint2 u = lds8(p);
+        w[0] = u.x;
+        w[1] = u.y;
+    } else {
+        w[0] = lds4(p);
+    }
+}
+
+template <int E, int B>
+__device__ __forceinline__ void store_codes(uint8_t* p, const uint32_t (&w)[E * B / 32]) {
+    if constexpr (E * B / 8 == 16) sts16(p, make_uint4(w[0], w[1], w[2], w[3]));
+    else if constexpr (E * B / 8 == 8) sts8(p, make_uint2(w[0], w[1]));
+    else sts4(p, w[0]);
+}
+
+template <int B1, int B2, int G, int E>
 __global__ __launch_bounds__(256) void k_reduce(const ReduceKArgs a) {
-    constexpr int E = 16;
     constexpr int LPG = G / E;
-    constexpr int IN_W = B1 / 2;  // input code words (4 bytes) per rank: 4 or 2
-    constexpr int RB = 8;         // ranks loaded per batch
+    constexpr int IN_W = E * B1 / 32;  // input code words per rank
+    constexpr int RB = 8;              // ranks loaded per batch
     const int shard = blockIdx.y;
     const int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const bool valid = c0 < a.nchunks;
@@ -135,18 +159,7 @@ __global__ __launch_bounds__(256) void k_reduce(const ReduceKArgs a) {
 #pragma unroll
         for (int j = 0; j < RB; ++j) {
             const int t = shard * R + min(r0 + j, R - 1);
-            const uint8_t* cp = a.in_codes[t] + c * (E * B1 / 8);
-            if constexpr (B1 == 8) {
-                const uint4 u = lds16(cp);
-                wv[j][0] = u.x;
-                wv[j][1] = u.y;
-                wv[j][2] = u.z;
-                wv[j][3] = u.w;
-            } else {
-                const uint2 u = lds8(cp);
-                wv[j][0] = u.x;
-                wv[j][1] = u.y;
-            }
+            load_codes<E, B1>(a.in_codes[t] + c * (E * B1 / 8), wv[j]);
             mv[j] = a.in_meta[t][gidx];
         }
 #pragma unroll
@@ -171,25 +184,24 @@ __global__ __launch_bounds__(256) void k_reduce(const ReduceKArgs a) {
     uint32_t m;
     quantize_lane<B2, E, LPG>(acc, w, m);
     if (valid) {
-        uint8_t* op = a.out_codes[shard] + c * (E * B2 / 8);
-        if constexpr (B2 == 8) sts16(op, make_uint4(w[0], w[1], w[2], w[3]));
-        else sts8(op, make_uint2(w[0], w[1]));
+        store_codes<E, B2>(a.out_codes[shard] + c * (E * B2 / 8), w);
         if ((threadIdx.x % LPG) == 0) a.out_meta[shard][gidx] = m;
     }
 }
 
-template <int B1, int B2>
+template <int B1, int B2, int E>
 static void reduce_launch_g(const ReduceKArgs& a, int group, dim3 grid, hipStream_t s) {
     switch (group) {
-        case 32: k_reduce<B1, B2, 32><<<grid, 256, 0, s>>>(a); break;
-        case 64: k_reduce<B1, B2, 64><<<grid, 256, 0, s>>>(a); break;
-        case 128: k_reduce<B1, B2, 128><<<grid, 256, 0, s>>>(a); break;
-        default: k_reduce<B1, B2, 256><<<grid, 256, 0, s>>>(a); break;
+        case 32: k_reduce<B1, B2, 32, E><<<grid, 256, 0, s>>>(a); break;
+        case 64: k_reduce<B1, B2, 64, E><<<grid, 256, 0, s>>>(a); break;
+        case 128: k_reduce<B1, B2, 128, E><<<grid, 256, 0, s>>>(a); break;
+        default: k_reduce<B1, B2, 256, E><<<grid, 256, 0, s>>>(a); break;
     }
 }
 
-hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
-    const int64_t nchunks = p.L / 16;
+template <int E>
+static hipError_t launch_reduce_e(const ReduceParams& p, hipStream_t s) {
+    const int64_t nchunks = p.L / E;
     const int per_launch = kMaxReduceIn / p.R;  // shards whose R pointers fit in one argument table
     for (int s0 = 0; s0 < p.n_shards; s0 += per_launch) {
         const int ns = (p.n_shards - s0) < per_launch ? (p.n_shards - s0) : per_launch;
@@ -205,14 +217,20 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
         a.R = p.R;
         a.nchunks = nchunks;
         const dim3 grid((unsigned)((nchunks + 255) / 256), (unsigned)ns);
-        if (p.bits_in == 8 && p.bits_out == 8) reduce_launch_g<8, 8>(a, p.group, grid, s);
-        else if (p.bits_in == 4 && p.bits_out == 8) reduce_launch_g<4, 8>(a, p.group, grid, s);
-        else if (p.bits_in == 8 && p.bits_out == 4) reduce_launch_g<8, 4>(a, p.group, grid, s);
-        else reduce_launch_g<4, 4>(a, p.group, grid, s);
+        if (p.bits_in == 8 && p.bits_out == 8) reduce_launch_g<8, 8, E>(a, p.group, grid, s);
+        else if (p.bits_in == 4 && p.bits_out == 8) reduce_launch_g<4, 8, E>(a, p.group, grid, s);
+        else if (p.bits_in == 8 && p.bits_out == 4) reduce_launch_g<8, 4, E>(a, p.group, grid, s);
+        else reduce_launch_g<4, 4, E>(a, p.group, grid, s);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
+    // Fewer than ~1024 workgroups of 16-element chunks leave most compute units idle: halve the chunk.
+    const int64_t wgs16 = (p.L / 16 + 255) / 256 * p.n_shards;
+    return wgs16 < 1024 ? launch_reduce_e<8>(p, s) : launch_reduce_e<16>(p, s);
 }
 
 // =====================================================================================================
@@ -574,9 +592,10 @@ hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t s) {
 
 // =====================================================================================================
 // Self-synchronizing slots (flash-comm, abstract): the receiver validates each block's epoch words
-// itself, with no barrier.  A wavefront owns a tile of 256 slots read by two instructions of 128 slots
-// (2 slots = 16 bytes per lane).  A block of B slots covers B/2 aligned lanes of one instruction when
-// B <= 128 (its verdict is a field of that instruction's ballot), or both instructions when B = 256.
+// itself, with no barrier.  A wavefront owns a tile of KI*128 slots, read by KI instructions of 128
+// slots (2 slots = 16 bytes per lane), KI = 2 so that 2*8 slot loads are in flight per lane.  A block of
+// B <= 128 slots covers B/2 aligned lanes of one instruction (its verdict is a field of that
+// instruction's ballot); a block of 256 slots covers two consecutive instructions (the OR of both).
 // =====================================================================================================
 struct LLKArgs {
     const uint64_t* slots[kMaxRanks];
@@ -592,59 +611,61 @@ struct LLKArgs {
 
 template <int B>
 __global__ __launch_bounds__(256) void k_ll_unpack(const LLKArgs a) {
+    constexpr int KI = 2;                      // instructions per wavefront tile
+    constexpr int IB = B <= 128 ? 1 : 2;       // instructions per block
+    constexpr int LB = B <= 128 ? B / 2 : 64;  // lanes of one instruction inside one block
     __shared__ uint32_t s_cnt[2];
     if (threadIdx.x < 2) s_cnt[threadIdx.x] = 0;
     __syncthreads();
-    constexpr int LB = B <= 128 ? B / 2 : 64;  // lanes of one instruction inside one block
     const uint64_t field = LB == 64 ? ~0ull : ((1ull << LB) - 1ull);
     const int lane = threadIdx.x & 63;
-    const int64_t tile = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 256;
-    int64_t slot[2], blk[2];
-    bool active[2], all_valid[2] = {true, true}, leader[2];
+    const int64_t tile = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (128 * KI);
+    int64_t slot[KI], blk[KI];
+    bool active[KI], all_valid[KI], leader[KI];
     // Loads are issued by every lane (a lane-divergent branch around a load would make the compiler
     // wait for it): lanes outside the buffer or in blocks already done read a valid, clamped address and
     // their results are masked.
-    int64_t src[2];
+    int64_t src[KI];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < KI; ++k) {
         slot[k] = tile + k * 128 + 2 * lane;
         const bool inside = slot[k] < a.nslots;
         blk[k] = inside ? slot[k] / B : a.nblk - 1;
         const uint8_t dn = a.done[blk[k]];
         active[k] = inside && dn == 0;
+        all_valid[k] = true;
         src[k] = active[k] ? slot[k] : 0;
-        leader[k] = B <= 128 ? (lane % LB) == 0 : (k == 0 && lane == 0);
+        leader[k] = IB == 1 ? (lane % LB) == 0 : (k % IB == 0 && lane == 0);
     }
-    float acc[2][4];
+    float acc[KI][4];
     uint32_t n_stale = 0;
     const int shift = lane & ~(LB - 1);
     constexpr int RB = 8;  // ranks whose slots are loaded before any is examined (a batch past the last
                            // rank re-reads the last rank's slots, which are ignored)
     for (int r0 = 0; r0 < a.R; r0 += RB) {
-        uint4 sv[RB][2];
+        uint4 sv[RB][KI];
 #pragma unroll
         for (int j = 0; j < RB; ++j)
 #pragma unroll
-            for (int k = 0; k < 2; ++k)
-                sv[j][k] = lds16(a.slots[min(r0 + j, a.R - 1)] + src[k]);  // ranks past R: unused
+            for (int k = 0; k < KI; ++k) sv[j][k] = lds16(a.slots[min(r0 + j, a.R - 1)] + src[k]);
 #pragma unroll
         for (int j = 0; j < RB; ++j) {
             const int r = r0 + j;
             if (r >= a.R) break;  // uniform across the wavefront
-            bool st[2];
+            bool bst[KI];
+            uint64_t bal[KI];
 #pragma unroll
-            for (int k = 0; k < 2; ++k)  // epoch words: the high halves of the two slots
-                st[k] = active[k] && ((sv[j][k].y != a.epoch) | (sv[j][k].w != a.epoch));
-            const uint64_t b0 = __ballot(st[0]), b1 = __ballot(st[1]);
-            bool bst[2];
-            if constexpr (B == 256) {
-                bst[0] = bst[1] = (b0 | b1) != 0;
+            for (int k = 0; k < KI; ++k)  // epoch words: the high halves of the two slots
+                bal[k] = __ballot(active[k] && ((sv[j][k].y != a.epoch) | (sv[j][k].w != a.epoch)));
+            if constexpr (IB == 2) {
+#pragma unroll
+                for (int k = 0; k < KI; k += 2) bst[k] = bst[k + 1] = (bal[k] | bal[k + 1]) != 0;
             } else {
-                bst[0] = ((b0 >> shift) & field) != 0;
-                bst[1] = ((b1 >> shift) & field) != 0;
+#pragma unroll
+                for (int k = 0; k < KI; ++k) bst[k] = ((bal[k] >> shift) & field) != 0;
             }
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
+            for (int k = 0; k < KI; ++k) {
                 if (active[k] && leader[k]) {
                     a.stale[(int64_t)r * a.nblk + blk[k]] = bst[k] ? 1 : 0;
                     n_stale += bst[k] ? 1u : 0u;
@@ -664,7 +685,7 @@ __global__ __launch_bounds__(256) void k_ll_unpack(const LLKArgs a) {
     }
     uint32_t n_pending = 0;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < KI; ++k) {
         if (!active[k]) continue;
         if (all_valid[k]) {
             sts8(a.out + 2 * slot[k], make_uint2(pack_bf16x2(acc[k][0], acc[k][1]), pack_bf16x2(acc[k][2], acc[k][3])));
@@ -690,7 +711,8 @@ hipError_t launch_ll_unpack(const LLParams& p, hipStream_t s) {
     a.stale = p.stale;
     a.done = p.done;
     a.counters = p.counters;
-    const dim3 grid((unsigned)((a.nslots + 1023) / 1024));  // 4 wavefronts x 256 slots per workgroup
+    const int64_t per_wg = 4 * 128 * 2;  // slots per workgroup: 4 wavefronts x 2 instructions x 128
+    const dim3 grid((unsigned)((a.nslots + per_wg - 1) / per_wg));
     switch (p.block_slots) {
         case 32: k_ll_unpack<32><<<grid, 256, 0, s>>>(a); break;
         case 64: k_ll_unpack<64><<<grid, 256, 0, s>>>(a); break;

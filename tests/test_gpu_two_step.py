@@ -213,3 +213,27 @@ def test_two_step_deterministic_repeat(fc):
     for o in outs[1:]:
         for a, b in zip(outs[0], o):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("b1,b2", [(8, 8), (4, 8)])
+def test_reduce_shard_large_shards(fc, orc, b1, b2):
+    """Shards large enough for the 16-element lane chunks (8 shards x 8 ranks x (2^19 + 384) elements, a
+    ragged tail), compared in full."""
+    import torch
+    from gpu_helpers import assert_equal_bits, down
+    R, G = 8, 128
+    L = (1 << 19) + 3 * G
+    ins_host = []
+    for s in range(R):
+        for r in range(R):
+            x = dg.synth_bf16((s, r, b1, 999), L, sigma=1.0, outlier_p=0.001, outlier_factor=50.0)
+            ins_host.append(orc.quantize(x, b1, G))
+    ins = _qmsgs_on_gpu(ins_host)
+    outs = [(torch.empty(L * b2 // 8, dtype=torch.uint8, device="cuda"),
+             torch.empty(L // G, dtype=torch.int32, device="cuda")) for _ in range(R)]
+    fc.fc_reduce_shard(ins, R, L, b1, b2, G, outs)
+    for s in (0, R - 1):
+        chunk = ins_host[s * R:(s + 1) * R]
+        rc, rm = orc.reduce_shard([c for c, _ in chunk], [m for _, m in chunk], L, b1, b2, G)
+        assert_equal_bits(down(outs[s][1], np.uint32), rm, f"meta shard {s}")
+        assert_equal_bits(down(outs[s][0], np.uint8), rc, f"codes shard {s}")
