@@ -44,9 +44,9 @@ def traffic_file(slug):
 
 def kernel_of_call(call, cfg):
     """Substring naming the kernel instantiation a call launches for this workload."""
-    return {"quantize": f"k_quantize<{cfg.bits_rs}, {cfg.group}>",
-            "reduce_shard": f"k_reduce<{cfg.bits_rs}, {cfg.bits_ag}, {cfg.group}>",
-            "gather_norm": f"k_rows<fc::GatherProducer<{cfg.bits_ag}>"}[call]
+    return {"quantize": f"k_quantize<{cfg.bits_rs}, {cfg.group},",
+            "reduce_shard": f"k_reduce<{cfg.bits_rs}, {cfg.bits_ag}, {cfg.group},",
+            "gather_norm": f"k_rows<fc::GatherProducer<{cfg.bits_ag},"}[call]
 
 
 def parse():
