@@ -23,11 +23,13 @@ ARCH = "gfx950"
 SOURCES = ["fc_kernels.hip", "fc_api.cpp"]
 
 # -ffp-contract=off: a*b+c stays two roundings unless written as an explicit fma, which the bit-exact
-# quantization codes depend on.  Packed fp32 instructions are disabled.
+# quantization codes depend on.  Packed fp32 instructions are disabled.  -fno-honor-nans on the kernels:
+# NaN inputs are outside the contract, and without NaNs fminf/fmaxf need no quieting of their operands,
+# which the compiler otherwise inserts before every min/max (and which blocks folding DPP moves).
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-function",
           "-I", INCLUDE, "-I", CSRC]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-fno-gpu-rdc"]
+          "-fno-gpu-rdc", "-fno-honor-nans"]
 
 
 def torch_lib_dir() -> str:

@@ -50,9 +50,11 @@ __device__ __forceinline__ uint32_t f16_ru(float v) {
 // the reduction over that group.
 enum : int { DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140 };
 
+// bound_ctrl is set: every control used here reads a lane of the same row, so it never applies, and with it
+// set the compiler folds the move into the VALU instruction that consumes it (v_min_f32_dpp etc.).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-    return u2f((uint32_t)__builtin_amdgcn_mov_dpp((int)f2u(v), CTRL, 0xF, 0xF, false));
+    return u2f((uint32_t)__builtin_amdgcn_mov_dpp((int)f2u(v), CTRL, 0xF, 0xF, true));
 }
 
 template <int LANES>
@@ -86,25 +88,31 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---- group quantizer --------------------------------------------------------------------------------
-// One lane holds E consecutive elements of a group that spans LPG aligned consecutive lanes.  Produces
-// the lane's packed codes (E*BITS/32 words) and the group's meta word (scale | zero << 16).
-// Codes: v = (x - z) * inv rounded to nearest even by adding 1.5*2^23, which leaves the integer in the low
-// mantissa bits (exact for 0 <= v < 2^22).  For in-contract inputs 0 <= v < qmax + 0.5: z <= x, and
-// s >= (max - z)/qmax up to the roundings of one division and one reciprocal, so v <= qmax*(1 + 2^-21);
-// the definition's clamp to [0, qmax] therefore never changes a code and is not executed.  Codes are
-// packed straight from the low byte (8-bit) or low nibble (4-bit) of the sum's bits, so an
-// out-of-contract input gives a wrong code but never touches a neighbour's bits.
-template <int BITS, int E, int LPG>
-__device__ __forceinline__ void quantize_lane(const float (&v)[E], uint32_t (&w)[E * BITS / 32], uint32_t& meta) {
-    constexpr int QMAX = (1 << BITS) - 1;
-    float lo = v[0], hi = v[0];
+// A group spans LPG aligned consecutive lanes, each holding E consecutive elements.  The quantizer is
+// split into its three steps so that a kernel can run the per-group step once for several groups:
+//   lane_minmax + group_min/max   the group's min and max in every lane of the group;
+//   group_params                  zero point, scale, reciprocal and meta word (scale | zero << 16);
+//   encode_lane                   the lane's packed codes (E * BITS / 32 words).
+// Non-finite inputs are outside the contract (the kernels are compiled assuming no NaN).
+template <int E>
+__device__ __forceinline__ void lane_minmax(const float (&v)[E], float& lo, float& hi) {
+    lo = v[0];
+    hi = v[0];
 #pragma unroll
     for (int i = 1; i < E; ++i) {
         lo = fminf(lo, v[i]);
         hi = fmaxf(hi, v[i]);
     }
-    lo = group_min<LPG>(lo);
-    hi = group_max<LPG>(hi);
+}
+
+struct GroupQ {
+    float z, inv;   // zero point and fp32 reciprocal of the scale (0 for a constant group)
+    uint32_t meta;  // scale | zero << 16
+};
+
+template <int BITS>
+__device__ __forceinline__ GroupQ group_params(float lo, float hi) {
+    constexpr int QMAX = (1 << BITS) - 1;
     lo = lo + 0.0f;  // -0 -> +0
     const uint32_t zb = f16_rd(lo);
     const float z = f16_to_f32(zb);
@@ -116,7 +124,17 @@ __device__ __forceinline__ void quantize_lane(const float (&v)[E], uint32_t (&w)
         sb = f16_ru(t);
         inv = 1.0f / f16_to_f32(sb);
     }
-    meta = sb | (zb << 16);
+    return GroupQ{z, inv, sb | (zb << 16)};
+}
+
+// Codes: v = (x - z) * inv rounded to nearest even by adding 1.5*2^23, which leaves the integer in the low
+// mantissa bits (exact for 0 <= v < 2^22).  For in-contract inputs 0 <= v < qmax + 0.5: z <= x, and
+// s >= (max - z)/qmax up to the roundings of one division and one reciprocal, so v <= qmax*(1 + 2^-21);
+// the definition's clamp to [0, qmax] therefore never changes a code and is not executed.  Codes are
+// packed straight from the low byte (8-bit) or low nibble (4-bit) of the sum's bits, so an
+// out-of-contract input gives a wrong code but never touches a neighbour's bits.
+template <int BITS, int E>
+__device__ __forceinline__ void encode_lane(const float (&v)[E], float z, float inv, uint32_t (&w)[E * BITS / 32]) {
     constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23; its bit pattern 0x4B400000 has a zero low byte
     uint32_t c[E];
 #pragma unroll
@@ -125,20 +143,45 @@ __device__ __forceinline__ void quantize_lane(const float (&v)[E], uint32_t (&w)
         const float q = d * inv;
         c[i] = f2u(q + MAGIC);  // low 8 bits = code
     }
+    // v_perm_b32 selectors: byte i of the result = byte sel_i of {src0:src1} (0x0c = zero); 0x0c0c0400
+    // puts the low bytes of src1 and src0 into bytes 0 and 1, 0x05040100 joins two such half-words.
 #pragma unroll
     for (int k = 0; k < E * BITS / 32; ++k) {
         if constexpr (BITS == 8) {
-            // v_perm_b32 selectors: byte i of the result = byte sel_i of {src0:src1} (0x0c = zero)
             const uint32_t lo = __builtin_amdgcn_perm(c[4 * k + 1], c[4 * k], 0x0c0c0400u);
             const uint32_t hi = __builtin_amdgcn_perm(c[4 * k + 3], c[4 * k + 2], 0x0c0c0400u);
             w[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
         } else {
-            uint32_t x = c[8 * k] & 0xfu;
-#pragma unroll
-            for (int j = 1; j < 8; ++j) x |= (c[8 * k + j] & 0xfu) << (4 * j);
-            w[k] = x;
+            // byte j of ev / od = code 2j / 2j+1; the low nibbles are merged into one word (bfi)
+            const uint32_t* cc = c + 8 * k;
+            const uint32_t ev = __builtin_amdgcn_perm(__builtin_amdgcn_perm(cc[6], cc[4], 0x0c0c0400u),
+                                                      __builtin_amdgcn_perm(cc[2], cc[0], 0x0c0c0400u), 0x05040100u);
+            const uint32_t od = __builtin_amdgcn_perm(__builtin_amdgcn_perm(cc[7], cc[5], 0x0c0c0400u),
+                                                      __builtin_amdgcn_perm(cc[3], cc[1], 0x0c0c0400u), 0x05040100u);
+            w[k] = (ev & 0x0f0f0f0fu) | ((od << 4) & 0xf0f0f0f0u);
         }
     }
+}
+
+// All three steps for one group per lane.
+template <int BITS, int E, int LPG>
+__device__ __forceinline__ void quantize_lane(const float (&v)[E], uint32_t (&w)[E * BITS / 32], uint32_t& meta) {
+    float lo, hi;
+    lane_minmax<E>(v, lo, hi);
+    const GroupQ q = group_params<BITS>(group_min<LPG>(lo), group_max<LPG>(hi));
+    meta = q.meta;
+    encode_lane<BITS, E>(v, q.z, q.inv, w);
+}
+
+// Value of lane J of the caller's LPG-lane group, in every lane of the group.  16-lane groups are DPP rows
+// (row_newbcast, gfx90a and later), 4-lane groups are quads (quad_perm [J,J,J,J]); other widths go
+// through ds_bpermute.
+template <int LPG, int J>
+__device__ __forceinline__ float group_bcast(float v, int lane) {
+    static_assert(J < LPG, "source lane inside the group");
+    if constexpr (LPG == 16) return dpp<0x150 + J>(v);
+    else if constexpr (LPG == 4) return dpp<J | (J << 2) | (J << 4) | (J << 6)>(v);
+    else return __shfl(v, (lane & ~(LPG - 1)) + J, 64);
 }
 
 // ---- dequantization of one packed code word -------------------------------------------------------

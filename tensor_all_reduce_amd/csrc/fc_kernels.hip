@@ -41,55 +41,102 @@ __device__ __forceinline__ void dequant8(const void* p, float s, float z, float 
 
 // =====================================================================================================
 // Group quantization (Flash Communication, summary "Core ideas of the solution": low-bit fine-grained
-// quantization of activations).  Lane-chunk = 8 bf16 (16 bytes); a group of G spans G/8 lanes.  Each
-// lane handles K lane-chunks, 64 chunks apart: K = 4 independent 16-byte loads in flight for large
-// inputs, K = 1 (four times as many workgroups) for small, latency-bound ones.
+// quantization of activations).  Lane-chunk = 8 bf16 (16 bytes); a group of G spans LPG = G/8 lanes.
+// Each lane handles K lane-chunks ("slots"), 64 chunks apart, so a wavefront covers K * 64/LPG groups.
+// Min/max are reduced per slot with DPP; then lane g*LPG + j picks slot j's values of its group g, so the
+// per-group step (zero point, scale, reciprocal: mostly divisions) runs once for all K slots, and its
+// results are broadcast back to the group's lanes.  K = 2 or 4 for large inputs (independent 16-byte
+// loads in flight, per-group work shared), K = 1 for small, latency-bound ones.
 // =====================================================================================================
 template <int BITS, int G, int K>
-__global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ x, int64_t nchunks,
+__global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ x, uint32_t nchunks,
                                                   uint8_t* __restrict__ codes, uint32_t* __restrict__ meta) {
     constexpr int LPG = G / 8;
     constexpr int CB = BITS;  // code bytes per 8-element chunk: 8 or 4
+    static_assert(K == 1 || K == 2 || K == 4, "slot select below");
+    static_assert(K <= LPG, "the K slots of a group are gathered into K of its lanes");
     const int lane = threadIdx.x & 63;
-    const int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 * K) + lane;
+    const uint32_t wbase = (blockIdx.x * 4u + (threadIdx.x >> 6)) * (64u * K);  // < 2^31 (launcher)
     float v[K][8];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         // Chunks past the end: whole groups lie on either side of it, so these lanes recompute the last
         // chunk (keeping their DPP partners' data valid) and store nothing.
-        const int64_t c = min(base + 64 * k, nchunks - 1);
-        unpack_bf16x8(lds16(x + c * 8), v[k]);
+        const uint32_t c = min(wbase + 64u * k + lane, nchunks - 1u);
+        unpack_bf16x8(lds16(x + (size_t)c * 8), v[k]);
+    }
+    float lo[K], hi[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        lane_minmax<8>(v[k], lo[k], hi[k]);
+        lo[k] = group_min<LPG>(lo[k]);
+        hi[k] = group_max<LPG>(hi[k]);
+    }
+    // lane g*LPG + j takes slot j % K of group g
+    float sl = lo[0], sh = hi[0];
+    if constexpr (K >= 2) {
+        const bool b0 = lane & 1;
+        sl = b0 ? lo[1] : lo[0];
+        sh = b0 ? hi[1] : hi[0];
+        if constexpr (K == 4) {
+            const bool b1 = lane & 2;
+            sl = b1 ? (b0 ? lo[3] : lo[2]) : sl;
+            sh = b1 ? (b0 ? hi[3] : hi[2]) : sh;
+        }
+    }
+    const GroupQ q = group_params<BITS>(sl, sh);
+    {
+        const int j = lane % LPG;
+        const uint32_t c0 = wbase + 64u * (j % K) + (lane - j);  // first chunk of the group this lane holds
+        if (j < K && c0 < nchunks) meta[c0 / LPG] = q.meta;
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
+        float z = q.z, inv = q.inv;
+        if constexpr (K > 1) {
+            if (k == 0) { z = group_bcast<LPG, 0>(q.z, lane); inv = group_bcast<LPG, 0>(q.inv, lane); }
+            if (k == 1) { z = group_bcast<LPG, 1>(q.z, lane); inv = group_bcast<LPG, 1>(q.inv, lane); }
+            if constexpr (K == 4) {
+                if (k == 2) { z = group_bcast<LPG, 2>(q.z, lane); inv = group_bcast<LPG, 2>(q.inv, lane); }
+                if (k == 3) { z = group_bcast<LPG, 3>(q.z, lane); inv = group_bcast<LPG, 3>(q.inv, lane); }
+            }
+        }
         uint32_t w[BITS / 4];
-        uint32_t m;
-        quantize_lane<BITS, 8, LPG>(v[k], w, m);
-        const int64_t c = base + 64 * k;
+        encode_lane<BITS, 8>(v[k], z, inv, w);
+        const uint32_t c = wbase + 64u * k + lane;
         if (c < nchunks) {
-            if constexpr (BITS == 8) sts8(codes + c * CB, make_uint2(w[0], w[1]));
-            else sts4(codes + c * CB, w[0]);
-            if ((lane % LPG) == 0) meta[c / LPG] = m;
+            if constexpr (BITS == 8) sts8(codes + (size_t)c * CB, make_uint2(w[0], w[1]));
+            else sts4(codes + (size_t)c * CB, w[0]);
         }
     }
 }
 
 template <int BITS, int K>
 static void quantize_k(const QuantizeParams& p, int64_t nchunks, hipStream_t s) {
-    const dim3 grid((unsigned)((nchunks + 256 * K - 1) / (256 * K)));
-    switch (p.group) {
-        case 32: k_quantize<BITS, 32, K><<<grid, 256, 0, s>>>(p.x, nchunks, p.codes, p.meta); break;
-        case 64: k_quantize<BITS, 64, K><<<grid, 256, 0, s>>>(p.x, nchunks, p.codes, p.meta); break;
-        case 128: k_quantize<BITS, 128, K><<<grid, 256, 0, s>>>(p.x, nchunks, p.codes, p.meta); break;
-        default: k_quantize<BITS, 256, K><<<grid, 256, 0, s>>>(p.x, nchunks, p.codes, p.meta); break;
+    // Pieces of at most 2^30 chunks keep every in-kernel chunk index below 2^31; a piece is a whole
+    // number of groups, so it starts on a group boundary.
+    constexpr int64_t PIECE = (int64_t)1 << 30;
+    for (int64_t c0 = 0; c0 < nchunks; c0 += PIECE) {
+        const uint32_t nc = (uint32_t)(nchunks - c0 < PIECE ? nchunks - c0 : PIECE);
+        const dim3 grid((nc + 256u * K - 1) / (256u * K));
+        const uint16_t* x = p.x + c0 * 8;
+        uint8_t* codes = p.codes + c0 * BITS;
+        uint32_t* meta = p.meta + c0 * 8 / p.group;
+        switch (p.group) {
+            case 32: k_quantize<BITS, 32, K><<<grid, 256, 0, s>>>(x, nc, codes, meta); break;
+            case 64: k_quantize<BITS, 64, K><<<grid, 256, 0, s>>>(x, nc, codes, meta); break;
+            case 128: k_quantize<BITS, 128, K><<<grid, 256, 0, s>>>(x, nc, codes, meta); break;
+            default: k_quantize<BITS, 256, K><<<grid, 256, 0, s>>>(x, nc, codes, meta); break;
+        }
     }
 }
 
 template <int BITS>
 static hipError_t quantize_bits(const QuantizeParams& p, hipStream_t s) {
     const int64_t nchunks = p.n / 8;
-    // below ~4096 workgroups of K = 4 the launch cannot fill the chip's 256 compute units several times
-    if (nchunks >= (int64_t)4096 * 1024) quantize_k<BITS, 4>(p, nchunks, s);
+    // below ~4096 workgroups of K = 4 the launch cannot fill the chip's 256 compute units several times;
+    // above, 4-bit codes run best with K = 2 and 8-bit codes with K = 4 (measured on the 70B prefill batch)
+    if (nchunks >= (int64_t)4096 * 1024) quantize_k<BITS, BITS == 4 ? 2 : 4>(p, nchunks, s);
     else quantize_k<BITS, 1>(p, nchunks, s);
     return hipGetLastError();
 }
