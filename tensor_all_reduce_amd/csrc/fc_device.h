@@ -205,8 +205,11 @@ template <>
 struct Unpack<4> {
     static constexpr int PER_WORD = 8;
     __device__ __forceinline__ static void run(uint32_t w, float s, float z, float* out) {
-        const uint32_t ev = w & 0x0f0f0f0fu;         // byte k = code 2k
-        const uint32_t od = (w >> 4) & 0x0f0f0f0fu;  // byte k = code 2k+1
+        uint32_t ev = w & 0x0f0f0f0fu;         // byte k = code 2k
+        uint32_t od = (w >> 4) & 0x0f0f0f0fu;  // byte k = code 2k+1
+        // Hide the masks' known-zero bits from the optimizer: otherwise it extracts every code with a
+        // bit-field instruction of its own instead of converting the bytes in place (v_cvt_f32_ubyteN).
+        asm("" : "+v"(ev), "+v"(od));
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             out[2 * k] = __builtin_fmaf((float)((ev >> (8 * k)) & 0xffu), s, z);

@@ -147,7 +147,7 @@ hipError_t launch_quantize(const QuantizeParams& p, hipStream_t s) {
 
 // =====================================================================================================
 // Reduce-scatter receive side (two-step all-reduce, step one).  Block row y = shard; lane-chunk = E
-// elements (16: 16 or 8 bytes of codes per rank; 8 for small shards, twice as many lanes in flight);
+// elements (16: 16 or 8 bytes of codes per rank; 8 or 4 for small shards, more lanes in flight);
 // a group spans G/E lanes.  Each lane dequantizes its chunk from every rank's message and folds the
 // values in fp32 in ascending rank order (flash-comm: reduction order fixed, independent of arrival
 // order), then requantizes the fp32 sums for the all-gather step.
@@ -242,7 +242,9 @@ static void reduce_launch_g(const ReduceKArgs& a, int group, dim3 grid, hipStrea
         case 32: k_reduce<B1, B2, 32, E><<<grid, 256, 0, s>>>(a); break;
         case 64: k_reduce<B1, B2, 64, E><<<grid, 256, 0, s>>>(a); break;
         case 128: k_reduce<B1, B2, 128, E><<<grid, 256, 0, s>>>(a); break;
-        default: k_reduce<B1, B2, 256, E><<<grid, 256, 0, s>>>(a); break;
+        default:
+            if constexpr (E >= 8) k_reduce<B1, B2, 256, E><<<grid, 256, 0, s>>>(a);  // 4-element chunks: G <= 128
+            break;
     }
 }
 
@@ -264,10 +266,14 @@ static hipError_t launch_reduce_e(const ReduceParams& p, hipStream_t s) {
         a.R = p.R;
         a.nchunks = nchunks;
         const dim3 grid((unsigned)((nchunks + 255) / 256), (unsigned)ns);
-        if (p.bits_in == 8 && p.bits_out == 8) reduce_launch_g<8, 8, E>(a, p.group, grid, s);
-        else if (p.bits_in == 4 && p.bits_out == 8) reduce_launch_g<4, 8, E>(a, p.group, grid, s);
-        else if (p.bits_in == 8 && p.bits_out == 4) reduce_launch_g<8, 4, E>(a, p.group, grid, s);
-        else reduce_launch_g<4, 4, E>(a, p.group, grid, s);
+        if constexpr (E == 4) {
+            reduce_launch_g<8, 8, 4>(a, p.group, grid, s);  // chosen only for 8-bit codes and G <= 128
+        } else {
+            if (p.bits_in == 8 && p.bits_out == 8) reduce_launch_g<8, 8, E>(a, p.group, grid, s);
+            else if (p.bits_in == 4 && p.bits_out == 8) reduce_launch_g<4, 8, E>(a, p.group, grid, s);
+            else if (p.bits_in == 8 && p.bits_out == 4) reduce_launch_g<8, 4, E>(a, p.group, grid, s);
+            else reduce_launch_g<4, 4, E>(a, p.group, grid, s);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -276,7 +282,11 @@ static hipError_t launch_reduce_e(const ReduceParams& p, hipStream_t s) {
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
     // Fewer than ~1024 workgroups of 16-element chunks leave most compute units idle: halve the chunk.
+    // Below 512 workgroups of 8-element chunks, 8-bit codes in and out halve it again (4 bytes of codes
+    // per lane and rank; a group of up to 128 then spans at most 32 lanes).
     const int64_t wgs16 = (p.L / 16 + 255) / 256 * p.n_shards;
+    const int64_t wgs8 = (p.L / 8 + 255) / 256 * p.n_shards;
+    if (wgs8 < 512 && p.bits_in == 8 && p.bits_out == 8 && p.group <= 128) return launch_reduce_e<4>(p, s);
     return wgs16 < 1024 ? launch_reduce_e<8>(p, s) : launch_reduce_e<16>(p, s);
 }
 
@@ -526,8 +536,17 @@ __global__ __launch_bounds__(BT * RPB) void k_rows(const P p, const NormKArgs na
 struct RowShape {
     int bt, cpt;
 };
-static RowShape row_shape(int64_t hidden) {
+// Lanes per row (bt) and 8-element chunks per lane (cpt).  With no more rows than compute units each
+// row has a workgroup of its own and nothing else to overlap with, so the row is spread over as many
+// lanes as possible (up to 1024, one chunk each); otherwise lanes take several chunks so that
+// workgroups stay small enough to keep several resident per compute unit.
+static RowShape row_shape(int64_t hidden, int64_t rows) {
     const int64_t nch = hidden / 8;
+    if (rows <= 256 && nch > 256) {
+        if (nch <= 512) return {512, 1};
+        if (nch <= 1024) return {1024, 1};
+        if (nch <= 2048) return {1024, 2};
+    }
     if (nch <= 64) return {64, 1};
     if (nch <= 128) return {128, 1};
     if (nch <= 256) return {256, 1};
@@ -543,7 +562,7 @@ static RowShape row_shape(int64_t hidden) {
 // chunks (so that the loads in flight still fit in registers).
 template <class P>
 static hipError_t launch_rows(const P& p, const NormKArgs& na, int64_t rows, int grid, hipStream_t s) {
-    const RowShape rs = row_shape(na.hidden);
+    const RowShape rs = row_shape(na.hidden, rows);
     if (rs.bt <= 256 && (int64_t)grid * 4 <= rows) {
 #define FC_ROWSN(BT, CPT, RPB)                                              \
         if (rs.bt == BT && rs.cpt == CPT) {                                 \
@@ -567,6 +586,9 @@ static hipError_t launch_rows(const P& p, const NormKArgs& na, int64_t rows, int
     FC_ROWS(256, 1)
     FC_ROWS(256, 2)
     FC_ROWS(256, 4)
+    FC_ROWS(512, 1)
+    FC_ROWS(1024, 1)
+    FC_ROWS(1024, 2)
     FC_ROWS(512, 4)
     FC_ROWS(1024, 4)
     FC_ROWS(1024, 8)

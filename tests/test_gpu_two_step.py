@@ -216,13 +216,15 @@ def test_two_step_deterministic_repeat(fc):
 
 
 @pytest.mark.parametrize("b1,b2", [(8, 8), (4, 8)])
-def test_reduce_shard_large_shards(fc, orc, b1, b2):
-    """Shards large enough for the 16-element lane chunks (8 shards x 8 ranks x (2^19 + 384) elements, a
-    ragged tail), compared in full."""
+@pytest.mark.parametrize("log2_L", [17, 19])
+def test_reduce_shard_large_shards(fc, orc, b1, b2, log2_L):
+    """Shards large enough for the 8-element (2^17) and 16-element (2^19) lane chunks of the launcher
+    (8 shards x 8 ranks x (2^k + 384) elements, a ragged tail), compared in full; smaller shards of
+    8-bit codes use 4-element chunks and are covered by the parity test above."""
     import torch
     from gpu_helpers import assert_equal_bits, down
     R, G = 8, 128
-    L = (1 << 19) + 3 * G
+    L = (1 << log2_L) + 3 * G
     ins_host = []
     for s in range(R):
         for r in range(R):
