@@ -113,9 +113,11 @@ fc_status fc_reduce_rmsnorm(const uint16_t* const* parts, int R, int64_t rows, c
  * done[b] == 0: stale[r*nblk + b] = 1 if any slot of rank r's copy carries an epoch word != epoch, else
  * 0; if no rank is stale the block is reduced (fp32 left fold in ascending rank order, bf16 out) and
  * done[b] = 1, otherwise out is left untouched and the block is pending.  Blocks with done[b] != 0 are
- * skipped entirely.  counters[0] += stale (rank, block) pairs seen, counters[1] += pending blocks; the
- * caller zeroes counters.  Calling again after late blocks have been rewritten completes them with the
- * same bits as if they had been on time.  n % (2*block_slots) == 0. */
+ * skipped: nothing of theirs is written (their slots may still be read).  counters[0] += stale
+ * (rank, block) pairs seen, counters[1] += pending blocks, both in one 64-bit atomic add per workgroup:
+ * counters must be 8-byte aligned (FC_E_ALIGN otherwise) and counters[0] must not wrap (a call adds at
+ * most R*nblk < 2^29); the caller zeroes counters.  Calling again after late blocks have been rewritten
+ * completes them with the same bits as if they had been on time.  n % (2*block_slots) == 0. */
 fc_status fc_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, int block_slots, uint32_t epoch,
                               uint16_t* out, uint8_t* stale, uint8_t* done, uint32_t* counters,
                               hipStream_t stream);

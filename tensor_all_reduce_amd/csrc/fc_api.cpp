@@ -229,7 +229,7 @@ fc_status fc_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, in
     if (n % (2 * block_slots) != 0 || n > kMaxElems) return FC_E_SHAPE;
     if (n == 0) return FC_OK;
     if (!slots || !out || !stale || !done || !counters) return FC_E_NULL;
-    if (!aligned(out, 16) || !aligned(counters, 4)) return FC_E_ALIGN;
+    if (!aligned(out, 16) || !aligned(counters, 8)) return FC_E_ALIGN;
     const int64_t nblk = n / 2 / block_slots;
     const Range ro = rng(out, 2 * n), rs = rng(stale, (int64_t)R * nblk), rd = rng(done, nblk), rc = rng(counters, 8);
     if (overlap(ro, rs) || overlap(ro, rd) || overlap(ro, rc) || overlap(rs, rd) || overlap(rs, rc) || overlap(rd, rc))

@@ -662,9 +662,10 @@ hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t s) {
 // =====================================================================================================
 // Self-synchronizing slots (flash-comm, abstract): the receiver validates each block's epoch words
 // itself, with no barrier.  A wavefront owns a tile of KI*128 slots, read by KI instructions of 128
-// slots (2 slots = 16 bytes per lane), KI = 2 so that 2*8 slot loads are in flight per lane.  A block of
-// B <= 128 slots covers B/2 aligned lanes of one instruction (its verdict is a field of that
-// instruction's ballot); a block of 256 slots covers two consecutive instructions (the OR of both).
+// slots (2 slots = 16 bytes per lane), KI = 2 so that 2*8 slot loads are in flight per lane.  Block
+// verdicts and counters are wavefront-uniform and kept on the scalar unit.  A block of B <= 128 slots
+// covers B/2 aligned lanes of one instruction (its verdict is a field of that instruction's ballot); a
+// block of 256 slots covers two consecutive instructions (the OR of both).
 // =====================================================================================================
 struct LLKArgs {
     const uint64_t* slots[kMaxRanks];
@@ -678,95 +679,162 @@ struct LLKArgs {
     uint32_t* counters;
 };
 
+// 1 if x != 0, else 0, for a wavefront-uniform x, on the scalar unit (written out because the compiler
+// turns the comparison into a vector select and a read-back).  s_min_u32 also sets SCC.
+__device__ __forceinline__ uint32_t s_nonzero(uint32_t x) {
+    uint32_t y;
+    asm("s_min_u32 %0, %1, 1" : "=s"(y) : "s"(x) : "scc");
+    return y;
+}
+
+// One rank's slots of a wavefront tile: fold the payload into acc and record, for each block, whether
+// this copy is stale (vs[k][b] bit r, block b of instruction k; wavefront-uniform).
+template <int LB, int KI>
+__device__ __forceinline__ void ll_examine(const uint4 (&q)[KI], int r, uint32_t epoch, const uint64_t (&amask)[KI],
+                                           float (&acc)[KI][4], uint32_t (&vs)[KI][64 / LB]) {
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+        // epoch words: the high halves of the two slots
+        const uint64_t bal = (__ballot(q[k].y != epoch) | __ballot(q[k].w != epoch)) & amask[k];
+        uint32_t lo = (uint32_t)bal, hi = (uint32_t)(bal >> 32);
+        // keep the halves opaque scalars: otherwise "hi != 0" becomes a 64-bit compare on the vector unit
+        asm("" : "+s"(lo), "+s"(hi));
+        if constexpr (LB == 64) {
+            vs[k][0] |= s_nonzero(lo | hi) << r;
+        } else if constexpr (LB == 32) {
+            vs[k][0] |= s_nonzero(lo) << r;
+            vs[k][1] |= s_nonzero(hi) << r;
+        } else {  // LB == 16
+            vs[k][0] |= s_nonzero(lo & 0xffffu) << r;
+            vs[k][1] |= s_nonzero(lo >> 16) << r;
+            vs[k][2] |= s_nonzero(hi & 0xffffu) << r;
+            vs[k][3] |= s_nonzero(hi >> 16) << r;
+        }
+        const float v[4] = {bf16_lo(q[k].x), bf16_hi(q[k].x), bf16_lo(q[k].z), bf16_hi(q[k].z)};
+        if (r == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[k][e] = v[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[k][e] = acc[k][e] + v[e];
+        }
+    }
+}
+
 template <int B>
 __global__ __launch_bounds__(256) void k_ll_unpack(const LLKArgs a) {
     constexpr int KI = 2;                      // instructions per wavefront tile
     constexpr int IB = B <= 128 ? 1 : 2;       // instructions per block
     constexpr int LB = B <= 128 ? B / 2 : 64;  // lanes of one instruction inside one block
-    __shared__ uint32_t s_cnt[2];
-    if (threadIdx.x < 2) s_cnt[threadIdx.x] = 0;
-    __syncthreads();
+    constexpr int RB = 8;                      // ranks whose slots are loaded before any is examined
+    static_assert(KI % IB == 0, "a tile holds whole blocks");
+    static_assert(LB >= kMaxRanks && (LB == 16 || LB == 32 || LB == 64), "one lane per rank writes a block's stale flags");
+    __shared__ uint32_t s_cnt[4][2];  // per wavefront: stale pairs, pending blocks
     const uint64_t field = LB == 64 ? ~0ull : ((1ull << LB) - 1ull);
     const int lane = threadIdx.x & 63;
+    const int bl = lane % LB;  // lane inside its block's lanes
     const int64_t tile = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (128 * KI);
-    int64_t slot[KI], blk[KI];
-    bool active[KI], all_valid[KI], leader[KI];
-    // Loads are issued by every lane (a lane-divergent branch around a load would make the compiler
-    // wait for it): lanes outside the buffer or in blocks already done read a valid, clamped address and
-    // their results are masked.
-    int64_t src[KI];
+    int64_t slot[KI], blk[KI], src[KI];
+    bool inside[KI];
 #pragma unroll
     for (int k = 0; k < KI; ++k) {
         slot[k] = tile + k * 128 + 2 * lane;
-        const bool inside = slot[k] < a.nslots;
-        blk[k] = inside ? slot[k] / B : a.nblk - 1;
-        const uint8_t dn = a.done[blk[k]];
-        active[k] = inside && dn == 0;
-        all_valid[k] = true;
-        src[k] = active[k] ? slot[k] : 0;
-        leader[k] = IB == 1 ? (lane % LB) == 0 : (k % IB == 0 && lane == 0);
+        inside[k] = slot[k] < a.nslots;
+        blk[k] = inside[k] ? slot[k] / B : a.nblk - 1;
+        src[k] = inside[k] ? slot[k] : 0;
     }
+    // The done flags and the first batch of slot loads are issued together, the slots at addresses that do
+    // not depend on the flags, so that their memory latencies overlap (a block already done is read anyway
+    // and ignored).  Loads are never inside a lane-divergent branch: blk is clamped, and a batch past the
+    // last rank re-reads the last rank's slots, which are ignored.
+    uint8_t dn[KI];
+#pragma unroll
+    for (int k = 0; k < KI; ++k) dn[k] = a.done[blk[k]];
+    uint4 sv[RB][KI];
+#pragma unroll
+    for (int j = 0; j < RB; ++j)
+#pragma unroll
+        for (int k = 0; k < KI; ++k) sv[j][k] = lds16(a.slots[min(j, a.R - 1)] + src[k]);
+    bool active[KI];
+    uint64_t amask[KI];  // lanes of blocks to examine (inside the buffer and not done yet)
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+        active[k] = inside[k] && dn[k] == 0;
+        amask[k] = __ballot(active[k]);
+    }
+
+    // Verdicts are wavefront-uniform: vs[k][q] bit r = rank r's copy of block q of instruction k is stale
+    // (NBW = 64/LB blocks per instruction), kept in scalar registers.
+    constexpr int NBW = 64 / LB;
     float acc[KI][4];
-    uint32_t n_stale = 0;
-    const int shift = lane & ~(LB - 1);
-    constexpr int RB = 8;  // ranks whose slots are loaded before any is examined (a batch past the last
-                           // rank re-reads the last rank's slots, which are ignored)
-    for (int r0 = 0; r0 < a.R; r0 += RB) {
-        uint4 sv[RB][KI];
+    uint32_t vs[KI][NBW] = {};
+    const uint32_t epoch = a.epoch;
+#pragma unroll
+    for (int j = 0; j < RB; ++j)
+        if (j < a.R) ll_examine<LB, KI>(sv[j], j, epoch, amask, acc, vs);  // uniform condition
+    for (int r0 = RB; r0 < a.R; r0 += RB) {  // more than 8 ranks
 #pragma unroll
         for (int j = 0; j < RB; ++j)
 #pragma unroll
             for (int k = 0; k < KI; ++k) sv[j][k] = lds16(a.slots[min(r0 + j, a.R - 1)] + src[k]);
 #pragma unroll
-        for (int j = 0; j < RB; ++j) {
-            const int r = r0 + j;
-            if (r >= a.R) break;  // uniform across the wavefront
-            bool bst[KI];
-            uint64_t bal[KI];
-#pragma unroll
-            for (int k = 0; k < KI; ++k)  // epoch words: the high halves of the two slots
-                bal[k] = __ballot(active[k] && ((sv[j][k].y != a.epoch) | (sv[j][k].w != a.epoch)));
-            if constexpr (IB == 2) {
-#pragma unroll
-                for (int k = 0; k < KI; k += 2) bst[k] = bst[k + 1] = (bal[k] | bal[k + 1]) != 0;
-            } else {
-#pragma unroll
-                for (int k = 0; k < KI; ++k) bst[k] = ((bal[k] >> shift) & field) != 0;
-            }
-#pragma unroll
-            for (int k = 0; k < KI; ++k) {
-                if (active[k] && leader[k]) {
-                    a.stale[(int64_t)r * a.nblk + blk[k]] = bst[k] ? 1 : 0;
-                    n_stale += bst[k] ? 1u : 0u;
-                }
-                all_valid[k] = all_valid[k] && !bst[k];
-                const uint4 q = sv[j][k];
-                const float v[4] = {bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.z), bf16_hi(q.z)};
-                if (r == 0) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[k][e] = v[e];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[k][e] = acc[k][e] + v[e];
-                }
-            }
-        }
+        for (int j = 0; j < RB; ++j)
+            if (r0 + j < a.R) ll_examine<LB, KI>(sv[j], r0 + j, epoch, amask, acc, vs);
     }
-    uint32_t n_pending = 0;
 #pragma unroll
     for (int k = 0; k < KI; ++k) {
+        // this lane's block verdict; a two-instruction block (IB = 2) combines both instructions
+        // (selected with masks: a select between array elements would make the array memory-resident)
+        uint32_t sm;
+        if constexpr (IB == 2) {
+            sm = vs[k & ~1][0] | vs[k | 1][0];
+        } else if constexpr (NBW == 1) {
+            sm = vs[k][0];
+        } else {
+            const uint32_t h32 = 0u - (uint32_t)(lane >> 5);  // all ones in the upper half-wavefront
+            if constexpr (NBW == 2) {
+                sm = (vs[k][0] & ~h32) | (vs[k][1] & h32);
+            } else {
+                const uint32_t h16 = 0u - (uint32_t)((lane >> 4) & 1);
+                const uint32_t lo2 = (vs[k][0] & ~h16) | (vs[k][1] & h16);
+                const uint32_t hi2 = (vs[k][2] & ~h16) | (vs[k][3] & h16);
+                sm = (lo2 & ~h32) | (hi2 & h32);
+            }
+        }
         if (!active[k]) continue;
-        if (all_valid[k]) {
+        // lane bl < R of the block writes rank bl's flag (for a two-instruction block, the first one's lanes)
+        if ((IB == 1 || k % 2 == 0) && bl < a.R) a.stale[(int64_t)bl * a.nblk + blk[k]] = (sm >> bl) & 1u;
+        if (sm == 0) {
             sts8(a.out + 2 * slot[k], make_uint2(pack_bf16x2(acc[k][0], acc[k][1]), pack_bf16x2(acc[k][2], acc[k][3])));
-            if (leader[k]) a.done[blk[k]] = 1;
-        } else if (leader[k]) {
-            n_pending += 1;
+            if ((IB == 1 || k % 2 == 0) && bl == 0) a.done[blk[k]] = 1;
         }
     }
-    if (n_stale) atomicAdd(&s_cnt[0], n_stale);
-    if (n_pending) atomicAdd(&s_cnt[1], n_pending);
+    // Counters, from wavefront-uniform values only (scalar unit): block b of instruction k was examined
+    // iff the first lane of its lanes was active.
+    uint32_t n_stale = 0, n_pending = 0;
+#pragma unroll
+    for (int k = 0; k < KI; k += IB) {
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) {
+            const uint32_t v = IB == 2 ? (vs[k][0] | vs[k + 1][0]) : vs[k][b];
+            const uint32_t on = (uint32_t)(amask[k] >> (b * LB)) & 1u;
+            n_pending += on & s_nonzero(v);
+            n_stale += on * (uint32_t)__builtin_popcount(v);
+        }
+    }
+    if (lane == 0) {
+        s_cnt[threadIdx.x >> 6][0] = n_stale;
+        s_cnt[threadIdx.x >> 6][1] = n_pending;
+    }
     __syncthreads();
-    if (threadIdx.x < 2 && s_cnt[threadIdx.x]) atomicAdd(&a.counters[threadIdx.x], s_cnt[threadIdx.x]);
+    // Both counters in one 64-bit atomic per workgroup: device-scope atomics on one address serialize,
+    // and the kernel ends only once the last one is done, so their number matters.  A call adds at most
+    // 2^29 stale pairs, so the low word does not carry.
+    if (threadIdx.x == 0) {
+        const uint32_t st = s_cnt[0][0] + s_cnt[1][0] + s_cnt[2][0] + s_cnt[3][0];
+        const uint32_t pe = s_cnt[0][1] + s_cnt[1][1] + s_cnt[2][1] + s_cnt[3][1];
+        if (st | pe) atomicAdd(reinterpret_cast<unsigned long long*>(a.counters), ((unsigned long long)pe << 32) | st);
+    }
 }
 
 hipError_t launch_ll_unpack(const LLParams& p, hipStream_t s) {

@@ -150,6 +150,7 @@ def test_ll_validation(L):
     assert g(out=None) == L.FC_E_NULL
     assert g(out=A + 0x3000008) == L.FC_E_ALIGN
     assert g(cnt=A + 0x6000002) == L.FC_E_ALIGN
+    assert g(cnt=A + 0x6000004) == L.FC_E_ALIGN    # both counters take one 64-bit atomic: 8-byte aligned
     assert g(done=A + 0x4000000 + 8) == L.FC_E_ARG   # done inside the stale flags
     assert g(out=A + 0x1000000 + 64) == L.FC_E_ARG   # out inside rank 0's slots
     p = L.lib.fc_ll_pack
