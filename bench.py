@@ -9,7 +9,8 @@ buffer set; the sets together exceed twice the 256 MB last-level cache, so input
 value = algorithmic bytes per step / time per step (GB/s).
 
 The other hot-path rows are measured at their own workloads and reported under "rows": the 70B prefill
-two-step path (int4 reduce-scatter / int8 all-gather), the self-synchronizing slot receiver (first pass
+two-step path (int4 reduce-scatter / int8 all-gather), one GPU's real share of both two-step workloads
+(its own quantize, one shard's reduce, the gather), the self-synchronizing slot receiver (first pass
 with late blocks, then the retry), and the unquantized reduce-RMSNorm on two wave-aware half batches,
 alone and overlapped with a bf16 GEMM on a second stream, with a workgroup-cap sweep.
 
@@ -59,7 +60,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", default="all", help="other hot-path rows to measure: all | none | comma list of "
-                                                  "prefill,ll,rmsnorm")
+                                                  "prefill,share,ll,rmsnorm")
     ap.add_argument("--kernel-reps", type=int, default=0, help="graph replays per call timing (0 = auto)")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"))
     return ap.parse_args()
@@ -274,6 +275,67 @@ def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic):
     return dict(ms_step=ms_step, wall=wall, step_bytes=step_bytes, nsets=nsets, per_call=per_call)
 
 
+def bench_share(cx, cfg, steps, warmup, kernel_reps):
+    """One GPU's real share (P mode) of the quantized two-step path, rank 0: its own quantize, its own
+    shard's reduce, the gather + epilogue of all shards.  The peers' chunks of shard 0 and the other
+    shards' all-gather messages are produced once by the whole emulated path and copied into every buffer
+    set outside the timed region (the transport's work).  Timed like the whole path: cold buffer sets,
+    whole steps from a HIP graph, then each call alone."""
+    torch = cx.torch
+    from tensor_all_reduce_amd import bytes_model as bm, datagen as dg
+    from tensor_all_reduce_amd.flash_allreduce import TwoStepAllReduce, TwoStepShare
+    R, T, H, G, b1, b2 = cfg.R, cfg.T, cfg.H, cfg.group, cfg.bits_rs, cfg.bits_ag
+    calls = bm.two_step_share(R, T, H, b1, b2, G)
+    step_bytes = sum(bm.total(v) for v in calls.values())
+    nsets = max(1, math.ceil(2 * MALL_BYTES / min(bm.total(v) for v in calls.values())))
+    whole = TwoStepAllReduce(R, T, H, b1, b2, G, device=cx.dev, parts=cx.up(cx.np.stack(dg.partials(cfg))))
+    whole.quantize()
+    whole.reduce_scatter()
+    res0, gam = cx.up(dg.residual(cfg)), cx.up(dg.gamma(cfg))
+    sets = []
+    for k in range(nsets):
+        sh = TwoStepShare(R, T, H, b1, b2, G, rank=0, device=cx.dev, x=whole.parts[0].clone())
+        for r in range(1, R):
+            c, m = whole.rank_chunk(r, 0)
+            sh.inbox_codes[r].copy_(c)
+            sh.inbox_meta[r].copy_(m)
+        for s in range(1, R):
+            c, m = whole.shard_msg(s)
+            sh.codes2[s].copy_(c)
+            sh.meta2[s].copy_(m)
+        out = torch.empty(cfg.n, dtype=torch.int16, device=cx.dev)
+        rout = torch.empty(cfg.n, dtype=torch.int16, device=cx.dev)
+        res = res0.clone()
+        sets.append((sh, sh.make_norm(gam, out, residual=res, residual_out=rout, eps=cfg.eps), (res, out, rout)))
+    del whole
+    torch.cuda.synchronize()
+
+    def step(k):
+        sh, norm, _ = sets[k]
+        sh.run(norm=norm)
+
+    g_all = cx.graph(step, nsets)
+    for _ in range(max(1, warmup // nsets)):
+        g_all.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // nsets)
+    us_step = cx.time_graph(g_all, reps, nsets)
+    fns = {"quantize": lambda k: sets[k][0].quantize(), "reduce_shard": lambda k: sets[k][0].reduce(),
+           "gather_norm": lambda k: sets[k][0].gather(norm=sets[k][1])}
+    per_call = {}
+    for name, fn in fns.items():
+        us = cx.time_graph(cx.graph(fn, nsets), kernel_reps or max(2, reps), nsets)
+        by = bm.total(calls[name])
+        per_call[name] = {"us": round(us, 3), "bytes": by, "GB/s": round(by / (us * 1e-6) / 1e9, 1)}
+    v = step_bytes / (us_step * 1e-6) / 1e9
+    res = {"workload": cfg.name, "mode": "one GPU's real share (rank 0)", "us_per_step": round(us_step, 3),
+           "bytes_per_step": step_bytes, "GB/s": round(v, 1), "pct_hbm_peak": round(100 * v / HBM_PEAK_GBPS, 2),
+           "buffer_sets": nsets, "steps_timed": reps * nsets, "calls": per_call}
+    del sets, g_all
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_ll(cx):
     """Self-synchronizing slots, 8 ranks x [128, 8192], 64-slot blocks, 2% late (rank, block) copies with the
     seeded mix of wrong epoch words: time the first pass and the retry after the late blocks arrive."""
@@ -464,7 +526,7 @@ def main():
                      "traffic": tr["total"] if tr else None},
         "wall_s": round(main_r["wall"], 3),
     }
-    rows = {"prefill", "ll", "rmsnorm"} if args.rows == "all" else set() if args.rows == "none" else set(
+    rows = {"prefill", "ll", "rmsnorm", "share"} if args.rows == "all" else set() if args.rows == "none" else set(
         args.rows.split(","))
     extra = {}
     if "prefill" in rows and args.config != 3:
@@ -474,6 +536,10 @@ def main():
         extra["prefill_two_step"] = {"workload": c3.name, "us_per_step": round(r3["ms_step"] * 1e3, 2),
                                      "GB/s": round(v3, 1), "pct_hbm_peak": round(100 * v3 / HBM_PEAK_GBPS, 2),
                                      "pct_copy_ceiling": round(100 * v3 / copy_gbps, 2), "calls": r3["per_call"]}
+    if "share" in rows:
+        extra["share_decode"] = bench_share(cx, cfg, args.steps, args.warmup, args.kernel_reps)
+        if args.config != 3:
+            extra["share_prefill"] = bench_share(cx, dg.CONFIGS[3], 30, 5, 0)
     if "ll" in rows:
         extra["self_sync_slots"] = bench_ll(cx)
     if "rmsnorm" in rows:

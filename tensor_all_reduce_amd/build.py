@@ -28,8 +28,11 @@ SOURCES = ["fc_kernels.hip", "fc_api.cpp"]
 # which the compiler otherwise inserts before every min/max (and which blocks folding DPP moves).
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-function",
           "-I", INCLUDE, "-I", CSRC]
+# Kernel-argument preloading (gfx950): the leading kernel arguments (up to 16 dwords) are loaded into
+# registers at dispatch, so a kernel's first memory address does not wait for an argument fetch.  The
+# code object keeps a prologue that fetches them itself where the firmware does not preload.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-fno-gpu-rdc", "-fno-honor-nans"]
+          "-fno-gpu-rdc", "-fno-honor-nans", "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 
 
 def torch_lib_dir() -> str:

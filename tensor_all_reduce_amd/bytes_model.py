@@ -54,3 +54,14 @@ def two_step_whole(R, T, H, bits_rs, bits_ag, group, residual=True, residual_out
     r = reduce_shard(R, L, bits_rs, bits_ag, group, R)
     g = gather(R, L, bits_ag, group, H, plain=False, norm=True, residual=residual, residual_out=residual_out)
     return dict(quantize=q, reduce_shard=r, gather_norm=g)
+
+
+def two_step_share(R, T, H, bits_rs, bits_ag, group, residual=True, residual_out=True) -> dict:
+    """One GPU's real share: its own quantize, its own shard's reduce (R chunks in, one shard out), the
+    gather + epilogue of all R shards."""
+    n = T * H
+    L = n // R
+    q = quantize(n, bits_rs, group)
+    r = reduce_shard(R, L, bits_rs, bits_ag, group, 1)
+    g = gather(R, L, bits_ag, group, H, plain=False, norm=True, residual=residual, residual_out=residual_out)
+    return dict(quantize=q, reduce_shard=r, gather_norm=g)

@@ -152,13 +152,14 @@ hipError_t launch_quantize(const QuantizeParams& p, hipStream_t s) {
 // values in fp32 in ascending rank order (flash-comm: reduction order fixed, independent of arrival
 // order), then requantizes the fp32 sums for the all-gather step.
 // =====================================================================================================
+constexpr int kReduceShards = kMaxReduceIn / kMaxRanks;  // shards per launch
 struct ReduceKArgs {
-    const uint8_t* in_codes[kMaxReduceIn];
-    const uint32_t* in_meta[kMaxReduceIn];
-    uint8_t* out_codes[kMaxRanks];
-    uint32_t* out_meta[kMaxRanks];
-    int R;
-    int64_t nchunks;  // E-element chunks per shard = L / E
+    // [shard in launch][rank]: rank r's chunk of the shard.  Entries r >= R repeat rank R-1, so a table
+    // address depends only on the block index and every pointer arrives in one kernel-argument fetch.
+    const uint8_t* in_codes[kReduceShards][kMaxRanks];
+    const uint32_t* in_meta[kReduceShards][kMaxRanks];
+    uint8_t* out_codes[kReduceShards];
+    uint32_t* out_meta[kReduceShards];
 };
 
 // E codes of B bits: load (E*B/8 bytes) as 32-bit words
@@ -187,31 +188,32 @@ __device__ __forceinline__ void store_codes(uint8_t* p, const uint32_t (&w)[E * 
 }
 
 template <int B1, int B2, int G, int E>
-__global__ __launch_bounds__(256) void k_reduce(const ReduceKArgs a) {
+__global__ __launch_bounds__(256) void k_reduce(const int64_t nchunks, const int R, const ReduceKArgs a) {
     constexpr int LPG = G / E;
     constexpr int IN_W = E * B1 / 32;  // input code words per rank
     constexpr int RB = 8;              // ranks loaded per batch
     const int shard = blockIdx.y;
     const int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const bool valid = c0 < a.nchunks;
-    const int64_t c = valid ? c0 : a.nchunks - 1;  // whole groups lie on either side of the end
+    const bool valid = c0 < nchunks;
+    const int64_t c = valid ? c0 : nchunks - 1;  // whole groups lie on either side of the end
     const int64_t gidx = c / LPG;
-    const int R = a.R;
     float acc[E];
-    for (int r0 = 0; r0 < R; r0 += RB) {
-        uint32_t wv[RB][IN_W];
-        uint32_t mv[RB];
-        // All RB loads are issued unconditionally (ranks past R re-read rank R-1 and are ignored), so no
-        // branch separates them and they are all in flight together.
+    // All RB loads of a batch are issued unconditionally (ranks past R re-read rank R-1 and are ignored),
+    // so no branch separates them and they are all in flight together.  The first batch is outside the
+    // loop: its loads wait for nothing but the kernel arguments (not for R).
+    uint32_t wv[RB][IN_W];
+    uint32_t mv[RB];
+    auto load_batch = [&](int r0) {
 #pragma unroll
         for (int j = 0; j < RB; ++j) {
-            const int t = shard * R + min(r0 + j, R - 1);
-            load_codes<E, B1>(a.in_codes[t] + c * (E * B1 / 8), wv[j]);
-            mv[j] = a.in_meta[t][gidx];
+            load_codes<E, B1>(a.in_codes[shard][r0 + j] + c * (E * B1 / 8), wv[j]);
+            mv[j] = a.in_meta[shard][r0 + j][gidx];
         }
+    };
+    auto fold_batch = [&](int r0) {
 #pragma unroll
         for (int j = 0; j < RB; ++j) {
-            if (r0 + j < R) {
+            if (r0 + j < R) {  // uniform
                 const float sc = meta_scale(mv[j]);
                 const float z = meta_zero(mv[j]);
                 float d[E];
@@ -226,6 +228,12 @@ __global__ __launch_bounds__(256) void k_reduce(const ReduceKArgs a) {
                 }
             }
         }
+    };
+    load_batch(0);
+    fold_batch(0);
+    for (int r0 = RB; r0 < R; r0 += RB) {  // more than 8 ranks
+        load_batch(r0);
+        fold_batch(r0);
     }
     uint32_t w[E * B2 / 32];
     uint32_t m;
@@ -237,13 +245,13 @@ __global__ __launch_bounds__(256) void k_reduce(const ReduceKArgs a) {
 }
 
 template <int B1, int B2, int E>
-static void reduce_launch_g(const ReduceKArgs& a, int group, dim3 grid, hipStream_t s) {
+static void reduce_launch_g(int64_t nchunks, int R, const ReduceKArgs& a, int group, dim3 grid, hipStream_t s) {
     switch (group) {
-        case 32: k_reduce<B1, B2, 32, E><<<grid, 256, 0, s>>>(a); break;
-        case 64: k_reduce<B1, B2, 64, E><<<grid, 256, 0, s>>>(a); break;
-        case 128: k_reduce<B1, B2, 128, E><<<grid, 256, 0, s>>>(a); break;
+        case 32: k_reduce<B1, B2, 32, E><<<grid, 256, 0, s>>>(nchunks, R, a); break;
+        case 64: k_reduce<B1, B2, 64, E><<<grid, 256, 0, s>>>(nchunks, R, a); break;
+        case 128: k_reduce<B1, B2, 128, E><<<grid, 256, 0, s>>>(nchunks, R, a); break;
         default:
-            if constexpr (E >= 8) k_reduce<B1, B2, 256, E><<<grid, 256, 0, s>>>(a);  // 4-element chunks: G <= 128
+            if constexpr (E >= 8) k_reduce<B1, B2, 256, E><<<grid, 256, 0, s>>>(nchunks, R, a);  // 4-element chunks: G <= 128
             break;
     }
 }
@@ -251,28 +259,29 @@ static void reduce_launch_g(const ReduceKArgs& a, int group, dim3 grid, hipStrea
 template <int E>
 static hipError_t launch_reduce_e(const ReduceParams& p, hipStream_t s) {
     const int64_t nchunks = p.L / E;
-    const int per_launch = kMaxReduceIn / p.R;  // shards whose R pointers fit in one argument table
-    for (int s0 = 0; s0 < p.n_shards; s0 += per_launch) {
-        const int ns = (p.n_shards - s0) < per_launch ? (p.n_shards - s0) : per_launch;
+    for (int s0 = 0; s0 < p.n_shards; s0 += kReduceShards) {
+        const int ns = (p.n_shards - s0) < kReduceShards ? (p.n_shards - s0) : kReduceShards;
         ReduceKArgs a;
-        for (int i = 0; i < ns * p.R; ++i) {
-            a.in_codes[i] = p.in_codes[s0 * p.R + i];
-            a.in_meta[i] = p.in_meta[s0 * p.R + i];
+        for (int i = 0; i < ns; ++i) {
+            for (int r = 0; r < kMaxRanks; ++r) {
+                const int t = (s0 + i) * p.R + (r < p.R ? r : p.R - 1);
+                a.in_codes[i][r] = p.in_codes[t];
+                a.in_meta[i][r] = p.in_meta[t];
+            }
         }
         for (int i = 0; i < ns; ++i) {
             a.out_codes[i] = p.out_codes[s0 + i];
             a.out_meta[i] = p.out_meta[s0 + i];
         }
-        a.R = p.R;
-        a.nchunks = nchunks;
         const dim3 grid((unsigned)((nchunks + 255) / 256), (unsigned)ns);
+        const int R = p.R;
         if constexpr (E == 4) {
-            reduce_launch_g<8, 8, 4>(a, p.group, grid, s);  // chosen only for 8-bit codes and G <= 128
+            reduce_launch_g<8, 8, 4>(nchunks, R, a, p.group, grid, s);  // chosen only for 8-bit codes and G <= 128
         } else {
-            if (p.bits_in == 8 && p.bits_out == 8) reduce_launch_g<8, 8, E>(a, p.group, grid, s);
-            else if (p.bits_in == 4 && p.bits_out == 8) reduce_launch_g<4, 8, E>(a, p.group, grid, s);
-            else if (p.bits_in == 8 && p.bits_out == 4) reduce_launch_g<8, 4, E>(a, p.group, grid, s);
-            else reduce_launch_g<4, 4, E>(a, p.group, grid, s);
+            if (p.bits_in == 8 && p.bits_out == 8) reduce_launch_g<8, 8, E>(nchunks, R, a, p.group, grid, s);
+            else if (p.bits_in == 4 && p.bits_out == 8) reduce_launch_g<4, 8, E>(nchunks, R, a, p.group, grid, s);
+            else if (p.bits_in == 8 && p.bits_out == 4) reduce_launch_g<8, 4, E>(nchunks, R, a, p.group, grid, s);
+            else reduce_launch_g<4, 4, E>(nchunks, R, a, p.group, grid, s);
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -336,10 +345,9 @@ struct NormKArgs {
 // table staged in LDS (which costs a barrier before the first load).
 template <int BITS, bool UNIFORM>
 struct GatherProducer {
+    // the leading kernel arguments a0 = L (shard length), a1 = log2(group)
     const uint8_t* codes[kMaxRanks];
     const uint32_t* meta[kMaxRanks];
-    uint32_t L;
-    int log2g;
 
     static constexpr bool kNeedsSync = !UNIFORM;
     struct Shared {
@@ -362,7 +370,7 @@ struct GatherProducer {
             }
         }
     }
-    __device__ __forceinline__ Row begin_row(uint32_t rbase) const {
+    __device__ __forceinline__ Row begin_row(uint32_t rbase, uint32_t L, int) const {
         if constexpr (UNIFORM) {
             const uint32_t s = rbase / L;
             return Row{codes[s], meta[s], s * L};
@@ -375,7 +383,8 @@ struct GatherProducer {
         uint32_t meta;
     };
     // Issue the loads of chunk i (no waiting); decode() turns them into y once they have arrived.
-    __device__ __forceinline__ void fetch(const Shared& sh, const Row& row, uint32_t i, Raw& raw) const {
+    __device__ __forceinline__ void fetch(const Shared& sh, const Row& row, uint32_t i, Raw& raw, uint32_t L,
+                                          int log2g) const {
         const uint8_t* cp;
         const uint32_t* mp;
         uint32_t off;
@@ -406,14 +415,15 @@ struct GatherProducer {
 
 // y from R bf16 partial sums, folded in fp32 in ascending rank order.
 struct BF16ReduceProducer {
+    // the leading kernel argument a0 = R; entries past R repeat rank R-1 (read and ignored), so the table
+    // addresses need no kernel argument
     const uint16_t* parts[kMaxRanks];
-    int R;
 
     static constexpr bool kNeedsSync = false;
     struct Shared {};
     struct Row {};
     __device__ void init(Shared&) const {}
-    __device__ __forceinline__ Row begin_row(uint32_t) const { return Row{}; }
+    __device__ __forceinline__ Row begin_row(uint32_t, uint32_t, int) const { return Row{}; }
     struct Raw {
         float y[8];
     };
@@ -421,16 +431,14 @@ struct BF16ReduceProducer {
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = raw.y[e];
     }
-    __device__ __forceinline__ void fetch(const Shared&, const Row&, uint32_t i, Raw& raw) const {
+    __device__ __forceinline__ void fetch(const Shared&, const Row&, uint32_t i, Raw& raw, uint32_t R, int) const {
         float (&y)[8] = raw.y;
         constexpr int RB = 8;
-        for (int r0 = 0; r0 < R; r0 += RB) {
-            uint4 a[RB];
-#pragma unroll
-            for (int j = 0; j < RB; ++j) a[j] = lds16(parts[min(r0 + j, R - 1)] + i);  // past R: unused
+        uint4 a[RB];
+        auto fold = [&](int r0) {
 #pragma unroll
             for (int j = 0; j < RB; ++j) {
-                if (r0 + j < R) {
+                if (r0 + j < (int)R) {  // uniform
                     float v[8];
                     unpack_bf16x8(a[j], v);
                     if (r0 + j == 0) {
@@ -442,6 +450,15 @@ struct BF16ReduceProducer {
                     }
                 }
             }
+        };
+        // first batch outside the loop: its loads wait for nothing but the kernel arguments
+#pragma unroll
+        for (int j = 0; j < RB; ++j) a[j] = lds16(parts[j] + i);
+        fold(0);
+        for (int r0 = RB; r0 < (int)R; r0 += RB) {
+#pragma unroll
+            for (int j = 0; j < RB; ++j) a[j] = lds16(parts[r0 + j] + i);
+            fold(r0);
         }
     }
 };
@@ -449,8 +466,14 @@ struct BF16ReduceProducer {
 // A workgroup of RPB * BT lanes keeps RPB rows in flight (sub-block j owns row base + j); RPB > 1 is used
 // when the grid is capped well below the number of rows, so that each compute unit still has enough
 // loads in flight.
+// Scalars lead the argument list, so that they arrive preloaded in registers at dispatch (gfx950 kernel
+// argument preloading); only the producer's pointer table is read from the argument segment.
 template <class P, int BT, int CPT, int RPB>
-__global__ __launch_bounds__(BT * RPB) void k_rows(const P p, const NormKArgs na, int64_t rows) {
+__global__ __launch_bounds__(BT * RPB) void k_rows(const int64_t rows, const int hidden, const float eps,
+                                                   const uint16_t* __restrict__ gamma,
+                                                   const uint16_t* __restrict__ residual, uint16_t* out,
+                                                   uint16_t* residual_out, const uint32_t a0, const int a1, const P p) {
+    const NormKArgs na{residual, gamma, eps, hidden, out, residual_out};
     __shared__ float s_part[RPB][BT / 64];
     __shared__ typename P::Shared sh;
     p.init(sh);
@@ -475,7 +498,7 @@ __global__ __launch_bounds__(BT * RPB) void k_rows(const P p, const NormKArgs na
         const int64_t row = row0 + sub;
         const bool has_row = row < rows;
         const uint32_t rbase = (uint32_t)((has_row ? row : rows - 1) * H);
-        const typename P::Row pr = p.begin_row(rbase);
+        const typename P::Row pr = p.begin_row(rbase, a0, a1);
         uint32_t idx[CPT];
         bool ok[CPT];
         typename P::Raw raw[CPT];
@@ -484,7 +507,7 @@ __global__ __launch_bounds__(BT * RPB) void k_rows(const P p, const NormKArgs na
             const int ch = t + k * BT;
             ok[k] = has_row && ch < nch;
             idx[k] = rbase + min(ch, nch - 1) * 8;
-            p.fetch(sh, pr, idx[k], raw[k]);
+            p.fetch(sh, pr, idx[k], raw[k], a0, a1);
         }
         uint4 rres[CPT];
         if (na.residual) {
@@ -520,7 +543,11 @@ __global__ __launch_bounds__(BT * RPB) void k_rows(const P p, const NormKArgs na
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             float gk[8];
-            unpack_bf16x8(kHoistGamma ? g[k] : ld16(na.gamma + (idx[k] - rbase)), gk);
+            uint4 gw = kHoistGamma ? g[k] : ld16(na.gamma + (idx[k] - rbase));
+            // Keeps the unpacking (and the wait for the gamma load) here: hoisted out of the row loop, it
+            // would hold back every load of the first row until gamma has arrived.
+            asm volatile("" : "+v"(gw.x), "+v"(gw.y), "+v"(gw.z), "+v"(gw.w));
+            unpack_bf16x8(gw, gk);
             float o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -561,12 +588,14 @@ static RowShape row_shape(int64_t hidden, int64_t rows) {
 // on rows of at most 256 lanes puts several rows in flight per workgroup: 4, or 2 when each lane holds 4
 // chunks (so that the loads in flight still fit in registers).
 template <class P>
-static hipError_t launch_rows(const P& p, const NormKArgs& na, int64_t rows, int grid, hipStream_t s) {
+static hipError_t launch_rows(const P& p, uint32_t a0, int a1, const NormKArgs& na, int64_t rows, int grid,
+                              hipStream_t s) {
     const RowShape rs = row_shape(na.hidden, rows);
     if (rs.bt <= 256 && (int64_t)grid * 4 <= rows) {
 #define FC_ROWSN(BT, CPT, RPB)                                              \
         if (rs.bt == BT && rs.cpt == CPT) {                                 \
-            k_rows<P, BT, CPT, RPB><<<grid, BT * RPB, 0, s>>>(p, na, rows); \
+            k_rows<P, BT, CPT, RPB><<<grid, BT * RPB, 0, s>>>(rows, na.hidden, na.eps, na.gamma, na.residual, \
+                                                               na.out, na.residual_out, a0, a1, p);       \
             return hipGetLastError();                                      \
         }
         FC_ROWSN(64, 1, 4)
@@ -578,7 +607,8 @@ static hipError_t launch_rows(const P& p, const NormKArgs& na, int64_t rows, int
     }
 #define FC_ROWS(BT, CPT)                                                    \
     if (rs.bt == BT && rs.cpt == CPT) {                                     \
-        k_rows<P, BT, CPT, 1><<<grid, BT, 0, s>>>(p, na, rows);             \
+        k_rows<P, BT, CPT, 1><<<grid, BT, 0, s>>>(rows, na.hidden, na.eps, na.gamma, na.residual, na.out, \
+                                                  na.residual_out, a0, a1, p);                           \
         return hipGetLastError();                                          \
     }
     FC_ROWS(64, 1)
@@ -613,9 +643,7 @@ static hipError_t gather_norm_layout(const GatherParams& p, const NormKArgs& na,
         g.codes[i] = i < p.R ? p.codes[i] : nullptr;
         g.meta[i] = i < p.R ? p.meta[i] : nullptr;
     }
-    g.L = (uint32_t)p.L;
-    g.log2g = ilog2(p.group);
-    return launch_rows(g, na, rows, (int)rows, s);
+    return launch_rows(g, (uint32_t)p.L, ilog2(p.group), na, rows, (int)rows, s);
 }
 
 template <int BITS>
@@ -651,12 +679,11 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t s) {
 
 hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t s) {
     BF16ReduceProducer b;
-    for (int i = 0; i < kMaxRanks; ++i) b.parts[i] = i < p.R ? p.parts[i] : nullptr;
-    b.R = p.R;
+    for (int i = 0; i < kMaxRanks; ++i) b.parts[i] = p.parts[i < p.R ? i : p.R - 1];
     const int64_t rows = p.rows;
     int grid = (int)rows;
     if (p.max_workgroups > 0 && p.max_workgroups < grid) grid = p.max_workgroups;
-    return launch_rows(b, norm_args(p.norm), rows, grid, s);
+    return launch_rows(b, (uint32_t)p.R, 0, norm_args(p.norm), rows, grid, s);
 }
 
 // =====================================================================================================
@@ -667,16 +694,10 @@ hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t s) {
 // covers B/2 aligned lanes of one instruction (its verdict is a field of that instruction's ballot); a
 // block of 256 slots covers two consecutive instructions (the OR of both).
 // =====================================================================================================
-struct LLKArgs {
-    const uint64_t* slots[kMaxRanks];
-    int R;
-    int64_t nslots;
-    int64_t nblk;
-    uint32_t epoch;
-    uint16_t* out;
-    uint8_t* stale;
-    uint8_t* done;
-    uint32_t* counters;
+// Only the slot pointers are read from the argument segment; the scalars lead the kernel's argument
+// list and arrive preloaded in registers.  Entries past R repeat rank R-1 (read and ignored).
+struct LLSlots {
+    const uint64_t* p[kMaxRanks];
 };
 
 // 1 if x != 0, else 0, for a wavefront-uniform x, on the scalar unit (written out because the compiler
@@ -722,7 +743,9 @@ __device__ __forceinline__ void ll_examine(const uint4 (&q)[KI], int r, uint32_t
 }
 
 template <int B>
-__global__ __launch_bounds__(256) void k_ll_unpack(const LLKArgs a) {
+__global__ __launch_bounds__(256) void k_ll_unpack(const int64_t nslots, const int64_t nblk, uint8_t* done,
+                                                   const uint32_t epoch, const int R, uint16_t* out, uint8_t* stale,
+                                                   uint32_t* counters, const LLSlots slots) {
     constexpr int KI = 2;                      // instructions per wavefront tile
     constexpr int IB = B <= 128 ? 1 : 2;       // instructions per block
     constexpr int LB = B <= 128 ? B / 2 : 64;  // lanes of one instruction inside one block
@@ -739,22 +762,22 @@ __global__ __launch_bounds__(256) void k_ll_unpack(const LLKArgs a) {
 #pragma unroll
     for (int k = 0; k < KI; ++k) {
         slot[k] = tile + k * 128 + 2 * lane;
-        inside[k] = slot[k] < a.nslots;
-        blk[k] = inside[k] ? slot[k] / B : a.nblk - 1;
+        inside[k] = slot[k] < nslots;
+        blk[k] = inside[k] ? slot[k] / B : nblk - 1;
         src[k] = inside[k] ? slot[k] : 0;
     }
     // The done flags and the first batch of slot loads are issued together, the slots at addresses that do
     // not depend on the flags, so that their memory latencies overlap (a block already done is read anyway
     // and ignored).  Loads are never inside a lane-divergent branch: blk is clamped, and a batch past the
-    // last rank re-reads the last rank's slots, which are ignored.
+    // last rank re-reads the last rank's slots (the launcher repeats its pointer), which are ignored.
     uint8_t dn[KI];
 #pragma unroll
-    for (int k = 0; k < KI; ++k) dn[k] = a.done[blk[k]];
+    for (int k = 0; k < KI; ++k) dn[k] = done[blk[k]];
     uint4 sv[RB][KI];
 #pragma unroll
     for (int j = 0; j < RB; ++j)
 #pragma unroll
-        for (int k = 0; k < KI; ++k) sv[j][k] = lds16(a.slots[min(j, a.R - 1)] + src[k]);
+        for (int k = 0; k < KI; ++k) sv[j][k] = lds16(slots.p[j] + src[k]);
     bool active[KI];
     uint64_t amask[KI];  // lanes of blocks to examine (inside the buffer and not done yet)
 #pragma unroll
@@ -768,18 +791,17 @@ __global__ __launch_bounds__(256) void k_ll_unpack(const LLKArgs a) {
     constexpr int NBW = 64 / LB;
     float acc[KI][4];
     uint32_t vs[KI][NBW] = {};
-    const uint32_t epoch = a.epoch;
 #pragma unroll
     for (int j = 0; j < RB; ++j)
-        if (j < a.R) ll_examine<LB, KI>(sv[j], j, epoch, amask, acc, vs);  // uniform condition
-    for (int r0 = RB; r0 < a.R; r0 += RB) {  // more than 8 ranks
+        if (j < R) ll_examine<LB, KI>(sv[j], j, epoch, amask, acc, vs);  // uniform condition
+    for (int r0 = RB; r0 < R; r0 += RB) {  // more than 8 ranks
 #pragma unroll
         for (int j = 0; j < RB; ++j)
 #pragma unroll
-            for (int k = 0; k < KI; ++k) sv[j][k] = lds16(a.slots[min(r0 + j, a.R - 1)] + src[k]);
+            for (int k = 0; k < KI; ++k) sv[j][k] = lds16(slots.p[r0 + j] + src[k]);
 #pragma unroll
         for (int j = 0; j < RB; ++j)
-            if (r0 + j < a.R) ll_examine<LB, KI>(sv[j], r0 + j, epoch, amask, acc, vs);
+            if (r0 + j < R) ll_examine<LB, KI>(sv[j], r0 + j, epoch, amask, acc, vs);
     }
 #pragma unroll
     for (int k = 0; k < KI; ++k) {
@@ -803,10 +825,10 @@ __global__ __launch_bounds__(256) void k_ll_unpack(const LLKArgs a) {
         }
         if (!active[k]) continue;
         // lane bl < R of the block writes rank bl's flag (for a two-instruction block, the first one's lanes)
-        if ((IB == 1 || k % 2 == 0) && bl < a.R) a.stale[(int64_t)bl * a.nblk + blk[k]] = (sm >> bl) & 1u;
+        if ((IB == 1 || k % 2 == 0) && bl < R) stale[(int64_t)bl * nblk + blk[k]] = (sm >> bl) & 1u;
         if (sm == 0) {
-            sts8(a.out + 2 * slot[k], make_uint2(pack_bf16x2(acc[k][0], acc[k][1]), pack_bf16x2(acc[k][2], acc[k][3])));
-            if ((IB == 1 || k % 2 == 0) && bl == 0) a.done[blk[k]] = 1;
+            sts8(out + 2 * slot[k], make_uint2(pack_bf16x2(acc[k][0], acc[k][1]), pack_bf16x2(acc[k][2], acc[k][3])));
+            if ((IB == 1 || k % 2 == 0) && bl == 0) done[blk[k]] = 1;
         }
     }
     // Counters, from wavefront-uniform values only (scalar unit): block b of instruction k was examined
@@ -833,29 +855,24 @@ __global__ __launch_bounds__(256) void k_ll_unpack(const LLKArgs a) {
     if (threadIdx.x == 0) {
         const uint32_t st = s_cnt[0][0] + s_cnt[1][0] + s_cnt[2][0] + s_cnt[3][0];
         const uint32_t pe = s_cnt[0][1] + s_cnt[1][1] + s_cnt[2][1] + s_cnt[3][1];
-        if (st | pe) atomicAdd(reinterpret_cast<unsigned long long*>(a.counters), ((unsigned long long)pe << 32) | st);
+        if (st | pe) atomicAdd(reinterpret_cast<unsigned long long*>(counters), ((unsigned long long)pe << 32) | st);
     }
 }
 
 hipError_t launch_ll_unpack(const LLParams& p, hipStream_t s) {
-    LLKArgs a;
-    for (int i = 0; i < kMaxRanks; ++i) a.slots[i] = i < p.R ? p.slots[i] : nullptr;
-    a.R = p.R;
-    a.nslots = p.n / 2;
-    a.nblk = a.nslots / p.block_slots;
-    a.epoch = p.epoch;
-    a.out = p.out;
-    a.stale = p.stale;
-    a.done = p.done;
-    a.counters = p.counters;
+    LLSlots t;
+    for (int i = 0; i < kMaxRanks; ++i) t.p[i] = p.slots[i < p.R ? i : p.R - 1];
+    const int64_t nslots = p.n / 2, nblk = nslots / p.block_slots;
     const int64_t per_wg = 4 * 128 * 2;  // slots per workgroup: 4 wavefronts x 2 instructions x 128
-    const dim3 grid((unsigned)((a.nslots + per_wg - 1) / per_wg));
+    const dim3 grid((unsigned)((nslots + per_wg - 1) / per_wg));
+#define FC_LL(B) k_ll_unpack<B><<<grid, 256, 0, s>>>(nslots, nblk, p.done, p.epoch, p.R, p.out, p.stale, p.counters, t)
     switch (p.block_slots) {
-        case 32: k_ll_unpack<32><<<grid, 256, 0, s>>>(a); break;
-        case 64: k_ll_unpack<64><<<grid, 256, 0, s>>>(a); break;
-        case 128: k_ll_unpack<128><<<grid, 256, 0, s>>>(a); break;
-        default: k_ll_unpack<256><<<grid, 256, 0, s>>>(a); break;
+        case 32: FC_LL(32); break;
+        case 64: FC_LL(64); break;
+        case 128: FC_LL(128); break;
+        default: FC_LL(256); break;
     }
+#undef FC_LL
     return hipGetLastError();
 }
 

@@ -104,6 +104,66 @@ class TwoStepAllReduce:
         self.all_gather(y, norm, stream)
 
 
+class TwoStepShare:
+    """One GPU's real share of the quantized two-step all-reduce (rank `rank` owns shard `rank`).
+
+    Buffers of this rank only: its partial x (bf16 [T*H]), its quantized message, the inbox of its shard
+    (R chunk messages of L elements: rank r's chunk of shard `rank`; this rank's own chunk is read in
+    place from its message), and the R all-gather messages (shard `rank` is written by reduce(); the
+    others arrive from the peers).  On one GPU the caller fills the peers' inbox chunks and gather
+    messages (upload or copy); on a real node the transport would.  Steps: quantize (own partial),
+    reduce (own shard: fixed-order dequant-sum-requant of the R chunks), gather (all R shards, optionally
+    with the residual-add + RMSNorm epilogue)."""
+
+    def __init__(self, R: int, T: int, H: int, bits_rs: int, bits_ag: int, group: int, rank: int = 0,
+                 device="cuda", x: torch.Tensor | None = None):
+        self.R, self.T, self.H, self.b1, self.b2, self.G, self.rank = R, T, H, bits_rs, bits_ag, group, rank
+        n = T * H
+        assert n % R == 0 and 0 <= rank < R
+        self.n, self.L = n, n // R
+        L, dev = self.L, torch.device(device)
+        cb1, cb2, mb = L * bits_rs // 8, L * bits_ag // 8, L // group
+        self.x = x if x is not None else torch.empty(n, dtype=i16, device=dev)
+        self.codes1 = torch.empty(n * bits_rs // 8, dtype=u8, device=dev)   # own message, all R chunks
+        self.meta1 = torch.empty(n // group, dtype=i32, device=dev)
+        self.inbox_codes = torch.empty(R, cb1, dtype=u8, device=dev)        # peers' chunks of own shard
+        self.inbox_meta = torch.empty(R, mb, dtype=i32, device=dev)
+        self.codes2 = torch.empty(R, cb2, dtype=u8, device=dev)             # all-gather messages
+        self.meta2 = torch.empty(R, mb, dtype=i32, device=dev)
+        own = _lib.QMsg(self.codes1.data_ptr() + rank * cb1, self.meta1.data_ptr() + 4 * rank * mb)
+        self._q = _lib.QMsg(self.codes1.data_ptr(), self.meta1.data_ptr())
+        self._rs_in = (_lib.QMsg * R)(*[own if r == rank else
+                                        _lib.QMsg(self.inbox_codes[r].data_ptr(), self.inbox_meta[r].data_ptr())
+                                        for r in range(R)])
+        self._ag = (_lib.QMsg * R)(*[_lib.QMsg(self.codes2[s].data_ptr(), self.meta2[s].data_ptr())
+                                     for s in range(R)])
+        self._rs_out = C.cast(C.addressof(self._ag) + C.sizeof(_lib.QMsg) * rank, C.POINTER(_lib.QMsg))
+
+    def quantize(self, stream=None):
+        st = _lib.lib.fc_quantize(self.x.data_ptr(), self.n, self.b1, self.G, self._q, _lib._stream(stream))
+        _lib._check(st, "fc_quantize")
+
+    def reduce(self, stream=None):
+        st = _lib.lib.fc_reduce_shard(self._rs_in, self.R, self.L, 1, self.b1, self.b2, self.G, self._rs_out,
+                                      _lib._stream(stream))
+        _lib._check(st, "fc_reduce_shard")
+
+    def make_norm(self, gamma, out, residual=None, residual_out=None, eps: float = 1e-5) -> _lib.Norm:
+        return _lib.Norm(residual.data_ptr() if residual is not None else None, gamma.data_ptr(), float(eps), self.H,
+                         out.data_ptr(), residual_out.data_ptr() if residual_out is not None else None)
+
+    def gather(self, y=None, norm: _lib.Norm | None = None, stream=None):
+        st = _lib.lib.fc_gather_dequant(self._ag, self.R, self.L, self.b2, self.G,
+                                        y.data_ptr() if y is not None else None,
+                                        C.byref(norm) if norm is not None else None, _lib._stream(stream))
+        _lib._check(st, "fc_gather_dequant")
+
+    def run(self, y=None, norm=None, stream=None):
+        self.quantize(stream)
+        self.reduce(stream)
+        self.gather(y, norm, stream)
+
+
 class ReduceRMSNorm:
     """Unquantized fused reduce + residual-add + RMSNorm over R bf16 partials [rows, H] (TokenWeave)."""
 

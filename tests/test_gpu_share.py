@@ -1,0 +1,49 @@
+"""One GPU's real share of the two-step all-reduce (rank s: its own quantize, the reduce of shard s, the
+gather + epilogue of all shards) against the oracle's whole all-reduce.  The peers' chunks of shard s and
+the other shards' all-gather messages are the oracle's, as the transport would deliver them."""
+import numpy as np
+import pytest
+
+from tensor_all_reduce_amd import datagen as dg
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fc():
+    from tensor_all_reduce_amd import _lib
+    return _lib
+
+
+@pytest.mark.parametrize("cfg_idx,rank", [(1, 0), (1, 1), (2, 0), (2, 5), (2, 7)])
+def test_share_matches_whole_all_reduce(fc, orc, cfg_idx, rank):
+    import torch
+    from gpu_helpers import assert_bf16_close, assert_equal_bits, down, up
+    from tensor_all_reduce_amd.flash_allreduce import TwoStepShare
+    cfg = dg.CONFIGS[cfg_idx]
+    R, L, G, b1, b2 = cfg.R, cfg.L, cfg.group, cfg.bits_rs, cfg.bits_ag
+    parts = dg.partials(cfg)
+    res, gam = dg.residual(cfg), dg.gamma(cfg)
+    ref = orc.two_step(parts, b1, b2, G, residual=res, gamma=gam, eps=cfg.eps, hidden=cfg.H, plain=False)
+    sh = TwoStepShare(R, cfg.T, cfg.H, b1, b2, G, rank=rank, x=up(parts[rank]))
+    cb1, cb2, mb = L * b1 // 8, L * b2 // 8, L // G
+    for r in range(R):  # what the peers send: their chunk of shard `rank`
+        if r != rank:
+            sh.inbox_codes[r].copy_(up(ref["codes1"][r, rank * cb1:(rank + 1) * cb1]).view(torch.uint8))
+            sh.inbox_meta[r].copy_(up(ref["meta1"][r, rank * mb:(rank + 1) * mb]).view(torch.int32))
+    for s in range(R):  # the other shards' all-gather messages; the own one must come from reduce()
+        if s != rank:
+            sh.codes2[s].copy_(up(ref["codes2"][s * cb2:(s + 1) * cb2]).view(torch.uint8))
+            sh.meta2[s].copy_(up(ref["meta2"][s * mb:(s + 1) * mb]).view(torch.int32))
+        else:
+            sh.codes2[s].zero_()
+            sh.meta2[s].zero_()
+    out = torch.empty(cfg.n, dtype=torch.int16, device="cuda")
+    rout = torch.empty(cfg.n, dtype=torch.int16, device="cuda")
+    sh.run(norm=sh.make_norm(up(gam), out, residual=up(res), residual_out=rout, eps=cfg.eps))
+    assert_equal_bits(down(sh.meta1, np.uint32), ref["meta1"][rank], "own message: meta")
+    assert_equal_bits(down(sh.codes1, np.uint8), ref["codes1"][rank], "own message: codes")
+    assert_equal_bits(down(sh.meta2[rank], np.uint32), ref["meta2"][rank * mb:(rank + 1) * mb], "own shard: meta")
+    assert_equal_bits(down(sh.codes2[rank], np.uint8), ref["codes2"][rank * cb2:(rank + 1) * cb2], "own shard: codes")
+    assert_bf16_close(down(rout, np.uint16), ref["residual_out"], 0, "residual_out")
+    assert_bf16_close(down(out, np.uint16), ref["out"], 2, "out")
