@@ -65,6 +65,13 @@ def lib():
             L.or_reduce_rmsnorm.argtypes = [vp, C.c_int, i64, i64, vp, u16p, C.c_float, u16p, vp, vp]
             L.or_ll_pack.argtypes = [u16p, i64, C.c_int, C.c_uint32, vp, u64p]
             L.or_ll_unpack_reduce.argtypes = [vp, C.c_int, i64, C.c_int, C.c_uint32, u16p, u8p, u8p, u32p]
+            L.or_sumsq_tree.argtypes = [f32p, i64]
+            L.or_sumsq_tree.restype = C.c_float
+            L.or_norm_rows_f32.argtypes = [f32p, vp, u16p, C.c_float, i64, i64, f32p, vp]
+            L.or_reduce_norm_quant.argtypes = [vp, vp, C.c_int, i64, C.c_int, C.c_int, C.c_int, vp, u16p, C.c_float,
+                                               i64, vp, u8p, u32p, vp]
+            L.or_two_step_normfirst.argtypes = [vp, C.c_int, i64, C.c_int, C.c_int, C.c_int, u8p, u32p, u8p, u32p,
+                                                vp, u16p, C.c_float, i64, vp, u16p]
         return _lib
 
 
@@ -183,6 +190,55 @@ def two_step(parts, bits1, bits2, group, residual=None, gamma=None, eps=1e-5, hi
                       hidden if hidden else n, _ptr(out), _ptr(rout))
     return dict(codes1=c1.reshape(R, -1), meta1=m1.reshape(R, -1), codes2=c2, meta2=m2, y=y, out=out,
                 residual_out=rout)
+
+
+# ---- norm before the all-gather ---------------------------------------------------------------------
+def sumsq_tree(h):
+    """Fixed-order sum of squares of one row (8-element chunk folds, pairwise tree over chunks)."""
+    h = _c(h, np.float32).ravel()
+    return np.float32(lib().or_sumsq_tree(h, h.size))
+
+
+def norm_rows_f32(y, residual, gamma, eps, hidden):
+    """fp32 normalized rows o (not rounded) and bf16 residual_out (None without residual)."""
+    y = _c(y, np.float32).ravel()
+    o = np.empty(y.size, np.float32)
+    rout = np.empty(y.size, np.uint16) if residual is not None else None
+    res = _c(residual, np.uint16).ravel() if residual is not None else None
+    lib().or_norm_rows_f32(y, _ptr(res), _c(gamma, np.uint16), eps, y.size // hidden, hidden, o, _ptr(rout))
+    return o, rout
+
+
+def reduce_norm_quant(codes_list, meta_list, L, bits_in, bits_out, group, residual, gamma, eps, hidden):
+    """One shard with the norm first: returns (codes, meta, residual_out, o) of the shard."""
+    R = len(codes_list)
+    cl = [_c(c, np.uint8) for c in codes_list]
+    ml = [_c(m, np.uint32) for m in meta_list]
+    res = _c(residual, np.uint16).ravel() if residual is not None else None
+    rout = np.empty(L, np.uint16) if residual is not None else None
+    oc = np.zeros(L * bits_out // 8, np.uint8)
+    om = np.zeros(L // group, np.uint32)
+    o = np.empty(L, np.float32)
+    lib().or_reduce_norm_quant(_ptr_array(cl), _ptr_array(ml), R, L, bits_in, bits_out, group, _ptr(res),
+                               _c(gamma, np.uint16), eps, hidden, _ptr(rout), oc, om, _ptr(o))
+    return oc, om, rout, o
+
+
+def two_step_normfirst(parts, bits1, bits2, group, residual, gamma, eps, hidden):
+    """The whole two-step all-reduce with the norm applied to each shard before the all-gather."""
+    R = len(parts)
+    ps = [_c(p, np.uint16).ravel() for p in parts]
+    n = ps[0].size
+    c1 = np.zeros(R * n * bits1 // 8, np.uint8)
+    m1 = np.zeros(R * n // group, np.uint32)
+    c2 = np.zeros(n * bits2 // 8, np.uint8)
+    m2 = np.zeros(n // group, np.uint32)
+    res = _c(residual, np.uint16).ravel() if residual is not None else None
+    rout = np.empty(n, np.uint16) if residual is not None else None
+    y = np.empty(n, np.uint16)
+    lib().or_two_step_normfirst(_ptr_array(ps), R, n, bits1, bits2, group, c1, m1, c2, m2, _ptr(res),
+                                _c(gamma, np.uint16), eps, hidden, _ptr(rout), y)
+    return dict(codes1=c1.reshape(R, -1), meta1=m1.reshape(R, -1), codes2=c2, meta2=m2, y=y, residual_out=rout)
 
 
 def reduce_rmsnorm(parts, rows, hidden, residual, gamma, eps, want_y=False):

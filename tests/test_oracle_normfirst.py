@@ -1,0 +1,122 @@
+"""Pins of the oracle's norm-before-all-gather variant (TokenWeave, abstract: the RMSNorm moved relative to
+the communication, applied to each reduce-scattered shard; the normalized rows are then quantized for the
+all-gather).
+
+The row's sum of squares uses a fixed order (8-element chunk folds, then a pairwise tree over the chunks)
+because the normalized values decide integer codes.  The pins: exact sums on integer data, hand-derived
+values where the order changes the result, bit-identity with the standard epilogue whenever every sum
+is exact, a closed form for constant rows, and the quantization round trip."""
+import numpy as np
+import pytest
+
+from tensor_all_reduce_amd import datagen as dg
+
+
+def _bf16(x):
+    """Exact bf16 values of a float array of bf16-representable numbers, as uint16 bits."""
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("H", [8, 24, 1000, 4096, 8192])
+def test_sumsq_tree_exact_on_integers(orc, H):
+    rng = np.random.default_rng(H)
+    h = rng.integers(-16, 17, H).astype(np.float32)   # every partial sum < 2^24: exact in fp32
+    assert orc.sumsq_tree(h) == np.float32(np.sum(h.astype(np.int64) ** 2))
+
+
+def test_sumsq_tree_order():
+    """Chunk partials [2^24, 1, 1, 1]: the pairwise tree gives (2^24 + 1) + (1 + 1) = 2^24 + 2, a sequential
+    fold would give 2^24.  Inside a chunk the fold is sequential: [4096, 1, 1, 1] gives 2^24 (a tree would
+    give 2^24 + 2).  Five chunks [2^24, 1, 1, 1, 1] pad to eight: ((2^24 + 1) + (1 + 1)) + ((1 + 0) + 0)
+    = (2^24 + 2) + 1, a tie rounded to even: 2^24 + 4."""
+    import oracle as orc
+    h = np.zeros(32, np.float32)
+    h[[0, 8, 16, 24]] = [4096, 1, 1, 1]
+    assert orc.sumsq_tree(h) == np.float32(16777218)
+    h = np.zeros(8, np.float32)
+    h[:4] = [4096, 1, 1, 1]
+    assert orc.sumsq_tree(h) == np.float32(16777216)
+    h = np.zeros(40, np.float32)
+    h[[0, 8, 16, 24, 32]] = [4096, 1, 1, 1, 1]
+    assert orc.sumsq_tree(h) == np.float32(16777220)
+
+
+def test_sumsq_tree_close_to_exact_sum(orc):
+    rng = np.random.default_rng(7)
+    for H in (256, 4096, 8192):
+        h = rng.standard_normal(H).astype(np.float32)
+        exact = np.sum(h.astype(np.float64) ** 2)
+        assert abs(float(orc.sumsq_tree(h)) - exact) <= exact * 2.0 ** -18
+
+
+@pytest.mark.parametrize("H", [256, 1024, 4096])
+def test_norm_matches_standard_epilogue_when_sums_are_exact(orc, H):
+    """With integer-valued y and residual every sum of squares is exact in any order, so the fp32
+    normalized values rounded to bf16 must equal the standard epilogue's output bit for bit."""
+    rng = np.random.default_rng(H + 1)
+    rows = 3
+    y = rng.integers(-8, 9, rows * H).astype(np.float32)
+    res = _bf16(rng.integers(-8, 9, rows * H).astype(np.float32))
+    gam = _bf16(rng.integers(1, 5, H).astype(np.float32) * 0.25)
+    o, rout = orc.norm_rows_f32(y, res, gam, 1e-5, H)
+    out_std, rout_std = orc.rmsnorm(y, res, gam, 1e-5, H)
+    assert np.array_equal(orc.f32_to_bf16(o), out_std)
+    assert np.array_equal(rout, rout_std)
+
+
+def test_norm_constant_row_closed_form(orc):
+    """h = c on the whole row: sum of squares H*c^2 exactly (c a power of two), o_j = (c / sqrt(c^2 + eps))
+    * gamma_j up to three fp32 roundings."""
+    H, eps = 4096, 1e-5
+    rng = np.random.default_rng(3)
+    gam = orc.f32_to_bf16(rng.normal(1.0, 0.1, H).astype(np.float32))
+    gf = (gam.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for c in (0.125, 1.0, 4.0, -2.0):
+        o, _ = orc.norm_rows_f32(np.full(H, c, np.float32), None, gam, eps, H)
+        ref = c / np.sqrt(c * c + np.float64(np.float32(eps))) * gf
+        assert np.max(np.abs(o - ref) / np.abs(ref)) <= 4 * 2.0 ** -24
+
+
+@pytest.mark.parametrize("b1,b2", [(8, 8), (4, 8), (8, 4)])
+def test_reduce_norm_quant_round_trip(orc, b1, b2):
+    """The shard's sums, residual-add and norm, then quantization: every dequantized value lies within half
+    a scale of the normalized value (plus the fp32 slack of the quantizer), and residual_out is
+    bf16(sum + residual)."""
+    R, H, G, rows = 4, 512, 128, 3
+    L = rows * H
+    rng = np.random.default_rng(b1 * 10 + b2)
+    msgs = [orc.quantize(dg.synth_bf16((r, b1, 5), L, sigma=1.0, outlier_p=0.01, outlier_factor=20.0), b1, G)
+            for r in range(R)]
+    res = orc.f32_to_bf16(rng.standard_normal(L).astype(np.float32))
+    gam = orc.f32_to_bf16(rng.normal(1.0, 0.1, H).astype(np.float32))
+    codes, meta, rout, o = orc.reduce_norm_quant([c for c, _ in msgs], [m for _, m in msgs], L, b1, b2, G, res,
+                                                 gam, 1e-5, H)
+    _, _, S = orc.reduce_shard([c for c, _ in msgs], [m for _, m in msgs], L, b1, b1, G, want_sum=True)
+    resf = (res.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(rout, orc.f32_to_bf16(S + resf))
+    # the quantizer's input is the fp32 normalized value, not its bf16 rounding
+    qc, qm = orc.quantize(o, b2, G)
+    assert np.array_equal(codes, qc) and np.array_equal(meta, qm)
+    bc, _ = orc.quantize(((orc.f32_to_bf16(o).astype(np.uint32)) << 16).view(np.float32), b2, G)
+    assert not np.array_equal(codes, bc)
+    d = orc.dequant(codes, meta, L, b2, G).astype(np.float64)
+    scale = orc.f16_to_f32((meta & 0xFFFF).astype(np.uint16)).astype(np.float64)
+    s_el = np.repeat(scale, G)
+    assert np.all(np.abs(d - o) <= s_el / 2 + s_el * ((1 << b2) - 1) * 2.0 ** -22)
+
+
+def test_two_step_normfirst_close_to_standard_path(orc):
+    """Norm first, then an 8-bit quantized all-gather, versus the standard path (all-gather of the sums,
+    then the norm): the same rows up to one 8-bit quantization step of the normalized values, and the
+    same residual stream up to the quantization of the sums."""
+    cfg = dg.CONFIGS[1]
+    parts = dg.partials(cfg)
+    res, gam = dg.residual(cfg), dg.gamma(cfg)
+    nf = orc.two_step_normfirst(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, res, gam, cfg.eps, cfg.H)
+    st = orc.two_step(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, residual=res, gamma=gam, eps=cfg.eps,
+                      hidden=cfg.H, plain=False)
+    f = lambda u: (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    o_nf, o_st = f(nf["y"]).reshape(-1, cfg.group), f(st["out"]).reshape(-1, cfg.group)
+    rng_g = o_st.max(axis=1, keepdims=True) - o_st.min(axis=1, keepdims=True)
+    assert np.all(np.abs(o_nf - o_st) <= rng_g / 255 * 2 + np.abs(o_st) * 2.0 ** -6)
+    assert np.max(np.abs(f(nf["residual_out"]) - f(st["residual_out"]))) < 0.1
