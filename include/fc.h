@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define FC_ABI_VERSION 1
+#define FC_ABI_VERSION 2
 
 typedef enum {
     FC_OK = 0,
@@ -90,6 +90,21 @@ fc_status fc_quantize(const uint16_t* x, int64_t n, int bits, int group, fc_qmsg
  * exceeds 128. */
 fc_status fc_reduce_shard(const fc_qmsg* in, int R, int64_t L, int n_shards, int bits_in, int bits_out,
                           int group, const fc_qmsg* out, hipStream_t stream);
+
+/* Reduce-scatter receive side with the norm before the all-gather (TokenWeave, abstract: the RMSNorm
+ * fused with the all-reduce and moved relative to the communication, so each rank normalizes only its
+ * 1/R of the rows).  in, R, L, n_shards, bits_in, group as for fc_reduce_shard; every shard holds whole
+ * rows: L % norm->hidden == 0 and norm->hidden % group == 0.  For each shard: S = the fixed-order fp32
+ * fold of the R dequantized chunks; h = S + residual; residual_out = bf16(h); the rows of h are
+ * normalized in fp32, o = (h * (1/sqrt(sum(h^2)/hidden + eps))) * gamma, and o is quantized at bits_out
+ * into out[shard] (the all-gather payload; fc_gather_dequant with y gives the normalized bf16 rows).
+ * The sum of squares has a fixed order, because o decides integer codes: per 8-element chunk a left
+ * fold of h*h, then a pairwise tree over the chunks of the row (the chunk count padded to a power of
+ * two with zeros).  norm->residual and norm->residual_out (bf16 [n_shards*L], shard i's rows at i*L;
+ * either may be NULL; they may alias exactly) and norm->gamma, eps, hidden as for the other epilogues;
+ * norm->out must be NULL (FC_E_ARG otherwise).  Outputs may not overlap inputs or each other. */
+fc_status fc_reduce_shard_norm(const fc_qmsg* in, int R, int64_t L, int n_shards, int bits_in, int bits_out,
+                               int group, const fc_norm* norm, const fc_qmsg* out, hipStream_t stream);
 
 /* All-gather receive side (Flash Communication, two-step all-reduce, step two).  shards[s] [host array,
  * R entries] holds elements [s*L, (s+1)*L) of the flat [rows, hidden] result.  Each element is

@@ -66,12 +66,14 @@ def _load():
     lib.fc_abi_version.restype = i32
     lib.fc_quantize.argtypes = [vp, i64, i32, i32, QMsg, vp]
     lib.fc_reduce_shard.argtypes = [C.POINTER(QMsg), i32, i64, i32, i32, i32, i32, C.POINTER(QMsg), vp]
+    lib.fc_reduce_shard_norm.argtypes = [C.POINTER(QMsg), i32, i64, i32, i32, i32, i32, C.POINTER(Norm),
+                                         C.POINTER(QMsg), vp]
     lib.fc_gather_dequant.argtypes = [C.POINTER(QMsg), i32, i64, i32, i32, vp, C.POINTER(Norm), vp]
     lib.fc_reduce_rmsnorm.argtypes = [C.POINTER(vp), i32, i64, C.POINTER(Norm), i32, vp]
     lib.fc_ll_unpack_reduce.argtypes = [C.POINTER(vp), i32, i64, i32, u32, vp, vp, vp, vp, vp]
     lib.fc_ll_pack.argtypes = [vp, i64, i32, u32, vp, vp, vp]
     lib.fc_copy.argtypes = [vp, vp, i64, vp]
-    for f in ("fc_quantize", "fc_reduce_shard", "fc_gather_dequant", "fc_reduce_rmsnorm", "fc_ll_unpack_reduce",
+    for f in ("fc_quantize", "fc_reduce_shard", "fc_reduce_shard_norm", "fc_gather_dequant", "fc_reduce_rmsnorm", "fc_ll_unpack_reduce",
               "fc_ll_pack", "fc_copy"):
         getattr(lib, f).restype = i32
     return lib
@@ -111,7 +113,7 @@ def _norm(norm) -> Norm | None:
     if norm is None:
         return None
     return Norm(_ptr(norm.get("residual")), _ptr(norm["gamma"]), float(norm.get("eps", 1e-5)), int(norm["hidden"]),
-                _ptr(norm["out"]), _ptr(norm.get("residual_out")))
+                _ptr(norm.get("out")), _ptr(norm.get("residual_out")))
 
 
 def fc_quantize(x, bits: int, group: int, codes, meta, n: int | None = None, stream=None) -> None:
@@ -127,6 +129,19 @@ def fc_reduce_shard(inputs, R: int, L: int, bits_in: int, bits_out: int, group: 
     outs = (QMsg * n_shards)(*[_qmsg(m) for m in outputs])
     _check(_lib.fc_reduce_shard(ins, R, L, n_shards, bits_in, bits_out, group, outs, _stream(stream)),
            "fc_reduce_shard")
+
+
+def fc_reduce_shard_norm(inputs, R: int, L: int, bits_in: int, bits_out: int, group: int, norm: dict, outputs,
+                         stream=None) -> None:
+    """As fc_reduce_shard, with the residual-add + RMSNorm applied to the shards' rows before the
+    normalized rows are quantized into `outputs`.  norm: dict(residual, gamma, eps, hidden, residual_out)
+    over the n_shards*L elements of the shards, without "out"."""
+    n_shards = len(outputs)
+    ins = (QMsg * len(inputs))(*[_qmsg(m) for m in inputs])
+    outs = (QMsg * n_shards)(*[_qmsg(m) for m in outputs])
+    nm = _norm(norm)
+    _check(_lib.fc_reduce_shard_norm(ins, R, L, n_shards, bits_in, bits_out, group, C.byref(nm), outs,
+                                     _stream(stream)), "fc_reduce_shard_norm")
 
 
 def fc_gather_dequant(shards, L: int, bits: int, group: int, y=None, norm: dict | None = None, stream=None) -> None:

@@ -145,6 +145,87 @@ fc_status fc_reduce_shard(const fc_qmsg* in, int R, int64_t L, int n_shards, int
     return FC_OK;
 }
 
+fc_status fc_reduce_shard_norm(const fc_qmsg* in, int R, int64_t L, int n_shards, int bits_in, int bits_out,
+                               int group, const fc_norm* norm, const fc_qmsg* out, hipStream_t stream) {
+    if (R < 1 || R > fc::kMaxRanks || n_shards < 1 || n_shards > fc::kMaxRanks || !valid_bits(bits_in) ||
+        !valid_bits(bits_out) || !valid_group(group) || L < 0)
+        return FC_E_ARG;
+    if (!norm) return FC_E_NULL;
+    if (!norm->gamma) return FC_E_NULL;
+    if (norm->out) return FC_E_ARG;  // the normalized rows go to the quantized messages
+    if (!(norm->eps > 0.0f) || norm->eps != norm->eps || norm->eps > 3.0e38f) return FC_E_ARG;
+    const int64_t H = norm->hidden;
+    if (H <= 0 || H % 8 != 0 || H > kMaxHidden || H % group != 0) return FC_E_SHAPE;
+    if (L % group != 0 || L % H != 0 || L > kMaxElems) return FC_E_SHAPE;
+    if (L == 0) return FC_OK;
+    if (!in || !out) return FC_E_NULL;
+    if (!aligned(norm->gamma, 16) || (norm->residual && !aligned(norm->residual, 16)) ||
+        (norm->residual_out && !aligned(norm->residual_out, 16)))
+        return FC_E_ALIGN;
+    const int64_t cin = L * bits_in / 8, min_ = 4 * (L / group), cout = L * bits_out / 8;
+    const int64_t nb = 2 * (int64_t)n_shards * L;  // bytes of the shards' residual rows
+    for (int i = 0; i < n_shards * R; ++i) {
+        if (!in[i].codes || !in[i].meta) return FC_E_NULL;
+        if (!aligned(in[i].codes, 16) || !aligned(in[i].meta, 4)) return FC_E_ALIGN;
+    }
+    for (int s = 0; s < n_shards; ++s) {
+        if (!out[s].codes || !out[s].meta) return FC_E_NULL;
+        if (!aligned(out[s].codes, 16) || !aligned(out[s].meta, 4)) return FC_E_ALIGN;
+    }
+    // outputs: the n_shards messages and residual_out; none may overlap another output or any input
+    const Range g = rng(norm->gamma, 2 * H);
+    const Range ro = norm->residual_out ? rng(norm->residual_out, nb) : Range{0, 0};
+    if (norm->residual_out) {
+        if (overlap(ro, g)) return FC_E_ARG;
+        if (norm->residual && norm->residual != norm->residual_out && overlap(ro, rng(norm->residual, nb)))
+            return FC_E_ARG;
+    }
+    for (int s = 0; s < n_shards; ++s) {
+        const Range oc = rng(out[s].codes, cout), om = rng(out[s].meta, min_);
+        if (overlap(oc, om) || overlap(oc, g) || overlap(om, g) || overlap(oc, ro) || overlap(om, ro)) return FC_E_ARG;
+        if (norm->residual && (overlap(oc, rng(norm->residual, nb)) || overlap(om, rng(norm->residual, nb))))
+            return FC_E_ARG;
+        for (int t = s + 1; t < n_shards; ++t)
+            if (overlap(oc, rng(out[t].codes, cout)) || overlap(oc, rng(out[t].meta, min_)) ||
+                overlap(om, rng(out[t].codes, cout)) || overlap(om, rng(out[t].meta, min_)))
+                return FC_E_ARG;
+    }
+    for (int i = 0; i < n_shards * R; ++i) {
+        const Range ic = rng(in[i].codes, cin), im = rng(in[i].meta, min_);
+        if (overlap(ro, ic) || overlap(ro, im)) return FC_E_ARG;
+        for (int s = 0; s < n_shards; ++s) {
+            const Range oc = rng(out[s].codes, cout), om = rng(out[s].meta, min_);
+            if (overlap(oc, ic) || overlap(oc, im) || overlap(om, ic) || overlap(om, im)) return FC_E_ARG;
+        }
+    }
+    fc::ReduceNormQParams q;
+    q.norm = norm_params(norm);
+    const int per_launch = fc::kMaxReduceIn / R;
+    for (int s0 = 0; s0 < n_shards; s0 += per_launch) {
+        const int ns = (n_shards - s0) < per_launch ? (n_shards - s0) : per_launch;
+        fc::ReduceParams& p = q.rs;
+        for (int i = 0; i < ns * R; ++i) {
+            p.in_codes[i] = in[s0 * R + i].codes;
+            p.in_meta[i] = in[s0 * R + i].meta;
+        }
+        for (int i = 0; i < ns; ++i) {
+            p.out_codes[i] = out[s0 + i].codes;
+            p.out_meta[i] = out[s0 + i].meta;
+        }
+        p.R = R;
+        p.n_shards = ns;
+        p.L = L;
+        p.bits_in = bits_in;
+        p.bits_out = bits_out;
+        p.group = group;
+        q.norm.residual = norm->residual ? norm->residual + (int64_t)s0 * L : nullptr;
+        q.norm.residual_out = norm->residual_out ? norm->residual_out + (int64_t)s0 * L : nullptr;
+        const fc_status st = launched(fc::launch_reduce_norm(q, stream));
+        if (st != FC_OK) return st;
+    }
+    return FC_OK;
+}
+
 fc_status fc_gather_dequant(const fc_qmsg* shards, int R, int64_t L, int bits, int group, uint16_t* y,
                             const fc_norm* norm, hipStream_t stream) {
     if (R < 1 || R > fc::kMaxRanks || !valid_bits(bits) || !valid_group(group) || L < 0) return FC_E_ARG;

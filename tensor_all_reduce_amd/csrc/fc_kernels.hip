@@ -350,6 +350,7 @@ struct GatherProducer {
     const uint32_t* meta[kMaxRanks];
 
     static constexpr bool kNeedsSync = !UNIFORM;
+    static constexpr int kOutBits = 0;  // bf16 output rows
     struct Shared {
         const uint8_t* codes[kMaxRanks];
         const uint32_t* meta[kMaxRanks];
@@ -402,7 +403,7 @@ struct GatherProducer {
         if constexpr (BITS == 8) raw.codes = lds8(cp + off);
         else raw.codes = make_uint2(lds4(cp + off / 2), 0u);
     }
-    __device__ __forceinline__ void decode(const Raw& raw, float (&y)[8]) const {
+    __device__ __forceinline__ void decode(const Raw& raw, float (&y)[8], const Row&, uint32_t, uint32_t, int) const {
         const float sc = meta_scale(raw.meta), z = meta_zero(raw.meta);
         if constexpr (BITS == 8) {
             Unpack<8>::run(raw.codes.x, sc, z, y);
@@ -420,6 +421,7 @@ struct BF16ReduceProducer {
     const uint16_t* parts[kMaxRanks];
 
     static constexpr bool kNeedsSync = false;
+    static constexpr int kOutBits = 0;  // bf16 output rows
     struct Shared {};
     struct Row {};
     __device__ void init(Shared&) const {}
@@ -427,7 +429,7 @@ struct BF16ReduceProducer {
     struct Raw {
         float y[8];
     };
-    __device__ __forceinline__ void decode(const Raw& raw, float (&y)[8]) const {
+    __device__ __forceinline__ void decode(const Raw& raw, float (&y)[8], const Row&, uint32_t, uint32_t, int) const {
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = raw.y[e];
     }
@@ -463,6 +465,106 @@ struct BF16ReduceProducer {
     }
 };
 
+// y from the R quantized chunks of the row's shard (the reduce-scatter receive side), folded in fp32 in
+// ascending rank order; the row's normalized values are quantized into the shard's all-gather message
+// (the norm applied before the all-gather, TokenWeave, abstract).  Leading kernel arguments: a0 = L
+// (shard length, a multiple of the row length), a1 = log2(group) | R << 8.  Pointer tables: [shard in
+// launch][rank], entries past R repeat rank R-1.
+constexpr int kNormShards = 8;  // shards per launch
+template <int B1, int B2>
+struct QReduceProducer {
+    static constexpr bool kNeedsSync = false;
+    static constexpr int kOutBits = B2;
+    const uint8_t* codes[kNormShards][kMaxRanks];
+    const uint32_t* meta[kNormShards][kMaxRanks];
+    uint8_t* out_codes[kNormShards];
+    uint32_t* out_meta[kNormShards];
+    struct Shared {};
+    struct Row {
+        uint32_t s, base;  // shard in the launch, flat index of its first element
+    };
+    __device__ void init(Shared&) const {}
+    __device__ __forceinline__ Row begin_row(uint32_t rbase, uint32_t L, int) const {
+        const uint32_t s = rbase / L;
+        return Row{s, s * L};
+    }
+    static constexpr int RB = 8;  // ranks whose loads are issued by fetch()
+    struct Raw {
+        uint32_t c[RB][B1 / 4];  // the chunk's 8 codes of rank j
+        uint32_t m[RB];
+    };
+    __device__ __forceinline__ void load(const Row& row, uint32_t i, int r0, int log2g, Raw& raw) const {
+        const uint32_t off = i - row.base;
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+            raw.m[j] = meta[row.s][r0 + j][off >> log2g];
+            if constexpr (B1 == 8) {
+                const uint2 u = lds8(codes[row.s][r0 + j] + off);
+                raw.c[j][0] = u.x;
+                raw.c[j][1] = u.y;
+            } else {
+                raw.c[j][0] = lds4(codes[row.s][r0 + j] + off / 2);
+            }
+        }
+    }
+    __device__ __forceinline__ void fetch(const Shared&, const Row& row, uint32_t i, Raw& raw, uint32_t, int a1) const {
+        load(row, i, 0, a1 & 0xff, raw);
+    }
+    __device__ __forceinline__ void fold(const Raw& raw, int r0, int R, float (&y)[8]) const {
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+            if (r0 + j < R) {  // uniform
+                float d[8];
+#pragma unroll
+                for (int w = 0; w < B1 / 4; ++w)
+                    Unpack<B1>::run(raw.c[j][w], meta_scale(raw.m[j]), meta_zero(raw.m[j]), d + w * Unpack<B1>::PER_WORD);
+                if (r0 + j == 0) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] = d[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] = y[e] + d[e];
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void decode(const Raw& raw, float (&y)[8], const Row& row, uint32_t i, uint32_t,
+                                           int a1) const {
+        const int R = a1 >> 8;
+        fold(raw, 0, R, y);
+        for (int r0 = RB; r0 < R; r0 += RB) {  // more than 8 ranks: the next batch is loaded here
+            Raw more;
+            load(row, i, r0, a1 & 0xff, more);
+            fold(more, r0, R, y);
+        }
+    }
+    // Quantize this lane's 8 normalized values (a group of G spans G/8 aligned lanes) and store them.
+    template <int LPG>
+    __device__ __forceinline__ void quantize_store(const Row& row, uint32_t i, const float (&o)[8], bool ok,
+                                                   bool leader, int log2g) const {
+        uint32_t w[B2 / 4];
+        uint32_t m;
+        quantize_lane<B2, 8, LPG>(o, w, m);
+        if (ok) {
+            const uint32_t off = i - row.base;
+            if constexpr (B2 == 8) sts8(out_codes[row.s] + off, make_uint2(w[0], w[1]));
+            else sts4(out_codes[row.s] + off / 2, w[0]);
+            if (leader) out_meta[row.s][off >> log2g] = m;
+        }
+    }
+    // t = the lane's index inside its row; groups never straddle a row end (hidden % group == 0).
+    __device__ __forceinline__ void store(const Row& row, uint32_t i, const float (&o)[8], bool ok, int t,
+                                          int a1) const {
+        const int log2g = a1 & 0xff;
+        switch (log2g) {  // uniform
+            case 5: quantize_store<4>(row, i, o, ok, (t & 3) == 0, log2g); break;
+            case 6: quantize_store<8>(row, i, o, ok, (t & 7) == 0, log2g); break;
+            case 7: quantize_store<16>(row, i, o, ok, (t & 15) == 0, log2g); break;
+            default: quantize_store<32>(row, i, o, ok, (t & 31) == 0, log2g); break;
+        }
+    }
+};
+
 // A workgroup of RPB * BT lanes keeps RPB rows in flight (sub-block j owns row base + j); RPB > 1 is used
 // when the grid is capped well below the number of rows, so that each compute unit still has enough
 // loads in flight.
@@ -474,7 +576,13 @@ __global__ __launch_bounds__(BT * RPB) void k_rows(const int64_t rows, const int
                                                    const uint16_t* __restrict__ residual, uint16_t* out,
                                                    uint16_t* residual_out, const uint32_t a0, const int a1, const P p) {
     const NormKArgs na{residual, gamma, eps, hidden, out, residual_out};
-    __shared__ float s_part[RPB][BT / 64];
+    // Quantized output (the norm before the all-gather): the normalized values decide integer codes, so
+    // the row's sum of squares follows a fixed order, the same for every launch shape: chunk partials
+    // (left fold of h*h over the chunk's 8 elements), then a pairwise tree over the chunk index
+    // c = t + k*BT, i.e. over the lane inside the wavefront (the DPP butterfly is that tree), over the
+    // wavefronts, then over k.  bf16 output: any order (fused multiply-adds, lane-serial over k).
+    constexpr bool kTreeSum = P::kOutBits != 0;
+    __shared__ float s_part[RPB][kTreeSum ? CPT : 1][BT / 64];
     __shared__ typename P::Shared sh;
     p.init(sh);
     if constexpr (P::kNeedsSync) __syncthreads();
@@ -516,9 +624,10 @@ __global__ __launch_bounds__(BT * RPB) void k_rows(const int64_t rows, const int
         }
         float h[CPT][8];
         float ss = 0.0f;
+        float pk[CPT];
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
-            p.decode(raw[k], h[k]);
+            p.decode(raw[k], h[k], pr, idx[k], a0, a1);
             if (na.residual) {
                 float rv[8];
                 unpack_bf16x8(rres[k], rv);
@@ -526,17 +635,53 @@ __global__ __launch_bounds__(BT * RPB) void k_rows(const int64_t rows, const int
                 for (int e = 0; e < 8; ++e) h[k][e] = h[k][e] + rv[e];
             }
             if (na.residual_out && ok[k]) sts16(na.residual_out + idx[k], pack_bf16x8(h[k]));
-            float sk = 0.0f;
+            if constexpr (kTreeSum) {
+                float q = h[k][0] * h[k][0];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sk = __builtin_fmaf(h[k][e], h[k][e], sk);
-            ss += ok[k] ? sk : 0.0f;
+                for (int e = 1; e < 8; ++e) {
+                    const float sq = h[k][e] * h[k][e];
+                    q = q + sq;
+                }
+                pk[k] = ok[k] ? q : 0.0f;
+            } else {
+                float sk = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sk = __builtin_fmaf(h[k][e], h[k][e], sk);
+                ss += ok[k] ? sk : 0.0f;
+            }
         }
-        const float ws = wave_sum(ss);
-        if (lane == 0) s_part[sub][wid] = ws;
-        __syncthreads();
         float tot = 0.0f;
+        if constexpr (kTreeSum) {
 #pragma unroll
-        for (int w = 0; w < BT / 64; ++w) tot += s_part[sub][w];
+            for (int k = 0; k < CPT; ++k) {
+                const float ws = wave_sum(pk[k]);
+                if (lane == 0) s_part[sub][k][wid] = ws;
+            }
+            __syncthreads();
+            float lv[CPT];
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) {
+                float a[BT / 64];
+#pragma unroll
+                for (int w = 0; w < BT / 64; ++w) a[w] = s_part[sub][k][w];
+#pragma unroll
+                for (int width = BT / 64; width > 1; width /= 2)
+#pragma unroll
+                    for (int j = 0; j < width / 2; ++j) a[j] = a[2 * j] + a[2 * j + 1];
+                lv[k] = a[0];
+            }
+#pragma unroll
+            for (int width = CPT; width > 1; width /= 2)
+#pragma unroll
+                for (int j = 0; j < width / 2; ++j) lv[j] = lv[2 * j] + lv[2 * j + 1];
+            tot = lv[0];
+        } else {
+            const float ws = wave_sum(ss);
+            if (lane == 0) s_part[sub][0][wid] = ws;
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < BT / 64; ++w) tot += s_part[sub][0][w];
+        }
         __syncthreads();
         const float ms = tot / (float)H;
         const float rinv = 1.0f / sqrtf(ms + na.eps);
@@ -554,7 +699,11 @@ __global__ __launch_bounds__(BT * RPB) void k_rows(const int64_t rows, const int
                 const float a = h[k][e] * rinv;
                 o[e] = a * gk[e];
             }
-            if (ok[k]) sts16(na.out + idx[k], pack_bf16x8(o));
+            if constexpr (P::kOutBits == 0) {
+                if (ok[k]) sts16(na.out + idx[k], pack_bf16x8(o));
+            } else {
+                p.store(pr, idx[k], o, ok[k], t + k * BT, a1);  // every lane: the group reduction needs them all
+            }
         }
     }
 }
@@ -591,18 +740,20 @@ template <class P>
 static hipError_t launch_rows(const P& p, uint32_t a0, int a1, const NormKArgs& na, int64_t rows, int grid,
                               hipStream_t s) {
     const RowShape rs = row_shape(na.hidden, rows);
-    if (rs.bt <= 256 && (int64_t)grid * 4 <= rows) {
+    if (P::kOutBits == 0 && rs.bt <= 256 && (int64_t)grid * 4 <= rows) {
 #define FC_ROWSN(BT, CPT, RPB)                                              \
         if (rs.bt == BT && rs.cpt == CPT) {                                 \
             k_rows<P, BT, CPT, RPB><<<grid, BT * RPB, 0, s>>>(rows, na.hidden, na.eps, na.gamma, na.residual, \
                                                                na.out, na.residual_out, a0, a1, p);       \
             return hipGetLastError();                                      \
         }
-        FC_ROWSN(64, 1, 4)
-        FC_ROWSN(128, 1, 4)
-        FC_ROWSN(256, 1, 4)
-        FC_ROWSN(256, 2, 4)
-        FC_ROWSN(256, 4, 2)
+        if constexpr (P::kOutBits == 0) {  // capped grids: only the bf16-output producers take a cap
+            FC_ROWSN(64, 1, 4)
+            FC_ROWSN(128, 1, 4)
+            FC_ROWSN(256, 1, 4)
+            FC_ROWSN(256, 2, 4)
+            FC_ROWSN(256, 4, 2)
+        }
 #undef FC_ROWSN
     }
 #define FC_ROWS(BT, CPT)                                                    \
@@ -675,6 +826,46 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t s) {
                            : gather_norm_bits<4>(p, norm_args(p.norm), rows, s);
     }
     return hipSuccess;
+}
+
+template <int B1, int B2>
+static hipError_t reduce_norm_bits(const ReduceNormQParams& q, hipStream_t s) {
+    const ReduceParams& p = q.rs;
+    const int64_t H = q.norm.hidden;
+    // row indices are 32-bit: a launch covers at most kMaxElems-sized runs of whole shards
+    const int64_t fit = (((int64_t)1 << 31) - 16) / (p.L > 0 ? p.L : 1);
+    const int per = fit < kNormShards ? (fit > 0 ? (int)fit : 1) : kNormShards;
+    for (int s0 = 0; s0 < p.n_shards; s0 += per) {
+        const int ns = (p.n_shards - s0) < per ? (p.n_shards - s0) : per;
+        QReduceProducer<B1, B2> prod;
+        for (int i = 0; i < kNormShards; ++i) {
+            const int si = s0 + (i < ns ? i : ns - 1);
+            for (int r = 0; r < kMaxRanks; ++r) {
+                const int t = si * p.R + (r < p.R ? r : p.R - 1);
+                prod.codes[i][r] = p.in_codes[t];
+                prod.meta[i][r] = p.in_meta[t];
+            }
+            prod.out_codes[i] = p.out_codes[si];
+            prod.out_meta[i] = p.out_meta[si];
+        }
+        NormKArgs na = norm_args(q.norm);
+        const int64_t off = (int64_t)s0 * p.L;
+        if (na.residual) na.residual += off;
+        if (na.residual_out) na.residual_out += off;
+        na.out = nullptr;
+        const int64_t rows = (int64_t)ns * p.L / H;
+        const hipError_t e = launch_rows(prod, (uint32_t)p.L, ilog2(p.group) | (p.R << 8), na, rows, (int)rows, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_reduce_norm(const ReduceNormQParams& q, hipStream_t s) {
+    const int b1 = q.rs.bits_in, b2 = q.rs.bits_out;
+    if (b1 == 8 && b2 == 8) return reduce_norm_bits<8, 8>(q, s);
+    if (b1 == 4 && b2 == 8) return reduce_norm_bits<4, 8>(q, s);
+    if (b1 == 8 && b2 == 4) return reduce_norm_bits<8, 4>(q, s);
+    return reduce_norm_bits<4, 4>(q, s);
 }
 
 hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t s) {
@@ -753,7 +944,6 @@ __global__ __launch_bounds__(256) void k_ll_unpack(const int64_t nslots, const i
     static_assert(KI % IB == 0, "a tile holds whole blocks");
     static_assert(LB >= kMaxRanks && (LB == 16 || LB == 32 || LB == 64), "one lane per rank writes a block's stale flags");
     __shared__ uint32_t s_cnt[4][2];  // per wavefront: stale pairs, pending blocks
-    const uint64_t field = LB == 64 ? ~0ull : ((1ull << LB) - 1ull);
     const int lane = threadIdx.x & 63;
     const int bl = lane % LB;  // lane inside its block's lanes
     const int64_t tile = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (128 * KI);

@@ -77,7 +77,15 @@ struct PackParams {
     uint64_t* slots;
 };
 
+// Reduce-scatter receive side with the norm before the all-gather: rs as for launch_reduce; norm's
+// residual / residual_out hold the rows of rs's shards in order (shard i at i*L); norm.out is unused.
+struct ReduceNormQParams {
+    ReduceParams rs;
+    NormParams norm;
+};
+
 hipError_t launch_quantize(const QuantizeParams& p, hipStream_t s);
+hipError_t launch_reduce_norm(const ReduceNormQParams& p, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t s);

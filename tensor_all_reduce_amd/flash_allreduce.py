@@ -90,7 +90,21 @@ class TwoStepAllReduce:
 
     def make_norm(self, gamma, out, residual=None, residual_out=None, eps: float = 1e-5) -> _lib.Norm:
         return _lib.Norm(residual.data_ptr() if residual is not None else None, gamma.data_ptr(), float(eps), self.H,
-                         out.data_ptr(), residual_out.data_ptr() if residual_out is not None else None)
+                         out.data_ptr() if out is not None else None,
+                         residual_out.data_ptr() if residual_out is not None else None)
+
+    def reduce_scatter_norm(self, norm: _lib.Norm, stream=None):
+        """Every shard's reduce with the norm first (make_norm with out=None; residual and residual_out
+        over all T*H elements): the all-gather payload is the quantized normalized rows."""
+        st = _lib.lib.fc_reduce_shard_norm(self._rs_in, self.R, self.L, self.R, self.b1, self.b2, self.G,
+                                           C.byref(norm), self._rs_out, _lib._stream(stream))
+        _lib._check(st, "fc_reduce_shard_norm")
+
+    def run_norm_first(self, y, norm: _lib.Norm, stream=None):
+        """Quantize, reduce + norm per shard, gather the normalized rows into y (bf16 [T*H])."""
+        self.quantize(stream)
+        self.reduce_scatter_norm(norm, stream)
+        self.all_gather(y=y, stream=stream)
 
     def all_gather(self, y=None, norm: _lib.Norm | None = None, stream=None):
         st = _lib.lib.fc_gather_dequant(self._ag_in, self.R, self.L, self.b2, self.G,
@@ -150,7 +164,20 @@ class TwoStepShare:
 
     def make_norm(self, gamma, out, residual=None, residual_out=None, eps: float = 1e-5) -> _lib.Norm:
         return _lib.Norm(residual.data_ptr() if residual is not None else None, gamma.data_ptr(), float(eps), self.H,
-                         out.data_ptr(), residual_out.data_ptr() if residual_out is not None else None)
+                         out.data_ptr() if out is not None else None,
+                         residual_out.data_ptr() if residual_out is not None else None)
+
+    def reduce_norm(self, norm: _lib.Norm, stream=None):
+        """Own shard's reduce with the norm first (make_norm with out=None; residual and residual_out are
+        the own shard's L elements): the own all-gather message holds the quantized normalized rows."""
+        st = _lib.lib.fc_reduce_shard_norm(self._rs_in, self.R, self.L, 1, self.b1, self.b2, self.G, C.byref(norm),
+                                           self._rs_out, _lib._stream(stream))
+        _lib._check(st, "fc_reduce_shard_norm")
+
+    def run_norm_first(self, y, norm: _lib.Norm, stream=None):
+        self.quantize(stream)
+        self.reduce_norm(norm, stream)
+        self.gather(y=y, stream=stream)
 
     def gather(self, y=None, norm: _lib.Norm | None = None, stream=None):
         st = _lib.lib.fc_gather_dequant(self._ag, self.R, self.L, self.b2, self.G,

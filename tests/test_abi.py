@@ -27,11 +27,12 @@ def declared_functions():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert {"fc_quantize", "fc_reduce_shard", "fc_gather_dequant", "fc_reduce_rmsnorm", "fc_ll_unpack_reduce",
+    assert {"fc_quantize", "fc_reduce_shard", "fc_reduce_shard_norm", "fc_gather_dequant", "fc_reduce_rmsnorm",
+            "fc_ll_unpack_reduce",
             "fc_ll_pack", "fc_copy", "fc_status_string", "fc_last_hip_error", "fc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L.lib, n), n
-    assert L.fc_abi_version() == 1
+    assert L.fc_abi_version() == 2
 
 
 def test_single_hip_runtime(L):
@@ -83,6 +84,39 @@ def test_reduce_shard_validation(L):
     assert f(ins, 2, 1024, 2, 8, 8, 32, alias, None) == L.FC_E_ARG
     twin = (L.QMsg * 2)(q(A + 0x800000, A + 0x900000), q(A + 0x800000, A + 0x910000))  # two shards, one buffer
     assert f(ins, 2, 1024, 2, 8, 8, 32, twin, None) == L.FC_E_ARG
+
+
+def test_reduce_shard_norm_validation(L):
+    """The reduce with the norm first: the reduce's checks, whole rows per shard, groups inside rows, no bf16
+    out, and no output overlapping an input or another output."""
+    f = L.lib.fc_reduce_shard_norm
+    QA = L.QMsg * 4
+    ins = QA(*[q(A + 0x10000 * i, A + 0x400000 + 0x1000 * i) for i in range(4)])
+    outs = (L.QMsg * 2)(q(A + 0x800000, A + 0x900000), q(A + 0x810000, A + 0x910000))
+
+    def nm(**kw):
+        d = dict(residual=A + 0xA00000, gamma=A + 0xB00000, eps=1e-5, hidden=256, out=None, residual_out=A + 0xC00000)
+        d.update(kw)
+        return L.Norm(d["residual"], d["gamma"], d["eps"], d["hidden"], d["out"], d["residual_out"])
+    g = lambda R=2, Lx=1024, b1=8, b2=8, G=32, n=None, o=outs, i=ins: f(i, R, Lx, 2, b1, b2, G,
+                                                                         C.byref(n if n is not None else nm()), o, None)
+    assert g(R=17) == L.FC_E_ARG
+    assert g(b2=5) == L.FC_E_ARG
+    assert f(ins, 2, 1024, 2, 8, 8, 32, None, outs, None) == L.FC_E_NULL
+    assert g(n=nm(gamma=None)) == L.FC_E_NULL
+    assert g(n=nm(out=A + 0xD00000)) == L.FC_E_ARG          # the normalized rows go to the messages only
+    assert g(n=nm(eps=0.0)) == L.FC_E_ARG
+    assert g(n=nm(hidden=100)) == L.FC_E_SHAPE                # not a multiple of 8
+    assert g(n=nm(hidden=384)) == L.FC_E_SHAPE                # 1024 is not whole rows of 384
+    assert g(G=256, n=nm(hidden=128)) == L.FC_E_SHAPE         # a group would straddle rows
+    assert g(Lx=0) == L.FC_OK
+    assert g(n=nm(gamma=A + 0xB00008)) == L.FC_E_ALIGN
+    assert g(n=nm(residual_out=A + 0x10000)) == L.FC_E_ARG   # residual_out over an input message
+    assert g(n=nm(residual_out=A + 0x800000)) == L.FC_E_ARG  # residual_out over an output message
+    alias = (L.QMsg * 2)(q(A + 0x10000, A + 0x900000), q(A + 0x810000, A + 0x910000))
+    assert g(o=alias) == L.FC_E_ARG
+    over_res = (L.QMsg * 2)(q(A + 0xA00000, A + 0x900000), q(A + 0x810000, A + 0x910000))
+    assert g(o=over_res) == L.FC_E_ARG                        # an output over the residual rows
 
 
 def norm(L, **kw):
