@@ -10,7 +10,8 @@ value = algorithmic bytes per step / time per step (GB/s).
 
 The other hot-path rows are measured at their own workloads and reported under "rows": the 70B prefill
 two-step path (int4 reduce-scatter / int8 all-gather), one GPU's real share of both two-step workloads
-(its own quantize, one shard's reduce, the gather), the self-synchronizing slot receiver (first pass
+(its own quantize, one shard's reduce, the gather), the variant with the norm applied to each shard before
+the all-gather (whole path and one GPU's share), the self-synchronizing slot receiver (first pass
 with late blocks, then the retry), and the unquantized reduce-RMSNorm on two wave-aware half batches,
 alone and overlapped with a bf16 GEMM on a second stream, with a workgroup-cap sweep.
 
@@ -60,7 +61,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", default="all", help="other hot-path rows to measure: all | none | comma list of "
-                                                  "prefill,share,ll,rmsnorm")
+                                                  "prefill,share,normfirst,ll,rmsnorm")
     ap.add_argument("--kernel-reps", type=int, default=0, help="graph replays per call timing (0 = auto)")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"))
     return ap.parse_args()
@@ -213,13 +214,14 @@ def copy_ceiling(cx):
     return 2 * nb * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
-def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic):
-    """The quantized two-step path: timed whole steps, then each call alone."""
+def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_first=False):
+    """The quantized two-step path: timed whole steps, then each call alone.  norm_first: the variant with
+    the norm applied to each shard before the all-gather (gather of the normalized rows)."""
     torch = cx.torch
     from tensor_all_reduce_amd import bytes_model as bm, datagen as dg
     from tensor_all_reduce_amd.flash_allreduce import TwoStepAllReduce
     R, T, H, G, b1, b2 = cfg.R, cfg.T, cfg.H, cfg.group, cfg.bits_rs, cfg.bits_ag
-    calls = bm.two_step_whole(R, T, H, b1, b2, G)
+    calls = (bm.two_step_normfirst_whole if norm_first else bm.two_step_whole)(R, T, H, b1, b2, G)
     step_bytes = sum(bm.total(v) for v in calls.values())
     # every call's own working set over all buffer sets exceeds twice the last-level cache
     nsets = 1 if warm else max(1, math.ceil(2 * MALL_BYTES / min(bm.total(v) for v in calls.values())))
@@ -231,12 +233,16 @@ def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic):
         res = res0.clone() if k else res0
         out = torch.empty(cfg.n, dtype=torch.int16, device=cx.dev)
         rout = torch.empty(cfg.n, dtype=torch.int16, device=cx.dev)
-        sets.append((p, p.make_norm(gam, out, residual=res, residual_out=rout, eps=cfg.eps), (res, out, rout)))
+        norm = p.make_norm(gam, None if norm_first else out, residual=res, residual_out=rout, eps=cfg.eps)
+        sets.append((p, norm, (res, out, rout)))
     torch.cuda.synchronize()
 
     def step(k):
-        p, norm, _ = sets[k]
-        p.run(norm=norm)
+        p, norm, bufs = sets[k]
+        if norm_first:
+            p.run_norm_first(bufs[1], norm)
+        else:
+            p.run(norm=norm)
 
     for k in range(min(warmup, nsets)):
         step(k)
@@ -261,21 +267,27 @@ def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic):
     ms_step = e0.elapsed_time(e1) / steps
 
     reps = kernel_reps or max(2, steps // nsets)
-    fns = {"quantize": lambda k: sets[k][0].quantize(), "reduce_shard": lambda k: sets[k][0].reduce_scatter(),
-           "gather_norm": lambda k: sets[k][0].all_gather(norm=sets[k][1])}
+    if norm_first:
+        fns = {"quantize": lambda k: sets[k][0].quantize(),
+               "reduce_shard": lambda k: sets[k][0].reduce_scatter_norm(sets[k][1]),
+               "gather": lambda k: sets[k][0].all_gather(y=sets[k][2][1])}
+    else:
+        fns = {"quantize": lambda k: sets[k][0].quantize(), "reduce_shard": lambda k: sets[k][0].reduce_scatter(),
+               "gather_norm": lambda k: sets[k][0].all_gather(norm=sets[k][1])}
     per_call = {}
     for name, fn in fns.items():
         us = cx.time_graph(cx.graph(fn, nsets), reps, nsets)
         by = bm.total(calls[name])
         gbps = by / (us * 1e-6) / 1e9
         per_call[name] = {"us": round(us, 3), "bytes": by, "GB/s": round(gbps, 1),
-                          "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_for(name, cfg, traffic)}
+                          "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
+                          "traffic": None if norm_first else traffic_for(name, cfg, traffic)}
     del sets, g_all, g_tail
     torch.cuda.empty_cache()
     return dict(ms_step=ms_step, wall=wall, step_bytes=step_bytes, nsets=nsets, per_call=per_call)
 
 
-def bench_share(cx, cfg, steps, warmup, kernel_reps):
+def bench_share(cx, cfg, steps, warmup, kernel_reps, norm_first=False):
     """One GPU's real share (P mode) of the quantized two-step path, rank 0: its own quantize, its own
     shard's reduce, the gather + epilogue of all shards.  The peers' chunks of shard 0 and the other
     shards' all-gather messages are produced once by the whole emulated path and copied into every buffer
@@ -285,13 +297,16 @@ def bench_share(cx, cfg, steps, warmup, kernel_reps):
     from tensor_all_reduce_amd import bytes_model as bm, datagen as dg
     from tensor_all_reduce_amd.flash_allreduce import TwoStepAllReduce, TwoStepShare
     R, T, H, G, b1, b2 = cfg.R, cfg.T, cfg.H, cfg.group, cfg.bits_rs, cfg.bits_ag
-    calls = bm.two_step_share(R, T, H, b1, b2, G)
+    calls = (bm.two_step_normfirst_share if norm_first else bm.two_step_share)(R, T, H, b1, b2, G)
     step_bytes = sum(bm.total(v) for v in calls.values())
     nsets = max(1, math.ceil(2 * MALL_BYTES / min(bm.total(v) for v in calls.values())))
     whole = TwoStepAllReduce(R, T, H, b1, b2, G, device=cx.dev, parts=cx.up(cx.np.stack(dg.partials(cfg))))
-    whole.quantize()
-    whole.reduce_scatter()
     res0, gam = cx.up(dg.residual(cfg)), cx.up(dg.gamma(cfg))
+    whole.quantize()
+    if norm_first:
+        whole.reduce_scatter_norm(whole.make_norm(gam, None, residual=res0, eps=cfg.eps))
+    else:
+        whole.reduce_scatter()
     sets = []
     for k in range(nsets):
         sh = TwoStepShare(R, T, H, b1, b2, G, rank=0, device=cx.dev, x=whole.parts[0].clone())
@@ -304,15 +319,24 @@ def bench_share(cx, cfg, steps, warmup, kernel_reps):
             sh.codes2[s].copy_(c)
             sh.meta2[s].copy_(m)
         out = torch.empty(cfg.n, dtype=torch.int16, device=cx.dev)
-        rout = torch.empty(cfg.n, dtype=torch.int16, device=cx.dev)
-        res = res0.clone()
-        sets.append((sh, sh.make_norm(gam, out, residual=res, residual_out=rout, eps=cfg.eps), (res, out, rout)))
+        if norm_first:  # the own shard's rows only
+            res = res0[:cfg.L].clone()
+            rout = torch.empty(cfg.L, dtype=torch.int16, device=cx.dev)
+            norm = sh.make_norm(gam, None, residual=res, residual_out=rout, eps=cfg.eps)
+        else:
+            res = res0.clone()
+            rout = torch.empty(cfg.n, dtype=torch.int16, device=cx.dev)
+            norm = sh.make_norm(gam, out, residual=res, residual_out=rout, eps=cfg.eps)
+        sets.append((sh, norm, (res, out, rout)))
     del whole
     torch.cuda.synchronize()
 
     def step(k):
-        sh, norm, _ = sets[k]
-        sh.run(norm=norm)
+        sh, norm, bufs = sets[k]
+        if norm_first:
+            sh.run_norm_first(bufs[1], norm)
+        else:
+            sh.run(norm=norm)
 
     g_all = cx.graph(step, nsets)
     for _ in range(max(1, warmup // nsets)):
@@ -320,15 +344,21 @@ def bench_share(cx, cfg, steps, warmup, kernel_reps):
     torch.cuda.synchronize()
     reps = max(1, steps // nsets)
     us_step = cx.time_graph(g_all, reps, nsets)
-    fns = {"quantize": lambda k: sets[k][0].quantize(), "reduce_shard": lambda k: sets[k][0].reduce(),
-           "gather_norm": lambda k: sets[k][0].gather(norm=sets[k][1])}
+    if norm_first:
+        fns = {"quantize": lambda k: sets[k][0].quantize(), "reduce_shard": lambda k: sets[k][0].reduce_norm(sets[k][1]),
+               "gather": lambda k: sets[k][0].gather(y=sets[k][2][1])}
+    else:
+        fns = {"quantize": lambda k: sets[k][0].quantize(), "reduce_shard": lambda k: sets[k][0].reduce(),
+               "gather_norm": lambda k: sets[k][0].gather(norm=sets[k][1])}
     per_call = {}
     for name, fn in fns.items():
         us = cx.time_graph(cx.graph(fn, nsets), kernel_reps or max(2, reps), nsets)
         by = bm.total(calls[name])
         per_call[name] = {"us": round(us, 3), "bytes": by, "GB/s": round(by / (us * 1e-6) / 1e9, 1)}
     v = step_bytes / (us_step * 1e-6) / 1e9
-    res = {"workload": cfg.name, "mode": "one GPU's real share (rank 0)", "us_per_step": round(us_step, 3),
+    res = {"workload": cfg.name, "mode": "one GPU's real share (rank 0)" + (", norm before the all-gather"
+                                                                              if norm_first else ""),
+           "us_per_step": round(us_step, 3),
            "bytes_per_step": step_bytes, "GB/s": round(v, 1), "pct_hbm_peak": round(100 * v / HBM_PEAK_GBPS, 2),
            "buffer_sets": nsets, "steps_timed": reps * nsets, "calls": per_call}
     del sets, g_all
@@ -526,8 +556,8 @@ def main():
                      "traffic": tr["total"] if tr else None},
         "wall_s": round(main_r["wall"], 3),
     }
-    rows = {"prefill", "ll", "rmsnorm", "share"} if args.rows == "all" else set() if args.rows == "none" else set(
-        args.rows.split(","))
+    rows = {"prefill", "ll", "rmsnorm", "share", "normfirst"} if args.rows == "all" else set() if args.rows == "none" \
+        else set(args.rows.split(","))
     extra = {}
     if "prefill" in rows and args.config != 3:
         c3 = dg.CONFIGS[3]
@@ -540,6 +570,17 @@ def main():
         extra["share_decode"] = bench_share(cx, cfg, args.steps, args.warmup, args.kernel_reps)
         if args.config != 3:
             extra["share_prefill"] = bench_share(cx, dg.CONFIGS[3], 30, 5, 0)
+    if "normfirst" in rows:
+        for c, tag, st, wu in ((cfg, "decode", min(args.steps, 300), 20), (dg.CONFIGS[3], "prefill", 30, 5)):
+            if tag == "prefill" and args.config == 3:
+                continue
+            rw = bench_two_step(cx, c, st, wu, False, 0, None, norm_first=True)
+            vw = rw["step_bytes"] / (rw["ms_step"] * 1e-3) / 1e9
+            extra[f"norm_first_{tag}"] = {
+                "workload": c.name, "mode": "whole emulated all-reduce, norm before the all-gather",
+                "us_per_step": round(rw["ms_step"] * 1e3, 3), "GB/s": round(vw, 1),
+                "pct_hbm_peak": round(100 * vw / HBM_PEAK_GBPS, 2), "calls": rw["per_call"],
+                "share": bench_share(cx, c, st, wu, 0, norm_first=True)}
     if "ll" in rows:
         extra["self_sync_slots"] = bench_ll(cx)
     if "rmsnorm" in rows:

@@ -65,3 +65,32 @@ def two_step_share(R, T, H, bits_rs, bits_ag, group, residual=True, residual_out
     r = reduce_shard(R, L, bits_rs, bits_ag, group, 1)
     g = gather(R, L, bits_ag, group, H, plain=False, norm=True, residual=residual, residual_out=residual_out)
     return dict(quantize=q, reduce_shard=r, gather_norm=g)
+
+
+def reduce_norm(R: int, L: int, bits_in: int, bits_out: int, group: int, n_shards: int, hidden: int,
+                residual: bool = True, residual_out: bool = True) -> dict:
+    """The reduce with the norm first: R quantized chunks per shard in, the shard's residual rows and
+    gamma in; the quantized normalized rows and residual_out out."""
+    n = n_shards * L
+    return dict(read=n_shards * R * (L * bits_in // 8 + 4 * (L // group)) + 2 * hidden + (2 * n if residual else 0),
+                write=n_shards * (L * bits_out // 8 + 4 * (L // group)) + (2 * n if residual_out else 0))
+
+
+def two_step_normfirst_whole(R, T, H, bits_rs, bits_ag, group) -> dict:
+    """Norm before the all-gather, the whole emulated all-reduce: every rank's quantize, every shard's
+    reduce + norm + quantization, the gather of the normalized rows to bf16."""
+    n = T * H
+    L = n // R
+    return dict(quantize=quantize(R * n, bits_rs, group),
+                reduce_shard=reduce_norm(R, L, bits_rs, bits_ag, group, R, H),
+                gather=gather(R, L, bits_ag, group, H, plain=True, norm=False, residual=False, residual_out=False))
+
+
+def two_step_normfirst_share(R, T, H, bits_rs, bits_ag, group) -> dict:
+    """Norm before the all-gather, one GPU's real share: its quantize, its shard's reduce + norm, the
+    gather of all R normalized shards."""
+    n = T * H
+    L = n // R
+    return dict(quantize=quantize(n, bits_rs, group),
+                reduce_shard=reduce_norm(R, L, bits_rs, bits_ag, group, 1, H),
+                gather=gather(R, L, bits_ag, group, H, plain=True, norm=False, residual=False, residual_out=False))
