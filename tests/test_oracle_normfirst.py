@@ -41,6 +41,27 @@ def test_sumsq_tree_order():
     assert orc.sumsq_tree(h) == np.float32(16777220)
 
 
+def _rn32(x):
+    """Round an exact rational to the nearest fp32, ties to even."""
+    from fractions import Fraction
+    v = np.float32(float(x))
+    cands = [np.nextafter(v, np.float32(-np.inf)), v, np.nextafter(v, np.float32(np.inf))]
+    return min(cands, key=lambda c: (abs(Fraction(float(c)) - x), int(np.float32(c).view(np.uint32)) & 1))
+
+
+def test_sumsq_tree_chunk_fold_rounds_each_square(orc):
+    """Inside a chunk every square is rounded before it is added (no fused multiply-add): for the chunk
+    [1, b, 0, ...] with b = 1 + 3370 * 2^-23, fl(1 + fl(b*b)) and fl(1 + b*b) differ."""
+    from fractions import Fraction
+    b = np.float32(1.0 + 3370 * 2.0 ** -23)
+    unfused = _rn32(Fraction(1) + Fraction(float(_rn32(Fraction(float(b)) ** 2))))
+    fused = _rn32(Fraction(1) + Fraction(float(b)) ** 2)
+    assert unfused != fused
+    h = np.zeros(8, np.float32)
+    h[:2] = [1.0, b]
+    assert orc.sumsq_tree(h) == unfused
+
+
 def test_sumsq_tree_close_to_exact_sum(orc):
     rng = np.random.default_rng(7)
     for H in (256, 4096, 8192):
