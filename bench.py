@@ -17,7 +17,8 @@ alone and overlapped with a bf16 GEMM on a second stream, with a workgroup-cap s
 
 Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
 `python bench.py --pmc-summary FETCH_CSV WRITE_CSV OUT` turns two rocprofv3 --pmc runs into the traffic
-summary that later runs report (see profiles/).
+summary that later runs report, and `--profile-report` writes a workload's whole profile summary (see
+profiles/).
 """
 import argparse
 import csv
@@ -64,6 +65,8 @@ def parse():
                                                   "prefill,share,normfirst,ll,rmsnorm")
     ap.add_argument("--kernel-reps", type=int, default=0, help="graph replays per call timing (0 = auto)")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"))
+    ap.add_argument("--profile-report", nargs=6, metavar=("CONFIG", "STATS_CSV", "FETCH_CSV", "WRITE_CSV", "VALU_CSV",
+                                                          "OUT_MD"))
     return ap.parse_args()
 
 
@@ -98,6 +101,76 @@ def pmc_summary(fetch_csv, write_csv, out_path):
             continue
         lines.append(f"kernel {round(f[k] * fs * 1024)} {round(w.get(k, 0.0) * ws * 1024)} {k}")
     with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def profile_report(config, stats_csv, fetch_csv, write_csv, valu_csv, out_md):
+    """The profile summary of one two-step workload (profiles/two_step_<slug>.md) from four rocprofv3 runs of
+    the benchmark: --kernel-trace --stats, then --pmc FETCH_SIZE, --pmc WRITE_SIZE and
+    --pmc SQ_INSTS_VALU SQ_WAVES, each in a run of its own.  Also writes the traffic summary that later
+    benchmark runs report (profiles/pmc_traffic_<slug>.txt)."""
+    from tensor_all_reduce_amd import bytes_model as bm, datagen as dg
+    cfg = dg.CONFIGS[config]
+    pmc_summary(fetch_csv, write_csv, traffic_file(cfg.slug))
+    calls = bm.two_step_whole(cfg.R, cfg.T, cfg.H, cfg.bits_rs, cfg.bits_ag, cfg.group)
+    keys = {call: kernel_of_call(call, cfg) for call in calls}
+
+    def call_of(name):
+        return next((c for c, k in keys.items() if k in name), None)
+
+    def short(name):
+        return name.replace("void ", "").split("(")[0]
+    stats = list(csv.DictReader(open(stats_csv)))
+    pmc = {}
+    for path in (fetch_csv, write_csv, valu_csv):
+        for r in csv.DictReader(open(path)):
+            pmc.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    med = {k: statistics.median(v) for k, v in pmc.items()}
+    traffic = load_traffic(cfg)
+    runs = "" if config == 2 else f" --config {config} --steps 30 --warmup 5"
+    x = " --steps 290 --warmup 0 --kernel-reps 1" if config == 2 else f" --config {config} --steps 4 --warmup 1 --kernel-reps 1"
+    base = "python3 bench.py --no-cpu-baseline --rows none"
+    lines = [f"# Two-step all-reduce kernels on the {cfg.name} workload", "",
+             "Kernel durations from a rocprofv3 kernel trace of the benchmark (run from the repository root on one "
+             "MI355X; the benchmark replays each call from HIP graphs over cold buffer sets):", "", "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/st{config} -o st{config} -- {base}{runs}",
+             "```", "", "| kernel | calls | avg us | min us | max us | algorithmic bytes | GB/s at avg |",
+             "|---|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        c = call_of(name)
+        by = bm.total(calls[c]) if c else (2 << 30 if "k_copy" in name else None)
+        if by is None:
+            continue
+        avg = float(r["AverageNs"]) / 1e3
+        lines.append(f"| `{short(name)}` | {r['Calls']} | {avg:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {by} | {by / (avg * 1e-6) / 1e9:.0f} |")
+    lines += ["", "(`k_copy` is the 1 GiB copy-ceiling kernel of the benchmark: 2 GiB moved per call.  Durations "
+              "under the tracer run longer than the graph-timed figures the benchmark reports.)", "",
+              "HBM traffic per launch from two counter runs (FETCH_SIZE, then WRITE_SIZE), scaled by what the same "
+              "counters read for the 1 GiB copy kernel, and vector-ALU instructions per wavefront and per byte "
+              f"from a third run (kernel sources {sources_sha()}):", "", "```"]
+    for i, ctr in enumerate(("FETCH_SIZE", "WRITE_SIZE", "SQ_INSTS_VALU SQ_WAVES")):
+        lines.append(f"timeout -s KILL 240 rocprofv3 --pmc {ctr} --output-format csv -d gpurun_out/p{i}{config} "
+                     f"-o p{i}{config} -- {base}{x}")
+    lines += ["```", "", f"Summarised with `python bench.py --profile-report {config} STATS FETCH WRITE VALU {out_md}`.",
+              "", "| kernel | fetch bytes | algorithmic read | write bytes | algorithmic write | VALU instr / wavefront "
+              "| VALU instr / algorithmic byte (per wavefront lane-op: x64) |", "|---|---|---|---|---|---|---|"]
+    for name in sorted({k for k, _ in med}):
+        c = call_of(name)
+        if not c:
+            continue
+        tr = traffic_for(c, cfg, traffic) or {}
+        a = calls[c]
+        v, w = med.get((name, "SQ_INSTS_VALU")), med.get((name, "SQ_WAVES"))
+        vpw = f"{v / w:.0f}" if v and w else "-"
+        vpb = f"{v / bm.total(a):.4f} ({64 * v / bm.total(a):.2f})" if v else "-"
+        fb, wb = tr.get("fetch"), tr.get("write")
+        lines.append(f"| `{short(name)}` | {fb} ({fb / a['read']:.3f}x) | {a['read']} | {wb} ({wb / a['write']:.3f}x) | "
+                     f"{a['write']} | {vpw} | {vpb} |" if fb is not None else f"| `{short(name)}` | - | {a['read']} | - | "
+                     f"{a['write']} | {vpw} | {vpb} |")
+    with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -522,6 +595,10 @@ def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return 0
+    if args.profile_report:
+        c, *paths = args.profile_report
+        profile_report(int(c), *paths)
         return 0
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build emulates the R ranks on one GPU "
