@@ -13,7 +13,8 @@ two-step path (int4 reduce-scatter / int8 all-gather), one GPU's real share of b
 (its own quantize, one shard's reduce, the gather), the variant with the norm applied to each shard before
 the all-gather (whole path and one GPU's share), the self-synchronizing slot receiver (first pass
 with late blocks, then the retry), and the unquantized reduce-RMSNorm on two wave-aware half batches,
-alone and overlapped with a bf16 GEMM on a second stream, with a workgroup-cap sweep.
+alone and overlapped with a bf16 GEMM on a second stream, with a workgroup-cap sweep, and the two-half pipelined layer step (wave-aware split, each half's
+all-reduce overlapping the other half's GEMM).
 
 Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
 `python bench.py --pmc-summary FETCH_CSV WRITE_CSV OUT` turns two rocprofv3 --pmc runs into the traffic
@@ -62,7 +63,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", default="all", help="other hot-path rows to measure: all | none | comma list of "
-                                                  "prefill,share,normfirst,ll,rmsnorm")
+                                                  "prefill,share,normfirst,ll,rmsnorm,layer")
     ap.add_argument("--kernel-reps", type=int, default=0, help="graph replays per call timing (0 = auto)")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"))
     ap.add_argument("--profile-report", nargs=6, metavar=("CONFIG", "STATS_CSV", "FETCH_CSV", "WRITE_CSV", "VALU_CSV",
@@ -591,6 +592,59 @@ def bench_rmsnorm_overlap(cx):
     return res
 
 
+def bench_layer(cx):
+    """The two-half pipelined layer step (GEMM [T_h, 8192] x [8192, 8192] of each half on one stream, the
+    8-rank all-reduce + RMSNorm of each half on another) against the same halves run serially and against
+    no split, at T = 8192 and at T = 6000 (a split that is not a halving)."""
+    torch = cx.torch
+    from tensor_all_reduce_amd import datagen as dg
+    from tensor_all_reduce_amd.schedule import TwoHalfLayer, gemm_waves, wave_aware_split
+    cfg = dg.CONFIGS[5]
+    R, H = cfg.R, cfg.H
+    res_rows = {}
+    for T in (cfg.T, 6000):
+        gen = torch.Generator(device=cx.dev)
+        gen.manual_seed(0xFC07 + T)
+        x = torch.randn(T, H, device=cx.dev, dtype=torch.bfloat16, generator=gen)
+        w = (torch.randn(H, H, device=cx.dev, dtype=torch.bfloat16, generator=gen) * H ** -0.5).to(torch.bfloat16)
+        peers = [torch.randn(T, H, device=cx.dev, dtype=torch.bfloat16, generator=gen).view(torch.int16)
+                 for _ in range(R - 1)]
+        res = torch.randn(T, H, device=cx.dev, dtype=torch.bfloat16, generator=gen).view(torch.int16)
+        gam = cx.up(dg.gamma(cfg))
+        out = torch.empty(T * H, dtype=torch.int16, device=cx.dev)
+        rout = torch.empty(T * H, dtype=torch.int16, device=cx.dev)
+        s1, s2 = torch.cuda.Stream(device=cx.dev), torch.cuda.Stream(device=cx.dev)
+        split = TwoHalfLayer(x, w, peers, res, gam, out, residual_out=rout)
+        whole = TwoHalfLayer(x, w, peers, res, gam, out, residual_out=rout, t1=T)
+
+        def timed(fn, reps=5):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                a = cx.ev()
+                a.record(torch.cuda.current_stream())
+                s1.wait_event(a)
+                s2.wait_event(a)
+                fn()
+                b1, b2 = cx.ev(), cx.ev()
+                b1.record(s1)
+                b2.record(s2)
+                torch.cuda.synchronize()
+                ts.append(max(a.elapsed_time(b1), a.elapsed_time(b2)) * 1e3)
+            return statistics.median(ts)
+        t1 = split.t1
+        res_rows[str(T)] = {
+            "t1": t1, "waves": [gemm_waves(t1, H), gemm_waves(T - t1, H)], "unsplit_waves": gemm_waves(T, H),
+            "unsplit_us": round(timed(lambda: whole.run_serial(s1)), 1),
+            "serial_halves_us": round(timed(lambda: split.run_serial(s1)), 1),
+            "pipelined_us": round(timed(lambda: split.run(s1, s2)), 1)}
+        del x, w, peers, res, out, rout, split, whole
+        torch.cuda.empty_cache()
+    return {"workload": f"two-half layer step, GEMM [T, {H}] x [{H}, {H}] bf16 + {R}-rank bf16 all-reduce + RMSNorm",
+            "by_T": res_rows}
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -633,7 +687,7 @@ def main():
                      "traffic": tr["total"] if tr else None},
         "wall_s": round(main_r["wall"], 3),
     }
-    rows = {"prefill", "ll", "rmsnorm", "share", "normfirst"} if args.rows == "all" else set() if args.rows == "none" \
+    rows = {"prefill", "ll", "rmsnorm", "share", "normfirst", "layer"} if args.rows == "all" else set() if args.rows == "none" \
         else set(args.rows.split(","))
     extra = {}
     if "prefill" in rows and args.config != 3:
@@ -662,6 +716,8 @@ def main():
         extra["self_sync_slots"] = bench_ll(cx)
     if "rmsnorm" in rows:
         extra["tokenweave_reduce_rmsnorm"] = bench_rmsnorm_overlap(cx)
+    if "layer" in rows:
+        extra["two_half_layer"] = bench_layer(cx)
     if extra:
         line["rows"] = extra
     if not args.no_cpu_baseline:
