@@ -524,4 +524,34 @@ void or_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, int blo
     }
 }
 
+// ---- standalone all-gather on self-synchronizing blocks (flash-comm, abstract: readiness evidence per
+// block; the all-gather is the second workload of the mechanism).  Rank r's payload is nwords 32-bit words
+// (bf16 pairs, or the words of a quantized message: codes then meta) carried in the low halves of its
+// slots, epoch words in the high halves; a block is `block_slots` consecutive slots.  For every
+// (rank, block) not yet done: the copy is stale if any slot carries an epoch other than the expected one;
+// a valid block's words are copied to out[r] and it is marked done; a stale one is left untouched and
+// pending.  counters[0] += stale (rank, block) pairs, counters[1] += pending (rank, block) pairs (here the
+// same pairs: nothing is reduced across ranks, so every pair stands alone).
+void or_ll_gather(const uint64_t* const* slots, int R, int64_t nwords, int block_slots, uint32_t epoch,
+                  uint32_t* const* out, uint8_t* stale, uint8_t* done, uint32_t* counters) {
+    const int64_t nblk = nwords / block_slots;
+    for (int r = 0; r < R; ++r) {
+        for (int64_t b = 0; b < nblk; ++b) {
+            const int64_t f = (int64_t)r * nblk + b;
+            if (done[f]) continue;
+            bool st = false;
+            for (int64_t k = b * block_slots; k < (b + 1) * block_slots; ++k)
+                if ((uint32_t)(slots[r][k] >> 32) != epoch) st = true;
+            stale[f] = st ? 1 : 0;
+            if (st) {
+                counters[0] += 1;
+                counters[1] += 1;
+                continue;
+            }
+            for (int64_t k = b * block_slots; k < (b + 1) * block_slots; ++k) out[r][k] = (uint32_t)slots[r][k];
+            done[f] = 1;
+        }
+    }
+}
+
 }  // extern "C"

@@ -65,6 +65,7 @@ def lib():
             L.or_reduce_rmsnorm.argtypes = [vp, C.c_int, i64, i64, vp, u16p, C.c_float, u16p, vp, vp]
             L.or_ll_pack.argtypes = [u16p, i64, C.c_int, C.c_uint32, vp, u64p]
             L.or_ll_unpack_reduce.argtypes = [vp, C.c_int, i64, C.c_int, C.c_uint32, u16p, u8p, u8p, u32p]
+            L.or_ll_gather.argtypes = [vp, C.c_int, i64, C.c_int, C.c_uint32, vp, u8p, u8p, u32p]
             L.or_sumsq_tree.argtypes = [f32p, i64]
             L.or_sumsq_tree.restype = C.c_float
             L.or_norm_rows_f32.argtypes = [f32p, vp, u16p, C.c_float, i64, i64, f32p, vp]
@@ -190,6 +191,21 @@ def two_step(parts, bits1, bits2, group, residual=None, gamma=None, eps=1e-5, hi
                       hidden if hidden else n, _ptr(out), _ptr(rout))
     return dict(codes1=c1.reshape(R, -1), meta1=m1.reshape(R, -1), codes2=c2, meta2=m2, y=y, out=out,
                 residual_out=rout)
+
+
+def ll_gather(slots_list, nwords, block_slots, epoch, out=None, done=None, counters=None):
+    """Standalone all-gather on epoch-tagged blocks: returns (out [R][nwords] uint32, stale [R*nblk],
+    done [R*nblk], counters [2]); out/done/counters may be passed in to continue a previous pass."""
+    R = len(slots_list)
+    nblk = nwords // block_slots
+    sl = [_c(s, np.uint64) for s in slots_list]
+    out = [np.zeros(nwords, np.uint32) for _ in range(R)] if out is None else [_c(o, np.uint32) for o in out]
+    done = np.zeros(R * nblk, np.uint8) if done is None else _c(done, np.uint8).copy()
+    counters = np.zeros(2, np.uint32) if counters is None else _c(counters, np.uint32).copy()
+    stale = np.zeros(R * nblk, np.uint8)
+    lib().or_ll_gather(_ptr_array(sl), R, nwords, block_slots, epoch & 0xFFFFFFFF, _ptr_array(out), stale, done,
+                       counters)
+    return out, stale, done, counters
 
 
 # ---- norm before the all-gather ---------------------------------------------------------------------
