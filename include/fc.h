@@ -137,6 +137,20 @@ fc_status fc_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, in
                               uint16_t* out, uint8_t* stale, uint8_t* done, uint32_t* counters,
                               hipStream_t stream);
 
+/* Standalone all-gather on self-synchronizing blocks (flash-comm, abstract: every block carries evidence
+ * of its readiness; the same mechanism serves an all-gather).  slots [host array, R entries]: rank r's
+ * uint64 [nwords] slots, payload word k in bits 0..31 of slot k (bf16 pairs, or the words of a quantized
+ * message: codes, then meta, in one buffer), epoch word in bits 32..63.  A block is `block_slots`
+ * consecutive slots; nblk = nwords / block_slots.  For each (rank r, block b) with done[r*nblk + b] == 0:
+ * stale[r*nblk + b] = 1 if any slot carries an epoch word != epoch, else 0; a valid block's words are
+ * copied to out[r] (uint32 [nwords], host array of R device pointers, 8-byte aligned) and done is set; a
+ * stale one is left untouched and pending.  counters[0] += stale (rank, block) pairs and counters[1] +=
+ * pending pairs (the same pairs: nothing is reduced across ranks), in one 64-bit atomic add per
+ * workgroup (counters 8-byte aligned, caller zeroes).  A done block's slots may still be read.  Calling
+ * again after late blocks have been rewritten completes them.  nwords % block_slots == 0. */
+fc_status fc_ll_gather(const uint64_t* const* slots, int R, int64_t nwords, int block_slots, uint32_t epoch,
+                       uint32_t* const* out, uint8_t* stale, uint8_t* done, uint32_t* counters, hipStream_t stream);
+
 /* Sender side of the slots above, used to emulate a peer's writes: packs bf16 [n] into n/2 slots tagged
  * with `epoch`, writing blocks in the order block_order[0..nblk) (an int32 permutation of the block
  * indices, or NULL for ascending).  The result does not depend on the order. */

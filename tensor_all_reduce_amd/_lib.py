@@ -72,9 +72,10 @@ def _load():
     lib.fc_reduce_rmsnorm.argtypes = [C.POINTER(vp), i32, i64, C.POINTER(Norm), i32, vp]
     lib.fc_ll_unpack_reduce.argtypes = [C.POINTER(vp), i32, i64, i32, u32, vp, vp, vp, vp, vp]
     lib.fc_ll_pack.argtypes = [vp, i64, i32, u32, vp, vp, vp]
+    lib.fc_ll_gather.argtypes = [C.POINTER(vp), i32, i64, i32, u32, C.POINTER(vp), vp, vp, vp, vp]
     lib.fc_copy.argtypes = [vp, vp, i64, vp]
     for f in ("fc_quantize", "fc_reduce_shard", "fc_reduce_shard_norm", "fc_gather_dequant", "fc_reduce_rmsnorm", "fc_ll_unpack_reduce",
-              "fc_ll_pack", "fc_copy"):
+              "fc_ll_pack", "fc_ll_gather", "fc_copy"):
         getattr(lib, f).restype = i32
     return lib
 
@@ -166,6 +167,15 @@ def fc_ll_unpack_reduce(slots, n: int, block_slots: int, epoch: int, out, stale,
     arr = (C.c_void_p * R)(*[_ptr(s) for s in slots])
     _check(_lib.fc_ll_unpack_reduce(arr, R, n, block_slots, epoch & 0xFFFFFFFF, _ptr(out), _ptr(stale), _ptr(done),
                                     _ptr(counters), _stream(stream)), "fc_ll_unpack_reduce")
+
+
+def fc_ll_gather(slots, nwords: int, block_slots: int, epoch: int, out, stale, done, counters, stream=None) -> None:
+    """slots: R uint64 slot buffers; out: R uint32 (or any 4-byte) destination buffers."""
+    R = len(slots)
+    sa = (C.c_void_p * R)(*[_ptr(s) for s in slots])
+    oa = (C.c_void_p * R)(*[_ptr(o) for o in out])
+    _check(_lib.fc_ll_gather(sa, R, nwords, block_slots, epoch & 0xFFFFFFFF, oa, _ptr(stale), _ptr(done),
+                             _ptr(counters), _stream(stream)), "fc_ll_gather")
 
 
 def fc_ll_pack(x, block_slots: int, epoch: int, slots, block_order=None, n: int | None = None, stream=None) -> None:

@@ -334,6 +334,45 @@ fc_status fc_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, in
     return launched(fc::launch_ll_unpack(p, stream));
 }
 
+fc_status fc_ll_gather(const uint64_t* const* slots, int R, int64_t nwords, int block_slots, uint32_t epoch,
+                       uint32_t* const* out, uint8_t* stale, uint8_t* done, uint32_t* counters, hipStream_t stream) {
+    if (R < 1 || R > fc::kMaxRanks || !valid_block(block_slots) || nwords < 0) return FC_E_ARG;
+    if (nwords % block_slots != 0 || nwords > kMaxElems) return FC_E_SHAPE;
+    if (nwords == 0) return FC_OK;
+    if (!slots || !out || !stale || !done || !counters) return FC_E_NULL;
+    if (!aligned(counters, 8)) return FC_E_ALIGN;
+    const int64_t nblk = nwords / block_slots;
+    const Range rs = rng(stale, (int64_t)R * nblk), rd = rng(done, (int64_t)R * nblk), rc = rng(counters, 8);
+    if (overlap(rs, rd) || overlap(rs, rc) || overlap(rd, rc)) return FC_E_ARG;
+    for (int r = 0; r < R; ++r) {
+        if (!slots[r] || !out[r]) return FC_E_NULL;
+        if (!aligned(slots[r], 16) || !aligned(out[r], 8)) return FC_E_ALIGN;
+    }
+    for (int r = 0; r < R; ++r) {
+        const Range ro = rng(out[r], 4 * nwords);
+        if (overlap(ro, rs) || overlap(ro, rd) || overlap(ro, rc)) return FC_E_ARG;
+        for (int q = 0; q < R; ++q) {
+            const Range sq = rng(slots[q], 8 * nwords);
+            if (overlap(ro, sq)) return FC_E_ARG;
+            if (q > r && overlap(ro, rng(out[q], 4 * nwords))) return FC_E_ARG;
+            if (r == 0 && (overlap(sq, rs) || overlap(sq, rd) || overlap(sq, rc))) return FC_E_ARG;
+        }
+    }
+    fc::LLGatherParams p;
+    for (int r = 0; r < fc::kMaxRanks; ++r) {
+        p.slots[r] = r < R ? slots[r] : nullptr;
+        p.out[r] = r < R ? out[r] : nullptr;
+    }
+    p.R = R;
+    p.nwords = nwords;
+    p.block_slots = block_slots;
+    p.epoch = epoch;
+    p.stale = stale;
+    p.done = done;
+    p.counters = counters;
+    return launched(fc::launch_ll_gather(p, stream));
+}
+
 fc_status fc_ll_pack(const uint16_t* x, int64_t n, int block_slots, uint32_t epoch, const int32_t* block_order,
                      uint64_t* slots, hipStream_t stream) {
     if (!valid_block(block_slots) || n < 0) return FC_E_ARG;

@@ -1066,6 +1066,133 @@ hipError_t launch_ll_unpack(const LLParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Standalone all-gather on self-synchronizing blocks (flash-comm, abstract: the same readiness evidence
+// carries an all-gather): grid row y = rank.  Rank r's payload words travel in the low halves of its slots;
+// a wavefront owns KI*128 slots of one rank (2 slots = 16 bytes per lane per instruction).  A block not yet
+// done is copied to out[r] when every slot carries the expected epoch, else flagged stale and left pending.
+// Block verdicts and counts are wavefront-uniform (scalar unit); counters: one 64-bit atomic per workgroup.
+struct LLGatherTabs {
+    const uint64_t* slots[kMaxRanks];
+    uint32_t* out[kMaxRanks];
+};
+
+template <int B>
+__global__ __launch_bounds__(256) void k_ll_gather(const int64_t nslots, const int64_t nblk, uint8_t* done,
+                                                   uint8_t* stale, const uint32_t epoch, uint32_t* counters,
+                                                   const LLGatherTabs t) {
+    constexpr int KI = 4;                      // instructions per wavefront tile
+    constexpr int IB = B <= 128 ? 1 : 2;       // instructions per block
+    constexpr int LB = B <= 128 ? B / 2 : 64;  // lanes of one instruction inside one block
+    constexpr int NBW = 64 / LB;               // blocks per instruction
+    static_assert(KI % IB == 0, "a tile holds whole blocks");
+    __shared__ uint32_t s_cnt[4];
+    const int r = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int bl = lane % LB;
+    const int64_t tile = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (128 * KI);
+    const uint64_t* sp = t.slots[r];
+    uint8_t* dn = done + (int64_t)r * nblk;
+    int64_t slot[KI], blk[KI];
+    bool inside[KI];
+    uint8_t dv[KI];
+    uint4 v[KI];
+    // done flags and slots are loaded together (a block already done is read and ignored); no load sits in
+    // a lane-divergent branch: lanes past the end read a clamped address
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+        slot[k] = tile + k * 128 + 2 * lane;
+        inside[k] = slot[k] < nslots;
+        blk[k] = inside[k] ? slot[k] / B : nblk - 1;
+        dv[k] = dn[blk[k]];
+    }
+#pragma unroll
+    for (int k = 0; k < KI; ++k) v[k] = lds16(sp + (inside[k] ? slot[k] : 0));
+    bool active[KI];
+    uint64_t amask[KI];
+    uint32_t vs[KI][NBW];
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+        active[k] = inside[k] && dv[k] == 0;
+        amask[k] = __ballot(active[k]);
+        const uint64_t bal = (__ballot(v[k].y != epoch) | __ballot(v[k].w != epoch)) & amask[k];
+        uint32_t lo = (uint32_t)bal, hi = (uint32_t)(bal >> 32);
+        asm("" : "+s"(lo), "+s"(hi));
+        if constexpr (LB == 64) {
+            vs[k][0] = s_nonzero(lo | hi);
+        } else if constexpr (LB == 32) {
+            vs[k][0] = s_nonzero(lo);
+            vs[k][1] = s_nonzero(hi);
+        } else {  // LB == 16
+            vs[k][0] = s_nonzero(lo & 0xffffu);
+            vs[k][1] = s_nonzero(lo >> 16);
+            vs[k][2] = s_nonzero(hi & 0xffffu);
+            vs[k][3] = s_nonzero(hi >> 16);
+        }
+    }
+    uint32_t* op = t.out[r];
+    uint8_t* sf = stale + (int64_t)r * nblk;
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+        uint32_t sm;  // this lane's block: 1 = stale
+        if constexpr (IB == 2) {
+            sm = vs[k & ~1][0] | vs[k | 1][0];
+        } else if constexpr (NBW == 1) {
+            sm = vs[k][0];
+        } else {
+            const uint32_t h32 = 0u - (uint32_t)(lane >> 5);
+            if constexpr (NBW == 2) {
+                sm = (vs[k][0] & ~h32) | (vs[k][1] & h32);
+            } else {
+                const uint32_t h16 = 0u - (uint32_t)((lane >> 4) & 1);
+                sm = (((vs[k][0] & ~h16) | (vs[k][1] & h16)) & ~h32) | (((vs[k][2] & ~h16) | (vs[k][3] & h16)) & h32);
+            }
+        }
+        if (!active[k]) continue;
+        const bool leader = (IB == 1 || k % 2 == 0) && bl == 0;
+        if (leader) sf[blk[k]] = (uint8_t)sm;
+        if (sm == 0) {
+            sts8(op + slot[k], make_uint2(v[k].x, v[k].z));
+            if (leader) dn[blk[k]] = 1;
+        }
+    }
+    uint32_t n_stale = 0;
+#pragma unroll
+    for (int k = 0; k < KI; k += IB) {
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) {
+            const uint32_t on = (uint32_t)(amask[k] >> (b * LB)) & 1u;
+            n_stale += on & (IB == 2 ? (vs[k][0] | vs[k + 1][0]) : vs[k][b]);
+        }
+    }
+    if (lane == 0) s_cnt[threadIdx.x >> 6] = n_stale;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t st = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+        // stale pairs and pending pairs are the same pairs here; one 64-bit atomic adds both counters
+        if (st) atomicAdd(reinterpret_cast<unsigned long long*>(counters), ((unsigned long long)st << 32) | st);
+    }
+}
+
+hipError_t launch_ll_gather(const LLGatherParams& p, hipStream_t s) {
+    LLGatherTabs t;
+    for (int i = 0; i < kMaxRanks; ++i) {
+        t.slots[i] = p.slots[i < p.R ? i : p.R - 1];
+        t.out[i] = p.out[i < p.R ? i : p.R - 1];
+    }
+    const int64_t nslots = p.nwords, nblk = nslots / p.block_slots;
+    const int64_t per_wg = 4 * 128 * 4;  // slots per workgroup: 4 wavefronts x 4 instructions x 128
+    const dim3 grid((unsigned)((nslots + per_wg - 1) / per_wg), (unsigned)p.R);
+#define FC_LLG(B) k_ll_gather<B><<<grid, 256, 0, s>>>(nslots, nblk, p.done, p.stale, p.epoch, p.counters, t)
+    switch (p.block_slots) {
+        case 32: FC_LLG(32); break;
+        case 64: FC_LLG(64); break;
+        case 128: FC_LLG(128); break;
+        default: FC_LLG(256); break;
+    }
+#undef FC_LLG
+    return hipGetLastError();
+}
+
 // Sender emulation: lane t of the write order packs 2 slots (4 bf16 in, 16 bytes out) of block
 // order[t / (B/2)].  An order entry outside [0, nblk) (not a permutation: out of contract) writes nothing.
 __global__ __launch_bounds__(256) void k_ll_pack(const uint16_t* __restrict__ x, int64_t nthreads, int lpb,

@@ -68,6 +68,18 @@ struct LLParams {
     uint32_t* counters;
 };
 
+struct LLGatherParams {
+    const uint64_t* slots[kMaxRanks];
+    uint32_t* out[kMaxRanks];
+    int R;
+    int64_t nwords;  // per rank
+    int block_slots;
+    uint32_t epoch;
+    uint8_t* stale;  // [R][nblk]
+    uint8_t* done;   // [R][nblk]
+    uint32_t* counters;
+};
+
 struct PackParams {
     const uint16_t* x;
     int64_t n;
@@ -91,6 +103,7 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t s);
 hipError_t launch_ll_unpack(const LLParams& p, hipStream_t s);
 hipError_t launch_ll_pack(const PackParams& p, hipStream_t s);
+hipError_t launch_ll_gather(const LLGatherParams& p, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 
 }  // namespace fc

@@ -194,6 +194,26 @@ def test_ll_validation(L):
     assert p(A, 4096, 64, 7, None, A + 1024, None) == L.FC_E_ARG
 
 
+def test_ll_gather_validation(L):
+    f = L.lib.fc_ll_gather
+    sl = (C.c_void_p * 2)(A + 0x1000000, A + 0x2000000)
+    out = (C.c_void_p * 2)(A + 0x3000000, A + 0x3800000)
+    d = dict(stale=A + 0x4000000, done=A + 0x5000000, cnt=A + 0x6000000)
+    g = lambda R=2, n=4096, B=64, o=out, s=sl, **kw: f(s, R, n, B, 7, o, kw.get("stale", d["stale"]),
+                                                       kw.get("done", d["done"]), kw.get("cnt", d["cnt"]), None)
+    assert g(B=48) == L.FC_E_ARG
+    assert g(R=0) == L.FC_E_ARG
+    assert g(n=4096 + 32) == L.FC_E_SHAPE
+    assert g(n=0) == L.FC_OK
+    assert g(cnt=None) == L.FC_E_NULL
+    assert g(cnt=A + 0x6000004) == L.FC_E_ALIGN
+    assert g(o=(C.c_void_p * 2)(A + 0x3000004, A + 0x3800000)) == L.FC_E_ALIGN
+    assert g(s=(C.c_void_p * 2)(A + 0x1000008, A + 0x2000000)) == L.FC_E_ALIGN
+    assert g(o=(C.c_void_p * 2)(A + 0x3000000, A + 0x3000000 + 64)) == L.FC_E_ARG   # two outputs overlap
+    assert g(o=(C.c_void_p * 2)(A + 0x3000000, A + 0x2000000 + 64)) == L.FC_E_ARG   # an output over slots
+    assert g(done=A + 0x4000000 + 8) == L.FC_E_ARG                                  # done over stale
+
+
 def test_copy_validation(L):
     f = L.lib.fc_copy
     assert f(A, A + 0x100000, 100, None) == L.FC_E_SHAPE
