@@ -11,7 +11,8 @@ value = algorithmic bytes per step / time per step (GB/s).
 The other hot-path rows are measured at their own workloads and reported under "rows": the 70B prefill
 two-step path (int4 reduce-scatter / int8 all-gather), one GPU's real share of both two-step workloads
 (its own quantize, one shard's reduce, the gather), the variant with the norm applied to each shard before
-the all-gather (whole path and one GPU's share), the self-synchronizing slot receiver (first pass
+the all-gather (whole path and one GPU's share), the standalone all-gather on epoch-tagged blocks, the
+self-synchronizing slot receiver (first pass
 with late blocks, then the retry), and the unquantized reduce-RMSNorm on two wave-aware half batches,
 alone and overlapped with a bf16 GEMM on a second stream, with a workgroup-cap sweep, and the two-half pipelined layer step (wave-aware split, each half's
 all-reduce overlapping the other half's GEMM).
@@ -38,7 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused quant-reduce-RMSNorm effective GB/s (% HBM peak) + µs per call"
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
-KERNEL_SOURCES = ["tensor_all_reduce_amd/csrc/fc_kernels.hip", "tensor_all_reduce_amd/csrc/fc_device.h"]
+KERNEL_SOURCES = ["tensor_all_reduce_amd/csrc/fc_twostep.hip", "tensor_all_reduce_amd/csrc/fc_device.h"]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -63,9 +64,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", default="all", help="other hot-path rows to measure: all | none | comma list of "
-                                                  "prefill,share,normfirst,ll,rmsnorm,layer")
+                                                  "prefill,share,normfirst,ll,llgather,rmsnorm,layer")
     ap.add_argument("--kernel-reps", type=int, default=0, help="graph replays per call timing (0 = auto)")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"))
+    ap.add_argument("--stats-table", nargs=4, metavar=("STATS_CSV", "OUT_MD", "TITLE", "COMMAND"))
     ap.add_argument("--profile-report", nargs=6, metavar=("CONFIG", "STATS_CSV", "FETCH_CSV", "WRITE_CSV", "VALU_CSV",
                                                           "OUT_MD"))
     return ap.parse_args()
@@ -171,6 +173,22 @@ def profile_report(config, stats_csv, fetch_csv, write_csv, valu_csv, out_md):
         lines.append(f"| `{short(name)}` | {fb} ({fb / a['read']:.3f}x) | {a['read']} | {wb} ({wb / a['write']:.3f}x) | "
                      f"{a['write']} | {vpw} | {vpb} |" if fb is not None else f"| `{short(name)}` | - | {a['read']} | - | "
                      f"{a['write']} | {vpw} | {vpb} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def stats_table(stats_csv, out_md, title, command):
+    """A kernel-duration table (rocprofv3 --kernel-trace --stats) of every library kernel in a run."""
+    rows = sorted(csv.DictReader(open(stats_csv)), key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"# {title}", "", "Kernel durations from a rocprofv3 kernel trace (run from the repository root on one "
+             "MI355X; durations under the tracer run longer than the benchmark's graph-timed figures):", "",
+             "```", command, "```", "", "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows:
+        if "fc::" not in r["Name"]:
+            continue
+        lines.append(f"| `{r['Name'].replace('void ', '').split('(')[0]}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -498,6 +516,67 @@ def bench_ll(cx):
     return res
 
 
+def bench_ll_gather(cx):
+    """Standalone all-gather on epoch-tagged blocks, 8 ranks, 64-slot blocks, 2% late (rank, block) copies:
+    bf16 shards of the slot workload ([16, 8192] per rank) and the int8 all-gather messages of the 70B
+    prefill shards (codes then meta, 1.08 M words per rank).  First pass, then the retry once the late
+    blocks have arrived."""
+    torch, np = cx.torch, cx.np
+    from tensor_all_reduce_amd import _lib, bytes_model as bm, datagen as dg
+    c4, c3 = dg.CONFIGS[4], dg.CONFIGS[3]
+    B, e = c4.block_slots, c4.epoch
+    res = {}
+    msg3 = c3.L * c3.bits_ag // 8 + 4 * (c3.L // c3.group)
+    for tag, R, nwords in (("bf16_shards", c4.R, c4.n // c4.R // 2), ("int8_prefill_messages", c3.R,
+                                                                         -(-msg3 // 4 // B) * B)):
+        nblk = nwords // B
+        nsets = max(1, math.ceil(2 * MALL_BYTES / (R * nwords * 12)))
+        gen = torch.Generator(device=cx.dev)
+        gen.manual_seed(0xFC0A + nwords)
+        eps = [torch.from_numpy(dg.stale_epochs(c4, r, nwords)[0].astype(np.int64)).to(cx.dev) for r in range(R)]
+        good = torch.full((nwords,), e, dtype=torch.int64, device=cx.dev)
+        sets = []
+        for k in range(nsets):
+            words = [torch.randint(0, 1 << 32, (nwords,), dtype=torch.int64, device=cx.dev, generator=gen)
+                     for _ in range(R)]
+            slots = [w.clone() for w in words]
+            out = [torch.empty(nwords, dtype=torch.int32, device=cx.dev) for _ in range(R)]
+            stale = torch.zeros(R * nblk, dtype=torch.uint8, device=cx.dev)
+            done = torch.zeros(R * nblk, dtype=torch.uint8, device=cx.dev)
+            cnt = torch.zeros(2, dtype=torch.int32, device=cx.dev)
+            sets.append((words, slots, out, stale, done, cnt))
+
+        def set_epochs(late):
+            for words, slots, *_ in sets:
+                for r in range(R):
+                    slots[r].copy_(words[r] | ((eps[r] if late else good) << 32))
+
+        def run(k):
+            _, slots, out, stale, done, cnt = sets[k]
+            _lib.fc_ll_gather(slots, nwords, B, e, out, stale, done, cnt)
+        g = cx.graph(run, nsets)
+        t1, t2 = [], []
+        for _ in range(5):
+            set_epochs(True)
+            for s in sets:
+                s[4].zero_()
+                s[5].zero_()
+            torch.cuda.synchronize()
+            t1.append(_once(cx, g, nsets))
+            pend = int(sets[0][5].cpu().numpy().view(np.uint32)[1])
+            set_epochs(False)
+            torch.cuda.synchronize()
+            t2.append(_once(cx, g, nsets))
+        by1 = bm.total(bm.ll_gather(R, nwords, B, completed_blocks=R * nblk - pend))
+        us1, us2 = statistics.median(t1), statistics.median(t2)
+        res[tag] = {"R": R, "words_per_rank": nwords, "pass1_us": round(us1, 2), "pass1_bytes": by1,
+                    "pass1_GB/s": round(by1 / (us1 * 1e-6) / 1e9, 1), "pending_pairs": pend, "pairs": R * nblk,
+                    "retry_us": round(us2, 2), "buffer_sets": nsets}
+        del sets, g
+        torch.cuda.empty_cache()
+    return {"workload": "standalone all-gather on epoch-tagged blocks, B=64, 2% late", "by_payload": res}
+
+
 def _once(cx, g, per):
     torch = cx.torch
     a, b = cx.ev(), cx.ev()
@@ -650,6 +729,9 @@ def main():
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
         return 0
+    if args.stats_table:
+        stats_table(*args.stats_table)
+        return 0
     if args.profile_report:
         c, *paths = args.profile_report
         profile_report(int(c), *paths)
@@ -687,7 +769,7 @@ def main():
                      "traffic": tr["total"] if tr else None},
         "wall_s": round(main_r["wall"], 3),
     }
-    rows = {"prefill", "ll", "rmsnorm", "share", "normfirst", "layer"} if args.rows == "all" else set() if args.rows == "none" \
+    rows = {"prefill", "ll", "llgather", "rmsnorm", "share", "normfirst", "layer"} if args.rows == "all" else set() if args.rows == "none" \
         else set(args.rows.split(","))
     extra = {}
     if "prefill" in rows and args.config != 3:
@@ -714,6 +796,8 @@ def main():
                 "share": bench_share(cx, c, st, wu, 0, norm_first=True)}
     if "ll" in rows:
         extra["self_sync_slots"] = bench_ll(cx)
+    if "llgather" in rows:
+        extra["self_sync_allgather"] = bench_ll_gather(cx)
     if "rmsnorm" in rows:
         extra["tokenweave_reduce_rmsnorm"] = bench_rmsnorm_overlap(cx)
     if "layer" in rows:

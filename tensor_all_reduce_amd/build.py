@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["fc_kernels.hip", "fc_api.cpp"]
+SOURCES = ["fc_twostep.hip", "fc_slots.hip", "fc_api.cpp"]
 
 # -ffp-contract=off: a*b+c stays two roundings unless written as an explicit fma, which the bit-exact
 # quantization codes depend on.  Packed fp32 instructions are disabled.  -fno-honor-nans on the kernels:
@@ -54,7 +54,8 @@ def _run(cmd):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = []
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
@@ -62,10 +63,13 @@ def build(verbose: bool = False) -> str:
             cmd = [HIPCC, *DEVICE, *COMMON, "-c", path, "-o", obj]
         else:
             cmd = [HIPCC, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-c", path, "-o", obj]
-        out = _run(cmd)
+        jobs.append((cmd, obj))
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:  # one compiler process per source file
+        outs = list(ex.map(lambda j: _run(j[0]), jobs))
+    for out in outs:
         if verbose and out.strip():
             print(out)
-        objs.append(obj)
+    objs = [obj for _, obj in jobs]
     tlib = torch_lib_dir()
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,

@@ -94,3 +94,12 @@ def two_step_normfirst_share(R, T, H, bits_rs, bits_ag, group) -> dict:
     return dict(quantize=quantize(n, bits_rs, group),
                 reduce_shard=reduce_norm(R, L, bits_rs, bits_ag, group, 1, H),
                 gather=gather(R, L, bits_ag, group, H, plain=True, norm=False, residual=False, residual_out=False))
+
+
+def ll_gather(R: int, nwords: int, block_slots: int, completed_blocks: int | None = None) -> dict:
+    """Standalone all-gather on epoch-tagged blocks: every rank's slots read once (8 B per payload word:
+    4 payload, 4 epoch), done flags read, payload words written for the (rank, block) pairs completed (all
+    by default), stale and done flags written."""
+    nblk = R * (nwords // block_slots)
+    done_b = nblk if completed_blocks is None else completed_blocks
+    return dict(read=R * 8 * nwords + nblk, write=4 * block_slots * done_b + nblk + done_b)

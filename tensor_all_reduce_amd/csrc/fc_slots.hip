@@ -1,0 +1,366 @@
+// fc_slots.hip -- gfx950 kernels of the self-synchronizing slot transfers (reduce-scatter receive side,
+// standalone all-gather, sender emulation) and the copy-ceiling kernel, with their launchers.
+//
+// Same layout rule as the other kernels: one wavefront-wide memory instruction covers one contiguous
+// span (2 slots = 16 bytes per lane), loads never sit in lane-divergent branches, and wavefront-uniform
+// values (block verdicts, counts) stay on the scalar unit.
+#include "fc_device.h"
+#include "fc_launch.h"
+
+namespace fc {
+
+// =====================================================================================================
+// Self-synchronizing slots (flash-comm, abstract): the receiver validates each block's epoch words
+// itself, with no barrier.  A wavefront owns a tile of KI*128 slots, read by KI instructions of 128
+// slots (2 slots = 16 bytes per lane), KI = 2 so that 2*8 slot loads are in flight per lane.  Block
+// verdicts and counters are wavefront-uniform and kept on the scalar unit.  A block of B <= 128 slots
+// covers B/2 aligned lanes of one instruction (its verdict is a field of that instruction's ballot); a
+// block of 256 slots covers two consecutive instructions (the OR of both).
+// =====================================================================================================
+// Only the slot pointers are read from the argument segment; the scalars lead the kernel's argument
+// list and arrive preloaded in registers.  Entries past R repeat rank R-1 (read and ignored).
+struct LLSlots {
+    const uint64_t* p[kMaxRanks];
+};
+
+// 1 if x != 0, else 0, for a wavefront-uniform x, on the scalar unit (written out because the compiler
+// turns the comparison into a vector select and a read-back).  s_min_u32 also sets SCC.
+__device__ __forceinline__ uint32_t s_nonzero(uint32_t x) {
+    uint32_t y;
+    asm("s_min_u32 %0, %1, 1" : "=s"(y) : "s"(x) : "scc");
+    return y;
+}
+
+// One rank's slots of a wavefront tile: fold the payload into acc and record, for each block, whether
+// this copy is stale (vs[k][b] bit r, block b of instruction k; wavefront-uniform).
+template <int LB, int KI>
+__device__ __forceinline__ void ll_examine(const uint4 (&q)[KI], int r, uint32_t epoch, const uint64_t (&amask)[KI],
+                                           float (&acc)[KI][4], uint32_t (&vs)[KI][64 / LB]) {
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+        // epoch words: the high halves of the two slots
+        const uint64_t bal = (__ballot(q[k].y != epoch) | __ballot(q[k].w != epoch)) & amask[k];
+        uint32_t lo = (uint32_t)bal, hi = (uint32_t)(bal >> 32);
+        // keep the halves opaque scalars: otherwise "hi != 0" becomes a 64-bit compare on the vector unit
+        asm("" : "+s"(lo), "+s"(hi));
+        if constexpr (LB == 64) {
+            vs[k][0] |= s_nonzero(lo | hi) << r;
+        } else if constexpr (LB == 32) {
+            vs[k][0] |= s_nonzero(lo) << r;
+            vs[k][1] |= s_nonzero(hi) << r;
+        } else {  // LB == 16
+            vs[k][0] |= s_nonzero(lo & 0xffffu) << r;
+            vs[k][1] |= s_nonzero(lo >> 16) << r;
+            vs[k][2] |= s_nonzero(hi & 0xffffu) << r;
+            vs[k][3] |= s_nonzero(hi >> 16) << r;
+        }
+        const float v[4] = {bf16_lo(q[k].x), bf16_hi(q[k].x), bf16_lo(q[k].z), bf16_hi(q[k].z)};
+        if (r == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[k][e] = v[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[k][e] = acc[k][e] + v[e];
+        }
+    }
+}
+
+template <int B>
+__global__ __launch_bounds__(256) void k_ll_unpack(const int64_t nslots, const int64_t nblk, uint8_t* done,
+                                                   const uint32_t epoch, const int R, uint16_t* out, uint8_t* stale,
+                                                   uint32_t* counters, const LLSlots slots) {
+    constexpr int KI = 2;                      // instructions per wavefront tile
+    constexpr int IB = B <= 128 ? 1 : 2;       // instructions per block
+    constexpr int LB = B <= 128 ? B / 2 : 64;  // lanes of one instruction inside one block
+    constexpr int RB = 8;                      // ranks whose slots are loaded before any is examined
+    static_assert(KI % IB == 0, "a tile holds whole blocks");
+    static_assert(LB >= kMaxRanks && (LB == 16 || LB == 32 || LB == 64), "one lane per rank writes a block's stale flags");
+    __shared__ uint32_t s_cnt[4][2];  // per wavefront: stale pairs, pending blocks
+    const int lane = threadIdx.x & 63;
+    const int bl = lane % LB;  // lane inside its block's lanes
+    const int64_t tile = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (128 * KI);
+    int64_t slot[KI], blk[KI], src[KI];
+    bool inside[KI];
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+        slot[k] = tile + k * 128 + 2 * lane;
+        inside[k] = slot[k] < nslots;
+        blk[k] = inside[k] ? slot[k] / B : nblk - 1;
+        src[k] = inside[k] ? slot[k] : 0;
+    }
+    // The done flags and the first batch of slot loads are issued together, the slots at addresses that do
+    // not depend on the flags, so that their memory latencies overlap (a block already done is read anyway
+    // and ignored).  Loads are never inside a lane-divergent branch: blk is clamped, and a batch past the
+    // last rank re-reads the last rank's slots (the launcher repeats its pointer), which are ignored.
+    uint8_t dn[KI];
+#pragma unroll
+    for (int k = 0; k < KI; ++k) dn[k] = done[blk[k]];
+    uint4 sv[RB][KI];
+#pragma unroll
+    for (int j = 0; j < RB; ++j)
+#pragma unroll
+        for (int k = 0; k < KI; ++k) sv[j][k] = lds16(slots.p[j] + src[k]);
+    bool active[KI];
+    uint64_t amask[KI];  // lanes of blocks to examine (inside the buffer and not done yet)
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+        active[k] = inside[k] && dn[k] == 0;
+        amask[k] = __ballot(active[k]);
+    }
+
+    // Verdicts are wavefront-uniform: vs[k][q] bit r = rank r's copy of block q of instruction k is stale
+    // (NBW = 64/LB blocks per instruction), kept in scalar registers.
+    constexpr int NBW = 64 / LB;
+    float acc[KI][4];
+    uint32_t vs[KI][NBW] = {};
+#pragma unroll
+    for (int j = 0; j < RB; ++j)
+        if (j < R) ll_examine<LB, KI>(sv[j], j, epoch, amask, acc, vs);  // uniform condition
+    for (int r0 = RB; r0 < R; r0 += RB) {  // more than 8 ranks
+#pragma unroll
+        for (int j = 0; j < RB; ++j)
+#pragma unroll
+            for (int k = 0; k < KI; ++k) sv[j][k] = lds16(slots.p[r0 + j] + src[k]);
+#pragma unroll
+        for (int j = 0; j < RB; ++j)
+            if (r0 + j < R) ll_examine<LB, KI>(sv[j], r0 + j, epoch, amask, acc, vs);
+    }
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+        // this lane's block verdict; a two-instruction block (IB = 2) combines both instructions
+        // (selected with masks: a select between array elements would make the array memory-resident)
+        uint32_t sm;
+        if constexpr (IB == 2) {
+            sm = vs[k & ~1][0] | vs[k | 1][0];
+        } else if constexpr (NBW == 1) {
+            sm = vs[k][0];
+        } else {
+            const uint32_t h32 = 0u - (uint32_t)(lane >> 5);  // all ones in the upper half-wavefront
+            if constexpr (NBW == 2) {
+                sm = (vs[k][0] & ~h32) | (vs[k][1] & h32);
+            } else {
+                const uint32_t h16 = 0u - (uint32_t)((lane >> 4) & 1);
+                const uint32_t lo2 = (vs[k][0] & ~h16) | (vs[k][1] & h16);
+                const uint32_t hi2 = (vs[k][2] & ~h16) | (vs[k][3] & h16);
+                sm = (lo2 & ~h32) | (hi2 & h32);
+            }
+        }
+        if (!active[k]) continue;
+        // lane bl < R of the block writes rank bl's flag (for a two-instruction block, the first one's lanes)
+        if ((IB == 1 || k % 2 == 0) && bl < R) stale[(int64_t)bl * nblk + blk[k]] = (sm >> bl) & 1u;
+        if (sm == 0) {
+            sts8(out + 2 * slot[k], make_uint2(pack_bf16x2(acc[k][0], acc[k][1]), pack_bf16x2(acc[k][2], acc[k][3])));
+            if ((IB == 1 || k % 2 == 0) && bl == 0) done[blk[k]] = 1;
+        }
+    }
+    // Counters, from wavefront-uniform values only (scalar unit): block b of instruction k was examined
+    // iff the first lane of its lanes was active.
+    uint32_t n_stale = 0, n_pending = 0;
+#pragma unroll
+    for (int k = 0; k < KI; k += IB) {
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) {
+            const uint32_t v = IB == 2 ? (vs[k][0] | vs[k + 1][0]) : vs[k][b];
+            const uint32_t on = (uint32_t)(amask[k] >> (b * LB)) & 1u;
+            n_pending += on & s_nonzero(v);
+            n_stale += on * (uint32_t)__builtin_popcount(v);
+        }
+    }
+    if (lane == 0) {
+        s_cnt[threadIdx.x >> 6][0] = n_stale;
+        s_cnt[threadIdx.x >> 6][1] = n_pending;
+    }
+    __syncthreads();
+    // Both counters in one 64-bit atomic per workgroup: device-scope atomics on one address serialize,
+    // and the kernel ends only once the last one is done, so their number matters.  A call adds at most
+    // 2^29 stale pairs, so the low word does not carry.
+    if (threadIdx.x == 0) {
+        const uint32_t st = s_cnt[0][0] + s_cnt[1][0] + s_cnt[2][0] + s_cnt[3][0];
+        const uint32_t pe = s_cnt[0][1] + s_cnt[1][1] + s_cnt[2][1] + s_cnt[3][1];
+        if (st | pe) atomicAdd(reinterpret_cast<unsigned long long*>(counters), ((unsigned long long)pe << 32) | st);
+    }
+}
+
+hipError_t launch_ll_unpack(const LLParams& p, hipStream_t s) {
+    LLSlots t;
+    for (int i = 0; i < kMaxRanks; ++i) t.p[i] = p.slots[i < p.R ? i : p.R - 1];
+    const int64_t nslots = p.n / 2, nblk = nslots / p.block_slots;
+    const int64_t per_wg = 4 * 128 * 2;  // slots per workgroup: 4 wavefronts x 2 instructions x 128
+    const dim3 grid((unsigned)((nslots + per_wg - 1) / per_wg));
+#define FC_LL(B) k_ll_unpack<B><<<grid, 256, 0, s>>>(nslots, nblk, p.done, p.epoch, p.R, p.out, p.stale, p.counters, t)
+    switch (p.block_slots) {
+        case 32: FC_LL(32); break;
+        case 64: FC_LL(64); break;
+        case 128: FC_LL(128); break;
+        default: FC_LL(256); break;
+    }
+#undef FC_LL
+    return hipGetLastError();
+}
+
+// Standalone all-gather on self-synchronizing blocks (flash-comm, abstract: the same readiness evidence
+// carries an all-gather): grid row y = rank.  Rank r's payload words travel in the low halves of its slots;
+// a wavefront owns KI*128 slots of one rank (2 slots = 16 bytes per lane per instruction).  A block not yet
+// done is copied to out[r] when every slot carries the expected epoch, else flagged stale and left pending.
+// Block verdicts and counts are wavefront-uniform (scalar unit); counters: one 64-bit atomic per workgroup.
+struct LLGatherTabs {
+    const uint64_t* slots[kMaxRanks];
+    uint32_t* out[kMaxRanks];
+};
+
+template <int B>
+__global__ __launch_bounds__(256) void k_ll_gather(const int64_t nslots, const int64_t nblk, uint8_t* done,
+                                                   uint8_t* stale, const uint32_t epoch, uint32_t* counters,
+                                                   const LLGatherTabs t) {
+    constexpr int KI = 4;                      // instructions per wavefront tile
+    constexpr int IB = B <= 128 ? 1 : 2;       // instructions per block
+    constexpr int LB = B <= 128 ? B / 2 : 64;  // lanes of one instruction inside one block
+    constexpr int NBW = 64 / LB;               // blocks per instruction
+    static_assert(KI % IB == 0, "a tile holds whole blocks");
+    __shared__ uint32_t s_cnt[4];
+    const int r = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int bl = lane % LB;
+    const int64_t tile = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (128 * KI);
+    const uint64_t* sp = t.slots[r];
+    uint8_t* dn = done + (int64_t)r * nblk;
+    int64_t slot[KI], blk[KI];
+    bool inside[KI];
+    uint8_t dv[KI];
+    uint4 v[KI];
+    // done flags and slots are loaded together (a block already done is read and ignored); no load sits in
+    // a lane-divergent branch: lanes past the end read a clamped address
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+        slot[k] = tile + k * 128 + 2 * lane;
+        inside[k] = slot[k] < nslots;
+        blk[k] = inside[k] ? slot[k] / B : nblk - 1;
+        dv[k] = dn[blk[k]];
+    }
+#pragma unroll
+    for (int k = 0; k < KI; ++k) v[k] = lds16(sp + (inside[k] ? slot[k] : 0));
+    bool active[KI];
+    uint64_t amask[KI];
+    uint32_t vs[KI][NBW];
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+        active[k] = inside[k] && dv[k] == 0;
+        amask[k] = __ballot(active[k]);
+        const uint64_t bal = (__ballot(v[k].y != epoch) | __ballot(v[k].w != epoch)) & amask[k];
+        uint32_t lo = (uint32_t)bal, hi = (uint32_t)(bal >> 32);
+        asm("" : "+s"(lo), "+s"(hi));
+        if constexpr (LB == 64) {
+            vs[k][0] = s_nonzero(lo | hi);
+        } else if constexpr (LB == 32) {
+            vs[k][0] = s_nonzero(lo);
+            vs[k][1] = s_nonzero(hi);
+        } else {  // LB == 16
+            vs[k][0] = s_nonzero(lo & 0xffffu);
+            vs[k][1] = s_nonzero(lo >> 16);
+            vs[k][2] = s_nonzero(hi & 0xffffu);
+            vs[k][3] = s_nonzero(hi >> 16);
+        }
+    }
+    uint32_t* op = t.out[r];
+    uint8_t* sf = stale + (int64_t)r * nblk;
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+        uint32_t sm;  // this lane's block: 1 = stale
+        if constexpr (IB == 2) {
+            sm = vs[k & ~1][0] | vs[k | 1][0];
+        } else if constexpr (NBW == 1) {
+            sm = vs[k][0];
+        } else {
+            const uint32_t h32 = 0u - (uint32_t)(lane >> 5);
+            if constexpr (NBW == 2) {
+                sm = (vs[k][0] & ~h32) | (vs[k][1] & h32);
+            } else {
+                const uint32_t h16 = 0u - (uint32_t)((lane >> 4) & 1);
+                sm = (((vs[k][0] & ~h16) | (vs[k][1] & h16)) & ~h32) | (((vs[k][2] & ~h16) | (vs[k][3] & h16)) & h32);
+            }
+        }
+        if (!active[k]) continue;
+        const bool leader = (IB == 1 || k % 2 == 0) && bl == 0;
+        if (leader) sf[blk[k]] = (uint8_t)sm;
+        if (sm == 0) {
+            sts8(op + slot[k], make_uint2(v[k].x, v[k].z));
+            if (leader) dn[blk[k]] = 1;
+        }
+    }
+    uint32_t n_stale = 0;
+#pragma unroll
+    for (int k = 0; k < KI; k += IB) {
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) {
+            const uint32_t on = (uint32_t)(amask[k] >> (b * LB)) & 1u;
+            n_stale += on & (IB == 2 ? (vs[k][0] | vs[k + 1][0]) : vs[k][b]);
+        }
+    }
+    if (lane == 0) s_cnt[threadIdx.x >> 6] = n_stale;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t st = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+        // stale pairs and pending pairs are the same pairs here; one 64-bit atomic adds both counters
+        if (st) atomicAdd(reinterpret_cast<unsigned long long*>(counters), ((unsigned long long)st << 32) | st);
+    }
+}
+
+hipError_t launch_ll_gather(const LLGatherParams& p, hipStream_t s) {
+    LLGatherTabs t;
+    for (int i = 0; i < kMaxRanks; ++i) {
+        t.slots[i] = p.slots[i < p.R ? i : p.R - 1];
+        t.out[i] = p.out[i < p.R ? i : p.R - 1];
+    }
+    const int64_t nslots = p.nwords, nblk = nslots / p.block_slots;
+    const int64_t per_wg = 4 * 128 * 4;  // slots per workgroup: 4 wavefronts x 4 instructions x 128
+    const dim3 grid((unsigned)((nslots + per_wg - 1) / per_wg), (unsigned)p.R);
+#define FC_LLG(B) k_ll_gather<B><<<grid, 256, 0, s>>>(nslots, nblk, p.done, p.stale, p.epoch, p.counters, t)
+    switch (p.block_slots) {
+        case 32: FC_LLG(32); break;
+        case 64: FC_LLG(64); break;
+        case 128: FC_LLG(128); break;
+        default: FC_LLG(256); break;
+    }
+#undef FC_LLG
+    return hipGetLastError();
+}
+
+// Sender emulation: lane t of the write order packs 2 slots (4 bf16 in, 16 bytes out) of block
+// order[t / (B/2)].  An order entry outside [0, nblk) (not a permutation: out of contract) writes nothing.
+__global__ __launch_bounds__(256) void k_ll_pack(const uint16_t* __restrict__ x, int64_t nthreads, int lpb,
+                                                 int block_slots, int64_t nblk, const int32_t* __restrict__ order,
+                                                 uint32_t epoch, uint64_t* __restrict__ slots) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= nthreads) return;
+    const int64_t j = t / lpb;
+    const int64_t b = order ? (int64_t)order[j] : j;
+    if (b < 0 || b >= nblk) return;
+    const int64_t k0 = b * block_slots + 2 * (t % lpb);
+    const uint2 xv = lds8(x + 2 * k0);
+    sts16(slots + k0, make_uint4(xv.x, epoch, xv.y, epoch));
+}
+
+hipError_t launch_ll_pack(const PackParams& p, hipStream_t s) {
+    const int64_t nthreads = p.n / 4;  // 2 slots = 4 elements per lane
+    const dim3 grid((unsigned)((nthreads + 255) / 256));
+    k_ll_pack<<<grid, 256, 0, s>>>(p.x, nthreads, p.block_slots / 2, p.block_slots, p.n / 2 / p.block_slots, p.order,
+                                   p.epoch, p.slots);
+    return hipGetLastError();
+}
+
+// =====================================================================================================
+// Copy ceiling: one 16-byte streamed load and store per lane.
+// =====================================================================================================
+__global__ __launch_bounds__(256) void k_copy(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t n16) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n16) sts16(dst + i, lds16(src + i));
+}
+
+hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s) {
+    const int64_t n16 = bytes / 16;
+    const int64_t blocks = (n16 + 255) / 256;  // bytes <= 2^40 keeps this under the grid limit
+    k_copy<<<(unsigned)blocks, 256, 0, s>>>(reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst), n16);
+    return hipGetLastError();
+}
+
+}  // namespace fc
