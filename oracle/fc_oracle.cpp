@@ -524,6 +524,35 @@ void or_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, int blo
     }
 }
 
+// ---- readiness by one flag word per block (flash-comm, abstract: the readiness evidence may also be a
+// per-block word published after the block's data; the cost-guided choice among encodings trades its
+// fence against the 8-byte slots' doubled bytes).  Rank r's payload is a dense bf16 [n] buffer; block b is
+// elements [b*E, (b+1)*E); flags[r][b] is written after the block (release) and read before it (acquire).
+// For every block not done: rank r's copy is stale iff flags[r][b] != epoch (its payload is then not read);
+// a block whose R copies are all valid is reduced (fp32 left fold in ascending rank order, one rounding to
+// bf16) and marked done, otherwise it is left untouched and pending.  counters as for the slots.
+void or_flag_unpack_reduce(const uint16_t* const* payload, const uint32_t* const* flags, int R, int64_t n,
+                           int block_elems, uint32_t epoch, uint16_t* out, uint8_t* stale, uint8_t* done,
+                           uint32_t* counters) {
+    const int64_t nblk = n / block_elems;
+    for (int64_t b = 0; b < nblk; ++b) {
+        if (done[b]) continue;
+        bool all_valid = true;
+        for (int r = 0; r < R; ++r) {
+            const bool st = flags[r][b] != epoch;
+            stale[(int64_t)r * nblk + b] = st ? 1 : 0;
+            if (st) { all_valid = false; counters[0] += 1; }
+        }
+        if (!all_valid) { counters[1] += 1; continue; }
+        for (int64_t i = b * block_elems; i < (b + 1) * block_elems; ++i) {
+            float acc = bf16_val(payload[0][i]);
+            for (int r = 1; r < R; ++r) acc = acc + bf16_val(payload[r][i]);
+            out[i] = bf16_rne(acc);
+        }
+        done[b] = 1;
+    }
+}
+
 // ---- standalone all-gather on self-synchronizing blocks (flash-comm, abstract: readiness evidence per
 // block; the all-gather is the second workload of the mechanism).  Rank r's payload is nwords 32-bit words
 // (bf16 pairs, or the words of a quantized message: codes then meta) carried in the low halves of its

@@ -66,6 +66,7 @@ def lib():
             L.or_ll_pack.argtypes = [u16p, i64, C.c_int, C.c_uint32, vp, u64p]
             L.or_ll_unpack_reduce.argtypes = [vp, C.c_int, i64, C.c_int, C.c_uint32, u16p, u8p, u8p, u32p]
             L.or_ll_gather.argtypes = [vp, C.c_int, i64, C.c_int, C.c_uint32, vp, u8p, u8p, u32p]
+            L.or_flag_unpack_reduce.argtypes = [vp, vp, C.c_int, i64, C.c_int, C.c_uint32, u16p, u8p, u8p, u32p]
             L.or_sumsq_tree.argtypes = [f32p, i64]
             L.or_sumsq_tree.restype = C.c_float
             L.or_norm_rows_f32.argtypes = [f32p, vp, u16p, C.c_float, i64, i64, f32p, vp]
@@ -191,6 +192,21 @@ def two_step(parts, bits1, bits2, group, residual=None, gamma=None, eps=1e-5, hi
                       hidden if hidden else n, _ptr(out), _ptr(rout))
     return dict(codes1=c1.reshape(R, -1), meta1=m1.reshape(R, -1), codes2=c2, meta2=m2, y=y, out=out,
                 residual_out=rout)
+
+
+def flag_unpack_reduce(payload_list, flags_list, n, block_elems, epoch, out=None, done=None, counters=None):
+    """Receiver of per-block flag words: returns (out bf16 [n], stale [R*nblk], done [nblk], counters [2])."""
+    R = len(payload_list)
+    nblk = n // block_elems
+    pl = [_c(p, np.uint16).ravel() for p in payload_list]
+    fl = [_c(f, np.uint32).ravel() for f in flags_list]
+    out = np.zeros(n, np.uint16) if out is None else _c(out, np.uint16).copy()
+    done = np.zeros(nblk, np.uint8) if done is None else _c(done, np.uint8).copy()
+    counters = np.zeros(2, np.uint32) if counters is None else _c(counters, np.uint32).copy()
+    stale = np.zeros(R * nblk, np.uint8)
+    lib().or_flag_unpack_reduce(_ptr_array(pl), _ptr_array(fl), R, n, block_elems, epoch & 0xFFFFFFFF, out, stale,
+                                done, counters)
+    return out, stale, done, counters
 
 
 def ll_gather(slots_list, nwords, block_slots, epoch, out=None, done=None, counters=None):
