@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define FC_ABI_VERSION 2
+#define FC_ABI_VERSION 3
 
 typedef enum {
     FC_OK = 0,
@@ -153,9 +153,53 @@ fc_status fc_ll_gather(const uint64_t* const* slots, int R, int64_t nwords, int 
 
 /* Sender side of the slots above, used to emulate a peer's writes: packs bf16 [n] into n/2 slots tagged
  * with `epoch`, writing blocks in the order block_order[0..nblk) (an int32 permutation of the block
- * indices, or NULL for ascending).  The result does not depend on the order. */
+ * indices, or NULL for ascending).  Each slot is written with one agent-scope atomic 64-bit store, so a
+ * receiver reading at the same time sees its payload and epoch word together.  pace (0..65536): each
+ * wavefront of the packer first sleeps pace x 512 clocks (a slow sender for runs where the receiver
+ * starts first; 0 for none).  The result does not depend on the order or the pace. */
 fc_status fc_ll_pack(const uint16_t* x, int64_t n, int block_slots, uint32_t epoch, const int32_t* block_order,
-                     uint64_t* slots, hipStream_t stream);
+                     int pace, uint64_t* slots, hipStream_t stream);
+
+/* Receiver of the slots above that may run while the senders still write (flash-comm, abstract: the
+ * receiver validates the blocks it needs itself, with no barrier between GPUs).  Arguments, verdicts and
+ * outputs as for fc_ll_unpack_reduce, except: every slot is read with an agent-scope atomic 64-bit load;
+ * a wavefront owns tiles of 256 slots and, while a rank still has a stale block in the tile, re-reads
+ * that rank's slots of the tile after a short sleep, at most max_polls times (0..2^20; 0 = one look, with
+ * the results of fc_ll_unpack_reduce); the verdicts are those of the last look.  max_workgroups > 0 caps
+ * the grid (the tiles are then walked with a stride), leaving compute units to a sender running at the
+ * same time; 0 = one tile per wavefront.  counters: uint32 [4], 8-byte aligned, zeroed by the caller:
+ * [0] stale (rank, block) pairs and [1] pending blocks at the last look (one 64-bit atomic add per
+ * workgroup), [2] += re-reads summed over wavefronts, [3] unused.  The call always ends: a block still
+ * stale after the budget is left pending for a later call. */
+fc_status fc_ll_poll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, int block_slots, uint32_t epoch,
+                                   int max_polls, int max_workgroups, uint16_t* out, uint8_t* stale, uint8_t* done,
+                                   uint32_t* counters, hipStream_t stream);
+
+/* Readiness by one flag word per block (flash-comm, abstract: the readiness encoding is a choice the
+ * protocol selector makes; this one sends the payload unchanged, plus one word per block).  payload
+ * [host array, R entries]: rank r's bf16 [n], 16-byte aligned; flags [host array, R entries]: rank r's
+ * uint32 [nblk], 4-byte aligned; a block is block_elems consecutive elements (a power of two, 512 ..
+ * 65536), nblk = n / block_elems.  The sender stores a block's payload, then the epoch into its flag
+ * word with release order (fc_flag_pack).  For each block b with done[b] == 0: rank r's copy is stale
+ * iff flags[r][b] != epoch, and stale[r*nblk + b] = 1, else 0; if no copy is stale, out (bf16 [n]) =
+ * bf16 of the fp32 sum of the R copies folded in ascending rank order, and done[b] = 1; otherwise the
+ * block stays pending and out is untouched.  The payload of a stale copy is never read.  Flags are read
+ * with agent-scope atomic loads, re-read after a short sleep while a copy in the wavefront's tile (one
+ * block, two of 512 elements) is stale, at most max_polls times (0..2^20; 0 = one look), then one
+ * acquire fence precedes the payload loads.  max_workgroups and counters as for
+ * fc_ll_poll_unpack_reduce.  Calling again after late blocks have been published completes them with
+ * the same bits as if they had been on time. */
+fc_status fc_flag_unpack_reduce(const uint16_t* const* payload, const uint32_t* const* flags, int R, int64_t n,
+                                int block_elems, uint32_t epoch, int max_polls, int max_workgroups, uint16_t* out,
+                                uint8_t* stale, uint8_t* done, uint32_t* counters, hipStream_t stream);
+
+/* Sender side of the flag encoding, used to emulate a peer: writes x (bf16 [n]) into payload block by
+ * block in the order block_order[0..nblk) (int32 permutation, or NULL for ascending), and after each
+ * block a release store of epoch into flags[b] (each wavefront of the writing workgroup first fences
+ * with release order, then the workgroup meets at a barrier).  pace: sleeps of 512 clocks before each
+ * block (0..65536).  block_elems as for fc_flag_unpack_reduce. */
+fc_status fc_flag_pack(const uint16_t* x, int64_t n, int block_elems, uint32_t epoch, const int32_t* block_order,
+                       int pace, uint16_t* payload, uint32_t* flags, hipStream_t stream);
 
 /* Measurement helper: copies `bytes` (a multiple of 16, at most 2^40, 16-byte aligned pointers, no
  * overlap) with one non-temporal 16-byte load and store per lane; its bandwidth is the practical HBM

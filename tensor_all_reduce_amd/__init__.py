@@ -5,7 +5,8 @@ bindings of the same names, loaded on first use.  ``datagen`` (seeded synthetic 
 import without loading the library.
 """
 _BINDINGS = ("fc_quantize", "fc_reduce_shard", "fc_gather_dequant", "fc_reduce_rmsnorm", "fc_ll_unpack_reduce",
-             "fc_ll_pack", "fc_copy", "fc_abi_version", "FcError", "lib")
+             "fc_ll_pack", "fc_ll_gather", "fc_ll_poll_unpack_reduce", "fc_flag_unpack_reduce", "fc_flag_pack",
+             "fc_reduce_shard_norm", "fc_copy", "fc_abi_version", "FcError", "lib")
 
 
 def __getattr__(name):

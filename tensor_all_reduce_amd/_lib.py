@@ -71,11 +71,16 @@ def _load():
     lib.fc_gather_dequant.argtypes = [C.POINTER(QMsg), i32, i64, i32, i32, vp, C.POINTER(Norm), vp]
     lib.fc_reduce_rmsnorm.argtypes = [C.POINTER(vp), i32, i64, C.POINTER(Norm), i32, vp]
     lib.fc_ll_unpack_reduce.argtypes = [C.POINTER(vp), i32, i64, i32, u32, vp, vp, vp, vp, vp]
-    lib.fc_ll_pack.argtypes = [vp, i64, i32, u32, vp, vp, vp]
+    lib.fc_ll_pack.argtypes = [vp, i64, i32, u32, vp, i32, vp, vp]
+    lib.fc_ll_poll_unpack_reduce.argtypes = [C.POINTER(vp), i32, i64, i32, u32, i32, i32, vp, vp, vp, vp, vp]
+    lib.fc_flag_unpack_reduce.argtypes = [C.POINTER(vp), C.POINTER(vp), i32, i64, i32, u32, i32, i32, vp, vp, vp,
+                                          vp, vp]
+    lib.fc_flag_pack.argtypes = [vp, i64, i32, u32, vp, i32, vp, vp, vp]
     lib.fc_ll_gather.argtypes = [C.POINTER(vp), i32, i64, i32, u32, C.POINTER(vp), vp, vp, vp, vp]
     lib.fc_copy.argtypes = [vp, vp, i64, vp]
     for f in ("fc_quantize", "fc_reduce_shard", "fc_reduce_shard_norm", "fc_gather_dequant", "fc_reduce_rmsnorm", "fc_ll_unpack_reduce",
-              "fc_ll_pack", "fc_ll_gather", "fc_copy"):
+              "fc_ll_pack", "fc_ll_gather", "fc_ll_poll_unpack_reduce", "fc_flag_unpack_reduce", "fc_flag_pack",
+              "fc_copy"):
         getattr(lib, f).restype = i32
     return lib
 
@@ -178,10 +183,39 @@ def fc_ll_gather(slots, nwords: int, block_slots: int, epoch: int, out, stale, d
                              _ptr(counters), _stream(stream)), "fc_ll_gather")
 
 
-def fc_ll_pack(x, block_slots: int, epoch: int, slots, block_order=None, n: int | None = None, stream=None) -> None:
+def fc_ll_pack(x, block_slots: int, epoch: int, slots, block_order=None, n: int | None = None, pace: int = 0,
+               stream=None) -> None:
     n = x.numel() if n is None else n
-    _check(_lib.fc_ll_pack(_ptr(x), n, block_slots, epoch & 0xFFFFFFFF, _ptr(block_order), _ptr(slots),
+    _check(_lib.fc_ll_pack(_ptr(x), n, block_slots, epoch & 0xFFFFFFFF, _ptr(block_order), pace, _ptr(slots),
                            _stream(stream)), "fc_ll_pack")
+
+
+def fc_ll_poll_unpack_reduce(slots, n: int, block_slots: int, epoch: int, out, stale, done, counters,
+                             max_polls: int = 0, max_workgroups: int = 0, stream=None) -> None:
+    """counters: 4 int32 (stale pairs, pending blocks, re-reads, unused)."""
+    R = len(slots)
+    arr = (C.c_void_p * R)(*[_ptr(s) for s in slots])
+    _check(_lib.fc_ll_poll_unpack_reduce(arr, R, n, block_slots, epoch & 0xFFFFFFFF, max_polls, max_workgroups,
+                                         _ptr(out), _ptr(stale), _ptr(done), _ptr(counters), _stream(stream)),
+           "fc_ll_poll_unpack_reduce")
+
+
+def fc_flag_unpack_reduce(payload, flags, n: int, block_elems: int, epoch: int, out, stale, done, counters,
+                          max_polls: int = 0, max_workgroups: int = 0, stream=None) -> None:
+    """payload: R bf16 (int16) buffers; flags: R int32 buffers of n / block_elems words; counters: 4 int32."""
+    R = len(payload)
+    pa = (C.c_void_p * R)(*[_ptr(p) for p in payload])
+    fa = (C.c_void_p * R)(*[_ptr(f) for f in flags])
+    _check(_lib.fc_flag_unpack_reduce(pa, fa, R, n, block_elems, epoch & 0xFFFFFFFF, max_polls, max_workgroups,
+                                      _ptr(out), _ptr(stale), _ptr(done), _ptr(counters), _stream(stream)),
+           "fc_flag_unpack_reduce")
+
+
+def fc_flag_pack(x, block_elems: int, epoch: int, payload, flags, block_order=None, n: int | None = None,
+                 pace: int = 0, stream=None) -> None:
+    n = x.numel() if n is None else n
+    _check(_lib.fc_flag_pack(_ptr(x), n, block_elems, epoch & 0xFFFFFFFF, _ptr(block_order), pace, _ptr(payload),
+                             _ptr(flags), _stream(stream)), "fc_flag_pack")
 
 
 def fc_copy(src, dst, nbytes: int | None = None, stream=None) -> None:

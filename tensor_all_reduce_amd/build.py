@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["fc_twostep.hip", "fc_slots.hip", "fc_api.cpp"]
+SOURCES = ["fc_twostep.hip", "fc_slots.hip", "fc_live.hip", "fc_api.cpp"]
 
 # -ffp-contract=off: a*b+c stays two roundings unless written as an explicit fma, which the bit-exact
 # quantization codes depend on.  Packed fp32 instructions are disabled.  -fno-honor-nans on the kernels:

@@ -17,6 +17,15 @@ constexpr int64_t kMaxHidden = 65536;
 bool valid_bits(int b) { return b == 4 || b == 8; }
 bool valid_group(int g) { return g == 32 || g == 64 || g == 128 || g == 256; }
 bool valid_block(int b) { return b == 32 || b == 64 || b == 128 || b == 256; }
+constexpr int kMaxPolls = 1 << 20;  // re-reads per tile of a polling receiver
+constexpr int kMaxPace = 1 << 16;   // sender sleeps per block
+
+// log2 of a flag-encoding block (a power of two from 512 to 65536 elements), or -1
+int log2_flag_block(int b) {
+    for (int l = 9; l <= 16; ++l)
+        if (b == (1 << l)) return l;
+    return -1;
+}
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 struct Range {
@@ -374,8 +383,8 @@ fc_status fc_ll_gather(const uint64_t* const* slots, int R, int64_t nwords, int 
 }
 
 fc_status fc_ll_pack(const uint16_t* x, int64_t n, int block_slots, uint32_t epoch, const int32_t* block_order,
-                     uint64_t* slots, hipStream_t stream) {
-    if (!valid_block(block_slots) || n < 0) return FC_E_ARG;
+                     int pace, uint64_t* slots, hipStream_t stream) {
+    if (!valid_block(block_slots) || n < 0 || pace < 0 || pace > kMaxPace) return FC_E_ARG;
     if (n % (2 * block_slots) != 0 || n > kMaxElems) return FC_E_SHAPE;
     if (n == 0) return FC_OK;
     if (!x || !slots) return FC_E_NULL;
@@ -383,7 +392,94 @@ fc_status fc_ll_pack(const uint16_t* x, int64_t n, int block_slots, uint32_t epo
     const Range sr = rng(slots, 4 * n);
     if (overlap(sr, rng(x, 2 * n)) || (block_order && overlap(sr, rng(block_order, 4 * (n / 2 / block_slots)))))
         return FC_E_ARG;
-    return launched(fc::launch_ll_pack(fc::PackParams{x, n, block_slots, epoch, block_order, slots}, stream));
+    return launched(fc::launch_ll_pack(fc::PackParams{x, n, block_slots, epoch, block_order, pace, slots}, stream));
+}
+
+fc_status fc_ll_poll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, int block_slots, uint32_t epoch,
+                                   int max_polls, int max_workgroups, uint16_t* out, uint8_t* stale, uint8_t* done,
+                                   uint32_t* counters, hipStream_t stream) {
+    if (R < 1 || R > fc::kMaxRanks || !valid_block(block_slots) || n < 0) return FC_E_ARG;
+    if (max_polls < 0 || max_polls > kMaxPolls || max_workgroups < 0) return FC_E_ARG;
+    if (n % (2 * block_slots) != 0 || n > kMaxElems) return FC_E_SHAPE;
+    if (n == 0) return FC_OK;
+    if (!slots || !out || !stale || !done || !counters) return FC_E_NULL;
+    if (!aligned(out, 16) || !aligned(counters, 8)) return FC_E_ALIGN;
+    const int64_t nblk = n / 2 / block_slots;
+    const Range ro = rng(out, 2 * n), rs = rng(stale, (int64_t)R * nblk), rd = rng(done, nblk), rc = rng(counters, 16);
+    if (overlap(ro, rs) || overlap(ro, rd) || overlap(ro, rc) || overlap(rs, rd) || overlap(rs, rc) || overlap(rd, rc))
+        return FC_E_ARG;
+    for (int r = 0; r < R; ++r) {
+        if (!slots[r]) return FC_E_NULL;
+        if (!aligned(slots[r], 16)) return FC_E_ALIGN;
+        const Range sr = rng(slots[r], 4 * n);
+        if (overlap(sr, ro) || overlap(sr, rs) || overlap(sr, rd) || overlap(sr, rc)) return FC_E_ARG;
+    }
+    fc::LLParams p;
+    for (int r = 0; r < fc::kMaxRanks; ++r) p.slots[r] = r < R ? slots[r] : nullptr;
+    p.R = R;
+    p.n = n;
+    p.block_slots = block_slots;
+    p.epoch = epoch;
+    p.out = out;
+    p.stale = stale;
+    p.done = done;
+    p.counters = counters;
+    return launched(fc::launch_ll_poll(p, fc::PollParams{max_polls, max_workgroups}, stream));
+}
+
+fc_status fc_flag_unpack_reduce(const uint16_t* const* payload, const uint32_t* const* flags, int R, int64_t n,
+                                int block_elems, uint32_t epoch, int max_polls, int max_workgroups, uint16_t* out,
+                                uint8_t* stale, uint8_t* done, uint32_t* counters, hipStream_t stream) {
+    const int lb = log2_flag_block(block_elems);
+    if (R < 1 || R > fc::kMaxRanks || lb < 0 || n < 0) return FC_E_ARG;
+    if (max_polls < 0 || max_polls > kMaxPolls || max_workgroups < 0) return FC_E_ARG;
+    if (n % block_elems != 0 || n > kMaxElems) return FC_E_SHAPE;
+    if (n == 0) return FC_OK;
+    if (!payload || !flags || !out || !stale || !done || !counters) return FC_E_NULL;
+    if (!aligned(out, 16) || !aligned(counters, 8)) return FC_E_ALIGN;
+    const int64_t nblk = n / block_elems;
+    const Range ro = rng(out, 2 * n), rs = rng(stale, (int64_t)R * nblk), rd = rng(done, nblk), rc = rng(counters, 16);
+    if (overlap(ro, rs) || overlap(ro, rd) || overlap(ro, rc) || overlap(rs, rd) || overlap(rs, rc) || overlap(rd, rc))
+        return FC_E_ARG;
+    for (int r = 0; r < R; ++r) {
+        if (!payload[r] || !flags[r]) return FC_E_NULL;
+        if (!aligned(payload[r], 16) || !aligned(flags[r], 4)) return FC_E_ALIGN;
+        for (const Range in : {rng(payload[r], 2 * n), rng(flags[r], 4 * nblk)})
+            if (overlap(in, ro) || overlap(in, rs) || overlap(in, rd) || overlap(in, rc)) return FC_E_ARG;
+    }
+    fc::FlagParams p;
+    for (int r = 0; r < fc::kMaxRanks; ++r) {
+        p.payload[r] = r < R ? payload[r] : nullptr;
+        p.flags[r] = r < R ? flags[r] : nullptr;
+    }
+    p.R = R;
+    p.n = n;
+    p.log2_block = lb;
+    p.epoch = epoch;
+    p.out = out;
+    p.stale = stale;
+    p.done = done;
+    p.counters = counters;
+    p.poll = fc::PollParams{max_polls, max_workgroups};
+    return launched(fc::launch_flag_unpack(p, stream));
+}
+
+fc_status fc_flag_pack(const uint16_t* x, int64_t n, int block_elems, uint32_t epoch, const int32_t* block_order,
+                       int pace, uint16_t* payload, uint32_t* flags, hipStream_t stream) {
+    const int lb = log2_flag_block(block_elems);
+    if (lb < 0 || n < 0 || pace < 0 || pace > kMaxPace) return FC_E_ARG;
+    if (n % block_elems != 0 || n > kMaxElems) return FC_E_SHAPE;
+    if (n == 0) return FC_OK;
+    if (!x || !payload || !flags) return FC_E_NULL;
+    if (!aligned(x, 16) || !aligned(payload, 16) || !aligned(flags, 4) || (block_order && !aligned(block_order, 4)))
+        return FC_E_ALIGN;
+    const int64_t nblk = n / block_elems;
+    const Range rp = rng(payload, 2 * n), rf = rng(flags, 4 * nblk);
+    if (overlap(rp, rf) || overlap(rp, rng(x, 2 * n)) || overlap(rf, rng(x, 2 * n))) return FC_E_ARG;
+    if (block_order && (overlap(rp, rng(block_order, 4 * nblk)) || overlap(rf, rng(block_order, 4 * nblk))))
+        return FC_E_ARG;
+    return launched(
+        fc::launch_flag_pack(fc::FlagPackParams{x, n, lb, epoch, block_order, pace, payload, flags}, stream));
 }
 
 fc_status fc_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {

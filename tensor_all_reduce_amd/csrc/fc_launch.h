@@ -86,7 +86,39 @@ struct PackParams {
     int block_slots;
     uint32_t epoch;
     const int32_t* order;
+    int pace;
     uint64_t* slots;
+};
+
+// Receivers that may run while the senders write: bounded re-reads, optional cap on the grid.
+struct PollParams {
+    int max_polls;      // re-reads of a stale tile, 0 = one look
+    int max_workgroups; // 0 = one tile per wavefront
+};
+
+struct FlagParams {
+    const uint16_t* payload[kMaxRanks];
+    const uint32_t* flags[kMaxRanks];
+    int R;
+    int64_t n;
+    int log2_block;  // block of 2^log2_block elements, 9..16
+    uint32_t epoch;
+    uint16_t* out;
+    uint8_t* stale;  // [R][nblk]
+    uint8_t* done;   // [nblk]
+    uint32_t* counters;
+    PollParams poll;
+};
+
+struct FlagPackParams {
+    const uint16_t* x;
+    int64_t n;
+    int log2_block;
+    uint32_t epoch;
+    const int32_t* order;
+    int pace;
+    uint16_t* payload;
+    uint32_t* flags;
 };
 
 // Reduce-scatter receive side with the norm before the all-gather: rs as for launch_reduce; norm's
@@ -104,6 +136,9 @@ hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t s);
 hipError_t launch_ll_unpack(const LLParams& p, hipStream_t s);
 hipError_t launch_ll_pack(const PackParams& p, hipStream_t s);
 hipError_t launch_ll_gather(const LLGatherParams& p, hipStream_t s);
+hipError_t launch_ll_poll(const LLParams& p, const PollParams& q, hipStream_t s);
+hipError_t launch_flag_unpack(const FlagParams& p, hipStream_t s);
+hipError_t launch_flag_pack(const FlagPackParams& p, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 
 }  // namespace fc

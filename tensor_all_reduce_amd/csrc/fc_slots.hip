@@ -6,6 +6,7 @@
 // values (block verdicts, counts) stay on the scalar unit.
 #include "fc_device.h"
 #include "fc_launch.h"
+#include "fc_sync.h"
 
 namespace fc {
 
@@ -17,20 +18,6 @@ namespace fc {
 // covers B/2 aligned lanes of one instruction (its verdict is a field of that instruction's ballot); a
 // block of 256 slots covers two consecutive instructions (the OR of both).
 // =====================================================================================================
-// Only the slot pointers are read from the argument segment; the scalars lead the kernel's argument
-// list and arrive preloaded in registers.  Entries past R repeat rank R-1 (read and ignored).
-struct LLSlots {
-    const uint64_t* p[kMaxRanks];
-};
-
-// 1 if x != 0, else 0, for a wavefront-uniform x, on the scalar unit (written out because the compiler
-// turns the comparison into a vector select and a read-back).  s_min_u32 also sets SCC.
-__device__ __forceinline__ uint32_t s_nonzero(uint32_t x) {
-    uint32_t y;
-    asm("s_min_u32 %0, %1, 1" : "=s"(y) : "s"(x) : "scc");
-    return y;
-}
-
 // One rank's slots of a wavefront tile: fold the payload into acc and record, for each block, whether
 // this copy is stale (vs[k][b] bit r, block b of instruction k; wavefront-uniform).
 template <int LB, int KI>
@@ -325,26 +312,31 @@ hipError_t launch_ll_gather(const LLGatherParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Sender emulation: lane t of the write order packs 2 slots (4 bf16 in, 16 bytes out) of block
-// order[t / (B/2)].  An order entry outside [0, nblk) (not a permutation: out of contract) writes nothing.
+// Sender emulation: lane t of the write order packs 2 slots (4 bf16 in) of block order[t / (B/2)], each
+// slot with one agent-scope atomic 64-bit store, so that a receiver reading at the same time sees payload
+// and epoch word together.  Each wavefront first sleeps `pace` times (a slow sender).  An order entry
+// outside [0, nblk) (not a permutation: out of contract) writes nothing.
 __global__ __launch_bounds__(256) void k_ll_pack(const uint16_t* __restrict__ x, int64_t nthreads, int lpb,
                                                  int block_slots, int64_t nblk, const int32_t* __restrict__ order,
-                                                 uint32_t epoch, uint64_t* __restrict__ slots) {
+                                                 uint32_t epoch, int pace, uint64_t* __restrict__ slots) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    pace_sleep(pace);
     if (t >= nthreads) return;
     const int64_t j = t / lpb;
     const int64_t b = order ? (int64_t)order[j] : j;
     if (b < 0 || b >= nblk) return;
     const int64_t k0 = b * block_slots + 2 * (t % lpb);
     const uint2 xv = lds8(x + 2 * k0);
-    sts16(slots + k0, make_uint4(xv.x, epoch, xv.y, epoch));
+    const uint64_t tag = (uint64_t)epoch << 32;
+    st_relaxed(slots + k0, tag | xv.x);
+    st_relaxed(slots + k0 + 1, tag | xv.y);
 }
 
 hipError_t launch_ll_pack(const PackParams& p, hipStream_t s) {
     const int64_t nthreads = p.n / 4;  // 2 slots = 4 elements per lane
     const dim3 grid((unsigned)((nthreads + 255) / 256));
     k_ll_pack<<<grid, 256, 0, s>>>(p.x, nthreads, p.block_slots / 2, p.block_slots, p.n / 2 / p.block_slots, p.order,
-                                   p.epoch, p.slots);
+                                   p.epoch, p.pace, p.slots);
     return hipGetLastError();
 }
 

@@ -19,7 +19,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-PURPOSE = dict(values=0, outliers=1, residual=2, gamma=3, stale_mask=4, stale_values=5, permutation=6, gemm=7)
+PURPOSE = dict(values=0, outliers=1, residual=2, gamma=3, stale_mask=4, stale_values=5, permutation=6, gemm=7,
+               flag_mask=8, flag_values=9)
 
 
 @dataclass(frozen=True)
@@ -70,8 +71,9 @@ CONFIGS = {
 }
 
 
-def rng_for(cfg: int, purpose: str, rank: int = 0) -> np.random.Generator:
-    return np.random.default_rng(np.random.SeedSequence([0xFC, int(cfg), PURPOSE[purpose], int(rank)]))
+def rng_for(cfg: int, purpose: str, rank: int = 0, salt: int = 0) -> np.random.Generator:
+    words = [0xFC, int(cfg), PURPOSE[purpose], int(rank)] + ([int(salt)] if salt else [])
+    return np.random.default_rng(np.random.SeedSequence(words))
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -158,6 +160,36 @@ def stale_epochs(cfg: Config, rank: int, nslots: int, epoch: int | None = None,
         else:  # torn: one slot of the block not yet written
             ep[b * B + int(rv.integers(0, B))] = (e - 1) & M
     return ep, stale
+
+
+FLAG_KINDS = ("prev", "zero", "next", "not", "msb", "random")
+FLAG_WEIGHTS = (0.75, 0.05, 0.05, 0.05, 0.05, 0.05)
+
+
+def stale_flags(cfg: Config, rank: int, nblk: int, epoch: int | None = None, p: float | None = None,
+                salt: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """Per-block flag words of rank `rank` as the receiver sees them, and the stale mask.
+
+    Returns (flags uint32 [nblk], stale uint8 [nblk]).  A valid block's flag carries `epoch`; a stale one
+    carries one of the wrong words of FLAG_KINDS (a flag word is one store, so it cannot be torn)."""
+    e = int(cfg.epoch if epoch is None else epoch) & 0xFFFFFFFF
+    M = 0xFFFFFFFF
+    p = cfg.stale_p if p is None else p
+    stale = (rng_for(cfg.idx, "flag_mask", rank, salt).random(nblk) < p).astype(np.uint8)
+    fl = np.full(nblk, e, np.uint32)
+    rv = rng_for(cfg.idx, "flag_values", rank, salt)
+    idx = np.nonzero(stale)[0]
+    kinds = rv.choice(len(FLAG_KINDS), size=idx.size, p=FLAG_WEIGHTS)
+    wrong = {"prev": (e - 1) & M, "zero": 0 if e != 0 else 1, "next": (e + 1) & M, "not": (~e) & M,
+             "msb": e ^ 0x80000000}
+    for b, k in zip(idx, kinds):
+        kind = FLAG_KINDS[k]
+        if kind == "random":
+            r = int(rv.integers(0, 2**32, dtype=np.uint64))
+            fl[b] = r if r != e else e ^ 1
+        else:
+            fl[b] = wrong[kind]
+    return fl, stale
 
 
 def _seed_words(seed) -> list[int]:

@@ -28,11 +28,11 @@ def declared_functions():
 def test_exports_every_declared_function(L):
     names = declared_functions()
     assert {"fc_quantize", "fc_reduce_shard", "fc_reduce_shard_norm", "fc_gather_dequant", "fc_reduce_rmsnorm",
-            "fc_ll_unpack_reduce",
+            "fc_ll_unpack_reduce", "fc_ll_poll_unpack_reduce", "fc_flag_unpack_reduce", "fc_flag_pack",
             "fc_ll_pack", "fc_copy", "fc_status_string", "fc_last_hip_error", "fc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L.lib, n), n
-    assert L.fc_abi_version() == 2
+    assert L.fc_abi_version() == 3
 
 
 def test_single_hip_runtime(L):
@@ -188,10 +188,64 @@ def test_ll_validation(L):
     assert g(done=A + 0x4000000 + 8) == L.FC_E_ARG   # done inside the stale flags
     assert g(out=A + 0x1000000 + 64) == L.FC_E_ARG   # out inside rank 0's slots
     p = L.lib.fc_ll_pack
-    assert p(A, 4096, 60, 7, None, A + 0x1000000, None) == L.FC_E_ARG
-    assert p(A, 4000, 64, 7, None, A + 0x1000000, None) == L.FC_E_SHAPE
-    assert p(A, 4096, 64, 7, None, A + 8, None) == L.FC_E_ALIGN
-    assert p(A, 4096, 64, 7, None, A + 1024, None) == L.FC_E_ARG
+    assert p(A, 4096, 60, 7, None, 0, A + 0x1000000, None) == L.FC_E_ARG
+    assert p(A, 4096, 64, 7, None, -1, A + 0x1000000, None) == L.FC_E_ARG    # pace
+    assert p(A, 4096, 64, 7, None, 65537, A + 0x1000000, None) == L.FC_E_ARG
+    assert p(A, 4000, 64, 7, None, 0, A + 0x1000000, None) == L.FC_E_SHAPE
+    assert p(A, 4096, 64, 7, None, 0, A + 8, None) == L.FC_E_ALIGN
+    assert p(A, 4096, 64, 7, None, 0, A + 1024, None) == L.FC_E_ARG
+
+
+def test_ll_poll_validation(L):
+    f = L.lib.fc_ll_poll_unpack_reduce
+    sl = (C.c_void_p * 2)(A + 0x1000000, A + 0x2000000)
+    d = dict(out=A + 0x3000000, stale=A + 0x4000000, done=A + 0x5000000, cnt=A + 0x6000000)
+    g = lambda R=2, n=4096, B=64, polls=0, mw=0, s=sl, **kw: f(
+        s, R, n, B, 7, polls, mw, kw.get("out", d["out"]), kw.get("stale", d["stale"]), kw.get("done", d["done"]),
+        kw.get("cnt", d["cnt"]), None)
+    assert g(B=48) == L.FC_E_ARG
+    assert g(R=17) == L.FC_E_ARG
+    assert g(polls=-1) == L.FC_E_ARG
+    assert g(polls=(1 << 20) + 1) == L.FC_E_ARG
+    assert g(mw=-1) == L.FC_E_ARG
+    assert g(n=4096 + 64) == L.FC_E_SHAPE
+    assert g(n=0) == L.FC_OK
+    assert g(cnt=None) == L.FC_E_NULL
+    assert g(cnt=A + 0x6000004) == L.FC_E_ALIGN
+    assert g(out=A + 0x3000008) == L.FC_E_ALIGN
+    assert g(s=(C.c_void_p * 2)(A + 0x1000008, A + 0x2000000)) == L.FC_E_ALIGN
+    assert g(cnt=A + 0x5000000 - 8) == L.FC_E_ARG                    # counter words 2..3 reach into done
+    assert g(out=A + 0x2000000 + 64) == L.FC_E_ARG                   # out inside rank 1's slots
+
+
+def test_flag_validation(L):
+    f = L.lib.fc_flag_unpack_reduce
+    pl = (C.c_void_p * 2)(A + 0x1000000, A + 0x2000000)
+    fl = (C.c_void_p * 2)(A + 0x7000000, A + 0x7100000)
+    d = dict(out=A + 0x3000000, stale=A + 0x4000000, done=A + 0x5000000, cnt=A + 0x6000000)
+    g = lambda R=2, n=8192, be=1024, polls=0, mw=0, p=pl, fg=fl, **kw: f(
+        p, fg, R, n, be, 7, polls, mw, kw.get("out", d["out"]), kw.get("stale", d["stale"]),
+        kw.get("done", d["done"]), kw.get("cnt", d["cnt"]), None)
+    for be in (256, 768, 1 << 17):
+        assert g(be=be) == L.FC_E_ARG                               # block: a power of two, 512 .. 65536
+    assert g(R=0) == L.FC_E_ARG
+    assert g(polls=-1) == L.FC_E_ARG
+    assert g(mw=-1) == L.FC_E_ARG
+    assert g(n=8192 + 512) == L.FC_E_SHAPE
+    assert g(n=0) == L.FC_OK
+    assert g(fg=(C.c_void_p * 2)(A + 0x7000000, None)) == L.FC_E_NULL
+    assert g(fg=(C.c_void_p * 2)(A + 0x7000002, A + 0x7100000)) == L.FC_E_ALIGN   # flag words: 4-byte aligned
+    assert g(p=(C.c_void_p * 2)(A + 0x1000004, A + 0x2000000)) == L.FC_E_ALIGN
+    assert g(cnt=A + 0x6000004) == L.FC_E_ALIGN
+    assert g(fg=(C.c_void_p * 2)(A + 0x7000000, A + 0x3000000 + 16)) == L.FC_E_ARG  # flags inside out
+    assert g(done=A + 0x2000000 + 8) == L.FC_E_ARG                                  # done inside a payload
+    pk = L.lib.fc_flag_pack
+    assert pk(A, 8192, 1000, 7, None, 0, A + 0x1000000, A + 0x2000000, None) == L.FC_E_ARG
+    assert pk(A, 8192, 1024, 7, None, -1, A + 0x1000000, A + 0x2000000, None) == L.FC_E_ARG
+    assert pk(A, 8192 + 16, 1024, 7, None, 0, A + 0x1000000, A + 0x2000000, None) == L.FC_E_SHAPE
+    assert pk(A, 8192, 1024, 7, None, 0, A + 0x1000000, A + 0x2000002, None) == L.FC_E_ALIGN
+    assert pk(A, 8192, 1024, 7, None, 0, A + 0x1000000, A + 0x1000000 + 64, None) == L.FC_E_ARG  # flags in payload
+    assert pk(A, 8192, 1024, 7, A + 0x1000000, 0, A + 0x1000000, A + 0x2000000, None) == L.FC_E_ARG  # order in payload
 
 
 def test_ll_gather_validation(L):
