@@ -66,6 +66,7 @@ def parse():
     ap.add_argument("--rows", default="all", help="other hot-path rows to measure: all | none | comma list of "
                                                   "prefill,share,normfirst,ll,llgather,rmsnorm,layer")
     ap.add_argument("--kernel-reps", type=int, default=0, help="graph replays per call timing (0 = auto)")
+    ap.add_argument("--fit-encodings", metavar="JSON", help="write the selector's fitted cost table here")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"))
     ap.add_argument("--stats-table", nargs=4, metavar=("STATS_CSV", "OUT_MD", "TITLE", "COMMAND"))
     ap.add_argument("--profile-report", nargs=6, metavar=("CONFIG", "STATS_CSV", "FETCH_CSV", "WRITE_CSV", "VALU_CSV",
@@ -577,6 +578,117 @@ def bench_ll_gather(cx):
     return {"workload": "standalone all-gather on epoch-tagged blocks, B=64, 2% late", "by_payload": res}
 
 
+def bench_encodings(cx, fit_out=None):
+    """Readiness encodings with a sender and a receiver running at the same time: per rank count R and
+    payload size S, the receiver (fc_ll_poll_unpack_reduce or fc_flag_unpack_reduce) is launched first on
+    a stream of its own compute units, where it spins within its poll budget; the R senders (one launch of
+    fc_ll_pack or fc_flag_pack) follow on a stream of the other compute units.  Latency = from the senders'
+    start to the receiver's end (a copy kernel holds the senders' stream while the host enqueues, so no
+    host launch gap is timed).  Every live pass must complete every block.  The cost model of the
+    protocol selector is fitted to these latencies."""
+    torch, np = cx.torch, cx.np
+    from tensor_all_reduce_amd import _lib, datagen as dg, selector as sel
+    from tensor_all_reduce_amd.streams import sender_receiver_streams
+    rcu = 128
+    sa, sb = sender_receiver_streams(receiver_cus=rcu)
+    xa, xb = torch.cuda.ExternalStream(sa.cuda_stream), torch.cuda.ExternalStream(sb.cuda_stream)
+    hold = [torch.empty(256 << 20, dtype=torch.uint8, device=cx.dev) for _ in range(2)]
+    polls, mwg, reps = 200_000, 2 * rcu, 7
+    sizes = [16 << 10, 32 << 10, 128 << 10, 512 << 10, 2 << 20, 8 << 20, 16 << 20]
+    rows, detail = [], []
+    for R in (2, 4, 8):
+        for S in sizes:
+            n = S // 2
+            xs = [cx.up(dg.synth_bf16((0xE1, R, S, r), n)) for r in range(R)]
+            for enc in sel.ENCODINGS:
+                if enc == "ll":
+                    B = sel.LL_BLOCK_SLOTS
+                    nblk = n // 2 // B
+                    bufs = [torch.empty(n // 2, dtype=torch.int64, device=cx.dev) for _ in range(R)]
+                    _lib.fc_ll_pack(xs, B, 1000, bufs)  # an earlier epoch: every copy starts stale
+                else:
+                    be = sel.flag_block(enc)
+                    nblk = n // be
+                    pays = [torch.zeros(n, dtype=torch.int16, device=cx.dev) for _ in range(R)]
+                    fls = [torch.full((nblk,), 1000, dtype=torch.int32, device=cx.dev) for _ in range(R)]
+                out = torch.empty(n, dtype=torch.int16, device=cx.dev)
+                stale = torch.empty(R * nblk, dtype=torch.uint8, device=cx.dev)
+                done = torch.zeros(nblk, dtype=torch.uint8, device=cx.dev)
+                cnt = torch.zeros(4, dtype=torch.int32, device=cx.dev)
+
+                def receive(e, stream):
+                    if enc == "ll":
+                        _lib.fc_ll_poll_unpack_reduce(bufs, n, B, e, out, stale, done, cnt, max_polls=polls,
+                                                      max_workgroups=mwg, stream=stream)
+                    else:
+                        _lib.fc_flag_unpack_reduce(pays, fls, n, be, e, out, stale, done, cnt, max_polls=polls,
+                                                   max_workgroups=mwg, stream=stream)
+
+                def send(e, stream):
+                    if enc == "ll":
+                        _lib.fc_ll_pack(xs, B, e, bufs, stream=stream)
+                    else:
+                        _lib.fc_flag_pack(xs, be, e, pays, fls, stream=stream)
+
+                live, alone, ok = [], [], True
+                for rep in range(reps):
+                    e = 1001 + rep
+                    done.zero_()
+                    cnt.zero_()
+                    torch.cuda.synchronize()
+                    a, b = cx.ev(), cx.ev()
+                    receive(e, sa)                      # spins on its own compute units
+                    _lib.fc_copy(hold[0], hold[1], stream=sb)
+                    a.record(xb)
+                    send(e, sb)
+                    b.record(xa)
+                    torch.cuda.synchronize()
+                    c = cnt.cpu().numpy().view(np.uint32)
+                    ok = ok and int(c[1]) == 0
+                    live.append(a.elapsed_time(b) * 1e3)
+                    # the receiver alone, every block already there
+                    done.zero_()
+                    cnt.zero_()
+                    torch.cuda.synchronize()
+                    a, b = cx.ev(), cx.ev()
+                    _lib.fc_copy(hold[0], hold[1], stream=sa)
+                    a.record(xa)
+                    receive(e, sa)
+                    b.record(xa)
+                    torch.cuda.synchronize()
+                    alone.append(a.elapsed_time(b) * 1e3)
+                t = statistics.median(live)
+                if ok:
+                    rows.append((enc, S, R, round(t, 2)))
+                detail.append({"enc": enc, "S": S, "R": R, "live_us": round(t, 2),
+                               "receiver_alone_us": round(statistics.median(alone), 2), "all_blocks_live": ok})
+                del out, stale, done, cnt
+                if enc == "ll":
+                    del bufs
+                else:
+                    del pays, fls
+    sa.close()
+    sb.close()
+    del hold
+    torch.cuda.empty_cache()
+    costs = sel.fit(rows)
+    agree = 0
+    for R in (2, 4, 8):
+        for S in sizes:
+            meas = {r[0]: r[3] for r in rows if r[1] == S and r[2] == R}
+            if len(meas) == len(sel.ENCODINGS):
+                agree += sel.select(costs, S, R) == min(meas, key=meas.get)
+    res = {"receiver_cus": rcu, "sender_cus": "the rest", "reps": reps, "points": detail,
+           "model": {e: list(c.coef) for e, c in costs.items()},
+           "choice_matches_fastest_measured": f"{agree}/{len(sizes) * 3}",
+           "crossover_R8": sel.crossover(costs, 8), "crossover_R2": sel.crossover(costs, 2)}
+    if fit_out:
+        total = torch.cuda.get_device_properties(0).multi_processor_count
+        sel.save(fit_out, costs, rows, "python bench.py --rows encodings --no-cpu-baseline --fit-encodings " + fit_out,
+                 f"one {torch.cuda.get_device_name(0)}: receiver on {rcu} compute units, senders on {total - rcu}")
+    return res
+
+
 def _once(cx, g, per):
     torch = cx.torch
     a, b = cx.ev(), cx.ev()
@@ -769,7 +881,8 @@ def main():
                      "traffic": tr["total"] if tr else None},
         "wall_s": round(main_r["wall"], 3),
     }
-    rows = {"prefill", "ll", "llgather", "rmsnorm", "share", "normfirst", "layer"} if args.rows == "all" else set() if args.rows == "none" \
+    rows = {"prefill", "ll", "llgather", "rmsnorm", "share", "normfirst", "layer", "encodings"} if args.rows == "all" \
+        else set() if args.rows == "none" \
         else set(args.rows.split(","))
     extra = {}
     if "prefill" in rows and args.config != 3:
@@ -802,6 +915,8 @@ def main():
         extra["tokenweave_reduce_rmsnorm"] = bench_rmsnorm_overlap(cx)
     if "layer" in rows:
         extra["two_half_layer"] = bench_layer(cx)
+    if "encodings" in rows:
+        extra["readiness_encodings"] = bench_encodings(cx, args.fit_encodings)
     if extra:
         line["rows"] = extra
     if not args.no_cpu_baseline:

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define FC_ABI_VERSION 3
+#define FC_ABI_VERSION 4
 
 typedef enum {
     FC_OK = 0,
@@ -151,14 +151,16 @@ fc_status fc_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, in
 fc_status fc_ll_gather(const uint64_t* const* slots, int R, int64_t nwords, int block_slots, uint32_t epoch,
                        uint32_t* const* out, uint8_t* stale, uint8_t* done, uint32_t* counters, hipStream_t stream);
 
-/* Sender side of the slots above, used to emulate a peer's writes: packs bf16 [n] into n/2 slots tagged
- * with `epoch`, writing blocks in the order block_order[0..nblk) (an int32 permutation of the block
- * indices, or NULL for ascending).  Each slot is written with one agent-scope atomic 64-bit store, so a
- * receiver reading at the same time sees its payload and epoch word together.  pace (0..65536): each
- * wavefront of the packer first sleeps pace x 512 clocks (a slow sender for runs where the receiver
- * starts first; 0 for none).  The result does not depend on the order or the pace. */
-fc_status fc_ll_pack(const uint16_t* x, int64_t n, int block_slots, uint32_t epoch, const int32_t* block_order,
-                     int pace, uint64_t* slots, hipStream_t stream);
+/* Sender side of the slots above, used to emulate R peers writing at the same time (one launch): packs
+ * rank r's bf16 x[r] [n] into n/2 slots[r] tagged with `epoch`, writing blocks in the order
+ * block_order[r][0..nblk) (an int32 permutation of the block indices; block_order NULL, or an entry NULL,
+ * for ascending).  x, block_order, slots: host arrays of R device pointers.  Each slot is written with one
+ * agent-scope atomic 64-bit store, so a receiver reading at the same time sees its payload and epoch word
+ * together.  pace (0..65536): each wavefront of the packer first sleeps pace x 512 clocks (slow senders
+ * for runs where the receiver starts first; 0 for none).  The result does not depend on the order or the
+ * pace.  No rank's slots may overlap any rank's input or order, or another rank's slots. */
+fc_status fc_ll_pack(const uint16_t* const* x, int R, int64_t n, int block_slots, uint32_t epoch,
+                     const int32_t* const* block_order, int pace, uint64_t* const* slots, hipStream_t stream);
 
 /* Receiver of the slots above that may run while the senders still write (flash-comm, abstract: the
  * receiver validates the blocks it needs itself, with no barrier between GPUs).  Arguments, verdicts and
@@ -193,13 +195,15 @@ fc_status fc_flag_unpack_reduce(const uint16_t* const* payload, const uint32_t* 
                                 int block_elems, uint32_t epoch, int max_polls, int max_workgroups, uint16_t* out,
                                 uint8_t* stale, uint8_t* done, uint32_t* counters, hipStream_t stream);
 
-/* Sender side of the flag encoding, used to emulate a peer: writes x (bf16 [n]) into payload block by
- * block in the order block_order[0..nblk) (int32 permutation, or NULL for ascending), and after each
- * block a release store of epoch into flags[b] (each wavefront of the writing workgroup first fences
- * with release order, then the workgroup meets at a barrier).  pace: sleeps of 512 clocks before each
- * block (0..65536).  block_elems as for fc_flag_unpack_reduce. */
-fc_status fc_flag_pack(const uint16_t* x, int64_t n, int block_elems, uint32_t epoch, const int32_t* block_order,
-                       int pace, uint16_t* payload, uint32_t* flags, hipStream_t stream);
+/* Sender side of the flag encoding, used to emulate R peers writing at the same time (one launch): writes
+ * rank r's x[r] (bf16 [n]) into payload[r] block by block in the order block_order[r] (as for fc_ll_pack),
+ * and after each block a release store of epoch into flags[r][b] (each wavefront of the writing
+ * workgroup first fences with release order, then the workgroup meets at a barrier).  pace: sleeps of
+ * 512 clocks before each block (0..65536).  block_elems as for fc_flag_unpack_reduce.  Host arrays of R
+ * device pointers; no output may overlap an input or another output. */
+fc_status fc_flag_pack(const uint16_t* const* x, int R, int64_t n, int block_elems, uint32_t epoch,
+                       const int32_t* const* block_order, int pace, uint16_t* const* payload, uint32_t* const* flags,
+                       hipStream_t stream);
 
 /* Measurement helper: copies `bytes` (a multiple of 16, at most 2^40, 16-byte aligned pointers, no
  * overlap) with one non-temporal 16-byte load and store per lane; its bandwidth is the practical HBM

@@ -71,11 +71,12 @@ def _load():
     lib.fc_gather_dequant.argtypes = [C.POINTER(QMsg), i32, i64, i32, i32, vp, C.POINTER(Norm), vp]
     lib.fc_reduce_rmsnorm.argtypes = [C.POINTER(vp), i32, i64, C.POINTER(Norm), i32, vp]
     lib.fc_ll_unpack_reduce.argtypes = [C.POINTER(vp), i32, i64, i32, u32, vp, vp, vp, vp, vp]
-    lib.fc_ll_pack.argtypes = [vp, i64, i32, u32, vp, i32, vp, vp]
+    lib.fc_ll_pack.argtypes = [C.POINTER(vp), i32, i64, i32, u32, C.POINTER(vp), i32, C.POINTER(vp), vp]
     lib.fc_ll_poll_unpack_reduce.argtypes = [C.POINTER(vp), i32, i64, i32, u32, i32, i32, vp, vp, vp, vp, vp]
     lib.fc_flag_unpack_reduce.argtypes = [C.POINTER(vp), C.POINTER(vp), i32, i64, i32, u32, i32, i32, vp, vp, vp,
                                           vp, vp]
-    lib.fc_flag_pack.argtypes = [vp, i64, i32, u32, vp, i32, vp, vp, vp]
+    lib.fc_flag_pack.argtypes = [C.POINTER(vp), i32, i64, i32, u32, C.POINTER(vp), i32, C.POINTER(vp), C.POINTER(vp),
+                                 vp]
     lib.fc_ll_gather.argtypes = [C.POINTER(vp), i32, i64, i32, u32, C.POINTER(vp), vp, vp, vp, vp]
     lib.fc_copy.argtypes = [vp, vp, i64, vp]
     for f in ("fc_quantize", "fc_reduce_shard", "fc_reduce_shard_norm", "fc_gather_dequant", "fc_reduce_rmsnorm", "fc_ll_unpack_reduce",
@@ -183,10 +184,22 @@ def fc_ll_gather(slots, nwords: int, block_slots: int, epoch: int, out, stale, d
                              _ptr(counters), _stream(stream)), "fc_ll_gather")
 
 
+def _ranks(v):
+    """A tensor (one rank) or a list of R tensors -> list."""
+    return list(v) if isinstance(v, (list, tuple)) else [v]
+
+
+def _ptrs(lst):
+    return (C.c_void_p * len(lst))(*[_ptr(t) for t in lst])
+
+
 def fc_ll_pack(x, block_slots: int, epoch: int, slots, block_order=None, n: int | None = None, pace: int = 0,
                stream=None) -> None:
-    n = x.numel() if n is None else n
-    _check(_lib.fc_ll_pack(_ptr(x), n, block_slots, epoch & 0xFFFFFFFF, _ptr(block_order), pace, _ptr(slots),
+    """x, slots, block_order: one tensor each (one rank) or lists of R (R peers in one launch)."""
+    xs, ss = _ranks(x), _ranks(slots)
+    n = xs[0].numel() if n is None else n
+    oa = None if block_order is None else _ptrs(_ranks(block_order))
+    _check(_lib.fc_ll_pack(_ptrs(xs), len(xs), n, block_slots, epoch & 0xFFFFFFFF, oa, pace, _ptrs(ss),
                            _stream(stream)), "fc_ll_pack")
 
 
@@ -213,9 +226,12 @@ def fc_flag_unpack_reduce(payload, flags, n: int, block_elems: int, epoch: int, 
 
 def fc_flag_pack(x, block_elems: int, epoch: int, payload, flags, block_order=None, n: int | None = None,
                  pace: int = 0, stream=None) -> None:
-    n = x.numel() if n is None else n
-    _check(_lib.fc_flag_pack(_ptr(x), n, block_elems, epoch & 0xFFFFFFFF, _ptr(block_order), pace, _ptr(payload),
-                             _ptr(flags), _stream(stream)), "fc_flag_pack")
+    """x, payload, flags, block_order: one tensor each (one rank) or lists of R (R peers in one launch)."""
+    xs = _ranks(x)
+    n = xs[0].numel() if n is None else n
+    oa = None if block_order is None else _ptrs(_ranks(block_order))
+    _check(_lib.fc_flag_pack(_ptrs(xs), len(xs), n, block_elems, epoch & 0xFFFFFFFF, oa, pace,
+                             _ptrs(_ranks(payload)), _ptrs(_ranks(flags)), _stream(stream)), "fc_flag_pack")
 
 
 def fc_copy(src, dst, nbytes: int | None = None, stream=None) -> None:

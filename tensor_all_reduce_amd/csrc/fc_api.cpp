@@ -382,17 +382,39 @@ fc_status fc_ll_gather(const uint64_t* const* slots, int R, int64_t nwords, int 
     return launched(fc::launch_ll_gather(p, stream));
 }
 
-fc_status fc_ll_pack(const uint16_t* x, int64_t n, int block_slots, uint32_t epoch, const int32_t* block_order,
-                     int pace, uint64_t* slots, hipStream_t stream) {
-    if (!valid_block(block_slots) || n < 0 || pace < 0 || pace > kMaxPace) return FC_E_ARG;
+fc_status fc_ll_pack(const uint16_t* const* x, int R, int64_t n, int block_slots, uint32_t epoch,
+                     const int32_t* const* block_order, int pace, uint64_t* const* slots, hipStream_t stream) {
+    if (R < 1 || R > fc::kMaxRanks || !valid_block(block_slots) || n < 0 || pace < 0 || pace > kMaxPace)
+        return FC_E_ARG;
     if (n % (2 * block_slots) != 0 || n > kMaxElems) return FC_E_SHAPE;
     if (n == 0) return FC_OK;
     if (!x || !slots) return FC_E_NULL;
-    if (!aligned(x, 16) || !aligned(slots, 16) || (block_order && !aligned(block_order, 4))) return FC_E_ALIGN;
-    const Range sr = rng(slots, 4 * n);
-    if (overlap(sr, rng(x, 2 * n)) || (block_order && overlap(sr, rng(block_order, 4 * (n / 2 / block_slots)))))
-        return FC_E_ARG;
-    return launched(fc::launch_ll_pack(fc::PackParams{x, n, block_slots, epoch, block_order, pace, slots}, stream));
+    const int64_t nblk = n / 2 / block_slots;
+    for (int r = 0; r < R; ++r) {
+        if (!x[r] || !slots[r]) return FC_E_NULL;
+        const int32_t* o = block_order ? block_order[r] : nullptr;
+        if (!aligned(x[r], 16) || !aligned(slots[r], 16) || (o && !aligned(o, 4))) return FC_E_ALIGN;
+    }
+    for (int r = 0; r < R; ++r) {  // a rank's slots overlap no input of any rank and no other rank's slots
+        const Range sr = rng(slots[r], 4 * n);
+        for (int q = 0; q < R; ++q) {
+            const int32_t* o = block_order ? block_order[q] : nullptr;
+            if (overlap(sr, rng(x[q], 2 * n)) || (o && overlap(sr, rng(o, 4 * nblk)))) return FC_E_ARG;
+            if (q > r && overlap(sr, rng(slots[q], 4 * n))) return FC_E_ARG;
+        }
+    }
+    fc::PackParams p;
+    for (int r = 0; r < fc::kMaxRanks; ++r) {
+        p.x[r] = r < R ? x[r] : nullptr;
+        p.order[r] = r < R && block_order ? block_order[r] : nullptr;
+        p.slots[r] = r < R ? slots[r] : nullptr;
+    }
+    p.R = R;
+    p.n = n;
+    p.block_slots = block_slots;
+    p.epoch = epoch;
+    p.pace = pace;
+    return launched(fc::launch_ll_pack(p, stream));
 }
 
 fc_status fc_ll_poll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, int block_slots, uint32_t epoch,
@@ -464,22 +486,46 @@ fc_status fc_flag_unpack_reduce(const uint16_t* const* payload, const uint32_t* 
     return launched(fc::launch_flag_unpack(p, stream));
 }
 
-fc_status fc_flag_pack(const uint16_t* x, int64_t n, int block_elems, uint32_t epoch, const int32_t* block_order,
-                       int pace, uint16_t* payload, uint32_t* flags, hipStream_t stream) {
+fc_status fc_flag_pack(const uint16_t* const* x, int R, int64_t n, int block_elems, uint32_t epoch,
+                       const int32_t* const* block_order, int pace, uint16_t* const* payload, uint32_t* const* flags,
+                       hipStream_t stream) {
     const int lb = log2_flag_block(block_elems);
-    if (lb < 0 || n < 0 || pace < 0 || pace > kMaxPace) return FC_E_ARG;
+    if (R < 1 || R > fc::kMaxRanks || lb < 0 || n < 0 || pace < 0 || pace > kMaxPace) return FC_E_ARG;
     if (n % block_elems != 0 || n > kMaxElems) return FC_E_SHAPE;
     if (n == 0) return FC_OK;
     if (!x || !payload || !flags) return FC_E_NULL;
-    if (!aligned(x, 16) || !aligned(payload, 16) || !aligned(flags, 4) || (block_order && !aligned(block_order, 4)))
-        return FC_E_ALIGN;
     const int64_t nblk = n / block_elems;
-    const Range rp = rng(payload, 2 * n), rf = rng(flags, 4 * nblk);
-    if (overlap(rp, rf) || overlap(rp, rng(x, 2 * n)) || overlap(rf, rng(x, 2 * n))) return FC_E_ARG;
-    if (block_order && (overlap(rp, rng(block_order, 4 * nblk)) || overlap(rf, rng(block_order, 4 * nblk))))
-        return FC_E_ARG;
-    return launched(
-        fc::launch_flag_pack(fc::FlagPackParams{x, n, lb, epoch, block_order, pace, payload, flags}, stream));
+    for (int r = 0; r < R; ++r) {
+        if (!x[r] || !payload[r] || !flags[r]) return FC_E_NULL;
+        const int32_t* o = block_order ? block_order[r] : nullptr;
+        if (!aligned(x[r], 16) || !aligned(payload[r], 16) || !aligned(flags[r], 4) || (o && !aligned(o, 4)))
+            return FC_E_ALIGN;
+    }
+    for (int r = 0; r < R; ++r) {  // outputs overlap no input of any rank and no other output
+        const Range rp = rng(payload[r], 2 * n), rf = rng(flags[r], 4 * nblk);
+        if (overlap(rp, rf)) return FC_E_ARG;
+        for (int q = 0; q < R; ++q) {
+            const int32_t* o = block_order ? block_order[q] : nullptr;
+            for (const Range out : {rp, rf}) {
+                if (overlap(out, rng(x[q], 2 * n)) || (o && overlap(out, rng(o, 4 * nblk)))) return FC_E_ARG;
+                if (q > r && (overlap(out, rng(payload[q], 2 * n)) || overlap(out, rng(flags[q], 4 * nblk))))
+                    return FC_E_ARG;
+            }
+        }
+    }
+    fc::FlagPackParams p;
+    for (int r = 0; r < fc::kMaxRanks; ++r) {
+        p.x[r] = r < R ? x[r] : nullptr;
+        p.order[r] = r < R && block_order ? block_order[r] : nullptr;
+        p.payload[r] = r < R ? payload[r] : nullptr;
+        p.flags[r] = r < R ? flags[r] : nullptr;
+    }
+    p.R = R;
+    p.n = n;
+    p.log2_block = lb;
+    p.epoch = epoch;
+    p.pace = pace;
+    return launched(fc::launch_flag_pack(p, stream));
 }
 
 fc_status fc_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {

@@ -80,14 +80,16 @@ struct LLGatherParams {
     uint32_t* counters;
 };
 
+// Sender emulation of R peers writing at the same time (one launch, one grid row per rank).
 struct PackParams {
-    const uint16_t* x;
+    const uint16_t* x[kMaxRanks];
+    const int32_t* order[kMaxRanks];  // entries may be null (ascending)
+    uint64_t* slots[kMaxRanks];
+    int R;
     int64_t n;
     int block_slots;
     uint32_t epoch;
-    const int32_t* order;
     int pace;
-    uint64_t* slots;
 };
 
 // Receivers that may run while the senders write: bounded re-reads, optional cap on the grid.
@@ -111,14 +113,15 @@ struct FlagParams {
 };
 
 struct FlagPackParams {
-    const uint16_t* x;
+    const uint16_t* x[kMaxRanks];
+    const int32_t* order[kMaxRanks];  // entries may be null (ascending)
+    uint16_t* payload[kMaxRanks];
+    uint32_t* flags[kMaxRanks];
+    int R;
     int64_t n;
     int log2_block;
     uint32_t epoch;
-    const int32_t* order;
     int pace;
-    uint16_t* payload;
-    uint32_t* flags;
 };
 
 // Reduce-scatter receive side with the norm before the all-gather: rs as for launch_reduce; norm's

@@ -13,34 +13,69 @@
 namespace fc {
 
 // =====================================================================================================
-// Flag encoding, sender side (peer emulation).  Workgroup j writes block order[j] (ascending without an
-// order) of x into the payload, 16 bytes per lane, then publishes it: each wavefront fences with release
-// order at agent scope (its stores complete and written back past its XCD's L2), the workgroup meets at
-// a barrier, and one lane stores the epoch into the block's flag word with release order.
+// Flag encoding, sender side: R peers writing at the same time, grid row y = rank.  A workgroup writes a
+// span of K consecutive entries of the write order (K blocks, at least 8192 elements: K = 1 for blocks of
+// 8192 elements and more), 16 bytes per lane, then publishes them: a barrier (which orders every wave's
+// stores before it at workgroup scope), one release fence at agent scope by the first wavefront, which
+// writes the span back past its XCD's L2, and the K flag stores.  The fence is the expensive step (it
+// writes back the L2), so one fence covers a whole span rather than each block.
 // =====================================================================================================
-__global__ __launch_bounds__(256) void k_flag_pack(const uint16_t* __restrict__ x, const int64_t nblk,
-                                                   const int log2_be, const int32_t* __restrict__ order,
-                                                   const uint32_t epoch, const int pace, uint16_t* payload,
-                                                   uint32_t* flags) {
+struct FlagPackTabs {
+    const uint16_t* x[kMaxRanks];
+    const int32_t* order[kMaxRanks];
+    uint16_t* payload[kMaxRanks];
+    uint32_t* flags[kMaxRanks];
+};
+
+__global__ __launch_bounds__(256) void k_flag_pack(const int64_t nblk, const int log2_be, const int log2_k,
+                                                   const uint32_t epoch, const int pace, const FlagPackTabs t) {
+    const int r = blockIdx.y;
+    const uint16_t* x = t.x[r];
+    const int32_t* order = t.order[r];
+    uint16_t* payload = t.payload[r];
+    uint32_t* flags = t.flags[r];
     const int64_t be = int64_t(1) << log2_be;
-    for (int64_t j = blockIdx.x; j < nblk; j += gridDim.x) {  // trip count uniform over the workgroup
-        const int64_t b = order ? (int64_t)order[j] : j;
-        if (b < 0 || b >= nblk) continue;  // not a permutation: out of contract, nothing written
+    const int64_t nspan = (nblk + (1 << log2_k) - 1) >> log2_k;
+    for (int64_t j = blockIdx.x; j < nspan; j += gridDim.x) {  // trip count uniform over the workgroup
         pace_sleep(pace);
-        for (int64_t e = (int64_t)threadIdx.x * 8; e < be; e += 256 * 8) {
-            const int64_t i = (b << log2_be) + e;
+        for (int64_t e = (int64_t)threadIdx.x * 8; e < (be << log2_k); e += 256 * 8) {
+            const int64_t q = (j << log2_k) + (e >> log2_be);  // entry of the write order
+            if (q >= nblk) break;                                // ragged last span
+            const int64_t b = order ? (int64_t)order[q] : q;
+            if (b < 0 || b >= nblk) continue;  // not a permutation: out of contract, nothing written
+            const int64_t i = (b << log2_be) + (e & (be - 1));
             *reinterpret_cast<uint4*>(payload + i) = ld16(x + i);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // The barrier orders every wave's stores before the first wavefront's fence at workgroup scope,
+        // and the fence at agent scope is cumulative; each wave also waits here until its own stores have
+        // reached the L2, so the write-back that the fence starts sees the whole span.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (threadIdx.x == 0) __hip_atomic_store(flags + b, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x < 64) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            const int64_t q = (j << log2_k) + threadIdx.x;
+            if (threadIdx.x < (1 << log2_k) && q < nblk) {
+                const int64_t b = order ? (int64_t)order[q] : q;
+                if (b >= 0 && b < nblk) __hip_atomic_store(flags + b, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
     }
 }
 
 hipError_t launch_flag_pack(const FlagPackParams& p, hipStream_t s) {
+    FlagPackTabs t;
+    for (int i = 0; i < kMaxRanks; ++i) {
+        const int q = i < p.R ? i : p.R - 1;
+        t.x[i] = p.x[q];
+        t.order[i] = p.order[q];
+        t.payload[i] = p.payload[q];
+        t.flags[i] = p.flags[q];
+    }
     const int64_t nblk = p.n >> p.log2_block;
-    const unsigned grid = (unsigned)(nblk < 4096 ? nblk : 4096);
-    k_flag_pack<<<grid, 256, 0, s>>>(p.x, nblk, p.log2_block, p.order, p.epoch, p.pace, p.payload, p.flags);
+    const int log2_k = p.log2_block >= 13 ? 0 : 13 - p.log2_block;  // spans of at least 8192 elements
+    const int64_t nspan = (nblk + (1 << log2_k) - 1) >> log2_k;
+    const dim3 grid((unsigned)(nspan < 2048 ? nspan : 2048), (unsigned)p.R);
+    k_flag_pack<<<grid, 256, 0, s>>>(nblk, p.log2_block, log2_k, p.epoch, p.pace, t);
     return hipGetLastError();
 }
 

@@ -312,31 +312,47 @@ hipError_t launch_ll_gather(const LLGatherParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Sender emulation: lane t of the write order packs 2 slots (4 bf16 in) of block order[t / (B/2)], each
-// slot with one agent-scope atomic 64-bit store, so that a receiver reading at the same time sees payload
-// and epoch word together.  Each wavefront first sleeps `pace` times (a slow sender).  An order entry
-// outside [0, nblk) (not a permutation: out of contract) writes nothing.
-__global__ __launch_bounds__(256) void k_ll_pack(const uint16_t* __restrict__ x, int64_t nthreads, int lpb,
-                                                 int block_slots, int64_t nblk, const int32_t* __restrict__ order,
-                                                 uint32_t epoch, int pace, uint64_t* __restrict__ slots) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// Sender emulation of R peers writing at the same time: grid row y = rank.  Lane t of the write order
+// packs 2 slots (4 bf16 in) of block order[t / (B/2)], each slot with one agent-scope atomic 64-bit store,
+// so that a receiver reading at the same time sees payload and epoch word together.  Each wavefront first
+// sleeps `pace` times (a slow sender).  An order entry outside [0, nblk) (not a permutation: out of
+// contract) writes nothing.
+struct PackTabs {
+    const uint16_t* x[kMaxRanks];
+    const int32_t* order[kMaxRanks];
+    uint64_t* slots[kMaxRanks];
+};
+
+__global__ __launch_bounds__(256) void k_ll_pack(const int64_t nthreads, const int lpb, const int block_slots,
+                                                 const int64_t nblk, const uint32_t epoch, const int pace,
+                                                 const PackTabs t) {
+    const int r = blockIdx.y;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     pace_sleep(pace);
-    if (t >= nthreads) return;
-    const int64_t j = t / lpb;
+    if (i >= nthreads) return;
+    const int64_t j = i / lpb;
+    const int32_t* order = t.order[r];
     const int64_t b = order ? (int64_t)order[j] : j;
     if (b < 0 || b >= nblk) return;
-    const int64_t k0 = b * block_slots + 2 * (t % lpb);
-    const uint2 xv = lds8(x + 2 * k0);
+    const int64_t k0 = b * block_slots + 2 * (i % lpb);
+    const uint2 xv = lds8(t.x[r] + 2 * k0);
     const uint64_t tag = (uint64_t)epoch << 32;
-    st_relaxed(slots + k0, tag | xv.x);
-    st_relaxed(slots + k0 + 1, tag | xv.y);
+    st_relaxed(t.slots[r] + k0, tag | xv.x);
+    st_relaxed(t.slots[r] + k0 + 1, tag | xv.y);
 }
 
 hipError_t launch_ll_pack(const PackParams& p, hipStream_t s) {
+    PackTabs t;
+    for (int i = 0; i < kMaxRanks; ++i) {
+        const int q = i < p.R ? i : p.R - 1;
+        t.x[i] = p.x[q];
+        t.order[i] = p.order[q];
+        t.slots[i] = p.slots[q];
+    }
     const int64_t nthreads = p.n / 4;  // 2 slots = 4 elements per lane
-    const dim3 grid((unsigned)((nthreads + 255) / 256));
-    k_ll_pack<<<grid, 256, 0, s>>>(p.x, nthreads, p.block_slots / 2, p.block_slots, p.n / 2 / p.block_slots, p.order,
-                                   p.epoch, p.pace, p.slots);
+    const dim3 grid((unsigned)((nthreads + 255) / 256), (unsigned)p.R);
+    k_ll_pack<<<grid, 256, 0, s>>>(nthreads, p.block_slots / 2, p.block_slots, p.n / 2 / p.block_slots, p.epoch,
+                                   p.pace, t);
     return hipGetLastError();
 }
 

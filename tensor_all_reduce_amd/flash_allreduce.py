@@ -218,3 +218,67 @@ class LLUnpackReduce:
         st = _lib.lib.fc_ll_unpack_reduce(self._slots, self.R, self.n, self.B, epoch & 0xFFFFFFFF, *self._ptrs,
                                           _lib._stream(stream))
         _lib._check(st, "fc_ll_unpack_reduce")
+
+
+class SelfSyncReduce:
+    """Receive side of a one-shot all-reduce whose R inbound messages carry their own readiness evidence
+    (flash-comm, abstract), in the encoding the protocol selector picks for the message size and rank
+    count ("auto"), or a given one ("ll", "flag512", "flag2048", "flag8192").
+
+    inbox(): the buffers the R senders write (rank r's slots, or payload + flag words);
+    send(): emulates the R senders in one launch (the peers' writes, on one GPU);
+    begin(): clears done flags and counters for a new epoch; receive(): folds every block whose R copies
+    carry the epoch, in ascending rank order, into out (bf16 [n]); with max_polls > 0 the receiver waits
+    (bounded) for late blocks, so it may run while the senders still write."""
+
+    def __init__(self, R: int, n: int, encoding: str = "auto", costs=None, device="cuda"):
+        from . import selector as sel
+        ok = {e for e in sel.ENCODINGS
+              if (n % (2 * sel.LL_BLOCK_SLOTS) == 0 if e == "ll" else n % sel.flag_block(e) == 0)}
+        if encoding == "auto":
+            if not ok:
+                raise ValueError(f"n={n} fits no encoding's block size")
+            encoding = sel.select(costs if costs is not None else sel.load(), 2 * n, R, allowed=ok)
+        elif encoding not in ok:
+            raise ValueError(f"encoding {encoding!r} does not divide n={n}")
+        self.R, self.n, self.encoding = R, n, encoding
+        if encoding == "ll":
+            self.B = sel.LL_BLOCK_SLOTS
+            self.nblk = n // 2 // self.B
+            self.slots = [torch.zeros(n // 2, dtype=torch.int64, device=device) for _ in range(R)]
+        else:
+            self.B = sel.flag_block(encoding)
+            self.nblk = n // self.B
+            self.payload = [torch.zeros(n, dtype=torch.int16, device=device) for _ in range(R)]
+            self.flags = [torch.zeros(self.nblk, dtype=torch.int32, device=device) for _ in range(R)]
+        self.out = torch.zeros(n, dtype=torch.int16, device=device)
+        self.stale = torch.zeros(R * self.nblk, dtype=torch.uint8, device=device)
+        self.done = torch.zeros(self.nblk, dtype=torch.uint8, device=device)
+        self.counters = torch.zeros(4, dtype=torch.int32, device=device)
+
+    def inbox(self):
+        return self.slots if self.encoding == "ll" else (self.payload, self.flags)
+
+    def begin(self, stream=None):
+        """stream: a torch stream (or None for the current one); the clears are fill kernels."""
+        import contextlib
+        with torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext():
+            self.done.zero_()
+            self.counters.zero_()
+
+    def send(self, xs, epoch: int, block_order=None, pace: int = 0, stream=None):
+        if self.encoding == "ll":
+            _lib.fc_ll_pack(list(xs), self.B, epoch, self.slots, block_order=block_order, pace=pace, stream=stream)
+        else:
+            _lib.fc_flag_pack(list(xs), self.B, epoch, self.payload, self.flags, block_order=block_order, pace=pace,
+                              stream=stream)
+
+    def receive(self, epoch: int, max_polls: int = 0, max_workgroups: int = 0, stream=None):
+        if self.encoding == "ll":
+            _lib.fc_ll_poll_unpack_reduce(self.slots, self.n, self.B, epoch, self.out, self.stale, self.done,
+                                          self.counters, max_polls=max_polls, max_workgroups=max_workgroups,
+                                          stream=stream)
+        else:
+            _lib.fc_flag_unpack_reduce(self.payload, self.flags, self.n, self.B, epoch, self.out, self.stale,
+                                       self.done, self.counters, max_polls=max_polls,
+                                       max_workgroups=max_workgroups, stream=stream)

@@ -1,0 +1,124 @@
+"""Cost-guided choice of the readiness encoding (flash-comm, abstract: a protocol selector adapts the
+readiness encoding to the message size and the number of participating GPUs, balancing the cost of
+synchronization against the extra bytes an encoding sends).
+
+Encodings built here:
+
+  "ll"        8-byte slots, 4 payload bytes + 4 epoch bytes: twice the payload bytes on the wire, and no
+              fence anywhere: a slot is valid when its epoch word is.
+  "flag<B>"   the payload unchanged plus one 4-byte flag word per block of B bf16 elements; the sender
+              fences (release) before each flag store, the receiver reads the flag, fences (acquire),
+              then reads the block: fewer bytes, one synchronization per block and a dependent read.
+
+Model (the plainest reading of the trade the selector makes): the latency of one transfer of S payload
+bytes from each of R ranks is
+
+    t(enc, S, R) = a + b * R + c * R * wire(enc, S)
+
+where wire() is the bytes one rank sends.  a holds an encoding's fixed synchronization latency (for a
+flag: the dependent flag-then-payload read), b its per-rank cost, c its cost per byte on the wire, which
+for a flag encoding also carries its per-block fence (a block is a fixed number of bytes, so blocks and
+bytes cannot be told apart within one encoding).  The three non-negative coefficients are fitted per
+encoding, by non-negative least squares, to latencies measured with a sender and a receiver running at
+the same time.  ``select`` returns the encoding with the lowest predicted latency (ties: the listed
+order).  Host logic only.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from dataclasses import dataclass
+
+DEFAULT_TABLE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "encoding_costs.json")
+ENCODINGS = ("ll", "flag512", "flag2048", "flag8192")
+LL_BLOCK_SLOTS = 64  # slot block of the "ll" encoding
+
+
+def flag_block(enc: str) -> int:
+    """Block elements of a "flag<B>" encoding."""
+    if not enc.startswith("flag"):
+        raise ValueError(f"not a flag encoding: {enc}")
+    return int(enc[4:])
+
+
+def wire_bytes(enc: str, S: int) -> int:
+    """Bytes one rank sends to carry S payload bytes (bf16 elements, S even)."""
+    if enc == "ll":
+        return 2 * S
+    return S + 4 * math.ceil(S / 2 / flag_block(enc))
+
+
+def blocks(enc: str, S: int) -> int:
+    """Blocks one rank publishes (each one a readiness decision of the receiver)."""
+    if enc == "ll":
+        return math.ceil(S / 4 / LL_BLOCK_SLOTS)
+    return math.ceil(S / 2 / flag_block(enc))
+
+
+def features(enc: str, S: int, R: int) -> list[float]:
+    return [1.0, float(R), float(R * wire_bytes(enc, S))]
+
+
+@dataclass(frozen=True)
+class EncodingCost:
+    enc: str
+    coef: tuple  # (a us, b us per rank, c us per wire byte)
+
+    def predict(self, S: int, R: int) -> float:
+        return sum(k * f for k, f in zip(self.coef, features(self.enc, S, R)))
+
+
+def fit(rows) -> dict[str, EncodingCost]:
+    """rows: iterable of (enc, S, R, t_us), t_us > 0.  Non-negative least squares per encoding on the
+    relative error (each row divided by its latency): the choice compares latencies at one size, so a
+    microsecond matters as much at 10 us as a hundred at 1 ms."""
+    import numpy as np
+    from scipy.optimize import nnls
+    by = {}
+    for enc, S, R, t in rows:
+        by.setdefault(enc, []).append((features(enc, S, R), t))
+    out = {}
+    for enc, pts in by.items():
+        y = np.array([p[1] for p in pts], dtype=np.float64)
+        A = np.array([p[0] for p in pts], dtype=np.float64) / y[:, None]
+        scale = np.maximum(A.max(axis=0), 1e-30)  # column scaling keeps the problem well conditioned
+        x, _ = nnls(A / scale, np.ones_like(y))
+        out[enc] = EncodingCost(enc, tuple(float(v) for v in x / scale))
+    return out
+
+
+def select(costs: dict[str, EncodingCost], S: int, R: int, allowed=None) -> str:
+    """The encoding with the lowest predicted latency for S payload bytes per rank and R ranks."""
+    names = [e for e in ENCODINGS if e in costs and (allowed is None or e in allowed)]
+    if not names:
+        raise ValueError("no encoding to choose from")
+    return min(names, key=lambda e: (costs[e].predict(S, R), names.index(e)))
+
+
+def crossover(costs: dict[str, EncodingCost], R: int, lo: int = 1 << 10, hi: int = 1 << 30) -> list:
+    """[(S, encoding)] at each payload size (powers of two from lo to hi) where the choice changes."""
+    out, prev = [], None
+    S = lo
+    while S <= hi:
+        e = select(costs, S, R)
+        if e != prev:
+            out.append((S, e))
+            prev = e
+        S *= 2
+    return out
+
+
+def save(path: str, costs: dict[str, EncodingCost], measured, command: str, machine: str) -> None:
+    doc = {"model": "t_us = a + b*R + c*R*wire_bytes", "command": command, "machine": machine,
+           "coefficients": {e: list(c.coef) for e, c in costs.items()},
+           "measured": [list(r) for r in measured]}
+    with open(path, "w") as f:
+        json.dump(doc, f, indent=1)
+        f.write("\n")
+
+
+def load(path: str = DEFAULT_TABLE) -> dict[str, EncodingCost]:
+    with open(path) as f:
+        doc = json.load(f)
+    return {e: EncodingCost(e, tuple(c)) for e, c in doc["coefficients"].items()}

@@ -32,7 +32,7 @@ def test_exports_every_declared_function(L):
             "fc_ll_pack", "fc_copy", "fc_status_string", "fc_last_hip_error", "fc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L.lib, n), n
-    assert L.fc_abi_version() == 3
+    assert L.fc_abi_version() == 4
 
 
 def test_single_hip_runtime(L):
@@ -188,12 +188,20 @@ def test_ll_validation(L):
     assert g(done=A + 0x4000000 + 8) == L.FC_E_ARG   # done inside the stale flags
     assert g(out=A + 0x1000000 + 64) == L.FC_E_ARG   # out inside rank 0's slots
     p = L.lib.fc_ll_pack
-    assert p(A, 4096, 60, 7, None, 0, A + 0x1000000, None) == L.FC_E_ARG
-    assert p(A, 4096, 64, 7, None, -1, A + 0x1000000, None) == L.FC_E_ARG    # pace
-    assert p(A, 4096, 64, 7, None, 65537, A + 0x1000000, None) == L.FC_E_ARG
-    assert p(A, 4000, 64, 7, None, 0, A + 0x1000000, None) == L.FC_E_SHAPE
-    assert p(A, 4096, 64, 7, None, 0, A + 8, None) == L.FC_E_ALIGN
-    assert p(A, 4096, 64, 7, None, 0, A + 1024, None) == L.FC_E_ARG
+    one = lambda *v: (C.c_void_p * len(v))(*v)
+    X, S = one(A), one(A + 0x1000000)
+    assert p(X, 1, 4096, 60, 7, None, 0, S, None) == L.FC_E_ARG
+    assert p(X, 0, 4096, 64, 7, None, 0, S, None) == L.FC_E_ARG                # R
+    assert p(X, 1, 4096, 64, 7, None, -1, S, None) == L.FC_E_ARG               # pace
+    assert p(X, 1, 4096, 64, 7, None, 65537, S, None) == L.FC_E_ARG
+    assert p(X, 1, 4000, 64, 7, None, 0, S, None) == L.FC_E_SHAPE
+    assert p(X, 1, 4096, 64, 7, None, 0, one(A + 8), None) == L.FC_E_ALIGN
+    assert p(X, 1, 4096, 64, 7, None, 0, one(A + 1024), None) == L.FC_E_ARG     # slots over the input
+    assert p(X, 1, 4096, 64, 7, one(A + 0x1000000 + 64), 0, S, None) == L.FC_E_ARG  # order inside the slots
+    X2 = one(A, A + 0x100000)
+    assert p(X2, 2, 4096, 64, 7, None, 0, one(A + 0x1000000, None), None) == L.FC_E_NULL
+    assert p(X2, 2, 4096, 64, 7, None, 0, one(A + 0x1000000, A + 0x1000000 + 4096), None) == L.FC_E_ARG
+    assert p(X2, 2, 4096, 64, 7, None, 0, one(A + 0x1000000, A + 0x100000 + 16), None) == L.FC_E_ARG  # over x[1]
 
 
 def test_ll_poll_validation(L):
@@ -240,12 +248,19 @@ def test_flag_validation(L):
     assert g(fg=(C.c_void_p * 2)(A + 0x7000000, A + 0x3000000 + 16)) == L.FC_E_ARG  # flags inside out
     assert g(done=A + 0x2000000 + 8) == L.FC_E_ARG                                  # done inside a payload
     pk = L.lib.fc_flag_pack
-    assert pk(A, 8192, 1000, 7, None, 0, A + 0x1000000, A + 0x2000000, None) == L.FC_E_ARG
-    assert pk(A, 8192, 1024, 7, None, -1, A + 0x1000000, A + 0x2000000, None) == L.FC_E_ARG
-    assert pk(A, 8192 + 16, 1024, 7, None, 0, A + 0x1000000, A + 0x2000000, None) == L.FC_E_SHAPE
-    assert pk(A, 8192, 1024, 7, None, 0, A + 0x1000000, A + 0x2000002, None) == L.FC_E_ALIGN
-    assert pk(A, 8192, 1024, 7, None, 0, A + 0x1000000, A + 0x1000000 + 64, None) == L.FC_E_ARG  # flags in payload
-    assert pk(A, 8192, 1024, 7, A + 0x1000000, 0, A + 0x1000000, A + 0x2000000, None) == L.FC_E_ARG  # order in payload
+    one = lambda *v: (C.c_void_p * len(v))(*v)
+    X, P, F = one(A), one(A + 0x1000000), one(A + 0x2000000)
+    assert pk(X, 1, 8192, 1000, 7, None, 0, P, F, None) == L.FC_E_ARG
+    assert pk(X, 17, 8192, 1024, 7, None, 0, P, F, None) == L.FC_E_ARG
+    assert pk(X, 1, 8192, 1024, 7, None, -1, P, F, None) == L.FC_E_ARG
+    assert pk(X, 1, 8192 + 16, 1024, 7, None, 0, P, F, None) == L.FC_E_SHAPE
+    assert pk(X, 1, 8192, 1024, 7, None, 0, P, one(A + 0x2000002), None) == L.FC_E_ALIGN
+    assert pk(X, 1, 8192, 1024, 7, None, 0, P, one(A + 0x1000000 + 64), None) == L.FC_E_ARG    # flags in payload
+    assert pk(X, 1, 8192, 1024, 7, one(A + 0x1000000), 0, P, F, None) == L.FC_E_ARG            # order in payload
+    X2, P2 = one(A, A + 0x100000), one(A + 0x1000000, A + 0x1800000)
+    assert pk(X2, 2, 8192, 1024, 7, None, 0, P2, one(A + 0x2000000, A + 0x2000000 + 16), None) == L.FC_E_ARG
+    assert pk(X2, 2, 8192, 1024, 7, None, 0, P2, one(A + 0x2000000, A + 0x1800000 + 32), None) == L.FC_E_ARG
+    assert pk(X2, 2, 8192, 1024, 7, None, 0, P2, one(A + 0x2000000, None), None) == L.FC_E_NULL
 
 
 def test_ll_gather_validation(L):

@@ -92,16 +92,16 @@ def test_flag_pack_round_trip(fc, orc, be):
     R, nblk, e = 4, 45, 9
     n = be * nblk
     xs = [dg.synth_bf16((be, 7, r), n) for r in range(R)]
-    pays, fls = [], []
+    pays = [torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(R)]
+    fls = [torch.full((nblk,), e - 1, dtype=torch.int32, device="cuda") for _ in range(R)]
+    orders = [up(np.random.default_rng(r).permutation(nblk).astype(np.int32)) for r in range(R)]
+    # ranks 0 and 1 in one launch (two peers at once), ranks 2 and 3 one launch each
+    fc.fc_flag_pack([up(xs[0]), up(xs[1])], be, e, pays[:2], fls[:2], block_order=orders[:2])
+    for r in (2, 3):
+        fc.fc_flag_pack(up(xs[r]), be, e, pays[r], fls[r], block_order=orders[r] if r == 2 else None)
     for r in range(R):
-        p = torch.zeros(n, dtype=torch.int16, device="cuda")
-        f = torch.full((nblk,), e - 1, dtype=torch.int32, device="cuda")
-        order = np.random.default_rng(r).permutation(nblk).astype(np.int32)
-        fc.fc_flag_pack(up(xs[r]), be, e, p, f, block_order=up(order))
-        assert_equal_bits(down(p, np.uint16), xs[r], "payload")
-        assert_equal_bits(down(f, np.uint32), np.full(nblk, e, np.uint32), "flags")
-        pays.append(p)
-        fls.append(f)
+        assert_equal_bits(down(pays[r], np.uint16), xs[r], f"payload {r}")
+        assert_equal_bits(down(fls[r], np.uint32), np.full(nblk, e, np.uint32), f"flags {r}")
     out, stale, done, cnt = _bufs(R, n, nblk)
     fc.fc_flag_unpack_reduce(pays, fls, n, be, e, out, stale, done, cnt)
     got_out, got_st, got_dn, got_c = _down_all(out, stale, done, cnt, R, nblk)
@@ -225,8 +225,7 @@ def test_live_sender_and_receiver(fc, orc, enc):
         fls = [torch.full((nblk,), e0 - 1, dtype=torch.int32, device="cuda") for _ in range(R)]
     else:
         slots = [torch.zeros(n // 2, dtype=torch.int64, device="cuda") for _ in range(R)]
-        for r in range(R):
-            fc.fc_ll_pack(up(dg.synth_bf16((0xDEAD, r), n)), B, e0 - 1, slots[r])
+        fc.fc_ll_pack([up(dg.synth_bf16((0xDEAD, r), n)) for r in range(R)], B, e0 - 1, slots)
     torch.cuda.synchronize()
     for step in range(2):  # two epochs in a row on the same buffers
         e = e0 + step
@@ -240,14 +239,12 @@ def test_live_sender_and_receiver(fc, orc, enc):
             fc.fc_flag_unpack_reduce(pays, fls, n, be, e, out, stale, done, cnt, max_polls=LIVE_POLLS,
                                      max_workgroups=LIVE_WGS, stream=sa)
             time.sleep(0.002)  # the receiver is spinning before the sender starts
-            for r in range(R):
-                fc.fc_flag_pack(xd[r], be, e, pays[r], fls[r], block_order=orders[r], pace=2, stream=sb)
+            fc.fc_flag_pack(xd, be, e, pays, fls, block_order=orders, pace=2, stream=sb)  # R peers at once
         else:
             fc.fc_ll_poll_unpack_reduce(slots, n, B, e, out, stale, done, cnt, max_polls=LIVE_POLLS,
                                         max_workgroups=LIVE_WGS, stream=sa)
             time.sleep(0.002)
-            for r in range(R):
-                fc.fc_ll_pack(xd[r], B, e, slots[r], block_order=orders[r], pace=2, stream=sb)
+            fc.fc_ll_pack(xd, B, e, slots, block_order=orders, pace=2, stream=sb)
         torch.cuda.synchronize()
         got = _down_all(out, stale, done, cnt, R, nblk)
         print(f"  pending after the live pass {int(got[3][1])}, re-reads {int(got[3][2])}", flush=True)
@@ -268,3 +265,27 @@ def test_live_sender_and_receiver(fc, orc, enc):
         assert_equal_bits(got[0], ro, "out of the live pass")
     sa.close()
     sb.close()
+
+
+@pytest.mark.parametrize("R,n", [(8, 8192), (8, 1 << 20), (3, 65536)])
+def test_selector_driven_receiver(fc, orc, R, n):
+    """SelfSyncReduce picks the encoding from the measured cost table, the senders write, the receiver
+    folds: the result equals the oracle's fixed-order sum, whichever encoding was chosen."""
+    import torch
+    from gpu_helpers import assert_equal_bits, down, up
+    from tensor_all_reduce_amd.flash_allreduce import SelfSyncReduce
+    xs = [dg.synth_bf16((0x5E1, R, n, r), n) for r in range(R)]
+    ss = SelfSyncReduce(R, n)
+    print(f"R={R} n={n}: encoding {ss.encoding}", flush=True)
+    for e in (3, 4):
+        ss.begin()
+        ss.send([up(x) for x in xs], e)
+        ss.receive(e)
+        torch.cuda.synchronize()
+        c = down(ss.counters, np.uint32)
+        assert down(ss.done, np.uint8).all() and list(c) == [0, 0, 0, 0]
+        if ss.encoding == "ll":
+            ro, _, _, _ = orc.ll_unpack_reduce([orc.ll_pack(x, ss.B, e) for x in xs], n, ss.B, e)
+        else:
+            ro, _, _, _ = orc.flag_unpack_reduce(xs, [np.full(ss.nblk, e, np.uint32)] * R, n, ss.B, e)
+        assert_equal_bits(down(ss.out, np.uint16), ro, f"out ({ss.encoding})")

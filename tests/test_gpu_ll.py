@@ -48,6 +48,21 @@ class GpuLL:
                 down(self.done, np.uint8), down(self.cnt, np.uint32))
 
 
+def test_pack_ranks_in_one_launch(fc, orc):
+    """Three peers packed in one launch, one of them in ascending order: each equals the oracle's packing."""
+    import torch
+    from gpu_helpers import assert_equal_bits, down, up
+    B, nblk, e = 64, 29, 0xABCDEF01
+    n = 2 * B * nblk
+    xs = [dg.synth_bf16((B, 3, r), n) for r in range(3)]
+    orders = [np.random.default_rng(r).permutation(nblk).astype(np.int32) for r in range(3)]
+    slots = [torch.empty(n // 2, dtype=torch.int64, device="cuda") for _ in range(3)]
+    fc.fc_ll_pack([up(x) for x in xs], B, e, slots, block_order=[up(orders[0]), None, up(orders[2])], pace=1)
+    for r in range(3):
+        o = None if r == 1 else orders[r]
+        assert_equal_bits(down(slots[r], np.uint64), orc.ll_pack(xs[r], B, e, order=o), f"slots {r}")
+
+
 @pytest.mark.parametrize("B", [32, 64, 128, 256])
 def test_pack_matches_oracle(fc, orc, B):
     import torch

@@ -1,0 +1,105 @@
+"""CPU tests of the protocol selector's cost model (host logic): wire bytes of each encoding, the
+non-negative least-squares fit, the choice and its crossover, and the committed table measured on the GPU."""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from tensor_all_reduce_amd import selector as sel
+
+
+def test_wire_bytes_and_blocks():
+    assert sel.wire_bytes("ll", 4096) == 8192                      # 4 payload + 4 epoch bytes per slot
+    assert sel.wire_bytes("flag512", 1024) == 1024 + 4             # one flag word per 512-element block
+    assert sel.wire_bytes("flag2048", 1 << 20) == (1 << 20) + 4 * 256
+    assert sel.blocks("flag8192", 1 << 20) == 64
+    assert sel.blocks("ll", 1 << 20) == (1 << 20) // 4 // sel.LL_BLOCK_SLOTS
+    with pytest.raises(ValueError):
+        sel.flag_block("ll")
+
+
+def synthetic(coefs, sizes=(1 << 12, 1 << 15, 1 << 18, 1 << 21, 1 << 23), ranks=(2, 4, 8)):
+    rows = []
+    for enc, (a, b, c) in coefs.items():
+        for S in sizes:
+            for R in ranks:
+                rows.append((enc, S, R, a + b * R + c * R * sel.wire_bytes(enc, S)))
+    return rows
+
+
+COEFS = {"ll": (6.0, 0.3, 1.0 / 3000.0), "flag512": (11.0, 0.5, 1.0 / 5200.0),
+         "flag2048": (14.0, 0.4, 1.0 / 6000.0), "flag8192": (20.0, 0.4, 1.0 / 6100.0)}
+
+
+def test_fit_recovers_exact_coefficients():
+    costs = sel.fit(synthetic(COEFS))
+    for enc, want in COEFS.items():
+        got = costs[enc].coef
+        for g, w in zip(got, want):
+            assert g == pytest.approx(w, rel=1e-6, abs=1e-9), enc
+
+
+def test_fit_is_non_negative():
+    rows = [("ll", S, 8, 100.0 - S * 1e-5) for S in (1 << 10, 1 << 14, 1 << 18, 1 << 20)]  # falling with size
+    c = sel.fit(rows)["ll"].coef
+    assert all(v >= 0 for v in c)
+
+
+def test_choice_and_crossover_match_the_closed_form():
+    costs = {e: sel.EncodingCost(e, c) for e, c in COEFS.items()}
+    assert sel.select(costs, 1 << 10, 8) == "ll"         # small: the fixed latency decides
+    assert sel.select(costs, 1 << 26, 8) == "flag8192"    # large: bytes decide
+    # ll against flag512 alone: equal where a_l + b_l R + c_l R 2S = a_f + b_f R + c_f R (S + 4 S / 1024)
+    a_l, b_l, c_l = COEFS["ll"]
+    a_f, b_f, c_f = COEFS["flag512"]
+    R = 8
+    S_eq = ((a_f - a_l) + (b_f - b_l) * R) / (R * (2 * c_l - c_f * (1 + 4 / 1024)))
+    two = {"ll", "flag512"}
+    below, above = int(S_eq * 0.9) // 2 * 2, int(S_eq * 1.1) // 2 * 2
+    assert sel.select(costs, below, R, allowed=two) == "ll"
+    assert sel.select(costs, above, R, allowed=two) == "flag512"
+    steps = sel.crossover(costs, R)
+    assert steps[0] == (1 << 10, "ll") and steps[-1][1] == "flag8192"
+    assert [S for S, _ in steps] == sorted(S for S, _ in steps)
+
+
+def test_ties_take_the_listed_order():
+    same = {e: sel.EncodingCost(e, (5.0, 0.0, 0.0)) for e in sel.ENCODINGS}
+    assert sel.select(same, 1 << 20, 4) == sel.ENCODINGS[0]
+    with pytest.raises(ValueError):
+        sel.select(same, 1 << 20, 4, allowed=set())
+
+
+def test_save_load_round_trip(tmp_path):
+    costs = {e: sel.EncodingCost(e, c) for e, c in COEFS.items()}
+    p = os.path.join(tmp_path, "t.json")
+    sel.save(p, costs, [("ll", 1024, 2, 7.5)], "cmd", "machine")
+    back = sel.load(p)
+    assert {e: c.coef for e, c in back.items()} == {e: tuple(c) for e, c in COEFS.items()}
+
+
+@pytest.mark.skipif(not os.path.exists(sel.DEFAULT_TABLE), reason="no measured table committed")
+def test_committed_table_chooses_well_on_its_own_measurements():
+    """On the latencies measured on the GPU, the fitted model's choice costs little against the fastest
+    encoding measured at each point."""
+    import json
+    doc = json.load(open(sel.DEFAULT_TABLE))
+    costs = sel.load()
+    by = {}
+    for enc, S, R, t in doc["measured"]:
+        by.setdefault((S, R), {})[enc] = t
+    regrets = []
+    for (S, R), meas in by.items():
+        choice = sel.select(costs, S, R, allowed=set(meas))
+        regrets.append(meas[choice] / min(meas.values()) - 1.0)
+    assert len(regrets) >= 10
+    assert max(regrets) <= 0.30 and float(np.mean(regrets)) <= 0.08, regrets
+
+
+def test_committed_choice_on_the_slot_workload():
+    """The measured table picks flag words for small messages and slots for the 8-rank [128, 8192] bf16
+    workload (2 MiB per rank), where the flag sender's fences cost more than the slots' extra bytes."""
+    costs = sel.load()
+    assert sel.select(costs, 2 << 20, 8) == "ll"
+    assert sel.select(costs, 16 << 10, 8).startswith("flag")
