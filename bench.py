@@ -251,8 +251,70 @@ def cpu_baseline(cfg, seconds):
             break
     return {"value": round(step_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": sample + f" {reps}x in {el:.1f} s; single-threaded C++ (g++ -O2 -ffp-contract=off)",
-            "us_per_step": round(el / reps * 1e6, 1), "host_cpu": platform.processor() or platform.machine(),
+            "us_per_step": round(el / reps * 1e6, 1), "host_cpu": host_cpu_model(),
             "host_cores": os.cpu_count()}
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def oracle_by_config(max_elems=1 << 22):
+    """The oracle on each of the five workloads: single-threaded, pinned to one host core, median of 5 runs
+    (3 for the two largest).  Workloads over `max_elems` elements per rank run on a block of their rows
+    and are scaled to the whole workload (rows are independent, so the cost is linear in them)."""
+    sys.path.insert(0, os.path.join(ROOT, "oracle"))
+    import numpy as np
+    import oracle
+    from tensor_all_reduce_amd import bytes_model as bm, datagen as dg
+    oracle.lib()
+    old = os.sched_getaffinity(0)
+    cpus = sorted(old)
+    os.sched_setaffinity(0, {cpus[min(2, len(cpus) - 1)]})
+    out = {}
+    try:
+        for idx, cfg in dg.CONFIGS.items():
+            T = cfg.T if cfg.n <= max_elems else max(cfg.R, max_elems // cfg.H // cfg.R * cfg.R)
+            n = T * cfg.H
+            reps = 3 if cfg.n > max_elems else 5
+            parts = [dg.partial(cfg, r, n) for r in range(cfg.R)]
+            if cfg.kind == "two_step":
+                res, gam = dg.residual(cfg, n), dg.gamma(cfg)
+                run = lambda: oracle.two_step(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, residual=res, gamma=gam,
+                                              eps=cfg.eps, hidden=cfg.H, plain=False)
+                full_bytes = sum(bm.total(v) for v in bm.two_step_whole(cfg.R, cfg.T, cfg.H, cfg.bits_rs,
+                                                                        cfg.bits_ag, cfg.group).values())
+            elif cfg.kind == "ll":
+                nslots, nblk = n // 2, n // 2 // cfg.block_slots
+                slots = []
+                for r in range(cfg.R):
+                    sl = oracle.ll_pack(parts[r], cfg.block_slots, cfg.epoch, order=dg.write_order(cfg, r, nblk))
+                    ep = dg.stale_epochs(cfg, r, nslots)[0]
+                    slots.append((sl & np.uint64(0xFFFFFFFF)) | (ep.astype(np.uint64) << np.uint64(32)))
+                run = lambda: oracle.ll_unpack_reduce(slots, n, cfg.block_slots, cfg.epoch)
+                full_bytes = cfg.R * 4 * cfg.n + 2 * cfg.n
+            else:
+                res, gam = dg.residual(cfg, n), dg.gamma(cfg)
+                run = lambda: oracle.reduce_rmsnorm(parts, T, cfg.H, res, gam, cfg.eps)
+                full_bytes = (2 * cfg.R + 6) * cfg.n
+            times = []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                run()
+                times.append(time.perf_counter() - t0)
+            us = statistics.median(times) * 1e6 * (cfg.T / T)
+            out[cfg.slug] = {"us_per_step": round(us, 1), "GB/s": round(full_bytes / (us * 1e-6) / 1e9, 4),
+                             "runs": reps, "sample_rows": T, "rows": cfg.T}
+    finally:
+        os.sched_setaffinity(0, old)
+    return out
 
 
 # ---------------------------------------------------------------------------------------------------------
@@ -359,6 +421,22 @@ def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_firs
     wall = time.perf_counter() - w0
     ms_step = e0.elapsed_time(e1) / steps
 
+    # spread: the same steps replayed in chunks of c consecutive buffer sets, one event pair per chunk
+    c = max(1, min(20, nsets // 10))
+    nchunk = min(30, nsets // c)
+    chunks = [cx.graph(lambda k, i=i: step(i * c + k), c) for i in range(nchunk)]
+    evs = [cx.ev() for _ in range(nchunk + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i, gc in enumerate(chunks):
+        gc.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 / c for i in range(nchunk))
+    pct = lambda q: round(per[min(len(per) - 1, int(q * (len(per) - 1) + 0.5))], 3)
+    spread = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "chunks": nchunk, "steps_per_chunk": c}
+    del chunks
+
     reps = kernel_reps or max(2, steps // nsets)
     if norm_first:
         fns = {"quantize": lambda k: sets[k][0].quantize(),
@@ -377,7 +455,7 @@ def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_firs
                           "traffic": None if norm_first else traffic_for(name, cfg, traffic)}
     del sets, g_all, g_tail
     torch.cuda.empty_cache()
-    return dict(ms_step=ms_step, wall=wall, step_bytes=step_bytes, nsets=nsets, per_call=per_call)
+    return dict(ms_step=ms_step, wall=wall, step_bytes=step_bytes, nsets=nsets, per_call=per_call, spread=spread)
 
 
 def bench_share(cx, cfg, steps, warmup, kernel_reps, norm_first=False):
@@ -872,7 +950,8 @@ def main():
                    "bits_ag": cfg.bits_ag, "group": cfg.group, "mode": "whole emulated all-reduce on one GPU",
                    "cache": "warm" if args.warm else "cold", "buffer_sets": main_r["nsets"],
                    "launch": "hip graph, 3 kernels per step"},
-        "us_per_step": round(ms_step * 1e3, 3), "bytes_per_step": main_r["step_bytes"],
+        "us_per_step": round(ms_step * 1e3, 3), "us_per_step_spread": main_r["spread"],
+        "bytes_per_step": main_r["step_bytes"],
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "copy_ceiling_GBps": round(copy_gbps, 1), "pct_copy_ceiling": round(100 * value / copy_gbps, 2),
         "calls": per_call,
@@ -890,6 +969,7 @@ def main():
         r3 = bench_two_step(cx, c3, 30, 5, False, 0, load_traffic(c3))
         v3 = r3["step_bytes"] / (r3["ms_step"] * 1e-3) / 1e9
         extra["prefill_two_step"] = {"workload": c3.name, "us_per_step": round(r3["ms_step"] * 1e3, 2),
+                                     "us_per_step_spread": r3["spread"],
                                      "GB/s": round(v3, 1), "pct_hbm_peak": round(100 * v3 / HBM_PEAK_GBPS, 2),
                                      "pct_copy_ceiling": round(100 * v3 / copy_gbps, 2), "calls": r3["per_call"]}
     if "share" in rows:
@@ -921,6 +1001,7 @@ def main():
         line["rows"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        line["cpu_baseline"]["oracle_by_config"] = oracle_by_config()
     print(json.dumps(line), flush=True)
     return 0
 

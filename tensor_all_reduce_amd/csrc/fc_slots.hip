@@ -52,8 +52,8 @@ __device__ __forceinline__ void ll_examine(const uint4 (&q)[KI], int r, uint32_t
     }
 }
 
-template <int B>
-__global__ __launch_bounds__(256) void k_ll_unpack(const int64_t nslots, const int64_t nblk, uint8_t* done,
+template <int B, int W>  // W wavefronts per workgroup
+__global__ __launch_bounds__(64 * W) void k_ll_unpack(const int64_t nslots, const int64_t nblk, uint8_t* done,
                                                    const uint32_t epoch, const int R, uint16_t* out, uint8_t* stale,
                                                    uint32_t* counters, const LLSlots slots) {
     constexpr int KI = 2;                      // instructions per wavefront tile
@@ -62,10 +62,10 @@ __global__ __launch_bounds__(256) void k_ll_unpack(const int64_t nslots, const i
     constexpr int RB = 8;                      // ranks whose slots are loaded before any is examined
     static_assert(KI % IB == 0, "a tile holds whole blocks");
     static_assert(LB >= kMaxRanks && (LB == 16 || LB == 32 || LB == 64), "one lane per rank writes a block's stale flags");
-    __shared__ uint32_t s_cnt[4][2];  // per wavefront: stale pairs, pending blocks
+    __shared__ uint32_t s_cnt[W][2];  // per wavefront: stale pairs, pending blocks
     const int lane = threadIdx.x & 63;
     const int bl = lane % LB;  // lane inside its block's lanes
-    const int64_t tile = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (128 * KI);
+    const int64_t tile = ((int64_t)blockIdx.x * W + (threadIdx.x >> 6)) * (128 * KI);
     int64_t slot[KI], blk[KI], src[KI];
     bool inside[KI];
 #pragma unroll
@@ -162,19 +162,28 @@ __global__ __launch_bounds__(256) void k_ll_unpack(const int64_t nslots, const i
     // and the kernel ends only once the last one is done, so their number matters.  A call adds at most
     // 2^29 stale pairs, so the low word does not carry.
     if (threadIdx.x == 0) {
-        const uint32_t st = s_cnt[0][0] + s_cnt[1][0] + s_cnt[2][0] + s_cnt[3][0];
-        const uint32_t pe = s_cnt[0][1] + s_cnt[1][1] + s_cnt[2][1] + s_cnt[3][1];
+        uint32_t st = 0, pe = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            st += s_cnt[w][0];
+            pe += s_cnt[w][1];
+        }
         if (st | pe) atomicAdd(reinterpret_cast<unsigned long long*>(counters), ((unsigned long long)pe << 32) | st);
     }
 }
+
+// Wavefronts per workgroup of the slot receiver: the counters cost one atomic per workgroup, and those
+// atomics serialize, so larger workgroups mean fewer of them.
+constexpr int kLLWaves = 8;
 
 hipError_t launch_ll_unpack(const LLParams& p, hipStream_t s) {
     LLSlots t;
     for (int i = 0; i < kMaxRanks; ++i) t.p[i] = p.slots[i < p.R ? i : p.R - 1];
     const int64_t nslots = p.n / 2, nblk = nslots / p.block_slots;
-    const int64_t per_wg = 4 * 128 * 2;  // slots per workgroup: 4 wavefronts x 2 instructions x 128
+    const int64_t per_wg = kLLWaves * 128 * 2;  // slots per workgroup: wavefronts x 2 instructions x 128
     const dim3 grid((unsigned)((nslots + per_wg - 1) / per_wg));
-#define FC_LL(B) k_ll_unpack<B><<<grid, 256, 0, s>>>(nslots, nblk, p.done, p.epoch, p.R, p.out, p.stale, p.counters, t)
+#define FC_LL(B) \
+    k_ll_unpack<B, kLLWaves><<<grid, 64 * kLLWaves, 0, s>>>(nslots, nblk, p.done, p.epoch, p.R, p.out, p.stale, p.counters, t)
     switch (p.block_slots) {
         case 32: FC_LL(32); break;
         case 64: FC_LL(64); break;
@@ -195,8 +204,8 @@ struct LLGatherTabs {
     uint32_t* out[kMaxRanks];
 };
 
-template <int B>
-__global__ __launch_bounds__(256) void k_ll_gather(const int64_t nslots, const int64_t nblk, uint8_t* done,
+template <int B, int W>  // W wavefronts per workgroup
+__global__ __launch_bounds__(64 * W) void k_ll_gather(const int64_t nslots, const int64_t nblk, uint8_t* done,
                                                    uint8_t* stale, const uint32_t epoch, uint32_t* counters,
                                                    const LLGatherTabs t) {
     constexpr int KI = 4;                      // instructions per wavefront tile
@@ -204,11 +213,11 @@ __global__ __launch_bounds__(256) void k_ll_gather(const int64_t nslots, const i
     constexpr int LB = B <= 128 ? B / 2 : 64;  // lanes of one instruction inside one block
     constexpr int NBW = 64 / LB;               // blocks per instruction
     static_assert(KI % IB == 0, "a tile holds whole blocks");
-    __shared__ uint32_t s_cnt[4];
+    __shared__ uint32_t s_cnt[W];
     const int r = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int bl = lane % LB;
-    const int64_t tile = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (128 * KI);
+    const int64_t tile = ((int64_t)blockIdx.x * W + (threadIdx.x >> 6)) * (128 * KI);
     const uint64_t* sp = t.slots[r];
     uint8_t* dn = done + (int64_t)r * nblk;
     int64_t slot[KI], blk[KI];
@@ -286,11 +295,15 @@ __global__ __launch_bounds__(256) void k_ll_gather(const int64_t nslots, const i
     if (lane == 0) s_cnt[threadIdx.x >> 6] = n_stale;
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t st = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+        uint32_t st = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) st += s_cnt[w];
         // stale pairs and pending pairs are the same pairs here; one 64-bit atomic adds both counters
         if (st) atomicAdd(reinterpret_cast<unsigned long long*>(counters), ((unsigned long long)st << 32) | st);
     }
 }
+
+constexpr int kLLGWaves = 16;  // wavefronts per workgroup (one counter atomic per workgroup)
 
 hipError_t launch_ll_gather(const LLGatherParams& p, hipStream_t s) {
     LLGatherTabs t;
@@ -299,9 +312,10 @@ hipError_t launch_ll_gather(const LLGatherParams& p, hipStream_t s) {
         t.out[i] = p.out[i < p.R ? i : p.R - 1];
     }
     const int64_t nslots = p.nwords, nblk = nslots / p.block_slots;
-    const int64_t per_wg = 4 * 128 * 4;  // slots per workgroup: 4 wavefronts x 4 instructions x 128
+    const int64_t per_wg = kLLGWaves * 128 * 4;  // slots per workgroup: wavefronts x 4 instructions x 128
     const dim3 grid((unsigned)((nslots + per_wg - 1) / per_wg), (unsigned)p.R);
-#define FC_LLG(B) k_ll_gather<B><<<grid, 256, 0, s>>>(nslots, nblk, p.done, p.stale, p.epoch, p.counters, t)
+#define FC_LLG(B) \
+    k_ll_gather<B, kLLGWaves><<<grid, 64 * kLLGWaves, 0, s>>>(nslots, nblk, p.done, p.stale, p.epoch, p.counters, t)
     switch (p.block_slots) {
         case 32: FC_LLG(32); break;
         case 64: FC_LLG(64); break;
