@@ -67,6 +67,8 @@ def parse():
                                                   "prefill,share,normfirst,ll,llgather,rmsnorm,layer")
     ap.add_argument("--kernel-reps", type=int, default=0, help="graph replays per call timing (0 = auto)")
     ap.add_argument("--fit-encodings", metavar="JSON", help="write the selector's fitted cost table here")
+    ap.add_argument("--pmc-rows", metavar="BYTES_JSON", help="only launch the row kernels for counter runs")
+    ap.add_argument("--rows-pmc-report", nargs=5, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV", "BYTES_JSON", "OUT_MD"))
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"))
     ap.add_argument("--stats-table", nargs=4, metavar=("STATS_CSV", "OUT_MD", "TITLE", "COMMAND"))
     ap.add_argument("--profile-report", nargs=6, metavar=("CONFIG", "STATS_CSV", "FETCH_CSV", "WRITE_CSV", "VALU_CSV",
@@ -74,10 +76,12 @@ def parse():
     return ap.parse_args()
 
 
-def sources_sha() -> str:
+def sources_sha(files=None) -> str:
+    """Hash of kernel sources (default: those of the two-step kernels), recorded with counter summaries."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
+    for f in files or KERNEL_SOURCES:
+        path = f if "/" in f else os.path.join(ROOT, "tensor_all_reduce_amd", "csrc", f)
+        with open(path if os.path.isabs(path) else os.path.join(ROOT, path), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -174,6 +178,164 @@ def profile_report(config, stats_csv, fetch_csv, write_csv, valu_csv, out_md):
         lines.append(f"| `{short(name)}` | {fb} ({fb / a['read']:.3f}x) | {a['read']} | {wb} ({wb / a['write']:.3f}x) | "
                      f"{a['write']} | {vpw} | {vpb} |" if fb is not None else f"| `{short(name)}` | - | {a['read']} | - | "
                      f"{a['write']} | {vpw} | {vpb} |")
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def pmc_rows(out_json):
+    """Single-workload launches of the row kernels, for counter runs (one counter per run): the 1 GiB copy
+    (the counters' scale reference), then per kernel a few launches over 3 rotating buffer sets (together
+    larger than the L2s): the slot receiver's first pass on the slot workload, half A of the TokenWeave
+    reduce + RMSNorm, the all-gather of the int8 prefill messages (first pass), and the two f2 receivers
+    (flag words per 2048 elements, polling slot receiver) on 8 x 2 MiB with every block there.  Writes the
+    algorithmic bytes of one launch of each kernel to `out_json`."""
+    import numpy as np
+    import torch
+    from tensor_all_reduce_amd import _lib, bytes_model as bm, datagen as dg
+    from tensor_all_reduce_amd.flash_allreduce import ReduceRMSNorm
+    dev = torch.device("cuda:0")
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view({2: np.int16, 4: np.int32, 8: np.int64}[a.dtype.itemsize])).to(dev)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    _lib.fc_copy(src, dst)
+    del src, dst
+    algo = {}
+    # slot receiver, first pass
+    c4 = dg.CONFIGS[4]
+    R, n, B, e = c4.R, c4.n, c4.block_slots, c4.epoch
+    nslots, nblk = n // 2, n // 2 // B
+    sets = []
+    for k in range(3):
+        slots = []
+        for r in range(R):
+            s_ = torch.empty(nslots, dtype=torch.int64, device=dev)
+            _lib.fc_ll_pack(up(dg.partial(c4, r)), B, e, s_, block_order=up(dg.write_order(c4, r, nblk)))
+            s_.view(torch.int32).view(-1, 2)[:, 1] = up(dg.stale_epochs(c4, r, nslots)[0])
+            slots.append(s_)
+        sets.append(slots)
+    out = torch.empty(n, dtype=torch.int16, device=dev)
+    stale = torch.empty(R * nblk, dtype=torch.uint8, device=dev)
+    done = torch.zeros(nblk, dtype=torch.uint8, device=dev)
+    cnt = torch.zeros(2, dtype=torch.int32, device=dev)
+    for k in range(6):
+        done.zero_()
+        cnt.zero_()
+        _lib.fc_ll_unpack_reduce(sets[k % 3], n, B, e, out, stale, done, cnt)
+    torch.cuda.synchronize()
+    pend = int(cnt.cpu().numpy().view(np.uint32)[1])
+    algo["k_ll_unpack"] = bm.ll_unpack(R, n, B, completed_blocks=nblk - pend)
+    del sets, out, stale, done, cnt
+    # TokenWeave half A
+    c5 = dg.CONFIGS[5]
+    a = c5.splits[0]
+    na = a * c5.H
+    parts = [up(dg.partial(c5, r, na)) for r in range(c5.R)]
+    res, gam = up(dg.residual(c5, na)), up(dg.gamma(c5))
+    o5, ro5 = torch.empty(na, dtype=torch.int16, device=dev), torch.empty(na, dtype=torch.int16, device=dev)
+    rr = ReduceRMSNorm(parts, a, c5.H, gam, o5, residual=res, residual_out=ro5, eps=c5.eps)
+    for _ in range(3):
+        rr.run()
+    torch.cuda.synchronize()
+    algo["BF16ReduceProducer"] = bm.reduce_rmsnorm(c5.R, a, c5.H, True, True)
+    del parts, res, o5, ro5, rr
+    # all-gather of the int8 prefill messages, first pass
+    c3 = dg.CONFIGS[3]
+    msg3 = c3.L * c3.bits_ag // 8 + 4 * (c3.L // c3.group)
+    nwords = -(-msg3 // 4 // B) * B
+    gblk = nwords // B
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0xFC0B)
+    gsets = []
+    for k in range(3):
+        sl = []
+        for r in range(c3.R):
+            w = torch.randint(0, 1 << 32, (nwords,), dtype=torch.int64, device=dev, generator=gen)
+            ep = torch.from_numpy(dg.stale_epochs(c4, r, nwords)[0].astype(np.int64)).to(dev)
+            sl.append(w | (ep << 32))
+        gsets.append(sl)
+    gout = [torch.empty(nwords, dtype=torch.int32, device=dev) for _ in range(c3.R)]
+    gst = torch.empty(c3.R * gblk, dtype=torch.uint8, device=dev)
+    gdn = torch.zeros(c3.R * gblk, dtype=torch.uint8, device=dev)
+    gcnt = torch.zeros(2, dtype=torch.int32, device=dev)
+    for k in range(6):
+        gdn.zero_()
+        gcnt.zero_()
+        _lib.fc_ll_gather(gsets[k % 3], nwords, B, e, gout, gst, gdn, gcnt)
+    torch.cuda.synchronize()
+    gpend = int(gcnt.cpu().numpy().view(np.uint32)[1])
+    algo["k_ll_gather"] = bm.ll_gather(c3.R, nwords, B, completed_blocks=c3.R * gblk - gpend)
+    del gsets, gout
+    # f2 receivers, every block there
+    n2, be = 1 << 20, 2048
+    xs = [up(dg.synth_bf16((0xF2, r), n2)) for r in range(8)]
+    fsets, lsets = [], []
+    for k in range(3):
+        pays = [torch.empty(n2, dtype=torch.int16, device=dev) for _ in range(8)]
+        fls = [torch.empty(n2 // be, dtype=torch.int32, device=dev) for _ in range(8)]
+        _lib.fc_flag_pack(xs, be, 7, pays, fls)
+        fsets.append((pays, fls))
+        sl = [torch.empty(n2 // 2, dtype=torch.int64, device=dev) for _ in range(8)]
+        _lib.fc_ll_pack(xs, 64, 7, sl)
+        lsets.append(sl)
+    out2 = torch.empty(n2, dtype=torch.int16, device=dev)
+    st2 = torch.empty(8 * (n2 // 64), dtype=torch.uint8, device=dev)
+    dn2 = torch.zeros(n2 // 64, dtype=torch.uint8, device=dev)
+    c2 = torch.zeros(4, dtype=torch.int32, device=dev)
+    for k in range(6):
+        dn2.zero_()
+        _lib.fc_flag_unpack_reduce(*fsets[k % 3], n2, be, 7, out2, st2, dn2, c2)
+    for k in range(6):
+        dn2.zero_()
+        _lib.fc_ll_poll_unpack_reduce(lsets[k % 3], n2, 64, 7, out2, st2, dn2, c2)
+    torch.cuda.synchronize()
+    algo["k_flag_unpack"] = bm.flag_unpack(8, n2, be)
+    algo["k_ll_poll"] = bm.ll_unpack(8, n2, 64)
+    with open(out_json, "w") as f:
+        json.dump(algo, f, indent=1)
+    print(json.dumps(algo))
+
+
+def rows_pmc_report(stats_csv, fetch_csv, write_csv, bytes_json, out_md):
+    """Profile summary of the row kernels: durations and per-launch HBM traffic against algorithmic bytes."""
+    algo = json.load(open(bytes_json))
+
+    def load(path, counter):
+        d = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                d.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: statistics.median(v) for k, v in d.items()}
+    f, w = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    copy = next(k for k in f if "k_copy" in k)
+    fs, ws = (1 << 30) / (f[copy] * 1024), (1 << 30) / (w[copy] * 1024)
+    stats = {r["Name"]: r for r in csv.DictReader(open(stats_csv))}
+    cmd = "python3 bench.py --pmc-rows gpurun_out/pmc_rows_bytes.json"
+    lines = ["# Row kernels: durations and HBM traffic per launch", "",
+             "One workload per kernel, launched over 3 rotating buffer sets (together larger than the L2s), in "
+             "four runs of the same command on one MI355X (run from the repository root, under /tmp as TMPDIR):", "",
+             "```", f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/sr -o sr -- {cmd}",
+             f"timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/fr -o fr -- {cmd}",
+             f"timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/wr -o wr -- {cmd}",
+             "```", "",
+             f"Counters are scaled by what they read for the 1 GiB copy kernel (fetch x{fs:.4f}, write x{ws:.4f}); "
+             f"summarised with `python bench.py --rows-pmc-report STATS FETCH WRITE BYTES_JSON {out_md}` "
+             f"(kernel sources {sources_sha(('fc_slots.hip', 'fc_live.hip', 'fc_twostep.hip', 'fc_device.h', 'fc_sync.h'))}).", "",
+             "| kernel | workload | avg us (traced) | fetch bytes | algorithmic read | write bytes | algorithmic write "
+             "| GB/s at avg (algorithmic) |", "|---|---|---|---|---|---|---|---|"]
+    what = {"k_ll_unpack": "slot workload, first pass (2% late)", "BF16ReduceProducer": "TokenWeave half A, 4096 rows",
+            "k_ll_gather": "int8 prefill messages, first pass", "k_flag_unpack": "8 x 2 MiB, flag per 2048, all there",
+            "k_ll_poll": "8 x 2 MiB slots, all there, no re-read"}
+    for key, a in algo.items():
+        name = next((k for k in f if key in k), None)
+        if name is None:
+            continue
+        st = next((r for k, r in stats.items() if key in k), None)
+        avg = float(st["AverageNs"]) / 1e3 if st else float("nan")
+        fb, wb = round(f[name] * 1024 * fs), round(w.get(name, 0.0) * 1024 * ws)
+        gbps = (a["read"] + a["write"]) / (avg * 1e-6) / 1e9
+        lines.append(f"| `{name.replace('void ', '').split('(')[0]}` | {what[key]} | {avg:.2f} | {fb} ({fb / a['read']:.3f}x) "
+                     f"| {a['read']} | {wb} ({wb / a['write']:.3f}x) | {a['write']} | {gbps:.0f} |")
     with open(out_md, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -921,6 +1083,12 @@ def main():
         return 0
     if args.stats_table:
         stats_table(*args.stats_table)
+        return 0
+    if args.rows_pmc_report:
+        rows_pmc_report(*args.rows_pmc_report)
+        return 0
+    if args.pmc_rows:
+        pmc_rows(args.pmc_rows)
         return 0
     if args.profile_report:
         c, *paths = args.profile_report

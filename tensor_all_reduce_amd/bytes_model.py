@@ -103,3 +103,10 @@ def ll_gather(R: int, nwords: int, block_slots: int, completed_blocks: int | Non
     nblk = R * (nwords // block_slots)
     done_b = nblk if completed_blocks is None else completed_blocks
     return dict(read=R * 8 * nwords + nblk, write=4 * block_slots * done_b + nblk + done_b)
+
+
+def flag_unpack(R: int, n: int, block_elems: int) -> dict:
+    """Receiver of the flag encoding with every block valid: each rank's payload (2 B per element) and flag
+    words read, done flags read, the output and the stale and done flags written."""
+    nblk = n // block_elems
+    return dict(read=R * 2 * n + R * 4 * nblk + nblk, write=2 * n + R * nblk + nblk)

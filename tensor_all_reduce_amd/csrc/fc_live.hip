@@ -80,89 +80,108 @@ hipError_t launch_flag_pack(const FlagPackParams& p, hipStream_t s) {
 }
 
 // =====================================================================================================
-// Flag encoding, receiver side.  A wavefront owns tiles of NB whole blocks (NB = 2 for 512-element
-// blocks, else 1), walked with a grid stride.  Lane (q, r) = (lane / 16, lane % 16) reads rank r's flag
-// of the tile's block q with an agent-scope atomic load; while any copy is stale and the budget lasts,
-// the flags are read again after a short sleep.  One acquire fence, then each valid block's payload is
-// read (16 bytes per lane per instruction; 8 ranks' loads in flight, the launcher repeating the last
-// rank's pointer past R) and folded in ascending rank order.  A stale copy's payload is never read.
+// Flag encoding, receiver side.  A workgroup owns tiles of max(block, 2048) elements (NBW = 4, 2 or 1
+// whole blocks), walked with a grid stride.  Its first wavefront checks the readiness evidence: lane
+// (q, r) = (lane / 16, lane % 16) reads rank r's flag of the tile's block q with an agent-scope atomic
+// load, re-reads the flags after a short sleep while a copy is stale and the budget lasts, fences once
+// with acquire order and posts the verdicts in LDS.  After a barrier (which carries the acquire to the
+// other wavefronts), all four wavefronts read the valid blocks' payload, 512 elements per instruction
+// (16 bytes per lane, 8 ranks' loads in flight, the launcher repeating the last rank's pointer past R),
+// and fold it in ascending rank order.  A stale copy's payload is never read.  One fence per tile and
+// the whole workgroup on one block keep both the fences and the dependent flag-then-payload round trip
+// per byte low.
 // =====================================================================================================
 struct FlagTabs {
     const uint16_t* payload[kMaxRanks];
     const uint32_t* flags[kMaxRanks];
 };
 
-template <int NB>
+template <int NBW>
 __global__ __launch_bounds__(256) void k_flag_unpack(const int64_t ntiles, const int64_t nblk, const int log2_be,
                                                      const uint32_t epoch, const int R, const int max_polls,
                                                      uint8_t* done, uint16_t* out, uint8_t* stale,
                                                      uint32_t* counters, const FlagTabs t) {
     constexpr int RB = 8;  // ranks per batch of payload loads
-    __shared__ uint32_t s_cnt[4][3];
-    const int lane = threadIdx.x & 63;
+    __shared__ uint64_t s_bad[2], s_watch[2];  // verdicts, double-buffered by tile parity
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 4, rk = lane & 15;
     const uint32_t* fp = t.flags[rk < R ? rk : R - 1];
-    const int log2_te = NB == 2 ? 10 : log2_be;  // tile elements
-    const int it = 1 << (log2_te - 9);           // 512-element instructions per tile
+    const int log2_te = NBW > 1 ? 11 : log2_be;  // tile elements
+    const int per_wave = 1 << (log2_te - 11);     // 512-element instructions per wavefront and tile
     uint32_t n_stale = 0, n_pending = 0, n_polls = 0;
-    const int64_t nwaves = (int64_t)gridDim.x * 4;
-    for (int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); tile < ntiles; tile += nwaves) {
-        const int64_t b0 = tile * NB;
-        const int64_t qb = b0 + (q < NB ? q : NB - 1);
-        const int64_t fb = qb < nblk ? qb : nblk - 1;  // this lane's flag word (clamped, always inside)
-        const bool watch = q < NB && rk < R && b0 + q < nblk && done[fb] == 0;
-        uint32_t f = ld_relaxed(fp + fb);
-        uint64_t bad = __ballot(watch && f != epoch);
-        for (int p = 0; bad != 0 && p < max_polls; ++p) {
-            __builtin_amdgcn_s_sleep(2);
-            f = ld_relaxed(fp + fb);
-            bad = __ballot(watch && f != epoch);
-            ++n_polls;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        if (watch) stale[(int64_t)rk * nblk + fb] = f != epoch ? 1 : 0;
-        const uint64_t wm = __ballot(watch);
-        // block verdicts (wavefront-uniform): examined = its rank-0 lane watched; valid = examined, none stale
-        bool valid[NB];
+    int par = 0;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x, par ^= 1) {  // uniform over the workgroup
+        const int64_t b0 = tile * NBW;
+        if (wave == 0) {
+            const int64_t qb = b0 + (q < NBW ? q : NBW - 1);
+            const int64_t fb = qb < nblk ? qb : nblk - 1;  // this lane's flag word (clamped, always inside)
+            const bool watch = q < NBW && rk < R && b0 + q < nblk && done[fb] == 0;
+            uint32_t f = ld_relaxed(fp + fb);
+            uint64_t bad = __ballot(watch && f != epoch);
+            for (int p = 0; bad != 0 && p < max_polls; ++p) {
+                __builtin_amdgcn_s_sleep(2);
+                f = ld_relaxed(fp + fb);
+                bad = __ballot(watch && f != epoch);
+                ++n_polls;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            if (watch) stale[(int64_t)rk * nblk + fb] = f != epoch ? 1 : 0;
+            const uint64_t wm = __ballot(watch);
+            if (lane == 0) {
+                s_bad[par] = bad;
+                s_watch[par] = wm;
+            }
+            n_stale += (uint32_t)__builtin_popcountll(bad);
 #pragma unroll
-        for (int k = 0; k < NB; ++k) {
-            const bool examined = (wm >> (16 * k)) & 1u;
-            const uint32_t sb = (uint32_t)(bad >> (16 * k)) & 0xffffu;
-            valid[k] = examined && sb == 0;
-            n_pending += examined && sb != 0 ? 1u : 0u;
+            for (int k = 0; k < NBW; ++k)
+                n_pending += ((wm >> (16 * k)) & 1u) && ((bad >> (16 * k)) & 0xffffu) ? 1u : 0u;
+            // block `lane` of the tile is done when examined (its rank-0 lane watched) with no stale copy
+            if (lane < NBW && ((wm >> (16 * lane)) & 1u) && ((bad >> (16 * lane)) & 0xffffu) == 0) done[b0 + lane] = 1;
         }
-        n_stale += (uint32_t)__builtin_popcountll(bad);
+        __syncthreads();
+        const uint64_t bad = s_bad[par], wm = s_watch[par];
+        bool valid[NBW];  // wavefront-uniform
+#pragma unroll
+        for (int k = 0; k < NBW; ++k) valid[k] = ((wm >> (16 * k)) & 1u) && ((bad >> (16 * k)) & 0xffffu) == 0;
         bool any = false;
 #pragma unroll
-        for (int k = 0; k < NB; ++k) any = any || valid[k];
+        for (int k = 0; k < NBW; ++k) any = any || valid[k];
         if (!any) continue;
         const int64_t tbase = tile << log2_te;
-        for (int i0 = 0; i0 < it; i0 += 2) {
-            // instruction k of the pair belongs to block (i0 + k) * 512 >> log2_be of the tile
+        for (int j = 0; j < per_wave; j += 2) {
+            // this wavefront's instructions i = wave + 4 j (+ 4): block (i * 512) >> log2_be of the tile
             bool vk[2];
+            int64_t e0[2];
 #pragma unroll
-            for (int k = 0; k < 2; ++k) vk[k] = NB == 2 ? valid[k & (NB - 1)] : valid[0];
-            const int64_t e0 = tbase + (int64_t)i0 * 512 + lane * 8;
+            for (int k = 0; k < 2; ++k) {
+                const int i = wave + 4 * (j + k);
+                const int kb = (i << 9) >> log2_be;
+                bool v = false;
+#pragma unroll
+                for (int c = 0; c < NBW; ++c) v = v || (kb == c && valid[c]);
+                vk[k] = j + k < per_wave && v;
+                e0[k] = tbase + (int64_t)i * 512 + lane * 8;
+            }
             float acc[2][8];
             auto batch = [&](int r0, bool first) {
                 uint4 sv[RB][2];
 #pragma unroll
-                for (int j = 0; j < RB; ++j)
+                for (int jr = 0; jr < RB; ++jr)
 #pragma unroll
                     for (int k = 0; k < 2; ++k)
-                        if (vk[k]) sv[j][k] = lds16(t.payload[r0 + j] + e0 + k * 512);
+                        if (vk[k]) sv[jr][k] = lds16(t.payload[r0 + jr] + e0[k]);
 #pragma unroll
-                for (int j = 0; j < RB; ++j) {
-                    if (r0 + j >= R) continue;
+                for (int jr = 0; jr < RB; ++jr) {
+                    if (r0 + jr >= R) continue;
 #pragma unroll
                     for (int k = 0; k < 2; ++k) {
                         if (!vk[k]) continue;
-                        const uint32_t w[4] = {sv[j][k].x, sv[j][k].y, sv[j][k].z, sv[j][k].w};
+                        const uint32_t w[4] = {sv[jr][k].x, sv[jr][k].y, sv[jr][k].z, sv[jr][k].w};
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const float lo = bf16_lo(w[e]), hi = bf16_hi(w[e]);
-                            acc[k][2 * e] = first && j == 0 ? lo : acc[k][2 * e] + lo;
-                            acc[k][2 * e + 1] = first && j == 0 ? hi : acc[k][2 * e + 1] + hi;
+                            acc[k][2 * e] = first && jr == 0 ? lo : acc[k][2 * e] + lo;
+                            acc[k][2 * e + 1] = first && jr == 0 ? hi : acc[k][2 * e + 1] + hi;
                         }
                     }
                 }
@@ -172,26 +191,17 @@ __global__ __launch_bounds__(256) void k_flag_unpack(const int64_t ntiles, const
 #pragma unroll
             for (int k = 0; k < 2; ++k)
                 if (vk[k])
-                    sts16(out + e0 + k * 512,
+                    sts16(out + e0[k],
                           make_uint4(pack_bf16x2(acc[k][0], acc[k][1]), pack_bf16x2(acc[k][2], acc[k][3]),
                                      pack_bf16x2(acc[k][4], acc[k][5]), pack_bf16x2(acc[k][6], acc[k][7])));
         }
-        if (lane < NB && (lane == 0 ? valid[0] : valid[NB - 1])) done[b0 + lane] = 1;
     }
-    if (lane == 0) {
-        s_cnt[threadIdx.x >> 6][0] = n_stale;
-        s_cnt[threadIdx.x >> 6][1] = n_pending;
-        s_cnt[threadIdx.x >> 6][2] = n_polls;
-    }
-    __syncthreads();
-    // stale pairs and pending blocks in one 64-bit atomic per workgroup (a call adds at most 2^29 stale
-    // pairs, so the low word does not carry); re-reads in one 32-bit atomic
+    // wave 0 holds the counts: stale pairs and pending blocks in one 64-bit atomic (a call adds at most 2^29
+    // stale pairs, so the low word does not carry), re-reads in one 32-bit atomic
     if (threadIdx.x == 0) {
-        const uint32_t st = s_cnt[0][0] + s_cnt[1][0] + s_cnt[2][0] + s_cnt[3][0];
-        const uint32_t pe = s_cnt[0][1] + s_cnt[1][1] + s_cnt[2][1] + s_cnt[3][1];
-        const uint32_t po = s_cnt[0][2] + s_cnt[1][2] + s_cnt[2][2] + s_cnt[3][2];
-        if (st | pe) atomicAdd(reinterpret_cast<unsigned long long*>(counters), ((unsigned long long)pe << 32) | st);
-        if (po) atomicAdd(counters + 2, po);
+        if (n_stale | n_pending)
+            atomicAdd(reinterpret_cast<unsigned long long*>(counters), ((unsigned long long)n_pending << 32) | n_stale);
+        if (n_polls) atomicAdd(counters + 2, n_polls);
     }
 }
 
@@ -209,14 +219,19 @@ hipError_t launch_flag_unpack(const FlagParams& p, hipStream_t s) {
         t.flags[i] = p.flags[i < p.R ? i : p.R - 1];
     }
     const int64_t nblk = p.n >> p.log2_block;
-    if (p.log2_block == 9) {
-        const int64_t ntiles = (nblk + 1) / 2;
-        k_flag_unpack<2><<<poll_grid(ntiles, p.poll.max_workgroups), 256, 0, s>>>(
-            ntiles, nblk, p.log2_block, p.epoch, p.R, p.poll.max_polls, p.done, p.out, p.stale, p.counters, t);
-    } else {
-        k_flag_unpack<1><<<poll_grid(nblk, p.poll.max_workgroups), 256, 0, s>>>(
-            nblk, nblk, p.log2_block, p.epoch, p.R, p.poll.max_polls, p.done, p.out, p.stale, p.counters, t);
+    const int nbw = p.log2_block >= 11 ? 1 : 1 << (11 - p.log2_block);  // blocks per workgroup tile
+    const int64_t ntiles = (nblk + nbw - 1) / nbw;
+    const unsigned grid =
+        (unsigned)(p.poll.max_workgroups > 0 && ntiles > p.poll.max_workgroups ? p.poll.max_workgroups : ntiles);
+#define FC_FU(NBW)                                                                                             \
+    k_flag_unpack<NBW><<<grid, 256, 0, s>>>(ntiles, nblk, p.log2_block, p.epoch, p.R, p.poll.max_polls, p.done, \
+                                            p.out, p.stale, p.counters, t)
+    switch (nbw) {
+        case 4: FC_FU(4); break;
+        case 2: FC_FU(2); break;
+        default: FC_FU(1); break;
     }
+#undef FC_FU
     return hipGetLastError();
 }
 

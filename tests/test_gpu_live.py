@@ -80,7 +80,7 @@ def test_flag_receiver_matches_oracle(fc, orc, be, nblk, R, polls):
     assert np.all(got_st[:, skipped] == 0xAB), "blocks already done are not examined"
     assert_equal_bits(got_st[:, ~skipped], rst[:, ~skipped], "stale (examined)")
     assert_equal_bits(got_st[:, ~skipped], np.stack(masks)[:, ~skipped], "stale == injected")
-    want_polls = polls * _tiles_polled(np.stack(masks).astype(bool), done0, 2 if be == 512 else 1)
+    want_polls = polls * _tiles_polled(np.stack(masks).astype(bool), done0, max(1, 2048 // be))
     assert int(got_c[2]) == want_polls and int(got_c[3]) == 0
 
 
