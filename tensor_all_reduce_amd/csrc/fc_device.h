@@ -204,16 +204,25 @@ struct Unpack<8> {
 template <>
 struct Unpack<4> {
     static constexpr int PER_WORD = 8;
+    // Codes as fp16 subnormals: the half-word q (a code, 0..15) is the fp16 value q * 2^-24, and the mixed-
+    // precision fma converts it exactly, so fma(q * 2^-24, s * 2^24, z) = fl(q*s + z) with no int-to-float
+    // conversion.  s * 2^24 is exact.  Byte permutes put each code alone in a half-word.
     __device__ __forceinline__ static void run(uint32_t w, float s, float z, float* out) {
+        const float s24 = s * 16777216.0f;
         uint32_t ev = w & 0x0f0f0f0fu;         // byte k = code 2k
         uint32_t od = (w >> 4) & 0x0f0f0f0fu;  // byte k = code 2k+1
-        // Hide the masks' known-zero bits from the optimizer: otherwise it extracts every code with a
-        // bit-field instruction of its own instead of converting the bytes in place (v_cvt_f32_ubyteN).
-        asm("" : "+v"(ev), "+v"(od));
+        const uint32_t h[4] = {__builtin_amdgcn_perm(0u, ev, 0x0c010c00u), __builtin_amdgcn_perm(0u, ev, 0x0c030c02u),
+                               __builtin_amdgcn_perm(0u, od, 0x0c010c00u), __builtin_amdgcn_perm(0u, od, 0x0c030c02u)};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            out[2 * k] = __builtin_fmaf((float)((ev >> (8 * k)) & 0xffu), s, z);
-            out[2 * k + 1] = __builtin_fmaf((float)((od >> (8 * k)) & 0xffu), s, z);
+        for (int k = 0; k < 2; ++k) {
+            const _Float16 a0 = __builtin_bit_cast(_Float16, (uint16_t)(h[k] & 0xffffu));
+            const _Float16 a1 = __builtin_bit_cast(_Float16, (uint16_t)(h[k] >> 16));
+            const _Float16 b0 = __builtin_bit_cast(_Float16, (uint16_t)(h[k + 2] & 0xffffu));
+            const _Float16 b1 = __builtin_bit_cast(_Float16, (uint16_t)(h[k + 2] >> 16));
+            out[4 * k + 0] = __builtin_fmaf((float)a0, s24, z);  // code 4k
+            out[4 * k + 1] = __builtin_fmaf((float)b0, s24, z);  // code 4k+1
+            out[4 * k + 2] = __builtin_fmaf((float)a1, s24, z);  // code 4k+2
+            out[4 * k + 3] = __builtin_fmaf((float)b1, s24, z);  // code 4k+3
         }
     }
 };
