@@ -206,7 +206,8 @@ struct Unpack<4> {
     static constexpr int PER_WORD = 8;
     // Codes as fp16 subnormals: the half-word q (a code, 0..15) is the fp16 value q * 2^-24, and the mixed-
     // precision fma converts it exactly, so fma(q * 2^-24, s * 2^24, z) = fl(q*s + z) with no int-to-float
-    // conversion.  s * 2^24 is exact.  Byte permutes put each code alone in a half-word.
+    // conversion.  s * 2^24 is exact.  Byte permutes put each code alone in a half-word.  This relies on
+    // fp16 subnormals being kept (the kernels' floating-point mode flushes no fp16 or fp32 subnormals).
     __device__ __forceinline__ static void run(uint32_t w, float s, float z, float* out) {
         const float s24 = s * 16777216.0f;
         uint32_t ev = w & 0x0f0f0f0fu;         // byte k = code 2k

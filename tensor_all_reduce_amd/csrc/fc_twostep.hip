@@ -189,16 +189,25 @@ __device__ __forceinline__ void store_codes(uint8_t* p, const uint32_t (&w)[E * 
     else sts4(p, w[0]);
 }
 
-template <int B1, int B2, int G, int E>
-__global__ __launch_bounds__(256) void k_reduce(const int64_t nchunks, const int R, const ReduceKArgs a) {
+// R8: the rank count is 8 (every workload here), known at compile time.  Otherwise the compiler, not
+// knowing which ranks are folded, moves one rank's loads into its conditional fold, behind the scalar load
+// of its pointer, and that rank's data arrives a memory round trip late.
+template <int B1, int B2, int G, int E, bool R8>
+__global__ __launch_bounds__(256) void k_reduce(const int64_t nchunks, const int R_arg, const ReduceKArgs a) {
     constexpr int LPG = G / E;
     constexpr int IN_W = E * B1 / 32;  // input code words per rank
     constexpr int RB = 8;              // ranks loaded per batch
+    const int R = R8 ? 8 : R_arg;
+    __builtin_assume(R >= 1);  // validated on the host: rank 0 is always folded
     const int shard = blockIdx.y;
     const int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const bool valid = c0 < nchunks;
     const int64_t c = valid ? c0 : nchunks - 1;  // whole groups lie on either side of the end
     const int64_t gidx = c / LPG;
+    // 32-bit byte offsets from each rank's (wavefront-uniform) chunk base: a shard's codes are at most
+    // 2^31 bytes, and a uniform base plus a 32-bit lane offset needs no 64-bit address arithmetic per rank
+    const uint32_t coff = (uint32_t)c * (uint32_t)(E * B1 / 8);
+    const uint32_t moff = (uint32_t)gidx * 4u;
     float acc[E];
     // All RB loads of a batch are issued unconditionally (ranks past R re-read rank R-1 and are ignored),
     // so no branch separates them and they are all in flight together.  The first batch is outside the
@@ -208,8 +217,8 @@ __global__ __launch_bounds__(256) void k_reduce(const int64_t nchunks, const int
     auto load_batch = [&](int r0) {
 #pragma unroll
         for (int j = 0; j < RB; ++j) {
-            load_codes<E, B1>(a.in_codes[shard][r0 + j] + c * (E * B1 / 8), wv[j]);
-            mv[j] = a.in_meta[shard][r0 + j][gidx];
+            load_codes<E, B1>(a.in_codes[shard][r0 + j] + coff, wv[j]);
+            mv[j] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(a.in_meta[shard][r0 + j]) + moff);
         }
     };
     auto fold_batch = [&](int r0) {
@@ -246,16 +255,22 @@ __global__ __launch_bounds__(256) void k_reduce(const int64_t nchunks, const int
     }
 }
 
-template <int B1, int B2, int E>
-static void reduce_launch_g(int64_t nchunks, int R, const ReduceKArgs& a, int group, dim3 grid, hipStream_t s) {
+template <int B1, int B2, int E, bool R8>
+static void reduce_launch_gr(int64_t nchunks, int R, const ReduceKArgs& a, int group, dim3 grid, hipStream_t s) {
     switch (group) {
-        case 32: k_reduce<B1, B2, 32, E><<<grid, 256, 0, s>>>(nchunks, R, a); break;
-        case 64: k_reduce<B1, B2, 64, E><<<grid, 256, 0, s>>>(nchunks, R, a); break;
-        case 128: k_reduce<B1, B2, 128, E><<<grid, 256, 0, s>>>(nchunks, R, a); break;
+        case 32: k_reduce<B1, B2, 32, E, R8><<<grid, 256, 0, s>>>(nchunks, R, a); break;
+        case 64: k_reduce<B1, B2, 64, E, R8><<<grid, 256, 0, s>>>(nchunks, R, a); break;
+        case 128: k_reduce<B1, B2, 128, E, R8><<<grid, 256, 0, s>>>(nchunks, R, a); break;
         default:
-            if constexpr (E >= 8) k_reduce<B1, B2, 256, E><<<grid, 256, 0, s>>>(nchunks, R, a);  // 4-element chunks: G <= 128
+            if constexpr (E >= 8) k_reduce<B1, B2, 256, E, R8><<<grid, 256, 0, s>>>(nchunks, R, a);  // 4-element chunks: G <= 128
             break;
     }
+}
+
+template <int B1, int B2, int E>
+static void reduce_launch_g(int64_t nchunks, int R, const ReduceKArgs& a, int group, dim3 grid, hipStream_t s) {
+    if (R == 8) reduce_launch_gr<B1, B2, E, true>(nchunks, R, a, group, grid, s);
+    else reduce_launch_gr<B1, B2, E, false>(nchunks, R, a, group, grid, s);
 }
 
 template <int E>
