@@ -431,7 +431,9 @@ def host_cpu_model() -> str:
 def oracle_by_config(max_elems=1 << 22):
     """The oracle on each of the five workloads: single-threaded, pinned to one host core, median of 5 runs
     (3 for the two largest).  Workloads over `max_elems` elements per rank run on a block of their rows
-    and are scaled to the whole workload (rows are independent, so the cost is linear in them)."""
+    and are scaled to the whole workload (rows are independent, so the cost is linear in them).  Then the
+    norm-first path on the decode workload, the all-gather of the int8 prefill messages and the flag
+    receiver on 8 x 2 MiB, as their benchmark rows run them."""
     sys.path.insert(0, os.path.join(ROOT, "oracle"))
     import numpy as np
     import oracle
@@ -474,6 +476,36 @@ def oracle_by_config(max_elems=1 << 22):
             us = statistics.median(times) * 1e6 * (cfg.T / T)
             out[cfg.slug] = {"us_per_step": round(us, 1), "GB/s": round(full_bytes / (us * 1e-6) / 1e9, 4),
                              "runs": reps, "sample_rows": T, "rows": cfg.T}
+        # the rows beyond the five workloads, on the workloads their benchmark rows use
+        c2, c3, c4 = dg.CONFIGS[2], dg.CONFIGS[3], dg.CONFIGS[4]
+        parts = [dg.partial(c2, r) for r in range(c2.R)]
+        res, gam = dg.residual(c2), dg.gamma(c2)
+        extra = {
+            "norm_first_decode": (lambda: oracle.two_step_normfirst(parts, c2.bits_rs, c2.bits_ag, c2.group, res, gam,
+                                                                    c2.eps, c2.H),
+                                  sum(bm.total(v) for v in bm.two_step_normfirst_whole(
+                                      c2.R, c2.T, c2.H, c2.bits_rs, c2.bits_ag, c2.group).values())),
+        }
+        msg3 = c3.L * c3.bits_ag // 8 + 4 * (c3.L // c3.group)
+        nwords = -(-msg3 // 4 // c4.block_slots) * c4.block_slots
+        rng = np.random.default_rng(0xFC0C)
+        gsl = [(rng.integers(0, 1 << 32, nwords, dtype=np.uint64)
+                | (dg.stale_epochs(c4, r, nwords)[0].astype(np.uint64) << np.uint64(32))) for r in range(c3.R)]
+        extra["allgather_int8_prefill_messages"] = (lambda: oracle.ll_gather(gsl, nwords, c4.block_slots, c4.epoch),
+                                                    bm.total(bm.ll_gather(c3.R, nwords, c4.block_slots)))
+        n2, be = 1 << 20, 2048
+        xs = [dg.synth_bf16((0xF2, r), n2) for r in range(8)]
+        fl = [np.full(n2 // be, 7, np.uint32) for _ in range(8)]
+        extra["flag_receiver_8x2MiB"] = (lambda: oracle.flag_unpack_reduce(xs, fl, n2, be, 7),
+                                         bm.total(bm.flag_unpack(8, n2, be)))
+        for name, (run, by) in extra.items():
+            times = []
+            for _ in range(5):
+                t0 = time.perf_counter()
+                run()
+                times.append(time.perf_counter() - t0)
+            us = statistics.median(times) * 1e6
+            out[name] = {"us_per_step": round(us, 1), "GB/s": round(by / (us * 1e-6) / 1e9, 4), "runs": 5}
     finally:
         os.sched_setaffinity(0, old)
     return out
