@@ -64,7 +64,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", default="all", help="other hot-path rows to measure: all | none | comma list of "
-                                                  "prefill,share,normfirst,ll,llgather,rmsnorm,layer")
+                                                  "prefill,warm,share,normfirst,ll,llgather,rmsnorm,layer,encodings")
     ap.add_argument("--kernel-reps", type=int, default=0, help="graph replays per call timing (0 = auto)")
     ap.add_argument("--fit-encodings", metavar="JSON", help="write the selector's fitted cost table here")
     ap.add_argument("--pmc-rows", metavar="BYTES_JSON", help="only launch the row kernels for counter runs")
@@ -584,6 +584,8 @@ def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_firs
         rout = torch.empty(cfg.n, dtype=torch.int16, device=cx.dev)
         norm = p.make_norm(gam, None if norm_first else out, residual=res, residual_out=rout, eps=cfg.eps)
         sets.append((p, norm, (res, out, rout)))
+    if warm:  # graphs of 64 steps on the one buffer set (a graph of one step would time its launch)
+        sets, nsets = sets * 64, 64
     torch.cuda.synchronize()
 
     def step(k):
@@ -1160,7 +1162,7 @@ def main():
                      "traffic": tr["total"] if tr else None},
         "wall_s": round(main_r["wall"], 3),
     }
-    rows = {"prefill", "ll", "llgather", "rmsnorm", "share", "normfirst", "layer", "encodings"} if args.rows == "all" \
+    rows = {"prefill", "warm", "ll", "llgather", "rmsnorm", "share", "normfirst", "layer", "encodings"} if args.rows == "all" \
         else set() if args.rows == "none" \
         else set(args.rows.split(","))
     extra = {}
@@ -1172,6 +1174,13 @@ def main():
                                      "us_per_step_spread": r3["spread"],
                                      "GB/s": round(v3, 1), "pct_hbm_peak": round(100 * v3 / HBM_PEAK_GBPS, 2),
                                      "pct_copy_ceiling": round(100 * v3 / copy_gbps, 2), "calls": r3["per_call"]}
+    if "warm" in rows and not args.warm:
+        # context, not the headline: inputs already in the caches, as right after the GEMM that produced them
+        rw = bench_two_step(cx, cfg, args.steps, args.warmup, True, args.kernel_reps, None)
+        vw = rw["step_bytes"] / (rw["ms_step"] * 1e-3) / 1e9
+        extra["warm_caches"] = {"workload": cfg.name, "mode": "one buffer set, cache-resident",
+                                "us_per_step": round(rw["ms_step"] * 1e3, 3), "GB/s": round(vw, 1),
+                                "calls": {k: v["us"] for k, v in rw["per_call"].items()}}
     if "share" in rows:
         extra["share_decode"] = bench_share(cx, cfg, args.steps, args.warmup, args.kernel_reps)
         if args.config != 3:
