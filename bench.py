@@ -547,20 +547,39 @@ class Ctx:
 
 
 def copy_ceiling(cx):
+    """Copy, read-only and write-only bandwidth on 1 GiB (GB/s): the ceilings a kernel's access mix is
+    compared with."""
     from tensor_all_reduce_amd import _lib
     torch = cx.torch
     nb = 1 << 30
     src = torch.empty(nb, dtype=torch.uint8, device=cx.dev)
     dst = torch.empty(nb, dtype=torch.uint8, device=cx.dev)
-    _lib.fc_copy(src, dst)
-    torch.cuda.synchronize()
-    a, b = cx.ev(), cx.ev()
-    a.record()
-    for _ in range(10):
-        _lib.fc_copy(src, dst)
-    b.record()
-    torch.cuda.synchronize()
-    return 2 * nb * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+    out = {}
+    for mode, name, moved in ((0, "copy", 2 * nb), (1, "read", nb), (2, "write", nb)):
+        _lib.fc_bandwidth_probe(src, dst, nb, mode)
+        torch.cuda.synchronize()
+        a, b = cx.ev(), cx.ev()
+        a.record()
+        for _ in range(10):
+            _lib.fc_bandwidth_probe(src, dst, nb, mode)
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = moved * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def mixed_ceiling_us(read_bytes, write_bytes, ceil):
+    """Shortest time for this access mix at the measured read and write ceilings (microseconds)."""
+    return (read_bytes / (ceil["read"] * 1e9) + write_bytes / (ceil["write"] * 1e9)) * 1e6
+
+
+def add_mixed(per_call, calls, ceil):
+    for name, c in per_call.items():
+        if name in calls:
+            t = mixed_ceiling_us(calls[name]["read"], calls[name]["write"], ceil)
+            c["pct_mixed_ceiling"] = round(100 * t / c["us"], 1)
 
 
 def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_first=False):
@@ -1142,7 +1161,10 @@ def main():
     value = main_r["step_bytes"] / (ms_step * 1e-3) / 1e9
     per_call = main_r["per_call"]
     dom = max(per_call, key=lambda k: per_call[k]["us"])
-    copy_gbps = copy_ceiling(cx)
+    ceil = copy_ceiling(cx)
+    copy_gbps = ceil["copy"]
+    from tensor_all_reduce_amd import bytes_model as bm
+    add_mixed(per_call, bm.two_step_whole(cfg.R, cfg.T, cfg.H, cfg.bits_rs, cfg.bits_ag, cfg.group), ceil)
     tr = per_call[dom]["traffic"]
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -1156,6 +1178,7 @@ def main():
         "bytes_per_step": main_r["step_bytes"],
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "copy_ceiling_GBps": round(copy_gbps, 1), "pct_copy_ceiling": round(100 * value / copy_gbps, 2),
+        "read_ceiling_GBps": round(ceil["read"], 1), "write_ceiling_GBps": round(ceil["write"], 1),
         "calls": per_call,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": per_call[dom]["GB/s"], "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": per_call[dom]["frac_hbm"],
@@ -1174,6 +1197,7 @@ def main():
                                      "us_per_step_spread": r3["spread"],
                                      "GB/s": round(v3, 1), "pct_hbm_peak": round(100 * v3 / HBM_PEAK_GBPS, 2),
                                      "pct_copy_ceiling": round(100 * v3 / copy_gbps, 2), "calls": r3["per_call"]}
+        add_mixed(r3["per_call"], bm.two_step_whole(c3.R, c3.T, c3.H, c3.bits_rs, c3.bits_ag, c3.group), ceil)
     if "warm" in rows and not args.warm:
         # context, not the headline: inputs already in the caches, as right after the GEMM that produced them
         rw = bench_two_step(cx, cfg, args.steps, args.warmup, True, args.kernel_reps, None)

@@ -210,6 +210,13 @@ fc_status fc_flag_pack(const uint16_t* const* x, int R, int64_t n, int block_ele
  * ceiling the kernels above are compared with. */
 fc_status fc_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
+/* Measurement helper: the HBM ceilings the kernels are compared with, by access mix.  mode 0: the copy
+ * above (src -> dst, `bytes` each way); mode 1: read `bytes` of src (16-byte aligned) with four
+ * non-temporal 16-byte loads per lane, folding them so the loads stay; dst is a 4-byte sink that is
+ * written only if the fold hits one fixed value; mode 2: write `bytes` of dst with non-temporal 16-byte
+ * stores (src unused, may be NULL).  bytes: a multiple of 16, at most 2^40. */
+fc_status fc_bandwidth_probe(const void* src, void* dst, int64_t bytes, int mode, hipStream_t stream);
+
 const char* fc_status_string(fc_status s);
 int fc_last_hip_error(void); /* hipError_t of the last FC_E_LAUNCH on this thread */
 int fc_abi_version(void);

@@ -79,9 +79,10 @@ def _load():
                                  vp]
     lib.fc_ll_gather.argtypes = [C.POINTER(vp), i32, i64, i32, u32, C.POINTER(vp), vp, vp, vp, vp]
     lib.fc_copy.argtypes = [vp, vp, i64, vp]
+    lib.fc_bandwidth_probe.argtypes = [vp, vp, i64, i32, vp]
     for f in ("fc_quantize", "fc_reduce_shard", "fc_reduce_shard_norm", "fc_gather_dequant", "fc_reduce_rmsnorm", "fc_ll_unpack_reduce",
               "fc_ll_pack", "fc_ll_gather", "fc_ll_poll_unpack_reduce", "fc_flag_unpack_reduce", "fc_flag_pack",
-              "fc_copy"):
+              "fc_copy", "fc_bandwidth_probe"):
         getattr(lib, f).restype = i32
     return lib
 
@@ -237,6 +238,11 @@ def fc_flag_pack(x, block_elems: int, epoch: int, payload, flags, block_order=No
 def fc_copy(src, dst, nbytes: int | None = None, stream=None) -> None:
     nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
     _check(_lib.fc_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "fc_copy")
+
+
+def fc_bandwidth_probe(src, dst, nbytes: int, mode: int, stream=None) -> None:
+    """mode 0 copy, 1 read (dst: a 4-byte sink), 2 write (src unused)."""
+    _check(_lib.fc_bandwidth_probe(_ptr(src), _ptr(dst), nbytes, mode, _stream(stream)), "fc_bandwidth_probe")
 
 
 def fc_abi_version() -> int:

@@ -528,6 +528,17 @@ fc_status fc_flag_pack(const uint16_t* const* x, int R, int64_t n, int block_ele
     return launched(fc::launch_flag_pack(p, stream));
 }
 
+fc_status fc_bandwidth_probe(const void* src, void* dst, int64_t bytes, int mode, hipStream_t stream) {
+    if (mode < 0 || mode > 2 || bytes < 0) return FC_E_ARG;
+    if (bytes % 16 != 0 || bytes > (int64_t(1) << 40)) return FC_E_SHAPE;
+    if (bytes == 0) return FC_OK;
+    if ((mode != 2 && !src) || !dst) return FC_E_NULL;  // dst: the copy's target, the sink, or the written range
+    if ((src && !aligned(src, 16)) || !aligned(dst, mode == 1 ? 4 : 16)) return FC_E_ALIGN;
+    if (mode == 0 && overlap(rng(src, bytes), rng(dst, bytes))) return FC_E_ARG;
+    if (mode == 1 && overlap(rng(src, bytes), rng(dst, 4))) return FC_E_ARG;
+    return launched(fc::launch_bandwidth_probe(src, dst, bytes, mode, stream));
+}
+
 fc_status fc_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
     if (bytes < 0) return FC_E_ARG;
     if (bytes % 16 != 0 || bytes > (int64_t(1) << 40)) return FC_E_SHAPE;

@@ -143,5 +143,6 @@ hipError_t launch_ll_poll(const LLParams& p, const PollParams& q, hipStream_t s)
 hipError_t launch_flag_unpack(const FlagParams& p, hipStream_t s);
 hipError_t launch_flag_pack(const FlagPackParams& p, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+hipError_t launch_bandwidth_probe(const void* src, void* dst, int64_t bytes, int mode, hipStream_t s);
 
 }  // namespace fc

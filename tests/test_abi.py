@@ -29,7 +29,7 @@ def test_exports_every_declared_function(L):
     names = declared_functions()
     assert {"fc_quantize", "fc_reduce_shard", "fc_reduce_shard_norm", "fc_gather_dequant", "fc_reduce_rmsnorm",
             "fc_ll_unpack_reduce", "fc_ll_poll_unpack_reduce", "fc_flag_unpack_reduce", "fc_flag_pack",
-            "fc_ll_pack", "fc_copy", "fc_status_string", "fc_last_hip_error", "fc_abi_version"} <= set(names)
+            "fc_ll_pack", "fc_copy", "fc_bandwidth_probe", "fc_status_string", "fc_last_hip_error", "fc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L.lib, n), n
     assert L.fc_abi_version() == 4
@@ -289,3 +289,16 @@ def test_copy_validation(L):
     assert f(A, A + 64, 1024, None) == L.FC_E_ARG
     assert f(A, A + 0x100000, 0, None) == L.FC_OK
     assert f(None, A, 1024, None) == L.FC_E_NULL
+
+
+def test_bandwidth_probe_validation(L):
+    f = L.lib.fc_bandwidth_probe
+    assert f(A, A + 0x100000, 1024, 3, None) == L.FC_E_ARG        # mode
+    assert f(A, A + 0x100000, 100, 1, None) == L.FC_E_SHAPE
+    assert f(A, A + 0x100000, 0, 2, None) == L.FC_OK
+    assert f(None, A, 1024, 1, None) == L.FC_E_NULL                # read needs its source
+    assert f(A, None, 1024, 1, None) == L.FC_E_NULL                # ... and its sink
+    assert f(A, A + 0x100002, 1024, 1, None) == L.FC_E_ALIGN        # sink: 4-byte aligned
+    assert f(A, A + 0x100004, 1024, 2, None) == L.FC_E_ALIGN        # written range: 16-byte aligned
+    assert f(A, A + 512, 1024, 1, None) == L.FC_E_ARG               # sink inside the range read
+    assert f(A, A + 64, 1024, 0, None) == L.FC_E_ARG                # copy: overlap
