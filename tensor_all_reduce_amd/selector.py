@@ -11,17 +11,17 @@ Encodings built here:
               then reads the block: fewer bytes, one synchronization per block and a dependent read.
 
 Model (the plainest reading of the trade the selector makes): the latency of one transfer of S payload
-bytes from each of R ranks is
+bytes from each of R ranks is the larger of a synchronization floor and a transfer time,
 
-    t(enc, S, R) = a + b * R + c * R * wire(enc, S)
+    t(enc, S, R) = max(a + b * R,  d + c * R * wire(enc, S))
 
-where wire() is the bytes one rank sends.  a holds an encoding's fixed synchronization latency (for a
-flag: the dependent flag-then-payload read), b its per-rank cost, c its cost per byte on the wire, which
-for a flag encoding also carries its per-block fence (a block is a fixed number of bytes, so blocks and
-bytes cannot be told apart within one encoding).  The three non-negative coefficients are fitted per
-encoding, by non-negative least squares, to latencies measured with a sender and a receiver running at
-the same time.  ``select`` returns the encoding with the lowest predicted latency (ties: the listed
-order).  Host logic only.
+where wire() is the bytes one rank sends.  a + b R is what the encoding costs however small the message
+(launch, readiness checks, for a flag the dependent flag-then-payload read); d + c R wire is the time
+to move its bytes, c also carrying a flag encoding's per-block fence (a block is a fixed number of bytes,
+so blocks and bytes cannot be told apart within one encoding).  The four non-negative coefficients are
+fitted per encoding to latencies measured with a sender and a receiver running at the same time,
+minimising the relative error.  ``select`` returns the encoding with the lowest predicted latency (ties:
+the listed order).  Host logic only.
 """
 from __future__ import annotations
 
@@ -56,35 +56,41 @@ def blocks(enc: str, S: int) -> int:
     return math.ceil(S / 2 / flag_block(enc))
 
 
-def features(enc: str, S: int, R: int) -> list[float]:
-    return [1.0, float(R), float(R * wire_bytes(enc, S))]
-
-
 @dataclass(frozen=True)
 class EncodingCost:
     enc: str
-    coef: tuple  # (a us, b us per rank, c us per wire byte)
+    coef: tuple  # (a us, b us per rank, c us per wire byte, d us)
 
     def predict(self, S: int, R: int) -> float:
-        return sum(k * f for k, f in zip(self.coef, features(self.enc, S, R)))
+        a, b, c, d = self.coef
+        return max(a + b * R, d + c * R * wire_bytes(self.enc, S))
 
 
 def fit(rows) -> dict[str, EncodingCost]:
-    """rows: iterable of (enc, S, R, t_us), t_us > 0.  Non-negative least squares per encoding on the
-    relative error (each row divided by its latency): the choice compares latencies at one size, so a
-    microsecond matters as much at 10 us as a hundred at 1 ms."""
+    """rows: iterable of (enc, S, R, t_us), t_us > 0.  Per encoding, non-negative coefficients minimising
+    the relative error (the choice compares latencies at one size, so a microsecond matters as much at
+    10 us as a hundred at 1 ms), from several starting points (the max makes the problem non-convex)."""
     import numpy as np
-    from scipy.optimize import nnls
+    from scipy.optimize import least_squares
     by = {}
     for enc, S, R, t in rows:
-        by.setdefault(enc, []).append((features(enc, S, R), t))
+        by.setdefault(enc, []).append((float(R), float(R * wire_bytes(enc, S)), float(t)))
     out = {}
     for enc, pts in by.items():
-        y = np.array([p[1] for p in pts], dtype=np.float64)
-        A = np.array([p[0] for p in pts], dtype=np.float64) / y[:, None]
-        scale = np.maximum(A.max(axis=0), 1e-30)  # column scaling keeps the problem well conditioned
-        x, _ = nnls(A / scale, np.ones_like(y))
-        out[enc] = EncodingCost(enc, tuple(float(v) for v in x / scale))
+        R = np.array([p[0] for p in pts])
+        x = np.array([p[1] for p in pts])
+        t = np.array([p[2] for p in pts])
+        scale = np.array([t.min(), t.min(), t.max() / x.max(), t.min()])  # unit steps of comparable size
+
+        def resid(q):
+            a, b, c, d = q * scale
+            return np.maximum(a + b * R, d + c * x) / t - 1.0
+        best = None
+        for x0 in ((1.0, 0.1, 1.0, 0.1), (0.5, 0.05, 0.5, 0.5), (1.0, 0.0, 2.0, 0.0), (0.8, 0.2, 1.0, 1.0)):
+            r = least_squares(resid, x0=np.array(x0), bounds=(0.0, np.inf))
+            if best is None or r.cost < best.cost:
+                best = r
+        out[enc] = EncodingCost(enc, tuple(float(v) for v in best.x * scale))
     return out
 
 
@@ -110,7 +116,7 @@ def crossover(costs: dict[str, EncodingCost], R: int, lo: int = 1 << 10, hi: int
 
 
 def save(path: str, costs: dict[str, EncodingCost], measured, command: str, machine: str) -> None:
-    doc = {"model": "t_us = a + b*R + c*R*wire_bytes", "command": command, "machine": machine,
+    doc = {"model": "t_us = max(a + b*R, d + c*R*wire_bytes)", "command": command, "machine": machine,
            "coefficients": {e: list(c.coef) for e, c in costs.items()},
            "measured": [list(r) for r in measured]}
     with open(path, "w") as f:

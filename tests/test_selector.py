@@ -19,53 +19,55 @@ def test_wire_bytes_and_blocks():
         sel.flag_block("ll")
 
 
-def synthetic(coefs, sizes=(1 << 12, 1 << 15, 1 << 18, 1 << 21, 1 << 23), ranks=(2, 4, 8)):
+def synthetic(coefs, sizes=(1 << 12, 1 << 14, 1 << 16, 1 << 18, 1 << 20, 1 << 22, 1 << 24), ranks=(2, 4, 8)):
     rows = []
-    for enc, (a, b, c) in coefs.items():
+    for enc, (a, b, c, d) in coefs.items():
         for S in sizes:
             for R in ranks:
-                rows.append((enc, S, R, a + b * R + c * R * sel.wire_bytes(enc, S)))
+                rows.append((enc, S, R, max(a + b * R, d + c * R * sel.wire_bytes(enc, S))))
     return rows
 
 
-COEFS = {"ll": (6.0, 0.3, 1.0 / 3000.0), "flag512": (11.0, 0.5, 1.0 / 5200.0),
-         "flag2048": (14.0, 0.4, 1.0 / 6000.0), "flag8192": (20.0, 0.4, 1.0 / 6100.0)}
+# (a, b, c, d): floor a + b R, transfer d + c R wire; each branch binds on part of the sizes above
+COEFS = {"ll": (7.5, 0.25, 9.0e-7, 2.0), "flag512": (6.0, 0.25, 2.3e-6, 1.0),
+         "flag2048": (6.5, 0.2, 2.2e-6, 1.5), "flag8192": (8.0, 0.3, 2.0e-6, 2.5)}
 
 
 def test_fit_recovers_exact_coefficients():
     costs = sel.fit(synthetic(COEFS))
     for enc, want in COEFS.items():
-        got = costs[enc].coef
-        for g, w in zip(got, want):
-            assert g == pytest.approx(w, rel=1e-6, abs=1e-9), enc
+        for g, w in zip(costs[enc].coef, want):
+            assert g == pytest.approx(w, rel=1e-4, abs=1e-9), (enc, costs[enc].coef)
 
 
 def test_fit_is_non_negative():
-    rows = [("ll", S, 8, 100.0 - S * 1e-5) for S in (1 << 10, 1 << 14, 1 << 18, 1 << 20)]  # falling with size
+    rows = [("ll", S, R, 100.0 - S * 1e-5) for S in (1 << 10, 1 << 14, 1 << 18, 1 << 20) for R in (2, 8)]
     c = sel.fit(rows)["ll"].coef
     assert all(v >= 0 for v in c)
 
 
 def test_choice_and_crossover_match_the_closed_form():
     costs = {e: sel.EncodingCost(e, c) for e, c in COEFS.items()}
-    assert sel.select(costs, 1 << 10, 8) == "ll"         # small: the fixed latency decides
-    assert sel.select(costs, 1 << 26, 8) == "flag8192"    # large: bytes decide
-    # ll against flag512 alone: equal where a_l + b_l R + c_l R 2S = a_f + b_f R + c_f R (S + 4 S / 1024)
-    a_l, b_l, c_l = COEFS["ll"]
-    a_f, b_f, c_f = COEFS["flag512"]
+    assert sel.select(costs, 1 << 10, 8) == "flag512"   # small: the lowest floor decides
+    assert sel.select(costs, 1 << 26, 8) == "ll"        # large: the cheapest byte decides
+    # ll against flag512 at R = 8: ll still sits on its floor 7.5 + 0.25 R = 9.5 where flag512's transfer
+    # time 1 + 2.3e-6 * R * S * (1 + 4/1024) reaches it, so that is where the choice flips
+    a_l, b_l, c_l, d_l = COEFS["ll"]
+    a_f, b_f, c_f, d_f = COEFS["flag512"]
     R = 8
-    S_eq = ((a_f - a_l) + (b_f - b_l) * R) / (R * (2 * c_l - c_f * (1 + 4 / 1024)))
+    S_eq = (a_l + b_l * R - d_f) / (c_f * R * (1 + 4 / 1024))
+    assert d_l + c_l * R * 2 * S_eq < a_l + b_l * R  # (ll on its floor there)
     two = {"ll", "flag512"}
-    below, above = int(S_eq * 0.9) // 2 * 2, int(S_eq * 1.1) // 2 * 2
-    assert sel.select(costs, below, R, allowed=two) == "ll"
-    assert sel.select(costs, above, R, allowed=two) == "flag512"
+    below, above = int(S_eq * 0.95) // 2 * 2, int(S_eq * 1.05) // 2 * 2
+    assert sel.select(costs, below, R, allowed=two) == "flag512"
+    assert sel.select(costs, above, R, allowed=two) == "ll"
     steps = sel.crossover(costs, R)
-    assert steps[0] == (1 << 10, "ll") and steps[-1][1] == "flag8192"
+    assert steps[0][1] == "flag512" and steps[-1][1] == "ll"
     assert [S for S, _ in steps] == sorted(S for S, _ in steps)
 
 
 def test_ties_take_the_listed_order():
-    same = {e: sel.EncodingCost(e, (5.0, 0.0, 0.0)) for e in sel.ENCODINGS}
+    same = {e: sel.EncodingCost(e, (5.0, 0.0, 0.0, 0.0)) for e in sel.ENCODINGS}
     assert sel.select(same, 1 << 20, 4) == sel.ENCODINGS[0]
     with pytest.raises(ValueError):
         sel.select(same, 1 << 20, 4, allowed=set())
@@ -94,7 +96,7 @@ def test_committed_table_chooses_well_on_its_own_measurements():
         choice = sel.select(costs, S, R, allowed=set(meas))
         regrets.append(meas[choice] / min(meas.values()) - 1.0)
     assert len(regrets) >= 10
-    assert max(regrets) <= 0.30 and float(np.mean(regrets)) <= 0.08, regrets
+    assert max(regrets) <= 0.15 and float(np.mean(regrets)) <= 0.03, regrets
 
 
 def test_committed_choice_on_the_slot_workload():
