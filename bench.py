@@ -1230,6 +1230,21 @@ def main():
         extra["two_half_layer"] = bench_layer(cx)
     if "encodings" in rows:
         extra["readiness_encodings"] = bench_encodings(cx, args.fit_encodings)
+    # each row's time against the ceiling for its own read/write mix
+    if "self_sync_slots" in extra:
+        r, c4 = extra["self_sync_slots"], dg.CONFIGS[4]
+        a = bm.ll_unpack(c4.R, c4.n, c4.block_slots, completed_blocks=r["blocks"] - r["pending_blocks"])
+        r["pass1_pct_mixed_ceiling"] = round(100 * mixed_ceiling_us(a["read"], a["write"], ceil) / r["pass1_us"], 1)
+    if "self_sync_allgather" in extra:
+        for r in extra["self_sync_allgather"]["by_payload"].values():
+            a = bm.ll_gather(r["R"], r["words_per_rank"], dg.CONFIGS[4].block_slots,
+                             completed_blocks=r["pairs"] - r["pending_pairs"])
+            r["pass1_pct_mixed_ceiling"] = round(100 * mixed_ceiling_us(a["read"], a["write"], ceil) / r["pass1_us"], 1)
+    if "tokenweave_reduce_rmsnorm" in extra:
+        r, c5 = extra["tokenweave_reduce_rmsnorm"], dg.CONFIGS[5]
+        a = bm.reduce_rmsnorm(c5.R, c5.splits[0], c5.H, True, True)
+        r["both_halves_pct_mixed_ceiling"] = round(
+            100 * 2 * mixed_ceiling_us(a["read"], a["write"], ceil) / r["both_halves_us"], 1)
     if extra:
         line["rows"] = extra
     if not args.no_cpu_baseline:
