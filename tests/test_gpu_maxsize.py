@@ -1,7 +1,8 @@
 """GPU parity at the largest sizes the C ABI accepts, on sampled groups, rows and blocks that the oracle
 recomputes one by one (they are independent): the quantizer past one launch piece (2^33 elements), the
-reduce of a 2^31 - 128 element shard, the gather + epilogue of 2^31 - 8192 elements and the slot receiver
-on 2^31 - 128 elements per rank.  These exercise the 32-bit element indexes and the 64-bit byte offsets
+reduce of a 2^31 - 128 element shard, the gather + epilogue of 2^31 - 8192 elements, the slot receiver
+on 2^31 - 128 elements per rank, the unquantized reduce + RMSNorm of 2^31 - 8192 elements, the flag
+receiver with 65536-element blocks and the all-gather of 2^31 - 64 words.  These exercise the 32-bit element indexes and the 64-bit byte offsets
 at their limits.  Inputs are seeded on the GPU (torch generators; the oracle gets the sampled bytes)."""
 import numpy as np
 import pytest
@@ -157,3 +158,78 @@ def test_slot_receiver_largest(fc, orc):
                           rst[:, 0], f"stale flags of block {b}")
         got = _host(out, 2 * B * b, 2 * B * (b + 1), np.uint16)
         assert_equal_bits(got, ro if rdn[0] else np.zeros(2 * B, np.uint16), f"out of block {b}")
+
+
+def test_reduce_rmsnorm_largest(fc, orc):
+    import torch
+    from gpu_helpers import assert_bf16_close, assert_equal_bits
+    R, H = 2, 8192
+    rows = KMAX // H
+    n = rows * H
+    parts = [_bf16(n, 60 + r) for r in range(R)]
+    res, gam = _bf16(n, 62), _bf16(H, 63)
+    out = torch.empty(n, dtype=torch.int16, device="cuda")
+    rout = torch.empty(n, dtype=torch.int16, device="cuda")
+    fc.fc_reduce_rmsnorm(parts, rows, dict(residual=res, gamma=gam, eps=1e-5, hidden=H, out=out, residual_out=rout))
+    torch.cuda.synchronize()
+    gh = gam.cpu().numpy().view(np.uint16)
+    for row in _samples(rows, np.random.default_rng(6)):
+        lo, hi = row * H, (row + 1) * H
+        ro, rr, _ = orc.reduce_rmsnorm([_host(p, lo, hi, np.uint16) for p in parts], 1, H,
+                                       _host(res, lo, hi, np.uint16), gh, 1e-5)
+        assert_equal_bits(_host(rout, lo, hi, np.uint16), rr, f"residual_out of row {row}")
+        assert_bf16_close(_host(out, lo, hi, np.uint16), ro, 2, f"out of row {row}")
+
+
+def test_flag_receiver_largest(fc, orc):
+    import torch
+    from gpu_helpers import assert_equal_bits
+    R, be, e = 2, 65536, 0xF1A6
+    n = KMAX // be * be
+    nblk = n // be
+    pays = [_bf16(n, 70 + r) for r in range(R)]
+    fls = [torch.full((nblk,), e, dtype=torch.int32, device="cuda") for _ in range(R)]
+    late = [nblk - 1, 0]
+    for b in late:
+        fls[1][b] = e - 1
+    out = torch.zeros(n, dtype=torch.int16, device="cuda")
+    stale = torch.zeros(R * nblk, dtype=torch.uint8, device="cuda")
+    done = torch.zeros(nblk, dtype=torch.uint8, device="cuda")
+    cnt = torch.zeros(4, dtype=torch.int32, device="cuda")
+    fc.fc_flag_unpack_reduce(pays, fls, n, be, e, out, stale, done, cnt)
+    torch.cuda.synchronize()
+    assert list(cnt.cpu().numpy().view(np.uint32)) == [len(late), len(late), 0, 0]
+    for b in _samples(nblk, np.random.default_rng(7), extra=late):
+        lo, hi = b * be, (b + 1) * be
+        ro, rst, rdn, _ = orc.flag_unpack_reduce([_host(p, lo, hi, np.uint16) for p in pays],
+                                                 [_host(f, b, b + 1, np.uint32) for f in fls], be, be, e)
+        assert_equal_bits(_host(done, b, b + 1, np.uint8), rdn, f"done of block {b}")
+        assert_equal_bits(np.array([_host(stale, r * nblk + b, r * nblk + b + 1, np.uint8)[0] for r in range(R)]),
+                          rst, f"stale flags of block {b}")
+        assert_equal_bits(_host(out, lo, hi, np.uint16), ro if rdn[0] else np.zeros(be, np.uint16), f"out of block {b}")
+
+
+def test_allgather_largest(fc, orc):
+    import torch
+    from gpu_helpers import assert_equal_bits
+    R, B, e = 1, 64, 0x6A7
+    nwords = KMAX // B * B
+    nblk = nwords // B
+    w = torch.randint(0, 1 << 31, (nwords,), generator=_gen(80), device="cuda", dtype=torch.int64)
+    slots = [w | (e << 32)]
+    del w
+    late = [nblk - 1, 5]
+    for b in late:
+        slots[0][b * B] = (slots[0][b * B] & 0xFFFFFFFF) | ((e + 1) << 32)
+    out = [torch.zeros(nwords, dtype=torch.int32, device="cuda")]
+    stale = torch.zeros(R * nblk, dtype=torch.uint8, device="cuda")
+    done = torch.zeros(R * nblk, dtype=torch.uint8, device="cuda")
+    cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
+    fc.fc_ll_gather(slots, nwords, B, e, out, stale, done, cnt)
+    torch.cuda.synchronize()
+    assert list(cnt.cpu().numpy().view(np.uint32)) == [len(late), len(late)]
+    for b in _samples(nblk, np.random.default_rng(8), extra=late):
+        ro, rst, rdn, _ = orc.ll_gather([_host(slots[0], b * B, (b + 1) * B, np.uint64)], B, B, e)
+        assert_equal_bits(_host(done, b, b + 1, np.uint8), rdn, f"done of block {b}")
+        assert_equal_bits(_host(stale, b, b + 1, np.uint8), rst, f"stale of block {b}")
+        assert_equal_bits(_host(out[0], b * B, (b + 1) * B, np.uint32), ro[0], f"words of block {b}")
