@@ -2,7 +2,8 @@
 recomputes one by one (they are independent): the quantizer past one launch piece (2^33 elements), the
 reduce of a 2^31 - 128 element shard, the gather + epilogue of 2^31 - 8192 elements, the slot receiver
 on 2^31 - 128 elements per rank, the unquantized reduce + RMSNorm of 2^31 - 8192 elements, the flag
-receiver with 65536-element blocks and the all-gather of 2^31 - 64 words.  These exercise the 32-bit element indexes and the 64-bit byte offsets
+receiver with 65536-element blocks, the all-gather of 2^31 - 64 words, and the norm before the all-gather
+on the largest shard and on shards whose rows together pass 2^31 elements.  These exercise the 32-bit element indexes and the 64-bit byte offsets
 at their limits.  Inputs are seeded on the GPU (torch generators; the oracle gets the sampled bytes)."""
 import numpy as np
 import pytest
@@ -233,3 +234,31 @@ def test_allgather_largest(fc, orc):
         assert_equal_bits(_host(done, b, b + 1, np.uint8), rdn, f"done of block {b}")
         assert_equal_bits(_host(stale, b, b + 1, np.uint8), rst, f"stale of block {b}")
         assert_equal_bits(_host(out[0], b * B, (b + 1) * B, np.uint32), ro[0], f"words of block {b}")
+
+
+@pytest.mark.parametrize("n_shards,L", [(1, KMAX // 8192 * 8192), (3, (1 << 30) - 8192)])
+def test_reduce_norm_first_largest(fc, orc, n_shards, L):
+    """The norm before the all-gather at the largest shard, and 3 shards whose rows together pass 2^31
+    elements (the launcher splits them into launches below that)."""
+    import torch
+    from gpu_helpers import assert_equal_bits
+    R, H, G, b1, b2 = 2, 8192, 128, 8, 8
+    ins = [(_codes(L, 90 + 10 * s + r), _meta(L // G, 95 + 10 * s + r)) for s in range(n_shards) for r in range(R)]
+    res, gam = _bf16(n_shards * L, 99), _bf16(H, 98)
+    rout = torch.empty(n_shards * L, dtype=torch.int16, device="cuda")
+    outs = [(torch.empty(L, dtype=torch.uint8, device="cuda"), torch.empty(L // G, dtype=torch.int32, device="cuda"))
+            for _ in range(n_shards)]
+    fc.fc_reduce_shard_norm(ins, R, L, b1, b2, G, dict(residual=res, gamma=gam, eps=1e-5, hidden=H, residual_out=rout),
+                            outs)
+    torch.cuda.synchronize()
+    gh = gam.cpu().numpy().view(np.uint16)
+    for s in range(n_shards):
+        for row in _samples(L // H, np.random.default_rng(10 + s)):
+            lo, hi = row * H, (row + 1) * H
+            cs = [_host(ins[s * R + r][0], lo, hi, np.uint8) for r in range(R)]
+            ms = [_host(ins[s * R + r][1], lo // G, hi // G, np.uint32) for r in range(R)]
+            oc, om, rr, _ = orc.reduce_norm_quant(cs, ms, H, b1, b2, G, _host(res, s * L + lo, s * L + hi, np.uint16),
+                                                   gh, 1e-5, H)
+            assert_equal_bits(_host(outs[s][1], lo // G, hi // G, np.uint32), om, f"meta, shard {s} row {row}")
+            assert_equal_bits(_host(outs[s][0], lo, hi, np.uint8), oc, f"codes, shard {s} row {row}")
+            assert_equal_bits(_host(rout, s * L + lo, s * L + hi, np.uint16), rr, f"residual_out, shard {s} row {row}")
