@@ -14,11 +14,12 @@ namespace fc {
 
 // =====================================================================================================
 // Flag encoding, sender side: R peers writing at the same time, grid row y = rank.  A workgroup writes a
-// span of K consecutive entries of the write order (K blocks, at least 8192 elements: K = 1 for blocks of
-// 8192 elements and more), 16 bytes per lane, then publishes them: a barrier (which orders every wave's
-// stores before it at workgroup scope), one release fence at agent scope by the first wavefront, which
-// writes the span back past its XCD's L2, and the K flag stores.  The fence is the expensive step (it
-// writes back the L2), so one fence covers a whole span rather than each block.
+// span of K consecutive entries of the write order (K blocks: the span is chosen by the launcher from the
+// message size, 2^13 to 2^17 elements, and K = 1 for blocks as large as the span), 16 bytes per lane, then
+// publishes them: a barrier (which orders every wave's stores before it at workgroup scope), one release
+// fence at agent scope by the first wavefront, which writes the span back past its XCD's L2, and the K
+// flag stores.  The fence is the expensive step (it writes back the L2), so one fence covers a whole span
+// rather than each block.
 // =====================================================================================================
 struct FlagPackTabs {
     const uint16_t* x[kMaxRanks];
@@ -53,8 +54,9 @@ __global__ __launch_bounds__(256) void k_flag_pack(const int64_t nblk, const int
         __syncthreads();
         if (threadIdx.x < 64) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            const int64_t q = (j << log2_k) + threadIdx.x;
-            if (threadIdx.x < (1 << log2_k) && q < nblk) {
+            for (int k = threadIdx.x; k < (1 << log2_k); k += 64) {  // the span's K flags, 64 at a time
+                const int64_t q = (j << log2_k) + k;
+                if (q >= nblk) break;
                 const int64_t b = order ? (int64_t)order[q] : q;
                 if (b >= 0 && b < nblk) __hip_atomic_store(flags + b, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -72,7 +74,11 @@ hipError_t launch_flag_pack(const FlagPackParams& p, hipStream_t s) {
         t.flags[i] = p.flags[q];
     }
     const int64_t nblk = p.n >> p.log2_block;
-    const int log2_k = p.log2_block >= 13 ? 0 : 13 - p.log2_block;  // spans of at least 8192 elements
+    // Span of one fence: about a 32nd of the message, between 2^13 and 2^17 elements (never less than a
+    // block).  Larger spans mean fewer L2 writebacks; smaller ones more workgroups and earlier flags.
+    int log2_span = 13;
+    while (log2_span < 17 && (int64_t(1) << (log2_span + 5)) < p.n) ++log2_span;
+    const int log2_k = p.log2_block >= log2_span ? 0 : log2_span - p.log2_block;
     const int64_t nspan = (nblk + (1 << log2_k) - 1) >> log2_k;
     const dim3 grid((unsigned)(nspan < 2048 ? nspan : 2048), (unsigned)p.R);
     k_flag_pack<<<grid, 256, 0, s>>>(nblk, p.log2_block, log2_k, p.epoch, p.pace, t);

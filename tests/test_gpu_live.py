@@ -84,12 +84,14 @@ def test_flag_receiver_matches_oracle(fc, orc, be, nblk, R, polls):
     assert int(got_c[2]) == want_polls and int(got_c[3]) == 0
 
 
-@pytest.mark.parametrize("be", [512, 2048])
-def test_flag_pack_round_trip(fc, orc, be):
-    """The sender writes every block (shuffled order) and its flag; the receiver completes every block."""
+@pytest.mark.parametrize("be,nblk", [(512, 45), (2048, 45), (512, 8192 + 3)])
+def test_flag_pack_round_trip(fc, orc, be, nblk):
+    """The sender writes every block (shuffled order) and its flag; the receiver completes every block.
+    The last case is a message large enough for the widest fence span (256 blocks of 512 per fence) and
+    ends in a ragged span."""
     import torch
     from gpu_helpers import assert_equal_bits, down, up
-    R, nblk, e = 4, 45, 9
+    R, e = 4, 9
     n = be * nblk
     xs = [dg.synth_bf16((be, 7, r), n) for r in range(R)]
     pays = [torch.zeros(n, dtype=torch.int16, device="cuda") for _ in range(R)]
