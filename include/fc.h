@@ -196,11 +196,14 @@ fc_status fc_flag_unpack_reduce(const uint16_t* const* payload, const uint32_t* 
                                 uint8_t* stale, uint8_t* done, uint32_t* counters, hipStream_t stream);
 
 /* Sender side of the flag encoding, used to emulate R peers writing at the same time (one launch): writes
- * rank r's x[r] (bf16 [n]) into payload[r] block by block in the order block_order[r] (as for fc_ll_pack),
- * and after each block a release store of epoch into flags[r][b] (each wavefront of the writing
- * workgroup first fences with release order, then the workgroup meets at a barrier).  pace: sleeps of
- * 512 clocks before each block (0..65536).  block_elems as for fc_flag_unpack_reduce.  Host arrays of R
- * device pointers; no output may overlap an input or another output. */
+ * rank r's x[r] (bf16 [n]) into payload[r] in the block order block_order[r] (as for fc_ll_pack), and
+ * publishes every block by storing epoch into flags[r][b] after a release fence.  A workgroup writes a
+ * span of consecutive entries of the order (2^13 to 2^17 elements, growing with n; at least one block),
+ * waits for its stores, meets at a barrier, fences once with release order at agent scope and stores
+ * the span's flags: a receiver that reads a flag and then fences with acquire order sees the whole
+ * block.  pace: sleeps of 512 clocks before each span (0..65536).  block_elems as for
+ * fc_flag_unpack_reduce.  Host arrays of R device pointers; no output may overlap an input or another
+ * output. */
 fc_status fc_flag_pack(const uint16_t* const* x, int R, int64_t n, int block_elems, uint32_t epoch,
                        const int32_t* const* block_order, int pace, uint16_t* const* payload, uint32_t* const* flags,
                        hipStream_t stream);
