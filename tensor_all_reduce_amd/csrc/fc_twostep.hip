@@ -8,6 +8,8 @@
 // instruction, and a quantization group spans G/8 (or G/16) aligned lanes whose min/max are combined
 // with DPP.  Intermediate fp32 values stay in registers; RMSNorm row sums use DPP inside a wavefront and
 // LDS across wavefronts.  Nothing here is a contraction, so matrix cores are not used.
+#include <type_traits>
+
 #include "fc_device.h"
 #include "fc_launch.h"
 
@@ -845,6 +847,202 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t s) {
     return hipSuccess;
 }
 
+// =====================================================================================================
+// Reduce-scatter receive side fused with the residual-add + RMSNorm, the normalized row quantized into
+// the shard's all-gather message (the norm applied before the all-gather, TokenWeave, abstract).  One
+// workgroup per row, one 16-element slot per lane (lane t owns elements [16t, 16t + 16) of the row):
+// each rank's codes arrive in one 16-byte (8-bit) or 8-byte (4-bit) load and one scale/zero word, and
+// the residual in two 16-byte loads.  The row's sum of squares takes the order fixed for quantized-output
+// rows: 8-element chunk partials (left fold of h*h), then a pairwise tree over the chunk index c = 2t + j,
+// i.e. the lane's two chunks, the lanes of the wavefront (DPP butterfly), then the wavefronts.  Rows of
+// more than 1024 slots go through k_rows instead.
+// =====================================================================================================
+struct QNormTabs {
+    // [shard in launch][rank]: entries past R repeat rank R-1
+    const uint8_t* codes[kNormShards][kMaxRanks];
+    const uint32_t* meta[kNormShards][kMaxRanks];
+    uint8_t* out_codes[kNormShards];
+    uint32_t* out_meta[kNormShards];
+};
+constexpr int kQNormMaxSlots = 1024;  // 16-element slots per row (H <= 16384)
+
+// a1 = log2(group) | R << 8; L = shard length (a multiple of H); grid = rows, rows * H < 2^31.  One
+// workgroup per row and no loop: loading the next row ahead into a second set of registers costs more
+// occupancy than it hides, and a loop would let the compiler hoist gamma's unpacking (and the wait for
+// it) in front of the first row's loads.
+template <int B1, int B2, int BT, bool R8>
+__global__ __launch_bounds__(BT) void k_reduce_norm(const int H, const float eps,
+                                                    const uint16_t* __restrict__ gamma,
+                                                    const uint16_t* residual, uint16_t* residual_out,
+                                                    const uint32_t L, const int a1, const QNormTabs tb) {
+    constexpr int E = 16;
+    constexpr int IN_W = E * B1 / 32;  // code words per rank
+    constexpr int RB = 8;              // ranks per batch of loads
+    constexpr int NW = BT / 64;
+    const int R = R8 ? 8 : (a1 >> 8);
+    __builtin_assume(R >= 1);
+    const int log2g = a1 & 0xff;
+    const int nl = H / E;
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const bool ok = t < nl;
+    const uint32_t e0 = (uint32_t)(ok ? t : nl - 1) * E;  // the slot's first element in the row
+    __shared__ float s_part[NW];
+    struct Where {
+        uint32_t rbase, sh, off;  // row start, shard in the launch, element offset inside the shard
+    };
+    Where cw;
+    cw.rbase = (uint32_t)blockIdx.x * (uint32_t)H;
+    cw.sh = cw.rbase / L;
+    cw.off = cw.rbase - cw.sh * L + e0;
+    struct Batch {
+        uint32_t wv[RB][IN_W];
+        uint32_t mv[RB];
+    };
+    // byte offsets without a product that would pass 2^32 (off < 2^31)
+    auto load_batch = [&](const Where& w, int r0, Batch& b) {
+        const uint32_t coff = B1 == 8 ? w.off : w.off >> 1, moff = (w.off >> log2g) * 4u;
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+            load_codes<E, B1>(tb.codes[w.sh][r0 + j] + coff, b.wv[j]);
+            b.mv[j] = lds4(reinterpret_cast<const uint8_t*>(tb.meta[w.sh][r0 + j]) + moff);
+        }
+    };
+    auto load_residual = [&](const Where& w, uint4 (&rv)[2]) {
+        if (residual) {
+            rv[0] = lds16(residual + w.rbase + e0);
+            rv[1] = lds16(residual + w.rbase + e0 + 8);
+        }
+    };
+    float h[E];
+    auto fold_batch = [&](const Batch& b, int r0) {
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+            if (r0 + j < R) {  // uniform
+                float d[E];
+#pragma unroll
+                for (int w = 0; w < IN_W; ++w)
+                    Unpack<B1>::run(b.wv[j][w], meta_scale(b.mv[j]), meta_zero(b.mv[j]), d + w * Unpack<B1>::PER_WORD);
+                if (r0 + j == 0) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) h[e] = d[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) h[e] = h[e] + d[e];
+                }
+            }
+        }
+    };
+    {
+        Batch cb;
+        uint4 cr[2] = {};
+        load_batch(cw, 0, cb);
+        load_residual(cw, cr);
+        const uint4 g0 = ld16(gamma + e0), g1 = ld16(gamma + e0 + 8);  // gamma: shared by every row, an L2 hit
+        fold_batch(cb, 0);
+        for (int r0 = RB; r0 < R; r0 += RB) {  // more than 8 ranks
+            Batch more;
+            load_batch(cw, r0, more);
+            fold_batch(more, r0);
+        }
+        if (residual) {
+            float rv[8];
+            unpack_bf16x8(cr[0], rv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = h[e] + rv[e];
+            unpack_bf16x8(cr[1], rv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[8 + e] = h[8 + e] + rv[e];
+        }
+        if (residual_out && ok) {
+            float a[8], b[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                a[e] = h[e];
+                b[e] = h[8 + e];
+            }
+            sts16(residual_out + cw.rbase + e0, pack_bf16x8(a));
+            sts16(residual_out + cw.rbase + e0 + 8, pack_bf16x8(b));
+        }
+        float p[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            float q = h[8 * c] * h[8 * c];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) {
+                const float sq = h[8 * c + e] * h[8 * c + e];
+                q = q + sq;
+            }
+            p[c] = q;
+        }
+        float tot = wave_sum(ok ? p[0] + p[1] : 0.0f);
+        if constexpr (NW > 1) {
+            if (lane == 0) s_part[wid] = tot;
+            __syncthreads();
+            float a[NW];
+#pragma unroll
+            for (int w = 0; w < NW; ++w) a[w] = s_part[w];
+#pragma unroll
+            for (int width = NW; width > 1; width /= 2)
+#pragma unroll
+                for (int j = 0; j < width / 2; ++j) a[j] = a[2 * j] + a[2 * j + 1];
+            tot = a[0];
+        }
+        const float ms = tot / (float)H;
+        const float rinv = 1.0f / sqrtf(ms + eps);
+        float gk[E];
+        {
+            float gv[8];
+            unpack_bf16x8(g0, gv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gk[e] = gv[e];
+            unpack_bf16x8(g1, gv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gk[8 + e] = gv[e];
+        }
+        float o[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float a = h[e] * rinv;
+            o[e] = a * gk[e];
+        }
+        auto quantize_store = [&](auto lpg) {
+            constexpr int LPG = decltype(lpg)::value;
+            uint32_t w[E * B2 / 32];
+            uint32_t m;
+            quantize_lane<B2, E, LPG>(o, w, m);  // every lane: the group reduction needs them all
+            if (ok) {
+                store_codes<E, B2>(tb.out_codes[cw.sh] + (B2 == 8 ? cw.off : cw.off >> 1), w);
+                if ((t & (LPG - 1)) == 0) tb.out_meta[cw.sh][cw.off >> log2g] = m;
+            }
+        };
+        switch (log2g) {  // uniform; a group spans G/16 lanes
+            case 5: quantize_store(std::integral_constant<int, 2>{}); break;
+            case 6: quantize_store(std::integral_constant<int, 4>{}); break;
+            case 7: quantize_store(std::integral_constant<int, 8>{}); break;
+            default: quantize_store(std::integral_constant<int, 16>{}); break;
+        }
+    }
+}
+
+template <int B1, int B2, bool R8>
+static void reduce_norm_shape(int bt, int rows, const NormKArgs& na, uint32_t L, int a1, const QNormTabs& tb,
+                              hipStream_t s) {
+#define FC_QN(BT)                                                                                      \
+    case BT:                                                                                           \
+        if constexpr (BT < 1024 || R8)                                                                 \
+            k_reduce_norm<B1, B2, BT, R8><<<rows, BT, 0, s>>>(na.hidden, na.eps, na.gamma, na.residual, \
+                                                              na.residual_out, L, a1, tb);             \
+        break;
+    switch (bt) {
+        FC_QN(64)
+        FC_QN(128)
+        FC_QN(256)
+        FC_QN(512)
+        FC_QN(1024)
+    }
+#undef FC_QN
+}
+
 template <int B1, int B2>
 static hipError_t reduce_norm_bits(const ReduceNormQParams& q, hipStream_t s) {
     const ReduceParams& p = q.rs;
@@ -871,7 +1069,28 @@ static hipError_t reduce_norm_bits(const ReduceNormQParams& q, hipStream_t s) {
         if (na.residual_out) na.residual_out += off;
         na.out = nullptr;
         const int64_t rows = (int64_t)ns * p.L / H;
-        const hipError_t e = launch_rows(prod, (uint32_t)p.L, ilog2(p.group) | (p.R << 8), na, rows, (int)rows, s);
+        const int a1 = ilog2(p.group) | (p.R << 8);
+        hipError_t e;
+        // one 16-element slot per lane; rows of more than 512 slots from other than 8 ranks take the
+        // chunk-per-lane kernel (beside 1024 lanes, a second batch of rank loads does not fit in registers)
+        if (H / 16 <= 512 || (H / 16 <= kQNormMaxSlots && p.R == 8)) {
+            QNormTabs tb;
+            for (int i = 0; i < kNormShards; ++i) {
+                for (int r = 0; r < kMaxRanks; ++r) {
+                    tb.codes[i][r] = prod.codes[i][r];
+                    tb.meta[i][r] = prod.meta[i][r];
+                }
+                tb.out_codes[i] = prod.out_codes[i];
+                tb.out_meta[i] = prod.out_meta[i];
+            }
+            int bt = 64;  // one 16-element slot per lane
+            while (bt * 16 < H) bt *= 2;
+            if (p.R == 8) reduce_norm_shape<B1, B2, true>(bt, (int)rows, na, (uint32_t)p.L, a1, tb, s);
+            else reduce_norm_shape<B1, B2, false>(bt, (int)rows, na, (uint32_t)p.L, a1, tb, s);
+            e = hipGetLastError();
+        } else {
+            e = launch_rows(prod, (uint32_t)p.L, a1, na, rows, (int)rows, s);
+        }
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

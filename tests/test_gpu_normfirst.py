@@ -63,6 +63,21 @@ def test_reduce_norm_shapes(fc, orc, R, n_shards, rows, H):
     _run_shards(orc, R, n_shards, rows, H, 8, 8, 128, seed=R * 7 + rows + H)
 
 
+# 16-element slots per lane: a row of 6 slots (lanes past it hold a clamped copy and store nothing, whole
+# 2-lane groups of them), 1022 slots (an unaligned wavefront tail; from 2 ranks, the chunk-per-lane
+# kernel), 1024 slots (the largest one-slot row), and 1026 slots (past it: the chunk-per-lane kernel)
+@pytest.mark.parametrize("R,rows,H", [(3, 5, 96), (8, 1, 16352), (2, 1, 16352), (8, 2, 16384), (2, 1, 16416)])
+def test_reduce_norm_slot_edges(fc, orc, R, rows, H):
+    _run_shards(orc, R, 2, rows, H, 8, 4, 32, seed=R * 5 + H)
+
+
+# more rows than the grid holds workgroups (64 lanes: 8192), so that workgroups take several rows and load
+# the next one ahead; 16 ranks add a second batch of rank loads inside that loop
+@pytest.mark.parametrize("R,rows,H,b1", [(3, 4500, 96, 8), (16, 4200, 256, 4)])
+def test_reduce_norm_rows_ahead(fc, orc, R, rows, H, b1):
+    _run_shards(orc, R, 2, rows, H, b1, 8, 32, seed=R + rows)
+
+
 def test_reduce_norm_without_residual(fc, orc):
     _run_shards(orc, 4, 2, 2, 4096, 8, 8, 128, with_residual=False, seed=11)
 
