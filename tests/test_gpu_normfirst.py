@@ -71,10 +71,9 @@ def test_reduce_norm_slot_edges(fc, orc, R, rows, H):
     _run_shards(orc, R, 2, rows, H, 8, 4, 32, seed=R * 5 + H)
 
 
-# more rows than the grid holds workgroups (64 lanes: 8192), so that workgroups take several rows and load
-# the next one ahead; 16 ranks add a second batch of rank loads inside that loop
+# many short rows (over 8000 one-row workgroups of 64 lanes); 16 ranks add a second batch of rank loads
 @pytest.mark.parametrize("R,rows,H,b1", [(3, 4500, 96, 8), (16, 4200, 256, 4)])
-def test_reduce_norm_rows_ahead(fc, orc, R, rows, H, b1):
+def test_reduce_norm_many_rows(fc, orc, R, rows, H, b1):
     _run_shards(orc, R, 2, rows, H, b1, 8, 32, seed=R + rows)
 
 
