@@ -187,8 +187,9 @@ def pmc_rows(out_json):
     """Single-workload launches of the row kernels, for counter runs (one counter per run): the 1 GiB copy
     (the counters' scale reference), then per kernel a few launches over 3 rotating buffer sets (together
     larger than the L2s): the slot receiver's first pass on the slot workload, half A of the TokenWeave
-    reduce + RMSNorm, the all-gather of the int8 prefill messages (first pass), and the two f2 receivers
-    (flag words per 2048 elements, polling slot receiver) on 8 x 2 MiB with every block there.  Writes the
+    reduce + RMSNorm, the all-gather of the int8 prefill messages (first pass), the two f2 receivers
+    (flag words per 2048 elements, polling slot receiver) on 8 x 2 MiB with every block there, and the
+    reduce with the norm first on every shard of the 70B prefill.  Writes the
     algorithmic bytes of one launch of each kernel to `out_json`."""
     import numpy as np
     import torch
@@ -291,6 +292,25 @@ def pmc_rows(out_json):
     torch.cuda.synchronize()
     algo["k_flag_unpack"] = bm.flag_unpack(8, n2, be)
     algo["k_ll_poll"] = bm.ll_unpack(8, n2, 64)
+    del fsets, lsets, out2, st2, dn2, c2
+    # the reduce with the norm first, every shard of the 70B prefill (int4 messages in, int8 rows out); the
+    # counters do not depend on the values: random codes, scale 1/16 and zero 0 in every group
+    R3, L3, G3, b13, b23 = c3.R, c3.L, c3.group, c3.bits_rs, c3.bits_ag
+    qsets = []
+    for k in range(3):
+        ins = [(torch.randint(0, 256, (L3 * b13 // 8,), dtype=torch.uint8, device=dev, generator=gen),
+                torch.full((L3 // G3,), 0x2C00, dtype=torch.int32, device=dev)) for _ in range(R3 * R3)]
+        outs = [(torch.empty(L3 * b23 // 8, dtype=torch.uint8, device=dev),
+                 torch.empty(L3 // G3, dtype=torch.int32, device=dev)) for _ in range(R3)]
+        res3 = torch.randn(R3 * L3, device=dev, generator=gen).to(torch.bfloat16).view(torch.int16)
+        qsets.append((ins, outs, res3, torch.empty_like(res3)))
+    gam3 = up(dg.gamma(c3))
+    for k in range(6):
+        ins, outs, res3, rout3 = qsets[k % 3]
+        _lib.fc_reduce_shard_norm(ins, R3, L3, b13, b23, G3,
+                                  dict(residual=res3, gamma=gam3, eps=c3.eps, hidden=c3.H, residual_out=rout3), outs)
+    torch.cuda.synchronize()
+    algo["k_reduce_norm"] = bm.reduce_norm(R3, L3, b13, b23, G3, R3, c3.H)
     with open(out_json, "w") as f:
         json.dump(algo, f, indent=1)
     print(json.dumps(algo))
@@ -325,7 +345,8 @@ def rows_pmc_report(stats_csv, fetch_csv, write_csv, bytes_json, out_md):
              "| GB/s at avg (algorithmic) |", "|---|---|---|---|---|---|---|---|"]
     what = {"k_ll_unpack": "slot workload, first pass (2% late)", "BF16ReduceProducer": "TokenWeave half A, 4096 rows",
             "k_ll_gather": "int8 prefill messages, first pass", "k_flag_unpack": "8 x 2 MiB, flag per 2048, all there",
-            "k_ll_poll": "8 x 2 MiB slots, all there, no re-read"}
+            "k_ll_poll": "8 x 2 MiB slots, all there, no re-read",
+            "k_reduce_norm": "norm first, 70B prefill, all 8 shards (int4 in, int8 out)"}
     for key, a in algo.items():
         name = next((k for k in f if key in k), None)
         if name is None:

@@ -13,18 +13,23 @@ Encodings built here:
 Model (the plainest reading of the trade the selector makes): the latency of one transfer of S payload
 bytes from each of R ranks is the larger of a synchronization floor and a transfer time,
 
-    t(enc, S, R) = max(a + b * R,  d + c * R * wire(enc, S))
+    t(enc, S, R) = max(a + b * R,  d + (c * R + e) * wire(enc, S))
 
 where wire() is the bytes one rank sends.  a + b R is what the encoding costs however small the message
-(launch, readiness checks, for a flag the dependent flag-then-payload read); d + c R wire is the time
-to move its bytes, c also carrying a flag encoding's per-block fence (a block is a fixed number of bytes,
-so blocks and bytes cannot be told apart within one encoding).  The four non-negative coefficients are
-fitted per encoding to latencies measured with a sender and a receiver running at the same time,
-minimising the relative error.  ``select`` returns the encoding with the lowest predicted latency (ties:
-the listed order).  Host logic only.
+(launch, readiness checks, for a flag the dependent flag-then-payload read).  The transfer time has a
+term for the bytes all R ranks move through the shared memory system (c R wire) and one for the bytes of
+a single rank (e wire): each rank's message is written and checked in order of its own blocks and spans
+whatever R is, which is why a flag encoding's latency grows with the message far more than with R.  c
+and e also carry a flag encoding's per-block fence (a block is a fixed number of bytes, so blocks and
+bytes cannot be told apart within one encoding).  The five non-negative coefficients are fitted per
+encoding to latencies measured with a sender and a receiver running at the same time, minimising the
+relative error.  ``select`` returns the encoding with the lowest predicted latency (ties: the listed
+order).  Host logic only; ``python -m tensor_all_reduce_amd.selector --refit FILE`` refits a table's
+coefficients from the latencies it stores.
 """
 from __future__ import annotations
 
+import argparse
 import json
 import math
 import os
@@ -59,11 +64,11 @@ def blocks(enc: str, S: int) -> int:
 @dataclass(frozen=True)
 class EncodingCost:
     enc: str
-    coef: tuple  # (a us, b us per rank, c us per wire byte, d us)
+    coef: tuple  # (a us, b us per rank, c us per wire byte and rank, d us, e us per wire byte)
 
     def predict(self, S: int, R: int) -> float:
-        a, b, c, d = self.coef
-        return max(a + b * R, d + c * R * wire_bytes(self.enc, S))
+        a, b, c, d, e = self.coef
+        return max(a + b * R, d + (c * R + e) * wire_bytes(self.enc, S))
 
 
 def fit(rows) -> dict[str, EncodingCost]:
@@ -74,19 +79,21 @@ def fit(rows) -> dict[str, EncodingCost]:
     from scipy.optimize import least_squares
     by = {}
     for enc, S, R, t in rows:
-        by.setdefault(enc, []).append((float(R), float(R * wire_bytes(enc, S)), float(t)))
+        by.setdefault(enc, []).append((float(R), float(wire_bytes(enc, S)), float(t)))
     out = {}
     for enc, pts in by.items():
         R = np.array([p[0] for p in pts])
-        x = np.array([p[1] for p in pts])
+        w = np.array([p[1] for p in pts])
         t = np.array([p[2] for p in pts])
-        scale = np.array([t.min(), t.min(), t.max() / x.max(), t.min()])  # unit steps of comparable size
+        # unit steps of comparable size for the five coefficients
+        scale = np.array([t.min(), t.min(), t.max() / (R * w).max(), t.min(), t.max() / w.max()])
 
         def resid(q):
-            a, b, c, d = q * scale
-            return np.maximum(a + b * R, d + c * x) / t - 1.0
+            a, b, c, d, e = q * scale
+            return np.maximum(a + b * R, d + (c * R + e) * w) / t - 1.0
         best = None
-        for x0 in ((1.0, 0.1, 1.0, 0.1), (0.5, 0.05, 0.5, 0.5), (1.0, 0.0, 2.0, 0.0), (0.8, 0.2, 1.0, 1.0)):
+        for x0 in ((1.0, 0.1, 1.0, 0.1, 0.1), (0.5, 0.05, 0.5, 0.5, 0.5), (1.0, 0.0, 2.0, 0.0, 0.0),
+                   (0.8, 0.2, 1.0, 1.0, 1.0), (1.0, 0.1, 0.1, 0.1, 2.0)):
             r = least_squares(resid, x0=np.array(x0), bounds=(0.0, np.inf))
             if best is None or r.cost < best.cost:
                 best = r
@@ -115,8 +122,11 @@ def crossover(costs: dict[str, EncodingCost], R: int, lo: int = 1 << 10, hi: int
     return out
 
 
+MODEL = "t_us = max(a + b*R, d + (c*R + e)*wire_bytes); coefficients [a, b, c, d, e]"
+
+
 def save(path: str, costs: dict[str, EncodingCost], measured, command: str, machine: str) -> None:
-    doc = {"model": "t_us = max(a + b*R, d + c*R*wire_bytes)", "command": command, "machine": machine,
+    doc = {"model": MODEL, "command": command, "machine": machine,
            "coefficients": {e: list(c.coef) for e, c in costs.items()},
            "measured": [list(r) for r in measured]}
     with open(path, "w") as f:
@@ -125,6 +135,35 @@ def save(path: str, costs: dict[str, EncodingCost], measured, command: str, mach
 
 
 def load(path: str = DEFAULT_TABLE) -> dict[str, EncodingCost]:
+    """A table's coefficients.  A table of the earlier four-coefficient model (no per-rank term) reads
+    with e = 0."""
     with open(path) as f:
         doc = json.load(f)
-    return {e: EncodingCost(e, tuple(c)) for e, c in doc["coefficients"].items()}
+    out = {}
+    for e, c in doc["coefficients"].items():
+        c = tuple(float(v) for v in c)
+        if len(c) == 4:
+            c = c + (0.0,)
+        if len(c) != 5:
+            raise ValueError(f"{path}: {e} has {len(c)} coefficients")
+        out[e] = EncodingCost(e, c)
+    return out
+
+
+def refit(path: str) -> dict[str, EncodingCost]:
+    """Refit a table's coefficients from the latencies it stores and rewrite it (its measurement command
+    and machine kept)."""
+    with open(path) as f:
+        doc = json.load(f)
+    rows = [tuple(r) for r in doc["measured"]]
+    costs = fit(rows)
+    save(path, costs, rows, doc["command"], doc["machine"])
+    return costs
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--refit", metavar="FILE", required=True, help="table to refit from its stored latencies")
+    args = ap.parse_args()
+    for enc, c in refit(args.refit).items():
+        print(enc, ["%.6g" % v for v in c.coef])
