@@ -204,26 +204,24 @@ struct Unpack<8> {
 template <>
 struct Unpack<4> {
     static constexpr int PER_WORD = 8;
-    // Codes as fp16 subnormals: the half-word q (a code, 0..15) is the fp16 value q * 2^-24, and the mixed-
-    // precision fma converts it exactly, so fma(q * 2^-24, s * 2^24, z) = fl(q*s + z) with no int-to-float
-    // conversion.  s * 2^24 is exact.  Byte permutes put each code alone in a half-word.  This relies on
-    // fp16 subnormals being kept (the kernels' floating-point mode flushes no fp16 or fp32 subnormals).
+    // Codes as fp16 subnormals: a half-word holding a code q (0..15) in bits 0..3 is the fp16 value
+    // q * 2^-24, and in bits 4..7 the value q * 2^-20.  The mixed-precision fma converts either exactly, so
+    // fma(q * 2^-24, s * 2^24, z) = fma(q * 2^-20, s * 2^20, z) = fl(q*s + z), with no int-to-float
+    // conversion (s * 2^24 and s * 2^20 are exact).  Masks that keep one nibble per half-word isolate the
+    // codes in pairs: w & 0x000f000f holds codes 0 and 4, w & 0x00f000f0 codes 1 and 5 (4 bits up), and
+    // the same masks on w >> 8 codes 2, 6 and 3, 7.  This relies on fp16 subnormals being kept (the
+    // kernels' floating-point mode flushes no fp16 or fp32 subnormals).
     __device__ __forceinline__ static void run(uint32_t w, float s, float z, float* out) {
-        const float s24 = s * 16777216.0f;
-        uint32_t ev = w & 0x0f0f0f0fu;         // byte k = code 2k
-        uint32_t od = (w >> 4) & 0x0f0f0f0fu;  // byte k = code 2k+1
-        const uint32_t h[4] = {__builtin_amdgcn_perm(0u, ev, 0x0c010c00u), __builtin_amdgcn_perm(0u, ev, 0x0c030c02u),
-                               __builtin_amdgcn_perm(0u, od, 0x0c010c00u), __builtin_amdgcn_perm(0u, od, 0x0c030c02u)};
+        const float s24 = s * 16777216.0f, s20 = s * 1048576.0f;
+        const uint32_t w8 = w >> 8;
+        const uint32_t p[4] = {w & 0x000f000fu, w & 0x00f000f0u, w8 & 0x000f000fu, w8 & 0x00f000f0u};
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const _Float16 a0 = __builtin_bit_cast(_Float16, (uint16_t)(h[k] & 0xffffu));
-            const _Float16 a1 = __builtin_bit_cast(_Float16, (uint16_t)(h[k] >> 16));
-            const _Float16 b0 = __builtin_bit_cast(_Float16, (uint16_t)(h[k + 2] & 0xffffu));
-            const _Float16 b1 = __builtin_bit_cast(_Float16, (uint16_t)(h[k + 2] >> 16));
-            out[4 * k + 0] = __builtin_fmaf((float)a0, s24, z);  // code 4k
-            out[4 * k + 1] = __builtin_fmaf((float)b0, s24, z);  // code 4k+1
-            out[4 * k + 2] = __builtin_fmaf((float)a1, s24, z);  // code 4k+2
-            out[4 * k + 3] = __builtin_fmaf((float)b1, s24, z);  // code 4k+3
+        for (int k = 0; k < 4; ++k) {  // p[k]: code k in the low half-word, code k + 4 in the high one
+            const float sk = (k & 1) ? s20 : s24;
+            const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(p[k] & 0xffffu));
+            const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(p[k] >> 16));
+            out[k] = __builtin_fmaf((float)lo, sk, z);
+            out[k + 4] = __builtin_fmaf((float)hi, sk, z);
         }
     }
 };

@@ -243,9 +243,13 @@ __global__ __launch_bounds__(256) void k_reduce(const int64_t nchunks, const int
         }
     };
     load_batch(0);
+    // Every load of the batch is issued before the first fold: left to itself, the scheduler moves some
+    // ranks' loads behind the first ranks' folds, and those ranks arrive a memory round trip late.
+    __builtin_amdgcn_sched_barrier(0);
     fold_batch(0);
     for (int r0 = RB; r0 < R; r0 += RB) {  // more than 8 ranks
         load_batch(r0);
+        __builtin_amdgcn_sched_barrier(0);
         fold_batch(r0);
     }
     uint32_t w[E * B2 / 32];
@@ -960,8 +964,11 @@ __global__ __launch_bounds__(BT) void k_reduce_norm(const int H, const float eps
                 a[e] = h[e];
                 b[e] = h[8 + e];
             }
-            sts16(residual_out + cw.rbase + e0, pack_bf16x8(a));
-            sts16(residual_out + cw.rbase + e0 + 8, pack_bf16x8(b));
+            // Write-back stores, not streamed: each of the two instructions fills every other 16 bytes of
+            // the wavefront's span, and streamed halves left L2 before their other halves arrived (1.33x
+            // the written bytes); in L2 the halves merge into whole lines.
+            *reinterpret_cast<uint4*>(residual_out + cw.rbase + e0) = pack_bf16x8(a);
+            *reinterpret_cast<uint4*>(residual_out + cw.rbase + e0 + 8) = pack_bf16x8(b);
         }
         float p[2];
 #pragma unroll
