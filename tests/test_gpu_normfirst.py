@@ -49,7 +49,7 @@ def _run_shards(orc, R, n_shards, rows, H, b1, b2, G, with_residual=True, seed=0
 
 
 @pytest.mark.parametrize("b1,b2", [(8, 8), (4, 8), (8, 4), (4, 4)])
-@pytest.mark.parametrize("G", [32, 128, 256])
+@pytest.mark.parametrize("G", [32, 64, 128, 256])
 def test_reduce_norm_bits_groups(fc, orc, b1, b2, G):
     _run_shards(orc, 8, 2, 3, 4096, b1, b2, G, seed=b1 * 100 + b2 * 10 + G)
 

@@ -24,7 +24,7 @@ def _qmsgs_on_gpu(msgs):
 
 
 @pytest.mark.parametrize("b1,b2", [(8, 8), (4, 8), (8, 4), (4, 4)])
-@pytest.mark.parametrize("group", [32, 128, 256])
+@pytest.mark.parametrize("group", [32, 64, 128, 256])
 @pytest.mark.parametrize("R,n_shards", [(1, 1), (2, 2), (3, 1), (8, 8), (8, 1), (16, 16)])
 def test_reduce_shard_parity(fc, orc, b1, b2, group, R, n_shards):
     import torch
@@ -65,18 +65,21 @@ def _shard_msgs(orc, R, L, bits, group, seed, sigma=6.0):
     return [orc.quantize(dg.synth_f32((seed, s), L, sigma), bits, group) for s in range(R)]
 
 
+# (R, T, H) shapes, each with every group that splits its shards into whole groups
+_GATHER_SHAPES = [(2, 4, 256), (8, 64, 4096), (8, 3, 4096), (4, 16, 8192), (3, 6, 2048), (8, 1, 4096), (1, 5, 12288),
+                  (16, 2, 1024), (5, 8, 1000), (2, 2, 65536)]
+_GATHER_CASES = [(G, R, T, H) for R, T, H in _GATHER_SHAPES for G in (32, 64, 128, 256)
+                 if (T * H) % R == 0 and (T * H // R) % G == 0]
+
+
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("group", [32, 128])
-@pytest.mark.parametrize("R,T,H", [(2, 4, 256), (8, 64, 4096), (8, 3, 4096), (4, 16, 8192), (3, 6, 2048),
-                                   (8, 1, 4096), (1, 5, 12288), (16, 2, 1024), (5, 8, 1000), (2, 2, 65536)])
+@pytest.mark.parametrize("group,R,T,H", _GATHER_CASES)
 def test_gather_parity(fc, orc, bits, group, R, T, H):
     """Plain dequantize and the fused residual-add + RMSNorm epilogue; includes rows that straddle shards
     (T*H/R not a multiple of H, e.g. one decode token) and row lengths needing 1..4 chunks per lane."""
     import torch
     from gpu_helpers import assert_bf16_close, assert_equal_bits, down, up
     n = T * H
-    if n % R or (n // R) % group:
-        pytest.skip("shape does not split into whole groups")
     L = n // R
     shards = _shard_msgs(orc, R, L, bits, group, seed=(R, T, H, bits))
     dsh = _qmsgs_on_gpu(shards)
