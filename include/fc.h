@@ -122,7 +122,13 @@ fc_status fc_gather_dequant(const fc_qmsg* shards, int R, int64_t L, int bits, i
 fc_status fc_reduce_rmsnorm(const uint16_t* const* parts, int R, int64_t rows, const fc_norm* norm,
                             int max_workgroups, hipStream_t stream);
 
-/* Self-synchronizing receive side (flash-comm, abstract).  slots [host array, R entries]: uint64 [n/2]
+/* Epochs (every call below that takes one): the readiness evidence is a comparison with `epoch` and
+ * nothing else, so a buffer must not already hold the epoch of a message it has not yet received: a
+ * caller uses a new epoch for each message through the same buffers, never one that an earlier message
+ * or the buffers' initial contents carry (zero-filled buffers: start at 1).  The library cannot tell a
+ * reused epoch from a delivered message.
+ *
+ * Self-synchronizing receive side (flash-comm, abstract).  slots [host array, R entries]: uint64 [n/2]
  * per rank; slot k = bf16 element 2k (bits 0..15), element 2k+1 (bits 16..31), epoch word (bits
  * 32..63).  A block is `block_slots` consecutive slots; nblk = n/2/block_slots.  For each block b with
  * done[b] == 0: stale[r*nblk + b] = 1 if any slot of rank r's copy carries an epoch word != epoch, else

@@ -229,7 +229,8 @@ class SelfSyncReduce:
     send(): emulates the R senders in one launch (the peers' writes, on one GPU);
     begin(): clears done flags and counters for a new epoch; receive(): folds every block whose R copies
     carry the epoch, in ascending rank order, into out (bf16 [n]); with max_polls > 0 the receiver waits
-    (bounded) for late blocks, so it may run while the senders still write."""
+    (bounded) for late blocks, so it may run while the senders still write.  The inbox starts zero-filled,
+    so epochs start at 1 and each message takes a new one (epoch 0 is refused)."""
 
     def __init__(self, R: int, n: int, encoding: str = "auto", costs=None, device="cuda"):
         from . import selector as sel
@@ -266,7 +267,13 @@ class SelfSyncReduce:
             self.done.zero_()
             self.counters.zero_()
 
+    @staticmethod
+    def _check_epoch(epoch: int) -> None:
+        if not 0 < epoch < (1 << 32):
+            raise ValueError(f"epoch {epoch}: the zero-filled inbox already carries 0; use 1 .. 2^32-1")
+
     def send(self, xs, epoch: int, block_order=None, pace: int = 0, stream=None):
+        self._check_epoch(epoch)
         if self.encoding == "ll":
             _lib.fc_ll_pack(list(xs), self.B, epoch, self.slots, block_order=block_order, pace=pace, stream=stream)
         else:
@@ -274,6 +281,7 @@ class SelfSyncReduce:
                               stream=stream)
 
     def receive(self, epoch: int, max_polls: int = 0, max_workgroups: int = 0, stream=None):
+        self._check_epoch(epoch)
         if self.encoding == "ll":
             _lib.fc_ll_poll_unpack_reduce(self.slots, self.n, self.B, epoch, self.out, self.stale, self.done,
                                           self.counters, max_polls=max_polls, max_workgroups=max_workgroups,

@@ -125,3 +125,14 @@ def test_committed_choice_on_the_slot_workload():
     costs = sel.load()
     assert sel.select(costs, 2 << 20, 8).startswith("flag")
     assert sel.select(costs, 16 << 10, 2) == "ll"
+
+
+def test_self_sync_reduce_refuses_epochs_its_inbox_already_carries():
+    """The inbox starts zero-filled, so epoch 0 would pass every readiness check before anything was sent;
+    the receive side refuses it (and anything that is not a 32-bit epoch word)."""
+    from tensor_all_reduce_amd.flash_allreduce import SelfSyncReduce
+    for bad in (0, -1, 1 << 32):
+        with pytest.raises(ValueError):
+            SelfSyncReduce._check_epoch(bad)
+    SelfSyncReduce._check_epoch(1)
+    SelfSyncReduce._check_epoch((1 << 32) - 1)
