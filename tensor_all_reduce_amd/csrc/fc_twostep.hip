@@ -6,7 +6,8 @@
 // at base + i * width (16 bytes of bf16, 16, 8 or 4 bytes of codes), so each instruction
 // moves whole cache lines.  A lane therefore holds 8 consecutive bf16 elements (or 16 codes) per
 // instruction, and a quantization group spans G/8 (or G/16) aligned lanes whose min/max are combined
-// with DPP.  Intermediate fp32 values stay in registers; RMSNorm row sums use DPP inside a wavefront and
+// with DPP.  One exception: the norm-before-gather reduce gives a lane 16 consecutive elements, so its
+// codes stay contiguous per instruction and its residual takes two 16-byte accesses 32 bytes apart.  Intermediate fp32 values stay in registers; RMSNorm row sums use DPP inside a wavefront and
 // LDS across wavefronts.  Nothing here is a contraction, so matrix cores are not used.
 #include <type_traits>
 
