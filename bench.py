@@ -25,6 +25,7 @@ profiles/).
 import argparse
 import csv
 import hashlib
+import re
 import json
 import math
 import os
@@ -76,13 +77,32 @@ def parse():
     return ap.parse_args()
 
 
+def _code_text(text: str) -> str:
+    """Source text without comments, blank lines and trailing blanks: what a compiler sees of it."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    lines = []
+    for line in text.splitlines():
+        # the first // outside a string literal starts a comment
+        cut = line.find("//")
+        while cut >= 0 and line.count('"', 0, cut) % 2 == 1:
+            cut = line.find("//", cut + 2)
+        if cut >= 0:
+            line = line[:cut]
+        line = line.rstrip()
+        if line.strip():
+            lines.append(line)
+    return "\n".join(lines)
+
+
 def sources_sha(files=None) -> str:
-    """Hash of kernel sources (default: those of the two-step kernels), recorded with counter summaries."""
+    """Hash of kernel sources (default: those of the two-step kernels) with their comments stripped,
+    recorded with counter summaries: counters taken before a change to the code stop being reported, a
+    change to a comment keeps them."""
     h = hashlib.sha256()
     for f in files or KERNEL_SOURCES:
         path = f if "/" in f else os.path.join(ROOT, "tensor_all_reduce_amd", "csrc", f)
-        with open(path if os.path.isabs(path) else os.path.join(ROOT, path), "rb") as fh:
-            h.update(fh.read())
+        with open(path if os.path.isabs(path) else os.path.join(ROOT, path), encoding="utf-8") as fh:
+            h.update(_code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
