@@ -136,3 +136,36 @@ def test_quantized_all_gather_in_slots_end_to_end(fc, orc):
                                                     out=o, residual_out=rout))
     assert_bf16_close(down(rout, np.uint16), ref["residual_out"], 0, "residual_out")
     assert_bf16_close(down(o, np.uint16), ref["out"], 2, "out")
+
+
+def test_all_gather_prefill_messages_as_benched(fc, orc):
+    """The benchmark's f3 workload: the 8 int8 shard messages of the 70B prefill (codes then meta, 1,081,344
+    words each) carried in 64-slot blocks with about 2% of the copies late (every kind), pass 1 then the
+    retry with every block rewritten: out, stale, done and counters of both passes equal the oracle's."""
+    from gpu_helpers import assert_equal_bits, down
+    cfg = dg.CONFIGS[3]
+    R, B = cfg.R, 64
+    nwords = (cfg.L * cfg.bits_ag // 8 + 4 * (cfg.L // cfg.group)) // 4
+    assert nwords % B == 0
+    nblk = nwords // B
+    rng = np.random.default_rng(0xF3)
+    words = [rng.integers(0, 1 << 32, nwords, dtype=np.uint64).astype(np.uint32) for _ in range(R)]
+    ep = _late(R, nblk, B, nwords, 23, frac=0.02)
+    first = [_slots(words[r], ep[r]) for r in range(R)]
+    print(f"f3 prefill messages: R={R} nwords={nwords} B={B}", flush=True)
+    out, stale, done, cnt = _gpu_gather(fc, first, nwords, B)
+    ro, rst, rdn, rc = orc.ll_gather(first, nwords, B, E)
+    for r in range(R):
+        assert_equal_bits(down(out[r], np.uint32), ro[r], f"pass 1 words of rank {r}")
+    assert_equal_bits(down(stale, np.uint8), rst, "pass 1 stale")
+    assert_equal_bits(down(done, np.uint8), rdn, "pass 1 done")
+    assert_equal_bits(down(cnt, np.uint32), rc, "pass 1 counters")
+    assert int(rc[1]) > 0
+    again = [_slots(words[r], np.full(nwords, E)) for r in range(R)]
+    out, stale, done, cnt = _gpu_gather(fc, again, nwords, B, out=out, done=done)
+    ro2, rst2, rdn2, rc2 = orc.ll_gather(again, nwords, B, E, out=ro, done=rdn)
+    for r in range(R):
+        assert_equal_bits(down(out[r], np.uint32), ro2[r], f"retry words of rank {r}")
+    assert_equal_bits(down(done, np.uint8), rdn2, "retry done")
+    assert rdn2.all() and int(rc2[1]) == 0
+    assert_equal_bits(down(cnt, np.uint32), rc2, "retry counters")
