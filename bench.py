@@ -17,7 +17,7 @@ with late blocks, then the retry), and the unquantized reduce-RMSNorm on two wav
 alone and overlapped with a bf16 GEMM on a second stream, with a workgroup-cap sweep, and the two-half pipelined layer step (wave-aware split, each half's
 all-reduce overlapping the other half's GEMM).
 
-Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+Prints one JSON line.  --gpus N > 1 is refused: everything runs on one GPU.
 `python bench.py --pmc-summary FETCH_CSV WRITE_CSV OUT` turns two rocprofv3 --pmc runs into the traffic
 summary that later runs report, and `--profile-report` writes a workload's whole profile summary (see
 profiles/).
@@ -60,7 +60,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=600)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=2, help="headline two-step workload: 1, 2 or 3")
+    ap.add_argument("--config", default="llama3-8b-decode",
+                    choices=["tiny-r2-t4-h256", "llama3-8b-decode", "llama3-70b-prefill"],
+                    help="headline two-step workload")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-resident)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -72,7 +74,7 @@ def parse():
     ap.add_argument("--rows-pmc-report", nargs=5, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV", "BYTES_JSON", "OUT_MD"))
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"))
     ap.add_argument("--stats-table", nargs=4, metavar=("STATS_CSV", "OUT_MD", "TITLE", "COMMAND"))
-    ap.add_argument("--profile-report", nargs=6, metavar=("CONFIG", "STATS_CSV", "FETCH_CSV", "WRITE_CSV", "VALU_CSV",
+    ap.add_argument("--profile-report", nargs=6, metavar=("WORKLOAD", "STATS_CSV", "FETCH_CSV", "WRITE_CSV", "VALU_CSV",
                                                           "OUT_MD"))
     return ap.parse_args()
 
@@ -139,7 +141,7 @@ def profile_report(config, stats_csv, fetch_csv, write_csv, valu_csv, out_md):
     --pmc SQ_INSTS_VALU SQ_WAVES, each in a run of its own.  Also writes the traffic summary that later
     benchmark runs report (profiles/pmc_traffic_<slug>.txt)."""
     from tensor_all_reduce_amd import bytes_model as bm, datagen as dg
-    cfg = dg.CONFIGS[config]
+    cfg = dg.WORKLOADS[config]
     pmc_summary(fetch_csv, write_csv, traffic_file(cfg.slug))
     calls = bm.two_step_whole(cfg.R, cfg.T, cfg.H, cfg.bits_rs, cfg.bits_ag, cfg.group)
     keys = {call: kernel_of_call(call, cfg) for call in calls}
@@ -156,13 +158,14 @@ def profile_report(config, stats_csv, fetch_csv, write_csv, valu_csv, out_md):
             pmc.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
     med = {k: statistics.median(v) for k, v in pmc.items()}
     traffic = load_traffic(cfg)
-    runs = "" if config == 2 else f" --config {config} --steps 30 --warmup 5"
-    x = " --steps 290 --warmup 0 --kernel-reps 1" if config == 2 else f" --config {config} --steps 4 --warmup 1 --kernel-reps 1"
+    decode = cfg is dg.DECODE_8B  # the default workload
+    runs = "" if decode else f" --config {config} --steps 30 --warmup 5"
+    x = " --steps 290 --warmup 0 --kernel-reps 1" if decode else f" --config {config} --steps 4 --warmup 1 --kernel-reps 1"
     base = "python3 bench.py --no-cpu-baseline --rows none"
     lines = [f"# Two-step all-reduce kernels on the {cfg.name} workload", "",
              "Kernel durations from a rocprofv3 kernel trace of the benchmark (run from the repository root on one "
              "MI355X; the benchmark replays each call from HIP graphs over cold buffer sets):", "", "```",
-             f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/st{config} -o st{config} -- {base}{runs}",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/st_{config} -o st -- {base}{runs}",
              "```", "", "| kernel | calls | avg us | min us | max us | algorithmic bytes | GB/s at avg |",
              "|---|---|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
@@ -180,8 +183,8 @@ def profile_report(config, stats_csv, fetch_csv, write_csv, valu_csv, out_md):
               "counters read for the 1 GiB copy kernel, and vector-ALU instructions per wavefront and per byte "
               f"from a third run (kernel sources {sources_sha()}):", "", "```"]
     for i, ctr in enumerate(("FETCH_SIZE", "WRITE_SIZE", "SQ_INSTS_VALU SQ_WAVES")):
-        lines.append(f"timeout -s KILL 240 rocprofv3 --pmc {ctr} --output-format csv -d gpurun_out/p{i}{config} "
-                     f"-o p{i}{config} -- {base}{x}")
+        lines.append(f"timeout -s KILL 240 rocprofv3 --pmc {ctr} --output-format csv -d gpurun_out/pmc{i}_{config} "
+                     f"-o pmc{i} -- {base}{x}")
     lines += ["```", "", f"Summarised with `python bench.py --profile-report {config} STATS FETCH WRITE VALU {out_md}`.",
               "", "| kernel | fetch bytes | algorithmic read | write bytes | algorithmic write | VALU instr / wavefront "
               "| VALU instr / algorithmic byte (per wavefront lane-op: x64) |", "|---|---|---|---|---|---|---|"]
@@ -223,7 +226,7 @@ def pmc_rows(out_json):
     del src, dst
     algo = {}
     # slot receiver, first pass
-    c4 = dg.CONFIGS[4]
+    c4 = dg.SLOTS
     R, n, B, e = c4.R, c4.n, c4.block_slots, c4.epoch
     nslots, nblk = n // 2, n // 2 // B
     sets = []
@@ -248,7 +251,7 @@ def pmc_rows(out_json):
     algo["k_ll_unpack"] = bm.ll_unpack(R, n, B, completed_blocks=nblk - pend)
     del sets, out, stale, done, cnt
     # TokenWeave half A
-    c5 = dg.CONFIGS[5]
+    c5 = dg.TOKENWEAVE
     a = c5.splits[0]
     na = a * c5.H
     parts = [up(dg.partial(c5, r, na)) for r in range(c5.R)]
@@ -261,7 +264,7 @@ def pmc_rows(out_json):
     algo["BF16ReduceProducer"] = bm.reduce_rmsnorm(c5.R, a, c5.H, True, True)
     del parts, res, o5, ro5, rr
     # all-gather of the int8 prefill messages, first pass
-    c3 = dg.CONFIGS[3]
+    c3 = dg.PREFILL_70B
     msg3 = c3.L * c3.bits_ag // 8 + 4 * (c3.L // c3.group)
     nwords = -(-msg3 // 4 // B) * B
     gblk = nwords // B
@@ -485,7 +488,7 @@ def oracle_by_config(max_elems=1 << 22):
     os.sched_setaffinity(0, {cpus[min(2, len(cpus) - 1)]})
     out = {}
     try:
-        for idx, cfg in dg.CONFIGS.items():
+        for cfg in dg.WORKLOADS.values():
             T = cfg.T if cfg.n <= max_elems else max(cfg.R, max_elems // cfg.H // cfg.R * cfg.R)
             n = T * cfg.H
             reps = 3 if cfg.n > max_elems else 5
@@ -518,7 +521,7 @@ def oracle_by_config(max_elems=1 << 22):
             out[cfg.slug] = {"us_per_step": round(us, 1), "GB/s": round(full_bytes / (us * 1e-6) / 1e9, 4),
                              "runs": reps, "sample_rows": T, "rows": cfg.T}
         # the rows beyond the five workloads, on the workloads their benchmark rows use
-        c2, c3, c4 = dg.CONFIGS[2], dg.CONFIGS[3], dg.CONFIGS[4]
+        c2, c3, c4 = dg.DECODE_8B, dg.PREFILL_70B, dg.SLOTS
         parts = [dg.partial(c2, r) for r in range(c2.R)]
         res, gam = dg.residual(c2), dg.gamma(c2)
         extra = {
@@ -799,7 +802,7 @@ def bench_ll(cx):
     torch, np = cx.torch, cx.np
     from tensor_all_reduce_amd import _lib, bytes_model as bm, datagen as dg
     from tensor_all_reduce_amd.flash_allreduce import LLUnpackReduce
-    cfg = dg.CONFIGS[4]
+    cfg = dg.SLOTS
     R, n, B, e = cfg.R, cfg.n, cfg.block_slots, cfg.epoch
     nslots, nblk = n // 2, n // 2 // B
     set_bytes = R * 4 * n
@@ -858,7 +861,7 @@ def bench_ll_gather(cx):
     blocks have arrived."""
     torch, np = cx.torch, cx.np
     from tensor_all_reduce_amd import _lib, bytes_model as bm, datagen as dg
-    c4, c3 = dg.CONFIGS[4], dg.CONFIGS[3]
+    c4, c3 = dg.SLOTS, dg.PREFILL_70B
     B, e = c4.block_slots, c4.epoch
     res = {}
     msg3 = c3.L * c3.bits_ag // 8 + 4 * (c3.L // c3.group)
@@ -1040,7 +1043,7 @@ def bench_rmsnorm_overlap(cx):
     torch, np = cx.torch, cx.np
     from tensor_all_reduce_amd import bytes_model as bm, datagen as dg
     from tensor_all_reduce_amd.flash_allreduce import ReduceRMSNorm
-    cfg = dg.CONFIGS[5]
+    cfg = dg.TOKENWEAVE
     R, T, H = cfg.R, cfg.T, cfg.H
     a = cfg.splits[0]
     parts = [cx.up(dg.partial(cfg, r)) for r in range(R)]
@@ -1124,7 +1127,7 @@ def bench_layer(cx):
     torch = cx.torch
     from tensor_all_reduce_amd import datagen as dg
     from tensor_all_reduce_amd.schedule import TwoHalfLayer, gemm_waves, wave_aware_split
-    cfg = dg.CONFIGS[5]
+    cfg = dg.TOKENWEAVE
     R, H = cfg.R, cfg.H
     res_rows = {}
     for T in (cfg.T, 6000):
@@ -1186,15 +1189,15 @@ def main():
         return 0
     if args.profile_report:
         c, *paths = args.profile_report
-        profile_report(int(c), *paths)
+        profile_report(c, *paths)
         return 0
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build emulates the R ranks on one GPU "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the R ranks are emulated on one GPU "
               "(inter-GPU transfers are local HBM buffers); run with --gpus 1", file=sys.stderr)
         return 2
     from tensor_all_reduce_amd import datagen as dg
     cx = Ctx()
-    cfg = dg.CONFIGS[args.config]
+    cfg = dg.WORKLOADS[args.config]
     traffic = load_traffic(cfg)
     assert cfg.kind == "two_step", "the benchmark's metric is the quantized two-step path"
     main_r = bench_two_step(cx, cfg, args.steps, args.warmup, args.warm, args.kernel_reps, traffic)
@@ -1230,8 +1233,8 @@ def main():
         else set() if args.rows == "none" \
         else set(args.rows.split(","))
     extra = {}
-    if "prefill" in rows and args.config != 3:
-        c3 = dg.CONFIGS[3]
+    if "prefill" in rows and cfg is not dg.PREFILL_70B:
+        c3 = dg.PREFILL_70B
         r3 = bench_two_step(cx, c3, 30, 5, False, 0, load_traffic(c3))
         v3 = r3["step_bytes"] / (r3["ms_step"] * 1e-3) / 1e9
         extra["prefill_two_step"] = {"workload": c3.name, "us_per_step": round(r3["ms_step"] * 1e3, 2),
@@ -1248,11 +1251,11 @@ def main():
                                 "calls": {k: v["us"] for k, v in rw["per_call"].items()}}
     if "share" in rows:
         extra["share_decode"] = bench_share(cx, cfg, args.steps, args.warmup, args.kernel_reps)
-        if args.config != 3:
-            extra["share_prefill"] = bench_share(cx, dg.CONFIGS[3], 30, 5, 0)
+        if cfg is not dg.PREFILL_70B:
+            extra["share_prefill"] = bench_share(cx, dg.PREFILL_70B, 30, 5, 0)
     if "normfirst" in rows:
-        for c, tag, st, wu in ((cfg, "decode", min(args.steps, 300), 20), (dg.CONFIGS[3], "prefill", 30, 5)):
-            if tag == "prefill" and args.config == 3:
+        for c, tag, st, wu in ((cfg, "decode", min(args.steps, 300), 20), (dg.PREFILL_70B, "prefill", 30, 5)):
+            if tag == "prefill" and cfg is dg.PREFILL_70B:
                 continue
             rw = bench_two_step(cx, c, st, wu, False, 0, None, norm_first=True)
             vw = rw["step_bytes"] / (rw["ms_step"] * 1e-3) / 1e9
@@ -1273,16 +1276,16 @@ def main():
         extra["readiness_encodings"] = bench_encodings(cx, args.fit_encodings)
     # each row's time against the ceiling for its own read/write mix
     if "self_sync_slots" in extra:
-        r, c4 = extra["self_sync_slots"], dg.CONFIGS[4]
+        r, c4 = extra["self_sync_slots"], dg.SLOTS
         a = bm.ll_unpack(c4.R, c4.n, c4.block_slots, completed_blocks=r["blocks"] - r["pending_blocks"])
         r["pass1_pct_mixed_ceiling"] = round(100 * mixed_ceiling_us(a["read"], a["write"], ceil) / r["pass1_us"], 1)
     if "self_sync_allgather" in extra:
         for r in extra["self_sync_allgather"]["by_payload"].values():
-            a = bm.ll_gather(r["R"], r["words_per_rank"], dg.CONFIGS[4].block_slots,
+            a = bm.ll_gather(r["R"], r["words_per_rank"], dg.SLOTS.block_slots,
                              completed_blocks=r["pairs"] - r["pending_pairs"])
             r["pass1_pct_mixed_ceiling"] = round(100 * mixed_ceiling_us(a["read"], a["write"], ceil) / r["pass1_us"], 1)
     if "tokenweave_reduce_rmsnorm" in extra:
-        r, c5 = extra["tokenweave_reduce_rmsnorm"], dg.CONFIGS[5]
+        r, c5 = extra["tokenweave_reduce_rmsnorm"], dg.TOKENWEAVE
         a = bm.reduce_rmsnorm(c5.R, c5.splits[0], c5.H, True, True)
         r["both_halves_pct_mixed_ceiling"] = round(
             100 * 2 * mixed_ceiling_us(a["read"], a["write"], ceil) / r["both_halves_us"], 1)

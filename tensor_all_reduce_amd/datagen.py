@@ -55,20 +55,21 @@ class Config:
         return self.n // self.R
 
 
-# The five workloads (shapes of Llama-3-8B / Llama-3-70B hidden sizes; see module docstring).
-CONFIGS = {
-    1: Config(1, "tiny R=2 T=4 H=256 int8 G=32", "two_step", R=2, T=4, H=256, sigma=1.0, outlier_p=0.01,
-              outlier_factor=20.0, bits_rs=8, bits_ag=8, group=32, slug="tiny-r2-t4-h256"),
-    2: Config(2, "llama3-8b decode R=8 T=64 H=4096 int8 G=128", "two_step", R=8, T=64, H=4096, sigma=0.5,
-              outlier_p=0.005, outlier_factor=30.0, bits_rs=8, bits_ag=8, group=128, slug="llama3-8b-decode"),
-    3: Config(3, "llama3-70b tp8 prefill R=8 T=4096 H=8192 int4-RS/int8-AG G=128", "two_step", R=8, T=4096,
-              H=8192, sigma=1.0, outlier_p=0.001, outlier_factor=50.0, bits_rs=4, bits_ag=8, group=128,
-              slug="llama3-70b-prefill"),
-    4: Config(4, "self-synchronizing slots R=8 T=128 H=8192 B=64 2% stale", "ll", R=8, T=128, H=8192, sigma=1.0,
-              block_slots=64, stale_p=0.02, slug="self-sync-slots"),
-    5: Config(5, "tokenweave split R=8 T=8192(4096+4096) H=8192 bf16", "rmsnorm", R=8, T=8192, H=8192, sigma=1.0,
-              splits=(4096, 4096), slug="tokenweave-split"),
-}
+# The five workloads (shapes of Llama-3-8B / Llama-3-70B hidden sizes; see module docstring).  ``idx`` is
+# part of every generator's seed.
+TINY = Config(1, "tiny R=2 T=4 H=256 int8 G=32", "two_step", R=2, T=4, H=256, sigma=1.0, outlier_p=0.01,
+              outlier_factor=20.0, bits_rs=8, bits_ag=8, group=32, slug="tiny-r2-t4-h256")
+DECODE_8B = Config(2, "llama3-8b decode R=8 T=64 H=4096 int8 G=128", "two_step", R=8, T=64, H=4096, sigma=0.5,
+                   outlier_p=0.005, outlier_factor=30.0, bits_rs=8, bits_ag=8, group=128, slug="llama3-8b-decode")
+PREFILL_70B = Config(3, "llama3-70b tp8 prefill R=8 T=4096 H=8192 int4-RS/int8-AG G=128", "two_step", R=8,
+                     T=4096, H=8192, sigma=1.0, outlier_p=0.001, outlier_factor=50.0, bits_rs=4, bits_ag=8,
+                     group=128, slug="llama3-70b-prefill")
+SLOTS = Config(4, "self-synchronizing slots R=8 T=128 H=8192 B=64 2% stale", "ll", R=8, T=128, H=8192, sigma=1.0,
+               block_slots=64, stale_p=0.02, slug="self-sync-slots")
+TOKENWEAVE = Config(5, "tokenweave split R=8 T=8192(4096+4096) H=8192 bf16", "rmsnorm", R=8, T=8192, H=8192,
+                    sigma=1.0, splits=(4096, 4096), slug="tokenweave-split")
+# by name (slug), in this order
+WORKLOADS = {c.slug: c for c in (TINY, DECODE_8B, PREFILL_70B, SLOTS, TOKENWEAVE)}
 
 
 def rng_for(cfg: int, purpose: str, rank: int = 0, salt: int = 0) -> np.random.Generator:

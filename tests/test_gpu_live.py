@@ -62,7 +62,7 @@ def _tiles_polled(stale_rb, done0, group):
 @pytest.mark.parametrize("be,nblk", [(512, 37), (1024, 21), (4096, 9), (65536, 3)])
 def test_flag_receiver_matches_oracle(fc, orc, be, nblk, R, polls):
     from gpu_helpers import assert_equal_bits, up
-    cfg = dg.CONFIGS[4]
+    cfg = dg.SLOTS
     n, e = be * nblk, 0xFFFFFFFF if R == 3 else 0x2A
     xs = [dg.synth_bf16((be, R, r), n) for r in range(R)]
     fls, masks = zip(*[dg.stale_flags(cfg, r, nblk, epoch=e, p=0.15, salt=be * 100 + R) for r in range(R)])
@@ -145,7 +145,7 @@ def _set_epochs_host(slots, ep):
 def test_ll_poll_matches_oracle(fc, orc, B, R, polls):
     import torch
     from gpu_helpers import assert_equal_bits, up
-    cfg = dg.CONFIGS[4]
+    cfg = dg.SLOTS
     nblk = 8 * 9 + 3  # 75 blocks: the last tile is ragged for every block size
     n, e = 2 * B * nblk, 0 if R == 3 else 0x2A
     xs = [dg.synth_bf16((B, R, r, 1), n) for r in range(R)]
@@ -178,7 +178,7 @@ def test_ll_poll_equals_one_look_receiver(fc):
     (8 ranks x [128, 8192], 2% late copies, shuffled write order), grid capped or not."""
     import torch
     from gpu_helpers import assert_equal_bits, down, up
-    cfg = dg.CONFIGS[4]
+    cfg = dg.SLOTS
     R, n, B, e = cfg.R, cfg.n, cfg.block_slots, cfg.epoch
     nslots, nblk = n // 2, n // 2 // B
     slots_d = []
@@ -212,7 +212,7 @@ LIVE_WGS = 32          # the receiver's grid and compute units; the sender has t
 def test_live_sender_and_receiver(fc, orc, enc):
     import torch
     from gpu_helpers import assert_equal_bits, up
-    cfg = dg.CONFIGS[4]
+    cfg = dg.SLOTS
     R, n = cfg.R, cfg.n
     be, B = 2048, cfg.block_slots
     nblk = n // be if enc == "flag" else n // 2 // B

@@ -83,7 +83,7 @@ def test_workload_stale_mix_and_retry(fc, orc):
     pass completes every pending block with the same bits as an all-on-time run."""
     from gpu_helpers import assert_equal_bits, up
     import torch
-    cfg = dg.CONFIGS[4]
+    cfg = dg.SLOTS
     R, n, B, e = cfg.R, cfg.n, cfg.block_slots, cfg.epoch
     nslots, nblk = n // 2, n // 2 // B
     xs = [dg.partial(cfg, r) for r in range(R)]

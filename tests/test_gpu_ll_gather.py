@@ -107,7 +107,7 @@ def test_quantized_all_gather_in_slots_end_to_end(fc, orc):
     gathered messages with the residual-add + RMSNorm epilogue."""
     import torch
     from gpu_helpers import assert_bf16_close, assert_equal_bits, down, up
-    cfg = dg.CONFIGS[2]
+    cfg = dg.DECODE_8B
     R, L, G, b2 = cfg.R, cfg.L, cfg.group, cfg.bits_ag
     parts = dg.partials(cfg)
     res, gam = dg.residual(cfg), dg.gamma(cfg)
@@ -143,7 +143,7 @@ def test_all_gather_prefill_messages_as_benched(fc, orc):
     words each) carried in 64-slot blocks with about 2% of the copies late (every kind), pass 1 then the
     retry with every block rewritten: out, stale, done and counters of both passes equal the oracle's."""
     from gpu_helpers import assert_equal_bits, down
-    cfg = dg.CONFIGS[3]
+    cfg = dg.PREFILL_70B
     R, B = cfg.R, 64
     nwords = (cfg.L * cfg.bits_ag // 8 + 4 * (cfg.L // cfg.group)) // 4
     assert nwords % B == 0

@@ -81,14 +81,14 @@ def test_reduce_norm_without_residual(fc, orc):
     _run_shards(orc, 4, 2, 2, 4096, 8, 8, 128, with_residual=False, seed=11)
 
 
-@pytest.mark.parametrize("cfg_idx", [1, 2])
-def test_norm_first_end_to_end(fc, orc, cfg_idx):
+@pytest.mark.parametrize("workload", ["tiny-r2-t4-h256", "llama3-8b-decode"])
+def test_norm_first_end_to_end(fc, orc, workload):
     """Quantize all ranks, every shard's reduce + norm + quantization, gather of the normalized rows,
     against the oracle's whole norm-first all-reduce."""
     import torch
     from gpu_helpers import assert_equal_bits, down, up
     from tensor_all_reduce_amd.flash_allreduce import TwoStepAllReduce
-    cfg = dg.CONFIGS[cfg_idx]
+    cfg = dg.WORKLOADS[workload]
     parts = dg.partials(cfg)
     res, gam = dg.residual(cfg), dg.gamma(cfg)
     ref = orc.two_step_normfirst(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, res, gam, cfg.eps, cfg.H)
@@ -110,7 +110,7 @@ def test_norm_first_70b_prefill_sampled(fc, orc):
     import torch
     from gpu_helpers import assert_equal_bits, down, up
     from tensor_all_reduce_amd.flash_allreduce import TwoStepAllReduce
-    cfg = dg.CONFIGS[3]
+    cfg = dg.PREFILL_70B
     R, T, H, G, b1, b2 = cfg.R, cfg.T, cfg.H, cfg.group, cfg.bits_rs, cfg.bits_ag
     parts = dg.partials(cfg)
     res, gam = dg.residual(cfg), dg.gamma(cfg)

@@ -63,11 +63,11 @@ def test_quantize_single_group_and_tiny(fc, orc, group):
             assert_equal_bits(c, rc, f"codes n={ngroups}")
 
 
-@pytest.mark.parametrize("cfg_idx", [1, 2])
-def test_quantize_workloads_full(fc, orc, cfg_idx):
+@pytest.mark.parametrize("workload", ["tiny-r2-t4-h256", "llama3-8b-decode"])
+def test_quantize_workloads_full(fc, orc, workload):
     """All ranks of the workload quantized in one batched call, compared in full."""
     from gpu_helpers import assert_equal_bits
-    cfg = dg.CONFIGS[cfg_idx]
+    cfg = dg.WORKLOADS[workload]
     parts = np.concatenate(dg.partials(cfg))
     c, m = run_quantize(fc, parts, cfg.bits_rs, cfg.group)
     rc, rm = orc.quantize(parts, cfg.bits_rs, cfg.group)
@@ -78,7 +78,7 @@ def test_quantize_workloads_full(fc, orc, cfg_idx):
 def test_quantize_70b_prefill_sampled(fc, orc):
     """8 ranks x [4096, 8192] bf16, int4 groups of 128, one batched launch (the benchmark's launch);
     2048 sampled groups plus the first and last group of every rank are recomputed by the oracle."""
-    cfg = dg.CONFIGS[3]
+    cfg = dg.PREFILL_70B
     from gpu_helpers import assert_equal_bits
     R, n, G, bits = cfg.R, cfg.n, cfg.group, cfg.bits_rs
     parts = [dg.partial(cfg, r) for r in range(R)]

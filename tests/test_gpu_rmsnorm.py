@@ -79,7 +79,7 @@ def test_tokenweave_workload_sampled(fc, orc):
     the benchmark does); halves equal the unsplit call bit for bit, and sampled rows match the oracle."""
     import torch
     from gpu_helpers import assert_bf16_close, down, up
-    cfg = dg.CONFIGS[5]
+    cfg = dg.TOKENWEAVE
     R, T, H = cfg.R, cfg.T, cfg.H
     parts_h = [dg.partial(cfg, r) for r in range(R)]
     res_h, gam_h = dg.residual(cfg), dg.gamma(cfg)

@@ -15,12 +15,13 @@ def fc():
     return _lib
 
 
-@pytest.mark.parametrize("cfg_idx,rank", [(1, 0), (1, 1), (2, 0), (2, 5), (2, 7)])
-def test_share_matches_whole_all_reduce(fc, orc, cfg_idx, rank):
+@pytest.mark.parametrize("workload,rank", [("tiny-r2-t4-h256", 0), ("tiny-r2-t4-h256", 1), ("llama3-8b-decode", 0),
+                                           ("llama3-8b-decode", 5), ("llama3-8b-decode", 7)])
+def test_share_matches_whole_all_reduce(fc, orc, workload, rank):
     import torch
     from gpu_helpers import assert_bf16_close, assert_equal_bits, down, up
     from tensor_all_reduce_amd.flash_allreduce import TwoStepShare
-    cfg = dg.CONFIGS[cfg_idx]
+    cfg = dg.WORKLOADS[workload]
     R, L, G, b1, b2 = cfg.R, cfg.L, cfg.group, cfg.bits_rs, cfg.bits_ag
     parts = dg.partials(cfg)
     res, gam = dg.residual(cfg), dg.gamma(cfg)

@@ -124,13 +124,13 @@ def _pipeline(cfg, parts_np):
     return p
 
 
-@pytest.mark.parametrize("cfg_idx", [1, 2])
-def test_two_step_end_to_end(fc, orc, cfg_idx):
+@pytest.mark.parametrize("workload", ["tiny-r2-t4-h256", "llama3-8b-decode"])
+def test_two_step_end_to_end(fc, orc, workload):
     """The whole GPU pipeline (batched quantize, all shards' reduce-scatter, gather + epilogue) against the
     oracle's whole two-step all-reduce, stage by stage."""
     import torch
     from gpu_helpers import assert_bf16_close, assert_equal_bits, down, up
-    cfg = dg.CONFIGS[cfg_idx]
+    cfg = dg.WORKLOADS[workload]
     parts = dg.partials(cfg)
     res, gam = dg.residual(cfg), dg.gamma(cfg)
     ref = orc.two_step(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, residual=res, gamma=gam, eps=cfg.eps, hidden=cfg.H)
@@ -165,7 +165,7 @@ def test_two_step_70b_prefill_sampled(fc, orc):
     partial sums (groups never cross rows, and a row's norm needs only that row)."""
     import torch
     from gpu_helpers import assert_bf16_close, assert_equal_bits, down, up
-    cfg = dg.CONFIGS[3]
+    cfg = dg.PREFILL_70B
     R, T, H, G, b1, b2 = cfg.R, cfg.T, cfg.H, cfg.group, cfg.bits_rs, cfg.bits_ag
     parts = dg.partials(cfg)
     res, gam = dg.residual(cfg), dg.gamma(cfg)
@@ -203,7 +203,7 @@ def test_two_step_deterministic_repeat(fc):
     """The same inputs give the same bits on every call (no atomics, fixed order)."""
     import torch
     from gpu_helpers import up
-    cfg = dg.CONFIGS[2]
+    cfg = dg.DECODE_8B
     parts = dg.partials(cfg)
     p = _pipeline(cfg, parts)
     outs = []

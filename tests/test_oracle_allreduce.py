@@ -101,15 +101,15 @@ def test_grid_identity_small_R(orc, R, bits):
     assert np.array_equal(f32(res["y"]).astype(np.float64), R * f32(p).astype(np.float64))
 
 
-@pytest.mark.parametrize("cfg_idx", [1, 2])
+@pytest.mark.parametrize("workload", ["tiny-r2-t4-h256", "llama3-8b-decode"])
 @pytest.mark.parametrize("bits1,bits2", [(8, 8), (4, 8), (4, 4), (8, 4)])
-def test_two_step_error_bound(orc, cfg_idx, bits1, bits2):
+def test_two_step_error_bound(orc, workload, bits1, bits2):
     """End-to-end: |y - sum_r x_r| <= sum_r s_r/2 + s'/2 + fp32 slack, where s_r are the rank-message
     scales of each element's group and s' the requantized scale (half-step bound of each quantization,
     exact sum in double).  A dropped rank, a wrong shard or group index, or a wrong sign breaks it."""
-    cfg = dg.CONFIGS[cfg_idx]
+    cfg = dg.WORKLOADS[workload]
     R, n, G = cfg.R, cfg.n, cfg.group
-    if cfg_idx == 2:
+    if cfg is dg.DECODE_8B:
         n = 8 * 4096  # 8 rows keep the test quick
     parts = [dg.partial(cfg, r, n) for r in range(R)]
     res = orc.two_step(parts, bits1, bits2, G)
@@ -194,7 +194,7 @@ def test_reduce_rmsnorm_identical_partials(orc, R):
 
 def test_reduce_rmsnorm_generic_sum(orc):
     """Generic partials: the fp32 ascending fold is within R fp32 roundings of the exact sum."""
-    cfg = dg.CONFIGS[5]
+    cfg = dg.TOKENWEAVE
     rows, H, R = 2, cfg.H, cfg.R
     parts = [dg.partial(cfg, r, rows * H) for r in range(R)]
     res = dg.residual(cfg, rows * H)

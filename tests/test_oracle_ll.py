@@ -104,7 +104,7 @@ def test_seeded_stale_mix_flags_and_retry(orc):
     """The workload's stale mix (2% of (rank, block) pairs, several kinds of wrong words): flags equal
     the injected set, counters count it, and after the late blocks are rewritten with the right epoch a
     second pass completes every pending block with the same bits as an all-valid run."""
-    cfg = dg.CONFIGS[4]
+    cfg = dg.SLOTS
     R, B, e = cfg.R, cfg.block_slots, cfg.epoch
     n = 2 * B * 512
     nslots, nblk = n // 2, n // 2 // B

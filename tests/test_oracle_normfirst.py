@@ -130,7 +130,7 @@ def test_two_step_normfirst_close_to_standard_path(orc):
     """Norm first, then an 8-bit quantized all-gather, versus the standard path (all-gather of the sums,
     then the norm): the same rows up to one 8-bit quantization step of the normalized values, and the
     same residual stream up to the quantization of the sums."""
-    cfg = dg.CONFIGS[1]
+    cfg = dg.TINY
     parts = dg.partials(cfg)
     res, gam = dg.residual(cfg), dg.gamma(cfg)
     nf = orc.two_step_normfirst(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, res, gam, cfg.eps, cfg.H)
