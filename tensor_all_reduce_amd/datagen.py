@@ -9,7 +9,8 @@ value structure are used: Gaussian partial sums with rare large outliers (activa
 make per-group low-bit quantization non-trivial), a Gaussian residual stream and a near-one RMSNorm
 weight.
 
-Generator: numpy PCG64 with ``SeedSequence([0xFC, cfg, purpose, rank])``; purposes are listed in
+Generator: numpy PCG64 with ``SeedSequence([0xFC, idx, purpose, rank])``, idx being the workload's number
+(``Config.idx``); purposes are listed in
 ``PURPOSE``.  A partial is sigma*N(0,1) in fp32, multiplied by ``outlier_factor`` where an i.i.d.
 Bernoulli(``outlier_p``) mask is set, then rounded to bf16 with ties to even.
 """
