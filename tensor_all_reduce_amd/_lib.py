@@ -91,12 +91,28 @@ _lib = _load()
 lib = _lib
 
 
-def _ptr(t) -> int | None:
+def _dev(t, nbytes: int | None = None, what: str = "buffer") -> int | None:
+    """Address of a device buffer.  None passes through (an optional argument) and an int is taken as a
+    raw device address that the caller vouches for.  A tensor must be contiguous, in device memory and
+    at least `nbytes` long, else ValueError: the kernels would otherwise read or write a host or too
+    small buffer out of bounds, which is a device fault rather than an error."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: a torch tensor, an int device address or None is required, got {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: the tensor must be in device memory (it is on {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: the tensor must be contiguous")
+    have = t.numel() * t.element_size()
+    if nbytes is not None and have < nbytes:
+        raise ValueError(f"{what}: {have} bytes, the call reads or writes {nbytes}")
     return t.data_ptr()
+
+
+_ptr = _dev
 
 
 def _stream(stream) -> int | None:
@@ -112,29 +128,36 @@ def _check(st: int, where: str):
         raise FcError(st, where)
 
 
-def _qmsg(m) -> QMsg:
+def _qmsg(m, n: int = 0, bits: int = 8, group: int = 1, what: str = "message") -> QMsg:
+    """A quantized message of n elements: n*bits/8 bytes of codes, a 4-byte word per group."""
     codes, meta = m
-    return QMsg(_ptr(codes), _ptr(meta))
+    return QMsg(_dev(codes, max(0, n) * bits // 8, what + " codes"),
+                _dev(meta, 4 * (max(0, n) // max(1, group)), what + " meta"))
 
 
-def _norm(norm) -> Norm | None:
+def _norm(norm, elems: int = 0) -> Norm | None:
+    """The epilogue's arguments; residual, out and residual_out cover `elems` bf16 elements."""
     if norm is None:
         return None
-    return Norm(_ptr(norm.get("residual")), _ptr(norm["gamma"]), float(norm.get("eps", 1e-5)), int(norm["hidden"]),
-                _ptr(norm.get("out")), _ptr(norm.get("residual_out")))
+    hidden = int(norm["hidden"])
+    nb = 2 * max(0, elems)
+    return Norm(_dev(norm.get("residual"), nb, "residual"), _dev(norm["gamma"], 2 * max(0, hidden), "gamma"),
+                float(norm.get("eps", 1e-5)), hidden, _dev(norm.get("out"), nb, "out"),
+                _dev(norm.get("residual_out"), nb, "residual_out"))
 
 
 def fc_quantize(x, bits: int, group: int, codes, meta, n: int | None = None, stream=None) -> None:
     """Group-quantize bf16 `x` (n elements, default x.numel()) into `codes` and `meta`."""
     n = x.numel() if n is None else n
-    _check(_lib.fc_quantize(_ptr(x), n, bits, group, QMsg(_ptr(codes), _ptr(meta)), _stream(stream)), "fc_quantize")
+    _check(_lib.fc_quantize(_dev(x, 2 * max(0, n), "x"), n, bits, group, _qmsg((codes, meta), n, bits, group, "out"),
+                            _stream(stream)), "fc_quantize")
 
 
 def fc_reduce_shard(inputs, R: int, L: int, bits_in: int, bits_out: int, group: int, outputs, stream=None) -> None:
     """inputs: n_shards*R (codes, meta) pairs, [shard][rank]; outputs: n_shards (codes, meta) pairs."""
     n_shards = len(outputs)
-    ins = (QMsg * len(inputs))(*[_qmsg(m) for m in inputs])
-    outs = (QMsg * n_shards)(*[_qmsg(m) for m in outputs])
+    ins = (QMsg * len(inputs))(*[_qmsg(m, L, bits_in, group, "input") for m in inputs])
+    outs = (QMsg * n_shards)(*[_qmsg(m, L, bits_out, group, "output") for m in outputs])
     _check(_lib.fc_reduce_shard(ins, R, L, n_shards, bits_in, bits_out, group, outs, _stream(stream)),
            "fc_reduce_shard")
 
@@ -145,9 +168,9 @@ def fc_reduce_shard_norm(inputs, R: int, L: int, bits_in: int, bits_out: int, gr
     normalized rows are quantized into `outputs`.  norm: dict(residual, gamma, eps, hidden, residual_out)
     over the n_shards*L elements of the shards, without "out"."""
     n_shards = len(outputs)
-    ins = (QMsg * len(inputs))(*[_qmsg(m) for m in inputs])
-    outs = (QMsg * n_shards)(*[_qmsg(m) for m in outputs])
-    nm = _norm(norm)
+    ins = (QMsg * len(inputs))(*[_qmsg(m, L, bits_in, group, "input") for m in inputs])
+    outs = (QMsg * n_shards)(*[_qmsg(m, L, bits_out, group, "output") for m in outputs])
+    nm = _norm(norm, n_shards * L)
     _check(_lib.fc_reduce_shard_norm(ins, R, L, n_shards, bits_in, bits_out, group, C.byref(nm), outs,
                                      _stream(stream)), "fc_reduce_shard_norm")
 
@@ -156,33 +179,40 @@ def fc_gather_dequant(shards, L: int, bits: int, group: int, y=None, norm: dict 
     """shards: R (codes, meta) pairs; y: bf16 [R*L] or None; norm: dict(residual, gamma, eps, hidden, out,
     residual_out) or None."""
     R = len(shards)
-    arr = (QMsg * R)(*[_qmsg(m) for m in shards])
-    nm = _norm(norm)
-    _check(_lib.fc_gather_dequant(arr, R, L, bits, group, _ptr(y), C.byref(nm) if nm is not None else None,
+    arr = (QMsg * R)(*[_qmsg(m, L, bits, group, "shard") for m in shards])
+    nm = _norm(norm, R * L)
+    _check(_lib.fc_gather_dequant(arr, R, L, bits, group, _dev(y, 2 * R * max(0, L), "y"),
+                                  C.byref(nm) if nm is not None else None,
                                   _stream(stream)), "fc_gather_dequant")
 
 
 def fc_reduce_rmsnorm(parts, rows: int, norm: dict, max_workgroups: int = 0, stream=None) -> None:
     R = len(parts)
-    arr = (C.c_void_p * R)(*[_ptr(p) for p in parts])
-    nm = _norm(norm)
+    elems = max(0, rows) * max(0, int(norm["hidden"]))
+    arr = (C.c_void_p * R)(*[_dev(p, 2 * elems, "part") for p in parts])
+    nm = _norm(norm, elems)
     _check(_lib.fc_reduce_rmsnorm(arr, R, rows, C.byref(nm), max_workgroups, _stream(stream)), "fc_reduce_rmsnorm")
 
 
 def fc_ll_unpack_reduce(slots, n: int, block_slots: int, epoch: int, out, stale, done, counters, stream=None) -> None:
     R = len(slots)
-    arr = (C.c_void_p * R)(*[_ptr(s) for s in slots])
-    _check(_lib.fc_ll_unpack_reduce(arr, R, n, block_slots, epoch & 0xFFFFFFFF, _ptr(out), _ptr(stale), _ptr(done),
-                                    _ptr(counters), _stream(stream)), "fc_ll_unpack_reduce")
+    n, nblk = max(0, n), max(0, n) // 2 // max(1, block_slots)
+    arr = (C.c_void_p * R)(*[_dev(s, 4 * n, "slots") for s in slots])
+    _check(_lib.fc_ll_unpack_reduce(arr, R, n, block_slots, epoch & 0xFFFFFFFF, _dev(out, 2 * n, "out"),
+                                    _dev(stale, R * nblk, "stale"), _dev(done, nblk, "done"),
+                                    _dev(counters, 8, "counters"), _stream(stream)), "fc_ll_unpack_reduce")
 
 
 def fc_ll_gather(slots, nwords: int, block_slots: int, epoch: int, out, stale, done, counters, stream=None) -> None:
     """slots: R uint64 slot buffers; out: R uint32 (or any 4-byte) destination buffers."""
     R = len(slots)
-    sa = (C.c_void_p * R)(*[_ptr(s) for s in slots])
-    oa = (C.c_void_p * R)(*[_ptr(o) for o in out])
-    _check(_lib.fc_ll_gather(sa, R, nwords, block_slots, epoch & 0xFFFFFFFF, oa, _ptr(stale), _ptr(done),
-                             _ptr(counters), _stream(stream)), "fc_ll_gather")
+    nw = max(0, nwords)
+    nblk = nw // max(1, block_slots)
+    sa = (C.c_void_p * R)(*[_dev(s, 8 * nw, "slots") for s in slots])
+    oa = (C.c_void_p * R)(*[_dev(o, 4 * nw, "out") for o in out])
+    _check(_lib.fc_ll_gather(sa, R, nwords, block_slots, epoch & 0xFFFFFFFF, oa, _dev(stale, R * nblk, "stale"),
+                             _dev(done, R * nblk, "done"), _dev(counters, 8, "counters"), _stream(stream)),
+           "fc_ll_gather")
 
 
 def _ranks(v):
@@ -190,8 +220,8 @@ def _ranks(v):
     return list(v) if isinstance(v, (list, tuple)) else [v]
 
 
-def _ptrs(lst):
-    return (C.c_void_p * len(lst))(*[_ptr(t) for t in lst])
+def _ptrs(lst, nbytes: int | None = None, what: str = "buffer"):
+    return (C.c_void_p * len(lst))(*[_dev(t, nbytes, what) for t in lst])
 
 
 def fc_ll_pack(x, block_slots: int, epoch: int, slots, block_order=None, n: int | None = None, pace: int = 0,
@@ -199,18 +229,23 @@ def fc_ll_pack(x, block_slots: int, epoch: int, slots, block_order=None, n: int 
     """x, slots, block_order: one tensor each (one rank) or lists of R (R peers in one launch)."""
     xs, ss = _ranks(x), _ranks(slots)
     n = xs[0].numel() if n is None else n
-    oa = None if block_order is None else _ptrs(_ranks(block_order))
-    _check(_lib.fc_ll_pack(_ptrs(xs), len(xs), n, block_slots, epoch & 0xFFFFFFFF, oa, pace, _ptrs(ss),
-                           _stream(stream)), "fc_ll_pack")
+    nn = max(0, n)
+    oa = None if block_order is None else _ptrs(_ranks(block_order), 4 * (nn // 2 // max(1, block_slots)),
+                                                "block_order")
+    _check(_lib.fc_ll_pack(_ptrs(xs, 2 * nn, "x"), len(xs), n, block_slots, epoch & 0xFFFFFFFF, oa, pace,
+                           _ptrs(ss, 4 * nn, "slots"), _stream(stream)), "fc_ll_pack")
 
 
 def fc_ll_poll_unpack_reduce(slots, n: int, block_slots: int, epoch: int, out, stale, done, counters,
                              max_polls: int = 0, max_workgroups: int = 0, stream=None) -> None:
     """counters: 4 int32 (stale pairs, pending blocks, re-reads, unused)."""
     R = len(slots)
-    arr = (C.c_void_p * R)(*[_ptr(s) for s in slots])
+    nn = max(0, n)
+    nblk = nn // 2 // max(1, block_slots)
+    arr = (C.c_void_p * R)(*[_dev(s, 4 * nn, "slots") for s in slots])
     _check(_lib.fc_ll_poll_unpack_reduce(arr, R, n, block_slots, epoch & 0xFFFFFFFF, max_polls, max_workgroups,
-                                         _ptr(out), _ptr(stale), _ptr(done), _ptr(counters), _stream(stream)),
+                                         _dev(out, 2 * nn, "out"), _dev(stale, R * nblk, "stale"),
+                                         _dev(done, nblk, "done"), _dev(counters, 16, "counters"), _stream(stream)),
            "fc_ll_poll_unpack_reduce")
 
 
@@ -218,10 +253,13 @@ def fc_flag_unpack_reduce(payload, flags, n: int, block_elems: int, epoch: int, 
                           max_polls: int = 0, max_workgroups: int = 0, stream=None) -> None:
     """payload: R bf16 (int16) buffers; flags: R int32 buffers of n / block_elems words; counters: 4 int32."""
     R = len(payload)
-    pa = (C.c_void_p * R)(*[_ptr(p) for p in payload])
-    fa = (C.c_void_p * R)(*[_ptr(f) for f in flags])
+    nn = max(0, n)
+    nblk = nn // max(1, block_elems)
+    pa = (C.c_void_p * R)(*[_dev(p, 2 * nn, "payload") for p in payload])
+    fa = (C.c_void_p * R)(*[_dev(f, 4 * nblk, "flags") for f in flags])
     _check(_lib.fc_flag_unpack_reduce(pa, fa, R, n, block_elems, epoch & 0xFFFFFFFF, max_polls, max_workgroups,
-                                      _ptr(out), _ptr(stale), _ptr(done), _ptr(counters), _stream(stream)),
+                                      _dev(out, 2 * nn, "out"), _dev(stale, R * nblk, "stale"),
+                                      _dev(done, nblk, "done"), _dev(counters, 16, "counters"), _stream(stream)),
            "fc_flag_unpack_reduce")
 
 
@@ -230,19 +268,26 @@ def fc_flag_pack(x, block_elems: int, epoch: int, payload, flags, block_order=No
     """x, payload, flags, block_order: one tensor each (one rank) or lists of R (R peers in one launch)."""
     xs = _ranks(x)
     n = xs[0].numel() if n is None else n
-    oa = None if block_order is None else _ptrs(_ranks(block_order))
-    _check(_lib.fc_flag_pack(_ptrs(xs), len(xs), n, block_elems, epoch & 0xFFFFFFFF, oa, pace,
-                             _ptrs(_ranks(payload)), _ptrs(_ranks(flags)), _stream(stream)), "fc_flag_pack")
+    nn = max(0, n)
+    nblk = nn // max(1, block_elems)
+    oa = None if block_order is None else _ptrs(_ranks(block_order), 4 * nblk, "block_order")
+    _check(_lib.fc_flag_pack(_ptrs(xs, 2 * nn, "x"), len(xs), n, block_elems, epoch & 0xFFFFFFFF, oa, pace,
+                             _ptrs(_ranks(payload), 2 * nn, "payload"), _ptrs(_ranks(flags), 4 * nblk, "flags"),
+                             _stream(stream)), "fc_flag_pack")
 
 
 def fc_copy(src, dst, nbytes: int | None = None, stream=None) -> None:
     nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
-    _check(_lib.fc_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "fc_copy")
+    _check(_lib.fc_copy(_dev(src, max(0, nbytes), "src"), _dev(dst, max(0, nbytes), "dst"), nbytes, _stream(stream)),
+           "fc_copy")
 
 
 def fc_bandwidth_probe(src, dst, nbytes: int, mode: int, stream=None) -> None:
     """mode 0 copy, 1 read (dst: a 4-byte sink), 2 write (src unused)."""
-    _check(_lib.fc_bandwidth_probe(_ptr(src), _ptr(dst), nbytes, mode, _stream(stream)), "fc_bandwidth_probe")
+    nb = max(0, nbytes)
+    _check(_lib.fc_bandwidth_probe(_dev(src, nb if mode in (0, 1) else None, "src"),
+                                   _dev(dst, nb if mode in (0, 2) else 4, "dst"), nbytes, mode, _stream(stream)),
+           "fc_bandwidth_probe")
 
 
 def fc_abi_version() -> int:

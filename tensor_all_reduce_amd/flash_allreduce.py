@@ -24,6 +24,19 @@ from . import _lib
 u8, i16, i32, i64 = torch.uint8, torch.int16, torch.int32, torch.int64
 
 
+def _device(device) -> torch.device:
+    dev = torch.device(device)
+    if dev.type != "cuda":
+        raise ValueError(f"buffers must be in device memory, not on {dev}: every step runs in the HIP kernels")
+    return dev
+
+
+def _norm_args(gamma, out, residual, residual_out, eps: float, H: int, elems: int) -> _lib.Norm:
+    """Checked epilogue arguments: residual, out and residual_out cover `elems` bf16 elements."""
+    return _lib.Norm(_lib._dev(residual, 2 * elems, "residual"), _lib._dev(gamma, 2 * H, "gamma"), float(eps), H,
+                     _lib._dev(out, 2 * elems, "out"), _lib._dev(residual_out, 2 * elems, "residual_out"))
+
+
 def bf16_buffer(n: int, device) -> torch.Tensor:
     """bf16 bit patterns are held in int16 tensors (the kernels see raw 16-bit words)."""
     return torch.empty(n, dtype=i16, device=device)
@@ -43,8 +56,9 @@ class TwoStepAllReduce:
         assert n % R == 0, "T*H must split into R shards"
         self.n, self.L = n, n // R
         L = self.L
-        dev = torch.device(device)
+        dev = _device(device)
         self.parts = parts if parts is not None else torch.empty(R, n, dtype=i16, device=dev)
+        _lib._dev(self.parts, 2 * R * n, "parts")
         self.codes1 = torch.empty(R, n * bits_rs // 8, dtype=u8, device=dev)
         self.meta1 = torch.empty(R, n // group, dtype=i32, device=dev)
         self.codes2 = torch.empty(n * bits_ag // 8, dtype=u8, device=dev)
@@ -71,8 +85,8 @@ class TwoStepAllReduce:
 
     # -- steps
     def quantize(self, stream=None):
-        st = _lib.lib.fc_quantize(self.parts.data_ptr(), self.R * self.n, self.b1, self.G, self._q,
-                                  _lib._stream(stream))
+        st = _lib.lib.fc_quantize(_lib._dev(self.parts, 2 * self.R * self.n, "parts"), self.R * self.n, self.b1,
+                                  self.G, self._q, _lib._stream(stream))
         _lib._check(st, "fc_quantize")
 
     def reduce_scatter(self, shard: int | None = None, stream=None):
@@ -89,9 +103,9 @@ class TwoStepAllReduce:
         _lib._check(st, "fc_reduce_shard")
 
     def make_norm(self, gamma, out, residual=None, residual_out=None, eps: float = 1e-5) -> _lib.Norm:
-        return _lib.Norm(residual.data_ptr() if residual is not None else None, gamma.data_ptr(), float(eps), self.H,
-                         out.data_ptr() if out is not None else None,
-                         residual_out.data_ptr() if residual_out is not None else None)
+        """The epilogue's arguments: every row of the T*H elements (as the gather's epilogue, or with out=None
+        for the norm first)."""
+        return _norm_args(gamma, out, residual, residual_out, eps, self.H, self.n)
 
     def reduce_scatter_norm(self, norm: _lib.Norm, stream=None):
         """Every shard's reduce with the norm first (make_norm with out=None; residual and residual_out
@@ -107,8 +121,7 @@ class TwoStepAllReduce:
         self.all_gather(y=y, stream=stream)
 
     def all_gather(self, y=None, norm: _lib.Norm | None = None, stream=None):
-        st = _lib.lib.fc_gather_dequant(self._ag_in, self.R, self.L, self.b2, self.G,
-                                        y.data_ptr() if y is not None else None,
+        st = _lib.lib.fc_gather_dequant(self._ag_in, self.R, self.L, self.b2, self.G, _lib._dev(y, 2 * self.n, "y"),
                                         C.byref(norm) if norm is not None else None, _lib._stream(stream))
         _lib._check(st, "fc_gather_dequant")
 
@@ -135,9 +148,10 @@ class TwoStepShare:
         n = T * H
         assert n % R == 0 and 0 <= rank < R
         self.n, self.L = n, n // R
-        L, dev = self.L, torch.device(device)
+        L, dev = self.L, _device(device)
         cb1, cb2, mb = L * bits_rs // 8, L * bits_ag // 8, L // group
         self.x = x if x is not None else torch.empty(n, dtype=i16, device=dev)
+        _lib._dev(self.x, 2 * n, "x")
         self.codes1 = torch.empty(n * bits_rs // 8, dtype=u8, device=dev)   # own message, all R chunks
         self.meta1 = torch.empty(n // group, dtype=i32, device=dev)
         self.inbox_codes = torch.empty(R, cb1, dtype=u8, device=dev)        # peers' chunks of own shard
@@ -154,7 +168,8 @@ class TwoStepShare:
         self._rs_out = C.cast(C.addressof(self._ag) + C.sizeof(_lib.QMsg) * rank, C.POINTER(_lib.QMsg))
 
     def quantize(self, stream=None):
-        st = _lib.lib.fc_quantize(self.x.data_ptr(), self.n, self.b1, self.G, self._q, _lib._stream(stream))
+        st = _lib.lib.fc_quantize(_lib._dev(self.x, 2 * self.n, "x"), self.n, self.b1, self.G, self._q,
+                                  _lib._stream(stream))
         _lib._check(st, "fc_quantize")
 
     def reduce(self, stream=None):
@@ -163,9 +178,9 @@ class TwoStepShare:
         _lib._check(st, "fc_reduce_shard")
 
     def make_norm(self, gamma, out, residual=None, residual_out=None, eps: float = 1e-5) -> _lib.Norm:
-        return _lib.Norm(residual.data_ptr() if residual is not None else None, gamma.data_ptr(), float(eps), self.H,
-                         out.data_ptr() if out is not None else None,
-                         residual_out.data_ptr() if residual_out is not None else None)
+        """The epilogue's arguments: the gather's (out given: all T*H elements) or the own shard's norm first
+        (out=None: its L elements)."""
+        return _norm_args(gamma, out, residual, residual_out, eps, self.H, self.n if out is not None else self.L)
 
     def reduce_norm(self, norm: _lib.Norm, stream=None):
         """Own shard's reduce with the norm first (make_norm with out=None; residual and residual_out are
@@ -180,8 +195,7 @@ class TwoStepShare:
         self.gather(y=y, stream=stream)
 
     def gather(self, y=None, norm: _lib.Norm | None = None, stream=None):
-        st = _lib.lib.fc_gather_dequant(self._ag, self.R, self.L, self.b2, self.G,
-                                        y.data_ptr() if y is not None else None,
+        st = _lib.lib.fc_gather_dequant(self._ag, self.R, self.L, self.b2, self.G, _lib._dev(y, 2 * self.n, "y"),
                                         C.byref(norm) if norm is not None else None, _lib._stream(stream))
         _lib._check(st, "fc_gather_dequant")
 
@@ -196,9 +210,8 @@ class ReduceRMSNorm:
 
     def __init__(self, parts: list, rows: int, H: int, gamma, out, residual=None, residual_out=None, eps=1e-5):
         self.R, self.rows, self.H = len(parts), rows, H
-        self._parts = (C.c_void_p * self.R)(*[p.data_ptr() for p in parts])
-        self.norm = _lib.Norm(residual.data_ptr() if residual is not None else None, gamma.data_ptr(), float(eps), H,
-                              out.data_ptr(), residual_out.data_ptr() if residual_out is not None else None)
+        self._parts = (C.c_void_p * self.R)(*[_lib._dev(p, 2 * rows * H, "part") for p in parts])
+        self.norm = _norm_args(gamma, out, residual, residual_out, eps, H, rows * H)
 
     def run(self, max_workgroups: int = 0, stream=None):
         st = _lib.lib.fc_reduce_rmsnorm(self._parts, self.R, self.rows, C.byref(self.norm), max_workgroups,
@@ -211,8 +224,10 @@ class LLUnpackReduce:
 
     def __init__(self, slots: list, n: int, block_slots: int, out, stale, done, counters):
         self.R, self.n, self.B = len(slots), n, block_slots
-        self._slots = (C.c_void_p * self.R)(*[s.data_ptr() for s in slots])
-        self._ptrs = (out.data_ptr(), stale.data_ptr(), done.data_ptr(), counters.data_ptr())
+        nblk = n // 2 // block_slots
+        self._slots = (C.c_void_p * self.R)(*[_lib._dev(s, 4 * n, "slots") for s in slots])
+        self._ptrs = (_lib._dev(out, 2 * n, "out"), _lib._dev(stale, self.R * nblk, "stale"),
+                      _lib._dev(done, nblk, "done"), _lib._dev(counters, 8, "counters"))
 
     def run(self, epoch: int, stream=None):
         st = _lib.lib.fc_ll_unpack_reduce(self._slots, self.R, self.n, self.B, epoch & 0xFFFFFFFF, *self._ptrs,
