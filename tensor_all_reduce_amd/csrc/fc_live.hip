@@ -116,13 +116,25 @@ __global__ __launch_bounds__(256) void k_flag_unpack(const int64_t ntiles, const
     const int per_wave = 1 << (log2_te - 11);     // 512-element instructions per wavefront and tile
     uint32_t n_stale = 0, n_pending = 0, n_polls = 0;
     int par = 0;
+    // The first wavefront reads a tile's flag words and done bytes one tile ahead: the next tile's are
+    // issued before this tile's payload loads, so their round trip overlaps this tile's payload.
+    auto flag_word = [&](int64_t b0) {
+        const int64_t qb = b0 + (q < NBW ? q : NBW - 1);
+        return qb < nblk ? qb : nblk - 1;  // this lane's flag word (clamped, always inside)
+    };
+    uint32_t f_next = 0;
+    uint8_t d_next = 1;
+    if (wave == 0 && (int64_t)blockIdx.x < ntiles) {
+        const int64_t fb = flag_word((int64_t)blockIdx.x * NBW);
+        f_next = ld_relaxed(fp + fb);
+        d_next = done[fb];
+    }
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x, par ^= 1) {  // uniform over the workgroup
         const int64_t b0 = tile * NBW;
         if (wave == 0) {
-            const int64_t qb = b0 + (q < NBW ? q : NBW - 1);
-            const int64_t fb = qb < nblk ? qb : nblk - 1;  // this lane's flag word (clamped, always inside)
-            const bool watch = q < NBW && rk < R && b0 + q < nblk && done[fb] == 0;
-            uint32_t f = ld_relaxed(fp + fb);
+            const int64_t fb = flag_word(b0);
+            const bool watch = q < NBW && rk < R && b0 + q < nblk && d_next == 0;
+            uint32_t f = f_next;
             uint64_t bad = __ballot(watch && f != epoch);
             for (int p = 0; bad != 0 && p < max_polls; ++p) {
                 __builtin_amdgcn_s_sleep(2);
@@ -143,6 +155,12 @@ __global__ __launch_bounds__(256) void k_flag_unpack(const int64_t ntiles, const
                 n_pending += ((wm >> (16 * k)) & 1u) && ((bad >> (16 * k)) & 0xffffu) ? 1u : 0u;
             // block `lane` of the tile is done when examined (its rank-0 lane watched) with no stale copy
             if (lane < NBW && ((wm >> (16 * lane)) & 1u) && ((bad >> (16 * lane)) & 0xffffu) == 0) done[b0 + lane] = 1;
+            const int64_t nt = tile + (int64_t)gridDim.x;
+            if (nt < ntiles) {  // uniform
+                const int64_t nfb = flag_word(nt * NBW);
+                f_next = ld_relaxed(fp + nfb);
+                d_next = done[nfb];
+            }
         }
         __syncthreads();
         const uint64_t bad = s_bad[par], wm = s_watch[par];

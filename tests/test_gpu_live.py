@@ -84,6 +84,34 @@ def test_flag_receiver_matches_oracle(fc, orc, be, nblk, R, polls):
     assert int(got_c[2]) == want_polls and int(got_c[3]) == 0
 
 
+
+@pytest.mark.parametrize("mw", [1, 3, 7])
+@pytest.mark.parametrize("be,nblk,R,polls", [(512, 37, 8, 3), (4096, 9, 3, 0), (2048, 40, 16, 2)])
+def test_flag_receiver_capped_grid(fc, orc, be, nblk, R, polls, mw):
+    """A grid capped below the tile count: each workgroup walks several tiles (reading the next tile's
+    flags ahead), with the same outputs, stale flags and re-read count as the oracle says."""
+    from gpu_helpers import assert_equal_bits, up
+    cfg = dg.SLOTS
+    n, e = be * nblk, 0x2A
+    xs = [dg.synth_bf16((be, R, r, mw), n) for r in range(R)]
+    fls, masks = zip(*[dg.stale_flags(cfg, r, nblk, epoch=e, p=0.15, salt=be * 100 + R + 7) for r in range(R)])
+    done0 = (np.arange(nblk) % 7 == 3).astype(np.uint8)
+    out, stale, done, cnt = _bufs(R, n, nblk, out_fill=77, done0=done0)
+    fc.fc_flag_unpack_reduce([up(x) for x in xs], [up(f) for f in fls], n, be, e, out, stale, done, cnt,
+                             max_polls=polls, max_workgroups=mw)
+    got_out, got_st, got_dn, got_c = _down_all(out, stale, done, cnt, R, nblk)
+    ro, rst, rdn, rc = orc.flag_unpack_reduce(xs, fls, n, be, e, out=np.full(n, 77, np.uint16), done=done0)
+    rst = rst.reshape(R, nblk)
+    assert_equal_bits(got_out, ro, "out")
+    assert_equal_bits(got_dn, rdn, "done")
+    assert_equal_bits(got_c[:2], rc, "counters")
+    skipped = done0.astype(bool)
+    assert np.all(got_st[:, skipped] == 0xAB), "blocks already done are not examined"
+    assert_equal_bits(got_st[:, ~skipped], rst[:, ~skipped], "stale (examined)")
+    want_polls = polls * _tiles_polled(np.stack(masks).astype(bool), done0, max(1, 2048 // be))
+    assert int(got_c[2]) == want_polls and int(got_c[3]) == 0
+
+
 @pytest.mark.parametrize("be,nblk", [(512, 45), (2048, 45), (512, 8192 + 3)])
 def test_flag_pack_round_trip(fc, orc, be, nblk):
     """The sender writes every block (shuffled order) and its flag; the receiver completes every block.
