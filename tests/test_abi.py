@@ -195,6 +195,7 @@ def test_ll_validation(L):
     assert p(X, 1, 4096, 64, 7, None, -1, S, None) == L.FC_E_ARG               # pace
     assert p(X, 1, 4096, 64, 7, None, 65537, S, None) == L.FC_E_ARG
     assert p(X, 1, 4000, 64, 7, None, 0, S, None) == L.FC_E_SHAPE
+    assert p(X, 1, 0, 64, 7, None, 0, S, None) == L.FC_OK                     # empty: no launch
     assert p(X, 1, 4096, 64, 7, None, 0, one(A + 8), None) == L.FC_E_ALIGN
     assert p(X, 1, 4096, 64, 7, None, 0, one(A + 1024), None) == L.FC_E_ARG     # slots over the input
     assert p(X, 1, 4096, 64, 7, one(A + 0x1000000 + 64), 0, S, None) == L.FC_E_ARG  # order inside the slots
@@ -254,6 +255,7 @@ def test_flag_validation(L):
     assert pk(X, 17, 8192, 1024, 7, None, 0, P, F, None) == L.FC_E_ARG
     assert pk(X, 1, 8192, 1024, 7, None, -1, P, F, None) == L.FC_E_ARG
     assert pk(X, 1, 8192 + 16, 1024, 7, None, 0, P, F, None) == L.FC_E_SHAPE
+    assert pk(X, 1, 0, 1024, 7, None, 0, P, F, None) == L.FC_OK                  # empty: no launch
     assert pk(X, 1, 8192, 1024, 7, None, 0, P, one(A + 0x2000002), None) == L.FC_E_ALIGN
     assert pk(X, 1, 8192, 1024, 7, None, 0, P, one(A + 0x1000000 + 64), None) == L.FC_E_ARG    # flags in payload
     assert pk(X, 1, 8192, 1024, 7, one(A + 0x1000000), 0, P, F, None) == L.FC_E_ARG            # order in payload
