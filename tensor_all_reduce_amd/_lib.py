@@ -87,8 +87,13 @@ def _load():
     return lib
 
 
+ABI_VERSION = 4  # the argument lists above follow include/fc.h at this FC_ABI_VERSION
+
 _lib = _load()
 lib = _lib
+if _lib.fc_abi_version() != ABI_VERSION:
+    raise ImportError(f"{LIB_PATH} has ABI version {_lib.fc_abi_version()}, this binding expects {ABI_VERSION}: "
+                      "rebuild it with `python -m tensor_all_reduce_amd.build`")
 
 
 def _dev(t, nbytes: int | None = None, what: str = "buffer") -> int | None:
