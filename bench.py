@@ -931,7 +931,7 @@ def bench_encodings(cx, fit_out=None):
     xa, xb = torch.cuda.ExternalStream(sa.cuda_stream), torch.cuda.ExternalStream(sb.cuda_stream)
     hold = [torch.empty(256 << 20, dtype=torch.uint8, device=cx.dev) for _ in range(2)]
     polls, mwg, reps = 200_000, 2 * rcu, 7
-    sizes = [16 << 10, 32 << 10, 128 << 10, 512 << 10, 2 << 20, 8 << 20, 16 << 20]
+    sizes = [16 << 10, 32 << 10, 64 << 10, 128 << 10, 256 << 10, 512 << 10, 1 << 20, 2 << 20, 4 << 20, 8 << 20, 16 << 20]
     rows, detail = [], []
     for R in (2, 4, 8):
         for S in sizes:
