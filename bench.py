@@ -55,19 +55,27 @@ def kernel_of_call(call, cfg):
             "gather_norm": f"k_rows<fc::GatherProducer<{cfg.bits_ag},"}[call]
 
 
+DEFAULT_ROWS = "decode,share,normfirst,ll,llgather,rmsnorm,layer"
+ALL_ROWS = DEFAULT_ROWS + ",warm,encodings"
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=600)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", default="llama3-8b-decode",
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 60 on the prefill, 600 else)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default steps / 10)")
+    ap.add_argument("--config", default="llama3-70b-prefill",
                     choices=["tiny-r2-t4-h256", "llama3-8b-decode", "llama3-70b-prefill"],
-                    help="headline two-step workload")
+                    help="headline two-step workload (default: the 70B prefill shard, the largest of the metric)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-resident)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rows", default="all", help="other hot-path rows to measure: all | none | comma list of "
-                                                  "prefill,warm,share,normfirst,ll,llgather,rmsnorm,layer,encodings")
+    ap.add_argument("--oracle-by-config", action="store_true",
+                    help="also time the oracle on every workload (a detail line; about a minute of CPU)")
+    ap.add_argument("--rows", default="default",
+                    help=f"other hot-path rows: default ({DEFAULT_ROWS}) | all (adds warm,encodings) | none | "
+                         "comma list")
+    ap.add_argument("--detail-out", metavar="JSON", help="also write every row's full record to this file")
     ap.add_argument("--kernel-reps", type=int, default=0, help="graph replays per call timing (0 = auto)")
     ap.add_argument("--fit-encodings", metavar="JSON", help="write the selector's fitted cost table here")
     ap.add_argument("--pmc-rows", metavar="BYTES_JSON", help="only launch the row kernels for counter runs")
@@ -76,7 +84,12 @@ def parse():
     ap.add_argument("--stats-table", nargs=4, metavar=("STATS_CSV", "OUT_MD", "TITLE", "COMMAND"))
     ap.add_argument("--profile-report", nargs=6, metavar=("WORKLOAD", "STATS_CSV", "FETCH_CSV", "WRITE_CSV", "VALU_CSV",
                                                           "OUT_MD"))
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 60 if args.config == "llama3-70b-prefill" else 600
+    if args.warmup is None:
+        args.warmup = max(1, args.steps // 10)
+    return args
 
 
 def _code_text(text: str) -> str:
@@ -430,12 +443,29 @@ def traffic_for(call, cfg, traffic):
 
 
 # ---------------------------------------------------------------------------------------------------------
+class one_core:
+    """Pins this process to one host core (the third, if there are three) while the oracle is timed, so
+    every oracle time is single-core whatever the host's scheduler does."""
+
+    def __enter__(self):
+        self.old = os.sched_getaffinity(0)
+        cpus = sorted(self.old)
+        self.core = cpus[min(2, len(cpus) - 1)]
+        os.sched_setaffinity(0, {self.core})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.old)
+        return False
+
+
 def cpu_baseline(cfg, seconds):
-    """The oracle (single-threaded C++) on the same workload, whole steps repeated for about `seconds`."""
+    """The oracle (single-threaded C++) on the same workload, pinned to one host core, whole steps
+    repeated for about `seconds`."""
     sys.path.insert(0, os.path.join(ROOT, "oracle"))
     import oracle
     from tensor_all_reduce_amd import bytes_model as bm, datagen as dg
-    if cfg.n > (1 << 22):  # the 70B prefill step takes minutes on one core: time a block of rows
+    if cfg.n > (1 << 22):  # the 70B prefill step takes seconds on one core: time a block of rows
         T = max(cfg.R, (1 << 22) // cfg.H // cfg.R * cfg.R)
         sample = f"{T} of {cfg.T} tokens x all {cfg.R} ranks, whole steps repeated"
     else:
@@ -447,16 +477,18 @@ def cpu_baseline(cfg, seconds):
     step_bytes = sum(bm.total(v) for v in bm.two_step_whole(cfg.R, T, cfg.H, cfg.bits_rs, cfg.bits_ag,
                                                              cfg.group).values())
     oracle.lib()
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.two_step(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, residual=res, gamma=gam, eps=cfg.eps,
-                        hidden=cfg.H, plain=False)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    with one_core() as pin:
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.two_step(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, residual=res, gamma=gam, eps=cfg.eps,
+                            hidden=cfg.H, plain=False)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
     return {"value": round(step_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": sample + f" {reps}x in {el:.1f} s; single-threaded C++ (g++ -O2 -ffp-contract=off)",
+            "sample": sample + f" {reps}x in {el:.1f} s; single-threaded C++ (g++ -O2 -ffp-contract=off) on host "
+                               f"core {pin.core}",
             "us_per_step": round(el / reps * 1e6, 1), "host_cpu": host_cpu_model(),
             "host_cores": os.cpu_count()}
 
@@ -483,11 +515,8 @@ def oracle_by_config(max_elems=1 << 22):
     import oracle
     from tensor_all_reduce_amd import bytes_model as bm, datagen as dg
     oracle.lib()
-    old = os.sched_getaffinity(0)
-    cpus = sorted(old)
-    os.sched_setaffinity(0, {cpus[min(2, len(cpus) - 1)]})
     out = {}
-    try:
+    with one_core():
         for cfg in dg.WORKLOADS.values():
             T = cfg.T if cfg.n <= max_elems else max(cfg.R, max_elems // cfg.H // cfg.R * cfg.R)
             n = T * cfg.H
@@ -550,8 +579,6 @@ def oracle_by_config(max_elems=1 << 22):
                 times.append(time.perf_counter() - t0)
             us = statistics.median(times) * 1e6
             out[name] = {"us_per_step": round(us, 1), "GB/s": round(by / (us * 1e-6) / 1e9, 4), "runs": 5}
-    finally:
-        os.sched_setaffinity(0, old)
     return out
 
 
@@ -1009,15 +1036,12 @@ def bench_encodings(cx, fit_out=None):
     del hold
     torch.cuda.empty_cache()
     costs = sel.fit(rows)
-    agree = 0
-    for R in (2, 4, 8):
-        for S in sizes:
-            meas = {r[0]: r[3] for r in rows if r[1] == S and r[2] == R}
-            if len(meas) == len(sel.ENCODINGS):
-                agree += sel.select(costs, S, R) == min(meas, key=meas.get)
+    refit_score = sel.regret(costs, rows)              # in sample: fitted to these latencies
+    committed = sel.regret(sel.load(), rows)          # out of sample: the table shipped in the package
     res = {"receiver_cus": rcu, "sender_cus": "the rest", "reps": reps, "points": detail,
            "model": {e: list(c.coef) for e, c in costs.items()},
-           "choice_matches_fastest_measured": f"{agree}/{len(sizes) * 3}",
+           "choice_matches_fastest_measured": f"{refit_score['fastest']}/{refit_score['points']}",
+           "refit_regret": refit_score, "committed_table": committed,
            "crossover_R8": sel.crossover(costs, 8), "crossover_R2": sel.crossover(costs, 2)}
     if fit_out:
         total = torch.cuda.get_device_properties(0).multi_processor_count
@@ -1195,7 +1219,7 @@ def main():
         print(f"bench.py: --gpus {args.gpus} is not supported: the R ranks are emulated on one GPU "
               "(inter-GPU transfers are local HBM buffers); run with --gpus 1", file=sys.stderr)
         return 2
-    from tensor_all_reduce_amd import datagen as dg
+    from tensor_all_reduce_amd import bytes_model as bm, datagen as dg
     cx = Ctx()
     cfg = dg.WORKLOADS[args.config]
     traffic = load_traffic(cfg)
@@ -1207,41 +1231,45 @@ def main():
     dom = max(per_call, key=lambda k: per_call[k]["us"])
     ceil = copy_ceiling(cx)
     copy_gbps = ceil["copy"]
-    from tensor_all_reduce_amd import bytes_model as bm
     add_mixed(per_call, bm.two_step_whole(cfg.R, cfg.T, cfg.H, cfg.bits_rs, cfg.bits_ag, cfg.group), ceil)
     tr = per_call[dom]["traffic"]
+    sp = main_r["spread"]
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": cfg.name, "R": cfg.R, "T": cfg.T, "H": cfg.H, "bits_rs": cfg.bits_rs,
-                   "bits_ag": cfg.bits_ag, "group": cfg.group, "mode": "whole emulated all-reduce on one GPU",
+                   "bits_ag": cfg.bits_ag, "group": cfg.group, "mode": "W: whole emulated all-reduce on one GPU",
                    "cache": "warm" if args.warm else "cold", "buffer_sets": main_r["nsets"],
                    "launch": "hip graph, 3 kernels per step"},
-        "us_per_step": round(ms_step * 1e3, 3), "us_per_step_spread": main_r["spread"],
+        "us_per_step": round(ms_step * 1e3, 3), "us_spread_p10_p50_p90": [sp["p10"], sp["p50"], sp["p90"]],
         "bytes_per_step": main_r["step_bytes"],
-        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "copy_ceiling_GBps": round(copy_gbps, 1), "pct_copy_ceiling": round(100 * value / copy_gbps, 2),
-        "read_ceiling_GBps": round(ceil["read"], 1), "write_ceiling_GBps": round(ceil["write"], 1),
-        "calls": per_call,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": per_call[dom]["GB/s"], "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": per_call[dom]["frac_hbm"],
-                     "traffic": tr["total"] if tr else None},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2), "pct_copy_ceiling": round(100 * value / copy_gbps, 2),
+        "ceilings_GBps": {k: round(v, 1) for k, v in ceil.items()},
+        "calls": {k: {"us": v["us"], "GBps": v["GB/s"], "frac": v["frac_hbm"], "pct_mix": v.get("pct_mixed_ceiling")}
+                  for k, v in per_call.items()},
+        "roofline": {"bound": "hbm", "kernel": dom + (f" ({tr['kernel'].split('(')[0].replace('void ', '')})"
+                                                      if tr else ""),
+                     "achieved": per_call[dom]["GB/s"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": per_call[dom]["frac_hbm"], "traffic": tr["total"] if tr else None,
+                     "algorithmic_bytes": per_call[dom]["bytes"]},
         "wall_s": round(main_r["wall"], 3),
     }
-    rows = {"prefill", "warm", "ll", "llgather", "rmsnorm", "share", "normfirst", "layer", "encodings"} if args.rows == "all" \
-        else set() if args.rows == "none" \
-        else set(args.rows.split(","))
+    rows = set(DEFAULT_ROWS.split(",")) if args.rows == "default" else set(ALL_ROWS.split(",")) \
+        if args.rows == "all" else set() if args.rows == "none" else set(args.rows.split(","))
+    other = dg.DECODE_8B if cfg is dg.PREFILL_70B else dg.PREFILL_70B
     extra = {}
-    if "prefill" in rows and cfg is not dg.PREFILL_70B:
-        c3 = dg.PREFILL_70B
-        r3 = bench_two_step(cx, c3, 30, 5, False, 0, load_traffic(c3))
-        v3 = r3["step_bytes"] / (r3["ms_step"] * 1e-3) / 1e9
-        extra["prefill_two_step"] = {"workload": c3.name, "us_per_step": round(r3["ms_step"] * 1e3, 2),
-                                     "us_per_step_spread": r3["spread"],
-                                     "GB/s": round(v3, 1), "pct_hbm_peak": round(100 * v3 / HBM_PEAK_GBPS, 2),
-                                     "pct_copy_ceiling": round(100 * v3 / copy_gbps, 2), "calls": r3["per_call"]}
-        add_mixed(r3["per_call"], bm.two_step_whole(c3.R, c3.T, c3.H, c3.bits_rs, c3.bits_ag, c3.group), ceil)
+    if "decode" in rows or "prefill" in rows:
+        so = 600 if other is dg.DECODE_8B else 30
+        ro = bench_two_step(cx, other, so, so // 10, False, 0, load_traffic(other))
+        add_mixed(ro["per_call"], bm.two_step_whole(other.R, other.T, other.H, other.bits_rs, other.bits_ag,
+                                                    other.group), ceil)
+        vo = ro["step_bytes"] / (ro["ms_step"] * 1e-3) / 1e9
+        extra[f"two_step_{other.slug}"] = {"workload": other.name, "us_per_step": round(ro["ms_step"] * 1e3, 3),
+                                           "us_per_step_spread": ro["spread"], "GB/s": round(vo, 1),
+                                           "pct_hbm_peak": round(100 * vo / HBM_PEAK_GBPS, 2),
+                                           "pct_copy_ceiling": round(100 * vo / copy_gbps, 2),
+                                           "calls": ro["per_call"]}
     if "warm" in rows and not args.warm:
         # context, not the headline: inputs already in the caches, as right after the GEMM that produced them
         rw = bench_two_step(cx, cfg, args.steps, args.warmup, True, args.kernel_reps, None)
@@ -1250,20 +1278,19 @@ def main():
                                 "us_per_step": round(rw["ms_step"] * 1e3, 3), "GB/s": round(vw, 1),
                                 "calls": {k: v["us"] for k, v in rw["per_call"].items()}}
     if "share" in rows:
-        extra["share_decode"] = bench_share(cx, cfg, args.steps, args.warmup, args.kernel_reps)
-        if cfg is not dg.PREFILL_70B:
-            extra["share_prefill"] = bench_share(cx, dg.PREFILL_70B, 30, 5, 0)
+        for c in (dg.PREFILL_70B, dg.DECODE_8B):
+            st = 30 if c is dg.PREFILL_70B else 600
+            extra[f"share_{c.slug}"] = bench_share(cx, c, st, st // 10, 0)
     if "normfirst" in rows:
-        for c, tag, st, wu in ((cfg, "decode", min(args.steps, 300), 20), (dg.PREFILL_70B, "prefill", 30, 5)):
-            if tag == "prefill" and cfg is dg.PREFILL_70B:
-                continue
-            rw = bench_two_step(cx, c, st, wu, False, 0, None, norm_first=True)
+        for c in (dg.PREFILL_70B, dg.DECODE_8B):
+            st = 30 if c is dg.PREFILL_70B else 300
+            rw = bench_two_step(cx, c, st, st // 10, False, 0, None, norm_first=True)
             vw = rw["step_bytes"] / (rw["ms_step"] * 1e-3) / 1e9
-            extra[f"norm_first_{tag}"] = {
+            extra[f"norm_first_{c.slug}"] = {
                 "workload": c.name, "mode": "whole emulated all-reduce, norm before the all-gather",
                 "us_per_step": round(rw["ms_step"] * 1e3, 3), "GB/s": round(vw, 1),
                 "pct_hbm_peak": round(100 * vw / HBM_PEAK_GBPS, 2), "calls": rw["per_call"],
-                "share": bench_share(cx, c, st, wu, 0, norm_first=True)}
+                "share": bench_share(cx, c, st, st // 10, 0, norm_first=True)}
     if "ll" in rows:
         extra["self_sync_slots"] = bench_ll(cx)
     if "llgather" in rows:
@@ -1289,13 +1316,64 @@ def main():
         a = bm.reduce_rmsnorm(c5.R, c5.splits[0], c5.H, True, True)
         r["both_halves_pct_mixed_ceiling"] = round(
             100 * 2 * mixed_ceiling_us(a["read"], a["write"], ceil) / r["both_halves_us"], 1)
-    if extra:
-        line["rows"] = extra
+    detail = {"headline_calls": per_call, "headline_spread": sp, "rows": extra}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
-        line["cpu_baseline"]["oracle_by_config"] = oracle_by_config()
+        if args.oracle_by_config:
+            detail["oracle_by_config"] = oracle_by_config()
+    line["rows"] = row_summary(extra)
+    # the full records first, one line each (the last line is the compact headline record)
+    for k, v in detail.items():
+        print(json.dumps({"detail": k, "record": v}), flush=True)
+    if args.detail_out:
+        with open(args.detail_out, "w") as fh:
+            json.dump(detail, fh, indent=1)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def _pct(gbps):
+    return round(100 * gbps / HBM_PEAK_GBPS, 1)
+
+
+def row_summary(extra: dict) -> dict:
+    """One short entry per measured row for the headline record: microseconds, effective GB/s (algorithmic
+    bytes / time) and % of the 8 TB/s HBM peak."""
+    out = {}
+    for k, r in extra.items():
+        if k.startswith("two_step_"):
+            out[k] = {"us": round(r["us_per_step"], 2), "GBps": r["GB/s"], "pct": _pct(r["GB/s"]),
+                      "calls_us": [round(c["us"], 2) for c in r["calls"].values()]}
+        elif k.startswith("share_"):
+            out[k] = {"mode": "P", "us": round(r["us_per_step"], 2), "GBps": r["GB/s"], "pct": _pct(r["GB/s"]),
+                      "calls_us": [round(c["us"], 2) for c in r["calls"].values()]}
+        elif k.startswith("norm_first_"):
+            sh = r["share"]
+            out[k] = {"us": round(r["us_per_step"], 2), "GBps": r["GB/s"], "pct": _pct(r["GB/s"]),
+                      "P_us": round(sh["us_per_step"], 2), "P_GBps": sh["GB/s"], "P_pct": _pct(sh["GB/s"])}
+        elif k == "self_sync_slots":
+            out[k] = {"pass1_us": r["pass1_us"], "GBps": r["pass1_GB/s"], "pct": _pct(r["pass1_GB/s"]),
+                      "retry_us": r["retry_us"], "pending": r["pending_blocks"]}
+            if "pass1_nocount_us" in r:
+                out[k].update(nocount_us=r["pass1_nocount_us"], nocount_pct=_pct(r["pass1_nocount_GB/s"]))
+        elif k == "self_sync_allgather":
+            for tag, g in r["by_payload"].items():
+                out[f"allgather_{tag}"] = {"pass1_us": g["pass1_us"], "GBps": g["pass1_GB/s"],
+                                           "pct": _pct(g["pass1_GB/s"]), "retry_us": g["retry_us"]}
+        elif k == "tokenweave_reduce_rmsnorm":
+            ov = r["max_workgroups_sweep"].get("rows", {})
+            out[k] = {"both_halves_us": r["both_halves_us"], "GBps": r["both_halves_GB/s"],
+                      "pct": _pct(r["both_halves_GB/s"]), "overlap_makespan_us": ov.get("overlap_makespan_us"),
+                      "serial_us": ov.get("serial_us")}
+        elif k == "two_half_layer":
+            t = r["by_T"].get("8192", {})
+            out[k] = {"T": 8192, "pipelined_us": t.get("pipelined_us"), "serial_us": t.get("serial_halves_us"),
+                      "unsplit_us": t.get("unsplit_us")}
+        elif k == "readiness_encodings":
+            out[k] = {"agree": r["choice_matches_fastest_measured"], "committed_regret": r.get("committed_table")}
+        elif k == "warm_caches":
+            out[k] = {"us": r["us_per_step"], "GBps": r["GB/s"]}
+    return out
 
 
 if __name__ == "__main__":

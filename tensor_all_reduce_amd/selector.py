@@ -122,6 +122,28 @@ def crossover(costs: dict[str, EncodingCost], R: int, lo: int = 1 << 10, hi: int
     return out
 
 
+def regret(costs: dict[str, EncodingCost], rows) -> dict:
+    """How much the choice of `costs` loses against the fastest encoding measured, over the (S, R) points of
+    `rows` ((enc, S, R, t_us) tuples) where every encoding was measured: the number of points, how many
+    chose the fastest, and the mean and largest loss in % of the fastest latency.  Scoring a stored table
+    on latencies it was not fitted to tells how well it carries to another run or machine."""
+    pts = {}
+    for enc, S, R, t in rows:
+        pts.setdefault((int(S), int(R)), {})[enc] = float(t)
+    losses, hits = [], 0
+    for (S, R), meas in sorted(pts.items()):
+        if any(e not in meas for e in ENCODINGS if e in costs):
+            continue
+        best = min(meas.values())
+        t = meas[select(costs, S, R, allowed=set(meas))]
+        hits += t == best
+        losses.append(100.0 * (t / best - 1.0))
+    if not losses:
+        return {"points": 0, "fastest": 0, "mean_pct": None, "max_pct": None}
+    return {"points": len(losses), "fastest": hits, "mean_pct": round(sum(losses) / len(losses), 2),
+            "max_pct": round(max(losses), 2)}
+
+
 MODEL = "t_us = max(a + b*R, d + (c*R + e)*wire_bytes); coefficients [a, b, c, d, e]"
 
 

@@ -136,3 +136,27 @@ def test_self_sync_reduce_refuses_epochs_its_inbox_already_carries():
             SelfSyncReduce._check_epoch(bad)
     SelfSyncReduce._check_epoch(1)
     SelfSyncReduce._check_epoch((1 << 32) - 1)
+
+
+def test_regret_scores_a_table_on_latencies_it_was_not_fitted_to():
+    """regret(): hand-built latencies where the closed-form choice is known.  Two points, four encodings; at
+    the first the table's choice is the fastest (0% loss), at the second it picks an encoding 25% slower
+    than the fastest.  Points where an encoding is missing are skipped."""
+    costs = {e: sel.EncodingCost(e, c) for e, c in (("ll", (1.0, 0, 0, 0, 0)), ("flag512", (2.0, 0, 0, 0, 0)),
+                                                    ("flag2048", (3.0, 0, 0, 0, 0)), ("flag8192", (4.0, 0, 0, 0, 0)))}
+    rows = [("ll", 1024, 2, 10.0), ("flag512", 1024, 2, 12.0), ("flag2048", 1024, 2, 13.0), ("flag8192", 1024, 2, 14.0),
+            ("ll", 4096, 8, 20.0), ("flag512", 4096, 8, 16.0), ("flag2048", 4096, 8, 17.0), ("flag8192", 4096, 8, 18.0),
+            ("ll", 8192, 8, 5.0)]
+    r = sel.regret(costs, rows)
+    assert r == {"points": 2, "fastest": 1, "mean_pct": 12.5, "max_pct": 25.0}
+    assert sel.regret(costs, rows[-1:]) == {"points": 0, "fastest": 0, "mean_pct": None, "max_pct": None}
+
+
+@pytest.mark.skipif(not os.path.exists(sel.DEFAULT_TABLE), reason="no measured table committed")
+def test_regret_of_the_committed_table_on_its_own_measurements():
+    """The committed table scored by regret() on the latencies stored with it: the same bound as the test
+    above, computed by the function the benchmark uses on fresh measurements."""
+    import json
+    doc = json.load(open(sel.DEFAULT_TABLE))
+    r = sel.regret(sel.load(), [tuple(x) for x in doc["measured"]])
+    assert r["points"] >= 10 and r["max_pct"] <= 10.0 and r["mean_pct"] <= 1.0, r
