@@ -133,6 +133,13 @@ def _check(st: int, where: str):
         raise FcError(st, where)
 
 
+def _count(lst, want: int, what: str, per: str) -> None:
+    """The C side reads exactly `want` entries of a host pointer array; a shorter list would make it read
+    past the array and launch with garbage device addresses, so the lengths are checked here."""
+    if len(lst) != want:
+        raise ValueError(f"{what}: {len(lst)} entries, the call reads {want} ({per})")
+
+
 def _qmsg(m, n: int = 0, bits: int = 8, group: int = 1, what: str = "message") -> QMsg:
     """A quantized message of n elements: n*bits/8 bytes of codes, a 4-byte word per group."""
     codes, meta = m
@@ -161,6 +168,7 @@ def fc_quantize(x, bits: int, group: int, codes, meta, n: int | None = None, str
 def fc_reduce_shard(inputs, R: int, L: int, bits_in: int, bits_out: int, group: int, outputs, stream=None) -> None:
     """inputs: n_shards*R (codes, meta) pairs, [shard][rank]; outputs: n_shards (codes, meta) pairs."""
     n_shards = len(outputs)
+    _count(inputs, n_shards * R, "inputs", f"{n_shards} shards x R={R}")
     ins = (QMsg * len(inputs))(*[_qmsg(m, L, bits_in, group, "input") for m in inputs])
     outs = (QMsg * n_shards)(*[_qmsg(m, L, bits_out, group, "output") for m in outputs])
     _check(_lib.fc_reduce_shard(ins, R, L, n_shards, bits_in, bits_out, group, outs, _stream(stream)),
@@ -173,6 +181,7 @@ def fc_reduce_shard_norm(inputs, R: int, L: int, bits_in: int, bits_out: int, gr
     normalized rows are quantized into `outputs`.  norm: dict(residual, gamma, eps, hidden, residual_out)
     over the n_shards*L elements of the shards, without "out"."""
     n_shards = len(outputs)
+    _count(inputs, n_shards * R, "inputs", f"{n_shards} shards x R={R}")
     ins = (QMsg * len(inputs))(*[_qmsg(m, L, bits_in, group, "input") for m in inputs])
     outs = (QMsg * n_shards)(*[_qmsg(m, L, bits_out, group, "output") for m in outputs])
     nm = _norm(norm, n_shards * L)
@@ -211,6 +220,7 @@ def fc_ll_unpack_reduce(slots, n: int, block_slots: int, epoch: int, out, stale,
 def fc_ll_gather(slots, nwords: int, block_slots: int, epoch: int, out, stale, done, counters, stream=None) -> None:
     """slots: R uint64 slot buffers; out: R uint32 (or any 4-byte) destination buffers."""
     R = len(slots)
+    _count(out, R, "out", "one per rank's slots")
     nw = max(0, nwords)
     nblk = nw // max(1, block_slots)
     sa = (C.c_void_p * R)(*[_dev(s, 8 * nw, "slots") for s in slots])
@@ -233,6 +243,9 @@ def fc_ll_pack(x, block_slots: int, epoch: int, slots, block_order=None, n: int 
                stream=None) -> None:
     """x, slots, block_order: one tensor each (one rank) or lists of R (R peers in one launch)."""
     xs, ss = _ranks(x), _ranks(slots)
+    _count(ss, len(xs), "slots", "one per rank's x")
+    if block_order is not None:
+        _count(_ranks(block_order), len(xs), "block_order", "one per rank's x")
     n = xs[0].numel() if n is None else n
     nn = max(0, n)
     oa = None if block_order is None else _ptrs(_ranks(block_order), 4 * (nn // 2 // max(1, block_slots)),
@@ -258,6 +271,7 @@ def fc_flag_unpack_reduce(payload, flags, n: int, block_elems: int, epoch: int, 
                           max_polls: int = 0, max_workgroups: int = 0, stream=None) -> None:
     """payload: R bf16 (int16) buffers; flags: R int32 buffers of n / block_elems words; counters: 4 int32."""
     R = len(payload)
+    _count(flags, R, "flags", "one per rank's payload")
     nn = max(0, n)
     nblk = nn // max(1, block_elems)
     pa = (C.c_void_p * R)(*[_dev(p, 2 * nn, "payload") for p in payload])
@@ -272,6 +286,10 @@ def fc_flag_pack(x, block_elems: int, epoch: int, payload, flags, block_order=No
                  pace: int = 0, stream=None) -> None:
     """x, payload, flags, block_order: one tensor each (one rank) or lists of R (R peers in one launch)."""
     xs = _ranks(x)
+    _count(_ranks(payload), len(xs), "payload", "one per rank's x")
+    _count(_ranks(flags), len(xs), "flags", "one per rank's x")
+    if block_order is not None:
+        _count(_ranks(block_order), len(xs), "block_order", "one per rank's x")
     n = xs[0].numel() if n is None else n
     nn = max(0, n)
     nblk = nn // max(1, block_elems)

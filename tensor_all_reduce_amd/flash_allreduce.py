@@ -32,9 +32,14 @@ def _device(device) -> torch.device:
 
 
 def _norm_args(gamma, out, residual, residual_out, eps: float, H: int, elems: int) -> _lib.Norm:
-    """Checked epilogue arguments: residual, out and residual_out cover `elems` bf16 elements."""
-    return _lib.Norm(_lib._dev(residual, 2 * elems, "residual"), _lib._dev(gamma, 2 * H, "gamma"), float(eps), H,
-                     _lib._dev(out, 2 * elems, "out"), _lib._dev(residual_out, 2 * elems, "residual_out"))
+    """Checked epilogue arguments: residual, out and residual_out cover `elems` bf16 elements.  The returned
+    structure holds raw device addresses, so it also keeps the tensors themselves (``_keep``): a temporary
+    passed here stays allocated as long as the structure, and its memory cannot be handed to another
+    tensor before the epilogue reads or writes it."""
+    nm = _lib.Norm(_lib._dev(residual, 2 * elems, "residual"), _lib._dev(gamma, 2 * H, "gamma"), float(eps), H,
+                   _lib._dev(out, 2 * elems, "out"), _lib._dev(residual_out, 2 * elems, "residual_out"))
+    nm._keep = (gamma, out, residual, residual_out)
+    return nm
 
 
 def bf16_buffer(n: int, device) -> torch.Tensor:
@@ -95,6 +100,8 @@ class TwoStepAllReduce:
         if shard is None:
             ins, outs, ns = self._rs_in, self._rs_out, R
         else:
+            if not 0 <= int(shard) < R:
+                raise ValueError(f"shard {shard}: the all-reduce has shards 0 .. {R - 1}")
             qs = C.sizeof(_lib.QMsg)
             ins = C.cast(C.addressof(self._rs_in) + qs * shard * R, C.POINTER(_lib.QMsg))
             outs = C.cast(C.addressof(self._rs_out) + qs * shard, C.POINTER(_lib.QMsg))
@@ -211,6 +218,7 @@ class ReduceRMSNorm:
     def __init__(self, parts: list, rows: int, H: int, gamma, out, residual=None, residual_out=None, eps=1e-5):
         self.R, self.rows, self.H = len(parts), rows, H
         self._parts = (C.c_void_p * self.R)(*[_lib._dev(p, 2 * rows * H, "part") for p in parts])
+        self._keep = list(parts)  # the table holds raw addresses: keep the tensors allocated with it
         self.norm = _norm_args(gamma, out, residual, residual_out, eps, H, rows * H)
 
     def run(self, max_workgroups: int = 0, stream=None):
@@ -228,6 +236,7 @@ class LLUnpackReduce:
         self._slots = (C.c_void_p * self.R)(*[_lib._dev(s, 4 * n, "slots") for s in slots])
         self._ptrs = (_lib._dev(out, 2 * n, "out"), _lib._dev(stale, self.R * nblk, "stale"),
                       _lib._dev(done, nblk, "done"), _lib._dev(counters, 8, "counters"))
+        self._keep = (list(slots), out, stale, done, counters)  # raw addresses above: keep the tensors
 
     def run(self, epoch: int, stream=None):
         st = _lib.lib.fc_ll_unpack_reduce(self._slots, self.R, self.n, self.B, epoch & 0xFFFFFFFF, *self._ptrs,

@@ -37,3 +37,63 @@ def test_helpers_refuse_host_buffers():
         TwoStepAllReduce(2, 4, 256, 8, 8, 32, device="cpu")
     with pytest.raises(ValueError, match="device memory"):
         TwoStepShare(2, 4, 256, 8, 8, 32, device="cpu")
+
+
+def test_pointer_lists_must_have_the_lengths_the_call_reads(L):
+    """The C side reads n_shards*R inputs, R outputs per rank list and so on from host pointer arrays; a
+    short list is refused before the call (the addresses here are ints that no kernel ever sees)."""
+    m = (1 << 20, 1 << 21)  # (codes, meta) device addresses that are never dereferenced
+    a = 1 << 22
+    with pytest.raises(ValueError, match="inputs: 3 entries, the call reads 4"):
+        L.fc_reduce_shard([m] * 3, 2, 1024, 8, 8, 128, [m] * 2)
+    with pytest.raises(ValueError, match="inputs: 5 entries, the call reads 4"):
+        L.fc_reduce_shard_norm([m] * 5, 2, 1024, 8, 8, 128, dict(gamma=a, hidden=256), [m] * 2)
+    with pytest.raises(ValueError, match="out: 1 entries, the call reads 2"):
+        L.fc_ll_gather([a, a], 64, 64, 1, [a], a, a, a)
+    with pytest.raises(ValueError, match="slots: 1 entries, the call reads 2"):
+        L.fc_ll_pack([a, a], 64, 1, [a], n=1024)
+    with pytest.raises(ValueError, match="block_order: 1 entries, the call reads 2"):
+        L.fc_ll_pack([a, a], 64, 1, [a, a], block_order=[a], n=1024)
+    with pytest.raises(ValueError, match="flags: 3 entries, the call reads 2"):
+        L.fc_flag_unpack_reduce([a, a], [a, a, a], 1024, 512, 1, a, a, a, a)
+    with pytest.raises(ValueError, match="payload: 1 entries, the call reads 2"):
+        L.fc_flag_pack([a, a], 512, 1, [a], [a, a], n=1024)
+    with pytest.raises(ValueError, match="flags: 1 entries, the call reads 2"):
+        L.fc_flag_pack([a, a], 512, 1, [a, a], [a], n=1024)
+
+
+def test_one_shard_index_is_range_checked():
+    """TwoStepAllReduce.reduce_scatter(shard) offsets into its argument table: a shard outside [0, R) is
+    refused before any pointer arithmetic (checked without building the object's device buffers)."""
+    from tensor_all_reduce_amd.flash_allreduce import TwoStepAllReduce
+    p = TwoStepAllReduce.__new__(TwoStepAllReduce)
+    p.R = 4
+    for bad in (-1, 4, 9):
+        with pytest.raises(ValueError, match="shards 0 .. 3"):
+            p.reduce_scatter(bad)
+
+
+def test_epilogue_arguments_keep_their_tensors():
+    """The epilogue structure holds raw addresses; it keeps the tensors it was built from, so temporaries
+    passed to it stay allocated (checked with weak references; ints stand in for nothing here)."""
+    import gc
+    import weakref
+
+    from tensor_all_reduce_amd import flash_allreduce as fa
+
+    class Buf:  # stands in for a device tensor: _dev takes its address from an int subclass
+        pass
+    objs = [Buf() for _ in range(4)]
+    refs = [weakref.ref(o) for o in objs]
+    orig = fa._lib._dev
+    fa._lib._dev = lambda t, nbytes=None, what="": None if t is None else 1 << 20
+    try:
+        nm = fa._norm_args(objs[0], objs[1], objs[2], objs[3], 1e-5, 256, 1024)
+    finally:
+        fa._lib._dev = orig
+    del objs
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    del nm
+    gc.collect()
+    assert all(r() is None for r in refs)

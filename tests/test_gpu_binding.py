@@ -50,3 +50,33 @@ def test_slot_receiver_checks_every_buffer():
     _lib.fc_ll_unpack_reduce(slots, n, B, 1, out, stale, done, cnt)  # epoch 1 against zero slots: all stale
     torch.cuda.synchronize()
     assert int(cnt[1]) == nblk and int(done.sum()) == 0
+
+
+def test_temporaries_passed_to_the_epilogue_stay_allocated():
+    """make_norm with temporaries (gamma and residual uploaded inline), then new device buffers allocated
+    and filled before the step runs: the epilogue must still read the residual and gamma it was given
+    (the structure keeps them), which the oracle's output checks."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from gpu_helpers import assert_bf16_close, assert_equal_bits, down, sync, up
+    from tensor_all_reduce_amd import datagen as dg
+    from tensor_all_reduce_amd.flash_allreduce import TwoStepAllReduce
+    cfg = dg.DECODE_8B
+    parts = dg.partials(cfg)
+    res, gam = dg.residual(cfg), dg.gamma(cfg)
+    p = TwoStepAllReduce(cfg.R, cfg.T, cfg.H, cfg.bits_rs, cfg.bits_ag, cfg.group, parts=up(np.stack(parts)))
+    out = torch.empty(cfg.n, dtype=torch.int16, device="cuda")
+    rout = torch.empty(cfg.n, dtype=torch.int16, device="cuda")
+    norm = p.make_norm(up(gam), out, residual=up(res), residual_out=rout, eps=cfg.eps)
+    # allocations of the same sizes, filled with other values, before the step
+    junk = [torch.full((cfg.n,), 0x3F80, dtype=torch.int16, device="cuda"),
+            torch.full((cfg.H,), -1, dtype=torch.int16, device="cuda")]
+    p.run(norm=norm)
+    sync()
+    ref = oracle.two_step(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, residual=res, gamma=gam, eps=cfg.eps,
+                          hidden=cfg.H)
+    assert_equal_bits(down(rout, np.uint16), ref["residual_out"], "residual_out")
+    assert_bf16_close(down(out, np.uint16), ref["out"], 2, "out")
+    del junk
