@@ -232,6 +232,17 @@ void dequant_f32(const uint8_t* codes, const uint32_t* meta, int64_t n, int bits
 // the product taken in fp32 before the single rounding to bf16, gamma applied last.
 // ---------------------------------------------------------------------------------------------------
 
+// Sum of squares of a row as the plain reading of the epilogue has it: the left fold of fl(h_j * h_j) over
+// j = 0 .. H-1 (each square rounded, then added; no fused multiply-add).
+float sumsq_seq(const float* h, int64_t hidden) {
+    float ss = 0.0f;
+    for (int64_t j = 0; j < hidden; ++j) {
+        const float sq = h[j] * h[j];
+        ss = ss + sq;
+    }
+    return ss;
+}
+
 void rmsnorm_row(const float* y, const uint16_t* residual, const uint16_t* gamma, float eps, int64_t hidden,
                  uint16_t* out, uint16_t* residual_out, float* hbuf) {
     for (int64_t j = 0; j < hidden; ++j) {
@@ -241,11 +252,7 @@ void rmsnorm_row(const float* y, const uint16_t* residual, const uint16_t* gamma
     }
     if (residual_out)
         for (int64_t j = 0; j < hidden; ++j) residual_out[j] = bf16_rne(hbuf[j]);
-    float ss = 0.0f;
-    for (int64_t j = 0; j < hidden; ++j) {
-        const float sq = hbuf[j] * hbuf[j];
-        ss = ss + sq;
-    }
+    const float ss = sumsq_seq(hbuf, hidden);
     const float ms = ss / (float)hidden;
     const float rinv = 1.0f / std::sqrt(ms + eps);
     for (int64_t j = 0; j < hidden; ++j) {
@@ -256,13 +263,15 @@ void rmsnorm_row(const float* y, const uint16_t* residual, const uint16_t* gamma
 }
 
 // ---------------------------------------------------------------------------------------------------
-// Sum of squares of a row in a fixed order, for the variant that normalizes the reduce-scattered shard
-// before the all-gather (TokenWeave, abstract: RMSNorm fused with, and moved relative to, the
-// communication).  There the normalized values are quantized, so the integer codes depend on the exact
-// fp32 sum and both sides must add in the same order; the pages fix no order.  reading: chunk c is
-// elements [8c, 8c+8) of the row; its partial p_c is the left fold of fl(h*h) over its 8 elements; the
-// row sum is the pairwise tree over p_0 .. p_{m-1}, m = the chunk count rounded up to a power of two,
-// absent chunks 0: level 0 = p, level k+1 [i] = level k [2i] + level k [2i+1].
+// Sum of squares of a row in the tree order of the kernels' reproducibility contract, for the variant
+// that normalizes the reduce-scattered shard before the all-gather (TokenWeave, abstract: RMSNorm fused
+// with, and moved relative to, the communication).  The plain reading of that variant sums the squares
+// as the epilogue does (sumsq_seq above); the pages fix no order, and the normalized values decide
+// integer codes, so the GPU commits to one fixed order of its own, independent of its launch shape, and
+// this function restates that order so that the kernels' other steps can be checked bit for bit: chunk
+// c is elements [8c, 8c+8) of the row; its partial p_c is the left fold of fl(h*h) over its 8 elements;
+// the row sum is the pairwise tree over p_0 .. p_{m-1}, m = the chunk count rounded up to a power of
+// two, absent chunks 0: level 0 = p, level k+1 [i] = level k [2i] + level k [2i+1].
 // ---------------------------------------------------------------------------------------------------
 float sumsq_tree(const float* h, int64_t hidden) {
     const int64_t nch = hidden / 8;
@@ -283,10 +292,11 @@ float sumsq_tree(const float* h, int64_t hidden) {
 }
 
 // Normalized rows in fp32, for quantization: h = y + residual, residual_out = bf16(h),
-// r = 1/sqrt(sumsq_tree(h)/H + eps), o = fl(fl(h * r) * gamma) (not rounded to bf16: the next step
-// quantizes it, as the all-gather payload is quantized from fp32 sums in the other variant).
+// r = 1/sqrt(ss/H + eps) with ss = sumsq_seq(h) (order 0, the plain reading) or sumsq_tree(h) (order 1),
+// o = fl(fl(h * r) * gamma) (not rounded to bf16: the next step quantizes it, as the all-gather payload
+// is quantized from fp32 sums in the other variant).
 void norm_row_f32(const float* y, const uint16_t* residual, const uint16_t* gamma, float eps, int64_t hidden,
-                  float* o, uint16_t* residual_out, float* hbuf) {
+                  int order, float* o, uint16_t* residual_out, float* hbuf) {
     for (int64_t j = 0; j < hidden; ++j) {
         float h = y[j];
         if (residual) h = h + bf16_val(residual[j]);
@@ -294,7 +304,7 @@ void norm_row_f32(const float* y, const uint16_t* residual, const uint16_t* gamm
     }
     if (residual_out)
         for (int64_t j = 0; j < hidden; ++j) residual_out[j] = bf16_rne(hbuf[j]);
-    const float ss = sumsq_tree(hbuf, hidden);
+    const float ss = order == 1 ? sumsq_tree(hbuf, hidden) : sumsq_seq(hbuf, hidden);
     const float ms = ss / (float)hidden;
     const float rinv = 1.0f / std::sqrt(ms + eps);
     for (int64_t j = 0; j < hidden; ++j) {
@@ -412,27 +422,28 @@ void or_two_step(const uint16_t* const* parts, int R, int64_t n, int bits1, int 
 // ---- norm before the all-gather (TokenWeave, abstract) ---------------------------------------------------
 // The fixed-order sum of squares of one row (exposed for the tests).
 float or_sumsq_tree(const float* h, int64_t hidden) { return sumsq_tree(h, hidden); }
+float or_sumsq_seq(const float* h, int64_t hidden) { return sumsq_seq(h, hidden); }
 
-// fp32 normalized rows (norm_row_f32) of y [rows*hidden].
+// fp32 normalized rows (norm_row_f32, order 0 plain or 1 tree) of y [rows*hidden].
 void or_norm_rows_f32(const float* y, const uint16_t* residual, const uint16_t* gamma, float eps, int64_t rows,
-                      int64_t hidden, float* o, uint16_t* residual_out) {
+                      int64_t hidden, int order, float* o, uint16_t* residual_out) {
     std::vector<float> h(hidden);
     for (int64_t t = 0; t < rows; ++t)
-        norm_row_f32(y + t * hidden, residual ? residual + t * hidden : nullptr, gamma, eps, hidden, o + t * hidden,
-                     residual_out ? residual_out + t * hidden : nullptr, h.data());
+        norm_row_f32(y + t * hidden, residual ? residual + t * hidden : nullptr, gamma, eps, hidden, order,
+                     o + t * hidden, residual_out ? residual_out + t * hidden : nullptr, h.data());
 }
 
 // One shard, norm first: S = the fixed-order fold of the R dequantized chunks (as or_reduce_shard); the
 // shard holds whole rows (L % hidden == 0); h = S + residual (the shard's rows), residual_out = bf16(h),
 // o = the normalized rows (norm_row_f32), quantized at bits_out for the all-gather.  o_out (may be NULL)
-// receives o.
+// receives o.  order: the sum of squares' order (0 plain, 1 tree; norm_row_f32).
 void or_reduce_norm_quant(const uint8_t* const* codes, const uint32_t* const* meta, int R, int64_t L, int bits_in,
                           int bits_out, int group, const uint16_t* residual, const uint16_t* gamma, float eps,
-                          int64_t hidden, uint16_t* residual_out, uint8_t* out_codes, uint32_t* out_meta,
+                          int64_t hidden, int order, uint16_t* residual_out, uint8_t* out_codes, uint32_t* out_meta,
                           float* o_out) {
     std::vector<float> S(L), o(L);
     or_reduce_shard(codes, meta, R, L, bits_in, bits_out, group, S.data(), nullptr, nullptr);
-    or_norm_rows_f32(S.data(), residual, gamma, eps, L / hidden, hidden, o.data(), residual_out);
+    or_norm_rows_f32(S.data(), residual, gamma, eps, L / hidden, hidden, order, o.data(), residual_out);
     if (o_out) std::memcpy(o_out, o.data(), sizeof(float) * L);
     quantize_f32(o.data(), L, bits_out, group, out_codes, out_meta);
 }
@@ -442,7 +453,7 @@ void or_reduce_norm_quant(const uint8_t* const* codes, const uint32_t* const* me
 // codes2/meta2 as in or_two_step), then the gather: y = bf16(dequant) of the normalized rows.
 void or_two_step_normfirst(const uint16_t* const* parts, int R, int64_t n, int bits1, int bits2, int group,
                            uint8_t* codes1, uint32_t* meta1, uint8_t* codes2, uint32_t* meta2,
-                           const uint16_t* residual, const uint16_t* gamma, float eps, int64_t hidden,
+                           const uint16_t* residual, const uint16_t* gamma, float eps, int64_t hidden, int order,
                            uint16_t* residual_out, uint16_t* y) {
     const int64_t L = n / R;
     const int64_t c1 = n * bits1 / 8, c2 = L * bits2 / 8, g1 = n / group, g2 = L / group;
@@ -455,8 +466,8 @@ void or_two_step_normfirst(const uint16_t* const* parts, int R, int64_t n, int b
             min_[r] = meta1 + r * g1 + s * (L / group);
         }
         or_reduce_norm_quant(cin.data(), min_.data(), R, L, bits1, bits2, group, residual ? residual + s * L : nullptr,
-                             gamma, eps, hidden, residual_out ? residual_out + s * L : nullptr, codes2 + s * c2,
-                             meta2 + s * g2, nullptr);
+                             gamma, eps, hidden, order, residual_out ? residual_out + s * L : nullptr,
+                             codes2 + s * c2, meta2 + s * g2, nullptr);
     }
     std::vector<const uint8_t*> gc(R);
     std::vector<const uint32_t*> gm(R);

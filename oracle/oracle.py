@@ -19,7 +19,13 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 # FC_ORACLE_SRC lets a mutation check build a deliberately altered copy of the oracle elsewhere.
 SRC = os.environ.get("FC_ORACLE_SRC", os.path.join(HERE, "fc_oracle.cpp"))
-LIB = os.path.join(os.path.dirname(SRC), "liboracle.so")
+# FC_SANITIZE=1 builds (and loads) a copy instrumented with AddressSanitizer and UndefinedBehaviorSanitizer
+# that stops at the first report; Python then needs the ASan runtime preloaded:
+#   FC_SANITIZE=1 LD_PRELOAD=$(g++ -print-file-name=libasan.so) ASAN_OPTIONS=detect_leaks=0 \
+#       python -m pytest tests -m "not gpu"
+SANITIZE = os.environ.get("FC_SANITIZE") == "1"
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+LIB = os.path.join(os.path.dirname(SRC), "liboracle_san.so" if SANITIZE else "liboracle.so")
 
 _lock = threading.Lock()
 _lib = None
@@ -39,7 +45,7 @@ def build(force: bool = False) -> str:
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
         tmp = LIB + ".tmp%d" % os.getpid()
         cmd = ["g++", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c++17", "-fPIC", "-shared",
-               SRC, "-o", tmp]
+               *(SAN_FLAGS if SANITIZE else []), SRC, "-o", tmp]
         subprocess.run(cmd, check=True)
         os.replace(tmp, LIB)
     return LIB
@@ -69,11 +75,13 @@ def lib():
             L.or_flag_unpack_reduce.argtypes = [vp, vp, C.c_int, i64, C.c_int, C.c_uint32, u16p, u8p, u8p, u32p]
             L.or_sumsq_tree.argtypes = [f32p, i64]
             L.or_sumsq_tree.restype = C.c_float
-            L.or_norm_rows_f32.argtypes = [f32p, vp, u16p, C.c_float, i64, i64, f32p, vp]
+            L.or_sumsq_seq.argtypes = [f32p, i64]
+            L.or_sumsq_seq.restype = C.c_float
+            L.or_norm_rows_f32.argtypes = [f32p, vp, u16p, C.c_float, i64, i64, C.c_int, f32p, vp]
             L.or_reduce_norm_quant.argtypes = [vp, vp, C.c_int, i64, C.c_int, C.c_int, C.c_int, vp, u16p, C.c_float,
-                                               i64, vp, u8p, u32p, vp]
+                                               i64, C.c_int, vp, u8p, u32p, vp]
             L.or_two_step_normfirst.argtypes = [vp, C.c_int, i64, C.c_int, C.c_int, C.c_int, u8p, u32p, u8p, u32p,
-                                                vp, u16p, C.c_float, i64, vp, u16p]
+                                                vp, u16p, C.c_float, i64, C.c_int, vp, u16p]
         return _lib
 
 
@@ -225,23 +233,37 @@ def ll_gather(slots_list, nwords, block_slots, epoch, out=None, done=None, count
 
 
 # ---- norm before the all-gather ---------------------------------------------------------------------
+# The order of a row's sum of squares: "seq" is the plain reading (the epilogue's left fold of the rounded
+# squares); "tree" is the fixed tree order the GPU kernels commit to (8-element chunk folds, then a
+# pairwise tree over the chunks), which lets tests check the kernels' other steps bit for bit.
+ORDER = {"seq": 0, "tree": 1}
+
+
 def sumsq_tree(h):
     """Fixed-order sum of squares of one row (8-element chunk folds, pairwise tree over chunks)."""
     h = _c(h, np.float32).ravel()
     return np.float32(lib().or_sumsq_tree(h, h.size))
 
 
-def norm_rows_f32(y, residual, gamma, eps, hidden):
+def sumsq_seq(h):
+    """Sum of squares of one row as a left fold of the rounded squares (the plain reading)."""
+    h = _c(h, np.float32).ravel()
+    return np.float32(lib().or_sumsq_seq(h, h.size))
+
+
+def norm_rows_f32(y, residual, gamma, eps, hidden, order="seq"):
     """fp32 normalized rows o (not rounded) and bf16 residual_out (None without residual)."""
     y = _c(y, np.float32).ravel()
     o = np.empty(y.size, np.float32)
     rout = np.empty(y.size, np.uint16) if residual is not None else None
     res = _c(residual, np.uint16).ravel() if residual is not None else None
-    lib().or_norm_rows_f32(y, _ptr(res), _c(gamma, np.uint16), eps, y.size // hidden, hidden, o, _ptr(rout))
+    lib().or_norm_rows_f32(y, _ptr(res), _c(gamma, np.uint16), eps, y.size // hidden, hidden, ORDER[order], o,
+                           _ptr(rout))
     return o, rout
 
 
-def reduce_norm_quant(codes_list, meta_list, L, bits_in, bits_out, group, residual, gamma, eps, hidden):
+def reduce_norm_quant(codes_list, meta_list, L, bits_in, bits_out, group, residual, gamma, eps, hidden,
+                      order="seq"):
     """One shard with the norm first: returns (codes, meta, residual_out, o) of the shard."""
     R = len(codes_list)
     cl = [_c(c, np.uint8) for c in codes_list]
@@ -252,11 +274,11 @@ def reduce_norm_quant(codes_list, meta_list, L, bits_in, bits_out, group, residu
     om = np.zeros(L // group, np.uint32)
     o = np.empty(L, np.float32)
     lib().or_reduce_norm_quant(_ptr_array(cl), _ptr_array(ml), R, L, bits_in, bits_out, group, _ptr(res),
-                               _c(gamma, np.uint16), eps, hidden, _ptr(rout), oc, om, _ptr(o))
+                               _c(gamma, np.uint16), eps, hidden, ORDER[order], _ptr(rout), oc, om, _ptr(o))
     return oc, om, rout, o
 
 
-def two_step_normfirst(parts, bits1, bits2, group, residual, gamma, eps, hidden):
+def two_step_normfirst(parts, bits1, bits2, group, residual, gamma, eps, hidden, order="seq"):
     """The whole two-step all-reduce with the norm applied to each shard before the all-gather."""
     R = len(parts)
     ps = [_c(p, np.uint16).ravel() for p in parts]
@@ -269,7 +291,7 @@ def two_step_normfirst(parts, bits1, bits2, group, residual, gamma, eps, hidden)
     rout = np.empty(n, np.uint16) if residual is not None else None
     y = np.empty(n, np.uint16)
     lib().or_two_step_normfirst(_ptr_array(ps), R, n, bits1, bits2, group, c1, m1, c2, m2, _ptr(res),
-                                _c(gamma, np.uint16), eps, hidden, _ptr(rout), y)
+                                _c(gamma, np.uint16), eps, hidden, ORDER[order], _ptr(rout), y)
     return dict(codes1=c1.reshape(R, -1), meta1=m1.reshape(R, -1), codes2=c2, meta2=m2, y=y, residual_out=rout)
 
 

@@ -258,7 +258,7 @@ def test_reduce_norm_first_largest(fc, orc, n_shards, L):
             cs = [_host(ins[s * R + r][0], lo, hi, np.uint8) for r in range(R)]
             ms = [_host(ins[s * R + r][1], lo // G, hi // G, np.uint32) for r in range(R)]
             oc, om, rr, _ = orc.reduce_norm_quant(cs, ms, H, b1, b2, G, _host(res, s * L + lo, s * L + hi, np.uint16),
-                                                   gh, 1e-5, H)
+                                                   gh, 1e-5, H, order="tree")
             assert_equal_bits(_host(outs[s][1], lo // G, hi // G, np.uint32), om, f"meta, shard {s} row {row}")
             assert_equal_bits(_host(outs[s][0], lo, hi, np.uint8), oc, f"codes, shard {s} row {row}")
             assert_equal_bits(_host(rout, s * L + lo, s * L + hi, np.uint16), rr, f"residual_out, shard {s} row {row}")

@@ -40,7 +40,8 @@ def _run_shards(orc, R, n_shards, rows, H, b1, b2, G, with_residual=True, seed=0
     for s in range(n_shards):
         chunk = ins_host[s * R:(s + 1) * R]
         rc, rm, rro, _ = orc.reduce_norm_quant([c for c, _ in chunk], [m for _, m in chunk], L, b1, b2, G,
-                                               res[s * L:(s + 1) * L] if with_residual else None, gam, 1e-5, H)
+                                               res[s * L:(s + 1) * L] if with_residual else None, gam, 1e-5, H,
+                                               order="tree")
         where = f"R={R} shard {s}/{n_shards} rows={rows} H={H} b={b1}/{b2} G={G}"
         assert_equal_bits(down(outs[s][1], np.uint32), rm, "meta " + where)
         assert_equal_bits(down(outs[s][0], np.uint8), rc, "codes " + where)
@@ -91,7 +92,7 @@ def test_norm_first_end_to_end(fc, orc, workload):
     cfg = dg.WORKLOADS[workload]
     parts = dg.partials(cfg)
     res, gam = dg.residual(cfg), dg.gamma(cfg)
-    ref = orc.two_step_normfirst(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, res, gam, cfg.eps, cfg.H)
+    ref = orc.two_step_normfirst(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, res, gam, cfg.eps, cfg.H, order="tree")
     p = TwoStepAllReduce(cfg.R, cfg.T, cfg.H, cfg.bits_rs, cfg.bits_ag, cfg.group, parts=up(np.stack(parts)))
     y = torch.empty(cfg.n, dtype=torch.int16, device="cuda")
     rout = torch.empty(cfg.n, dtype=torch.int16, device="cuda")
@@ -130,7 +131,7 @@ def test_norm_first_70b_prefill_sampled(fc, orc):
         sl = slice(t * H, (t + 1) * H)
         msgs = [orc.quantize(parts[r][sl], b1, G) for r in range(R)]
         c2, m2, ro, _ = orc.reduce_norm_quant([c for c, _ in msgs], [m for _, m in msgs], H, b1, b2, G, res[sl],
-                                              gam, cfg.eps, H)
+                                              gam, cfg.eps, H, order="tree")
         assert_equal_bits(codes2[t * H * b2 // 8:(t + 1) * H * b2 // 8], c2, f"row {t} payload codes")
         assert_equal_bits(meta2[t * gpr:(t + 1) * gpr], m2, f"row {t} payload meta")
         assert_equal_bits(rout_h[sl], ro, f"row {t} residual_out")

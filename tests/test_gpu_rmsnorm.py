@@ -74,13 +74,16 @@ def test_max_workgroups_and_split_invariance(fc):
     assert torch.equal(torch.cat([out_a, out_b]), base)
 
 
-def test_tokenweave_workload_sampled(fc, orc):
+@pytest.mark.timeout(300)
+def test_tokenweave_workload_full(fc, orc):
     """8 x [8192, 8192] bf16 split into two wave-aware halves of 4096 rows, each reduced on its own (as
-    the benchmark does); halves equal the unsplit call bit for bit, and sampled rows match the oracle."""
+    the benchmark does); the halves equal the unsplit call bit for bit, and every out and residual_out
+    element of both halves matches the oracle's whole run."""
     import torch
-    from gpu_helpers import assert_bf16_close, down, up
+    from gpu_helpers import assert_bf16_close, assert_equal_bits, down, up
     cfg = dg.TOKENWEAVE
     R, T, H = cfg.R, cfg.T, cfg.H
+    print(f"[full] {cfg.name}", flush=True)
     parts_h = [dg.partial(cfg, r) for r in range(R)]
     res_h, gam_h = dg.residual(cfg), dg.gamma(cfg)
     parts = [up(p) for p in parts_h]
@@ -90,12 +93,13 @@ def test_tokenweave_workload_sampled(fc, orc):
     a = cfg.splits[0]
     halves = []
     for lo, hi in ((0, a), (a, T)):
-        halves.append(_run(fc, [p[lo * H:hi * H] for p in parts], hi - lo, H, gam, res[lo * H:hi * H], max_wg=256))
+        halves.append(_run(fc, [p[lo * H:hi * H] for p in parts], hi - lo, H, gam, res[lo * H:hi * H]))
     assert torch.equal(torch.cat(halves), whole)
-    out_h, rout_h = down(whole, np.uint16), down(rout, np.uint16)
-    rng = np.random.default_rng(2)
-    for t in np.unique(np.concatenate([[0, a - 1, a, T - 1], rng.integers(0, T, 12)])):
-        sl = slice(t * H, (t + 1) * H)
-        o, ro, _ = orc.reduce_rmsnorm([p[sl] for p in parts_h], 1, H, res_h[sl], gam_h, cfg.eps)
-        assert_bf16_close(rout_h[sl], ro, 0, f"row {t} residual_out")
-        assert_bf16_close(out_h[sl], o, 2, f"row {t} out")
+    out_h = np.concatenate([down(h, np.uint16) for h in halves])
+    rout_h = down(rout, np.uint16)
+    del parts, halves, whole, rout
+    torch.cuda.empty_cache()
+    o, ro, _ = orc.reduce_rmsnorm(parts_h, T, H, res_h, gam_h, cfg.eps)
+    assert_equal_bits(rout_h, ro, "residual_out")
+    exact = assert_bf16_close(out_h, o, 2, "out")
+    print(f"[full] {cfg.name}: {T * H} outputs, {100 * exact:.3f}% bit-identical, the rest within 2 ulp", flush=True)

@@ -141,3 +141,114 @@ def test_two_step_normfirst_close_to_standard_path(orc):
     rng_g = o_st.max(axis=1, keepdims=True) - o_st.min(axis=1, keepdims=True)
     assert np.all(np.abs(o_nf - o_st) <= rng_g / 255 * 2 + np.abs(o_st) * 2.0 ** -6)
     assert np.max(np.abs(f(nf["residual_out"]) - f(st["residual_out"]))) < 0.1
+
+
+# ---- the plain order (the reading the GPU's fixed tree order is compared against) ----------------------
+def test_sumsq_seq_is_the_left_fold_of_rounded_squares(orc):
+    """Squares [2^24, 1, 1, 1] (placed at any positions): the left fold rounds each +1 back to 2^24 (a tie,
+    to even), so the plain order gives 2^24 where the tree gives 2^24 + 2; [1, 1, 1, 2^24] gives 2^24 + 4 in
+    the left fold (3 + 2^24 rounds to even, up)."""
+    h = np.zeros(32, np.float32)
+    h[[0, 8, 16, 24]] = [4096, 1, 1, 1]
+    assert orc.sumsq_seq(h) == np.float32(16777216)
+    assert orc.sumsq_tree(h) == np.float32(16777218)
+    h[[0, 8, 16, 24]] = [1, 1, 1, 4096]
+    assert orc.sumsq_seq(h) == np.float32(16777220)
+
+
+@pytest.mark.parametrize("H", [8, 1000, 8192])
+def test_sumsq_seq_exact_on_integers(orc, H):
+    rng = np.random.default_rng(H + 5)
+    h = rng.integers(-16, 17, H).astype(np.float32)
+    assert orc.sumsq_seq(h) == np.float32(np.sum(h.astype(np.int64) ** 2))
+
+
+def test_sumsq_seq_rounds_each_square(orc):
+    """As the tree's chunk fold: fl(1 + fl(b*b)), not a fused fl(1 + b*b)."""
+    from fractions import Fraction
+    b = np.float32(1.0 + 3370 * 2.0 ** -23)
+    unfused = _rn32(Fraction(1) + Fraction(float(_rn32(Fraction(float(b)) ** 2))))
+    h = np.zeros(5, np.float32)
+    h[[0, 4]] = [1.0, b]
+    assert orc.sumsq_seq(h) == unfused
+
+
+@pytest.mark.parametrize("H", [256, 4096, 8192])
+def test_plain_norm_rounds_to_the_standard_epilogue(orc, H):
+    """The plain-order normalized rows are the standard epilogue's values before their bf16 rounding: on
+    Gaussian rows (sums of squares not exact) bf16(o) equals the epilogue's output bit for bit, and
+    residual_out is the same."""
+    rng = np.random.default_rng(H + 9)
+    rows = 4
+    y = (rng.standard_normal(rows * H) * 3).astype(np.float32)
+    res = orc.f32_to_bf16(rng.standard_normal(rows * H).astype(np.float32))
+    gam = orc.f32_to_bf16(rng.normal(1.0, 0.1, H).astype(np.float32))
+    o, rout = orc.norm_rows_f32(y, res, gam, 1e-5, H, order="seq")
+    out_std, rout_std = orc.rmsnorm(y, res, gam, 1e-5, H)
+    assert np.array_equal(orc.f32_to_bf16(o), out_std)
+    assert np.array_equal(rout, rout_std)
+
+
+def test_plain_and_tree_orders_differ_where_the_sum_does():
+    """A row whose squares are [2^24, 1, 1, 1] at chunk starts: the two orders give different sums, hence
+    different normalized values; on integer rows with exact sums they agree."""
+    import oracle as orc
+    H = 32
+    y = np.zeros(H, np.float32)
+    y[[0, 8, 16, 24]] = [4096, 1, 1, 1]
+    gam = orc.f32_to_bf16(np.ones(H, np.float32))
+    o_s, _ = orc.norm_rows_f32(y, None, gam, 1e-5, H, order="seq")
+    o_t, _ = orc.norm_rows_f32(y, None, gam, 1e-5, H, order="tree")
+    assert not np.array_equal(o_s, o_t)
+    y = np.arange(H, dtype=np.float32) - 16
+    assert np.array_equal(orc.norm_rows_f32(y, None, gam, 1e-5, H, order="seq")[0],
+                          orc.norm_rows_f32(y, None, gam, 1e-5, H, order="tree")[0])
+
+
+def test_two_step_normfirst_orders_share_every_other_step():
+    """The whole norm-first path in both orders: identical reduce-scatter messages and residual stream (the
+    order only enters the norm), and gathered rows within one 8-bit step of each other."""
+    import oracle as orc
+    cfg = dg.DECODE_8B
+    parts = dg.partials(cfg)
+    res, gam = dg.residual(cfg), dg.gamma(cfg)
+    a = orc.two_step_normfirst(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, res, gam, cfg.eps, cfg.H, order="seq")
+    b = orc.two_step_normfirst(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, res, gam, cfg.eps, cfg.H, order="tree")
+    assert np.array_equal(a["codes1"], b["codes1"]) and np.array_equal(a["meta1"], b["meta1"])
+    assert np.array_equal(a["residual_out"], b["residual_out"])
+    scale = orc.f16_to_f32((a["meta2"] & 0xFFFF).astype(np.uint16)).astype(np.float64)
+    f = lambda u: (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    d = np.abs(f(a["y"]) - f(b["y"]))
+    assert np.all(d <= np.repeat(scale, cfg.group) * 1.01 + np.abs(f(a["y"])) * 2.0 ** -7)
+
+
+def test_order_bound_holds_for_the_tree_order(orc):
+    """The comparison the GPU test makes (tests/normfirst_bound.py), run with the oracle's tree order in the
+    kernels' place (its depth is the one the bound assumes): every decided group is bit-exact against the
+    plain order, the rest within the bound, and few groups are undecided."""
+    import sys
+    import os
+    sys.path.insert(0, os.path.dirname(__file__))
+    from normfirst_bound import compare
+    cfg = dg.DECODE_8B
+    parts = dg.partials(cfg)
+    res, gam = dg.residual(cfg), dg.gamma(cfg)
+    tree = orc.two_step_normfirst(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, res, gam, cfg.eps, cfg.H, order="tree")
+    flip, total = compare(orc, cfg, parts, res, gam, tree, log=lambda m: None)
+    assert flip < 0.1 * total
+
+
+def test_order_bound_catches_a_wrong_code(orc):
+    """The same comparison rejects a result with one code of a decided group changed."""
+    import sys
+    import os
+    sys.path.insert(0, os.path.dirname(__file__))
+    from normfirst_bound import compare
+    cfg = dg.DECODE_8B
+    parts = dg.partials(cfg)
+    res, gam = dg.residual(cfg), dg.gamma(cfg)
+    tree = orc.two_step_normfirst(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, res, gam, cfg.eps, cfg.H, order="tree")
+    tree["codes2"] = tree["codes2"].copy()
+    tree["codes2"][5] ^= 1
+    with pytest.raises(AssertionError):
+        compare(orc, cfg, parts, res, gam, tree, log=lambda m: None)
