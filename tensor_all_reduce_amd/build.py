@@ -15,8 +15,20 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-LIB = os.path.join(HERE, "libfc.so")
-BUILD_DIR = os.path.join(ROOT, "_build")
+# FC_SANITIZE=1 builds libfc_san.so instead: the host code (fc_api.cpp, the argument checks and launch
+# set-up) instrumented with AddressSanitizer and UndefinedBehaviorSanitizer, the kernels unchanged, linked
+# against the compiler's shared sanitizer runtime.  Load it with FC_LIB_PATH and that runtime preloaded,
+# on the CPU (the checks run before any GPU call):
+#   FC_SANITIZE=1 python -m tensor_all_reduce_amd.build
+#   FC_LIB_PATH=$PWD/tensor_all_reduce_amd/libfc_san.so ASAN_OPTIONS=detect_leaks=0 \
+#       LD_PRELOAD=$(/opt/rocm/lib/llvm/bin/clang++ -print-file-name=libclang_rt.asan-x86_64.so) \
+#       python -m pytest tests/test_abi.py tests/test_binding.py
+SANITIZE = os.environ.get("FC_SANITIZE") == "1"
+# host-only instrumentation: each flag reaches the host compiler and linker only
+HOST_SAN = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=all",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-shared-libsan"]
+LIB = os.path.join(HERE, "libfc_san.so" if SANITIZE else "libfc.so")
+BUILD_DIR = os.path.join(ROOT, "_build", "san" if SANITIZE else "")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -62,7 +74,8 @@ def build(verbose: bool = False) -> str:
         if src.endswith(".hip"):
             cmd = [HIPCC, *DEVICE, *COMMON, "-c", path, "-o", obj]
         else:
-            cmd = [HIPCC, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-c", path, "-o", obj]
+            cmd = [HIPCC, *COMMON, *(HOST_SAN if SANITIZE else []), "-x", "c++", "-D__HIP_PLATFORM_AMD__",
+                   "-I/opt/rocm/include", "-c", path, "-o", obj]
         jobs.append((cmd, obj))
     with ThreadPoolExecutor(max_workers=len(jobs)) as ex:  # one compiler process per source file
         outs = list(ex.map(lambda j: _run(j[0]), jobs))
@@ -72,7 +85,7 @@ def build(verbose: bool = False) -> str:
     objs = [obj for _, obj in jobs]
     tlib = torch_lib_dir()
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(HOST_SAN if SANITIZE else []), *objs, "-o", tmp,
            "-L" + tlib, "-l:libamdhip64.so", "-Wl,-rpath," + tlib, "-Wl,--no-undefined"]
     _run(cmd)
     os.replace(tmp, LIB)
