@@ -230,7 +230,7 @@ def pmc_rows(out_json):
     import numpy as np
     import torch
     from tensor_all_reduce_amd import _lib, bytes_model as bm, datagen as dg
-    from tensor_all_reduce_amd.flash_allreduce import ReduceRMSNorm
+    from tensor_all_reduce_amd.flash_allreduce import ReduceRMSNorm, rank_rows
     dev = torch.device("cuda:0")
     up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view({2: np.int16, 4: np.int32, 8: np.int64}[a.dtype.itemsize])).to(dev)
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -245,8 +245,7 @@ def pmc_rows(out_json):
     sets = []
     for k in range(3):
         slots = []
-        for r in range(R):
-            s_ = torch.empty(nslots, dtype=torch.int64, device=dev)
+        for r, s_ in enumerate(rank_rows(R, nslots, torch.int64, dev)[1]):
             _lib.fc_ll_pack(up(dg.partial(c4, r)), B, e, s_, block_order=up(dg.write_order(c4, r, nblk)))
             s_.view(torch.int32).view(-1, 2)[:, 1] = up(dg.stale_epochs(c4, r, nslots)[0])
             slots.append(s_)
@@ -267,7 +266,9 @@ def pmc_rows(out_json):
     c5 = dg.TOKENWEAVE
     a = c5.splits[0]
     na = a * c5.H
-    parts = [up(dg.partial(c5, r, na)) for r in range(c5.R)]
+    pbuf, parts = rank_rows(c5.R, na, torch.int16, dev)
+    for r in range(c5.R):
+        parts[r].copy_(up(dg.partial(c5, r, na)))
     res, gam = up(dg.residual(c5, na)), up(dg.gamma(c5))
     o5, ro5 = torch.empty(na, dtype=torch.int16, device=dev), torch.empty(na, dtype=torch.int16, device=dev)
     rr = ReduceRMSNorm(parts, a, c5.H, gam, o5, residual=res, residual_out=ro5, eps=c5.eps)
@@ -275,7 +276,7 @@ def pmc_rows(out_json):
         rr.run()
     torch.cuda.synchronize()
     algo["BF16ReduceProducer"] = bm.reduce_rmsnorm(c5.R, a, c5.H, True, True)
-    del parts, res, o5, ro5, rr
+    del parts, pbuf, res, o5, ro5, rr
     # all-gather of the int8 prefill messages, first pass
     c3 = dg.PREFILL_70B
     msg3 = c3.L * c3.bits_ag // 8 + 4 * (c3.L // c3.group)
@@ -828,7 +829,7 @@ def bench_ll(cx):
     seeded mix of wrong epoch words: time the first pass and the retry after the late blocks arrive."""
     torch, np = cx.torch, cx.np
     from tensor_all_reduce_amd import _lib, bytes_model as bm, datagen as dg
-    from tensor_all_reduce_amd.flash_allreduce import LLUnpackReduce
+    from tensor_all_reduce_amd.flash_allreduce import LLUnpackReduce, rank_rows
     cfg = dg.SLOTS
     R, n, B, e = cfg.R, cfg.n, cfg.block_slots, cfg.epoch
     nslots, nblk = n // 2, n // 2 // B
@@ -841,7 +842,7 @@ def bench_ll(cx):
     good_ep = torch.full((nslots,), e, dtype=torch.int64, device=cx.dev).to(torch.int32)
     sets = []
     for k in range(nsets):
-        slots = [torch.empty(nslots, dtype=torch.int64, device=cx.dev) for _ in range(R)]
+        slots = list(rank_rows(R, nslots, torch.int64, cx.dev)[1])  # the R inboxes staggered in one allocation
         for r in range(R):
             _lib.fc_ll_pack(xs[r], B, e, slots[r], block_order=orders[r])
         out = torch.zeros(n, dtype=torch.int16, device=cx.dev)
@@ -1066,11 +1067,13 @@ def bench_rmsnorm_overlap(cx):
     and half A's reduce on one stream overlapped with the GEMM on another."""
     torch, np = cx.torch, cx.np
     from tensor_all_reduce_amd import bytes_model as bm, datagen as dg
-    from tensor_all_reduce_amd.flash_allreduce import ReduceRMSNorm
+    from tensor_all_reduce_amd.flash_allreduce import ReduceRMSNorm, rank_rows
     cfg = dg.TOKENWEAVE
     R, T, H = cfg.R, cfg.T, cfg.H
     a = cfg.splits[0]
-    parts = [cx.up(dg.partial(cfg, r)) for r in range(R)]
+    pbuf, parts = rank_rows(R, T * H, torch.int16, cx.dev)  # the R partials staggered in one allocation
+    for r in range(R):
+        parts[r].copy_(cx.up(dg.partial(cfg, r)))
     res, gam = cx.up(dg.residual(cfg)), cx.up(dg.gamma(cfg))
     out = torch.empty(T * H, dtype=torch.int16, device=cx.dev)
     rout = torch.empty(T * H, dtype=torch.int16, device=cx.dev)
@@ -1139,7 +1142,7 @@ def bench_rmsnorm_overlap(cx):
            "both_halves_GB/s": round(2 * half_bytes / (both * 1e-6) / 1e9, 1),
            "gemm_alone_us": round(gemm_us, 1), "gemm_TFLOP/s": round(2 * a * H * H / (gemm_us * 1e-6) / 1e12, 1),
            "max_workgroups_sweep": sweep}
-    del parts, halves, A, Bm, C
+    del parts, pbuf, halves, A, Bm, C
     torch.cuda.empty_cache()
     return res
 
