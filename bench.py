@@ -849,21 +849,26 @@ def bench_ll(cx):
         stale = torch.zeros(R * nblk, dtype=torch.uint8, device=cx.dev)
         done = torch.zeros(nblk, dtype=torch.uint8, device=cx.dev)
         cnt = torch.zeros(2, dtype=torch.int32, device=cx.dev)
-        sets.append((slots, LLUnpackReduce(slots, n, B, out, stale, done, cnt), done, cnt))
+        sets.append((slots, LLUnpackReduce(slots, n, B, out, stale, done, cnt), done, cnt,
+                     LLUnpackReduce(slots, n, B, out, stale, done, None)))
 
     def set_epochs(which):
-        for slots, _, _, _ in sets:
+        for slots, *_ in sets:
             for r in range(R):
                 slots[r].view(torch.int32).view(-1, 2)[:, 1] = which[r] if which is not None else good_ep
 
     def reset():
-        for _, _, done, cnt in sets:
+        for _, _, done, cnt, _ in sets:
             done.zero_()
             cnt.zero_()
     g = cx.graph(lambda k: sets[k][1].run(e), nsets)
-    t1, t2 = [], []
+    g0 = cx.graph(lambda k: sets[k][4].run(e), nsets)  # the same receiver without counters
+    t1, t2, t0 = [], [], []
     for _ in range(5):
         set_epochs(late_ep)
+        reset()
+        torch.cuda.synchronize()
+        t0.append(_once(cx, g0, nsets))
         reset()
         torch.cuda.synchronize()
         t1.append(_once(cx, g, nsets))
@@ -873,11 +878,12 @@ def bench_ll(cx):
         t2.append(_once(cx, g, nsets))
     pending = int(cnt0[1])
     by1 = bm.total(bm.ll_unpack(R, n, B, completed_blocks=nblk - pending))
-    us1, us2 = statistics.median(t1), statistics.median(t2)
+    us1, us2, us0 = statistics.median(t1), statistics.median(t2), statistics.median(t0)
     res = {"workload": cfg.name, "pass1_us": round(us1, 2), "pass1_bytes": by1,
            "pass1_GB/s": round(by1 / (us1 * 1e-6) / 1e9, 1), "stale_pairs": int(cnt0[0]), "pending_blocks": pending,
-           "blocks": nblk, "retry_us": round(us2, 2), "buffer_sets": nsets}
-    del sets, g
+           "blocks": nblk, "retry_us": round(us2, 2), "buffer_sets": nsets,
+           "pass1_nocount_us": round(us0, 2), "pass1_nocount_GB/s": round(by1 / (us0 * 1e-6) / 1e9, 1)}
+    del sets, g, g0
     torch.cuda.empty_cache()
     return res
 

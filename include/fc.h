@@ -137,7 +137,9 @@ fc_status fc_reduce_rmsnorm(const uint16_t* const* parts, int R, int64_t rows, c
  * skipped: nothing of theirs is written (their slots may still be read).  counters[0] += stale
  * (rank, block) pairs seen, counters[1] += pending blocks, both in one 64-bit atomic add per workgroup:
  * counters must be 8-byte aligned (FC_E_ALIGN otherwise) and counters[0] must not wrap (a call adds at
- * most R*nblk < 2^29); the caller zeroes counters.  Calling again after late blocks have been rewritten
+ * most R*nblk < 2^29); the caller zeroes counters.  counters may be NULL: then nothing is counted and no
+ * atomic is issued (the stale and done flags hold every verdict; device-scope atomics on one address
+ * serialize, so the count costs time).  Calling again after late blocks have been rewritten
  * completes them with the same bits as if they had been on time.  n % (2*block_slots) == 0. */
 fc_status fc_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, int block_slots, uint32_t epoch,
                               uint16_t* out, uint8_t* stale, uint8_t* done, uint32_t* counters,
@@ -152,7 +154,7 @@ fc_status fc_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, in
  * copied to out[r] (uint32 [nwords], host array of R device pointers, 8-byte aligned) and done is set; a
  * stale one is left untouched and pending.  counters[0] += stale (rank, block) pairs and counters[1] +=
  * pending pairs (the same pairs: nothing is reduced across ranks), in one 64-bit atomic add per
- * workgroup (counters 8-byte aligned, caller zeroes).  A done block's slots may still be read.  Calling
+ * workgroup (counters 8-byte aligned, caller zeroes; or NULL: nothing counted, as above).  A done block's slots may still be read.  Calling
  * again after late blocks have been rewritten completes them.  nwords % block_slots == 0. */
 fc_status fc_ll_gather(const uint64_t* const* slots, int R, int64_t nwords, int block_slots, uint32_t epoch,
                        uint32_t* const* out, uint8_t* stale, uint8_t* done, uint32_t* counters, hipStream_t stream);
@@ -175,7 +177,8 @@ fc_status fc_ll_pack(const uint16_t* const* x, int R, int64_t n, int block_slots
  * that rank's slots of the tile after a short sleep, at most max_polls times (0..2^20; 0 = one look, with
  * the results of fc_ll_unpack_reduce); the verdicts are those of the last look.  max_workgroups > 0 caps
  * the grid (the tiles are then walked with a stride), leaving compute units to a sender running at the
- * same time; 0 = one tile per wavefront.  counters: uint32 [4], 8-byte aligned, zeroed by the caller:
+ * same time; 0 = one tile per wavefront.  counters: uint32 [4], 8-byte aligned, zeroed by the caller
+ * (or NULL: nothing counted):
  * [0] stale (rank, block) pairs and [1] pending blocks at the last look (one 64-bit atomic add per
  * workgroup), [2] += re-reads summed over wavefronts, [3] unused.  The call always ends: a block still
  * stale after the budget is left pending for a later call. */

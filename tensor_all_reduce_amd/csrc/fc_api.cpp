@@ -318,10 +318,10 @@ fc_status fc_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, in
     if (R < 1 || R > fc::kMaxRanks || !valid_block(block_slots) || n < 0) return FC_E_ARG;
     if (n % (2 * block_slots) != 0 || n > kMaxElems) return FC_E_SHAPE;
     if (n == 0) return FC_OK;
-    if (!slots || !out || !stale || !done || !counters) return FC_E_NULL;
-    if (!aligned(out, 16) || !aligned(counters, 8)) return FC_E_ALIGN;
+    if (!slots || !out || !stale || !done) return FC_E_NULL;
+    if (!aligned(out, 16) || (counters && !aligned(counters, 8))) return FC_E_ALIGN;
     const int64_t nblk = n / 2 / block_slots;
-    const Range ro = rng(out, 2 * n), rs = rng(stale, (int64_t)R * nblk), rd = rng(done, nblk), rc = rng(counters, 8);
+    const Range ro = rng(out, 2 * n), rs = rng(stale, (int64_t)R * nblk), rd = rng(done, nblk), rc = rng(counters, counters ? 8 : 0);
     if (overlap(ro, rs) || overlap(ro, rd) || overlap(ro, rc) || overlap(rs, rd) || overlap(rs, rc) || overlap(rd, rc))
         return FC_E_ARG;
     for (int r = 0; r < R; ++r) {
@@ -348,10 +348,10 @@ fc_status fc_ll_gather(const uint64_t* const* slots, int R, int64_t nwords, int 
     if (R < 1 || R > fc::kMaxRanks || !valid_block(block_slots) || nwords < 0) return FC_E_ARG;
     if (nwords % block_slots != 0 || nwords > kMaxElems) return FC_E_SHAPE;
     if (nwords == 0) return FC_OK;
-    if (!slots || !out || !stale || !done || !counters) return FC_E_NULL;
-    if (!aligned(counters, 8)) return FC_E_ALIGN;
+    if (!slots || !out || !stale || !done) return FC_E_NULL;
+    if ((counters && !aligned(counters, 8))) return FC_E_ALIGN;
     const int64_t nblk = nwords / block_slots;
-    const Range rs = rng(stale, (int64_t)R * nblk), rd = rng(done, (int64_t)R * nblk), rc = rng(counters, 8);
+    const Range rs = rng(stale, (int64_t)R * nblk), rd = rng(done, (int64_t)R * nblk), rc = rng(counters, counters ? 8 : 0);
     if (overlap(rs, rd) || overlap(rs, rc) || overlap(rd, rc)) return FC_E_ARG;
     for (int r = 0; r < R; ++r) {
         if (!slots[r] || !out[r]) return FC_E_NULL;
@@ -424,10 +424,10 @@ fc_status fc_ll_poll_unpack_reduce(const uint64_t* const* slots, int R, int64_t 
     if (max_polls < 0 || max_polls > kMaxPolls || max_workgroups < 0) return FC_E_ARG;
     if (n % (2 * block_slots) != 0 || n > kMaxElems) return FC_E_SHAPE;
     if (n == 0) return FC_OK;
-    if (!slots || !out || !stale || !done || !counters) return FC_E_NULL;
-    if (!aligned(out, 16) || !aligned(counters, 8)) return FC_E_ALIGN;
+    if (!slots || !out || !stale || !done) return FC_E_NULL;
+    if (!aligned(out, 16) || (counters && !aligned(counters, 8))) return FC_E_ALIGN;
     const int64_t nblk = n / 2 / block_slots;
-    const Range ro = rng(out, 2 * n), rs = rng(stale, (int64_t)R * nblk), rd = rng(done, nblk), rc = rng(counters, 16);
+    const Range ro = rng(out, 2 * n), rs = rng(stale, (int64_t)R * nblk), rd = rng(done, nblk), rc = rng(counters, counters ? 16 : 0);
     if (overlap(ro, rs) || overlap(ro, rd) || overlap(ro, rc) || overlap(rs, rd) || overlap(rs, rc) || overlap(rd, rc))
         return FC_E_ARG;
     for (int r = 0; r < R; ++r) {
@@ -457,10 +457,10 @@ fc_status fc_flag_unpack_reduce(const uint16_t* const* payload, const uint32_t* 
     if (max_polls < 0 || max_polls > kMaxPolls || max_workgroups < 0) return FC_E_ARG;
     if (n % block_elems != 0 || n > kMaxElems) return FC_E_SHAPE;
     if (n == 0) return FC_OK;
-    if (!payload || !flags || !out || !stale || !done || !counters) return FC_E_NULL;
-    if (!aligned(out, 16) || !aligned(counters, 8)) return FC_E_ALIGN;
+    if (!payload || !flags || !out || !stale || !done) return FC_E_NULL;
+    if (!aligned(out, 16) || (counters && !aligned(counters, 8))) return FC_E_ALIGN;
     const int64_t nblk = n / block_elems;
-    const Range ro = rng(out, 2 * n), rs = rng(stale, (int64_t)R * nblk), rd = rng(done, nblk), rc = rng(counters, 16);
+    const Range ro = rng(out, 2 * n), rs = rng(stale, (int64_t)R * nblk), rd = rng(done, nblk), rc = rng(counters, counters ? 16 : 0);
     if (overlap(ro, rs) || overlap(ro, rd) || overlap(ro, rc) || overlap(rs, rd) || overlap(rs, rc) || overlap(rd, rc))
         return FC_E_ARG;
     for (int r = 0; r < R; ++r) {

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256) void k_flag_unpack(const int64_t ntiles, const
     }
     // wave 0 holds the counts: stale pairs and pending blocks in one 64-bit atomic (a call adds at most 2^29
     // stale pairs, so the low word does not carry), re-reads in one 32-bit atomic
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0 && counters != nullptr) {  // counters == NULL: nothing is counted
         if (n_stale | n_pending)
             atomicAdd(reinterpret_cast<unsigned long long*>(counters), ((unsigned long long)n_pending << 32) | n_stale);
         if (n_polls) atomicAdd(counters + 2, n_polls);
@@ -364,6 +364,7 @@ __global__ __launch_bounds__(256) void k_ll_poll(const int64_t nslots, const int
             n_stale += (uint32_t)__builtin_popcount(vs[b]);
         }
     }
+    if (counters == nullptr) return;  // uniform: nothing is counted
     if (lane == 0) {
         s_cnt[threadIdx.x >> 6][0] = n_stale;
         s_cnt[threadIdx.x >> 6][1] = n_pending;

@@ -13,8 +13,9 @@ namespace fc {
 // =====================================================================================================
 // Self-synchronizing slots (flash-comm, abstract): the receiver validates each block's epoch words
 // itself, with no barrier.  A wavefront owns a tile of KI*128 slots, read by KI instructions of 128
-// slots (2 slots = 16 bytes per lane), KI = 2 so that 2*8 slot loads are in flight per lane.  Block
-// verdicts and counters are wavefront-uniform and kept on the scalar unit.  A block of B <= 128 slots
+// slots (2 slots = 16 bytes per lane); KI = 1 (two for 256-slot blocks) in 16-wavefront workgroups, so
+// the 8-rank slot workload is 4096 wavefronts of 8 loads, all in flight at once.  Block verdicts and
+// counters are wavefront-uniform and kept on the scalar unit.  A block of B <= 128 slots
 // covers B/2 aligned lanes of one instruction (its verdict is a field of that instruction's ballot); a
 // block of 256 slots covers two consecutive instructions (the OR of both).
 // =====================================================================================================
@@ -52,11 +53,13 @@ __device__ __forceinline__ void ll_examine(const uint4 (&q)[KI], int r, uint32_t
     }
 }
 
-template <int B, int W>  // W wavefronts per workgroup
+// W wavefronts per workgroup, KI instructions of 128 slots per wavefront tile; RK = 8 fixes the rank count
+// at compile time (the rank loop then has no uniform branches), RK = 0 reads it from R_arg.
+template <int B, int W, int KI, int RK>
 __global__ __launch_bounds__(64 * W) void k_ll_unpack(const int64_t nslots, const int64_t nblk, uint8_t* done,
-                                                   const uint32_t epoch, const int R, uint16_t* out, uint8_t* stale,
+                                                   const uint32_t epoch, const int R_arg, uint16_t* out, uint8_t* stale,
                                                    uint32_t* counters, const LLSlots slots) {
-    constexpr int KI = 2;                      // instructions per wavefront tile
+    const int R = RK ? RK : R_arg;
     constexpr int IB = B <= 128 ? 1 : 2;       // instructions per block
     constexpr int LB = B <= 128 ? B / 2 : 64;  // lanes of one instruction inside one block
     constexpr int RB = 8;                      // ranks whose slots are loaded before any is examined
@@ -65,15 +68,16 @@ __global__ __launch_bounds__(64 * W) void k_ll_unpack(const int64_t nslots, cons
     __shared__ uint32_t s_cnt[W][2];  // per wavefront: stale pairs, pending blocks
     const int lane = threadIdx.x & 63;
     const int bl = lane % LB;  // lane inside its block's lanes
-    const int64_t tile = ((int64_t)blockIdx.x * W + (threadIdx.x >> 6)) * (128 * KI);
-    int64_t slot[KI], blk[KI], src[KI];
+    const int64_t tile = ((int64_t)blockIdx.x * W + (threadIdx.x >> 6)) * (128 * KI);  // wavefront-uniform
+    int64_t slot[KI], blk[KI];
+    uint32_t src[KI];  // byte offset from the tile's first slot (a lane past the end reads that slot)
     bool inside[KI];
 #pragma unroll
     for (int k = 0; k < KI; ++k) {
         slot[k] = tile + k * 128 + 2 * lane;
         inside[k] = slot[k] < nslots;
         blk[k] = inside[k] ? slot[k] / B : nblk - 1;
-        src[k] = inside[k] ? slot[k] : 0;
+        src[k] = inside[k] ? (uint32_t)(k * 128 + 2 * lane) * 8u : 0u;
     }
     // The done flags and the first batch of slot loads are issued together, the slots at addresses that do
     // not depend on the flags, so that their memory latencies overlap (a block already done is read anyway
@@ -82,11 +86,12 @@ __global__ __launch_bounds__(64 * W) void k_ll_unpack(const int64_t nslots, cons
     uint8_t dn[KI];
 #pragma unroll
     for (int k = 0; k < KI; ++k) dn[k] = done[blk[k]];
+    // each rank's tile base is wavefront-uniform (scalar); the lanes add a 32-bit byte offset
     uint4 sv[RB][KI];
 #pragma unroll
     for (int j = 0; j < RB; ++j)
 #pragma unroll
-        for (int k = 0; k < KI; ++k) sv[j][k] = lds16(slots.p[j] + src[k]);
+        for (int k = 0; k < KI; ++k) sv[j][k] = lds16(reinterpret_cast<const uint8_t*>(slots.p[j] + tile) + src[k]);
     bool active[KI];
     uint64_t amask[KI];  // lanes of blocks to examine (inside the buffer and not done yet)
 #pragma unroll
@@ -107,7 +112,8 @@ __global__ __launch_bounds__(64 * W) void k_ll_unpack(const int64_t nslots, cons
 #pragma unroll
         for (int j = 0; j < RB; ++j)
 #pragma unroll
-            for (int k = 0; k < KI; ++k) sv[j][k] = lds16(slots.p[r0 + j] + src[k]);
+            for (int k = 0; k < KI; ++k)
+                sv[j][k] = lds16(reinterpret_cast<const uint8_t*>(slots.p[r0 + j] + tile) + src[k]);
 #pragma unroll
         for (int j = 0; j < RB; ++j)
             if (r0 + j < R) ll_examine<LB, KI>(sv[j], r0 + j, epoch, amask, acc, vs);
@@ -141,7 +147,9 @@ __global__ __launch_bounds__(64 * W) void k_ll_unpack(const int64_t nslots, cons
         }
     }
     // Counters, from wavefront-uniform values only (scalar unit): block b of instruction k was examined
-    // iff the first lane of its lanes was active.
+    // iff the first lane of its lanes was active.  counters == NULL: nothing is counted (the stale and done
+    // flags hold every verdict) and no atomic is issued.
+    if (counters == nullptr) return;  // uniform
     uint32_t n_stale = 0, n_pending = 0;
 #pragma unroll
     for (int k = 0; k < KI; k += IB) {
@@ -172,23 +180,39 @@ __global__ __launch_bounds__(64 * W) void k_ll_unpack(const int64_t nslots, cons
     }
 }
 
-// Wavefronts per workgroup of the slot receiver: the counters cost one atomic per workgroup, and those
-// atomics serialize, so larger workgroups mean fewer of them.
-constexpr int kLLWaves = 8;
+// Wavefronts per workgroup and instructions per wavefront tile of the slot receiver.  The counters cost
+// one atomic per workgroup, and those atomics serialize, so larger workgroups mean fewer of them; one
+// instruction per tile gives twice the wavefronts of two, each with half the work after its loads land
+// (8-rank slot workload, pass 1 without counters: 8.8 us with 2 x 8, 8.3 us with 1 x 16, measured).
+#ifndef FC_LL_WAVES
+#define FC_LL_WAVES 16
+#endif
+#ifndef FC_LL_KI
+#define FC_LL_KI 1
+#endif
+constexpr int kLLWaves = FC_LL_WAVES;
 
 hipError_t launch_ll_unpack(const LLParams& p, hipStream_t s) {
     LLSlots t;
     for (int i = 0; i < kMaxRanks; ++i) t.p[i] = p.slots[i < p.R ? i : p.R - 1];
     const int64_t nslots = p.n / 2, nblk = nslots / p.block_slots;
-    const int64_t per_wg = kLLWaves * 128 * 2;  // slots per workgroup: wavefronts x 2 instructions x 128
-    const dim3 grid((unsigned)((nslots + per_wg - 1) / per_wg));
-#define FC_LL(B) \
-    k_ll_unpack<B, kLLWaves><<<grid, 64 * kLLWaves, 0, s>>>(nslots, nblk, p.done, p.epoch, p.R, p.out, p.stale, p.counters, t)
+    constexpr int KI = FC_LL_KI;
+#define FC_LL(B, K)                                                                                        \
+    do {                                                                                                   \
+        const int64_t per_wg = kLLWaves * 128 * (K); /* slots per workgroup */                             \
+        const dim3 grid((unsigned)((nslots + per_wg - 1) / per_wg));                                       \
+        if (p.R == 8)                                                                                      \
+            k_ll_unpack<B, kLLWaves, K, 8><<<grid, 64 * kLLWaves, 0, s>>>(nslots, nblk, p.done, p.epoch, p.R, \
+                                                                          p.out, p.stale, p.counters, t);  \
+        else                                                                                               \
+            k_ll_unpack<B, kLLWaves, K, 0><<<grid, 64 * kLLWaves, 0, s>>>(nslots, nblk, p.done, p.epoch, p.R, \
+                                                                          p.out, p.stale, p.counters, t);  \
+    } while (0)
     switch (p.block_slots) {
-        case 32: FC_LL(32); break;
-        case 64: FC_LL(64); break;
-        case 128: FC_LL(128); break;
-        default: FC_LL(256); break;
+        case 32: FC_LL(32, KI); break;
+        case 64: FC_LL(64, KI); break;
+        case 128: FC_LL(128, KI); break;
+        default: FC_LL(256, 2); break;  // a 256-slot block spans two instructions
     }
 #undef FC_LL
     return hipGetLastError();
@@ -283,6 +307,7 @@ __global__ __launch_bounds__(64 * W) void k_ll_gather(const int64_t nslots, cons
             if (leader) dn[blk[k]] = 1;
         }
     }
+    if (counters == nullptr) return;  // uniform: nothing is counted
     uint32_t n_stale = 0;
 #pragma unroll
     for (int k = 0; k < KI; k += IB) {

@@ -185,6 +185,10 @@ def test_ll_validation(L):
     assert g(out=A + 0x3000008) == L.FC_E_ALIGN
     assert g(cnt=A + 0x6000002) == L.FC_E_ALIGN
     assert g(cnt=A + 0x6000004) == L.FC_E_ALIGN    # both counters take one 64-bit atomic: 8-byte aligned
+    # counters may be NULL (nothing counted); every other check still applies (no call here launches)
+    assert g(cnt=None, n=0) == L.FC_OK
+    assert g(cnt=None, done=None) == L.FC_E_NULL
+    assert g(cnt=None, out=A + 0x1000000 + 64) == L.FC_E_ARG
     assert g(done=A + 0x4000000 + 8) == L.FC_E_ARG   # done inside the stale flags
     assert g(out=A + 0x1000000 + 64) == L.FC_E_ARG   # out inside rank 0's slots
     p = L.lib.fc_ll_pack
@@ -219,7 +223,10 @@ def test_ll_poll_validation(L):
     assert g(mw=-1) == L.FC_E_ARG
     assert g(n=4096 + 64) == L.FC_E_SHAPE
     assert g(n=0) == L.FC_OK
-    assert g(cnt=None) == L.FC_E_NULL
+    # counters may be NULL (nothing counted); every other check still applies (no call here launches)
+    assert g(cnt=None, n=0) == L.FC_OK
+    assert g(cnt=None, out=None) == L.FC_E_NULL
+    assert g(cnt=None, out=A + 0x3000008) == L.FC_E_ALIGN
     assert g(cnt=A + 0x6000004) == L.FC_E_ALIGN
     assert g(out=A + 0x3000008) == L.FC_E_ALIGN
     assert g(s=(C.c_void_p * 2)(A + 0x1000008, A + 0x2000000)) == L.FC_E_ALIGN
@@ -276,7 +283,10 @@ def test_ll_gather_validation(L):
     assert g(R=0) == L.FC_E_ARG
     assert g(n=4096 + 32) == L.FC_E_SHAPE
     assert g(n=0) == L.FC_OK
-    assert g(cnt=None) == L.FC_E_NULL
+    # counters may be NULL (nothing counted); every other check still applies (no call here launches)
+    assert g(cnt=None, n=0) == L.FC_OK
+    assert g(cnt=None, stale=None) == L.FC_E_NULL
+    assert g(cnt=None, done=A + 0x4000000 + 8) == L.FC_E_ARG
     assert g(cnt=A + 0x6000004) == L.FC_E_ALIGN
     assert g(o=(C.c_void_p * 2)(A + 0x3000004, A + 0x3800000)) == L.FC_E_ALIGN
     assert g(s=(C.c_void_p * 2)(A + 0x1000008, A + 0x2000000)) == L.FC_E_ALIGN

@@ -191,3 +191,72 @@ def test_rank_counts_and_done_skip(fc, orc, R):
     skipped = done0.astype(bool)
     assert np.all(st[:, skipped] == 0xAB)
     assert_equal_bits(st[:, ~skipped], rst[:, ~skipped], "stale (examined)")
+
+
+def test_receivers_without_counters(fc, orc):
+    """counters = NULL: nothing is counted and no atomic is issued; out, stale and done are the same bits
+    as with counters, and as the oracle's, for the slot receiver (8-rank workload with its stale mix, both
+    passes), the standalone all-gather, the polling slot receiver and the flag receiver."""
+    import torch
+    from gpu_helpers import assert_equal_bits, down, up
+    cfg = dg.SLOTS
+    R, n, B, e = cfg.R, cfg.n, cfg.block_slots, cfg.epoch
+    nslots, nblk = n // 2, n // 2 // B
+    xs = [dg.partial(cfg, r) for r in range(R)]
+    orders = [dg.write_order(cfg, r, nblk) for r in range(R)]
+    eps = [dg.stale_epochs(cfg, r, nslots)[0] for r in range(R)]
+    slots_d = []
+    for r in range(R):
+        s = torch.empty(nslots, dtype=torch.int64, device="cuda")
+        fc.fc_ll_pack(up(xs[r]), B, e, s, block_order=up(orders[r]))
+        inject_gpu(s, eps[r])
+        slots_d.append(s)
+    late = [set_epochs_host(orc.ll_pack(xs[r], B, e, order=orders[r]), eps[r]) for r in range(R)]
+    ro, rst, rdn, _ = orc.ll_unpack_reduce(late, n, B, e)
+    res = {}
+    for tag, cnt in (("counted", torch.zeros(2, dtype=torch.int32, device="cuda")), ("uncounted", None)):
+        out = torch.zeros(n, dtype=torch.int16, device="cuda")
+        st = torch.full((R * nblk,), 0xAB, dtype=torch.uint8, device="cuda")
+        dn = torch.zeros(nblk, dtype=torch.uint8, device="cuda")
+        fc.fc_ll_unpack_reduce(slots_d, n, B, e, out, st, dn, cnt)
+        torch.cuda.synchronize()
+        res[tag] = (down(out, np.uint16), down(st, np.uint8).reshape(R, nblk), down(dn, np.uint8))
+    for a, b, what in zip(res["counted"], res["uncounted"], ("out", "stale", "done")):
+        assert_equal_bits(b, a, what + " without counters")
+    assert_equal_bits(res["uncounted"][1], rst, "stale vs oracle")
+    assert_equal_bits(res["uncounted"][2], rdn, "done vs oracle")
+    ok = np.repeat(rdn.astype(bool), 2 * B)
+    assert_equal_bits(res["uncounted"][0][ok], ro[ok], "out of completed blocks vs oracle")
+    # standalone all-gather on the same slots (rank r's words = its packed payload)
+    outs = [torch.zeros(nslots, dtype=torch.int32, device="cuda") for _ in range(R)]
+    gst = torch.full((R * nblk,), 0xAB, dtype=torch.uint8, device="cuda")
+    gdn = torch.zeros(R * nblk, dtype=torch.uint8, device="cuda")
+    fc.fc_ll_gather(slots_d, nslots, B, e, outs, gst, gdn, None)
+    torch.cuda.synchronize()
+    rg_out, rg_st, rg_dn, _ = orc.ll_gather(late, nslots, B, e)
+    assert_equal_bits(down(gst, np.uint8).ravel(), np.asarray(rg_st).ravel(), "all-gather stale without counters")
+    assert_equal_bits(down(gdn, np.uint8).ravel(), np.asarray(rg_dn).ravel(), "all-gather done without counters")
+    # polling slot receiver and flag receiver, every copy on time
+    st2 = torch.empty(R * nblk, dtype=torch.uint8, device="cuda")
+    dn2 = torch.zeros(nblk, dtype=torch.uint8, device="cuda")
+    out2 = torch.zeros(n, dtype=torch.int16, device="cuda")
+    good = [s.clone() for s in slots_d]
+    for r in range(R):
+        inject_gpu(good[r], np.full(nslots, e, np.uint32))
+    fc.fc_ll_poll_unpack_reduce(good, n, B, e, out2, st2, dn2, None, max_polls=2)
+    torch.cuda.synchronize()
+    ro2, _, _, _ = orc.ll_unpack_reduce([orc.ll_pack(xs[r], B, e, order=orders[r]) for r in range(R)], n, B, e)
+    assert_equal_bits(down(out2, np.uint16), ro2, "polling receiver out without counters")
+    assert int(down(dn2, np.uint8).sum()) == nblk
+    be = 2048
+    pays = [torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(R)]
+    fls = [torch.empty(n // be, dtype=torch.int32, device="cuda") for _ in range(R)]
+    fc.fc_flag_pack([up(x) for x in xs], be, e, pays, fls)
+    fb = n // be
+    out3 = torch.zeros(n, dtype=torch.int16, device="cuda")
+    st3 = torch.empty(R * fb, dtype=torch.uint8, device="cuda")
+    dn3 = torch.zeros(fb, dtype=torch.uint8, device="cuda")
+    fc.fc_flag_unpack_reduce(pays, fls, n, be, e, out3, st3, dn3, None, max_polls=1)
+    torch.cuda.synchronize()
+    assert_equal_bits(down(out3, np.uint16), ro2, "flag receiver out without counters")
+    assert int(down(dn3, np.uint8).sum()) == fb
