@@ -16,7 +16,8 @@ def fc():
 
 
 @pytest.mark.parametrize("workload,rank", [("tiny-r2-t4-h256", 0), ("tiny-r2-t4-h256", 1), ("llama3-8b-decode", 0),
-                                           ("llama3-8b-decode", 5), ("llama3-8b-decode", 7)])
+                                           ("llama3-8b-decode", 5), ("llama3-8b-decode", 7),
+                                           ("llama3-70b-prefill", 3)])
 def test_share_matches_whole_all_reduce(fc, orc, workload, rank):
     import torch
     from gpu_helpers import assert_bf16_close, assert_equal_bits, down, up
