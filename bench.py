@@ -55,8 +55,8 @@ def kernel_of_call(call, cfg):
             "gather_norm": f"k_rows<fc::GatherProducer<{cfg.bits_ag},"}[call]
 
 
-DEFAULT_ROWS = "decode,share,normfirst,ll,llgather,rmsnorm,layer"
-ALL_ROWS = DEFAULT_ROWS + ",warm,encodings"
+DEFAULT_ROWS = "decode,share,normfirst,ll,llgather,rmsnorm,layer,encodings"
+ALL_ROWS = DEFAULT_ROWS + ",warm"
 
 
 def parse():
@@ -73,8 +73,7 @@ def parse():
     ap.add_argument("--oracle-by-config", action="store_true",
                     help="also time the oracle on every workload (a detail line; about a minute of CPU)")
     ap.add_argument("--rows", default="default",
-                    help=f"other hot-path rows: default ({DEFAULT_ROWS}) | all (adds warm,encodings) | none | "
-                         "comma list")
+                    help=f"other hot-path rows: default ({DEFAULT_ROWS}) | all (adds warm) | none | comma list")
     ap.add_argument("--detail-out", metavar="JSON", help="also write every row's full record to this file")
     ap.add_argument("--kernel-reps", type=int, default=0, help="graph replays per call timing (0 = auto)")
     ap.add_argument("--fit-encodings", metavar="JSON", help="write the selector's fitted cost table here")
@@ -171,9 +170,9 @@ def profile_report(config, stats_csv, fetch_csv, write_csv, valu_csv, out_md):
             pmc.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
     med = {k: statistics.median(v) for k, v in pmc.items()}
     traffic = load_traffic(cfg)
-    decode = cfg is dg.DECODE_8B  # the default workload
-    runs = "" if decode else f" --config {config} --steps 30 --warmup 5"
-    x = " --steps 290 --warmup 0 --kernel-reps 1" if decode else f" --config {config} --steps 4 --warmup 1 --kernel-reps 1"
+    headline = cfg is dg.PREFILL_70B  # the default workload
+    runs = " --steps 30 --warmup 5" if headline else f" --config {config} --steps 290 --warmup 10"
+    x = " --steps 4 --warmup 1 --kernel-reps 1" if headline else f" --config {config} --steps 290 --warmup 0 --kernel-reps 1"
     base = "python3 bench.py --no-cpu-baseline --rows none"
     lines = [f"# Two-step all-reduce kernels on the {cfg.name} workload", "",
              "Kernel durations from a rocprofv3 kernel trace of the benchmark (run from the repository root on one "
@@ -733,8 +732,19 @@ def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_firs
         fns = {"quantize": lambda k: sets[k][0].quantize(), "reduce_shard": lambda k: sets[k][0].reduce_scatter(),
                "gather_norm": lambda k: sets[k][0].all_gather(norm=sets[k][1])}
     per_call = {}
-    for name, fn in fns.items():
-        us = cx.time_graph(cx.graph(fn, nsets), reps, nsets)
+    # each call alone over the buffer sets, the calls taken in turn, `reps` rounds: every call samples the
+    # same stretch of the run (the engine clock drifts under sustained load)
+    graphs = {name: cx.graph(fn, nsets) for name, fn in fns.items()}
+    samples = {name: [] for name in fns}
+    for name, g in graphs.items():
+        g.replay()
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        for name, g in graphs.items():
+            samples[name].append(_once(cx, g, nsets))
+    del graphs
+    for name in fns:
+        us = statistics.median(samples[name])
         by = bm.total(calls[name])
         gbps = by / (us * 1e-6) / 1e9
         per_call[name] = {"us": round(us, 3), "bytes": by, "GB/s": round(gbps, 1),
