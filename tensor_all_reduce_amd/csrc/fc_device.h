@@ -127,37 +127,40 @@ __device__ __forceinline__ GroupQ group_params(float lo, float hi) {
     return GroupQ{z, inv, sb | (zb << 16)};
 }
 
-// Codes: v = (x - z) * inv rounded to nearest even by adding 1.5*2^23, which leaves the integer in the low
-// mantissa bits (exact for 0 <= v < 2^22).  For in-contract inputs 0 <= v < qmax + 0.5: z <= x, and
-// s >= (max - z)/qmax up to the roundings of one division and one reciprocal, so v <= qmax*(1 + 2^-21);
-// the definition's clamp to [0, qmax] therefore never changes a code and is not executed.  Codes are
-// packed straight from the low byte (8-bit) or low nibble (4-bit) of the sum's bits, so an
-// out-of-contract input gives a wrong code but never touches a neighbour's bits.
+// Codes: q = clamp(round-half-even((x - z) * inv), 0, qmax), the subtraction and the product each rounded
+// (no contraction).  v_cvt_pk_u8_f32 converts a float to an unsigned byte with round-half-even and
+// saturation to [0, 255], and inserts it into byte `sel` of a word, leaving the other bytes (checked on
+// gfx950 against rint + clamp over ties, near-ties, negatives and values past 255).  For 8-bit codes that
+// is exactly the definition's rounding and clamp.  For 4-bit codes the saturation is at 255, not 15: for
+// in-contract inputs 0 <= v < qmax + 0.5 (z <= x, and s >= (max - z)/qmax up to the roundings of one
+// division and one reciprocal, so v <= qmax*(1 + 2^-21)), so the clamp at qmax never changes a code; an
+// out-of-contract input gives a wrong code but the masks below keep it out of its neighbour's nibble.
 template <int BITS, int E>
 __device__ __forceinline__ void encode_lane(const float (&v)[E], float z, float inv, uint32_t (&w)[E * BITS / 32]) {
-    constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23; its bit pattern 0x4B400000 has a zero low byte
-    uint32_t c[E];
+    float q[E];
 #pragma unroll
     for (int i = 0; i < E; ++i) {
         const float d = v[i] - z;
-        const float q = d * inv;
-        c[i] = f2u(q + MAGIC);  // low 8 bits = code
+        q[i] = d * inv;
     }
-    // v_perm_b32 selectors: byte i of the result = byte sel_i of {src0:src1} (0x0c = zero); 0x0c0c0400
-    // puts the low bytes of src1 and src0 into bytes 0 and 1, 0x05040100 joins two such half-words.
 #pragma unroll
     for (int k = 0; k < E * BITS / 32; ++k) {
         if constexpr (BITS == 8) {
-            const uint32_t lo = __builtin_amdgcn_perm(c[4 * k + 1], c[4 * k], 0x0c0c0400u);
-            const uint32_t hi = __builtin_amdgcn_perm(c[4 * k + 3], c[4 * k + 2], 0x0c0c0400u);
-            w[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+            uint32_t x = __builtin_amdgcn_cvt_pk_u8_f32(q[4 * k], 0, 0u);
+            x = __builtin_amdgcn_cvt_pk_u8_f32(q[4 * k + 1], 1, x);
+            x = __builtin_amdgcn_cvt_pk_u8_f32(q[4 * k + 2], 2, x);
+            w[k] = __builtin_amdgcn_cvt_pk_u8_f32(q[4 * k + 3], 3, x);
         } else {
-            // byte j of ev / od = code 2j / 2j+1; the low nibbles are merged into one word (bfi)
-            const uint32_t* cc = c + 8 * k;
-            const uint32_t ev = __builtin_amdgcn_perm(__builtin_amdgcn_perm(cc[6], cc[4], 0x0c0c0400u),
-                                                      __builtin_amdgcn_perm(cc[2], cc[0], 0x0c0c0400u), 0x05040100u);
-            const uint32_t od = __builtin_amdgcn_perm(__builtin_amdgcn_perm(cc[7], cc[5], 0x0c0c0400u),
-                                                      __builtin_amdgcn_perm(cc[3], cc[1], 0x0c0c0400u), 0x05040100u);
+            // byte j of ev / od = code 2j / 2j+1; the odd codes go to the high nibbles
+            const float* qq = q + 8 * k;
+            uint32_t ev = __builtin_amdgcn_cvt_pk_u8_f32(qq[0], 0, 0u);
+            ev = __builtin_amdgcn_cvt_pk_u8_f32(qq[2], 1, ev);
+            ev = __builtin_amdgcn_cvt_pk_u8_f32(qq[4], 2, ev);
+            ev = __builtin_amdgcn_cvt_pk_u8_f32(qq[6], 3, ev);
+            uint32_t od = __builtin_amdgcn_cvt_pk_u8_f32(qq[1], 0, 0u);
+            od = __builtin_amdgcn_cvt_pk_u8_f32(qq[3], 1, od);
+            od = __builtin_amdgcn_cvt_pk_u8_f32(qq[5], 2, od);
+            od = __builtin_amdgcn_cvt_pk_u8_f32(qq[7], 3, od);
             w[k] = (ev & 0x0f0f0f0fu) | ((od << 4) & 0xf0f0f0f0u);
         }
     }
