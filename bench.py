@@ -933,13 +933,18 @@ def bench_ll_gather(cx):
                 for r in range(R):
                     slots[r].copy_(words[r] | ((eps[r] if late else good) << 32))
 
-        def run(k):
+        def run(k, counted=True):
             _, slots, out, stale, done, cnt = sets[k]
-            _lib.fc_ll_gather(slots, nwords, B, e, out, stale, done, cnt)
+            _lib.fc_ll_gather(slots, nwords, B, e, out, stale, done, cnt if counted else None)
         g = cx.graph(run, nsets)
-        t1, t2 = [], []
+        g0 = cx.graph(lambda k: run(k, False), nsets)  # the same pass without counters
+        t1, t2, t0 = [], [], []
         for _ in range(5):
             set_epochs(True)
+            for s in sets:
+                s[4].zero_()
+            torch.cuda.synchronize()
+            t0.append(_once(cx, g0, nsets))
             for s in sets:
                 s[4].zero_()
                 s[5].zero_()
@@ -950,11 +955,12 @@ def bench_ll_gather(cx):
             torch.cuda.synchronize()
             t2.append(_once(cx, g, nsets))
         by1 = bm.total(bm.ll_gather(R, nwords, B, completed_blocks=R * nblk - pend))
-        us1, us2 = statistics.median(t1), statistics.median(t2)
+        us1, us2, us0 = statistics.median(t1), statistics.median(t2), statistics.median(t0)
         res[tag] = {"R": R, "words_per_rank": nwords, "pass1_us": round(us1, 2), "pass1_bytes": by1,
                     "pass1_GB/s": round(by1 / (us1 * 1e-6) / 1e9, 1), "pending_pairs": pend, "pairs": R * nblk,
-                    "retry_us": round(us2, 2), "buffer_sets": nsets}
-        del sets, g
+                    "retry_us": round(us2, 2), "buffer_sets": nsets, "pass1_nocount_us": round(us0, 2),
+                    "pass1_nocount_GB/s": round(by1 / (us0 * 1e-6) / 1e9, 1)}
+        del sets, g, g0
         torch.cuda.empty_cache()
     return {"workload": "standalone all-gather on epoch-tagged blocks, B=64, 2% late", "by_payload": res}
 
@@ -1379,6 +1385,9 @@ def row_summary(extra: dict) -> dict:
             for tag, g in r["by_payload"].items():
                 out[f"allgather_{tag}"] = {"pass1_us": g["pass1_us"], "GBps": g["pass1_GB/s"],
                                            "pct": _pct(g["pass1_GB/s"]), "retry_us": g["retry_us"]}
+                if "pass1_nocount_us" in g:
+                    out[f"allgather_{tag}"].update(nocount_us=g["pass1_nocount_us"],
+                                                   nocount_pct=_pct(g["pass1_nocount_GB/s"]))
         elif k == "tokenweave_reduce_rmsnorm":
             ov = r["max_workgroups_sweep"].get("rows", {})
             out[k] = {"both_halves_us": r["both_halves_us"], "GBps": r["both_halves_GB/s"],

@@ -228,11 +228,10 @@ struct LLGatherTabs {
     uint32_t* out[kMaxRanks];
 };
 
-template <int B, int W>  // W wavefronts per workgroup
+template <int B, int W, int KI>  // W wavefronts per workgroup, KI instructions of 128 slots per wavefront tile
 __global__ __launch_bounds__(64 * W) void k_ll_gather(const int64_t nslots, const int64_t nblk, uint8_t* done,
                                                    uint8_t* stale, const uint32_t epoch, uint32_t* counters,
                                                    const LLGatherTabs t) {
-    constexpr int KI = 4;                      // instructions per wavefront tile
     constexpr int IB = B <= 128 ? 1 : 2;       // instructions per block
     constexpr int LB = B <= 128 ? B / 2 : 64;  // lanes of one instruction inside one block
     constexpr int NBW = 64 / LB;               // blocks per instruction
@@ -328,7 +327,10 @@ __global__ __launch_bounds__(64 * W) void k_ll_gather(const int64_t nslots, cons
     }
 }
 
-constexpr int kLLGWaves = 16;  // wavefronts per workgroup (one counter atomic per workgroup)
+// Tile shape of the all-gather: counted, one atomic per workgroup, so large tiles (16 wavefronts of 4
+// instructions: fewer workgroups, fewer atomics on the one address); uncounted, smaller ones (8 wavefronts
+// of 2) keep more loads in flight.  int8 prefill messages, pass 1: counted 22.7 us (2 x 16: 26-27 us),
+// uncounted 19.6 us (4 x 16: 21.7 us).
 
 hipError_t launch_ll_gather(const LLGatherParams& p, hipStream_t s) {
     LLGatherTabs t;
@@ -337,16 +339,24 @@ hipError_t launch_ll_gather(const LLGatherParams& p, hipStream_t s) {
         t.out[i] = p.out[i < p.R ? i : p.R - 1];
     }
     const int64_t nslots = p.nwords, nblk = nslots / p.block_slots;
-    const int64_t per_wg = kLLGWaves * 128 * 4;  // slots per workgroup: wavefronts x 4 instructions x 128
-    const dim3 grid((unsigned)((nslots + per_wg - 1) / per_wg), (unsigned)p.R);
-#define FC_LLG(B) \
-    k_ll_gather<B, kLLGWaves><<<grid, 64 * kLLGWaves, 0, s>>>(nslots, nblk, p.done, p.stale, p.epoch, p.counters, t)
+#define FC_LLG(B, W, K)                                                                                    \
+    do {                                                                                                   \
+        const int64_t per_wg = (W) * 128 * (K); /* slots per workgroup */                                  \
+        const dim3 grid((unsigned)((nslots + per_wg - 1) / per_wg), (unsigned)p.R);                        \
+        k_ll_gather<B, W, K><<<grid, 64 * (W), 0, s>>>(nslots, nblk, p.done, p.stale, p.epoch, p.counters, t); \
+    } while (0)
+#define FC_LLG_B(B) \
+    do {                                              \
+        if (p.counters) FC_LLG(B, 16, 4);             \
+        else FC_LLG(B, 8, 2);                         \
+    } while (0)
     switch (p.block_slots) {
-        case 32: FC_LLG(32); break;
-        case 64: FC_LLG(64); break;
-        case 128: FC_LLG(128); break;
-        default: FC_LLG(256); break;
+        case 32: FC_LLG_B(32); break;
+        case 64: FC_LLG_B(64); break;
+        case 128: FC_LLG_B(128); break;
+        default: FC_LLG_B(256); break;  // a 256-slot block spans two instructions (both shapes have 2 or 4)
     }
+#undef FC_LLG_B
 #undef FC_LLG
     return hipGetLastError();
 }

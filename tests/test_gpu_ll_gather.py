@@ -22,7 +22,9 @@ def _slots(words, epochs):
     return (np.asarray(words, np.uint64) & np.uint64(0xFFFFFFFF)) | (np.asarray(epochs, np.uint64) << np.uint64(32))
 
 
-def _gpu_gather(fc, slots_h, nwords, B, out=None, done=None):
+def _gpu_gather(fc, slots_h, nwords, B, out=None, done=None, counted=True):
+    """counted=False passes NULL counters (the launcher then takes its smaller tile shape); the returned
+    counters are then zeros."""
     import torch
     from gpu_helpers import down, up
     R = len(slots_h)
@@ -32,7 +34,7 @@ def _gpu_gather(fc, slots_h, nwords, B, out=None, done=None):
     done = torch.zeros(R * nblk, dtype=torch.uint8, device="cuda") if done is None else done
     stale = torch.full((R * nblk,), 7, dtype=torch.uint8, device="cuda")
     cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
-    fc.fc_ll_gather(sl, nwords, B, E, out, stale, done, cnt)
+    fc.fc_ll_gather(sl, nwords, B, E, out, stale, done, cnt if counted else None)
     torch.cuda.synchronize()
     return out, stale, done, cnt
 
@@ -54,9 +56,12 @@ def _late(R, nblk, B, nwords, seed, frac=0.1):
     return ep
 
 
+@pytest.mark.parametrize("counted", [True, False])
 @pytest.mark.parametrize("B", [32, 64, 128, 256])
-@pytest.mark.parametrize("R,nblk", [(1, 7), (3, 33), (8, 64), (16, 5)])
-def test_ll_gather_parity_and_retry(fc, orc, B, R, nblk):
+@pytest.mark.parametrize("R,nblk", [(1, 7), (3, 33), (8, 64), (16, 5), (2, 3000)])
+def test_ll_gather_parity_and_retry(fc, orc, B, R, nblk, counted):
+    """Both tile shapes of the launcher (counted: 16 wavefronts of 4 instructions; uncounted: 8 of 2), every
+    block size, ragged tile counts."""
     from gpu_helpers import assert_equal_bits, down
     nwords = B * nblk
     rng = np.random.default_rng(B * 100 + R)
@@ -64,21 +69,23 @@ def test_ll_gather_parity_and_retry(fc, orc, B, R, nblk):
     ep = _late(R, nblk, B, nwords, B + R)
     slots = [_slots(ws[r], ep[r]) for r in range(R)]
     ro, rs, rd, rc = orc.ll_gather(slots, nwords, B, E)
-    out, stale, done, cnt = _gpu_gather(fc, slots, nwords, B)
-    where = f"B={B} R={R} nblk={nblk}"
+    out, stale, done, cnt = _gpu_gather(fc, slots, nwords, B, counted=counted)
+    where = f"B={B} R={R} nblk={nblk} counted={counted}"
     for r in range(R):
         assert_equal_bits(down(out[r], np.uint32), ro[r], f"out rank {r} " + where)
     assert_equal_bits(down(stale, np.uint8), rs, "stale " + where)
     assert_equal_bits(down(done, np.uint8), rd, "done " + where)
-    assert_equal_bits(down(cnt, np.uint32), rc, "counters " + where)
+    if counted:
+        assert_equal_bits(down(cnt, np.uint32), rc, "counters " + where)
     # the late blocks arrive: the retry completes them
     slots2 = [_slots(ws[r], np.full(nwords, E)) for r in range(R)]
     ro2, rs2, rd2, rc2 = orc.ll_gather(slots2, nwords, B, E, out=ro, done=rd)
-    out2, stale2, done2, cnt2 = _gpu_gather(fc, slots2, nwords, B, out=out, done=done)
+    out2, stale2, done2, cnt2 = _gpu_gather(fc, slots2, nwords, B, out=out, done=done, counted=counted)
     for r in range(R):
         assert_equal_bits(down(out2[r], np.uint32), ws[r], f"retry out rank {r} " + where)
     assert_equal_bits(down(done2, np.uint8), rd2, "retry done " + where)
-    assert_equal_bits(down(cnt2, np.uint32), rc2, "retry counters " + where)
+    if counted:
+        assert_equal_bits(down(cnt2, np.uint32), rc2, "retry counters " + where)
     # stale flags are written for the blocks examined in this pass only
     examined = rd == 0
     assert_equal_bits(down(stale2, np.uint8)[examined], rs2[examined], "retry stale " + where)
@@ -138,7 +145,8 @@ def test_quantized_all_gather_in_slots_end_to_end(fc, orc):
     assert_bf16_close(down(o, np.uint16), ref["out"], 2, "out")
 
 
-def test_all_gather_prefill_messages_as_benched(fc, orc):
+@pytest.mark.parametrize("counted", [True, False])
+def test_all_gather_prefill_messages_as_benched(fc, orc, counted):
     """The benchmark's f3 workload: the 8 int8 shard messages of the 70B prefill (codes then meta, 1,081,344
     words each) carried in 64-slot blocks with about 2% of the copies late (every kind), pass 1 then the
     retry with every block rewritten: out, stale, done and counters of both passes equal the oracle's."""
@@ -153,19 +161,21 @@ def test_all_gather_prefill_messages_as_benched(fc, orc):
     ep = _late(R, nblk, B, nwords, 23, frac=0.02)
     first = [_slots(words[r], ep[r]) for r in range(R)]
     print(f"f3 prefill messages: R={R} nwords={nwords} B={B}", flush=True)
-    out, stale, done, cnt = _gpu_gather(fc, first, nwords, B)
+    out, stale, done, cnt = _gpu_gather(fc, first, nwords, B, counted=counted)
     ro, rst, rdn, rc = orc.ll_gather(first, nwords, B, E)
     for r in range(R):
         assert_equal_bits(down(out[r], np.uint32), ro[r], f"pass 1 words of rank {r}")
     assert_equal_bits(down(stale, np.uint8), rst, "pass 1 stale")
     assert_equal_bits(down(done, np.uint8), rdn, "pass 1 done")
-    assert_equal_bits(down(cnt, np.uint32), rc, "pass 1 counters")
+    if counted:
+        assert_equal_bits(down(cnt, np.uint32), rc, "pass 1 counters")
     assert int(rc[1]) > 0
     again = [_slots(words[r], np.full(nwords, E)) for r in range(R)]
-    out, stale, done, cnt = _gpu_gather(fc, again, nwords, B, out=out, done=done)
+    out, stale, done, cnt = _gpu_gather(fc, again, nwords, B, out=out, done=done, counted=counted)
     ro2, rst2, rdn2, rc2 = orc.ll_gather(again, nwords, B, E, out=ro, done=rdn)
     for r in range(R):
         assert_equal_bits(down(out[r], np.uint32), ro2[r], f"retry words of rank {r}")
     assert_equal_bits(down(done, np.uint8), rdn2, "retry done")
     assert rdn2.all() and int(rc2[1]) == 0
-    assert_equal_bits(down(cnt, np.uint32), rc2, "retry counters")
+    if counted:
+        assert_equal_bits(down(cnt, np.uint32), rc2, "retry counters")
