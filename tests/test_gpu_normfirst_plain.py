@@ -38,3 +38,21 @@ def test_decode_in_full_against_plain_order(orc):
 @pytest.mark.timeout(300)
 def test_prefill_in_full_against_plain_order(orc):
     _run(orc, dg.PREFILL_70B)
+
+
+# Other launch paths of the same reading: rows longer than 16384 elements (the k_rows producer, whose tree
+# runs over lanes, wavefronts, then a lane's chunks), a chunk count that is not a power of two (the tree
+# pads with zeros), 4-bit codes out, group sizes 32 and 256.  Seeds use workload numbers of their own.
+EXTRA = [
+    dg.Config(31, "norm-first R=4 T=8 H=20480 int8/int8 G=128", "two_step", R=4, T=8, H=20480, sigma=1.0,
+              outlier_p=0.01, outlier_factor=20.0, bits_rs=8, bits_ag=8, group=128),
+    dg.Config(32, "norm-first R=2 T=12 H=1056 int4/int8 G=32", "two_step", R=2, T=12, H=1056, sigma=0.7,
+              outlier_p=0.02, outlier_factor=30.0, bits_rs=4, bits_ag=8, group=32),
+    dg.Config(33, "norm-first R=8 T=64 H=4096 int8/int4 G=256", "two_step", R=8, T=64, H=4096, sigma=0.5,
+              outlier_p=0.005, outlier_factor=30.0, bits_rs=8, bits_ag=4, group=256),
+]
+
+
+@pytest.mark.parametrize("cfg", EXTRA, ids=lambda c: c.name)
+def test_other_shapes_against_plain_order(orc, cfg):
+    _run(orc, cfg)

@@ -252,3 +252,20 @@ def test_order_bound_catches_a_wrong_code(orc):
     tree["codes2"][5] ^= 1
     with pytest.raises(AssertionError):
         compare(orc, cfg, parts, res, gam, tree, log=lambda m: None)
+
+
+@pytest.mark.parametrize("H,G,b2", [(1056, 32, 8), (4096, 256, 4)])
+def test_order_bound_holds_on_other_shapes(orc, H, G, b2):
+    """The comparison of tests/normfirst_bound.py with the oracle's tree order on shapes whose chunk count is
+    not a power of two, and with 4-bit codes out."""
+    import sys
+    import os
+    sys.path.insert(0, os.path.dirname(__file__))
+    from normfirst_bound import compare
+    cfg = dg.Config(34, f"bound H={H}", "two_step", R=2, T=12, H=H, sigma=0.7, outlier_p=0.02, outlier_factor=30.0,
+                    bits_rs=8, bits_ag=b2, group=G)
+    parts = dg.partials(cfg)
+    res, gam = dg.residual(cfg), dg.gamma(cfg)
+    tree = orc.two_step_normfirst(parts, cfg.bits_rs, cfg.bits_ag, cfg.group, res, gam, cfg.eps, cfg.H, order="tree")
+    flip, total = compare(orc, cfg, parts, res, gam, tree, log=lambda m: None)
+    assert flip < 0.1 * total
