@@ -223,10 +223,11 @@ fc_status fc_flag_pack(const uint16_t* const* x, int R, int64_t n, int block_ele
 fc_status fc_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
 /* Measurement helper: the HBM ceilings the kernels are compared with, by access mix.  mode 0: the copy
- * above (src -> dst, `bytes` each way); mode 1: read `bytes` of src (16-byte aligned) with four
- * non-temporal 16-byte loads per lane, folding them so the loads stay; dst is a 4-byte sink that is
- * written only if the fold hits one fixed value; mode 2: write `bytes` of dst with non-temporal 16-byte
- * stores (src unused, may be NULL).  bytes: a multiple of 16, at most 2^40. */
+ * above (src -> dst, `bytes` each way); mode 1: read `bytes` of src (16-byte aligned) with one
+ * non-temporal 16-byte load per lane (1024-lane workgroups), each lane folding its four words so the
+ * load stays; dst is a 4-byte sink that receives 0x9E3779B9 only if some lane's fold equals that value;
+ * mode 2: write `bytes` of dst with one 16-byte store per lane, uint4 i = (0x3F803F80, i mod 2^32, 0, 0)
+ * (src unused, may be NULL).  bytes: a multiple of 16, at most 2^40. */
 fc_status fc_bandwidth_probe(const void* src, void* dst, int64_t bytes, int mode, hipStream_t stream);
 
 const char* fc_status_string(fc_status s);

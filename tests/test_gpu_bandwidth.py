@@ -1,6 +1,6 @@
 """GPU checks of the bandwidth-measurement helper (fc_bandwidth_probe): the copy copies, the writer writes
 its documented pattern over exactly the requested range, and the reader leaves its sink alone unless a
-workgroup's fold hits the fixed value (predicted here on the host)."""
+lane's fold hits the fixed value (predicted here on the host)."""
 import numpy as np
 import pytest
 
@@ -25,27 +25,28 @@ def test_copy_write_read(fc):
     torch.cuda.synchronize()
     got = dst.cpu().numpy()
     assert np.array_equal(got[:nb], src_h) and not got[nb:].any()
-    # writer: uint4 i holds (0x3F803F80, workgroup * 1024 + lane, 0, 0), lane = i % 256 inside the 1024-uint4 tile
+    # writer: uint4 i holds (0x3F803F80, i, 0, 0), over exactly the requested range
     dst.zero_()
     fc.fc_bandwidth_probe(None, dst, nb, 2)
     torch.cuda.synchronize()
     w = dst.cpu().numpy()[:nb].view(np.uint32).reshape(-1, 4)
     i = np.arange(w.shape[0])
-    assert np.all(w[:, 0] == 0x3F803F80) and np.array_equal(w[:, 1], (i // 1024) * 1024 + i % 256)
+    assert np.all(w[:, 0] == 0x3F803F80) and np.array_equal(w[:, 1], i)
     assert not w[:, 2:].any() and not dst.cpu().numpy()[nb:].any()
-    # reader: the fold of each workgroup's 4 KiB (16 KiB of uint4s) tile, lanes' folds per lane
-    sink = torch.full((1,), 0x0BADF00D, dtype=torch.int32, device="cuda")
-    fc.fc_bandwidth_probe(src, sink, nb, 1)
-    torch.cuda.synchronize()
+    # reader: each lane folds one uint4 (lanes past the end re-read the last one); the sink is written only
+    # if some fold hits the fixed value.  First random data (no fold hits), then a source planted with one
+    # uint4 whose fold is the value.
     v = src_h.view(np.uint32).reshape(-1, 4)
-    n16 = v.shape[0]
     folds = np.bitwise_xor.reduce(v, axis=1)
-    hit = False
-    for b in range(-(-n16 // 1024)):
-        for t in range(256):
-            idx = [min(b * 1024 + t + u * 256, n16 - 1) for u in range(4)]
-            acc = np.uint32(0)
-            for k in idx:
-                acc ^= folds[k]
-            hit |= int(acc) == SENTINEL
-    assert (int(sink.cpu()[0]) & 0xFFFFFFFF) == (SENTINEL if hit else 0x0BADF00D)
+    for planted in (False, True):
+        if planted:
+            v = v.copy()
+            v[12345] = (SENTINEL ^ 0x11 ^ 0x22 ^ 0x33, 0x11, 0x22, 0x33)
+            folds = np.bitwise_xor.reduce(v, axis=1)
+            src = torch.from_numpy(v.view(np.uint8).reshape(-1)).cuda()
+        sink = torch.full((1,), 0x0BADF00D, dtype=torch.int32, device="cuda")
+        fc.fc_bandwidth_probe(src, sink, nb, 1)
+        torch.cuda.synchronize()
+        hit = bool(np.any(folds == SENTINEL))
+        assert hit == planted
+        assert (int(sink.cpu()[0]) & 0xFFFFFFFF) == (SENTINEL if hit else 0x0BADF00D)
