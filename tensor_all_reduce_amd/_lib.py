@@ -23,9 +23,9 @@ FC_OK, FC_E_NULL, FC_E_ARG, FC_E_SHAPE, FC_E_ALIGN, FC_E_LAUNCH = range(6)
 class FcError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        msg = _lib.fc_status_string(status).decode()
+        msg = lib.fc_status_string(status).decode()  # the library the failing call went through
         if status == FC_E_LAUNCH:
-            msg += " (hipError %d)" % _lib.fc_last_hip_error()
+            msg += " (hipError %d)" % lib.fc_last_hip_error()
         super().__init__(f"{where}: {msg}")
 
 
