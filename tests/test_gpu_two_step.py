@@ -1,9 +1,9 @@
 """GPU parity of the two-step all-reduce (fc_reduce_shard, fc_gather_dequant) against the CPU oracle.
 
 Each step is fed the oracle's own output of the previous step (so inputs never come from the HIP
-path), then the whole GPU pipeline is compared end to end on the decode workloads, and on the 70B
-prefill workload (8 x [4096, 8192], int4 reduce-scatter, int8 all-gather) on sampled rows recomputed
-by the oracle from the partial sums.  Codes and meta bit-exact; bf16 outputs within 2 ulp."""
+path), then the whole GPU pipeline is compared end to end on the decode workloads and, element by
+element, on the 70B prefill workload (8 x [4096, 8192], int4 reduce-scatter, int8 all-gather).  Codes
+and meta bit-exact; bf16 outputs within 2 ulp."""
 import numpy as np
 import pytest
 
