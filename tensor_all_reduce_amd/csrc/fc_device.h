@@ -292,4 +292,12 @@ __device__ __forceinline__ void sts4(void* p, uint32_t v) {
 #endif
 }
 
+// Quantized messages (the rank messages and the all-gather payload) are written with write-back stores:
+// the next call of the step reads them, and at the 70B prefill size (142 MB of rank messages, 35 MB of
+// payload) they stay in the 256 MB memory-side cache between the calls, which streamed stores bypass.
+// Same-process A/B on the prefill step: 181.5 -> 174.2 us (the quantize alone 108.5 -> 107.3 us).
+__device__ __forceinline__ void stm16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+__device__ __forceinline__ void stm8(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
+__device__ __forceinline__ void stm4(void* p, uint32_t v) { *reinterpret_cast<uint32_t*>(p) = v; }
+
 }  // namespace fc

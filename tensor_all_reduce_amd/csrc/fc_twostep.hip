@@ -110,8 +110,8 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ x
         encode_lane<BITS, 8>(v[k], z, inv, w);
         const uint32_t c = wbase + 64u * k + lane;
         if (c < nchunks) {
-            if constexpr (BITS == 8) sts8(codes + (size_t)c * CB, make_uint2(w[0], w[1]));
-            else sts4(codes + (size_t)c * CB, w[0]);
+            if constexpr (BITS == 8) stm8(codes + (size_t)c * CB, make_uint2(w[0], w[1]));
+            else stm4(codes + (size_t)c * CB, w[0]);
         }
     }
 }
@@ -187,9 +187,9 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&w)[E * B
 
 template <int E, int B>
 __device__ __forceinline__ void store_codes(uint8_t* p, const uint32_t (&w)[E * B / 32]) {
-    if constexpr (E * B / 8 == 16) sts16(p, make_uint4(w[0], w[1], w[2], w[3]));
-    else if constexpr (E * B / 8 == 8) sts8(p, make_uint2(w[0], w[1]));
-    else sts4(p, w[0]);
+    if constexpr (E * B / 8 == 16) stm16(p, make_uint4(w[0], w[1], w[2], w[3]));
+    else if constexpr (E * B / 8 == 8) stm8(p, make_uint2(w[0], w[1]));
+    else stm4(p, w[0]);
 }
 
 // R8: the rank count is 8 (every workload here), known at compile time.  Otherwise the compiler, not
@@ -579,8 +579,8 @@ struct QReduceProducer {
         quantize_lane<B2, 8, LPG>(o, w, m);
         if (ok) {
             const uint32_t off = i - row.base;
-            if constexpr (B2 == 8) sts8(out_codes[row.s] + off, make_uint2(w[0], w[1]));
-            else sts4(out_codes[row.s] + off / 2, w[0]);
+            if constexpr (B2 == 8) stm8(out_codes[row.s] + off, make_uint2(w[0], w[1]));
+            else stm4(out_codes[row.s] + off / 2, w[0]);
             if (leader) out_meta[row.s][off >> log2g] = m;
         }
     }
