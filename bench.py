@@ -711,16 +711,18 @@ def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_firs
     c = max(1, min(20, nsets // 10))
     nchunk = min(30, nsets // c)
     chunks = [cx.graph(lambda k, i=i: step(i * c + k), c) for i in range(nchunk)]
-    evs = [cx.ev() for _ in range(nchunk + 1)]
+    rounds = -(-16 // nchunk)  # at least 16 samples: few buffer sets are walked several times
+    evs = [cx.ev() for _ in range(rounds * nchunk + 1)]
     torch.cuda.synchronize()
     evs[0].record()
-    for i, gc in enumerate(chunks):
-        gc.replay()
-        evs[i + 1].record()
+    for r in range(rounds):
+        for i, gc in enumerate(chunks):
+            gc.replay()
+            evs[r * nchunk + i + 1].record()
     torch.cuda.synchronize()
-    per = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 / c for i in range(nchunk))
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 / c for i in range(rounds * nchunk))
     pct = lambda q: round(per[min(len(per) - 1, int(q * (len(per) - 1) + 0.5))], 3)
-    spread = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "chunks": nchunk, "steps_per_chunk": c}
+    spread = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "chunks": rounds * nchunk, "steps_per_chunk": c}
     del chunks
 
     reps = kernel_reps or max(2, steps // nsets)
