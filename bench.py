@@ -62,8 +62,8 @@ ALL_ROWS = DEFAULT_ROWS + ",warm"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 60 on the prefill, 600 else)")
-    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default steps / 10)")
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 200 on the prefill, 600 else)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps before them (default: as many)")
     ap.add_argument("--config", default="llama3-70b-prefill",
                     choices=["tiny-r2-t4-h256", "llama3-8b-decode", "llama3-70b-prefill"],
                     help="headline two-step workload (default: the 70B prefill shard, the largest of the metric)")
@@ -85,9 +85,11 @@ def parse():
                                                           "OUT_MD"))
     args = ap.parse_args()
     if args.steps is None:
-        args.steps = 60 if args.config == "llama3-70b-prefill" else 600
+        args.steps = 200 if args.config == "llama3-70b-prefill" else 600
     if args.warmup is None:
-        args.warmup = max(1, args.steps // 10)
+        # the prefill step runs up to 10% slower over its first ~80 replayed steps on fresh buffers: as
+        # many warm-up steps as timed ones keep that transient out of the timed region
+        args.warmup = args.steps
     return args
 
 
@@ -596,6 +598,14 @@ class Ctx:
     def ev(self):
         return self.torch.cuda.Event(enable_timing=True)
 
+    def warm(self, g, ms: float = 30.0):
+        """Replay g until `ms` of wall time has passed (rows other than the headline: their buffers are
+        fresh, and the first milliseconds of replays on fresh buffers run slower)."""
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < ms:
+            g.replay()
+            self.torch.cuda.synchronize()
+
     def graph(self, fn, count):
         g = self.torch.cuda.CUDAGraph()
         with self.torch.cuda.graph(g):
@@ -653,7 +663,7 @@ def add_mixed(per_call, calls, ceil):
             c["pct_mixed_ceiling"] = round(100 * t / c["us"], 1)
 
 
-def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_first=False):
+def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_first=False, warm_ms=0.0):
     """The quantized two-step path: timed whole steps, then each call alone.  norm_first: the variant with
     the norm applied to each shard before the all-gather (gather of the normalized rows)."""
     torch = cx.torch
@@ -693,6 +703,8 @@ def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_firs
     for _ in range(max(1, warmup // nsets)):
         g_all.replay()
     torch.cuda.synchronize()
+    if warm_ms:
+        cx.warm(g_all, warm_ms)
     # timed region: exactly `steps` steps
     e0, e1 = cx.ev(), cx.ev()
     torch.cuda.synchronize()
@@ -735,7 +747,7 @@ def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_firs
                "gather_norm": lambda k: sets[k][0].all_gather(norm=sets[k][1])}
     per_call = {}
     # each call alone over the buffer sets, the calls taken in turn, `reps` rounds: every call samples the
-    # same stretch of the run (the engine clock drifts under sustained load; DESIGN section 8)
+    # same stretch of the run (the engine clock drifts under sustained load)
     graphs = {name: cx.graph(fn, nsets) for name, fn in fns.items()}
     samples = {name: [] for name in fns}
     for name, g in graphs.items():
@@ -812,6 +824,7 @@ def bench_share(cx, cfg, steps, warmup, kernel_reps, norm_first=False):
     for _ in range(max(1, warmup // nsets)):
         g_all.replay()
     torch.cuda.synchronize()
+    cx.warm(g_all)
     reps = max(1, steps // nsets)
     us_step = cx.time_graph(g_all, reps, nsets)
     if norm_first:
@@ -875,6 +888,7 @@ def bench_ll(cx):
             cnt.zero_()
     g = cx.graph(lambda k: sets[k][1].run(e), nsets)
     g0 = cx.graph(lambda k: sets[k][4].run(e), nsets)  # the same receiver without counters
+    cx.warm(g0)
     t1, t2, t0 = [], [], []
     for _ in range(5):
         set_epochs(late_ep)
@@ -940,6 +954,7 @@ def bench_ll_gather(cx):
             _lib.fc_ll_gather(slots, nwords, B, e, out, stale, done, cnt if counted else None)
         g = cx.graph(run, nsets)
         g0 = cx.graph(lambda k: run(k, False), nsets)  # the same pass without counters
+        cx.warm(g0)
         t1, t2, t0 = [], [], []
         for _ in range(5):
             set_epochs(True)
@@ -1126,9 +1141,12 @@ def bench_rmsnorm_overlap(cx):
 
     def gemm():
         torch.matmul(A, Bm, out=C)
-    # warm up
-    for h in halves:
-        h.run(stream=s1)
+    # warm up (the first milliseconds on fresh buffers run slower)
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < 30.0:
+        for h in halves:
+            h.run(stream=s1)
+        torch.cuda.synchronize()
     with torch.cuda.stream(s2):
         gemm()
     torch.cuda.synchronize()
@@ -1288,7 +1306,7 @@ def main():
     extra = {}
     if "decode" in rows or "prefill" in rows:
         so = 600 if other is dg.DECODE_8B else 30
-        ro = bench_two_step(cx, other, so, so // 10, False, 0, load_traffic(other))
+        ro = bench_two_step(cx, other, so, so // 10, False, 0, load_traffic(other), warm_ms=30.0)
         add_mixed(ro["per_call"], bm.two_step_whole(other.R, other.T, other.H, other.bits_rs, other.bits_ag,
                                                     other.group), ceil)
         vo = ro["step_bytes"] / (ro["ms_step"] * 1e-3) / 1e9
@@ -1299,7 +1317,7 @@ def main():
                                            "calls": ro["per_call"]}
     if "warm" in rows and not args.warm:
         # context, not the headline: inputs already in the caches, as right after the GEMM that produced them
-        rw = bench_two_step(cx, cfg, args.steps, args.warmup, True, args.kernel_reps, None)
+        rw = bench_two_step(cx, cfg, args.steps, args.warmup, True, args.kernel_reps, None, warm_ms=30.0)
         vw = rw["step_bytes"] / (rw["ms_step"] * 1e-3) / 1e9
         extra["warm_caches"] = {"workload": cfg.name, "mode": "one buffer set, cache-resident",
                                 "us_per_step": round(rw["ms_step"] * 1e3, 3), "GB/s": round(vw, 1),
@@ -1311,7 +1329,7 @@ def main():
     if "normfirst" in rows:
         for c in (dg.PREFILL_70B, dg.DECODE_8B):
             st = 30 if c is dg.PREFILL_70B else 300
-            rw = bench_two_step(cx, c, st, st // 10, False, 0, None, norm_first=True)
+            rw = bench_two_step(cx, c, st, st // 10, False, 0, None, norm_first=True, warm_ms=30.0)
             vw = rw["step_bytes"] / (rw["ms_step"] * 1e-3) / 1e9
             extra[f"norm_first_{c.slug}"] = {
                 "workload": c.name, "mode": "whole emulated all-reduce, norm before the all-gather",

@@ -420,7 +420,7 @@ hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s)
     return hipGetLastError();
 }
 
-// Read and write ceilings, each in the access shape that measured fastest on the box over 1 GiB (graph-
+// Read and write ceilings, each in the access shape that measured fastest on one MI355X over 1 GiB (graph-
 // free back-to-back launches, three passes): reads as one streamed 16-byte load per lane in 1024-lane
 // workgroups (7.50 TB/s; 7.06 in 256-lane ones, 6.98 with four loads per lane), writes as one write-back
 // 16-byte store per lane in 256-lane workgroups (6.95 TB/s; 6.84 streamed, 6.03 with four streamed stores
