@@ -173,7 +173,7 @@ def profile_report(config, stats_csv, fetch_csv, write_csv, valu_csv, out_md):
     med = {k: statistics.median(v) for k, v in pmc.items()}
     traffic = load_traffic(cfg)
     headline = cfg is dg.PREFILL_70B  # the default workload
-    runs = " --steps 30 --warmup 5" if headline else f" --config {config} --steps 290 --warmup 10"
+    runs = "" if headline else f" --config {config}"  # the default steps and warm-up of the benchmark
     x = " --steps 4 --warmup 1 --kernel-reps 1" if headline else f" --config {config} --steps 290 --warmup 0 --kernel-reps 1"
     base = "python3 bench.py --no-cpu-baseline --rows none"
     lines = [f"# Two-step all-reduce kernels on the {cfg.name} workload", "",
