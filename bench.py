@@ -757,12 +757,30 @@ def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_firs
         for name, g in graphs.items():
             samples[name].append(_once(cx, g, nsets))
     del graphs
+    # each call inside the step: the steps launched one call at a time in step order, an event pair around
+    # every call (so each kernel runs after the same predecessor as in the timed steps, with the messages
+    # of its own step in the caches); the kernels' average duration there is the roofline's
+    in_step = {name: [] for name in fns}
+    names = list(fns)
+    for _ in range(reps):
+        evs = [[cx.ev() for _ in range(len(names) + 1)] for _ in range(nsets)]
+        for k in range(nsets):
+            evs[k][0].record()
+            for j, name in enumerate(names):
+                fns[name](k)
+                evs[k][j + 1].record()
+        torch.cuda.synchronize()
+        for k in range(nsets):
+            for j, name in enumerate(names):
+                in_step[name].append(evs[k][j].elapsed_time(evs[k][j + 1]) * 1e3)
     for name in fns:
         us = statistics.median(samples[name])
         by = bm.total(calls[name])
         gbps = by / (us * 1e-6) / 1e9
+        us_in = statistics.fmean(in_step[name])
         per_call[name] = {"us": round(us, 3), "bytes": by, "GB/s": round(gbps, 1),
-                          "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
+                          "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4), "us_in_step": round(us_in, 3),
+                          "GB/s_in_step": round(by / (us_in * 1e-6) / 1e9, 1),
                           "traffic": None if norm_first else traffic_for(name, cfg, traffic)}
     del sets, g_all, g_tail
     torch.cuda.empty_cache()
@@ -1291,13 +1309,16 @@ def main():
         "bytes_per_step": main_r["step_bytes"],
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2), "pct_copy_ceiling": round(100 * value / copy_gbps, 2),
         "ceilings_GBps": {k: round(v, 1) for k, v in ceil.items()},
-        "calls": {k: {"us": v["us"], "GBps": v["GB/s"], "frac": v["frac_hbm"], "pct_mix": v.get("pct_mixed_ceiling")}
-                  for k, v in per_call.items()},
+        "calls": {k: {"us": v["us"], "GBps": v["GB/s"], "frac": v["frac_hbm"], "pct_mix": v.get("pct_mixed_ceiling"),
+                      "us_in_step": v["us_in_step"]} for k, v in per_call.items()},
+        # the dominant kernel's average duration inside the step (event pairs around each launch, in step
+        # order), as a kernel trace of the same run averages it
         "roofline": {"bound": "hbm", "kernel": dom + (f" ({tr['kernel'].split('(')[0].replace('void ', '')})"
                                                       if tr else ""),
-                     "achieved": per_call[dom]["GB/s"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": per_call[dom]["frac_hbm"], "traffic": tr["total"] if tr else None,
-                     "algorithmic_bytes": per_call[dom]["bytes"]},
+                     "achieved": per_call[dom]["GB/s_in_step"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(per_call[dom]["GB/s_in_step"] / HBM_PEAK_GBPS, 4),
+                     "traffic": tr["total"] if tr else None, "algorithmic_bytes": per_call[dom]["bytes"],
+                     "us": per_call[dom]["us_in_step"]},
         "wall_s": round(main_r["wall"], 3),
     }
     rows = set(DEFAULT_ROWS.split(",")) if args.rows == "default" else set(ALL_ROWS.split(",")) \
