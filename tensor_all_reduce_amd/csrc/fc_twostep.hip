@@ -641,19 +641,22 @@ __global__ __launch_bounds__(BT * RPB) void k_rows(const int64_t rows, const int
         const typename P::Row pr = p.begin_row(rbase, a0, a1);
         uint32_t idx[CPT];
         bool ok[CPT];
-        typename P::Raw raw[CPT];
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             const int ch = t + k * BT;
             ok[k] = has_row && ch < nch;
             idx[k] = rbase + min(ch, nch - 1) * 8;
-            p.fetch(sh, pr, idx[k], raw[k], a0, a1);
         }
+        // the residual first: its addresses need no pointer table, so its loads go out while the row's
+        // table entries are still on their way (decode gather + norm 3.18 -> 3.04 us)
         uint4 rres[CPT];
         if (na.residual) {
 #pragma unroll
             for (int k = 0; k < CPT; ++k) rres[k] = lds16(na.residual + idx[k]);
         }
+        typename P::Raw raw[CPT];
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) p.fetch(sh, pr, idx[k], raw[k], a0, a1);
         float h[CPT][8];
         float ss = 0.0f;
         float pk[CPT];
