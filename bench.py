@@ -764,6 +764,7 @@ def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_firs
     names = list(fns)
     for _ in range(reps):
         evs = [[cx.ev() for _ in range(len(names) + 1)] for _ in range(nsets)]
+        g_all.replay()  # keeps the GPU busy while the host enqueues the calls, so no pair spans an idle GPU
         for k in range(nsets):
             evs[k][0].record()
             for j, name in enumerate(names):
