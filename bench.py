@@ -585,6 +585,9 @@ def oracle_by_config(max_elems=1 << 22):
 
 
 # ---------------------------------------------------------------------------------------------------------
+LEAD_CYCLES = 300_000  # the spin kernel's length (about 125 us at the engine clock)
+
+
 class Ctx:
     def __init__(self):
         import numpy as np
@@ -613,12 +616,23 @@ class Ctx:
                 fn(k)
         return g
 
+    def lead(self, stream=None):
+        """A spin kernel of ~125 us ahead of a start event: the GPU stays busy while the host submits the
+        work that follows, so the timed span never holds an idle GPU waiting for the first launch (a graph
+        launch takes the host 15-80 us)."""
+        if stream is None:
+            self.torch.cuda._sleep(LEAD_CYCLES)
+        else:
+            with self.torch.cuda.stream(stream):
+                self.torch.cuda._sleep(LEAD_CYCLES)
+
     def time_graph(self, g, reps, per):
         """Replay `g` reps times; microseconds per item (per = items per replay)."""
         torch = self.torch
         g.replay()
         torch.cuda.synchronize()
         a, b = self.ev(), self.ev()
+        self.lead()
         a.record()
         for _ in range(reps):
             g.replay()
@@ -640,6 +654,7 @@ def copy_ceiling(cx):
         _lib.fc_bandwidth_probe(src, dst, nb, mode)
         torch.cuda.synchronize()
         a, b = cx.ev(), cx.ev()
+        cx.lead()
         a.record()
         for _ in range(10):
             _lib.fc_bandwidth_probe(src, dst, nb, mode)
@@ -709,6 +724,7 @@ def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_firs
     e0, e1 = cx.ev(), cx.ev()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
+    cx.lead()
     e0.record()
     for _ in range(steps // nsets):
         g_all.replay()
@@ -726,6 +742,7 @@ def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_firs
     rounds = -(-16 // nchunk)  # at least 16 samples: few buffer sets are walked several times
     evs = [cx.ev() for _ in range(rounds * nchunk + 1)]
     torch.cuda.synchronize()
+    cx.lead()
     evs[0].record()
     for r in range(rounds):
         for i, gc in enumerate(chunks):
@@ -1112,6 +1129,7 @@ def bench_encodings(cx, fit_out=None):
 def _once(cx, g, per):
     torch = cx.torch
     a, b = cx.ev(), cx.ev()
+    cx.lead()
     a.record()
     g.replay()
     b.record()
@@ -1152,6 +1170,7 @@ def bench_rmsnorm_overlap(cx):
     def timed(stream, fn):
         ea, eb = cx.ev(), cx.ev()
         with torch.cuda.stream(stream):
+            cx.lead(stream)
             ea.record()
             for _ in range(reps):
                 fn()
@@ -1179,6 +1198,7 @@ def bench_rmsnorm_overlap(cx):
         alone = ea.elapsed_time(eb) * 1e3 / reps
         # overlapped: both streams start after a common event
         start = cx.ev()
+        cx.lead()
         start.record(torch.cuda.current_stream())
         s1.wait_event(start)
         s2.wait_event(start)
@@ -1239,6 +1259,7 @@ def bench_layer(cx):
             ts = []
             for _ in range(reps):
                 a = cx.ev()
+                cx.lead()
                 a.record(torch.cuda.current_stream())
                 s1.wait_event(a)
                 s2.wait_event(a)
