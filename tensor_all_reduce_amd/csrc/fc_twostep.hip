@@ -7,8 +7,9 @@
 // moves whole cache lines.  A lane therefore holds 8 consecutive bf16 elements (or 16 codes) per
 // instruction, and a quantization group spans G/8 (or G/16) aligned lanes whose min/max are combined
 // with DPP.  One exception: the norm-before-gather reduce gives a lane 16 consecutive elements, so its
-// codes stay contiguous per instruction and its residual takes two 16-byte accesses 32 bytes apart.  Intermediate fp32 values stay in registers; RMSNorm row sums use DPP inside a wavefront and
-// LDS across wavefronts.  Nothing here is a contraction, so matrix cores are not used.
+// codes stay contiguous per instruction and its residual takes two 16-byte accesses 32 bytes apart.
+// Intermediate fp32 values stay in registers; RMSNorm row sums use DPP inside a wavefront and LDS across
+// wavefronts.  Nothing here is a contraction, so matrix cores are not used.
 #include <type_traits>
 
 #include "fc_device.h"
