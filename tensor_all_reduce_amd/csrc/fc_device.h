@@ -243,6 +243,18 @@ __device__ __forceinline__ float meta_zero(uint32_t m) { return f16_to_f32(m >> 
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
+// base + a 32-bit byte offset: with a wavefront-uniform base the load or store takes the base in scalar
+// registers and one 32-bit offset register per lane, where element-indexed pointer arithmetic would
+// build a 64-bit address in two vector registers per access.
+template <class T>
+__device__ __forceinline__ T* at(T* base, uint32_t byte_off) {
+    return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off);
+}
+template <class T>
+__device__ __forceinline__ const T* at(const T* base, uint32_t byte_off) {
+    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 __device__ __forceinline__ uint4 lds16(const void* p) {

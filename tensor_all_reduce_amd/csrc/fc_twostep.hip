@@ -432,9 +432,9 @@ struct GatherProducer {
             mp = sh.meta[s];
             off = i - s * L;
         }
-        raw.meta = mp[off >> log2g];
-        if constexpr (BITS == 8) raw.codes = lds8(cp + off);
-        else raw.codes = make_uint2(lds4(cp + off / 2), 0u);
+        raw.meta = *reinterpret_cast<const uint32_t*>(at(mp, (off >> log2g) << 2));
+        if constexpr (BITS == 8) raw.codes = lds8(at(cp, off));
+        else raw.codes = make_uint2(lds4(at(cp, off / 2)), 0u);
     }
     __device__ __forceinline__ void decode(const Raw& raw, float (&y)[8], const Row&, uint32_t, uint32_t, int) const {
         const float sc = meta_scale(raw.meta), z = meta_zero(raw.meta);
@@ -488,11 +488,11 @@ struct BF16ReduceProducer {
         };
         // first batch outside the loop: its loads wait for nothing but the kernel arguments
 #pragma unroll
-        for (int j = 0; j < RB; ++j) a[j] = lds16(parts[j] + i);
+        for (int j = 0; j < RB; ++j) a[j] = lds16(at(parts[j], 2 * i));
         fold(0);
         for (int r0 = RB; r0 < (int)R; r0 += RB) {
 #pragma unroll
-            for (int j = 0; j < RB; ++j) a[j] = lds16(parts[r0 + j] + i);
+            for (int j = 0; j < RB; ++j) a[j] = lds16(at(parts[r0 + j], 2 * i));
             fold(r0);
         }
     }
@@ -621,7 +621,7 @@ __global__ __launch_bounds__(BT * RPB) void k_rows(const int64_t rows, const int
     if constexpr (P::kNeedsSync) __syncthreads();
     const int H = na.hidden;
     const int nch = H >> 3;
-    const int sub = threadIdx.x / BT;           // row slot inside the workgroup
+    const int sub = RPB == 1 ? 0 : threadIdx.x / BT;  // row slot inside the workgroup
     const int t = threadIdx.x - sub * BT;       // lane inside the row
     const int lane = threadIdx.x & 63, wid = t >> 6;
     // Loads are never issued inside a lane-divergent branch (the compiler would wait for each one before
@@ -633,7 +633,7 @@ __global__ __launch_bounds__(BT * RPB) void k_rows(const int64_t rows, const int
     uint4 g[kHoistGamma ? CPT : 1];  // kept as bf16 words until used, so that nothing waits for it early
     if constexpr (kHoistGamma) {
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) g[k] = ld16(na.gamma + min(t + k * BT, nch - 1) * 8);
+        for (int k = 0; k < CPT; ++k) g[k] = ld16(at(na.gamma, (uint32_t)min(t + k * BT, nch - 1) * 16));
     }
     for (int64_t row0 = (int64_t)blockIdx.x * RPB; row0 < rows; row0 += (int64_t)gridDim.x * RPB) {
         const int64_t row = row0 + sub;
@@ -653,7 +653,7 @@ __global__ __launch_bounds__(BT * RPB) void k_rows(const int64_t rows, const int
         uint4 rres[CPT];
         if (na.residual) {
 #pragma unroll
-            for (int k = 0; k < CPT; ++k) rres[k] = lds16(na.residual + idx[k]);
+            for (int k = 0; k < CPT; ++k) rres[k] = lds16(at(na.residual, 2 * idx[k]));
         }
         typename P::Raw raw[CPT];
 #pragma unroll
@@ -670,7 +670,7 @@ __global__ __launch_bounds__(BT * RPB) void k_rows(const int64_t rows, const int
 #pragma unroll
                 for (int e = 0; e < 8; ++e) h[k][e] = h[k][e] + rv[e];
             }
-            if (na.residual_out && ok[k]) sts16(na.residual_out + idx[k], pack_bf16x8(h[k]));
+            if (na.residual_out && ok[k]) sts16(at(na.residual_out, 2 * idx[k]), pack_bf16x8(h[k]));
             if constexpr (kTreeSum) {
                 float q = h[k][0] * h[k][0];
 #pragma unroll
@@ -724,7 +724,7 @@ __global__ __launch_bounds__(BT * RPB) void k_rows(const int64_t rows, const int
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             float gk[8];
-            uint4 gw = kHoistGamma ? g[k] : ld16(na.gamma + (idx[k] - rbase));
+            uint4 gw = kHoistGamma ? g[k] : ld16(at(na.gamma, 2 * (idx[k] - rbase)));
             // Keeps the unpacking (and the wait for the gamma load) here: hoisted out of the row loop, it
             // would hold back every load of the first row until gamma has arrived.
             asm volatile("" : "+v"(gw.x), "+v"(gw.y), "+v"(gw.z), "+v"(gw.w));
@@ -736,7 +736,7 @@ __global__ __launch_bounds__(BT * RPB) void k_rows(const int64_t rows, const int
                 o[e] = a * gk[e];
             }
             if constexpr (P::kOutBits == 0) {
-                if (ok[k]) sts16(na.out + idx[k], pack_bf16x8(o));
+                if (ok[k]) sts16(at(na.out, 2 * idx[k]), pack_bf16x8(o));
             } else {
                 p.store(pr, idx[k], o, ok[k], t + k * BT, a1);  // every lane: the group reduction needs them all
             }
