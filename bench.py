@@ -149,6 +149,15 @@ def pmc_summary(fetch_csv, write_csv, out_path):
     print("\n".join(lines))
 
 
+def _rp_out(csv_path):
+    """The rocprofv3 output options (-d DIR -o NAME) that wrote `csv_path` (DIR/NAME_<table>.csv)."""
+    d, f = os.path.split(csv_path)
+    for table in ("_kernel_stats.csv", "_counter_collection.csv"):
+        if f.endswith(table):
+            return f"-d {d} -o {f[:-len(table)]}"
+    raise ValueError(f"{csv_path}: not a rocprofv3 kernel-stats or counter-collection table")
+
+
 def profile_report(config, stats_csv, fetch_csv, write_csv, valu_csv, out_md):
     """The profile summary of one two-step workload (profiles/two_step_<slug>.md) from four rocprofv3 runs of
     the benchmark: --kernel-trace --stats, then --pmc FETCH_SIZE, --pmc WRITE_SIZE and
@@ -179,7 +188,7 @@ def profile_report(config, stats_csv, fetch_csv, write_csv, valu_csv, out_md):
     lines = [f"# Two-step all-reduce kernels on the {cfg.name} workload", "",
              "Kernel durations from a rocprofv3 kernel trace of the benchmark (run from the repository root on one "
              "MI355X; the benchmark replays each call from HIP graphs over cold buffer sets):", "", "```",
-             f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/st_{config} -o st -- {base}{runs}",
+             f"rocprofv3 --kernel-trace --stats --output-format csv {_rp_out(stats_csv)} -- {base}{runs}",
              "```", "", "| kernel | calls | avg us | min us | max us | algorithmic bytes | GB/s at avg |",
              "|---|---|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
@@ -196,9 +205,8 @@ def profile_report(config, stats_csv, fetch_csv, write_csv, valu_csv, out_md):
               "HBM traffic per launch from two counter runs (FETCH_SIZE, then WRITE_SIZE), scaled by what the same "
               "counters read for the 1 GiB copy kernel, and vector-ALU instructions per wavefront and per byte "
               f"from a third run (kernel sources {sources_sha()}):", "", "```"]
-    for i, ctr in enumerate(("FETCH_SIZE", "WRITE_SIZE", "SQ_INSTS_VALU SQ_WAVES")):
-        lines.append(f"timeout -s KILL 240 rocprofv3 --pmc {ctr} --output-format csv -d gpurun_out/pmc{i}_{config} "
-                     f"-o pmc{i} -- {base}{x}")
+    for ctr, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv), ("SQ_INSTS_VALU SQ_WAVES", valu_csv)):
+        lines.append(f"timeout -s KILL 240 rocprofv3 --pmc {ctr} --output-format csv {_rp_out(path)} -- {base}{x}")
     lines += ["```", "", f"Summarised with `python bench.py --profile-report {config} STATS FETCH WRITE VALU {out_md}`.",
               "", "| kernel | fetch bytes | algorithmic read | write bytes | algorithmic write | VALU instr / wavefront "
               "| VALU instr / algorithmic byte (per wavefront lane-op: x64) |", "|---|---|---|---|---|---|---|"]
@@ -368,13 +376,13 @@ def rows_pmc_report(stats_csv, fetch_csv, write_csv, bytes_json, out_md):
     copy = next(k for k in f if "k_copy" in k)
     fs, ws = (1 << 30) / (f[copy] * 1024), (1 << 30) / (w[copy] * 1024)
     stats = {r["Name"]: r for r in csv.DictReader(open(stats_csv))}
-    cmd = "python3 bench.py --pmc-rows gpurun_out/pmc_rows_bytes.json"
+    cmd = f"python3 bench.py --pmc-rows {bytes_json}"
     lines = ["# Row kernels: durations and HBM traffic per launch", "",
              "One workload per kernel, launched over 3 rotating buffer sets (together larger than the L2s), in "
              "four runs of the same command on one MI355X (run from the repository root, under /tmp as TMPDIR):", "",
-             "```", f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/sr -o sr -- {cmd}",
-             f"timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/fr -o fr -- {cmd}",
-             f"timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/wr -o wr -- {cmd}",
+             "```", f"rocprofv3 --kernel-trace --stats --output-format csv {_rp_out(stats_csv)} -- {cmd}",
+             f"timeout -s KILL 240 rocprofv3 --pmc FETCH_SIZE --output-format csv {_rp_out(fetch_csv)} -- {cmd}",
+             f"timeout -s KILL 240 rocprofv3 --pmc WRITE_SIZE --output-format csv {_rp_out(write_csv)} -- {cmd}",
              "```", "",
              f"Counters are scaled by what they read for the 1 GiB copy kernel (fetch x{fs:.4f}, write x{ws:.4f}); "
              f"summarised with `python bench.py --rows-pmc-report STATS FETCH WRITE BYTES_JSON {out_md}` "
