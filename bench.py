@@ -743,8 +743,10 @@ def bench_two_step(cx, cfg, steps, warmup, warm, kernel_reps, traffic, norm_firs
     wall = time.perf_counter() - w0
     ms_step = e0.elapsed_time(e1) / steps
 
-    # spread: the same steps replayed in chunks of c consecutive buffer sets, one event pair per chunk
-    c = max(1, min(20, nsets // 10))
+    # spread: the same steps replayed in chunks of c consecutive buffer sets, one event pair per chunk.  An
+    # event recorded between two replays costs about 5 us on the prefill step (its completion signal waits
+    # for the work before it), so a chunk holds several steps: every set when there are few of them
+    c = nsets if nsets < 10 else max(1, min(20, nsets // 10))
     nchunk = min(30, nsets // c)
     chunks = [cx.graph(lambda k, i=i: step(i * c + k), c) for i in range(nchunk)]
     rounds = -(-16 // nchunk)  # at least 16 samples: few buffer sets are walked several times
