@@ -2,7 +2,8 @@
 
 Sizes span several workgroups with a ragged last one; edge-case groups (constants, signed zeros, fp16
 subnormal range, top of the fp16 range, half-step ties, huge outliers); the workload shapes in full
-where the oracle is quick, and the 70B-prefill shape (8 ranks x 4096 x 8192, int4) on sampled groups."""
+where the oracle is quick, the 70B-prefill shape (8 ranks x 4096 x 8192, int4) on sampled groups, and
+inputs large enough for the several-chunks-per-lane kernel shape in full for every code width and group."""
 import numpy as np
 import pytest
 
@@ -93,3 +94,19 @@ def test_quantize_70b_prefill_sampled(fc, orc):
     assert_equal_bits(m[idx], rm, "meta (sampled)")
     cb = G * bits // 8
     assert_equal_bits(c.reshape(ngroups, cb)[idx].ravel(), rc, "codes (sampled)")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("group", [32, 64, 128, 256])
+def test_quantize_many_chunks_full(fc, orc, bits, group):
+    """Inputs of at least 4096 x 1024 chunks of 8 take the kernel shape with several chunks per lane (2 for
+    4-bit codes, 4 for 8-bit), whose per-group step runs in one lane per group and slot and is broadcast
+    back to the group's lanes: every group width, with whole groups past the last full tile.  Compared in
+    full (33.6 M elements)."""
+    from gpu_helpers import assert_equal_bits
+    n = 4096 * 1024 * 8 + group * 37
+    xb = dg.synth_bf16((bits, group, 77), n, sigma=1.0, outlier_p=0.01, outlier_factor=40.0)
+    c, m = run_quantize(fc, xb, bits, group)
+    rc, rm = orc.quantize(xb, bits, group)
+    assert_equal_bits(m, rm, f"meta bits={bits} G={group}")
+    assert_equal_bits(c, rc, f"codes bits={bits} G={group}")
