@@ -3,10 +3,11 @@
 
   * the reduce-scatter's 16-element chunks per lane (chosen once a launch has 2048 workgroups of them):
     8 ranks x 8 shards of a little over 2^20 elements, every (b1, b2) pair and group, a ragged last
-    workgroup; codes and meta bit-exact;
-  * the all-gather + residual-add + RMSNorm epilogue in its 256-lane, 4-chunk row shape (more than 256
-    rows of 8192): 4-bit and 8-bit payloads, several groups; y and residual_out bit-exact, out within
-    2 ulp.
+    workgroup, and rank counts of 3, 5 and 16 (the rank count known only at run time); codes and meta
+    bit-exact;
+  * the all-gather + residual-add + RMSNorm epilogue with more than 256 rows, in every row shape that
+    many rows select (256 x 1 to 1024 x 8 lanes x chunks), rows inside one shard or across shard
+    boundaries, 4-bit and 8-bit payloads, several groups; y and residual_out bit-exact, out within 2 ulp.
 
 The rank messages are drawn directly (uniform codes, fp16 scales and zero-points in a fixed range): the
 oracle's dequantization defines their values whatever produced them."""
@@ -72,6 +73,56 @@ def test_gather_norm_256_lane_rows(fc, orc, bits, group):
                          norm=dict(residual=up(res), gamma=up(gam), eps=1e-5, hidden=H, out=out, residual_out=rout))
     torch.cuda.synchronize()
     where = f"bits {bits} G={group}"
+    assert_equal_bits(down(y, np.uint16), y_ref, "y " + where)
+    assert_equal_bits(down(rout, np.uint16), rout_ref, "residual_out " + where)
+    assert_bf16_close(down(out, np.uint16), out_ref, 2, "out " + where)
+
+
+@pytest.mark.parametrize("R,b1,b2,group", [(16, 8, 8, 128), (16, 4, 8, 64), (5, 4, 4, 256), (3, 8, 4, 32)])
+def test_reduce_sixteen_element_chunks_other_rank_counts(fc, orc, R, b1, b2, group):
+    """The same chunk shape with the rank count known only at run time (two batches of loads at R = 16)."""
+    import torch
+    from gpu_helpers import assert_equal_bits, down, up
+    n_shards = R
+    L = -(-(2048 * 256 * 16) // n_shards) // group * group + group  # at least 2048 workgroups of 16-element chunks
+    rng = np.random.default_rng((R, b1, b2, group))
+    host = [_msg(rng, L, b1, group) for _ in range(n_shards * R)]
+    ins = [(up(c), up(m)) for c, m in host]
+    outs = [(torch.empty(L * b2 // 8, dtype=torch.uint8, device="cuda"),
+             torch.empty(L // group, dtype=torch.int32, device="cuda")) for _ in range(n_shards)]
+    fc.fc_reduce_shard(ins, R, L, b1, b2, group, outs)
+    torch.cuda.synchronize()
+    for s in (0, n_shards // 2, n_shards - 1):
+        chunk = host[s * R:(s + 1) * R]
+        rc, rm = orc.reduce_shard([c for c, _ in chunk], [m for _, m in chunk], L, b1, b2, group)
+        where = f"R={R} shard {s} bits {b1}->{b2} G={group}"
+        assert_equal_bits(down(outs[s][1], np.uint32), rm, "meta " + where)
+        assert_equal_bits(down(outs[s][0], np.uint8), rc, "codes " + where)
+
+
+@pytest.mark.parametrize("R,T,H,bits,group", [(8, 300, 2048, 8, 128), (8, 300, 4096, 4, 64), (4, 260, 16384, 8, 256),
+                                              (8, 264, 32768, 4, 128), (2, 258, 65536, 8, 32), (8, 300, 12288, 8, 128)])
+def test_gather_norm_many_rows(fc, orc, R, T, H, bits, group):
+    """More than 256 rows in each row shape (256 x 1, 256 x 2, 512 x 4, 1024 x 4, 1024 x 8 lanes x chunks);
+    T = 300 with 8 ranks puts rows across shard boundaries (the pointer table staged in LDS)."""
+    import torch
+    from gpu_helpers import assert_bf16_close, assert_equal_bits, down, up
+    n = T * H
+    L = n // R
+    rng = np.random.default_rng((R, T, H, bits, group))
+    shards = [_msg(rng, L, bits, group, scale_range=(1e-2, 3e-1), zero_range=(-2.0, 0.0)) for _ in range(R)]
+    res = (rng.standard_normal(n).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    gam = ((1.0 + 0.1 * rng.standard_normal(H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y_ref, out_ref, rout_ref = orc.gather([c for c, _ in shards], [m for _, m in shards], L, bits, group, plain=True,
+                                          residual=res, gamma=gam, eps=1e-5, hidden=H)
+    dsh = [(up(c), up(m)) for c, m in shards]
+    y = torch.empty(n, dtype=torch.int16, device="cuda")
+    out = torch.empty(n, dtype=torch.int16, device="cuda")
+    rout = torch.empty(n, dtype=torch.int16, device="cuda")
+    fc.fc_gather_dequant(dsh, L, bits, group, y=y,
+                         norm=dict(residual=up(res), gamma=up(gam), eps=1e-5, hidden=H, out=out, residual_out=rout))
+    torch.cuda.synchronize()
+    where = f"R={R} T={T} H={H} bits {bits} G={group}"
     assert_equal_bits(down(y, np.uint16), y_ref, "y " + where)
     assert_equal_bits(down(rout, np.uint16), rout_ref, "residual_out " + where)
     assert_bf16_close(down(out, np.uint16), out_ref, 2, "out " + where)
