@@ -7,7 +7,9 @@
     bit-exact;
   * the all-gather + residual-add + RMSNorm epilogue with more than 256 rows, in every row shape that
     many rows select (256 x 1 to 1024 x 8 lanes x chunks), rows inside one shard or across shard
-    boundaries, 4-bit and 8-bit payloads, several groups; y and residual_out bit-exact, out within 2 ulp.
+    boundaries, 4-bit and 8-bit payloads, several groups; y and residual_out bit-exact, out within 2 ulp;
+  * the unquantized reduce + RMSNorm with more than 256 rows in each row shape, and capped grids that
+    keep 2 or 4 rows in flight per workgroup.
 
 The rank messages are drawn directly (uniform codes, fp16 scales and zero-points in a fixed range): the
 oracle's dequantization defines their values whatever produced them."""
@@ -126,3 +128,28 @@ def test_gather_norm_many_rows(fc, orc, R, T, H, bits, group):
     assert_equal_bits(down(y, np.uint16), y_ref, "y " + where)
     assert_equal_bits(down(rout, np.uint16), rout_ref, "residual_out " + where)
     assert_bf16_close(down(out, np.uint16), out_ref, 2, "out " + where)
+
+
+@pytest.mark.parametrize("R,rows,H,mw", [(8, 300, 2048, 0), (16, 300, 4096, 0), (3, 260, 16384, 0), (8, 264, 32768, 0),
+                                         (2, 258, 65536, 0), (8, 400, 1024, 50), (8, 300, 8192, 64), (5, 520, 4096, 100),
+                                         (8, 300, 256, 32)])
+def test_reduce_rmsnorm_many_rows(fc, orc, R, rows, H, mw):
+    """The unquantized reduce + RMSNorm (TokenWeave, abstract) with more than 256 rows in each row shape,
+    and capped grids that keep 2 or 4 rows in flight per workgroup."""
+    import torch
+    from gpu_helpers import assert_bf16_close, assert_equal_bits, down, up
+    n = rows * H
+    rng = np.random.default_rng((R, rows, H, mw))
+    bf = lambda a: (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    parts = [bf(rng.standard_normal(n)) for _ in range(R)]
+    res, gam = bf(rng.standard_normal(n)), bf(1.0 + 0.1 * rng.standard_normal(H))
+    o, ro, _ = orc.reduce_rmsnorm(parts, rows, H, res, gam, 1e-5)
+    out = torch.empty(n, dtype=torch.int16, device="cuda")
+    rout = torch.empty(n, dtype=torch.int16, device="cuda")
+    fc.fc_reduce_rmsnorm([up(p) for p in parts], rows,
+                         dict(residual=up(res), gamma=up(gam), eps=1e-5, hidden=H, out=out, residual_out=rout),
+                         max_workgroups=mw)
+    torch.cuda.synchronize()
+    where = f"R={R} rows={rows} H={H} max_workgroups={mw}"
+    assert_equal_bits(down(rout, np.uint16), ro, "residual_out " + where)
+    assert_bf16_close(down(out, np.uint16), o, 2, "out " + where)
