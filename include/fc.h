@@ -154,8 +154,9 @@ fc_status fc_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, in
  * copied to out[r] (uint32 [nwords], host array of R device pointers, 8-byte aligned) and done is set; a
  * stale one is left untouched and pending.  counters[0] += stale (rank, block) pairs and counters[1] +=
  * pending pairs (the same pairs: nothing is reduced across ranks), in one 64-bit atomic add per
- * workgroup (counters 8-byte aligned, caller zeroes; or NULL: nothing counted, as above).  A done block's slots may still be read.  Calling
- * again after late blocks have been rewritten completes them.  nwords % block_slots == 0. */
+ * workgroup (counters 8-byte aligned, caller zeroes; or NULL: nothing counted, as above).  A done
+ * block's slots may still be read.  Calling again after late blocks have been rewritten completes them.
+ * nwords % block_slots == 0. */
 fc_status fc_ll_gather(const uint64_t* const* slots, int R, int64_t nwords, int block_slots, uint32_t epoch,
                        uint32_t* const* out, uint8_t* stale, uint8_t* done, uint32_t* counters, hipStream_t stream);
 
