@@ -49,3 +49,15 @@ def test_row_summary_stays_short():
     s = bench.row_summary(extra)
     assert len(s) == len(extra) + 1  # the all-gather row splits into its two payloads
     assert len(json.dumps(s)) < 2500
+
+
+def test_profile_commands_name_the_tables_they_came_from():
+    """The profile summaries print the rocprofv3 command of each table they read: output directory and
+    name come from the table's own path, whatever directory the run wrote to."""
+    import pytest
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench._rp_out("out/st_x/st_kernel_stats.csv") == "-d out/st_x -o st"
+    assert bench._rp_out("a/b/pmc1_counter_collection.csv") == "-d a/b -o pmc1"
+    with pytest.raises(ValueError):
+        bench._rp_out("a/b/st_kernel_trace.csv")
