@@ -66,6 +66,12 @@ def bf16_buffer(n: int, device) -> torch.Tensor:
     return torch.empty(n, dtype=i16, device=device)
 
 
+def _check_shards(n: int, R: int, group: int) -> None:
+    """The two-step layout needs R equal shards of whole groups."""
+    if R < 1 or n % R or (n // R) % group:
+        raise ValueError(f"T*H = {n} does not split into {R} shards of whole {group}-element groups")
+
+
 class TwoStepAllReduce:
     """Buffers and enqueue functions for the quantized two-step all-reduce of R emulated ranks.
 
@@ -81,7 +87,7 @@ class TwoStepAllReduce:
                  parts: torch.Tensor | None = None):
         self.R, self.T, self.H, self.b1, self.b2, self.G = R, T, H, bits_rs, bits_ag, group
         n = T * H
-        assert n % R == 0, "T*H must split into R shards"
+        _check_shards(n, R, group)
         self.n, self.L = n, n // R
         L = self.L
         dev = _device(device)
@@ -183,7 +189,9 @@ class TwoStepShare:
                  device="cuda", x: torch.Tensor | None = None):
         self.R, self.T, self.H, self.b1, self.b2, self.G, self.rank = R, T, H, bits_rs, bits_ag, group, rank
         n = T * H
-        assert n % R == 0 and 0 <= rank < R
+        _check_shards(n, R, group)
+        if not 0 <= rank < R:
+            raise ValueError(f"rank {rank} outside [0, {R})")
         self.n, self.L = n, n // R
         L, dev = self.L, _device(device)
         cb1, cb2, mb = L * bits_rs // 8, L * bits_ag // 8, L // group

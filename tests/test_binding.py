@@ -97,3 +97,17 @@ def test_epilogue_arguments_keep_their_tensors():
     del nm
     gc.collect()
     assert all(r() is None for r in refs)
+
+
+def test_shapes_must_split_into_shards_of_whole_groups():
+    """TwoStepAllReduce and TwoStepShare refuse shapes whose T*H does not split into R shards of whole
+    groups, and a rank outside [0, R), before allocating anything."""
+    from tensor_all_reduce_amd.flash_allreduce import TwoStepAllReduce, TwoStepShare
+    for R, T, H, G in ((3, 4, 256, 32), (8, 1, 4096, 1024 // 2 + 64), (0, 4, 256, 32), (8, 2, 128, 64)):
+        with pytest.raises(ValueError, match="shards of whole"):
+            TwoStepAllReduce(R, T, H, 8, 8, G, device="cpu")
+        with pytest.raises(ValueError, match="shards of whole"):
+            TwoStepShare(R, T, H, 8, 8, G, device="cpu")
+    for rank in (-1, 2):
+        with pytest.raises(ValueError, match="outside"):
+            TwoStepShare(2, 4, 256, 8, 8, 32, rank=rank, device="cpu")
