@@ -156,3 +156,96 @@ def test_slot_receiver_replays(fc, orc):
         assert_equal_bits(down(cnt, np.uint32), rc, f"counters replay {i}")
         assert_equal_bits(o[fin], ro[fin], f"out of completed blocks, replay {i}")
         assert np.all(o[~fin] == (0xA5 ^ i) * 0x0101), f"pending blocks written, replay {i}"
+
+
+@pytest.mark.parametrize("counted", [True, False])
+def test_all_gather_on_slots_replays(fc, orc, counted):
+    """The standalone all-gather on slots (8 ranks, 64-slot blocks, about 10% of the copies late, every
+    kind of wrong epoch word): between replays done, stale, counters and the outputs are reset or
+    poisoned; each replay copies the same blocks with the payload's bits and leaves the late ones pending."""
+    import torch
+    from gpu_helpers import assert_equal_bits, down, up
+    R, B, nblk, e = 8, 64, 300, 0x2A
+    nw = B * nblk
+    rng = np.random.default_rng(0x6A)
+    words = [rng.integers(0, 1 << 32, nw, dtype=np.uint64) for _ in range(R)]
+    slots_h = []
+    for r in range(R):
+        ep = np.full(nw, e, np.uint64)
+        for b in np.nonzero(rng.random(nblk) < 0.1)[0]:
+            if rng.random() < 0.5:
+                ep[b * B:(b + 1) * B] = int(rng.choice([e - 1, 0, e + 1, 0xFFFFFFFF ^ e]))
+            else:
+                ep[b * B + int(rng.integers(B))] = e - 1
+        slots_h.append((words[r] & np.uint64(0xFFFFFFFF)) | (ep << np.uint64(32)))
+    ro, rst, rdn, rc = orc.ll_gather(slots_h, nw, B, e)
+    slots = [up(s) for s in slots_h]
+    outs = [torch.empty(nw, dtype=torch.int32, device="cuda") for _ in range(R)]
+    stale = torch.empty(R * nblk, dtype=torch.uint8, device="cuda")
+    done = torch.zeros(R * nblk, dtype=torch.uint8, device="cuda")
+    cnt = torch.zeros(2, dtype=torch.int32, device="cuda") if counted else None
+
+    def call():
+        fc.fc_ll_gather(slots, nw, B, e, outs, stale, done, cnt)
+    g = _capture(call)
+    for i in range(REPLAYS):
+        _between(outs + [stale], i)
+        done.zero_()
+        if counted:
+            cnt.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        where = f"counted={counted} replay {i}"
+        assert_equal_bits(down(stale, np.uint8), np.asarray(rst).ravel(), "stale " + where)
+        assert_equal_bits(down(done, np.uint8), np.asarray(rdn).ravel(), "done " + where)
+        if counted:
+            assert_equal_bits(down(cnt, np.uint32), rc, "counters " + where)
+        fin = np.asarray(rdn).reshape(R, nblk).astype(bool)
+        for r in range(R):
+            o = down(outs[r], np.uint32)
+            ok = np.repeat(fin[r], B)
+            assert_equal_bits(o[ok], ro[r][ok], f"out[{r}] of copied blocks, " + where)
+            assert np.all(o[~ok] == np.uint32((0xA5 ^ i) * 0x01010101)), f"pending blocks of rank {r} written, {where}"
+
+
+def test_flag_receiver_replays(fc, orc):
+    """The flag receiver (8 ranks, 2048-element blocks, 15% of the flags wrong, a poll budget of 2, a
+    capped grid): every replay gives the oracle's out, stale, done and the same re-read count."""
+    import torch
+    from gpu_helpers import assert_equal_bits, down, up
+    cfg = dg.SLOTS
+    R, be, nblk, e = 8, 2048, 96, 0x51
+    n = be * nblk
+    xs = [dg.synth_bf16((be, R, r, 3), n) for r in range(R)]
+    fls, _ = zip(*[dg.stale_flags(cfg, r, nblk, epoch=e, p=0.15, salt=77) for r in range(R)])
+    ro, rst, rdn, rc = orc.flag_unpack_reduce(xs, fls, n, be, e)
+    pay, fl = [up(x) for x in xs], [up(f) for f in fls]
+    out = torch.empty(n, dtype=torch.int16, device="cuda")
+    stale = torch.empty(R * nblk, dtype=torch.uint8, device="cuda")
+    done = torch.zeros(nblk, dtype=torch.uint8, device="cuda")
+    cnt = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def call():
+        fc.fc_flag_unpack_reduce(pay, fl, n, be, e, out, stale, done, cnt, max_polls=2, max_workgroups=7)
+    done.zero_()
+    cnt.zero_()
+    g = _capture(call)
+    rereads = None
+    fin = np.repeat(np.asarray(rdn).astype(bool), be)
+    for i in range(REPLAYS):
+        _between([out, stale], i)
+        done.zero_()
+        cnt.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        c = down(cnt, np.uint32)
+        assert_equal_bits(down(stale, np.uint8), np.asarray(rst).ravel(), f"stale replay {i}")
+        assert_equal_bits(down(done, np.uint8), rdn, f"done replay {i}")
+        assert_equal_bits(c[:2], rc, f"counters replay {i}")
+        rereads = c[2] if rereads is None else rereads
+        assert c[2] == rereads and c[3] == 0, f"re-reads replay {i}"
+        o = down(out, np.uint16)
+        assert_equal_bits(o[fin], ro[fin], f"out of completed blocks, replay {i}")
+        assert np.all(o[~fin] == (0xA5 ^ i) * 0x0101), f"pending blocks written, replay {i}"
