@@ -249,3 +249,44 @@ def test_flag_receiver_replays(fc, orc):
         o = down(out, np.uint16)
         assert_equal_bits(o[fin], ro[fin], f"out of completed blocks, replay {i}")
         assert np.all(o[~fin] == (0xA5 ^ i) * 0x0101), f"pending blocks written, replay {i}"
+
+
+def test_one_gpu_share_replays(fc, orc):
+    """One GPU's share (rank 5 of the decode workload: its quantize, the reduce of shard 5, the gather +
+    epilogue of all shards), captured and replayed; the peers' chunks and the other shards' payloads are
+    the oracle's.  Every replay must rebuild the own message, the own shard's payload and the outputs."""
+    import torch
+    from gpu_helpers import assert_bf16_close, assert_equal_bits, down, up
+    from tensor_all_reduce_amd.flash_allreduce import TwoStepShare
+    cfg, rank = dg.DECODE_8B, 5
+    R, L, G, b1, b2 = cfg.R, cfg.L, cfg.group, cfg.bits_rs, cfg.bits_ag
+    parts = dg.partials(cfg)
+    res, gam = dg.residual(cfg), dg.gamma(cfg)
+    ref = orc.two_step(parts, b1, b2, G, residual=res, gamma=gam, eps=cfg.eps, hidden=cfg.H, plain=False)
+    sh = TwoStepShare(R, cfg.T, cfg.H, b1, b2, G, rank=rank, x=up(parts[rank]))
+    cb1, cb2, mb = L * b1 // 8, L * b2 // 8, L // G
+    for r in range(R):
+        if r != rank:
+            sh.inbox_codes[r].copy_(up(ref["codes1"][r, rank * cb1:(rank + 1) * cb1]).view(torch.uint8))
+            sh.inbox_meta[r].copy_(up(ref["meta1"][r, rank * mb:(rank + 1) * mb]).view(torch.int32))
+    for s in range(R):
+        if s != rank:
+            sh.codes2[s].copy_(up(ref["codes2"][s * cb2:(s + 1) * cb2]).view(torch.uint8))
+            sh.meta2[s].copy_(up(ref["meta2"][s * mb:(s + 1) * mb]).view(torch.int32))
+    out = torch.empty(cfg.n, dtype=torch.int16, device="cuda")
+    rout = torch.empty(cfg.n, dtype=torch.int16, device="cuda")
+    norm = sh.make_norm(up(gam), out, residual=up(res), residual_out=rout, eps=cfg.eps)
+    g = _capture(lambda: sh.run(norm=norm))
+    for i in range(REPLAYS):
+        _between([sh.codes1, sh.meta1, sh.codes2[rank], sh.meta2[rank], out, rout], i)
+        g.replay()
+        torch.cuda.synchronize()
+        where = f"replay {i}"
+        assert_equal_bits(down(sh.meta1, np.uint32), ref["meta1"][rank], "own message: meta, " + where)
+        assert_equal_bits(down(sh.codes1, np.uint8), ref["codes1"][rank], "own message: codes, " + where)
+        assert_equal_bits(down(sh.meta2[rank], np.uint32), ref["meta2"][rank * mb:(rank + 1) * mb],
+                          "own shard: meta, " + where)
+        assert_equal_bits(down(sh.codes2[rank], np.uint8), ref["codes2"][rank * cb2:(rank + 1) * cb2],
+                          "own shard: codes, " + where)
+        assert_equal_bits(down(rout, np.uint16), ref["residual_out"], "residual_out " + where)
+        assert_bf16_close(down(out, np.uint16), ref["out"], 2, "out " + where)
