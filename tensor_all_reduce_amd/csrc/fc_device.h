@@ -110,6 +110,21 @@ struct GroupQ {
     uint32_t meta;  // scale | zero << 16
 };
 
+// The quantizer's two quotients, correctly rounded (the IEEE results) without the division sequence: one
+// fma correction of an approximate quotient rounds them exactly.  Both are checked exhaustively on the GPU
+// against the IEEE division (the test-support library's self-check): div_by_qmax for every non-negative
+// finite float x and qmax = 15 and 255; recip_fp16 for every positive finite fp16 value s.
+template <int QMAX>
+__device__ __forceinline__ float div_by_qmax(float x) {
+    constexpr float r = 1.0f / (float)QMAX;  // RN(1 / qmax), folded at compile time
+    const float q0 = x * r;
+    return __builtin_fmaf(__builtin_fmaf(-q0, (float)QMAX, x), r, q0);
+}
+__device__ __forceinline__ float recip_fp16(float s) {
+    const float r0 = __builtin_amdgcn_rcpf(s);  // within one ulp
+    return __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
+}
+
 template <int BITS>
 __device__ __forceinline__ GroupQ group_params(float lo, float hi) {
     constexpr int QMAX = (1 << BITS) - 1;
@@ -120,9 +135,8 @@ __device__ __forceinline__ GroupQ group_params(float lo, float hi) {
     uint32_t sb = 0;
     float inv = 0.0f;
     if (diff != 0.0f) {
-        const float t = diff / (float)QMAX;
-        sb = f16_ru(t);
-        inv = 1.0f / f16_to_f32(sb);
+        sb = f16_ru(div_by_qmax<QMAX>(diff));   // diff >= 0: RN(diff / qmax)
+        inv = recip_fp16(f16_to_f32(sb));     // the scale is a positive fp16 value: RN(1 / s)
     }
     return GroupQ{z, inv, sb | (zb << 16)};
 }
