@@ -31,17 +31,20 @@ __device__ __forceinline__ uint32_t f16_rne(float x) {
 __device__ __forceinline__ float f16_to_f32(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
-// Largest fp16 <= v: nearest-even conversion, then one step toward -inf if it landed above v.
+// Largest fp16 <= v: nearest-even conversion, then one step toward -inf if it landed above v.  A step is
+// needed only when v < 0 or the result is positive: for a negative result (-0 included: -0 + 1 is the
+// negative subnormal 0x8001) the step is the next bit pattern up, for a positive one the next down; +0
+// never lands above v (a negative v converts to -0 or below).
 __device__ __forceinline__ uint32_t f16_rd(float v) {
-    uint32_t h = f16_rne(v);
-    if (f16_to_f32(h) > v) h = ((h & 0x7fffu) == 0) ? 0x8001u : ((h & 0x8000u) ? h + 1u : h - 1u);
-    return h;
+    const uint32_t h = f16_rne(v);
+    return f16_to_f32(h) > v ? ((h & 0x8000u) ? h + 1u : h - 1u) : h;
 }
-// Smallest fp16 >= v.
-__device__ __forceinline__ uint32_t f16_ru(float v) {
-    uint32_t h = f16_rne(v);
-    if (f16_to_f32(h) < v) h = ((h & 0x7fffu) == 0) ? 0x0001u : ((h & 0x8000u) ? h - 1u : h + 1u);
-    return h;
+// Smallest fp16 >= v, for v >= 0 (the only use: a group's range over qmax).  The nearest-even result
+// is then +0 or positive, and the next fp16 up is the next bit pattern (from +0, the smallest
+// subnormal).
+__device__ __forceinline__ uint32_t f16_ru_nonneg(float v) {
+    const uint32_t h = f16_rne(v);
+    return f16_to_f32(h) < v ? h + 1u : h;
 }
 
 // ---- wavefront reductions -------------------------------------------------------------------------
@@ -135,7 +138,7 @@ __device__ __forceinline__ GroupQ group_params(float lo, float hi) {
     uint32_t sb = 0;
     float inv = 0.0f;
     if (diff != 0.0f) {
-        sb = f16_ru(div_by_qmax<QMAX>(diff));   // diff >= 0: RN(diff / qmax)
+        sb = f16_ru_nonneg(div_by_qmax<QMAX>(diff));  // diff >= 0: RN(diff / qmax)
         inv = recip_fp16(f16_to_f32(sb));     // the scale is a positive fp16 value: RN(1 / s)
     }
     return GroupQ{z, inv, sb | (zb << 16)};

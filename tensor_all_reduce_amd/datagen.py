@@ -223,7 +223,8 @@ def synth_f32(seed, n: int, sigma: float = 1.0) -> np.ndarray:
 def adversarial_groups(group: int, seed: int = 0) -> np.ndarray:
     """bf16 bits of groups built to hit the quantizer's edge cases: constant groups, signed zeros, fp16
     subnormal-range values (zero-point not an fp16 value), values at the top of the fp16 range, exact
-    half-step ties on a power-of-two grid, one huge outlier among tiny values, all-negative groups."""
+    half-step ties on a power-of-two grid, one huge outlier among tiny values, all-negative groups, and
+    values below the fp16 subnormals with a negative minimum."""
     rng = np.random.default_rng(np.random.SeedSequence([0xFC, 0xAD, seed]))
     G = group
     gs = []
@@ -245,4 +246,9 @@ def adversarial_groups(group: int, seed: int = 0) -> np.ndarray:
     gs.append(o)
     gs.append(-np.abs(rng.standard_normal(G)).astype(np.float32) - 2.0)
     gs.append(np.linspace(-1, 1, G).astype(np.float32))
+    # below half the smallest fp16 subnormal, with a negative minimum: its nearest fp16 is -0, and the
+    # zero-point steps down from there to the negative subnormal
+    tiny = np.full(G, -1e-9, np.float32)
+    tiny[1::2] = 3e-9
+    gs.append(tiny)
     return f32_to_bf16_bits(np.concatenate(gs))
