@@ -135,12 +135,10 @@ __device__ __forceinline__ GroupQ group_params(float lo, float hi) {
     const uint32_t zb = f16_rd(lo);
     const float z = f16_to_f32(zb);
     const float diff = hi - z;
-    uint32_t sb = 0;
-    float inv = 0.0f;
-    if (diff != 0.0f) {
-        sb = f16_ru_nonneg(div_by_qmax<QMAX>(diff));  // diff >= 0: RN(diff / qmax)
-        inv = recip_fp16(f16_to_f32(sb));     // the scale is a positive fp16 value: RN(1 / s)
-    }
+    // Without a branch: diff >= 0, and the scale comes out +0 exactly when diff is 0 (the round-up of a
+    // positive quotient is at least the smallest subnormal); only the reciprocal needs the select.
+    const uint32_t sb = f16_ru_nonneg(div_by_qmax<QMAX>(diff));  // RN(diff / qmax), rounded up to fp16
+    const float inv = sb != 0 ? recip_fp16(f16_to_f32(sb)) : 0.0f;  // RN(1 / s) for a positive fp16 s
     return GroupQ{z, inv, sb | (zb << 16)};
 }
 
