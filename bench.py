@@ -1420,9 +1420,9 @@ def main():
         if args.oracle_by_config:
             detail["oracle_by_config"] = oracle_by_config()
     line["rows"] = row_summary(extra)
-    # the full records first, one line each (the last line is the compact headline record)
+    # the full records on stderr, one line each: stdout carries the one compact headline record
     for k, v in detail.items():
-        print(json.dumps({"detail": k, "record": v}), flush=True)
+        print(json.dumps({"detail": k, "record": v}), file=sys.stderr, flush=True)
     if args.detail_out:
         with open(args.detail_out, "w") as fh:
             json.dump(detail, fh, indent=1)
