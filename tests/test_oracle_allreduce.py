@@ -89,6 +89,38 @@ def test_fixed_ascending_rank_order(orc):
     assert np.all(S2 == np.float32(0.0))
 
 
+def test_two_step_folds_every_shard_in_ascending_rank_order(orc):
+    """The cancellation above at every position of a three-rank two-step run: ranks 0, 1 and 2 hold 2^15,
+    -2^15 and 2^-10 everywhere (constant fp16-exact groups dequantize exactly), so every shard's ascending
+    fold is exactly 2^-10 and so is every gathered value.  A shard that folded the ranks' chunks in
+    another order, or took another rank's chunk, would lose the 2^-10 or double a term."""
+    G, R = 32, 3
+    n = R * 2 * G
+    parts = [bf16(np.full(n, v)) for v in (2.0 ** 15, -(2.0 ** 15), 2.0 ** -10)]
+    res = orc.two_step(parts, 8, 8, G)
+    assert np.all(f32(res["y"]) == np.float32(2.0 ** -10))
+
+
+def test_requantization_takes_the_fp32_sums(orc):
+    """The all-gather payload is quantized from the fp32 sums themselves, not from their bf16 rounding.
+    Two ranks with 8-bit codes, fp16 scale 2^-10 and zero-point 1 dequantize exactly to 1 + q*2^-10, and
+    their sums 2 + (q0 + q1)*2^-10 are exact in fp32 but need up to 11 significant bits, more than bf16's
+    8.  The requantized message must be the quantizer (pinned on its own) applied to the exact sums,
+    computed here in double, and that differs from the quantizer applied to their bf16 rounding."""
+    G, L = 128, 512
+    rng = np.random.default_rng(77)
+    word = int(np.float16(2.0 ** -10).view(np.uint16)) | (int(np.float16(1.0).view(np.uint16)) << 16)
+    meta = np.full(L // G, word, np.uint32)
+    codes = [rng.integers(0, 256, L).astype(np.uint8) for _ in range(2)]
+    exact = (1.0 + codes[0] * 2.0 ** -10) + (1.0 + codes[1] * 2.0 ** -10)
+    assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)
+    oc, om = orc.reduce_shard(codes, [meta, meta], L, 8, 8, G)
+    wc, wm = orc.quantize(exact.astype(np.float32), 8, G)
+    assert np.array_equal(om, wm) and np.array_equal(oc, wc)
+    bc, bm = orc.quantize(f32(bf16(exact)), 8, G)
+    assert not (np.array_equal(bc, wc) and np.array_equal(bm, wm))
+
+
 @pytest.mark.parametrize("R", [1, 2])
 @pytest.mark.parametrize("bits", [4, 8])
 def test_grid_identity_small_R(orc, R, bits):

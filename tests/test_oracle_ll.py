@@ -100,6 +100,23 @@ def test_every_stale_word_detected(orc, e, kind):
     assert np.array_equal(f32(out[keep]).astype(np.float64), exact[keep])
 
 
+@pytest.mark.parametrize("pos", [0, 63])
+def test_torn_block_at_either_end(orc, pos):
+    """A copy whose only late slot is the first or the last of its block is stale."""
+    rng = np.random.default_rng(pos)
+    R, B, e, nblk = 2, 64, 40, 4
+    n = 2 * B * nblk
+    xs = [int_payload(rng, n) for _ in range(R)]
+    slots = [orc.ll_pack(x, B, e) for x in xs]
+    ep = np.full(n // 2, e, np.uint32)
+    ep[B + pos] = e + 1
+    slots[1] = set_epochs(slots[1], ep)
+    out, stale, done, cnt = orc.ll_unpack_reduce(slots, n, B, e)
+    want = np.zeros((R, nblk), np.uint8)
+    want[1, 1] = 1
+    assert np.array_equal(stale, want) and list(done) == [1, 0, 1, 1] and list(cnt) == [1, 1]
+
+
 def test_seeded_stale_mix_flags_and_retry(orc):
     """The workload's stale mix (2% of (rank, block) pairs, several kinds of wrong words): flags equal
     the injected set, counters count it, and after the late blocks are rewritten with the right epoch a
