@@ -262,13 +262,13 @@ def pmc_rows(out_json):
     out = torch.empty(n, dtype=torch.int16, device=dev)
     stale = torch.empty(R * nblk, dtype=torch.uint8, device=dev)
     done = torch.zeros(nblk, dtype=torch.uint8, device=dev)
-    cnt = torch.zeros(2, dtype=torch.int32, device=dev)
+    cnt = torch.zeros(_lib.COUNTER_WORDS, dtype=torch.int32, device=dev)
     for k in range(6):
         done.zero_()
         cnt.zero_()
         _lib.fc_ll_unpack_reduce(sets[k % 3], n, B, e, out, stale, done, cnt)
     torch.cuda.synchronize()
-    pend = int(cnt.cpu().numpy().view(np.uint32)[1])
+    pend = int(_lib.counter_totals(cnt)[1])
     algo["k_ll_unpack"] = bm.ll_unpack(R, n, B, completed_blocks=nblk - pend)
     del sets, out, stale, done, cnt
     # TokenWeave half A
@@ -304,13 +304,13 @@ def pmc_rows(out_json):
     gout = [torch.empty(nwords, dtype=torch.int32, device=dev) for _ in range(c3.R)]
     gst = torch.empty(c3.R * gblk, dtype=torch.uint8, device=dev)
     gdn = torch.zeros(c3.R * gblk, dtype=torch.uint8, device=dev)
-    gcnt = torch.zeros(2, dtype=torch.int32, device=dev)
+    gcnt = torch.zeros(_lib.COUNTER_WORDS, dtype=torch.int32, device=dev)
     for k in range(6):
         gdn.zero_()
         gcnt.zero_()
         _lib.fc_ll_gather(gsets[k % 3], nwords, B, e, gout, gst, gdn, gcnt)
     torch.cuda.synchronize()
-    gpend = int(gcnt.cpu().numpy().view(np.uint32)[1])
+    gpend = int(_lib.counter_totals(gcnt)[1])
     algo["k_ll_gather"] = bm.ll_gather(c3.R, nwords, B, completed_blocks=c3.R * gblk - gpend)
     del gsets, gout
     # f2 receivers, every block there
@@ -328,7 +328,7 @@ def pmc_rows(out_json):
     out2 = torch.empty(n2, dtype=torch.int16, device=dev)
     st2 = torch.empty(8 * (n2 // 64), dtype=torch.uint8, device=dev)
     dn2 = torch.zeros(n2 // 64, dtype=torch.uint8, device=dev)
-    c2 = torch.zeros(4, dtype=torch.int32, device=dev)
+    c2 = torch.zeros(_lib.COUNTER_WORDS, dtype=torch.int32, device=dev)
     for k in range(6):
         dn2.zero_()
         _lib.fc_flag_unpack_reduce(*fsets[k % 3], n2, be, 7, out2, st2, dn2, c2)
@@ -919,7 +919,7 @@ def bench_ll(cx):
         out = torch.zeros(n, dtype=torch.int16, device=cx.dev)
         stale = torch.zeros(R * nblk, dtype=torch.uint8, device=cx.dev)
         done = torch.zeros(nblk, dtype=torch.uint8, device=cx.dev)
-        cnt = torch.zeros(2, dtype=torch.int32, device=cx.dev)
+        cnt = torch.zeros(_lib.COUNTER_WORDS, dtype=torch.int32, device=cx.dev)
         sets.append((slots, LLUnpackReduce(slots, n, B, out, stale, done, cnt), done, cnt,
                      LLUnpackReduce(slots, n, B, out, stale, done, None)))
 
@@ -944,7 +944,7 @@ def bench_ll(cx):
         reset()
         torch.cuda.synchronize()
         t1.append(_once(cx, g, nsets))
-        cnt0 = sets[0][3].cpu().numpy().view(np.uint32).copy()
+        cnt0 = _lib.counter_totals(sets[0][3])
         set_epochs(None)
         torch.cuda.synchronize()
         t2.append(_once(cx, g, nsets))
@@ -987,7 +987,7 @@ def bench_ll_gather(cx):
             out = [torch.empty(nwords, dtype=torch.int32, device=cx.dev) for _ in range(R)]
             stale = torch.zeros(R * nblk, dtype=torch.uint8, device=cx.dev)
             done = torch.zeros(R * nblk, dtype=torch.uint8, device=cx.dev)
-            cnt = torch.zeros(2, dtype=torch.int32, device=cx.dev)
+            cnt = torch.zeros(_lib.COUNTER_WORDS, dtype=torch.int32, device=cx.dev)
             sets.append((words, slots, out, stale, done, cnt))
 
         def set_epochs(late):
@@ -1013,7 +1013,7 @@ def bench_ll_gather(cx):
                 s[5].zero_()
             torch.cuda.synchronize()
             t1.append(_once(cx, g, nsets))
-            pend = int(sets[0][5].cpu().numpy().view(np.uint32)[1])
+            pend = int(_lib.counter_totals(sets[0][5])[1])
             set_epochs(False)
             torch.cuda.synchronize()
             t2.append(_once(cx, g, nsets))
@@ -1064,7 +1064,7 @@ def bench_encodings(cx, fit_out=None):
                 out = torch.empty(n, dtype=torch.int16, device=cx.dev)
                 stale = torch.empty(R * nblk, dtype=torch.uint8, device=cx.dev)
                 done = torch.zeros(nblk, dtype=torch.uint8, device=cx.dev)
-                cnt = torch.zeros(4, dtype=torch.int32, device=cx.dev)
+                cnt = torch.zeros(_lib.COUNTER_WORDS, dtype=torch.int32, device=cx.dev)
 
                 def receive(e, stream):
                     if enc == "ll":
@@ -1093,7 +1093,7 @@ def bench_encodings(cx, fit_out=None):
                     send(e, sb)
                     b.record(xa)
                     torch.cuda.synchronize()
-                    c = cnt.cpu().numpy().view(np.uint32)
+                    c = _lib.counter_totals(cnt)
                     ok = ok and int(c[1]) == 0
                     live.append(a.elapsed_time(b) * 1e3)
                     # the receiver alone, every block already there

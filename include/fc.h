@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define FC_ABI_VERSION 4
+#define FC_ABI_VERSION 5
 
 typedef enum {
     FC_OK = 0,
@@ -122,6 +122,18 @@ fc_status fc_gather_dequant(const fc_qmsg* shards, int R, int64_t L, int bits, i
 fc_status fc_reduce_rmsnorm(const uint16_t* const* parts, int R, int64_t rows, const fc_norm* norm,
                             int max_workgroups, hipStream_t stream);
 
+/* Receiver counters (fc_ll_unpack_reduce, fc_ll_gather, fc_ll_poll_unpack_reduce, fc_flag_unpack_reduce).
+ * A counters buffer is FC_COUNTER_WORDS uint32 words, 8-byte aligned, zeroed by the caller (the calls
+ * add to it): FC_COUNTER_GROUPS groups of counter words, group g starting at word g * FC_COUNTER_STRIDE.  A workgroup of a receiver adds its counts to group (its index mod
+ * FC_COUNTER_GROUPS); the total of count k is the sum of word k over the groups.  Device-scope atomics
+ * on one address complete one at a time, and a receiver's workgroups all count at about the same time,
+ * at the end: spread over eight addresses 512 bytes apart they no longer queue on one (8-rank slot
+ * receiver, pass 1: 10.0 -> 8.2 us).  counters may be NULL: nothing is counted and no atomic is issued
+ * (the stale and done flags hold every verdict). */
+#define FC_COUNTER_GROUPS 8
+#define FC_COUNTER_STRIDE 128
+#define FC_COUNTER_WORDS (FC_COUNTER_GROUPS * FC_COUNTER_STRIDE)
+
 /* Epochs (every call below that takes one): the readiness evidence is a comparison with `epoch` and
  * nothing else, so a buffer must not already hold the epoch of a message it has not yet received: a
  * caller uses a new epoch for each message through the same buffers, never one that an earlier message
@@ -134,13 +146,11 @@ fc_status fc_reduce_rmsnorm(const uint16_t* const* parts, int R, int64_t rows, c
  * done[b] == 0: stale[r*nblk + b] = 1 if any slot of rank r's copy carries an epoch word != epoch, else
  * 0; if no rank is stale the block is reduced (fp32 left fold in ascending rank order, bf16 out) and
  * done[b] = 1, otherwise out is left untouched and the block is pending.  Blocks with done[b] != 0 are
- * skipped: nothing of theirs is written (their slots may still be read).  counters[0] += stale
- * (rank, block) pairs seen, counters[1] += pending blocks, both in one 64-bit atomic add per workgroup:
- * counters must be 8-byte aligned (FC_E_ALIGN otherwise) and counters[0] must not wrap (a call adds at
- * most R*nblk < 2^29); the caller zeroes counters.  counters may be NULL: then nothing is counted and no
- * atomic is issued (the stale and done flags hold every verdict; device-scope atomics on one address
- * serialize, so the count costs time).  Calling again after late blocks have been rewritten
- * completes them with the same bits as if they had been on time.  n % (2*block_slots) == 0. */
+ * skipped: nothing of theirs is written (their slots may still be read).  counters (FC_COUNTER_WORDS,
+ * grouped as above, or NULL): count 0 += stale (rank, block) pairs seen, count 1 += pending blocks, in
+ * one 64-bit atomic add per workgroup; count 0 must not wrap (a call adds at most R*nblk < 2^29).
+ * Calling again after late blocks have been rewritten completes them with the same bits as if they had
+ * been on time.  n % (2*block_slots) == 0. */
 fc_status fc_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, int block_slots, uint32_t epoch,
                               uint16_t* out, uint8_t* stale, uint8_t* done, uint32_t* counters,
                               hipStream_t stream);
@@ -152,11 +162,10 @@ fc_status fc_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, in
  * consecutive slots; nblk = nwords / block_slots.  For each (rank r, block b) with done[r*nblk + b] == 0:
  * stale[r*nblk + b] = 1 if any slot carries an epoch word != epoch, else 0; a valid block's words are
  * copied to out[r] (uint32 [nwords], host array of R device pointers, 8-byte aligned) and done is set; a
- * stale one is left untouched and pending.  counters[0] += stale (rank, block) pairs and counters[1] +=
- * pending pairs (the same pairs: nothing is reduced across ranks), in one 64-bit atomic add per
- * workgroup (counters 8-byte aligned, caller zeroes; or NULL: nothing counted, as above).  A done
- * block's slots may still be read.  Calling again after late blocks have been rewritten completes them.
- * nwords % block_slots == 0. */
+ * stale one is left untouched and pending.  counters (FC_COUNTER_WORDS, grouped as above, or NULL):
+ * count 0 += stale (rank, block) pairs and count 1 += pending pairs (the same pairs: nothing is reduced
+ * across ranks), in one 64-bit atomic add per workgroup.  A done block's slots may still be read.
+ * Calling again after late blocks have been rewritten completes them.  nwords % block_slots == 0. */
 fc_status fc_ll_gather(const uint64_t* const* slots, int R, int64_t nwords, int block_slots, uint32_t epoch,
                        uint32_t* const* out, uint8_t* stale, uint8_t* done, uint32_t* counters, hipStream_t stream);
 
@@ -178,11 +187,10 @@ fc_status fc_ll_pack(const uint16_t* const* x, int R, int64_t n, int block_slots
  * that rank's slots of the tile after a short sleep, at most max_polls times (0..2^20; 0 = one look, with
  * the results of fc_ll_unpack_reduce); the verdicts are those of the last look.  max_workgroups > 0 caps
  * the grid (the tiles are then walked with a stride), leaving compute units to a sender running at the
- * same time; 0 = one tile per wavefront.  counters: uint32 [4], 8-byte aligned, zeroed by the caller
- * (or NULL: nothing counted):
- * [0] stale (rank, block) pairs and [1] pending blocks at the last look (one 64-bit atomic add per
- * workgroup), [2] += re-reads summed over wavefronts, [3] unused.  The call always ends: a block still
- * stale after the budget is left pending for a later call. */
+ * same time; 0 = one tile per wavefront.  counters (FC_COUNTER_WORDS, grouped as above, or NULL):
+ * count 0 stale (rank, block) pairs and count 1 pending blocks at the last look (one 64-bit atomic add
+ * per workgroup), count 2 += re-reads summed over wavefronts, count 3 unused.  The call always ends: a
+ * block still stale after the budget is left pending for a later call. */
 fc_status fc_ll_poll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, int block_slots, uint32_t epoch,
                                    int max_polls, int max_workgroups, uint16_t* out, uint8_t* stale, uint8_t* done,
                                    uint32_t* counters, hipStream_t stream);

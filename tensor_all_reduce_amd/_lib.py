@@ -87,7 +87,7 @@ def _load():
     return lib
 
 
-ABI_VERSION = 4  # the argument lists above follow include/fc.h at this FC_ABI_VERSION
+ABI_VERSION = 5  # the argument lists above follow include/fc.h at this FC_ABI_VERSION
 
 _lib = _load()
 lib = _lib
@@ -208,13 +208,28 @@ def fc_reduce_rmsnorm(parts, rows: int, norm: dict, max_workgroups: int = 0, str
     _check(_lib.fc_reduce_rmsnorm(arr, R, rows, C.byref(nm), max_workgroups, _stream(stream)), "fc_reduce_rmsnorm")
 
 
+# Receiver counters (include/fc.h): COUNTER_GROUPS groups of words COUNTER_STRIDE words apart, one group
+# per workgroup index mod COUNTER_GROUPS; a count's total is the sum of its word over the groups.
+COUNTER_GROUPS, COUNTER_STRIDE = 8, 128
+COUNTER_WORDS = COUNTER_GROUPS * COUNTER_STRIDE
+COUNTER_BYTES = 4 * COUNTER_WORDS
+
+
+def counter_totals(counters, ncounts: int = 4):
+    """The first `ncounts` counts of a receiver's counters buffer (a tensor of COUNTER_WORDS 32-bit words,
+    read back to the host), summed over the groups: numpy uint64 [ncounts]."""
+    import numpy as np
+    w = counters.detach().cpu().numpy().view(np.uint32).reshape(COUNTER_GROUPS, COUNTER_STRIDE)
+    return w[:, :ncounts].astype(np.uint64).sum(axis=0)
+
+
 def fc_ll_unpack_reduce(slots, n: int, block_slots: int, epoch: int, out, stale, done, counters, stream=None) -> None:
     R = len(slots)
     n, nblk = max(0, n), max(0, n) // 2 // max(1, block_slots)
     arr = (C.c_void_p * R)(*[_dev(s, 4 * n, "slots") for s in slots])
     _check(_lib.fc_ll_unpack_reduce(arr, R, n, block_slots, epoch & 0xFFFFFFFF, _dev(out, 2 * n, "out"),
                                     _dev(stale, R * nblk, "stale"), _dev(done, nblk, "done"),
-                                    _dev(counters, 8, "counters"), _stream(stream)), "fc_ll_unpack_reduce")
+                                    _dev(counters, COUNTER_BYTES, "counters"), _stream(stream)), "fc_ll_unpack_reduce")
 
 
 def fc_ll_gather(slots, nwords: int, block_slots: int, epoch: int, out, stale, done, counters, stream=None) -> None:
@@ -226,7 +241,7 @@ def fc_ll_gather(slots, nwords: int, block_slots: int, epoch: int, out, stale, d
     sa = (C.c_void_p * R)(*[_dev(s, 8 * nw, "slots") for s in slots])
     oa = (C.c_void_p * R)(*[_dev(o, 4 * nw, "out") for o in out])
     _check(_lib.fc_ll_gather(sa, R, nwords, block_slots, epoch & 0xFFFFFFFF, oa, _dev(stale, R * nblk, "stale"),
-                             _dev(done, R * nblk, "done"), _dev(counters, 8, "counters"), _stream(stream)),
+                             _dev(done, R * nblk, "done"), _dev(counters, COUNTER_BYTES, "counters"), _stream(stream)),
            "fc_ll_gather")
 
 
@@ -256,20 +271,22 @@ def fc_ll_pack(x, block_slots: int, epoch: int, slots, block_order=None, n: int 
 
 def fc_ll_poll_unpack_reduce(slots, n: int, block_slots: int, epoch: int, out, stale, done, counters,
                              max_polls: int = 0, max_workgroups: int = 0, stream=None) -> None:
-    """counters: 4 int32 (stale pairs, pending blocks, re-reads, unused)."""
+    """counters: COUNTER_WORDS int32 or None; counts (counter_totals): stale pairs, pending blocks, re-reads."""
     R = len(slots)
     nn = max(0, n)
     nblk = nn // 2 // max(1, block_slots)
     arr = (C.c_void_p * R)(*[_dev(s, 4 * nn, "slots") for s in slots])
     _check(_lib.fc_ll_poll_unpack_reduce(arr, R, n, block_slots, epoch & 0xFFFFFFFF, max_polls, max_workgroups,
                                          _dev(out, 2 * nn, "out"), _dev(stale, R * nblk, "stale"),
-                                         _dev(done, nblk, "done"), _dev(counters, 16, "counters"), _stream(stream)),
+                                         _dev(done, nblk, "done"), _dev(counters, COUNTER_BYTES, "counters"),
+                                         _stream(stream)),
            "fc_ll_poll_unpack_reduce")
 
 
 def fc_flag_unpack_reduce(payload, flags, n: int, block_elems: int, epoch: int, out, stale, done, counters,
                           max_polls: int = 0, max_workgroups: int = 0, stream=None) -> None:
-    """payload: R bf16 (int16) buffers; flags: R int32 buffers of n / block_elems words; counters: 4 int32."""
+    """payload: R bf16 (int16) buffers; flags: R int32 buffers of n / block_elems words; counters as for
+    fc_ll_poll_unpack_reduce."""
     R = len(payload)
     _count(flags, R, "flags", "one per rank's payload")
     nn = max(0, n)
@@ -278,7 +295,7 @@ def fc_flag_unpack_reduce(payload, flags, n: int, block_elems: int, epoch: int, 
     fa = (C.c_void_p * R)(*[_dev(f, 4 * nblk, "flags") for f in flags])
     _check(_lib.fc_flag_unpack_reduce(pa, fa, R, n, block_elems, epoch & 0xFFFFFFFF, max_polls, max_workgroups,
                                       _dev(out, 2 * nn, "out"), _dev(stale, R * nblk, "stale"),
-                                      _dev(done, nblk, "done"), _dev(counters, 16, "counters"), _stream(stream)),
+                                      _dev(done, nblk, "done"), _dev(counters, COUNTER_BYTES, "counters"), _stream(stream)),
            "fc_flag_unpack_reduce")
 
 

@@ -38,8 +38,7 @@ SOURCES = ["fc_twostep.hip", "fc_slots.hip", "fc_live.hip", "fc_api.cpp"]
 # quantization codes depend on.  Packed fp32 instructions are disabled.  -fno-honor-nans on the kernels:
 # NaN inputs are outside the contract, and without NaNs fminf/fmaxf need no quieting of their operands,
 # which the compiler otherwise inserts before every min/max (and which blocks folding DPP moves).
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-function",
-          "-I", INCLUDE, "-I", CSRC]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-function", "-I", INCLUDE]
 # Kernel-argument preloading (gfx950): the leading kernel arguments (up to 16 dwords) are loaded into
 # registers at dispatch, so a kernel's first memory address does not wait for an argument fetch.  The
 # code object keeps a prologue that fetches them itself where the firmware does not preload.
@@ -64,17 +63,19 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, csrc: str = CSRC, lib: str = LIB, build_dir: str = BUILD_DIR) -> str:
+    """Compile the sources of `csrc` (default: the package's) into the shared library `lib` (default: the
+    in-tree libfc.so), with object files in `build_dir`.  Returns the library's path."""
+    os.makedirs(build_dir, exist_ok=True)
     from concurrent.futures import ThreadPoolExecutor
     jobs = []
     for src in SOURCES:
-        path = os.path.join(CSRC, src)
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        path = os.path.join(csrc, src)
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         if src.endswith(".hip"):
-            cmd = [HIPCC, *DEVICE, *COMMON, "-c", path, "-o", obj]
+            cmd = [HIPCC, *DEVICE, *COMMON, "-I", csrc, "-c", path, "-o", obj]
         else:
-            cmd = [HIPCC, *COMMON, *(HOST_SAN if SANITIZE else []), "-x", "c++", "-D__HIP_PLATFORM_AMD__",
+            cmd = [HIPCC, *COMMON, "-I", csrc, *(HOST_SAN if SANITIZE else []), "-x", "c++", "-D__HIP_PLATFORM_AMD__",
                    "-I/opt/rocm/include", "-c", path, "-o", obj]
         jobs.append((cmd, obj))
     with ThreadPoolExecutor(max_workers=len(jobs)) as ex:  # one compiler process per source file
@@ -84,12 +85,12 @@ def build(verbose: bool = False) -> str:
             print(out)
     objs = [obj for _, obj in jobs]
     tlib = torch_lib_dir()
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(HOST_SAN if SANITIZE else []), *objs, "-o", tmp,
            "-L" + tlib, "-l:libamdhip64.so", "-Wl,-rpath," + tlib, "-Wl,--no-undefined"]
     _run(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -321,7 +321,7 @@ fc_status fc_ll_unpack_reduce(const uint64_t* const* slots, int R, int64_t n, in
     if (!slots || !out || !stale || !done) return FC_E_NULL;
     if (!aligned(out, 16) || (counters && !aligned(counters, 8))) return FC_E_ALIGN;
     const int64_t nblk = n / 2 / block_slots;
-    const Range ro = rng(out, 2 * n), rs = rng(stale, (int64_t)R * nblk), rd = rng(done, nblk), rc = rng(counters, counters ? 8 : 0);
+    const Range ro = rng(out, 2 * n), rs = rng(stale, (int64_t)R * nblk), rd = rng(done, nblk), rc = rng(counters, counters ? 4 * FC_COUNTER_WORDS : 0);
     if (overlap(ro, rs) || overlap(ro, rd) || overlap(ro, rc) || overlap(rs, rd) || overlap(rs, rc) || overlap(rd, rc))
         return FC_E_ARG;
     for (int r = 0; r < R; ++r) {
@@ -351,7 +351,7 @@ fc_status fc_ll_gather(const uint64_t* const* slots, int R, int64_t nwords, int 
     if (!slots || !out || !stale || !done) return FC_E_NULL;
     if ((counters && !aligned(counters, 8))) return FC_E_ALIGN;
     const int64_t nblk = nwords / block_slots;
-    const Range rs = rng(stale, (int64_t)R * nblk), rd = rng(done, (int64_t)R * nblk), rc = rng(counters, counters ? 8 : 0);
+    const Range rs = rng(stale, (int64_t)R * nblk), rd = rng(done, (int64_t)R * nblk), rc = rng(counters, counters ? 4 * FC_COUNTER_WORDS : 0);
     if (overlap(rs, rd) || overlap(rs, rc) || overlap(rd, rc)) return FC_E_ARG;
     for (int r = 0; r < R; ++r) {
         if (!slots[r] || !out[r]) return FC_E_NULL;
@@ -427,7 +427,7 @@ fc_status fc_ll_poll_unpack_reduce(const uint64_t* const* slots, int R, int64_t 
     if (!slots || !out || !stale || !done) return FC_E_NULL;
     if (!aligned(out, 16) || (counters && !aligned(counters, 8))) return FC_E_ALIGN;
     const int64_t nblk = n / 2 / block_slots;
-    const Range ro = rng(out, 2 * n), rs = rng(stale, (int64_t)R * nblk), rd = rng(done, nblk), rc = rng(counters, counters ? 16 : 0);
+    const Range ro = rng(out, 2 * n), rs = rng(stale, (int64_t)R * nblk), rd = rng(done, nblk), rc = rng(counters, counters ? 4 * FC_COUNTER_WORDS : 0);
     if (overlap(ro, rs) || overlap(ro, rd) || overlap(ro, rc) || overlap(rs, rd) || overlap(rs, rc) || overlap(rd, rc))
         return FC_E_ARG;
     for (int r = 0; r < R; ++r) {
@@ -460,7 +460,7 @@ fc_status fc_flag_unpack_reduce(const uint16_t* const* payload, const uint32_t* 
     if (!payload || !flags || !out || !stale || !done) return FC_E_NULL;
     if (!aligned(out, 16) || (counters && !aligned(counters, 8))) return FC_E_ALIGN;
     const int64_t nblk = n / block_elems;
-    const Range ro = rng(out, 2 * n), rs = rng(stale, (int64_t)R * nblk), rd = rng(done, nblk), rc = rng(counters, counters ? 16 : 0);
+    const Range ro = rng(out, 2 * n), rs = rng(stale, (int64_t)R * nblk), rd = rng(done, nblk), rc = rng(counters, counters ? 4 * FC_COUNTER_WORDS : 0);
     if (overlap(ro, rs) || overlap(ro, rd) || overlap(ro, rc) || overlap(rs, rd) || overlap(rs, rc) || overlap(rd, rc))
         return FC_E_ARG;
     for (int r = 0; r < R; ++r) {

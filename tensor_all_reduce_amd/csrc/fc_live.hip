@@ -223,9 +223,10 @@ __global__ __launch_bounds__(256) void k_flag_unpack(const int64_t ntiles, const
     // wave 0 holds the counts: stale pairs and pending blocks in one 64-bit atomic (a call adds at most 2^29
     // stale pairs, so the low word does not carry), re-reads in one 32-bit atomic
     if (threadIdx.x == 0 && counters != nullptr) {  // counters == NULL: nothing is counted
+        uint32_t* const cg = counter_group(counters);
         if (n_stale | n_pending)
-            atomicAdd(reinterpret_cast<unsigned long long*>(counters), ((unsigned long long)n_pending << 32) | n_stale);
-        if (n_polls) atomicAdd(counters + 2, n_polls);
+            atomicAdd(reinterpret_cast<unsigned long long*>(cg), ((unsigned long long)n_pending << 32) | n_stale);
+        if (n_polls) atomicAdd(cg + 2, n_polls);
     }
 }
 
@@ -375,8 +376,9 @@ __global__ __launch_bounds__(256) void k_ll_poll(const int64_t nslots, const int
         const uint32_t st = s_cnt[0][0] + s_cnt[1][0] + s_cnt[2][0] + s_cnt[3][0];
         const uint32_t pe = s_cnt[0][1] + s_cnt[1][1] + s_cnt[2][1] + s_cnt[3][1];
         const uint32_t po = s_cnt[0][2] + s_cnt[1][2] + s_cnt[2][2] + s_cnt[3][2];
-        if (st | pe) atomicAdd(reinterpret_cast<unsigned long long*>(counters), ((unsigned long long)pe << 32) | st);
-        if (po) atomicAdd(counters + 2, po);
+        uint32_t* const cg = counter_group(counters);
+        if (st | pe) atomicAdd(reinterpret_cast<unsigned long long*>(cg), ((unsigned long long)pe << 32) | st);
+        if (po) atomicAdd(cg + 2, po);
     }
 }
 

@@ -118,6 +118,43 @@ __global__ __launch_bounds__(64 * W) void k_ll_unpack(const int64_t nslots, cons
         for (int j = 0; j < RB; ++j)
             if (r0 + j < R) ll_examine<LB, KI>(sv[j], r0 + j, epoch, amask, acc, vs);
     }
+    // Counters, from wavefront-uniform values only (scalar unit): block b of instruction k was examined
+    // iff the first lane of its lanes was active.  They are counted before the stores, so that the
+    // workgroup's atomic is on its way while the stores drain (pass 1 of the 8-rank slot workload, with the
+    // counts in eight groups: 8.23 -> 7.81 us, level with the uncounted pass).  counters == NULL: nothing
+    // is counted (the stale and done flags hold every verdict) and no atomic is issued.
+    if (counters != nullptr) {  // uniform
+        uint32_t n_stale = 0, n_pending = 0;
+#pragma unroll
+        for (int k = 0; k < KI; k += IB) {
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) {
+                const uint32_t v = IB == 2 ? (vs[k][0] | vs[k + 1][0]) : vs[k][b];
+                const uint32_t on = (uint32_t)(amask[k] >> (b * LB)) & 1u;
+                n_pending += on & s_nonzero(v);
+                n_stale += on * (uint32_t)__builtin_popcount(v);
+            }
+        }
+        if (lane == 0) {
+            s_cnt[threadIdx.x >> 6][0] = n_stale;
+            s_cnt[threadIdx.x >> 6][1] = n_pending;
+        }
+        __syncthreads();
+        // Both counts in one 64-bit atomic per workgroup, into the workgroup's counter group: device-scope
+        // atomics on one address serialize.  A call adds at most 2^29 stale pairs, so the low word does not
+        // carry.
+        if (threadIdx.x == 0) {
+            uint32_t st = 0, pe = 0;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                st += s_cnt[w][0];
+                pe += s_cnt[w][1];
+            }
+            if (st | pe)
+                atomicAdd(reinterpret_cast<unsigned long long*>(counter_group(counters)),
+                          ((unsigned long long)pe << 32) | st);
+        }
+    }
 #pragma unroll
     for (int k = 0; k < KI; ++k) {
         // this lane's block verdict; a two-instruction block (IB = 2) combines both instructions
@@ -146,44 +183,12 @@ __global__ __launch_bounds__(64 * W) void k_ll_unpack(const int64_t nslots, cons
             if ((IB == 1 || k % 2 == 0) && bl == 0) done[blk[k]] = 1;
         }
     }
-    // Counters, from wavefront-uniform values only (scalar unit): block b of instruction k was examined
-    // iff the first lane of its lanes was active.  counters == NULL: nothing is counted (the stale and done
-    // flags hold every verdict) and no atomic is issued.
-    if (counters == nullptr) return;  // uniform
-    uint32_t n_stale = 0, n_pending = 0;
-#pragma unroll
-    for (int k = 0; k < KI; k += IB) {
-#pragma unroll
-        for (int b = 0; b < NBW; ++b) {
-            const uint32_t v = IB == 2 ? (vs[k][0] | vs[k + 1][0]) : vs[k][b];
-            const uint32_t on = (uint32_t)(amask[k] >> (b * LB)) & 1u;
-            n_pending += on & s_nonzero(v);
-            n_stale += on * (uint32_t)__builtin_popcount(v);
-        }
-    }
-    if (lane == 0) {
-        s_cnt[threadIdx.x >> 6][0] = n_stale;
-        s_cnt[threadIdx.x >> 6][1] = n_pending;
-    }
-    __syncthreads();
-    // Both counters in one 64-bit atomic per workgroup: device-scope atomics on one address serialize,
-    // and the kernel ends only once the last one is done, so their number matters.  A call adds at most
-    // 2^29 stale pairs, so the low word does not carry.
-    if (threadIdx.x == 0) {
-        uint32_t st = 0, pe = 0;
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-            st += s_cnt[w][0];
-            pe += s_cnt[w][1];
-        }
-        if (st | pe) atomicAdd(reinterpret_cast<unsigned long long*>(counters), ((unsigned long long)pe << 32) | st);
-    }
 }
 
-// Wavefronts per workgroup and instructions per wavefront tile of the slot receiver.  The counters cost
-// one atomic per workgroup, and those atomics serialize, so larger workgroups mean fewer of them; one
-// instruction per tile gives twice the wavefronts of two, each with half the work after its loads land
-// (8-rank slot workload, pass 1 without counters: 8.8 us with 2 x 8, 8.3 us with 1 x 16, measured).
+// Wavefronts per workgroup and instructions per wavefront tile of the slot receiver.  One instruction per
+// tile gives twice the wavefronts of two, each with half the work after its loads land (8-rank slot
+// workload, pass 1 without counters: 8.8 us with 2 x 8, 8.3 us with 1 x 16, measured); large workgroups
+// also keep the counted pass at one atomic per 16 wavefronts.
 #ifndef FC_LL_WAVES
 #define FC_LL_WAVES 16
 #endif
@@ -323,14 +328,14 @@ __global__ __launch_bounds__(64 * W) void k_ll_gather(const int64_t nslots, cons
 #pragma unroll
         for (int w = 0; w < W; ++w) st += s_cnt[w];
         // stale pairs and pending pairs are the same pairs here; one 64-bit atomic adds both counters
-        if (st) atomicAdd(reinterpret_cast<unsigned long long*>(counters), ((unsigned long long)st << 32) | st);
+        if (st) atomicAdd(reinterpret_cast<unsigned long long*>(counter_group(counters)), ((unsigned long long)st << 32) | st);
     }
 }
 
-// Tile shape of the all-gather: counted, one atomic per workgroup, so large tiles (16 wavefronts of 4
-// instructions: fewer workgroups, fewer atomics on the one address); uncounted, smaller ones (8 wavefronts
-// of 2) keep more loads in flight.  int8 prefill messages, pass 1: counted 22.7 us (2 x 16: 26-27 us),
-// uncounted 19.6 us (4 x 16: 21.7 us).
+// Tile shape of the all-gather: 8 wavefronts of 2 instructions, counted or not (int8 prefill messages,
+// pass 1: 20.1 us uncounted, 20.3 us counted; 16 wavefronts of 4: 20.2 and 22.6 us; 4 x 16: 21.7 us
+// uncounted).  With the counts in eight groups, the smaller workgroups' atomics (one per workgroup) cost
+// next to nothing; into one address, they had cost 2.3 us more than the large tiles' fewer ones.
 
 hipError_t launch_ll_gather(const LLGatherParams& p, hipStream_t s) {
     LLGatherTabs t;
@@ -345,18 +350,12 @@ hipError_t launch_ll_gather(const LLGatherParams& p, hipStream_t s) {
         const dim3 grid((unsigned)((nslots + per_wg - 1) / per_wg), (unsigned)p.R);                        \
         k_ll_gather<B, W, K><<<grid, 64 * (W), 0, s>>>(nslots, nblk, p.done, p.stale, p.epoch, p.counters, t); \
     } while (0)
-#define FC_LLG_B(B) \
-    do {                                              \
-        if (p.counters) FC_LLG(B, 16, 4);             \
-        else FC_LLG(B, 8, 2);                         \
-    } while (0)
     switch (p.block_slots) {
-        case 32: FC_LLG_B(32); break;
-        case 64: FC_LLG_B(64); break;
-        case 128: FC_LLG_B(128); break;
-        default: FC_LLG_B(256); break;  // a 256-slot block spans two instructions (both shapes have 2 or 4)
+        case 32: FC_LLG(32, 8, 2); break;
+        case 64: FC_LLG(64, 8, 2); break;
+        case 128: FC_LLG(128, 8, 2); break;
+        default: FC_LLG(256, 8, 2); break;  // a 256-slot block spans the tile's two instructions
     }
-#undef FC_LLG_B
 #undef FC_LLG
     return hipGetLastError();
 }

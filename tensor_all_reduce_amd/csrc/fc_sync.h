@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fc.h"
 #include "fc_launch.h"
 
 namespace fc {
@@ -33,6 +34,13 @@ __device__ __forceinline__ uint64_t ld_relaxed(const uint64_t* p) {
 }
 __device__ __forceinline__ void st_relaxed(uint64_t* p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The counter group of this workgroup: the receivers' workgroups add their counts to FC_COUNTER_GROUPS
+// groups 512 bytes apart (by workgroup index), so that their device-scope atomics, all issued at about
+// the same time, do not queue on one address.
+__device__ __forceinline__ uint32_t* counter_group(uint32_t* counters) {
+    return counters + (blockIdx.x % FC_COUNTER_GROUPS) * FC_COUNTER_STRIDE;
 }
 
 // A slow sender, for runs where the receiver starts first: `pace` sleeps of 8 x 64 clocks.

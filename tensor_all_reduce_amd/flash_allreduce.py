@@ -274,7 +274,7 @@ class LLUnpackReduce:
         nblk = n // 2 // block_slots
         self._slots = (C.c_void_p * self.R)(*[_lib._dev(s, 4 * n, "slots") for s in slots])
         self._ptrs = (_lib._dev(out, 2 * n, "out"), _lib._dev(stale, self.R * nblk, "stale"),
-                      _lib._dev(done, nblk, "done"), _lib._dev(counters, 8, "counters"))
+                      _lib._dev(done, nblk, "done"), _lib._dev(counters, _lib.COUNTER_BYTES, "counters"))
         self._keep = (list(slots), out, stale, done, counters)  # raw addresses above: keep the tensors
 
     def run(self, epoch: int, stream=None):
@@ -318,7 +318,7 @@ class SelfSyncReduce:
         self.out = torch.zeros(n, dtype=torch.int16, device=device)
         self.stale = torch.zeros(R * self.nblk, dtype=torch.uint8, device=device)
         self.done = torch.zeros(self.nblk, dtype=torch.uint8, device=device)
-        self.counters = torch.zeros(4, dtype=torch.int32, device=device)
+        self.counters = torch.zeros(_lib.COUNTER_WORDS, dtype=torch.int32, device=device)
 
     def inbox(self):
         return self.slots if self.encoding == "ll" else (self.payload, self.flags)

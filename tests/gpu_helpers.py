@@ -16,6 +16,18 @@ def down(t: torch.Tensor, dtype) -> np.ndarray:
     return t.detach().cpu().contiguous().numpy().view(dtype)
 
 
+def counters_buf() -> torch.Tensor:
+    """A zeroed receiver counters buffer (the library's grouped layout)."""
+    from tensor_all_reduce_amd import _lib
+    return torch.zeros(_lib.COUNTER_WORDS, dtype=torch.int32, device=DEV)
+
+
+def counts(cnt: torch.Tensor, k: int = 2) -> np.ndarray:
+    """The first k counts of a receiver counters buffer, summed over its groups (uint32)."""
+    from tensor_all_reduce_amd import _lib
+    return _lib.counter_totals(cnt, k).astype(np.uint32)
+
+
 def ulp_dist(a, b):
     def ordv(u):
         u = np.asarray(u, np.uint16).astype(np.int64)

@@ -17,7 +17,7 @@ def build() -> str:
     src = os.path.join(HERE, "fc_selfcheck.hip")
     tlib = b.torch_lib_dir()
     tmp = LIB + ".tmp%d" % os.getpid()
-    b._run([b.HIPCC, *b.DEVICE, *b.COMMON, "-shared", src, "-o", tmp, "-L" + tlib, "-l:libamdhip64.so",
+    b._run([b.HIPCC, *b.DEVICE, *b.COMMON, "-I", b.CSRC, "-shared", src, "-o", tmp, "-L" + tlib, "-l:libamdhip64.so",
             "-Wl,-rpath," + tlib, "-Wl,--no-undefined"])
     os.replace(tmp, LIB)
     return LIB

@@ -32,7 +32,16 @@ def test_exports_every_declared_function(L):
             "fc_ll_pack", "fc_copy", "fc_bandwidth_probe", "fc_status_string", "fc_last_hip_error", "fc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L.lib, n), n
-    assert L.fc_abi_version() == 4
+    assert L.fc_abi_version() == 5
+
+
+def test_counter_layout_matches_the_header(L):
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define (FC_COUNTER_\w+) (\d+)", text))
+    assert int(defs["FC_COUNTER_GROUPS"]) == L.COUNTER_GROUPS and int(defs["FC_COUNTER_STRIDE"]) == L.COUNTER_STRIDE
+    assert L.COUNTER_WORDS == L.COUNTER_GROUPS * L.COUNTER_STRIDE and L.COUNTER_BYTES == 4 * L.COUNTER_WORDS
+    # groups 512 bytes apart, so that each 64-bit count pair sits on its own cache lines
+    assert 4 * L.COUNTER_STRIDE == 512
 
 
 def test_single_hip_runtime(L):
@@ -184,7 +193,8 @@ def test_ll_validation(L):
     assert g(out=None) == L.FC_E_NULL
     assert g(out=A + 0x3000008) == L.FC_E_ALIGN
     assert g(cnt=A + 0x6000002) == L.FC_E_ALIGN
-    assert g(cnt=A + 0x6000004) == L.FC_E_ALIGN    # both counters take one 64-bit atomic: 8-byte aligned
+    assert g(cnt=A + 0x6000004) == L.FC_E_ALIGN    # both counts take one 64-bit atomic: 8-byte aligned
+    assert g(cnt=A + 0x5000000 - 4 * L.COUNTER_WORDS + 8) == L.FC_E_ARG  # the last counter group reaches into done
     # counters may be NULL (nothing counted); every other check still applies (no call here launches)
     assert g(cnt=None, n=0) == L.FC_OK
     assert g(cnt=None, done=None) == L.FC_E_NULL
@@ -230,7 +240,8 @@ def test_ll_poll_validation(L):
     assert g(cnt=A + 0x6000004) == L.FC_E_ALIGN
     assert g(out=A + 0x3000008) == L.FC_E_ALIGN
     assert g(s=(C.c_void_p * 2)(A + 0x1000008, A + 0x2000000)) == L.FC_E_ALIGN
-    assert g(cnt=A + 0x5000000 - 8) == L.FC_E_ARG                    # counter words 2..3 reach into done
+    assert g(cnt=A + 0x5000000 - 8) == L.FC_E_ARG                    # the counter groups reach into done
+    assert g(cnt=A + 0x5000000 - 4 * L.COUNTER_WORDS + 8) == L.FC_E_ARG
     assert g(out=A + 0x2000000 + 64) == L.FC_E_ARG                   # out inside rank 1's slots
 
 

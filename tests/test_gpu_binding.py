@@ -38,18 +38,18 @@ def test_slot_receiver_checks_every_buffer():
     out = torch.empty(n, dtype=torch.int16, device="cuda")
     stale = torch.empty(R * nblk, dtype=torch.uint8, device="cuda")
     done = torch.zeros(nblk, dtype=torch.uint8, device="cuda")
-    cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(_lib.COUNTER_WORDS, dtype=torch.int32, device="cuda")
     for args, what in [((slots[:1] + [slots[1][:-1]], out, stale, done, cnt), "slots"),
                        ((slots, out[:-1], stale, done, cnt), "out"),
                        ((slots, out, stale[:-1], done, cnt), "stale"),
                        ((slots, out, stale, done[:-1], cnt), "done"),
-                       ((slots, out, stale, done, cnt[:1]), "counters")]:
+                       ((slots, out, stale, done, cnt[:-1]), "counters")]:
         s, o, st, d, c = args
         with pytest.raises(ValueError, match=what):
             _lib.fc_ll_unpack_reduce(s, n, B, 1, o, st, d, c)
     _lib.fc_ll_unpack_reduce(slots, n, B, 1, out, stale, done, cnt)  # epoch 1 against zero slots: all stale
     torch.cuda.synchronize()
-    assert int(cnt[1]) == nblk and int(done.sum()) == 0
+    assert int(_lib.counter_totals(cnt)[1]) == nblk and int(done.sum()) == 0
 
 
 def test_temporaries_passed_to_the_epilogue_stay_allocated():

@@ -124,7 +124,7 @@ def test_slot_receiver_replays(fc, orc):
     between replays the done flags and counters are reset and out, stale poisoned; each replay flags the
     same pairs, completes the same blocks with the oracle's bits and leaves the pending ones untouched."""
     import torch
-    from gpu_helpers import assert_equal_bits, down, up
+    from gpu_helpers import assert_equal_bits, counters_buf, counts, down, up
     from tensor_all_reduce_amd.flash_allreduce import LLUnpackReduce
     cfg = dg.SLOTS
     R, n, B, e = cfg.R, cfg.n, cfg.block_slots, cfg.epoch
@@ -139,7 +139,7 @@ def test_slot_receiver_replays(fc, orc):
     out = torch.empty(n, dtype=torch.int16, device="cuda")
     stale = torch.empty(R * nblk, dtype=torch.uint8, device="cuda")
     done = torch.zeros(nblk, dtype=torch.uint8, device="cuda")
-    cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
+    cnt = counters_buf()
     rx = LLUnpackReduce(slots, n, B, out, stale, done, cnt)
     g = _capture(lambda: rx.run(e))
     fin = np.repeat(rdn.astype(bool), 2 * B)
@@ -153,7 +153,7 @@ def test_slot_receiver_replays(fc, orc):
         o = down(out, np.uint16)
         assert_equal_bits(down(stale, np.uint8), rst.ravel(), f"stale replay {i}")
         assert_equal_bits(down(done, np.uint8), rdn, f"done replay {i}")
-        assert_equal_bits(down(cnt, np.uint32), rc, f"counters replay {i}")
+        assert_equal_bits(counts(cnt), rc, f"counters replay {i}")
         assert_equal_bits(o[fin], ro[fin], f"out of completed blocks, replay {i}")
         assert np.all(o[~fin] == (0xA5 ^ i) * 0x0101), f"pending blocks written, replay {i}"
 
@@ -164,7 +164,7 @@ def test_all_gather_on_slots_replays(fc, orc, counted):
     kind of wrong epoch word): between replays done, stale, counters and the outputs are reset or
     poisoned; each replay copies the same blocks with the payload's bits and leaves the late ones pending."""
     import torch
-    from gpu_helpers import assert_equal_bits, down, up
+    from gpu_helpers import assert_equal_bits, counters_buf, counts, down, up
     R, B, nblk, e = 8, 64, 300, 0x2A
     nw = B * nblk
     rng = np.random.default_rng(0x6A)
@@ -183,7 +183,7 @@ def test_all_gather_on_slots_replays(fc, orc, counted):
     outs = [torch.empty(nw, dtype=torch.int32, device="cuda") for _ in range(R)]
     stale = torch.empty(R * nblk, dtype=torch.uint8, device="cuda")
     done = torch.zeros(R * nblk, dtype=torch.uint8, device="cuda")
-    cnt = torch.zeros(2, dtype=torch.int32, device="cuda") if counted else None
+    cnt = counters_buf() if counted else None
 
     def call():
         fc.fc_ll_gather(slots, nw, B, e, outs, stale, done, cnt)
@@ -200,7 +200,7 @@ def test_all_gather_on_slots_replays(fc, orc, counted):
         assert_equal_bits(down(stale, np.uint8), np.asarray(rst).ravel(), "stale " + where)
         assert_equal_bits(down(done, np.uint8), np.asarray(rdn).ravel(), "done " + where)
         if counted:
-            assert_equal_bits(down(cnt, np.uint32), rc, "counters " + where)
+            assert_equal_bits(counts(cnt), rc, "counters " + where)
         fin = np.asarray(rdn).reshape(R, nblk).astype(bool)
         for r in range(R):
             o = down(outs[r], np.uint32)
@@ -213,7 +213,7 @@ def test_flag_receiver_replays(fc, orc):
     """The flag receiver (8 ranks, 2048-element blocks, 15% of the flags wrong, a poll budget of 2, a
     capped grid): every replay gives the oracle's out, stale, done and the same re-read count."""
     import torch
-    from gpu_helpers import assert_equal_bits, down, up
+    from gpu_helpers import assert_equal_bits, counters_buf, counts, down, up
     cfg = dg.SLOTS
     R, be, nblk, e = 8, 2048, 96, 0x51
     n = be * nblk
@@ -224,7 +224,7 @@ def test_flag_receiver_replays(fc, orc):
     out = torch.empty(n, dtype=torch.int16, device="cuda")
     stale = torch.empty(R * nblk, dtype=torch.uint8, device="cuda")
     done = torch.zeros(nblk, dtype=torch.uint8, device="cuda")
-    cnt = torch.zeros(4, dtype=torch.int32, device="cuda")
+    cnt = counters_buf()
 
     def call():
         fc.fc_flag_unpack_reduce(pay, fl, n, be, e, out, stale, done, cnt, max_polls=2, max_workgroups=7)
@@ -240,7 +240,7 @@ def test_flag_receiver_replays(fc, orc):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        c = down(cnt, np.uint32)
+        c = counts(cnt, 4)
         assert_equal_bits(down(stale, np.uint8), np.asarray(rst).ravel(), f"stale replay {i}")
         assert_equal_bits(down(done, np.uint8), rdn, f"done replay {i}")
         assert_equal_bits(c[:2], rc, f"counters replay {i}")

@@ -29,19 +29,20 @@ def fc():
 
 def _bufs(R, n, nblk, out_fill=0, done0=None):
     import torch
+    from gpu_helpers import counters_buf
     out = torch.full((n,), out_fill, dtype=torch.int16, device="cuda")
     stale = torch.full((R * nblk,), 0xAB, dtype=torch.uint8, device="cuda")
     done = torch.zeros(nblk, dtype=torch.uint8, device="cuda")
     if done0 is not None:
         done.copy_(torch.from_numpy(done0))
-    cnt = torch.zeros(4, dtype=torch.int32, device="cuda")
+    cnt = counters_buf()
     return out, stale, done, cnt
 
 
 def _down_all(out, stale, done, cnt, R, nblk):
-    from gpu_helpers import down
+    from gpu_helpers import counts, down
     return (down(out, np.uint16), down(stale, np.uint8).reshape(R, nblk), down(done, np.uint8),
-            down(cnt, np.uint32))
+            counts(cnt, 4))
 
 
 def _tiles_polled(stale_rb, done0, group):
@@ -205,7 +206,7 @@ def test_ll_poll_equals_one_look_receiver(fc):
     """With no re-reads the polling receiver gives the one-look receiver's bits on the slot workload
     (8 ranks x [128, 8192], 2% late copies, shuffled write order), grid capped or not."""
     import torch
-    from gpu_helpers import assert_equal_bits, down, up
+    from gpu_helpers import assert_equal_bits, counters_buf, down, up
     cfg = dg.SLOTS
     R, n, B, e = cfg.R, cfg.n, cfg.block_slots, cfg.epoch
     nslots, nblk = n // 2, n // 2 // B
@@ -216,7 +217,7 @@ def test_ll_poll_equals_one_look_receiver(fc):
         _inject(s, dg.stale_epochs(cfg, r, nslots)[0])
         slots_d.append(s)
     ref = _bufs(R, n, nblk)
-    c2 = torch.zeros(2, dtype=torch.int32, device="cuda")
+    c2 = counters_buf()
     fc.fc_ll_unpack_reduce(slots_d, n, B, e, ref[0], ref[1], ref[2], c2)
     want = _down_all(ref[0], ref[1], ref[2], c2, R, nblk)
     for mw in (0, 37):
@@ -225,7 +226,7 @@ def test_ll_poll_equals_one_look_receiver(fc):
         g = _down_all(*got, R, nblk)
         for a, b, what in zip(g[:3], want[:3], ("out", "stale", "done")):
             assert_equal_bits(a, b, f"{what} (max_workgroups={mw})")
-        assert_equal_bits(g[3][:2], want[3], "counters")
+        assert_equal_bits(g[3][:2], want[3][:2], "counters")
         assert int(g[3][1]) > 0
 
 
@@ -239,7 +240,7 @@ LIVE_WGS = 32          # the receiver's grid and compute units; the sender has t
 @pytest.mark.parametrize("enc", ["flag", "ll"])
 def test_live_sender_and_receiver(fc, orc, enc):
     import torch
-    from gpu_helpers import assert_equal_bits, up
+    from gpu_helpers import assert_equal_bits, counters_buf, up
     cfg = dg.SLOTS
     R, n = cfg.R, cfg.n
     be, B = 2048, cfg.block_slots
@@ -279,7 +280,7 @@ def test_live_sender_and_receiver(fc, orc, enc):
         got = _down_all(out, stale, done, cnt, R, nblk)
         print(f"  pending after the live pass {int(got[3][1])}, re-reads {int(got[3][2])}", flush=True)
         # whatever the budget left pending is completed by a second, one-look pass
-        c2 = torch.zeros(4, dtype=torch.int32, device="cuda")
+        c2 = counters_buf()
         if enc == "flag":
             fc.fc_flag_unpack_reduce(pays, fls, n, be, e, out, stale, done, c2)
             ro, _, _, _ = orc.flag_unpack_reduce(xs, [np.full(nblk, e, np.uint32)] * R, n, be, e)
@@ -302,7 +303,7 @@ def test_selector_driven_receiver(fc, orc, R, n):
     """SelfSyncReduce picks the encoding from the measured cost table, the senders write, the receiver
     folds: the result equals the oracle's fixed-order sum, whichever encoding was chosen."""
     import torch
-    from gpu_helpers import assert_equal_bits, down, up
+    from gpu_helpers import assert_equal_bits, counts, down, up
     from tensor_all_reduce_amd.flash_allreduce import SelfSyncReduce
     xs = [dg.synth_bf16((0x5E1, R, n, r), n) for r in range(R)]
     ss = SelfSyncReduce(R, n)
@@ -312,7 +313,7 @@ def test_selector_driven_receiver(fc, orc, R, n):
         ss.send([up(x) for x in xs], e)
         ss.receive(e)
         torch.cuda.synchronize()
-        c = down(ss.counters, np.uint32)
+        c = counts(ss.counters, 4)
         assert down(ss.done, np.uint8).all() and list(c) == [0, 0, 0, 0]
         if ss.encoding == "ll":
             ro, _, _, _ = orc.ll_unpack_reduce([orc.ll_pack(x, ss.B, e) for x in xs], n, ss.B, e)

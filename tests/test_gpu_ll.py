@@ -33,19 +33,20 @@ def inject_gpu(slots_d, ep):
 class GpuLL:
     def __init__(self, R, n, B):
         import torch
+        from gpu_helpers import counters_buf
         self.R, self.n, self.B = R, n, B
         self.nblk = n // 2 // B
         self.out = torch.zeros(n, dtype=torch.int16, device="cuda")
         self.stale = torch.full((R * self.nblk,), 0xAB, dtype=torch.uint8, device="cuda")
         self.done = torch.zeros(self.nblk, dtype=torch.uint8, device="cuda")
-        self.cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
+        self.cnt = counters_buf()
 
     def run(self, fc, slots_d, epoch):
         self.cnt.zero_()
         fc.fc_ll_unpack_reduce(slots_d, self.n, self.B, epoch, self.out, self.stale, self.done, self.cnt)
-        from gpu_helpers import down
+        from gpu_helpers import counts, down
         return (down(self.out, np.uint16), down(self.stale, np.uint8).reshape(self.R, self.nblk),
-                down(self.done, np.uint8), down(self.cnt, np.uint32))
+                down(self.done, np.uint8), counts(self.cnt))
 
 
 def test_pack_ranks_in_one_launch(fc, orc):
@@ -198,7 +199,7 @@ def test_receivers_without_counters(fc, orc):
     as with counters, and as the oracle's, for the slot receiver (8-rank workload with its stale mix, both
     passes), the standalone all-gather, the polling slot receiver and the flag receiver."""
     import torch
-    from gpu_helpers import assert_equal_bits, down, up
+    from gpu_helpers import assert_equal_bits, counters_buf, down, up
     cfg = dg.SLOTS
     R, n, B, e = cfg.R, cfg.n, cfg.block_slots, cfg.epoch
     nslots, nblk = n // 2, n // 2 // B
@@ -214,7 +215,7 @@ def test_receivers_without_counters(fc, orc):
     late = [set_epochs_host(orc.ll_pack(xs[r], B, e, order=orders[r]), eps[r]) for r in range(R)]
     ro, rst, rdn, _ = orc.ll_unpack_reduce(late, n, B, e)
     res = {}
-    for tag, cnt in (("counted", torch.zeros(2, dtype=torch.int32, device="cuda")), ("uncounted", None)):
+    for tag, cnt in (("counted", counters_buf()), ("uncounted", None)):
         out = torch.zeros(n, dtype=torch.int16, device="cuda")
         st = torch.full((R * nblk,), 0xAB, dtype=torch.uint8, device="cuda")
         dn = torch.zeros(nblk, dtype=torch.uint8, device="cuda")

@@ -23,17 +23,16 @@ def _slots(words, epochs):
 
 
 def _gpu_gather(fc, slots_h, nwords, B, out=None, done=None, counted=True):
-    """counted=False passes NULL counters (the launcher then takes its smaller tile shape); the returned
-    counters are then zeros."""
+    """counted=False passes NULL counters; the returned counters are then zeros."""
     import torch
-    from gpu_helpers import down, up
+    from gpu_helpers import counters_buf, down, up
     R = len(slots_h)
     nblk = nwords // B
     sl = [up(s) for s in slots_h]
     out = [torch.zeros(nwords, dtype=torch.int32, device="cuda") for _ in range(R)] if out is None else out
     done = torch.zeros(R * nblk, dtype=torch.uint8, device="cuda") if done is None else done
     stale = torch.full((R * nblk,), 7, dtype=torch.uint8, device="cuda")
-    cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
+    cnt = counters_buf()
     fc.fc_ll_gather(sl, nwords, B, E, out, stale, done, cnt if counted else None)
     torch.cuda.synchronize()
     return out, stale, done, cnt
@@ -62,7 +61,7 @@ def _late(R, nblk, B, nwords, seed, frac=0.1):
 def test_ll_gather_parity_and_retry(fc, orc, B, R, nblk, counted):
     """Both tile shapes of the launcher (counted: 16 wavefronts of 4 instructions; uncounted: 8 of 2), every
     block size, ragged tile counts."""
-    from gpu_helpers import assert_equal_bits, down
+    from gpu_helpers import assert_equal_bits, counts, down
     nwords = B * nblk
     rng = np.random.default_rng(B * 100 + R)
     ws = [rng.integers(0, 1 << 32, nwords, dtype=np.uint64).astype(np.uint32) for _ in range(R)]
@@ -76,7 +75,7 @@ def test_ll_gather_parity_and_retry(fc, orc, B, R, nblk, counted):
     assert_equal_bits(down(stale, np.uint8), rs, "stale " + where)
     assert_equal_bits(down(done, np.uint8), rd, "done " + where)
     if counted:
-        assert_equal_bits(down(cnt, np.uint32), rc, "counters " + where)
+        assert_equal_bits(counts(cnt), rc, "counters " + where)
     # the late blocks arrive: the retry completes them
     slots2 = [_slots(ws[r], np.full(nwords, E)) for r in range(R)]
     ro2, rs2, rd2, rc2 = orc.ll_gather(slots2, nwords, B, E, out=ro, done=rd)
@@ -85,7 +84,7 @@ def test_ll_gather_parity_and_retry(fc, orc, B, R, nblk, counted):
         assert_equal_bits(down(out2[r], np.uint32), ws[r], f"retry out rank {r} " + where)
     assert_equal_bits(down(done2, np.uint8), rd2, "retry done " + where)
     if counted:
-        assert_equal_bits(down(cnt2, np.uint32), rc2, "retry counters " + where)
+        assert_equal_bits(counts(cnt2), rc2, "retry counters " + where)
     # stale flags are written for the blocks examined in this pass only
     examined = rd == 0
     assert_equal_bits(down(stale2, np.uint8)[examined], rs2[examined], "retry stale " + where)
@@ -93,7 +92,7 @@ def test_ll_gather_parity_and_retry(fc, orc, B, R, nblk, counted):
 
 def test_ll_gather_done_blocks_untouched(fc, orc):
     import torch
-    from gpu_helpers import assert_equal_bits, down, up
+    from gpu_helpers import assert_equal_bits, counts, down, up
     R, B, nblk = 2, 64, 9
     nwords = B * nblk
     ws = [np.arange(nwords, dtype=np.uint32) + 1000 * r for r in range(R)]
@@ -105,7 +104,7 @@ def test_ll_gather_done_blocks_untouched(fc, orc):
     for r in range(R):
         assert_equal_bits(down(out[r], np.uint32), ro[r], f"rank {r}")
     assert_equal_bits(down(done, np.uint8), rd, "done")
-    assert_equal_bits(down(cnt, np.uint32), rc, "counters")
+    assert_equal_bits(counts(cnt), rc, "counters")
 
 
 def test_quantized_all_gather_in_slots_end_to_end(fc, orc):
@@ -113,7 +112,7 @@ def test_quantized_all_gather_in_slots_end_to_end(fc, orc):
     slots with ~10% late blocks; the receiver validates and copies (pass 1 + retry), then dequantizes the
     gathered messages with the residual-add + RMSNorm epilogue."""
     import torch
-    from gpu_helpers import assert_bf16_close, assert_equal_bits, down, up
+    from gpu_helpers import assert_bf16_close, assert_equal_bits, counts, down, up
     cfg = dg.DECODE_8B
     R, L, G, b2 = cfg.R, cfg.L, cfg.group, cfg.bits_ag
     parts = dg.partials(cfg)
@@ -131,7 +130,7 @@ def test_quantized_all_gather_in_slots_end_to_end(fc, orc):
         words.append(m)
     ep = _late(R, nwords // B, B, nwords, 17)
     out, stale, done, cnt = _gpu_gather(fc, [_slots(words[s], ep[s]) for s in range(R)], nwords, B)
-    assert int(down(cnt, np.uint32)[1]) > 0
+    assert int(counts(cnt, 4)[1]) > 0
     out, stale, done, cnt = _gpu_gather(fc, [_slots(w, np.full(nwords, E)) for w in words], nwords, B, out=out,
                                         done=done)
     assert down(done, np.uint8).all()
@@ -150,7 +149,7 @@ def test_all_gather_prefill_messages_as_benched(fc, orc, counted):
     """The benchmark's f3 workload: the 8 int8 shard messages of the 70B prefill (codes then meta, 1,081,344
     words each) carried in 64-slot blocks with about 2% of the copies late (every kind), pass 1 then the
     retry with every block rewritten: out, stale, done and counters of both passes equal the oracle's."""
-    from gpu_helpers import assert_equal_bits, down
+    from gpu_helpers import assert_equal_bits, counts, down
     cfg = dg.PREFILL_70B
     R, B = cfg.R, 64
     nwords = (cfg.L * cfg.bits_ag // 8 + 4 * (cfg.L // cfg.group)) // 4
@@ -168,7 +167,7 @@ def test_all_gather_prefill_messages_as_benched(fc, orc, counted):
     assert_equal_bits(down(stale, np.uint8), rst, "pass 1 stale")
     assert_equal_bits(down(done, np.uint8), rdn, "pass 1 done")
     if counted:
-        assert_equal_bits(down(cnt, np.uint32), rc, "pass 1 counters")
+        assert_equal_bits(counts(cnt), rc, "pass 1 counters")
     assert int(rc[1]) > 0
     again = [_slots(words[r], np.full(nwords, E)) for r in range(R)]
     out, stale, done, cnt = _gpu_gather(fc, again, nwords, B, out=out, done=done, counted=counted)
@@ -178,4 +177,4 @@ def test_all_gather_prefill_messages_as_benched(fc, orc, counted):
     assert_equal_bits(down(done, np.uint8), rdn2, "retry done")
     assert rdn2.all() and int(rc2[1]) == 0
     if counted:
-        assert_equal_bits(down(cnt, np.uint32), rc2, "retry counters")
+        assert_equal_bits(counts(cnt), rc2, "retry counters")

@@ -128,7 +128,7 @@ def test_gather_norm_largest(fc, orc):
 
 def test_slot_receiver_largest(fc, orc):
     import torch
-    from gpu_helpers import assert_equal_bits
+    from gpu_helpers import assert_equal_bits, counters_buf, counts
     R, B, e = 2, 64, 0x5EED
     n = KMAX // (2 * B) * (2 * B)  # 2^31 - 128 elements, 2^30 - 64 slots per rank
     nslots, nblk = n // 2, n // 2 // B
@@ -147,10 +147,10 @@ def test_slot_receiver_largest(fc, orc):
     out = torch.zeros(n, dtype=torch.int16, device="cuda")
     stale = torch.zeros(R * nblk, dtype=torch.uint8, device="cuda")
     done = torch.zeros(nblk, dtype=torch.uint8, device="cuda")
-    cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
+    cnt = counters_buf()
     fc.fc_ll_unpack_reduce(slots, n, B, e, out, stale, done, cnt)
     torch.cuda.synchronize()
-    assert list(cnt.cpu().numpy().view(np.uint32)) == [len(late), len(late)]
+    assert list(counts(cnt)) == [len(late), len(late)]
     for b in _samples(nblk, np.random.default_rng(4), extra=late):
         ss = [_host(s, b * B, (b + 1) * B, np.uint64) for s in slots]
         ro, rst, rdn, _ = orc.ll_unpack_reduce(ss, 2 * B, B, e)
@@ -184,7 +184,7 @@ def test_reduce_rmsnorm_largest(fc, orc):
 
 def test_flag_receiver_largest(fc, orc):
     import torch
-    from gpu_helpers import assert_equal_bits
+    from gpu_helpers import assert_equal_bits, counters_buf, counts
     R, be, e = 2, 65536, 0xF1A6
     n = KMAX // be * be
     nblk = n // be
@@ -196,10 +196,10 @@ def test_flag_receiver_largest(fc, orc):
     out = torch.zeros(n, dtype=torch.int16, device="cuda")
     stale = torch.zeros(R * nblk, dtype=torch.uint8, device="cuda")
     done = torch.zeros(nblk, dtype=torch.uint8, device="cuda")
-    cnt = torch.zeros(4, dtype=torch.int32, device="cuda")
+    cnt = counters_buf()
     fc.fc_flag_unpack_reduce(pays, fls, n, be, e, out, stale, done, cnt)
     torch.cuda.synchronize()
-    assert list(cnt.cpu().numpy().view(np.uint32)) == [len(late), len(late), 0, 0]
+    assert list(counts(cnt, 4)) == [len(late), len(late), 0, 0]
     for b in _samples(nblk, np.random.default_rng(7), extra=late):
         lo, hi = b * be, (b + 1) * be
         ro, rst, rdn, _ = orc.flag_unpack_reduce([_host(p, lo, hi, np.uint16) for p in pays],
@@ -212,7 +212,7 @@ def test_flag_receiver_largest(fc, orc):
 
 def test_allgather_largest(fc, orc):
     import torch
-    from gpu_helpers import assert_equal_bits
+    from gpu_helpers import assert_equal_bits, counters_buf, counts
     R, B, e = 1, 64, 0x6A7
     nwords = KMAX // B * B
     nblk = nwords // B
@@ -225,10 +225,10 @@ def test_allgather_largest(fc, orc):
     out = [torch.zeros(nwords, dtype=torch.int32, device="cuda")]
     stale = torch.zeros(R * nblk, dtype=torch.uint8, device="cuda")
     done = torch.zeros(R * nblk, dtype=torch.uint8, device="cuda")
-    cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
+    cnt = counters_buf()
     fc.fc_ll_gather(slots, nwords, B, e, out, stale, done, cnt)
     torch.cuda.synchronize()
-    assert list(cnt.cpu().numpy().view(np.uint32)) == [len(late), len(late)]
+    assert list(counts(cnt)) == [len(late), len(late)]
     for b in _samples(nblk, np.random.default_rng(8), extra=late):
         ro, rst, rdn, _ = orc.ll_gather([_host(slots[0], b * B, (b + 1) * B, np.uint64)], B, B, e)
         assert_equal_bits(_host(done, b, b + 1, np.uint8), rdn, f"done of block {b}")

@@ -92,7 +92,7 @@ def _slot_cases(count, seed):
 @pytest.mark.parametrize("R,B,nblk,e,frac,counted,seed", _slot_cases(40, 0x51075), ids=lambda v: str(v))
 def test_slot_receiver_random(fc, orc, R, B, nblk, e, frac, counted, seed):
     import torch
-    from gpu_helpers import assert_equal_bits, down, up
+    from gpu_helpers import assert_equal_bits, counters_buf, counts, down, up
     rng = np.random.default_rng(seed)
     nslots = B * nblk
     n = 2 * nslots
@@ -110,7 +110,7 @@ def test_slot_receiver_random(fc, orc, R, B, nblk, e, frac, counted, seed):
     out = torch.full((n,), int(fill.astype(np.int16)), dtype=torch.int16, device="cuda")
     stale = torch.full((R * nblk,), 0xAB, dtype=torch.uint8, device="cuda")
     done = up(done0.copy())
-    cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
+    cnt = counters_buf()
     where = f"R={R} B={B} nblk={nblk} e={e:#x} late={frac} counted={counted}"
 
     fc.fc_ll_unpack_reduce(slots_d, n, B, e, out, stale, done, cnt if counted else None)
@@ -123,7 +123,7 @@ def test_slot_receiver_random(fc, orc, R, B, nblk, e, frac, counted, seed):
     assert_equal_bits(st[:, ~skipped], np.asarray(rst).reshape(R, nblk)[:, ~skipped], "stale " + where)
     assert_equal_bits(down(done, np.uint8), rdn, "done " + where)
     assert_equal_bits(down(out, np.uint16), ro, "out " + where)
-    assert_equal_bits(down(cnt, np.uint32), rc if counted else np.zeros(2, np.uint32), "counters " + where)
+    assert_equal_bits(counts(cnt), rc if counted else np.zeros(2, np.uint32), "counters " + where)
 
     # the late blocks are published; the second pass completes them with the bits of an on-time pass
     fc.fc_ll_pack([up(x) for x in xs], B, e, slots_d)
@@ -134,7 +134,7 @@ def test_slot_receiver_random(fc, orc, R, B, nblk, e, frac, counted, seed):
     assert np.all(rdn2 == 1)
     assert_equal_bits(down(done, np.uint8), rdn2, "done, second pass " + where)
     assert_equal_bits(down(out, np.uint16), ro2, "out, second pass " + where)
-    assert_equal_bits(down(cnt, np.uint32), rc2 if counted else np.zeros(2, np.uint32), "counters, second pass " + where)
+    assert_equal_bits(counts(cnt), rc2 if counted else np.zeros(2, np.uint32), "counters, second pass " + where)
     # every block not done before the first pass now holds the on-time reduction
     full, _, _, _ = orc.ll_unpack_reduce(good, n, B, e)
     fresh = np.repeat(~skipped, 2 * B)
@@ -155,7 +155,7 @@ def _gather_cases(count, seed):
 @pytest.mark.parametrize("R,B,nblk,e,frac,counted,seed", _gather_cases(24, 0x6A7), ids=lambda v: str(v))
 def test_all_gather_random(fc, orc, R, B, nblk, e, frac, counted, seed):
     import torch
-    from gpu_helpers import assert_equal_bits, down, up
+    from gpu_helpers import assert_equal_bits, counters_buf, counts, down, up
     rng = np.random.default_rng(seed)
     nw = B * nblk
     words = [rng.integers(0, 1 << 32, nw, dtype=np.uint64) for _ in range(R)]
@@ -167,7 +167,7 @@ def test_all_gather_random(fc, orc, R, B, nblk, e, frac, counted, seed):
     outs = [torch.full((nw,), 0x5A5A5A5A, dtype=torch.int32, device="cuda") for _ in range(R)]
     stale = torch.full((R * nblk,), 0xAB, dtype=torch.uint8, device="cuda")
     done = up(done0.copy())
-    cnt = torch.zeros(2, dtype=torch.int32, device="cuda")
+    cnt = counters_buf()
     where = f"R={R} B={B} nblk={nblk} e={e:#x} late={frac} counted={counted}"
     r_out = [np.full(nw, 0x5A5A5A5A, np.uint32) for _ in range(R)]
     for p, slots_h in enumerate((late, good)):
@@ -183,7 +183,7 @@ def test_all_gather_random(fc, orc, R, B, nblk, e, frac, counted, seed):
         for r in range(R):
             assert_equal_bits(down(outs[r], np.uint32), r_out[r], f"out[{r}]" + tag)
         assert_equal_bits(down(done, np.uint8), r_dn, "done" + tag)
-        assert_equal_bits(down(cnt, np.uint32), rc if counted else np.zeros(2, np.uint32), "counters" + tag)
+        assert_equal_bits(counts(cnt), rc if counted else np.zeros(2, np.uint32), "counters" + tag)
         if p == 0:
             st = down(stale, np.uint8)
             ex = done0 == 0
@@ -210,7 +210,7 @@ def _flag_cases(count, seed):
 @pytest.mark.parametrize("R,be,nblk,e,polls,mw,seed", _flag_cases(24, 0xF1A6), ids=lambda v: str(v))
 def test_flag_receiver_random(fc, orc, R, be, nblk, e, polls, mw, seed):
     import torch
-    from gpu_helpers import assert_equal_bits, down, up
+    from gpu_helpers import assert_equal_bits, counters_buf, counts, down, up
     rng = np.random.default_rng(seed)
     n = be * nblk
     xs = [_bf16(rng, n) for _ in range(R)]
@@ -225,7 +225,7 @@ def test_flag_receiver_random(fc, orc, R, be, nblk, e, polls, mw, seed):
     out = torch.full((n,), 77, dtype=torch.int16, device="cuda")
     stale = torch.full((R * nblk,), 0xAB, dtype=torch.uint8, device="cuda")
     done = up(done0.copy())
-    cnt = torch.zeros(4, dtype=torch.int32, device="cuda")
+    cnt = counters_buf()
     where = f"R={R} be={be} nblk={nblk} e={e:#x} polls={polls} max_workgroups={mw}"
     fc.fc_flag_unpack_reduce([up(x) for x in xs], [up(f) for f in fls], n, be, e, out, stale, done, cnt,
                              max_polls=polls, max_workgroups=mw)
@@ -237,7 +237,7 @@ def test_flag_receiver_random(fc, orc, R, be, nblk, e, polls, mw, seed):
     assert_equal_bits(st[:, ~skipped], np.asarray(rst).reshape(R, nblk)[:, ~skipped], "stale " + where)
     assert_equal_bits(down(done, np.uint8), rdn, "done " + where)
     assert_equal_bits(down(out, np.uint16), ro, "out " + where)
-    c = down(cnt, np.uint32)
+    c = counts(cnt, 4)
     assert_equal_bits(c[:2], rc, "counters " + where)
     if polls == 0:
         assert c[2] == 0 and c[3] == 0, where
