@@ -332,10 +332,11 @@ __global__ __launch_bounds__(64 * W) void k_ll_gather(const int64_t nslots, cons
     }
 }
 
-// Tile shape of the all-gather: 8 wavefronts of 2 instructions, counted or not (int8 prefill messages,
-// pass 1: 20.1 us uncounted, 20.3 us counted; 16 wavefronts of 4: 20.2 and 22.6 us; 4 x 16: 21.7 us
-// uncounted).  With the counts in eight groups, the smaller workgroups' atomics (one per workgroup) cost
-// next to nothing; into one address, they had cost 2.3 us more than the large tiles' fewer ones.
+// Tile shape of the all-gather: 4 wavefronts of 2 instructions, counted or not.  int8 prefill messages,
+// pass 1, uncounted / counted (same process): 4 x 2 19.8 / 20.2 us; 8 x 2 20.3 / 20.6; 8 x 1 22.2 / 21.5;
+// 8 x 4 20.8 / 21.1; 16 x 2 20.9 / 21.5; 16 x 4 20.2 / 22.6.  With the counts in eight groups the
+// smaller workgroups' atomics (one per workgroup) cost little; into one address they had cost 2.3 us
+// more than the large tiles' fewer ones.
 
 hipError_t launch_ll_gather(const LLGatherParams& p, hipStream_t s) {
     LLGatherTabs t;
@@ -351,10 +352,10 @@ hipError_t launch_ll_gather(const LLGatherParams& p, hipStream_t s) {
         k_ll_gather<B, W, K><<<grid, 64 * (W), 0, s>>>(nslots, nblk, p.done, p.stale, p.epoch, p.counters, t); \
     } while (0)
     switch (p.block_slots) {
-        case 32: FC_LLG(32, 8, 2); break;
-        case 64: FC_LLG(64, 8, 2); break;
-        case 128: FC_LLG(128, 8, 2); break;
-        default: FC_LLG(256, 8, 2); break;  // a 256-slot block spans the tile's two instructions
+        case 32: FC_LLG(32, 4, 2); break;
+        case 64: FC_LLG(64, 4, 2); break;
+        case 128: FC_LLG(128, 4, 2); break;
+        default: FC_LLG(256, 4, 2); break;  // a 256-slot block spans the tile's two instructions
     }
 #undef FC_LLG
     return hipGetLastError();
